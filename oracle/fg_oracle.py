@@ -1,0 +1,583 @@
+"""Plain, slow CPU oracle of the fused gather-GEMM and of its signal protocol.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring). numpy, float64 for all
+floating point, Python loops where the definition is a loop.
+
+Pages cited (titles abbreviated):
+  "PCIe sync protocols"  = Compute-comm fused operators (4): cross-card sync
+                           protocols over PCIe -- single writer, election, watermark
+  "Know your platform"   = Compute-comm fused operators (2): know your platform
+  "NVLink atomic publish" = hardware atomic publish and monotonic counters over NVLink
+  "DeepEP FIFO pipeline" = DeepEP v2 FIFO / streaming pipeline analysis
+
+Where the pages leave a step open, the reading taken is named in the docstring
+of the function that takes it (R-numbers refer to the list of readings kept with
+the design notes).
+
+Every function here is pinned by tests against closed forms, invariants, hand
+worked examples, library special cases or brute force, except the latency
+figures, which are measurements only.
+"""
+from __future__ import annotations
+
+import dataclasses
+import itertools
+import math
+
+import numpy as np
+
+CHUNK_ROWS = 64     # PCIe sync protocols §4: the watermark cuts each producer stream every 64 rows
+ROW_BLOCK = 128     # PCIe sync protocols §5: the GEMM gate releases 128 gathered rows at a time
+
+BF16_MAX = float.fromhex("0x1.fep127")
+
+
+# ---------------------------------------------------------------------------
+# bf16 <-> float64 (the contraction's inputs are bf16; the oracle computes in fp64)
+# ---------------------------------------------------------------------------
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact decode: a bf16 is the upper half of a float32."""
+    b = np.asarray(bits, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(x) -> np.ndarray:
+    """Round float64 to bf16 bits, nearest with ties to even, in one step
+    (no intermediate float32, so no double rounding). NaN -> 0x7FC0."""
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.abs(x)
+    with np.errstate(over="ignore", invalid="ignore"):
+        _, e = np.frexp(ax)                       # ax = m * 2**e, m in [0.5, 1)
+        e = np.maximum(e, -125)                    # below 2**-126 the grid is 2**-133
+        q = np.ldexp(ax, (8 - e).astype(np.int32))  # bf16 grid points become integers
+        y = np.ldexp(np.rint(q), (e - 8).astype(np.int32))  # rint = round half to even
+        y = np.where(y > BF16_MAX, np.inf, y)
+        y = np.where(np.isinf(ax), np.inf, y)
+    bits = (y.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    bits = bits | (np.signbit(x).astype(np.uint16) << np.uint16(15))
+    return np.where(np.isnan(x), np.uint16(0x7FC0), bits).astype(np.uint16)
+
+
+def bf16_ulp(x) -> np.ndarray:
+    """Spacing of the bf16 grid at |x| (8 significant bits)."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(ax)
+    e = np.maximum(e, -125)
+    return np.ldexp(1.0, (e - 8).astype(np.int32))
+
+
+# ---------------------------------------------------------------------------
+# Layout / route (step a1): which source row lands on which gathered row
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Layout:
+    """Per shard s a stream of (src_row, dst_row) pairs in stream order; the
+    stream is what the producer emits and what the chunk watermark cuts
+    (PCIe sync protocols §4)."""
+    src_row: list           # n_shards arrays (int64)
+    dst_row: list           # n_shards arrays (int64)
+    m_pad: int              # gathered rows, a multiple of row_block
+    group_off: np.ndarray   # [n_groups + 1] first gathered row of each group, multiples of row_block
+    row_block: int = ROW_BLOCK
+    chunk_rows: int = CHUNK_ROWS
+
+    @property
+    def n_shards(self) -> int:
+        return len(self.src_row)
+
+    @property
+    def stream_len(self) -> np.ndarray:
+        return np.array([len(d) for d in self.dst_row], dtype=np.int64)
+
+    @property
+    def m(self) -> int:
+        return int(self.stream_len.sum())
+
+    @property
+    def n_rb(self) -> int:
+        return self.m_pad // self.row_block
+
+    @property
+    def n_groups(self) -> int:
+        return len(self.group_off) - 1
+
+
+def _round_up(x: int, b: int) -> int:
+    return -(-x // b) * b
+
+
+def layout_contiguous(n_shards: int, rows: int, row_block: int = ROW_BLOCK,
+                      chunk_rows: int = CHUNK_ROWS) -> Layout:
+    """All-gather layout: shard s's row i lands on gathered row s*rows + i."""
+    src = [np.arange(rows, dtype=np.int64) for _ in range(n_shards)]
+    dst = [s * rows + np.arange(rows, dtype=np.int64) for s in range(n_shards)]
+    m_pad = _round_up(n_shards * rows, row_block)
+    return Layout(src, dst, m_pad, np.array([0, m_pad], dtype=np.int64), row_block, chunk_rows)
+
+
+def layout_permutation(perm, n_shards: int, rows: int, row_block: int = ROW_BLOCK,
+                       chunk_rows: int = CHUNK_ROWS) -> Layout:
+    """Scattered all-gather: stream row (s, i) lands on gathered row perm[s*rows + i]."""
+    perm = np.asarray(perm, dtype=np.int64)
+    assert perm.shape == (n_shards * rows,)
+    src = [np.arange(rows, dtype=np.int64) for _ in range(n_shards)]
+    dst = [perm[s * rows:(s + 1) * rows].copy() for s in range(n_shards)]
+    m_pad = _round_up(n_shards * rows, row_block)
+    lay = Layout(src, dst, m_pad, np.array([0, m_pad], dtype=np.int64), row_block, chunk_rows)
+    check_layout(lay)
+    return lay
+
+
+def layout_topk(topk, expert_base: int, n_local: int, row_block: int = ROW_BLOCK,
+                chunk_rows: int = CHUNK_ROWS) -> Layout:
+    """Expert-parallel dispatch layout (the "notify" counting stage of the DeepEP
+    FIFO pipeline dispatch, with the padding rule of PCIe sync protocols §5).
+
+    Reading R11: source shard s, token t, choice k routes to local expert
+    e = topk[s][t][k] - expert_base when that lies in [0, n_local). Each shard's
+    stream lists its pairs in (t, k) order. Inside expert e, rows are ordered by
+    global token id g = s*T + t; expert e's rows start at off_e, where off_0 = 0 and
+    off_{e+1} = off_e + ceil(n_e / row_block) * row_block, so no row block spans
+    two experts and every padding row is at the end of its expert's segment.
+    """
+    topk = np.asarray(topk, dtype=np.int64)
+    S, T, KK = topk.shape
+    pairs = []                                   # (s, t, e) in (s, t, k) order = global token order
+    for s in range(S):
+        for t in range(T):
+            for k in range(KK):
+                e = int(topk[s, t, k]) - expert_base
+                if 0 <= e < n_local:
+                    pairs.append((s, t, e))
+    n_e = [0] * n_local
+    for (_, _, e) in pairs:
+        n_e[e] += 1
+    off = [0]
+    for e in range(n_local):
+        off.append(off[-1] + _round_up(n_e[e], row_block))
+    cursor = off[:-1]
+    src = [[] for _ in range(S)]
+    dst = [[] for _ in range(S)]
+    for (s, t, e) in pairs:
+        src[s].append(t)
+        dst[s].append(cursor[e])
+        cursor[e] += 1
+    lay = Layout([np.array(x, dtype=np.int64) for x in src],
+                 [np.array(x, dtype=np.int64) for x in dst],
+                 off[-1], np.array(off, dtype=np.int64), row_block, chunk_rows)
+    check_layout(lay)
+    return lay
+
+
+def check_layout(lay: Layout) -> None:
+    """dst rows are injective and in range; no group straddles a row block."""
+    d = np.concatenate(lay.dst_row) if lay.n_shards else np.zeros(0, np.int64)
+    assert d.size == 0 or (d.min() >= 0 and d.max() < lay.m_pad)
+    assert np.unique(d).size == d.size, "two stream rows target one gathered row"
+    assert np.all(lay.group_off % lay.row_block == 0)
+
+
+def group_of_row(lay: Layout) -> np.ndarray:
+    """Group (expert) index of every gathered row."""
+    g = np.zeros(lay.m_pad, dtype=np.int64)
+    for i in range(lay.n_groups):
+        g[lay.group_off[i]:lay.group_off[i + 1]] = i
+    return g
+
+
+def real_rows(lay: Layout) -> np.ndarray:
+    """Boolean [m_pad]: True where a stream row lands (False = padding row)."""
+    r = np.zeros(lay.m_pad, dtype=bool)
+    for d in lay.dst_row:
+        r[d] = True
+    return r
+
+
+# ---------------------------------------------------------------------------
+# Gather (step a3): a bitwise row copy
+# ---------------------------------------------------------------------------
+
+def gather(shards_bits, lay: Layout) -> np.ndarray:
+    """G[dst_row[s][i]] = X_s[src_row[s][i]] bit for bit; padding rows stay +0.
+    ``shards_bits``: n_shards uint16 arrays [rows, K] (bf16 bit patterns)."""
+    K = shards_bits[0].shape[1]
+    G = np.zeros((lay.m_pad, K), dtype=np.uint16)
+    for s in range(lay.n_shards):
+        for src, dst in zip(lay.src_row[s], lay.dst_row[s]):
+            G[dst] = shards_bits[s][src]
+    return G
+
+
+# ---------------------------------------------------------------------------
+# Closed forms of the protocol (PCIe sync protocols §2 point 2: writer counts and
+# signal counts must have a closed form; §4 chunk watermark; §5 seeded counters)
+# ---------------------------------------------------------------------------
+
+def chunk_table(lay: Layout) -> list:
+    """expected[s][c] = rows of stream s in chunk c = min(chunk, n_s - chunk*c)."""
+    out = []
+    for n in lay.stream_len:
+        n = int(n)
+        out.append(np.array([min(lay.chunk_rows, n - lay.chunk_rows * c)
+                             for c in range(-(-n // lay.chunk_rows))], dtype=np.int64))
+    return out
+
+
+def seeds(lay: Layout) -> np.ndarray:
+    """Padding seed per row block: row_block minus the real rows landing in it,
+    so real arrivals lift the counter to exactly row_block (PCIe sync protocols §5)."""
+    real = np.zeros(lay.n_rb, dtype=np.int64)
+    for d in lay.dst_row:
+        for r in d:
+            real[r // lay.row_block] += 1
+    return lay.row_block - real
+
+
+def signal_counts(lay: Layout) -> dict:
+    """Per-iteration closed forms."""
+    n = lay.stream_len
+    return dict(
+        publishes=int(sum(-(-int(x) // lay.chunk_rows) for x in n)),
+        arrivals=int(n.sum()),
+        gate_openings=lay.n_rb,
+        seed_sum=lay.m_pad - int(n.sum()),
+        publishers_per_chunk=1,
+    )
+
+
+@dataclasses.dataclass
+class ProtocolState:
+    slot: np.ndarray        # [S, chunk_cap]   monotonic sequence numbers, never reset
+    counter: np.ndarray     # [2, n_rb]        parity double-buffered arrival counters
+    elect: np.ndarray       # [2, S, chunk_cap] parity double-buffered election counts
+    pub_count: np.ndarray   # [S, chunk_cap]   publishes seen per slot
+
+
+def state_after(lay: Layout, t: int, chunk_cap: int) -> ProtocolState:
+    """Control-plane state after iterations 1..t over one fixed layout.
+
+    PCIe sync protocols §2 point 1: the slot of iteration k holds k and is never
+    cleared. Reading R4: counters and election counts are double-buffered by the
+    parity of the iteration (the phase trick of the DeepEP FIFO pipeline barrier):
+    iteration t consumes parity t&1 and re-arms parity (t+1)&1 (counters to the
+    seed, election counts to 0); before iteration 1 both parities hold the seed.
+    """
+    S = lay.n_shards
+    exp = chunk_table(lay)
+    sd = seeds(lay)
+    slot = np.zeros((S, chunk_cap), dtype=np.int64)
+    elect = np.zeros((2, S, chunk_cap), dtype=np.int64)
+    pub = np.zeros((S, chunk_cap), dtype=np.int64)
+    counter = np.zeros((2, lay.n_rb), dtype=np.int64)
+    counter[0] = sd
+    counter[1] = sd
+    if t >= 1:
+        for s in range(S):
+            nc = len(exp[s])
+            slot[s, :nc] = t
+            pub[s, :nc] = t
+            elect[t & 1, s, :nc] = exp[s]
+        counter[t & 1] = lay.row_block
+        counter[(t + 1) & 1] = sd
+    return ProtocolState(slot, counter, elect, pub)
+
+
+# ---------------------------------------------------------------------------
+# Step-by-step protocol simulation (the pages' steps in their order), used to pin
+# the closed forms above; Python loops, small inputs only.
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class SimResult:
+    state: ProtocolState
+    publishes: int
+    arrivals: int
+    gate_openings: int
+    early_gates: int        # gate opened while a real row of its block was unwritten
+    early_publishes: int    # chunk published while one of its rows was unwritten
+
+
+def simulate_iteration(lay: Layout, state: ProtocolState, t: int, batches, order,
+                       seed_vec=None) -> SimResult:
+    """One iteration of the comm side, batch by batch.
+
+    ``batches``: list of lists of (s, i) stream rows; each batch is what one wave
+    moves before it signals. ``order``: the order in which batches complete.
+    For each batch, in order (PCIe sync protocols §3 and §5):
+      1. write its rows into the gathered buffer;
+      2. per row block it touched, add its row count to the block's counter;
+      3. per chunk it touched, add its row count to the chunk's election count;
+         the add that brings the count to the chunk's expected size elects the
+         batch, which stores t into the chunk's slot (single writer).
+    A gate opens the first time its counter equals row_block. At the end, the
+    other parity is re-armed (reading R4). ``seed_vec`` overrides the seed used to
+    re-arm (to plant a mistake).
+    """
+    p = t & 1
+    exp = chunk_table(lay)
+    rb_of = lambda d: d // lay.row_block  # noqa: E731
+    written = np.zeros(lay.m_pad, dtype=bool)
+    real = real_rows(lay)
+    chunk_rows_written = {}
+    opened = np.zeros(lay.n_rb, dtype=bool)
+    pubs = arr = gates = early_g = early_p = 0
+    for b in order:
+        rows = batches[b]
+        for (s, i) in rows:
+            written[lay.dst_row[s][i]] = True
+        per_rb = {}
+        per_chunk = {}
+        for (s, i) in rows:
+            r = int(rb_of(lay.dst_row[s][i]))
+            per_rb[r] = per_rb.get(r, 0) + 1
+            c = (s, i // lay.chunk_rows)
+            per_chunk[c] = per_chunk.get(c, 0) + 1
+        for r, n in per_rb.items():
+            state.counter[p, r] += n
+            arr += n
+            if state.counter[p, r] == lay.row_block and not opened[r]:
+                opened[r] = True
+                gates += 1
+                blk = slice(r * lay.row_block, (r + 1) * lay.row_block)
+                if np.any(real[blk] & ~written[blk]):
+                    early_g += 1
+        for (s, c), n in per_chunk.items():
+            chunk_rows_written[(s, c)] = chunk_rows_written.get((s, c), 0) + n
+            old = state.elect[p, s, c]
+            state.elect[p, s, c] = old + n
+            if old + n == exp[s][c]:
+                state.slot[s, c] = t
+                state.pub_count[s, c] += 1
+                pubs += 1
+                lo = c * lay.chunk_rows
+                d = lay.dst_row[s][lo:lo + exp[s][c]]
+                if not np.all(written[d]):
+                    early_p += 1
+    q = (t + 1) & 1
+    state.counter[q] = seeds(lay) if seed_vec is None else seed_vec
+    state.elect[q] = 0
+    return SimResult(state, pubs, arr, gates, early_g, early_p)
+
+
+def election_brute_force(parts) -> int:
+    """A chunk of sum(parts) rows finished by len(parts) waves, wave w adding
+    parts[w]: over every completion order, count the adds that see
+    old + n == expected. The election is sound iff this is exactly 1 for every
+    order (PCIe sync protocols §3). Returns the number of orders that break it."""
+    expected = sum(parts)
+    bad = 0
+    for order in itertools.permutations(range(len(parts))):
+        total = 0
+        elected = 0
+        for w in order:
+            old = total
+            total += parts[w]
+            if old + parts[w] == expected:
+                elected += 1
+        bad += (elected != 1)
+    return bad
+
+
+def model_check_gate(programs, seed: int, target: int) -> int:
+    """Exhaustive interleavings of a toy sequentially consistent protocol.
+
+    ``programs``: one list of steps per producer; a step is ('w', row) to write a
+    row or ('a', n) to add n to the gate counter. The counter starts at ``seed``;
+    the consumer may check the gate between any two steps. Returns the number of
+    interleavings in which the consumer sees counter == target while some row is
+    unwritten (PCIe sync protocols §5: the gate must imply the data)."""
+    rows = {st[1] for p in programs for st in p if st[0] == 'w'}
+    lens = [len(p) for p in programs]
+    bad = 0
+    seqs = []
+    for pi, n in enumerate(lens):
+        seqs += [pi] * n
+    for perm in set(itertools.permutations(seqs)):
+        pos = [0] * len(programs)
+        ctr = seed
+        done = set()
+        violated = False
+        for pi in perm:
+            op, v = programs[pi][pos[pi]]
+            pos[pi] += 1
+            if op == 'w':
+                done.add(v)
+            else:
+                ctr += v
+            if ctr == target and done != rows:
+                violated = True
+        bad += violated
+    return bad
+
+
+# ---------------------------------------------------------------------------
+# The contraction (step a7)
+# ---------------------------------------------------------------------------
+
+def gemm(G_bits, W_bits, lay: Layout, rows=None) -> np.ndarray:
+    """C[m, n] = sum_k G[m, k] * W_g(m)[k, n] in float64 (exact bf16 decode).
+
+    ``W_bits``: uint16 [n_groups, N, K] holding W_g[k, n] at [g, n, k] (the
+    logical K x N weight stored contraction-index contiguous).
+    ``rows``: optional subset of gathered rows to compute (default: all).
+    Padding rows yield 0 (their gathered row is 0)."""
+    G = bf16_to_f64(G_bits if rows is None else G_bits[rows])
+    grp = group_of_row(lay) if rows is None else group_of_row(lay)[rows]
+    W = np.asarray(W_bits)
+    if W.ndim == 2:
+        W = W[None]
+    N = W.shape[1]
+    C = np.zeros((G.shape[0], N), dtype=np.float64)
+    for g in range(W.shape[0]):
+        sel = np.nonzero(grp == g)[0]
+        if sel.size:
+            C[sel] = G[sel] @ bf16_to_f64(W[g]).T
+    if rows is None:
+        C[~real_rows(lay)] = 0.0
+    else:
+        C[~real_rows(lay)[rows]] = 0.0
+    return C
+
+
+def gemm_tolerance(K: int, sigma_x: float, sigma_w: float) -> float:
+    """Stated tolerance on the contraction: 2e-2 of the output's standard
+    deviation sqrt(K) * sigma_x * sigma_w (reading R14)."""
+    return 2e-2 * math.sqrt(K) * sigma_x * sigma_w
+
+
+def gemm_check(out_bits, C64, K, sigma_x, sigma_w, real_mask=None) -> dict:
+    """Compare bf16 GPU output with the float64 result. Pass iff every element
+    satisfies |out - C| <= tol + ulp_bf16(C)/2, where tol is the stated
+    contraction tolerance and the half ulp is the output's own round-to-nearest
+    (reading R14); padding rows must be exactly 0 (either sign)."""
+    out = bf16_to_f64(out_bits)
+    tol = gemm_tolerance(K, sigma_x, sigma_w)
+    diff = np.abs(out - C64)
+    allow = tol + 0.5 * bf16_ulp(C64)
+    ok_mask = diff <= allow
+    if real_mask is not None:
+        ok_mask[~real_mask] = (out[~real_mask] == 0.0)
+    rms = float(np.sqrt(np.mean(C64 ** 2))) if C64.size else 0.0
+    return dict(ok=bool(ok_mask.all()), n_bad=int((~ok_mask).sum()),
+                max_abs=float(diff.max()) if diff.size else 0.0, tol=tol,
+                max_over_scale=float(diff.max() / (tol / 2e-2)) if diff.size else 0.0,
+                max_over_rms=float(diff.max() / rms) if rms else 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Protocol stress workload (PCIe sync protocols §3: tens of thousands of
+# signals per round over dozens of rounds; §4 chunked slots)
+# ---------------------------------------------------------------------------
+
+def stress_payload(seq: int, p: int, c: int, k: int, r: int, C: int, KC: int) -> int:
+    """The 4-byte word a producer writes for row r of chunk (p, c, k) at
+    iteration ``seq`` (reading R13): the iteration in the top bits, the row's
+    unique index below, so a stale row is visible."""
+    idx = ((p * C + c) * KC + k) * CHUNK_ROWS + r
+    return ((seq << 20) ^ idx) & 0xFFFFFFFF
+
+
+def stress_expected(chunk_rows, t: int) -> dict:
+    """After iterations 1..t: slot = t and pub_count = t where a chunk is active,
+    0 elsewhere; every written payload row holds iteration t's word. Independent
+    of the producers' delays."""
+    cr = np.asarray(chunk_rows, dtype=np.int64)
+    P, C, KC = cr.shape
+    active = cr > 0
+    slot = np.where(active, t, 0)
+    payload = np.zeros((C, P, KC, CHUNK_ROWS), dtype=np.uint32)
+    valid = np.zeros((C, P, KC, CHUNK_ROWS), dtype=bool)
+    if t >= 1:
+        for p in range(P):
+            for c in range(C):
+                for k in range(KC):
+                    for r in range(int(cr[p, c, k])):
+                        payload[c, p, k, r] = stress_payload(t, p, c, k, r, C, KC)
+                        valid[c, p, k, r] = True
+    return dict(slot=slot, pub_count=slot.copy(), payload=payload, valid=valid,
+                signals=int(active.sum()))
+
+
+def stress_simulate(chunk_rows, t: int, delays, waves: int = 4) -> dict:
+    """Event-order simulation of one stress iteration: producers' chunks complete
+    in the order of their delays (ties by index); each chunk is written by
+    ``waves`` waves that elect one publisher; consumers check each chunk's rows
+    after seeing its slot. Returns slots, publisher counts and stale rows."""
+    cr = np.asarray(chunk_rows, dtype=np.int64)
+    P, C, KC = cr.shape
+    d = np.asarray(delays, dtype=np.int64)
+    slot = np.zeros((P, C, KC), dtype=np.int64)
+    pubs = np.zeros((P, C, KC), dtype=np.int64)
+    mem = {}
+    events = sorted(((int(d[p, c, k]), p, c, k) for p in range(P) for c in range(C)
+                     for k in range(KC) if cr[p, c, k] > 0))
+    for (_, p, c, k) in events:
+        n = int(cr[p, c, k])
+        per = [len(range(w, n, waves)) for w in range(waves)]
+        total = 0
+        for w in range(waves):
+            for r in range(w, n, waves):
+                mem[(c, p, k, r)] = stress_payload(t, p, c, k, r, C, KC)
+            if per[w] == 0:
+                continue
+            old = total
+            total += per[w]
+            if old + per[w] == n:
+                slot[p, c, k] = t
+                pubs[p, c, k] += 1
+    stale = 0
+    for p in range(P):
+        for c in range(C):
+            for k in range(KC):
+                if slot[p, c, k] >= t:
+                    for r in range(int(cr[p, c, k])):
+                        stale += mem.get((c, p, k, r)) != stress_payload(t, p, c, k, r, C, KC)
+    return dict(slot=slot, pubs=pubs, stale=stale)
+
+
+# ---------------------------------------------------------------------------
+# Slot barrier (PCIe sync protocols §2: every rank owns one slot on every rank)
+# ---------------------------------------------------------------------------
+
+def barrier_expected(n_ranks: int, rounds: int) -> np.ndarray:
+    """After ``rounds`` barriers: bslot[j][i] = rounds for every rank pair."""
+    return np.full((n_ranks, n_ranks), rounds, dtype=np.int64)
+
+
+def barrier_simulate(n_ranks: int, rounds: int, order_seed: int = 0) -> np.ndarray:
+    """Ranks run rounds with a random interleaving of their slot stores; rank i
+    leaves round b only when every bslot[i][j] >= b. Returns the final slots."""
+    rng = np.random.default_rng(order_seed)
+    bslot = np.zeros((n_ranks, n_ranks), dtype=np.int64)
+    rnd = [1] * n_ranks          # round each rank is in
+    stored = [False] * n_ranks
+    while min(rnd) <= rounds:
+        i = int(rng.integers(n_ranks))
+        b = rnd[i]
+        if b > rounds:
+            continue
+        if not stored[i]:
+            for j in range(n_ranks):     # signal: my slot on every rank
+                bslot[j][i] = b
+            stored[i] = True
+        elif all(bslot[i][j] >= b for j in range(n_ranks)):
+            rnd[i] = b + 1
+            stored[i] = False
+    return bslot
+
+
+# ---------------------------------------------------------------------------
+# Measurement formulas (Know your platform §5)
+# ---------------------------------------------------------------------------
+
+def overlap_efficiency(t_comp: float, t_comm: float, t_total: float) -> float:
+    """(T_comp + T_comm - T_total) / min(T_comp, T_comm); target >= 0.8."""
+    return (t_comp + t_comm - t_total) / min(t_comp, t_comm)
+
+
+def compute_interference(t_comp_fused: float, t_comp_alone: float) -> float:
+    """T_comp measured inside the fused run over T_comp alone; target <= 1.1."""
+    return t_comp_fused / t_comp_alone
