@@ -1,0 +1,226 @@
+/*
+ * fg.h -- C ABI of the fused producer/consumer gather-GEMM for AMD MI355X (gfx950).
+ *
+ * One persistent HIP kernel: communication workgroups move rows from N source
+ * shards (separate HBM regions standing in for peer ranks) into a gathered
+ * buffer, optionally scattered by a routing index, and signal completion;
+ * compute workgroups spin-gate on the signals and run the bf16 contraction with
+ * fp32 accumulation.
+ *
+ * Pages this interface follows (titles abbreviated):
+ *   "PCIe sync protocols" -- compute-comm fused operators (4): cross-card sync
+ *       protocols over PCIe: single writer, election, watermark.
+ *       §1 the problem (how A tells B its data is written), §2 slot + monotonic
+ *       seq and the all-rank barrier, §3 local election + single-writer
+ *       publish, §4 64-row chunk watermark, §5 seeded 128-row arrival counters
+ *       gating the GEMM, §6 residency/deadlock audit, §7 isolated debug entries
+ *       and host-recomputed expectation tables.
+ *   "NVLink atomic publish" -- §3.1 control plane separate from data and
+ *       aligned, §5.2 one publish wrapper, §7 a hidden observation counter and
+ *       packaging as a small primitive library.
+ *   "Know your platform" -- §5 the three timings and overlap efficiency.
+ *   "DeepEP FIFO pipeline" -- dispatch "notify" stage (per-expert counts fix
+ *       offsets), bounded spins with timeouts.
+ *
+ * Conventions for every entry point:
+ *   - Pointers documented "device" are HIP device pointers owned by the caller
+ *     unless stated otherwise; "host" pointers are ordinary host memory.
+ *   - bf16 data are 16-bit bit patterns (uint16), rows contiguous (row-major).
+ *   - Every call returns an fg_status; nothing is thrown and nothing aborts.
+ *   - Launches are asynchronous on the given stream. A device-side failure
+ *     (a wait that timed out, a counter that overshot) is recorded in the
+ *     context and reported by the next call on it; the context then answers
+ *     FG_ESTATE to everything but fg_stats and fg_destroy.
+ *   - A context is bound to the first stream it is used with; work on a
+ *     different stream returns FG_EINVAL (the parity re-arming of the control
+ *     plane relies on stream order between consecutive calls).
+ */
+#ifndef FG_H
+#define FG_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FG_CHUNK_ROWS 64    /* "PCIe sync protocols" §4: one signal per 64 rows of a producer stream */
+#define FG_ROW_BLOCK 128    /* "PCIe sync protocols" §5: the GEMM gate releases 128 gathered rows */
+#define FG_MAX_SHARDS 64
+#define FG_MAX_GROUPS 64
+
+typedef enum {
+  FG_OK = 0,
+  FG_EINVAL = -1,      /* bad argument, shape or stream */
+  FG_ENOMEM = -2,      /* device or pinned allocation failed (fg_init only) */
+  FG_EHIP = -3,        /* a HIP runtime call failed */
+  FG_ERESIDENCY = -4,  /* the persistent grid would not be co-resident (deadlock risk) */
+  FG_ETIMEOUT = -5,    /* a device-side wait hit its watchdog */
+  FG_EPROTOCOL = -6,   /* a counter overshot its target / duplicate route row */
+  FG_ESTATE = -7       /* context carries an earlier device-side error */
+} fg_status;
+
+/* Per-call flags of fg_gather_gemm. */
+enum {
+  FG_CALL_COMM_ONLY = 1u << 0,  /* communication role only (T_comm alone) */
+  FG_CALL_GEMM_ONLY = 1u << 1,  /* compute role only, gates pre-opened, gathered pre-filled (T_comp alone) */
+  FG_CALL_VERIFY = 1u << 2,     /* count publishes per slot, polls and waits (observation counters) */
+  FG_CALL_STRICT = 1u << 3,     /* formal agent-scope release fences on every signal (slow reference mode) */
+  FG_CALL_SAME_ROUTE = 1u << 4, /* EXPLICIT/TOPK: route identical to the previous call, skip the layout step */
+  /* Fault injection (tests). Each makes a bounded wait or a check fail so that
+   * the error path is exercised; every kernel still runs to completion. */
+  FG_FAULT_SEED_LOW = 1u << 8,      /* seed of row block 0 one too low: its gate never opens -> FG_ETIMEOUT */
+  FG_FAULT_SEED_HIGH = 1u << 9,     /* seed of row block 0 one too high: counter overshoots -> FG_EPROTOCOL */
+  FG_FAULT_DROP_PUBLISH = 1u << 10  /* elected publisher of chunk (0,0) skips its slot store */
+};
+
+typedef struct {
+  int32_t n_shards;            /* source shards = virtual ranks, 1..FG_MAX_SHARDS */
+  int32_t max_rows_per_shard;  /* capacity of one shard's stream (rows) */
+  int32_t K;                   /* row width in bf16 elements; multiple of 128 */
+  int32_t N;                   /* GEMM output width; multiple of 128 */
+  int32_t n_groups;            /* 1 = one dense weight; >1 = one weight per group (expert) */
+  int32_t n_comm_wg;           /* communication workgroups (0 = default 16) */
+  int32_t n_gemm_wg;           /* compute workgroups (0 = CUs - n_comm_wg) */
+  int32_t tile_n;              /* GEMM tile width 128 or 256 (0 = default) */
+  int64_t timeout_ns;          /* watchdog of every device-side wait (0 = 2 s) */
+  int32_t stress_producers;    /* protocol-stress plane (0 = none): producers x consumers x chunks slots */
+  int32_t stress_consumers;
+  int32_t stress_max_chunks;
+  int32_t reserved;
+} fg_config;
+
+typedef enum {
+  FG_ROUTE_CONTIG = 0,   /* all-gather: shard s row i -> gathered row s*rows_per_shard + i */
+  FG_ROUTE_EXPLICIT = 1, /* caller-given stream (src_row, dst_row) per shard */
+  FG_ROUTE_TOPK = 2      /* expert dispatch: layout computed on the device from top-k choices */
+} fg_route_mode;
+
+typedef struct {
+  int32_t mode;               /* fg_route_mode */
+  int32_t rows_per_shard;     /* CONTIG: rows of every shard; TOPK: tokens of every shard */
+  /* EXPLICIT */
+  const int32_t* stream_len;  /* host  [n_shards] stream length of each shard */
+  const int32_t* src_row;     /* device [n_shards][max_rows_per_shard]: source row of stream entry i */
+  const int32_t* dst_row;     /* device [n_shards][max_rows_per_shard]: gathered row of stream entry i */
+  int32_t m_pad;              /* gathered rows, a multiple of FG_ROW_BLOCK */
+  const int32_t* group_off;   /* host [n_groups+1] first gathered row of each group (NULL: one group) */
+  /* TOPK */
+  const int32_t* topk;        /* device [n_shards][rows_per_shard][topk_k] chosen experts, distinct per token */
+  int32_t topk_k;
+  int32_t expert_base;        /* this GPU owns experts [expert_base, expert_base + n_groups) */
+} fg_route;
+
+typedef struct fg_ctx fg_ctx;
+
+typedef struct {
+  int32_t seq, bseq, stress_seq;  /* last sequence numbers issued (monotonic, never reset) */
+  int32_t m_pad;                  /* gathered rows of the last gather-GEMM (device-computed for TOPK) */
+  int32_t error_code, error_id;   /* first device-side error and the wait/slot it concerns */
+  int64_t publishes;              /* VERIFY: slot stores by elected publishers, cumulative */
+  int64_t gate_polls, slot_polls; /* VERIFY: relaxed polls issued by waiters, cumulative */
+  int64_t gate_passes;            /* VERIFY: gates passed by compute workgroups, cumulative */
+  int64_t stale;                  /* stress: rows read with a value other than the expected one */
+  double t_kernel_us;             /* last fused kernel: first start to last end (device clock) */
+  double t_comm_span_us;          /* last fused kernel: communication role span */
+  double t_gemm_span_us;          /* last fused kernel: compute role span */
+  double t_gemm_busy_us;          /* mean over compute WGs of (span - time spent waiting at gates) */
+  double t_gate_wait_us;          /* mean over compute WGs of time spent waiting at gates */
+  double t_barrier_us;            /* last fg_barrier: device time per barrier */
+  double t_rtt_us;                /* last fg_pingpong: device round trip */
+  int32_t n_comm_wg, n_gemm_wg, cu_count, m_pad_cap;
+} fg_stats_t;
+
+/* Read-only device views of the library-owned control plane (for tests that
+ * compare it element by element with the host-recomputed table). */
+typedef struct {
+  const int32_t* slot;        /* [n_shards][chunk_cap] */
+  const int32_t* counter;     /* [2][rb_cap] parity double-buffered */
+  const int32_t* elect;       /* [2][n_shards][chunk_cap] */
+  const int32_t* pub_count;   /* [n_shards][chunk_cap] (VERIFY) */
+  const int32_t* seed;        /* [rb_cap] */
+  const int32_t* inv_row;     /* [m_pad_cap] (shard << 24 | stream index) or -1 for padding */
+  const int32_t* group_of_rb; /* [rb_cap] */
+  const int32_t* src_row;     /* [n_shards][max_rows_per_shard] route in use */
+  const int32_t* dst_row;     /* [n_shards][max_rows_per_shard] */
+  const int32_t* stream_len;  /* [n_shards] */
+  const int32_t* group_off;   /* [n_groups + 1] */
+  const int32_t* bslot;       /* [n_shards][n_shards] barrier slots */
+  const int32_t* stress_slot; /* [P][C][KC] */
+  const int32_t* stress_pub;  /* [P][C][KC] */
+  int32_t chunk_cap, rb_cap, m_pad_cap;
+} fg_views_t;
+
+/* Create a context on `hip_device`: validates the configuration, allocates and
+ * zeroes the control plane (slots, counters x2, election counts x2, publisher
+ * counts, route tables, barrier slots, host-visible status word) and checks
+ * that the persistent grid is co-resident and that fewer workgroups spin than
+ * there are compute units ("PCIe sync protocols" §6 audit items 1 and 2).
+ * Returns FG_EINVAL, FG_ENOMEM, FG_EHIP or FG_ERESIDENCY on failure (*out = NULL). */
+fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out);
+
+/* One iteration of the hot path ("PCIe sync protocols" §3-§5): seq = ++seq;
+ * layout step (TOPK/EXPLICIT, unless FG_CALL_SAME_ROUTE); then one persistent
+ * kernel in which communication workgroups copy every stream row
+ * shards[s][src_row] -> gathered[dst_row] bitwise (device-coherent 16-byte
+ * stores), add arrivals to the 128-row counters (seeded with the padding
+ * count), elect the last writer of each 64-row chunk, which stores seq into the
+ * chunk's single-writer slot; compute workgroups wait for each 128-row block's
+ * counter to equal 128 and compute out[m][n] = sum_k gathered[m][k] * W_g(m)[k][n]
+ * (fp32 accumulation, bf16 round-to-nearest-even output; padding rows = 0).
+ *   shards:   host array of n_shards device pointers, bf16 [rows, K]
+ *   route:    NULL = CONTIG with rows_per_shard = max_rows_per_shard
+ *   W:        device bf16 [n_groups][N][K]: W_g[k][n] stored at W[g][n][k]
+ *   gathered: device bf16 [m_pad_cap][K] (written; padding rows never written)
+ *   out:      device bf16 [m_pad_cap][N]
+ *   flags:    FG_CALL_* / FG_FAULT_*
+ * Errors: FG_EINVAL (shapes, NULLs, stream), FG_ESTATE, FG_ETIMEOUT /
+ * FG_EPROTOCOL from an earlier call, FG_EHIP. */
+fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route* route,
+                         const void* W, void* gathered, void* out, uint32_t flags,
+                         hipStream_t stream);
+
+/* `rounds` consecutive all-rank barriers over n_shards virtual ranks in one
+ * kernel ("PCIe sync protocols" §2): rank i's lane j stores bseq into
+ * bslot[j][i] (its own slot on every rank), then waits until
+ * bslot[i][0..n) >= bseq. bseq advances by `rounds` (1..1e6). */
+fg_status fg_barrier(fg_ctx* ctx, int32_t rounds, hipStream_t stream);
+
+/* Slot ping-pong between two workgroups on different XCDs, `round_trips`
+ * round trips in one kernel; the mean round trip lands in fg_stats.t_rtt_us.
+ * sys_scope != 0 uses system-scope slot stores and polls. */
+fg_status fg_pingpong(fg_ctx* ctx, int32_t round_trips, int32_t sys_scope, hipStream_t stream);
+
+/* One iteration of the protocol-stress workload ("PCIe sync protocols" §3-§4
+ * at the scale of §3's validation): producer workgroup p, after waiting
+ * delays_ns[p][c][k], writes chunk_rows[p][c][k] 4-byte rows of payload
+ * ((seq << 20) ^ (((p*C + c)*KC + k)*64 + r)) into payload[c][p][k][r]; its waves
+ * elect one publisher per chunk, which stores seq into slot (p,c,k); consumer
+ * workgroup c waits for every active slot addressed to it and checks every
+ * row, counting mismatches in fg_stats.stale.
+ *   chunk_rows: device int32 [P][C][KC] (0 = inactive, else 1..64)
+ *   delays_ns:  device int32 [P][C][KC]
+ *   payload:    device int32 [C][P][KC][64]
+ *   flags:      FG_CALL_STRICT / FG_FAULT_DROP_PUBLISH */
+fg_status fg_stress(fg_ctx* ctx, const int32_t* chunk_rows, const int32_t* delays_ns,
+                    int32_t* payload, uint32_t flags, hipStream_t stream);
+
+/* Copy the observation counters to *out. wait != 0 first synchronises the
+ * bound stream (needed for device-computed fields and timings). */
+fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait);
+
+/* Device pointers of the control plane (valid until fg_destroy). */
+fg_status fg_views(fg_ctx* ctx, fg_views_t* out);
+
+/* Minimum number of gathered / output rows the caller must allocate. */
+fg_status fg_capacity(const fg_config* cfg, int32_t* m_pad_cap);
+
+fg_status fg_destroy(fg_ctx* ctx);
+const char* fg_strerror(fg_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FG_H */

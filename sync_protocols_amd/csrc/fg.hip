@@ -1,0 +1,520 @@
+// Host implementation of the fg C ABI (include/fg.h) for gfx950.
+//
+// The context owns only the control plane ("NVLink atomic publish" §3.1: control
+// separate from data, each array on its own 256-byte boundary): slots, the two
+// parities of arrival counters and election counts, publisher counts, route
+// tables, barrier slots, statistics, and one host-visible status word. All data
+// buffers (shards, weights, gathered rows, outputs, routes) belong to the caller.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "fg_kernels.hpp"
+
+using namespace fg;
+
+namespace {
+
+constexpr int kDefaultComm = 16;
+constexpr int64_t kDefaultTimeoutNs = 2000000000LL;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Plane {
+  int* slot;
+  int* counter;    // [2][rb_cap]
+  int* elect;      // [2][S * chunk_cap]
+  int* pub_count;
+  int* seed;
+  int* inv;
+  int* group_of_rb;
+  int* src_row;
+  int* dst_row;
+  int* stream_len;
+  int* group_off;
+  int* rbcount;
+  int* desc;
+  int* err;        // [2]
+  unsigned long long* stats;
+  int* bslot;
+  int* pp;         // ping-pong slots (two, 256 bytes apart)
+  long long* tdev; // [4] barrier / ping-pong timings
+  long long* wgtime;
+  int* s_slot;
+  int* s_elect;    // [2][P*C*KC]
+  int* s_pub;
+};
+
+}  // namespace
+
+struct fg_ctx {
+  fg_config cfg;
+  int device = 0;
+  int cu_count = 0;
+  int chunk_cap = 0, rb_cap = 0, m_pad_cap = 0, s_slots = 0;
+  int n_comm = 0, n_gemm = 0, tile_n = 256;
+  int64_t wall_khz = 100000;
+  char* plane_mem = nullptr;
+  Plane p{};
+  int* host_status = nullptr;
+  int seq = 0, bseq = 0, sseq = 0, ppseq = 0;
+  fg_status sticky = FG_OK;
+  bool stream_bound = false;
+  hipStream_t stream = nullptr;
+  // cached CONTIG route (so that repeated all-gathers skip the layout step)
+  int route_cached_mode = -1;
+  int route_cached_rows = -1;
+  int last_grid = 0;
+  int last_m_pad = 0;
+  int last_bm = 0;
+  unsigned long long host_stats[ST_COUNT] = {};
+};
+
+#define HIPCHK(x)                                   \
+  do {                                              \
+    hipError_t e_ = (x);                            \
+    if (e_ != hipSuccess) return FG_EHIP;           \
+  } while (0)
+
+static int round_up(int x, int b) { return (x + b - 1) / b * b; }
+
+static int m_pad_capacity(const fg_config& c) {
+  const long long m = (long long)c.n_shards * c.max_rows_per_shard;
+  long long cap = (long long)round_up((int)std::min<long long>(m, 1 << 30), FG_ROW_BLOCK);
+  if (c.n_groups > 1) cap = round_up((int)(m + (long long)c.n_groups * (FG_ROW_BLOCK - 1)), FG_ROW_BLOCK);
+  return (int)cap;
+}
+
+static bool config_ok(const fg_config* c) {
+  if (!c) return false;
+  if (c->n_shards < 1 || c->n_shards > FG_MAX_SHARDS) return false;
+  if (c->max_rows_per_shard < 1 || c->max_rows_per_shard > (1 << 24) - 1) return false;
+  if (c->K < 128 || c->K % 128 != 0) return false;
+  if (c->N < 128 || c->N % 128 != 0) return false;
+  if (c->n_groups < 1 || c->n_groups > FG_MAX_GROUPS) return false;
+  if (c->tile_n != 0 && c->tile_n != 128 && c->tile_n != 256) return false;
+  if (c->tile_n == 256 && c->N % 256 != 0) return false;
+  if (c->n_comm_wg < 0 || c->n_gemm_wg < 0) return false;
+  if (c->timeout_ns < 0) return false;
+  if (c->stress_producers < 0 || c->stress_consumers < 0 || c->stress_max_chunks < 0) return false;
+  const long long m = (long long)c->n_shards * c->max_rows_per_shard + (long long)c->n_groups * FG_ROW_BLOCK;
+  if (m * c->K * 2 >= (1ll << 32)) return false;   // 32-bit buffer offsets
+  if (m * c->N * 2 >= (1ll << 32)) return false;
+  if ((long long)c->N * c->K * 2 >= (1ll << 32)) return false;
+  return true;
+}
+
+template <int BM, int BN>
+static hipError_t occupancy(int* per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, fused_kernel<BM, BN>, kThreads, 0);
+}
+
+static fg_status map_device_error(int code) {
+  if (code == kErrTimeout) return FG_ETIMEOUT;
+  if (code == kErrProtocol) return FG_EPROTOCOL;
+  return code ? FG_EPROTOCOL : FG_OK;
+}
+
+// A device-side error recorded by an earlier launch becomes sticky here.
+static fg_status check_sticky(fg_ctx* ctx) {
+  if (ctx->sticky != FG_OK) return FG_ESTATE;
+  const int code = __atomic_load_n(ctx->host_status, __ATOMIC_ACQUIRE);
+  if (code != 0) {
+    ctx->sticky = map_device_error(code);
+    return ctx->sticky;
+  }
+  return FG_OK;
+}
+
+static fg_status bind_stream(fg_ctx* ctx, hipStream_t s) {
+  if (!ctx->stream_bound) {
+    ctx->stream = s;
+    ctx->stream_bound = true;
+    return FG_OK;
+  }
+  return ctx->stream == s ? FG_OK : FG_EINVAL;
+}
+
+static ErrorSink sink(fg_ctx* ctx) { return ErrorSink{ctx->p.err, ctx->host_status}; }
+
+static uint64_t timeout_ticks(const fg_ctx* ctx) {
+  const int64_t ns = ctx->cfg.timeout_ns ? ctx->cfg.timeout_ns : kDefaultTimeoutNs;
+  return (uint64_t)(ns / 1000000.0 * ctx->wall_khz);
+}
+
+static fg_status launch_route(fg_ctx* ctx, const fg_route* route, int mode, int rows, int m_pad, hipStream_t st) {
+  RouteArgs ra{};
+  const fg_config& c = ctx->cfg;
+  ra.mode = mode;
+  ra.n_shards = c.n_shards; ra.rs_cap = c.max_rows_per_shard; ra.chunk_cap = ctx->chunk_cap;
+  ra.rb_cap = ctx->rb_cap; ra.m_pad_cap = ctx->m_pad_cap;
+  ra.rows_per_shard = rows; ra.m_pad = m_pad;
+  ra.n_groups = (mode == FG_ROUTE_CONTIG) ? 1 : c.n_groups;
+  if (mode == FG_ROUTE_EXPLICIT) {
+    for (int s = 0; s < c.n_shards; ++s) ra.stream_len_in[s] = route->stream_len[s];
+    if (route->group_off) {
+      for (int g = 0; g <= c.n_groups; ++g) ra.group_off[g] = route->group_off[g];
+    } else {
+      ra.n_groups = 1; ra.group_off[0] = 0; ra.group_off[1] = m_pad;
+    }
+    ra.src_in = route->src_row; ra.dst_in = route->dst_row;
+  }
+  if (mode == FG_ROUTE_TOPK) { ra.topk = route->topk; ra.topk_k = route->topk_k; ra.expert_base = route->expert_base; }
+  const int cur = ctx->seq & 1;
+  ra.src_row = ctx->p.src_row; ra.dst_row = ctx->p.dst_row; ra.stream_len = ctx->p.stream_len;
+  ra.group_off_out = ctx->p.group_off; ra.inv = ctx->p.inv; ra.seed = ctx->p.seed;
+  ra.group_of_rb = ctx->p.group_of_rb; ra.rbcount = ctx->p.rbcount;
+  ra.counter_cur = ctx->p.counter + (size_t)cur * ctx->rb_cap;
+  ra.elect_cur = ctx->p.elect + (size_t)cur * c.n_shards * ctx->chunk_cap;
+  ra.desc = ctx->p.desc; ra.err = sink(ctx);
+  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, st, ra);
+  HIPCHK(hipGetLastError());
+  return FG_OK;
+}
+
+template <int BM, int BN>
+static fg_status launch_fused(fg_ctx* ctx, const FusedArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((fused_kernel<BM, BN>), dim3(a.n_comm + a.n_gemm), dim3(kThreads), 0, st, a);
+  HIPCHK(hipGetLastError());
+  ctx->last_bm = BM;
+  return FG_OK;
+}
+
+extern "C" {
+
+const char* fg_strerror(fg_status s) {
+  switch (s) {
+    case FG_OK: return "ok";
+    case FG_EINVAL: return "invalid argument";
+    case FG_ENOMEM: return "out of memory";
+    case FG_EHIP: return "HIP runtime error";
+    case FG_ERESIDENCY: return "persistent grid not co-resident";
+    case FG_ETIMEOUT: return "device wait timed out";
+    case FG_EPROTOCOL: return "protocol violation (counter overshoot or bad route)";
+    case FG_ESTATE: return "context carries an earlier device-side error";
+  }
+  return "unknown";
+}
+
+fg_status fg_capacity(const fg_config* cfg, int32_t* m_pad_cap) {
+  if (!config_ok(cfg) || !m_pad_cap) return FG_EINVAL;
+  *m_pad_cap = m_pad_capacity(*cfg);
+  return FG_OK;
+}
+
+fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
+  if (!out) return FG_EINVAL;
+  *out = nullptr;
+  if (!config_ok(cfg)) return FG_EINVAL;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || hip_device < 0 || hip_device >= ndev) return FG_EINVAL;
+  HIPCHK(hipSetDevice(hip_device));
+  fg_ctx* ctx = new (std::nothrow) fg_ctx();
+  if (!ctx) return FG_ENOMEM;
+  ctx->cfg = *cfg;
+  ctx->device = hip_device;
+  int wall = 0;
+  if (hipDeviceGetAttribute(&ctx->cu_count, hipDeviceAttributeMultiprocessorCount, hip_device) != hipSuccess ||
+      hipDeviceGetAttribute(&wall, hipDeviceAttributeWallClockRate, hip_device) != hipSuccess) {
+    delete ctx;
+    return FG_EHIP;
+  }
+  if (wall > 0) ctx->wall_khz = wall;
+  ctx->n_comm = cfg->n_comm_wg ? cfg->n_comm_wg : kDefaultComm;
+  ctx->n_gemm = cfg->n_gemm_wg ? cfg->n_gemm_wg : ctx->cu_count - ctx->n_comm;
+  ctx->tile_n = cfg->tile_n ? cfg->tile_n : (cfg->N % 256 == 0 ? 256 : 128);
+  // "PCIe sync protocols" §6 audit: every spinning workgroup must leave room
+  // for the suppliers, and the whole persistent grid must be resident at once.
+  if (ctx->n_gemm < 1 || ctx->n_gemm >= ctx->cu_count || ctx->n_comm < 1) { delete ctx; return FG_ERESIDENCY; }
+  {
+    int per_cu = 0, worst = 1 << 30;
+    hipError_t e = hipSuccess;
+    if (ctx->tile_n == 256) {
+      e = occupancy<256, 256>(&per_cu); worst = std::min(worst, per_cu);
+      if (e == hipSuccess) { e = occupancy<128, 256>(&per_cu); worst = std::min(worst, per_cu); }
+    } else {
+      e = occupancy<256, 128>(&per_cu); worst = std::min(worst, per_cu);
+      if (e == hipSuccess) { e = occupancy<128, 128>(&per_cu); worst = std::min(worst, per_cu); }
+    }
+    if (e != hipSuccess) { delete ctx; return FG_EHIP; }
+    if ((long long)worst * ctx->cu_count < ctx->n_comm + ctx->n_gemm) { delete ctx; return FG_ERESIDENCY; }
+  }
+  if (cfg->stress_producers + cfg->stress_consumers > ctx->cu_count ||
+      cfg->stress_consumers >= ctx->cu_count) { delete ctx; return FG_ERESIDENCY; }
+  if (cfg->n_shards > ctx->cu_count) { delete ctx; return FG_ERESIDENCY; }
+
+  const int S = cfg->n_shards;
+  ctx->chunk_cap = (cfg->max_rows_per_shard + FG_CHUNK_ROWS - 1) / FG_CHUNK_ROWS;
+  ctx->m_pad_cap = m_pad_capacity(*cfg);
+  ctx->rb_cap = ctx->m_pad_cap / FG_ROW_BLOCK;
+  ctx->s_slots = cfg->stress_producers * cfg->stress_consumers * cfg->stress_max_chunks;
+  const int grid_max = ctx->n_comm + ctx->n_gemm;
+  const size_t nch = (size_t)S * ctx->chunk_cap;
+  const size_t nrs = (size_t)S * cfg->max_rows_per_shard;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  const size_t o_slot = take(nch * 4), o_counter = take(2 * (size_t)ctx->rb_cap * 4),
+               o_elect = take(2 * nch * 4), o_pub = take(nch * 4), o_seed = take((size_t)ctx->rb_cap * 4),
+               o_inv = take((size_t)ctx->m_pad_cap * 4), o_grp = take((size_t)ctx->rb_cap * 4),
+               o_src = take(nrs * 4), o_dst = take(nrs * 4), o_slen = take((size_t)S * 4),
+               o_goff = take((FG_MAX_GROUPS + 1) * 4), o_rbc = take((size_t)ctx->rb_cap * 4), o_desc = take(64),
+               o_err = take(64), o_stats = take(ST_COUNT * 8), o_bslot = take((size_t)S * S * 4),
+               o_pp = take(512), o_tdev = take(64), o_wg = take((size_t)grid_max * 32),
+               o_sslot = take((size_t)ctx->s_slots * 4), o_select = take(2 * (size_t)ctx->s_slots * 4),
+               o_spub = take((size_t)ctx->s_slots * 4);
+  if (hipMalloc(&ctx->plane_mem, off) != hipSuccess) { delete ctx; return FG_ENOMEM; }
+  if (hipMemset(ctx->plane_mem, 0, off) != hipSuccess) { (void)hipFree(ctx->plane_mem); delete ctx; return FG_EHIP; }
+  char* b = ctx->plane_mem;
+  Plane& p = ctx->p;
+  p.slot = (int*)(b + o_slot); p.counter = (int*)(b + o_counter); p.elect = (int*)(b + o_elect);
+  p.pub_count = (int*)(b + o_pub); p.seed = (int*)(b + o_seed); p.inv = (int*)(b + o_inv);
+  p.group_of_rb = (int*)(b + o_grp); p.src_row = (int*)(b + o_src); p.dst_row = (int*)(b + o_dst);
+  p.stream_len = (int*)(b + o_slen); p.group_off = (int*)(b + o_goff); p.rbcount = (int*)(b + o_rbc);
+  p.desc = (int*)(b + o_desc); p.err = (int*)(b + o_err); p.stats = (unsigned long long*)(b + o_stats);
+  p.bslot = (int*)(b + o_bslot); p.pp = (int*)(b + o_pp); p.tdev = (long long*)(b + o_tdev);
+  p.wgtime = (long long*)(b + o_wg); p.s_slot = (int*)(b + o_sslot); p.s_elect = (int*)(b + o_select);
+  p.s_pub = (int*)(b + o_spub);
+  if (hipHostMalloc((void**)&ctx->host_status, 64, hipHostMallocCoherent) != hipSuccess) {
+    (void)hipFree(ctx->plane_mem); delete ctx; return FG_ENOMEM;
+  }
+  memset(ctx->host_status, 0, 64);
+  if (hipDeviceSynchronize() != hipSuccess) { fg_destroy(ctx); return FG_EHIP; }
+  *out = ctx;
+  return FG_OK;
+}
+
+fg_status fg_destroy(fg_ctx* ctx) {
+  if (!ctx) return FG_EINVAL;
+  (void)hipSetDevice(ctx->device);
+  if (ctx->stream_bound) (void)hipStreamSynchronize(ctx->stream);
+  if (ctx->plane_mem) (void)hipFree(ctx->plane_mem);
+  if (ctx->host_status) (void)hipHostFree(ctx->host_status);
+  delete ctx;
+  return FG_OK;
+}
+
+fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route* route, const void* W,
+                         void* gathered, void* out, uint32_t flags, hipStream_t stream) {
+  if (!ctx) return FG_EINVAL;
+  fg_status s = check_sticky(ctx);
+  if (s != FG_OK) return s;
+  const fg_config& c = ctx->cfg;
+  if (!shards || !W || !gathered || !out) return FG_EINVAL;
+  for (int i = 0; i < c.n_shards; ++i) if (!shards[i]) return FG_EINVAL;
+  if ((flags & FG_CALL_COMM_ONLY) && (flags & FG_CALL_GEMM_ONLY)) return FG_EINVAL;
+  const int mode = route ? route->mode : FG_ROUTE_CONTIG;
+  int rows = c.max_rows_per_shard, m_pad = 0;
+  if (mode == FG_ROUTE_CONTIG) {
+    if (route) rows = route->rows_per_shard;
+    if (rows < 1 || rows > c.max_rows_per_shard) return FG_EINVAL;
+    m_pad = round_up(c.n_shards * rows, FG_ROW_BLOCK);
+  } else if (mode == FG_ROUTE_EXPLICIT) {
+    if (!route->stream_len || !route->src_row || !route->dst_row) return FG_EINVAL;
+    rows = route->rows_per_shard;
+    if (rows < 1) return FG_EINVAL;
+    for (int i = 0; i < c.n_shards; ++i)
+      if (route->stream_len[i] < 0 || route->stream_len[i] > c.max_rows_per_shard) return FG_EINVAL;
+    m_pad = route->m_pad;
+    if (m_pad < FG_ROW_BLOCK || m_pad % FG_ROW_BLOCK || m_pad > ctx->m_pad_cap) return FG_EINVAL;
+    if (route->group_off) {
+      if (route->group_off[0] != 0 || route->group_off[c.n_groups] != m_pad) return FG_EINVAL;
+      for (int g = 0; g < c.n_groups; ++g)
+        if (route->group_off[g + 1] < route->group_off[g] || route->group_off[g + 1] % FG_ROW_BLOCK) return FG_EINVAL;
+    } else if (c.n_groups != 1) {
+      return FG_EINVAL;
+    }
+  } else if (mode == FG_ROUTE_TOPK) {
+    if (!route->topk || route->topk_k < 1 || route->topk_k > 64) return FG_EINVAL;
+    rows = route->rows_per_shard;
+    if (rows < 1 || (long long)rows * c.n_shards > (1 << 20)) return FG_EINVAL;
+    if (c.n_groups < 1) return FG_EINVAL;
+  } else {
+    return FG_EINVAL;
+  }
+  if (bind_stream(ctx, stream) != FG_OK) return FG_EINVAL;
+  HIPCHK(hipSetDevice(ctx->device));
+
+  ctx->seq += 1;
+  const int cur = ctx->seq & 1, nxt = cur ^ 1;
+  const bool same = flags & FG_CALL_SAME_ROUTE;
+  if (mode == FG_ROUTE_CONTIG) {
+    if (ctx->route_cached_mode != FG_ROUTE_CONTIG || ctx->route_cached_rows != rows) {
+      if ((s = launch_route(ctx, route, mode, rows, m_pad, stream)) != FG_OK) return s;
+      ctx->route_cached_mode = FG_ROUTE_CONTIG;
+      ctx->route_cached_rows = rows;
+    }
+  } else {
+    if (!same || ctx->route_cached_mode != mode) {
+      if ((s = launch_route(ctx, route, mode, rows, m_pad, stream)) != FG_OK) return s;
+    }
+    ctx->route_cached_mode = mode;
+    ctx->route_cached_rows = rows;
+  }
+  int* counter_cur = ctx->p.counter + (size_t)cur * ctx->rb_cap;
+  if (flags & (FG_FAULT_SEED_LOW | FG_FAULT_SEED_HIGH)) {
+    hipLaunchKernelGGL(poke_kernel, dim3(1), dim3(64), 0, stream, counter_cur, (flags & FG_FAULT_SEED_HIGH) ? 1 : -1);
+    HIPCHK(hipGetLastError());
+  }
+  if (flags & FG_CALL_GEMM_ONLY) {
+    hipLaunchKernelGGL(fill_kernel, dim3(std::max(1, std::min(64, ctx->rb_cap / 256 + 1))), dim3(256), 0, stream,
+                       counter_cur, ctx->rb_cap, FG_ROW_BLOCK);
+    HIPCHK(hipGetLastError());
+  }
+  FusedArgs a{};
+  for (int i = 0; i < c.n_shards; ++i) a.shards[i] = (const uint16_t*)shards[i];
+  a.W = (const uint16_t*)W; a.gathered = (uint16_t*)gathered; a.out = (uint16_t*)out;
+  a.K = c.K; a.N = c.N; a.n_shards = c.n_shards; a.chunk_cap = ctx->chunk_cap; a.rs_cap = c.max_rows_per_shard;
+  a.rb_cap = ctx->rb_cap; a.m_pad_cap = ctx->m_pad_cap;
+  a.shard_rows = rows;
+  a.slot = ctx->p.slot;
+  a.counter_cur = counter_cur;
+  a.counter_nxt = ctx->p.counter + (size_t)nxt * ctx->rb_cap;
+  a.elect_cur = ctx->p.elect + (size_t)cur * c.n_shards * ctx->chunk_cap;
+  a.elect_nxt = ctx->p.elect + (size_t)nxt * c.n_shards * ctx->chunk_cap;
+  a.pub_count = ctx->p.pub_count; a.seed = ctx->p.seed; a.inv = ctx->p.inv; a.group_of_rb = ctx->p.group_of_rb;
+  a.src_row = ctx->p.src_row; a.stream_len = ctx->p.stream_len; a.desc = ctx->p.desc; a.stats = ctx->p.stats;
+  a.wgtime = ctx->p.wgtime; a.err = sink(ctx); a.seq = ctx->seq;
+  a.n_comm = ctx->n_comm; a.n_gemm = ctx->n_gemm;
+  int rpb = 32768 / (c.K * 2);
+  rpb = std::max(1, std::min(16, rpb));
+  while (FG_ROW_BLOCK % rpb) --rpb;
+  a.rows_per_batch = rpb;
+  a.flags = flags;
+  a.timeout_ticks = timeout_ticks(ctx);
+  ctx->last_grid = a.n_comm + a.n_gemm;
+  ctx->last_m_pad = m_pad;
+  const bool bm256 = (mode != FG_ROUTE_TOPK) && (m_pad % 256 == 0) &&
+                     !(mode == FG_ROUTE_EXPLICIT && route->group_off && c.n_groups > 1);
+  if (ctx->tile_n == 256) {
+    s = bm256 ? launch_fused<256, 256>(ctx, a, stream) : launch_fused<128, 256>(ctx, a, stream);
+  } else {
+    s = bm256 ? launch_fused<256, 128>(ctx, a, stream) : launch_fused<128, 128>(ctx, a, stream);
+  }
+  return s;
+}
+
+fg_status fg_barrier(fg_ctx* ctx, int32_t rounds, hipStream_t stream) {
+  if (!ctx || rounds < 1 || rounds > 1000000) return FG_EINVAL;
+  fg_status s = check_sticky(ctx);
+  if (s != FG_OK) return s;
+  if (bind_stream(ctx, stream) != FG_OK) return FG_EINVAL;
+  HIPCHK(hipSetDevice(ctx->device));
+  const int n = ctx->cfg.n_shards;
+  hipLaunchKernelGGL(barrier_kernel, dim3(n), dim3(64), 0, stream, ctx->p.bslot, n, ctx->bseq, rounds, sink(ctx),
+                     timeout_ticks(ctx), ctx->p.tdev);
+  HIPCHK(hipGetLastError());
+  ctx->bseq += rounds;
+  ctx->host_stats[0] = (unsigned long long)rounds;
+  return FG_OK;
+}
+
+fg_status fg_pingpong(fg_ctx* ctx, int32_t round_trips, int32_t sys_scope, hipStream_t stream) {
+  if (!ctx || round_trips < 1 || round_trips > 10000000) return FG_EINVAL;
+  fg_status s = check_sticky(ctx);
+  if (s != FG_OK) return s;
+  if (bind_stream(ctx, stream) != FG_OK) return FG_EINVAL;
+  HIPCHK(hipSetDevice(ctx->device));
+  int* a = ctx->p.pp;
+  int* b = ctx->p.pp + 64;
+  if (sys_scope)
+    hipLaunchKernelGGL(pingpong_kernel<1>, dim3(2), dim3(64), 0, stream, a, b, ctx->ppseq, round_trips, sink(ctx),
+                       timeout_ticks(ctx), ctx->p.tdev + 1);
+  else
+    hipLaunchKernelGGL(pingpong_kernel<0>, dim3(2), dim3(64), 0, stream, a, b, ctx->ppseq, round_trips, sink(ctx),
+                       timeout_ticks(ctx), ctx->p.tdev + 1);
+  HIPCHK(hipGetLastError());
+  ctx->ppseq += round_trips;
+  ctx->host_stats[1] = (unsigned long long)round_trips;
+  return FG_OK;
+}
+
+fg_status fg_stress(fg_ctx* ctx, const int32_t* chunk_rows, const int32_t* delays_ns, int32_t* payload,
+                    uint32_t flags, hipStream_t stream) {
+  if (!ctx || !chunk_rows || !delays_ns || !payload) return FG_EINVAL;
+  if (ctx->s_slots == 0) return FG_EINVAL;
+  fg_status s = check_sticky(ctx);
+  if (s != FG_OK) return s;
+  if (bind_stream(ctx, stream) != FG_OK) return FG_EINVAL;
+  HIPCHK(hipSetDevice(ctx->device));
+  ctx->sseq += 1;
+  const int cur = ctx->sseq & 1;
+  StressArgs a{};
+  a.chunk_rows = chunk_rows; a.delays_ns = delays_ns; a.payload = payload;
+  a.slot = ctx->p.s_slot;
+  a.elect_cur = ctx->p.s_elect + (size_t)cur * ctx->s_slots;
+  a.elect_nxt = ctx->p.s_elect + (size_t)(cur ^ 1) * ctx->s_slots;
+  a.pub = ctx->p.s_pub; a.stats = ctx->p.stats; a.err = sink(ctx);
+  a.P = ctx->cfg.stress_producers; a.C = ctx->cfg.stress_consumers; a.KC = ctx->cfg.stress_max_chunks;
+  a.seq = ctx->sseq; a.flags = flags; a.timeout_ticks = timeout_ticks(ctx);
+  a.payload_bytes = (uint32_t)((size_t)ctx->s_slots * FG_CHUNK_ROWS * 4);
+  hipLaunchKernelGGL(stress_kernel, dim3(a.P + a.C), dim3(kThreads), 0, stream, a);
+  HIPCHK(hipGetLastError());
+  return FG_OK;
+}
+
+fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait) {
+  if (!ctx || !out) return FG_EINVAL;
+  HIPCHK(hipSetDevice(ctx->device));
+  if (wait && ctx->stream_bound) HIPCHK(hipStreamSynchronize(ctx->stream));
+  memset(out, 0, sizeof(*out));
+  out->seq = ctx->seq; out->bseq = ctx->bseq; out->stress_seq = ctx->sseq;
+  out->n_comm_wg = ctx->n_comm; out->n_gemm_wg = ctx->n_gemm; out->cu_count = ctx->cu_count;
+  out->m_pad_cap = ctx->m_pad_cap;
+  if (!wait) { out->m_pad = ctx->last_m_pad; return FG_OK; }
+  int err[2] = {0, 0}, desc = 0;
+  unsigned long long st[ST_COUNT];
+  long long td[4];
+  HIPCHK(hipMemcpy(err, ctx->p.err, 8, hipMemcpyDeviceToHost));
+  HIPCHK(hipMemcpy(&desc, ctx->p.desc, 4, hipMemcpyDeviceToHost));
+  HIPCHK(hipMemcpy(st, ctx->p.stats, sizeof(st), hipMemcpyDeviceToHost));
+  HIPCHK(hipMemcpy(td, ctx->p.tdev, sizeof(td), hipMemcpyDeviceToHost));
+  out->error_code = err[0]; out->error_id = err[1];
+  out->m_pad = desc;
+  out->publishes = (int64_t)st[ST_PUBLISHES]; out->gate_polls = (int64_t)st[ST_GATE_POLLS];
+  out->slot_polls = (int64_t)st[ST_SLOT_POLLS]; out->gate_passes = (int64_t)st[ST_GATE_PASSES];
+  out->stale = (int64_t)st[ST_STALE];
+  const double us_per_tick = 1000.0 / (double)ctx->wall_khz;
+  if (ctx->host_stats[0]) out->t_barrier_us = td[0] * us_per_tick / (double)ctx->host_stats[0];
+  if (ctx->host_stats[1]) out->t_rtt_us = td[1] * us_per_tick / (double)ctx->host_stats[1];
+  if (ctx->last_grid) {
+    const int g = ctx->last_grid;
+    long long* wg = new (std::nothrow) long long[(size_t)g * 4];
+    if (!wg) return FG_ENOMEM;
+    if (hipMemcpy(wg, ctx->p.wgtime, (size_t)g * 32, hipMemcpyDeviceToHost) != hipSuccess) { delete[] wg; return FG_EHIP; }
+    long long t0 = wg[0], t1 = wg[1], c0 = wg[0], c1 = wg[1], g0 = 0, g1 = 0;
+    double busy = 0, waitt = 0;
+    int ng = 0;
+    for (int i = 0; i < g; ++i) {
+      const long long* t = wg + (size_t)i * 4;
+      t0 = std::min(t0, t[0]); t1 = std::max(t1, t[1]);
+      if (i < ctx->n_comm) { c0 = std::min(c0, t[0]); c1 = std::max(c1, t[1]); }
+      else {
+        if (ng == 0) { g0 = t[0]; g1 = t[1]; }
+        g0 = std::min(g0, t[0]); g1 = std::max(g1, t[1]);
+        busy += (double)(t[1] - t[0] - t[2]); waitt += (double)t[2]; ++ng;
+      }
+    }
+    out->t_kernel_us = (t1 - t0) * us_per_tick;
+    out->t_comm_span_us = (c1 - c0) * us_per_tick;
+    out->t_gemm_span_us = (g1 - g0) * us_per_tick;
+    if (ng) { out->t_gemm_busy_us = busy / ng * us_per_tick; out->t_gate_wait_us = waitt / ng * us_per_tick; }
+    delete[] wg;
+  }
+  return FG_OK;
+}
+
+fg_status fg_views(fg_ctx* ctx, fg_views_t* v) {
+  if (!ctx || !v) return FG_EINVAL;
+  const Plane& p = ctx->p;
+  v->slot = p.slot; v->counter = p.counter; v->elect = p.elect; v->pub_count = p.pub_count; v->seed = p.seed;
+  v->inv_row = p.inv; v->group_of_rb = p.group_of_rb; v->src_row = p.src_row; v->dst_row = p.dst_row;
+  v->stream_len = p.stream_len; v->group_off = p.group_off; v->bslot = p.bslot; v->stress_slot = p.s_slot;
+  v->stress_pub = p.s_pub;
+  v->chunk_cap = ctx->chunk_cap; v->rb_cap = ctx->rb_cap; v->m_pad_cap = ctx->m_pad_cap;
+  return FG_OK;
+}
+
+}  // extern "C"

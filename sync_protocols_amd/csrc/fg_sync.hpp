@@ -1,0 +1,166 @@
+// Device-side signal primitives for gfx950 (single-writer slots, monotonic
+// sequence numbers, seeded arrival counters, bounded waits).
+//
+// Basis: "PCIe sync protocols" (compute-comm fused operators, part 4) §2 (slot
+// publish / wait, monotonic never-reset seq), §3 (local election, memory-order
+// chain), §5 (arrival counter gate), §6 (every wait needs a supplier); "NVLink
+// atomic publish" §5.2 (one publish wrapper for every publish), §5.4 (few,
+// centralised, backed-off polls); "DeepEP FIFO pipeline" (bounded spin with a
+// timeout on every wait).
+//
+// Memory model on gfx950 (measured on the part, see the design notes):
+//  * every XCD has its own L2; a plain or non-temporal store can sit in the
+//    writer's L2 where another XCD does not see it;
+//  * a store issued with the device-scope cache policy (sc1) writes through to
+//    the device coherence point before it is acknowledged;
+//  * the compiler's agent-scope release fence writes back the whole L2
+//    (buffer_wbl2) and serialises across the chip: one per 8 KB caps a copy at
+//    about 0.4 TB/s, so it cannot sit on a per-batch path.
+// The default release used here is therefore: every data store of the window
+// is a device-scope (sc1) store, and the release waits until all of this wave's
+// vector memory operations are acknowledged (s_waitcnt vmcnt(0)); only then is
+// the signal written. That is exactly the effect the agent-scope release
+// provides for write-through stores, without the L2 write-back. The strict
+// variant (formal __builtin_amdgcn_fence release) is kept behind a flag and
+// gives bit-identical results. The acquire side always uses the formal
+// agent-scope acquire fence after a relaxed poll.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fg {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Cache-policy immediates of the gfx950 buffer instructions.
+constexpr int kPolSC0 = 1;
+constexpr int kPolNT = 2;
+constexpr int kPolSC1 = 16;
+constexpr int kPolCoherentStream = kPolSC1 | kPolNT;   // device-coherent, non-temporal
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16-byte device-coherent streaming store at byte offset `off` of the buffer.
+__device__ __forceinline__ void store16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off, v4i v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kPolCoherentStream);
+}
+
+// 16-byte non-temporal store (no cross-XCD visibility guarantee; outputs only).
+__device__ __forceinline__ void store16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off, v4i v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kPolNT);
+}
+
+__device__ __forceinline__ v4i load16_stream(const v4i* p) { return __builtin_nontemporal_load(p); }
+
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+// Release of this wave's earlier device-coherent stores (see the header note).
+__device__ __forceinline__ void release_coherent(bool strict) {
+  if (strict) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
+
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+__device__ __forceinline__ int poll_relaxed(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The one publish operation: store the iteration's sequence number into a
+// single-writer slot. Called after release_coherent() of the data it covers.
+__device__ __forceinline__ void slot_publish(int* slot, int seq, bool strict) {
+  if (strict)
+    __hip_atomic_store(slot, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    __hip_atomic_store(slot, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int fetch_add_relaxed(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int fetch_add_acq_rel(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Exponential s_sleep backoff, 64 to 512 clocks (s_sleep needs an immediate).
+__device__ __forceinline__ void backoff(int& lvl) {
+  if (lvl == 0) __builtin_amdgcn_s_sleep(1);
+  else if (lvl == 1) __builtin_amdgcn_s_sleep(2);
+  else if (lvl == 2) __builtin_amdgcn_s_sleep(4);
+  else __builtin_amdgcn_s_sleep(8);
+  lvl += (lvl < 3);
+}
+
+// Error reporting shared by every kernel: first error wins; the code is also
+// stored (system scope, the only system-scope write) into a host-visible word.
+struct ErrorSink {
+  int* dev;          // [0] = code, [1] = id of the wait or slot that failed
+  int* host;         // host-visible status word (pinned, coherent)
+};
+
+__device__ __forceinline__ void raise_error(const ErrorSink& e, int code, int id) {
+  if (atomicCAS(e.dev, 0, code) == 0) {
+    __hip_atomic_store(e.dev + 1, id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(e.host, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
+__device__ __forceinline__ bool error_raised(const ErrorSink& e) { return poll_relaxed(e.dev) != 0; }
+
+// Wait outcome codes (match fg_status values in the public header).
+constexpr int kErrTimeout = -5;
+constexpr int kErrProtocol = -6;
+
+// Bounded wait, one lane: spin until *p == target (a gate) using relaxed polls
+// and backoff. Returns 1 on success, 0 on timeout / error elsewhere / overshoot.
+// On success the caller issues acquire_agent(). *polls counts the loads.
+__device__ __forceinline__ int wait_eq(const int* p, int target, uint64_t deadline,
+                                       const ErrorSink& e, int id, uint32_t* polls) {
+  int lvl = 0;
+  uint32_t n = 0;
+  while (true) {
+    int v = poll_relaxed(p);
+    ++n;
+    if (v == target) { *polls += n; return 1; }
+    if (v > target) { raise_error(e, kErrProtocol, id); *polls += n; return 0; }
+    if ((n & 15) == 0) {
+      if (now_ticks() > deadline) { raise_error(e, kErrTimeout, id); *polls += n; return 0; }
+      if (error_raised(e)) { *polls += n; return 0; }
+    }
+    backoff(lvl);
+  }
+}
+
+// Bounded wait, one lane: spin until *p >= seq (a monotonic slot; old values
+// are harmless, nothing is ever cleared).
+__device__ __forceinline__ int wait_ge(const int* p, int seq, uint64_t deadline,
+                                       const ErrorSink& e, int id, uint32_t* polls) {
+  int lvl = 0;
+  uint32_t n = 0;
+  while (true) {
+    int v = poll_relaxed(p);
+    ++n;
+    if (v >= seq) { *polls += n; return 1; }
+    if ((n & 15) == 0) {
+      if (now_ticks() > deadline) { raise_error(e, kErrTimeout, id); *polls += n; return 0; }
+      if (error_raised(e)) { *polls += n; return 0; }
+    }
+    backoff(lvl);
+  }
+}
+
+// Wave-level helpers (64 lanes).
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+}  // namespace fg

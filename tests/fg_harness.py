@@ -1,0 +1,184 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI on
+seeded inputs and compare every result with the CPU oracle."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import oracle as O
+from sync_protocols_amd import fg
+from sync_protocols_amd import workloads as W
+
+DEV = "cuda:0"
+POISON = 0x7FC1          # a bf16 NaN; a gate that opens early lets it into the output
+
+
+def log(msg: str) -> None:
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def poison_(t: torch.Tensor) -> None:
+    t.view(torch.int16).fill_(POISON)
+
+
+class Case:
+    """One workload instance: inputs on the device, the oracle's layout, a route."""
+
+    def __init__(self, kind, shards, w, lay, route, n_groups, sigma_x, sigma_w, rows_per_shard,
+                 topk=None, expert_base=0):
+        self.kind = kind
+        self.shards_cpu = shards
+        self.w_cpu = w
+        self.lay = lay
+        self.route = route
+        self.n_groups = n_groups
+        self.sigma_x, self.sigma_w = sigma_x, sigma_w
+        self.rows_per_shard = rows_per_shard
+        self.K = shards[0].shape[1]
+        self.N = w.shape[-2]
+        self.shards = [s.to(DEV) for s in shards]
+        self.w = w.to(DEV).contiguous()
+        self.topk = topk
+        self.expert_base = expert_base
+        self._oracle_G = None
+
+    @property
+    def oracle_G(self):
+        if self._oracle_G is None:
+            self._oracle_G = O.gather([bits(s) for s in self.shards_cpu], self.lay)
+        return self._oracle_G
+
+
+def dense_case(seed, n_shards, rows, K, N, gather="contiguous", use_explicit=False) -> Case:
+    d = W.dense_inputs(seed, n_shards, rows, K, N, gather=gather)
+    if gather == "contiguous":
+        lay = O.layout_contiguous(n_shards, rows)
+        if use_explicit:
+            src = torch.arange(rows, dtype=torch.int32).repeat(n_shards, 1)
+            dst = (torch.arange(n_shards, dtype=torch.int32)[:, None] * rows + torch.arange(rows, dtype=torch.int32))
+            route = fg.route_explicit([rows] * n_shards, src.contiguous().to(DEV), dst.contiguous().to(DEV),
+                                      lay.m_pad, rows)
+        else:
+            route = fg.route_contig(rows)
+    else:
+        lay = O.layout_permutation(d.perm.numpy(), n_shards, rows)
+        src = torch.arange(rows, dtype=torch.int32).repeat(n_shards, 1).contiguous()
+        dst = d.perm.reshape(n_shards, rows).contiguous()
+        route = fg.route_explicit([rows] * n_shards, src.to(DEV), dst.to(DEV), lay.m_pad, rows)
+    return Case("dense", d.shards, d.w, lay, route, 1, d.sigma_x, d.sigma_w, rows)
+
+
+def ep_case(seed, n_shards, tokens, K, N, n_experts=64, topk=8, n_local=8, expert_base=0) -> Case:
+    e = W.ep_inputs(seed, n_shards=n_shards, tokens=tokens, K=K, N=N, n_experts=n_experts, topk=topk,
+                    n_local=n_local, expert_base=expert_base)
+    lay = O.layout_topk(e.topk.numpy(), expert_base, n_local)
+    topk_dev = e.topk.to(DEV).contiguous()
+    route = fg.route_topk(topk_dev, tokens, expert_base)
+    return Case("ep", e.shards, e.w, lay, route, n_local, e.sigma_x, e.sigma_w, tokens, topk=topk_dev,
+                expert_base=expert_base)
+
+
+def make_ctx(case: Case, *, n_comm=0, n_gemm=0, tile_n=0, timeout_ns=0, max_rows=None) -> fg.Context:
+    max_rows = max_rows or max(int(case.lay.stream_len.max()), case.rows_per_shard)
+    cfg = fg.make_config(len(case.shards), max_rows, case.K, case.N, n_groups=case.n_groups,
+                         n_comm_wg=n_comm, n_gemm_wg=n_gemm, tile_n=tile_n, timeout_ns=timeout_ns)
+    return fg.Context(cfg)
+
+
+def buffers(ctx: fg.Context, case: Case):
+    cap = fg.capacity(ctx.cfg)
+    gathered = torch.zeros(cap, case.K, dtype=torch.bfloat16, device=DEV)
+    out = torch.zeros(cap, case.N, dtype=torch.bfloat16, device=DEV)
+    return gathered, out
+
+
+def run_iters(ctx, case, gathered, out, iters, flags=0, poison=True):
+    for t in range(iters):
+        if poison:
+            poison_(gathered)
+            poison_(out)
+        rc = ctx.gather_gemm(case.shards, case.w, gathered, out, route=case.route, flags=flags)
+        assert rc == fg.OK, fg.strerror(rc)
+    torch.cuda.synchronize()
+    st = ctx.stats()
+    assert st.error_code == 0, (st.error_code, hex(st.error_id))
+    return st
+
+
+def control_plane(ctx: fg.Context, n_shards: int):
+    v = ctx.views()
+    S, cc, rbc = n_shards, v.chunk_cap, v.rb_cap
+    return dict(
+        slot=ctx.read_i32(v.slot, S * cc).numpy().reshape(S, cc),
+        counter=ctx.read_i32(v.counter, 2 * rbc).numpy().reshape(2, rbc),
+        elect=ctx.read_i32(v.elect, 2 * S * cc).numpy().reshape(2, S, cc),
+        pub_count=ctx.read_i32(v.pub_count, S * cc).numpy().reshape(S, cc),
+        seed=ctx.read_i32(v.seed, rbc).numpy(),
+        inv=ctx.read_i32(v.inv_row, v.m_pad_cap).numpy(),
+        stream_len=ctx.read_i32(v.stream_len, S).numpy(),
+        group_off=ctx.read_i32(v.group_off, 65).numpy(),
+        src_row=ctx.read_i32(v.src_row, S * ctx.cfg.max_rows_per_shard).numpy().reshape(S, -1),
+        dst_row=ctx.read_i32(v.dst_row, S * ctx.cfg.max_rows_per_shard).numpy().reshape(S, -1),
+        chunk_cap=cc, rb_cap=rbc)
+
+
+def check_route(case: Case, cp) -> None:
+    lay = case.lay
+    assert np.array_equal(cp["stream_len"], lay.stream_len), "stream lengths"
+    for s in range(lay.n_shards):
+        n = int(lay.stream_len[s])
+        assert np.array_equal(cp["src_row"][s, :n], lay.src_row[s]), f"src_row shard {s}"
+        assert np.array_equal(cp["dst_row"][s, :n], lay.dst_row[s]), f"dst_row shard {s}"
+    assert np.array_equal(cp["group_off"][:lay.n_groups + 1], lay.group_off), "group offsets"
+    assert np.array_equal(cp["seed"][:lay.n_rb], O.seeds(lay)), "padding seeds"
+    real = O.real_rows(lay)
+    assert np.array_equal(cp["inv"][:lay.m_pad] >= 0, real), "padding rows of the inverse map"
+
+
+def check_control_plane(case: Case, cp, t: int, verify_iters: int | None) -> None:
+    lay = case.lay
+    want = O.state_after(lay, t, cp["chunk_cap"])
+    n_rb = lay.n_rb
+    assert np.array_equal(cp["slot"], want.slot), "slots"
+    assert np.array_equal(cp["counter"][:, :n_rb], want.counter), "arrival counters (both parities)"
+    assert np.array_equal(cp["elect"], want.elect), "election counts (both parities)"
+    if verify_iters is not None:
+        exp_pub = (want.pub_count > 0) * verify_iters
+        assert np.array_equal(cp["pub_count"], exp_pub), "one publisher per chunk per iteration"
+
+
+def check_gathered(case: Case, gathered: torch.Tensor, poisoned: bool) -> None:
+    lay = case.lay
+    G = bits(gathered[:lay.m_pad])
+    real = O.real_rows(lay)
+    assert np.array_equal(G[real], case.oracle_G[real]), "gathered real rows bit-exact"
+    pad_val = POISON if poisoned else 0
+    assert np.all(G[~real] == pad_val), "padding rows never written"
+
+
+def check_out(case: Case, out: torch.Tensor, rows=None) -> dict:
+    lay = case.lay
+    real = O.real_rows(lay)
+    wb = bits(case.w_cpu)
+    if wb.ndim == 2:
+        wb = wb[None]
+    if rows is None:
+        C64 = O.gemm(case.oracle_G, wb, lay)
+        ob = bits(out[:lay.m_pad])
+        mask = np.repeat(real[:, None], case.N, 1)
+    else:
+        rows = np.asarray(rows)
+        C64 = O.gemm(case.oracle_G, wb, lay, rows=rows)
+        ob = bits(out[torch.as_tensor(rows, device=out.device)])
+        mask = np.repeat(real[rows][:, None], case.N, 1)
+    r = O.gemm_check(ob, C64, case.K, case.sigma_x, case.sigma_w, mask)
+    assert r["ok"], r
+    return r

@@ -1,0 +1,177 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle: bit-exact
+gathered rows, route tables and control-plane state; the contraction within the
+stated tolerance; at small sizes element by element, at the full workload sizes
+on sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sync_protocols_amd import fg
+from sync_protocols_amd import workloads as W
+from fg_harness import (DEV, POISON, bits, buffers, check_control_plane, check_gathered, check_out,
+                        check_route, control_plane, dense_case, ep_case, log, make_ctx, poison_, run_iters)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_and_check(case, iters, *, flags=0, ctx_kw=None, full_out=True, sample_rows=None, verify=True):
+    ctx = make_ctx(case, **(ctx_kw or {}))
+    gathered, out = buffers(ctx, case)
+    f = flags | (fg.CALL_VERIFY if verify else 0)
+    st = run_iters(ctx, case, gathered, out, iters, flags=f)
+    cp = control_plane(ctx, len(case.shards))
+    check_route(case, cp)
+    check_control_plane(case, cp, iters, iters if verify else None)
+    check_gathered(case, gathered, poisoned=True)
+    r = check_out(case, out, rows=None if full_out else sample_rows)
+    if verify:
+        assert st.publishes == iters * O.signal_counts(case.lay)["publishes"]
+    ctx.close()
+    return r
+
+
+def test_tiny_contiguous_three_iterations():
+    log("tiny contiguous: 4 x 256 rows, K=256, N=512, 3 iterations")
+    c = W.CONFIGS["tiny"]
+    case = dense_case(c["seed"], c["n_shards"], c["rows"], c["K"], c["N"])
+    r = _run_and_check(case, c["iters"])
+    log(f"tiny ok: max|d|={r['max_abs']:.3g} tol={r['tol']:.3g}")
+
+
+def test_tiny_strict_fences_same_result():
+    log("tiny contiguous, formal release fences on every signal")
+    c = W.CONFIGS["tiny"]
+    case = dense_case(c["seed"], c["n_shards"], c["rows"], c["K"], c["N"])
+    _run_and_check(case, 3, flags=fg.CALL_STRICT)
+
+
+def test_ragged_contiguous_padding():
+    log("ragged contiguous: 3 x 50 rows (150 real of 256), K=256, N=256")
+    case = dense_case(31, 3, 50, 256, 256)
+    _run_and_check(case, 4)
+
+
+def test_ragged_rows_128_tile():
+    log("ragged contiguous: 5 x 77 rows (385 real of 512 -> BM 256), K=384, N=384 (BN 128)")
+    case = dense_case(32, 5, 77, 384, 384)
+    _run_and_check(case, 3, ctx_kw=dict(tile_n=128))
+
+
+def test_ragged_odd_row_blocks():
+    log("ragged contiguous: 3 x 100 rows (m_pad 384 -> BM 128 tiles), K=256, N=256")
+    case = dense_case(33, 3, 100, 256, 256)
+    _run_and_check(case, 3)
+
+
+def test_explicit_route_equals_contiguous():
+    log("explicit route carrying the contiguous layout")
+    case = dense_case(34, 4, 256, 256, 512, use_explicit=True)
+    _run_and_check(case, 3)
+
+
+def test_permutation_scatter():
+    log("permutation scatter: 4 x 200 rows, K=512, N=256")
+    case = dense_case(35, 4, 200, 512, 256, gather="permutation")
+    _run_and_check(case, 5)
+
+
+def test_ep_topk_small():
+    log("expert dispatch: 8 shards x 64 tokens, top-8 of 64, 8 local experts, K=256, N=256")
+    case = ep_case(36, 8, 64, 256, 256)
+    r = _run_and_check(case, 3)
+    log(f"ep small ok: m_pad={case.lay.m_pad} max|d|={r['max_abs']:.3g}")
+
+
+def test_ep_topk_other_base():
+    log("expert dispatch: local experts 24..31, 4 shards x 200 tokens")
+    case = ep_case(37, 4, 200, 256, 256, expert_base=24)
+    _run_and_check(case, 3)
+
+
+def test_fifty_iterations_poisoned():
+    log("tiny contiguous, 50 iterations, NaN poison before each")
+    c = W.CONFIGS["tiny"]
+    case = dense_case(c["seed"], c["n_shards"], c["rows"], c["K"], c["N"])
+    _run_and_check(case, 50)
+
+
+def test_comm_only_and_gemm_only_roles():
+    log("role-only modes: comm only then gemm only")
+    case = dense_case(38, 4, 256, 256, 512)
+    ctx = make_ctx(case)
+    gathered, out = buffers(ctx, case)
+    poison_(gathered)
+    poison_(out)
+    assert ctx.gather_gemm(case.shards, case.w, gathered, out, route=case.route, flags=fg.CALL_COMM_ONLY) == 0
+    torch.cuda.synchronize()
+    check_gathered(case, gathered, poisoned=True)
+    assert np.all(bits(out) == POISON), "comm-only must not write the output"
+    cp = control_plane(ctx, 4)
+    assert np.all(cp["counter"][1, :case.lay.n_rb] == 128)
+    assert ctx.gather_gemm(case.shards, case.w, gathered, out, route=case.route, flags=fg.CALL_GEMM_ONLY) == 0
+    torch.cuda.synchronize()
+    check_out(case, out)
+    assert ctx.stats().error_code == 0
+    ctx.close()
+
+
+def test_zero_length_shard_streams():
+    log("explicit route with empty and ragged shard streams")
+    torch.manual_seed(0)
+    S, R, K, N = 4, 96, 256, 256
+    d = W.dense_inputs(39, S, R, K, N)
+    lens = [0, 96, 17, 65]
+    rng = np.random.default_rng(39)
+    m = sum(lens)
+    m_pad = -(-m // 128) * 128
+    dst_all = rng.permutation(m_pad)[:m]
+    src = np.zeros((S, R), np.int32)
+    dst = np.zeros((S, R), np.int32)
+    j = 0
+    src_l, dst_l = [], []
+    for s in range(S):
+        srow = rng.permutation(R)[:lens[s]]
+        src[s, :lens[s]] = srow
+        dst[s, :lens[s]] = dst_all[j:j + lens[s]]
+        src_l.append(srow.astype(np.int64))
+        dst_l.append(dst_all[j:j + lens[s]].astype(np.int64))
+        j += lens[s]
+    lay = O.Layout(src_l, dst_l, m_pad, np.array([0, m_pad]))
+    route = fg.route_explicit(lens, torch.from_numpy(src).to(DEV), torch.from_numpy(dst).to(DEV), m_pad, R)
+    from fg_harness import Case
+    case = Case("dense", d.shards, d.w, lay, route, 1, d.sigma_x, d.sigma_w, R)
+    _run_and_check(case, 3)
+
+
+# ----------------------------------------------------------- full workload sizes
+
+def _sample_rows(lay, n=96, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set([0, 1, lay.m_pad - 1, lay.m_pad - 128])
+    rows.update(rng.integers(0, lay.m_pad, n).tolist())
+    return sorted(rows)
+
+
+def test_tp_full_size_sampled():
+    c = W.CONFIGS["tp"]
+    log("TP share: 4 x 2048 rows, K=N=4096, 4 iterations, sampled output rows")
+    case = dense_case(c["seed"], c["n_shards"], c["rows"], c["K"], c["N"])
+    r = _run_and_check(case, 4, full_out=False, sample_rows=_sample_rows(case.lay))
+    log(f"tp ok: max|d|={r['max_abs']:.3g} tol={r['tol']:.3g}")
+
+
+def test_ep_full_size_sampled():
+    c = W.CONFIGS["ep"]
+    log("EP dispatch: 8 x 1024 tokens, top-8/64, 8 local experts, K=7168, N=2048, sampled rows")
+    case = ep_case(c["seed"], c["n_shards"], c["tokens"], c["K"], c["N"])
+    r = _run_and_check(case, 3, full_out=False, sample_rows=_sample_rows(case.lay))
+    log(f"ep ok: m_pad={case.lay.m_pad} max|d|={r['max_abs']:.3g}")
+
+
+def test_large_full_size_sampled():
+    c = W.CONFIGS["large"]
+    log("Large: 8 x 4096 rows permuted, K=N=8192, 3 iterations, sampled rows")
+    case = dense_case(c["seed"], c["n_shards"], c["rows"], c["K"], c["N"], gather="permutation")
+    r = _run_and_check(case, 3, full_out=False, sample_rows=_sample_rows(case.lay, 64))
+    log(f"large ok: max|d|={r['max_abs']:.3g} tol={r['tol']:.3g}")

@@ -1,0 +1,177 @@
+"""Protocol entry points on the GPU: the all-rank slot barrier, the slot
+ping-pong, the protocol-stress workload, and the error paths (bounded waits that
+time out, counters that overshoot, invalid arguments)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sync_protocols_amd import fg
+from sync_protocols_amd import workloads as W
+from fg_harness import DEV, buffers, dense_case, log, make_ctx
+
+pytestmark = pytest.mark.gpu
+
+
+def _small_ctx(n_shards=4, timeout_ns=0, stress=(0, 0, 0)):
+    return fg.Context(fg.make_config(n_shards, 256, 256, 256, timeout_ns=timeout_ns, stress=stress))
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_barrier_slots(n):
+    log(f"slot barrier over {n} virtual ranks, 3 calls of 1, 10, 1000 rounds")
+    ctx = _small_ctx(n)
+    total = 0
+    for r in (1, 10, 1000):
+        assert ctx.barrier(r) == 0
+        total += r
+    st = ctx.stats()
+    assert st.error_code == 0 and st.bseq == total
+    v = ctx.views()
+    bs = ctx.read_i32(v.bslot, n * n).numpy().reshape(n, n)
+    assert np.array_equal(bs, O.barrier_expected(n, total))
+    assert st.t_barrier_us > 0
+    log(f"barrier n={n}: {st.t_barrier_us:.3f} us per barrier")
+    ctx.close()
+
+
+def test_pingpong_rtt():
+    log("slot ping-pong across XCDs, agent and system scope")
+    ctx = _small_ctx()
+    for sys_scope in (False, True):
+        assert ctx.pingpong(2000, sys_scope) == 0
+        st = ctx.stats()
+        assert st.error_code == 0 and 0 < st.t_rtt_us < 100
+        log(f"rtt sys={sys_scope}: {st.t_rtt_us:.3f} us")
+    ctx.close()
+
+
+def _stress_ctx(st_in, timeout_ns=0):
+    P, C, KC = st_in.chunk_rows.shape
+    return fg.Context(fg.make_config(4, 256, 256, 256, timeout_ns=timeout_ns, stress=(P, C, KC)))
+
+
+def test_stress_full_config():
+    c = W.CONFIGS["stress"]
+    log("protocol stress: 64 producers x 64 consumers, 10000 signals/iteration, 50 iterations, delays 0-20us")
+    st_in = W.stress_inputs(c["seed"], iters=c["iters"])
+    ctx = _stress_ctx(st_in)
+    cr = st_in.chunk_rows.to(DEV)
+    delays = st_in.delays_ns.to(DEV)
+    P, C, KC = st_in.chunk_rows.shape
+    payload = torch.zeros(C * P * KC * 64, dtype=torch.int32, device=DEV)
+    for t in range(c["iters"]):
+        assert ctx.stress(cr, delays[t].contiguous(), payload) == 0
+    st = ctx.stats()
+    assert st.error_code == 0 and st.stale == 0
+    want = O.stress_expected(st_in.chunk_rows.numpy(), c["iters"])
+    v = ctx.views()
+    slots = ctx.read_i32(v.stress_slot, P * C * KC).numpy().reshape(P, C, KC)
+    pubs = ctx.read_i32(v.stress_pub, P * C * KC).numpy().reshape(P, C, KC)
+    assert np.array_equal(slots, want["slot"])
+    assert np.array_equal(pubs, want["pub_count"])
+    got = payload.cpu().numpy().view(np.uint32).reshape(C, P, KC, 64)
+    assert np.array_equal(got[want["valid"]], want["payload"][want["valid"]])
+    log(f"stress ok: slot polls {st.slot_polls}")
+    ctx.close()
+
+
+def test_stress_strict_mode():
+    log("protocol stress, 5 iterations with formal release fences")
+    st_in = W.stress_inputs(1004, iters=5)
+    ctx = _stress_ctx(st_in)
+    cr = st_in.chunk_rows.to(DEV)
+    delays = st_in.delays_ns.to(DEV)
+    payload = torch.zeros(64 * 64 * 4 * 64, dtype=torch.int32, device=DEV)
+    for t in range(5):
+        assert ctx.stress(cr, delays[t].contiguous(), payload, flags=fg.CALL_STRICT) == 0
+    st = ctx.stats()
+    assert st.error_code == 0 and st.stale == 0
+    ctx.close()
+
+
+# ------------------------------------------------------------- error paths
+
+def test_dropped_publish_times_out_in_stress():
+    log("fault: dropped publish in the stress workload -> bounded wait times out")
+    st_in = W.stress_inputs(1004, producers=4, consumers=4, signals=40, iters=2)
+    ctx = _stress_ctx(st_in, timeout_ns=20_000_000)
+    cr = st_in.chunk_rows.to(DEV)
+    d = torch.zeros_like(st_in.delays_ns[0]).to(DEV)
+    payload = torch.zeros(4 * 4 * 4 * 64, dtype=torch.int32, device=DEV)
+    assert ctx.stress(cr, d, payload, flags=fg.FAULT_DROP_PUBLISH) == 0
+    st = ctx.stats()
+    assert st.error_code == fg.ETIMEOUT
+    assert ctx.stress(cr, d, payload) == fg.ETIMEOUT     # reported by the next call
+    assert ctx.stress(cr, d, payload) == fg.ESTATE       # then sticky
+    ctx.close()
+
+
+def test_seed_low_times_out():
+    log("fault: padding seed one too low -> gate never opens -> FG_ETIMEOUT")
+    case = dense_case(40, 3, 50, 256, 256)
+    ctx = make_ctx(case, timeout_ns=20_000_000)
+    g, o = buffers(ctx, case)
+    assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route, flags=fg.FAULT_SEED_LOW) == 0
+    st = ctx.stats()
+    assert st.error_code == fg.ETIMEOUT and st.error_id == 0
+    assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route) == fg.ETIMEOUT
+    assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route) == fg.ESTATE
+    ctx.close()
+
+
+def test_seed_high_overshoots():
+    log("fault: padding seed one too high -> counter overshoots -> FG_EPROTOCOL")
+    case = dense_case(41, 3, 50, 256, 256)
+    ctx = make_ctx(case, timeout_ns=20_000_000)
+    g, o = buffers(ctx, case)
+    assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route, flags=fg.FAULT_SEED_HIGH) == 0
+    st = ctx.stats()
+    assert st.error_code == fg.EPROTOCOL
+    assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route) == fg.EPROTOCOL
+    ctx.close()
+
+
+def test_dropped_publish_visible_in_slots():
+    log("fault: dropped publish in the gather -> slot (0,0) stays behind, nothing else changes")
+    case = dense_case(42, 4, 256, 256, 512)
+    ctx = make_ctx(case)
+    g, o = buffers(ctx, case)
+    assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route) == 0
+    assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route, flags=fg.FAULT_DROP_PUBLISH) == 0
+    torch.cuda.synchronize()
+    v = ctx.views()
+    slots = ctx.read_i32(v.slot, 4 * v.chunk_cap).numpy().reshape(4, -1)
+    assert slots[0, 0] == 1 and np.all(slots[:, :4][slots[:, :4] != 1] == 2)
+    assert (slots[:, :4] == 2).sum() == 15
+    ctx.close()
+
+
+def test_duplicate_route_row_rejected():
+    log("bad route: two stream rows target one gathered row -> FG_EPROTOCOL")
+    case = dense_case(43, 2, 128, 256, 256)
+    src = torch.arange(128, dtype=torch.int32).repeat(2, 1).contiguous().to(DEV)
+    dst = torch.arange(128, dtype=torch.int32).repeat(2, 1).contiguous().to(DEV)   # both shards -> rows 0..127
+    route = fg.route_explicit([128, 128], src, dst, 256, 128)
+    ctx = make_ctx(case, timeout_ns=20_000_000)
+    g, o = buffers(ctx, case)
+    assert ctx.gather_gemm(case.shards, case.w, g, o, route=route) == 0
+    st = ctx.stats()
+    assert st.error_code == fg.EPROTOCOL
+    ctx.close()
+
+
+def test_invalid_arguments():
+    log("invalid arguments: stream binding, both role flags, bad route sizes")
+    case = dense_case(44, 2, 128, 256, 256)
+    ctx = make_ctx(case)
+    g, o = buffers(ctx, case)
+    assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route) == 0
+    s2 = torch.cuda.Stream()
+    assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route, stream=s2) == fg.EINVAL
+    assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route,
+                           flags=fg.CALL_COMM_ONLY | fg.CALL_GEMM_ONLY) == fg.EINVAL
+    assert ctx.gather_gemm(case.shards, case.w, g, o, route=fg.route_contig(1000)) == fg.EINVAL
+    torch.cuda.synchronize()
+    assert ctx.stats().error_code == 0
+    ctx.close()
