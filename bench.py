@@ -1,0 +1,293 @@
+"""Benchmark of the fused producer/consumer gather-GEMM on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload tp|large|ep|tiny]
+
+A step is one pass of the hot path over one batch: layout (route) step, one
+persistent kernel that moves the rows, counts arrivals, elects publishers,
+publishes slots, gates and runs the bf16 contraction. Inputs are resident in
+HBM before timing starts. Prints ONE JSON line.
+
+Beside the fused throughput it reports the three timings of the measurement
+method ("Know your platform" §5: T_comp alone with the same workgroups, T_comm
+alone, T_total), overlap efficiency and compute interference, the gather's
+HBM rate, slot-signal latency (ping-pong round trip, slot barrier), the
+protocol-stress signal rate, the roofline of the fused kernel and the CPU
+oracle timed on a bounded sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _events_time(fn, n, torch):
+    """Per-call device time (ms) of n calls, HIP events on the current stream."""
+    times = []
+    for _ in range(n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return times
+
+
+def _pct(xs, p):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(p / 100 * (len(xs) - 1)))))]
+
+
+def setup_workload(name, torch, fg, W):
+    dev = "cuda:0"
+    c = dict(W.CONFIGS[name])
+    if c["kind"] == "dense":
+        d = W.dense_inputs(c["seed"], c["n_shards"], c["rows"], c["K"], c["N"], gather=c["gather"])
+        S, R, K, N = c["n_shards"], c["rows"], c["K"], c["N"]
+        shards = [s.to(dev) for s in d.shards]
+        w = d.w.to(dev)
+        if c["gather"] == "contiguous":
+            route = fg.route_contig(R)
+        else:
+            src = torch.arange(R, dtype=torch.int32).repeat(S, 1).contiguous().to(dev)
+            dst = d.perm.reshape(S, R).contiguous().to(dev)
+            route = fg.route_explicit([R] * S, src, dst, S * R, R)
+        m_real = S * R
+        n_groups = 1
+        max_rows = R
+        info = dict(n_shards=S, rows_per_shard=R, M=m_real, K=K, N=N, gather=c["gather"])
+        inputs = dict(dense=d)
+    else:
+        e = W.ep_inputs(c["seed"], n_shards=c["n_shards"], tokens=c["tokens"], K=c["K"], N=c["N"],
+                        n_experts=c["n_experts"], topk=c["topk"], n_local=c["n_local"],
+                        expert_base=c["expert_base"])
+        S, K, N = c["n_shards"], c["K"], c["N"]
+        shards = [s.to(dev) for s in e.shards]
+        w = e.w.to(dev)
+        topk = e.topk.to(dev).contiguous()
+        route = fg.route_topk(topk, c["tokens"], c["expert_base"])
+        local = ((e.topk >= c["expert_base"]) & (e.topk < c["expert_base"] + c["n_local"]))
+        m_real = int(local.sum())
+        n_groups = c["n_local"]
+        max_rows = c["tokens"] * min(c["topk"], c["n_local"])
+        info = dict(n_shards=S, tokens_per_shard=c["tokens"], M=m_real, K=K, N=N, topk=c["topk"],
+                    experts=c["n_experts"], local_experts=c["n_local"])
+        inputs = dict(ep=e)
+    return dict(name=name, shards=shards, w=w, route=route, m_real=m_real, n_groups=n_groups,
+                max_rows=max_rows, K=K, N=N, S=S, info=info, inputs=inputs, iters=c["iters"], cfg=c)
+
+
+def cpu_baseline(wl, budget_s=12.0):
+    """The oracle as it stands, on host cores, over a bounded sample of the
+    workload: layout + gather of all rows, then the float64 contraction of as
+    many gathered rows as fit the time budget. Returns TFLOP/s of the sample."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    c = wl["cfg"]
+
+    def bits(t):
+        return t.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+
+    t0 = time.perf_counter()
+    if c["kind"] == "dense":
+        d = wl["inputs"]["dense"]
+        if c["gather"] == "contiguous":
+            lay = O.layout_contiguous(c["n_shards"], c["rows"])
+        else:
+            lay = O.layout_permutation(d.perm.numpy(), c["n_shards"], c["rows"])
+        G = O.gather([bits(s) for s in d.shards], lay)
+        wb = bits(d.w)[None]
+    else:
+        e = wl["inputs"]["ep"]
+        lay = O.layout_topk(e.topk.numpy(), c["expert_base"], c["n_local"])
+        G = O.gather([bits(s) for s in e.shards], lay)
+        wb = bits(e.w)
+    O.seeds(lay)
+    O.signal_counts(lay)
+    t_layout = time.perf_counter() - t0
+    K, N = wl["K"], wl["N"]
+    real_idx = np.nonzero(O.real_rows(lay))[0]
+    rows = 16
+    t1 = time.perf_counter()
+    O.gemm(G, wb, lay, rows=real_idx[:rows])
+    dt = max(time.perf_counter() - t1, 1e-6)
+    rows = int(min(len(real_idx), max(rows, rows * (budget_s - t_layout) / dt)))
+    t1 = time.perf_counter()
+    O.gemm(G, wb, lay, rows=real_idx[:rows])
+    t_gemm = time.perf_counter() - t1
+    flop = 2.0 * rows * K * N
+    return dict(value=round(flop / t_gemm / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"layout+gather of all {lay.m} rows ({t_layout:.2f} s) and the float64 contraction of "
+                       f"{rows} gathered rows x K={K} x N={N} ({t_gemm:.2f} s); value = contraction FLOP / its time")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="tp", choices=["tp", "large", "ep", "tiny"])
+    ap.add_argument("--n-comm", type=int, default=0)
+    ap.add_argument("--tile-n", type=int, default=0)
+    ap.add_argument("--no-extras", action="store_true", help="fused timing only (for profiling runs)")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path runs on a single MI355X "
+              "(source shards are HBM regions on that GPU); --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sync_protocols_amd import fg
+    from sync_protocols_amd import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    wl = setup_workload(args.workload, torch, fg, W)
+    cfg = fg.make_config(wl["S"], wl["max_rows"], wl["K"], wl["N"], n_groups=wl["n_groups"],
+                         n_comm_wg=args.n_comm, tile_n=args.tile_n)
+    ctx = fg.Context(cfg)
+    cap = fg.capacity(cfg)
+    gathered = torch.zeros(cap, wl["K"], dtype=torch.bfloat16, device="cuda:0")
+    out = torch.zeros(cap, wl["N"], dtype=torch.bfloat16, device="cuda:0")
+    flop = 2.0 * wl["m_real"] * wl["K"] * wl["N"]
+    gather_bytes = 2.0 * wl["m_real"] * wl["K"] * 2
+
+    def step(flags=0):
+        rc = ctx.gather_gemm(wl["shards"], wl["w"], gathered, out, route=wl["route"], flags=flags)
+        if rc != fg.OK:
+            raise RuntimeError(f"fg_gather_gemm: {fg.strerror(rc)}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # ---- timed region: exactly `steps` steps, events around each launch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        step()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in ev]
+    st = ctx.stats()
+    if st.error_code:
+        raise RuntimeError(f"device error {st.error_code} id {st.error_id}")
+    ms_per_step = wall * 1000.0 / args.steps
+    avg_launch_ms = statistics.mean(per)
+    value = flop * args.steps / wall / 1e12
+
+    result = {
+        "metric": "fused gather-GEMM TFLOP/s + overlap efficiency; slot-signal latency (us)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": dict(workload=f"{args.workload}", **wl["info"], n_comm_wg=st.n_comm_wg,
+                       n_gemm_wg=st.n_gemm_wg),
+    }
+    achieved = flop / (avg_launch_ms * 1e-3) / 1e12
+    result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                          "kernel": "fused_kernel", "avg_launch_us": round(avg_launch_ms * 1000, 2)}
+
+    if not args.no_extras:
+        n_rep = max(10, args.steps)
+        t_total = _events_time(lambda: step(), n_rep, torch)
+        st_f = ctx.stats()
+        busy_fused = st_f.t_gemm_busy_us
+        t_comp = _events_time(lambda: step(fg.CALL_GEMM_ONLY), n_rep, torch)
+        st_c = ctx.stats()
+        busy_alone = st_c.t_gemm_busy_us
+        t_comm = _events_time(lambda: step(fg.CALL_COMM_ONLY), n_rep, torch)
+        step()  # leave the buffers in the fused state
+        torch.cuda.synchronize()
+        med = lambda xs: statistics.median(xs) * 1000.0  # noqa: E731  (us)
+        Tt, Tc, Tm = med(t_total), med(t_comp), med(t_comm)
+        ov = (Tc + Tm - Tt) / min(Tc, Tm)
+        result["overlap"] = {
+            "T_comp_alone_us": round(Tc, 2), "T_comm_alone_us": round(Tm, 2), "T_total_us": round(Tt, 2),
+            "T_total_p10_p90_us": [round(_pct(t_total, 10) * 1000, 2), round(_pct(t_total, 90) * 1000, 2)],
+            "overlap_efficiency": round(ov, 4),
+            "compute_interference": round(busy_fused / busy_alone, 4) if busy_alone else None,
+            "wall_interference": round(Tt / Tc, 4),
+            "gather_GBps": round(gather_bytes / (Tm * 1e-6) / 1e9, 1),
+            "gather_frac_hbm": round(gather_bytes / (Tm * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "gemm_alone_TFLOPs": round(flop / (Tc * 1e-6) / 1e12, 2),
+            "gate_wait_us_mean": round(st_f.t_gate_wait_us, 2),
+        }
+        # slot-signal latency
+        lat = fg.Context(fg.make_config(8, 256, 256, 256))
+        assert lat.pingpong(10000, False) == 0
+        rtt_a = lat.stats().t_rtt_us
+        assert lat.pingpong(10000, True) == 0
+        rtt_s = lat.stats().t_rtt_us
+        assert lat.barrier(1000) == 0
+        bar8 = lat.stats().t_barrier_us
+        lat.close()
+        lat4 = fg.Context(fg.make_config(4, 256, 256, 256))
+        assert lat4.barrier(1000) == 0
+        bar4 = lat4.stats().t_barrier_us
+        host = _events_time(lambda: lat4.barrier(1), 50, torch)
+        lat4.close()
+        result["slot_latency_us"] = {"pingpong_rtt_agent": round(rtt_a, 3), "pingpong_rtt_system": round(rtt_s, 3),
+                                     "barrier_4_ranks": round(bar4, 3), "barrier_8_ranks": round(bar8, 3),
+                                     "barrier_4_ranks_per_call_incl_launch": round(statistics.median(host) * 1000, 2)}
+        # protocol stress
+        sc = W.CONFIGS["stress"]
+        s_in = W.stress_inputs(sc["seed"], iters=sc["iters"])
+        P, Cc, KC = s_in.chunk_rows.shape
+        sctx = fg.Context(fg.make_config(4, 256, 256, 256, stress=(P, Cc, KC)))
+        cr = s_in.chunk_rows.cuda()
+        dl = s_in.delays_ns.cuda()
+        zero = torch.zeros_like(dl[0])
+        payload = torch.zeros(Cc * P * KC * 64, dtype=torch.int32, device="cuda:0")
+        assert sctx.stress(cr, zero, payload) == 0
+        t_nodelay = _events_time(lambda: sctx.stress(cr, zero, payload), 10, torch)
+        t_delay = []
+        for t in range(sc["iters"]):
+            t_delay += _events_time(lambda: sctx.stress(cr, dl[t].contiguous(), payload), 1, torch)
+        sst = sctx.stats()
+        sctx.close()
+        signals = int((s_in.chunk_rows > 0).sum())
+        result["stress"] = {"signals_per_iter": signals, "iters": sc["iters"] + 11, "stale": int(sst.stale),
+                            "errors": int(sst.error_code),
+                            "us_per_iter_no_delay": round(statistics.median(t_nodelay) * 1000, 2),
+                            "us_per_iter_delays_0_20us": round(statistics.median(t_delay) * 1000, 2),
+                            "signals_per_s_no_delay": round(signals / (statistics.median(t_nodelay) * 1e-3), 0)}
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(wl)
+    ctx.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

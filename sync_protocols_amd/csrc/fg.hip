@@ -92,7 +92,7 @@ static bool config_ok(const fg_config* c) {
   if (!c) return false;
   if (c->n_shards < 1 || c->n_shards > FG_MAX_SHARDS) return false;
   if (c->max_rows_per_shard < 1 || c->max_rows_per_shard > (1 << 24) - 1) return false;
-  if (c->K < 128 || c->K % 128 != 0) return false;
+  if (c->K < 128 || c->K % 128 != 0 || c->K > 16384) return false;
   if (c->N < 128 || c->N % 128 != 0) return false;
   if (c->n_groups < 1 || c->n_groups > FG_MAX_GROUPS) return false;
   if (c->tile_n != 0 && c->tile_n != 128 && c->tile_n != 256) return false;
@@ -378,10 +378,10 @@ fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route*
   a.src_row = ctx->p.src_row; a.stream_len = ctx->p.stream_len; a.desc = ctx->p.desc; a.stats = ctx->p.stats;
   a.wgtime = ctx->p.wgtime; a.err = sink(ctx); a.seq = ctx->seq;
   a.n_comm = ctx->n_comm; a.n_gemm = ctx->n_gemm;
-  int rpb = 32768 / (c.K * 2);
-  rpb = std::max(1, std::min(16, rpb));
-  while (FG_ROW_BLOCK % rpb) --rpb;
-  a.rows_per_batch = rpb;
+  // rows per communication batch: matches the copy template chosen on the
+  // device (about 32 KB of loads in flight per wave)
+  const int upr = (c.K / 8 + 63) / 64;
+  a.rows_per_batch = upr <= 2 ? 16 : upr <= 4 ? 8 : upr <= 8 ? 4 : upr <= 16 ? 2 : 1;
   a.flags = flags;
   a.timeout_ticks = timeout_ticks(ctx);
   ctx->last_grid = a.n_comm + a.n_gemm;

@@ -1,4 +1,4 @@
-// bf16 x bf16 -> fp32 MFMA tile for gfx950, LDS-staged, two-stage pipeline.
+// bf16 x bf16 -> fp32 MFMA tile for gfx950, LDS-staged, two stages.
 //
 // The contraction is the dense GEMM the compute workgroups run once a row
 // block's gate opens (the GEMM behind the gate of "PCIe sync protocols" §5):
@@ -13,9 +13,9 @@
 // l % 32 and k = 8 * (l / 32) + 0..7; result register v of lane l is
 // D[8 * (v / 4) + 4 * (l / 32) + v % 4][l % 32].
 //
-// LDS: per stage, each operand tile is stored as rows of 64 k (128 bytes =
-// 8 slots of 16 bytes); logical 16-byte chunk c of row r sits in slot
-// c ^ (r & 7), so the 8 lanes of a ds_read_b128 phase hit 8 distinct slots.
+// LDS: two stages; per stage each operand tile is stored as rows of 64 k (one
+// 128-byte line = 8 slots of 16 bytes; full lines keep the L2 request rate at
+// its best), logical chunk c of row r in slot c ^ ((r >> 1) & 7) (see swz).
 // Global -> LDS moves use buffer_load ... lds (16 bytes per lane, lane i writes
 // base + 16 i), so the swizzle is applied by choosing which chunk a lane fetches.
 #pragma once
@@ -29,7 +29,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 64;             // k per LDS stage
-constexpr int kRowB = kBK * 2;      // bytes per tile row per stage
+constexpr int kRowB = kBK * 2;      // bytes per tile row per stage: one 128-byte line
+constexpr int kRowsPerLoad = 1024 / kRowB;   // rows covered by one 64-lane 16-byte load
+constexpr int kKSteps = kBK / 16;   // MFMA k-steps per stage
 
 template <int BM, int BN>
 struct Tile {
@@ -38,36 +40,42 @@ struct Tile {
   static constexpr int A_BYTES = BM * kRowB;
   static constexpr int B_BYTES = BN * kRowB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LOADS_A = BM / 32;   // buffer_load_lds per wave per stage for A
-  static constexpr int LOADS_B = BN / 32;
+  static constexpr int LOADS_A = BM / kRowsPerLoad / 4;   // buffer_load_lds per wave per stage for A
+  static constexpr int LOADS_B = BN / kRowsPerLoad / 4;
   static constexpr int LOADS = LOADS_A + LOADS_B;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Issue this wave's share of one stage: `rows` rows starting at byte offset
-// `row0_off` of the buffer, k slice [k0, k0 + 64), into LDS at `lds`.
+// Slot of logical 16-byte chunk c (0..7) of tile row r. The LDS serves a
+// ds_read_b128 sixteen lanes (256 bytes, all 64 banks) at a time; the 16 rows
+// read together (same c) must land in 16 distinct 16-byte bank groups. With
+// 128-byte rows, rows of equal parity share a half of the bank space, so the
+// slot is permuted by (r >> 1) & 7.
+__device__ __forceinline__ int swz(int c, int r) { return c ^ ((r >> 1) & 7); }
+
+// Issue this wave's share of one stage: ROWS rows starting at byte offset
+// row0_off of the buffer, k slice [k0, k0 + 64), into LDS at `lds`. Each row
+// of the stage is one full 128-byte line (8 lanes x 16 bytes).
 template <int ROWS>
 __device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t r, uint32_t row0_off, uint32_t row_stride,
                                            uint32_t k0_bytes, char* lds, int wave, int lane) {
-  constexpr int PER_WAVE = ROWS / 32;  // instructions of 8 rows each
-  const int sub = lane >> 3;           // row within the 8-row instruction block
+  constexpr int PER_WAVE = ROWS / kRowsPerLoad / 4;
+  const int sub = lane >> 3;           // row within the 8-row block of one load
   const int slot = lane & 7;
-  const int chunk = slot ^ sub;        // (row & 7) == sub
 #pragma unroll
   for (int q = 0; q < PER_WAVE; ++q) {
     const int blk = wave * PER_WAVE + q;
-    const int row = blk * 8 + sub;
+    const int row = blk * kRowsPerLoad + sub;
+    const int chunk = swz(slot, row);  // the xor is its own inverse
     const uint32_t voff = row0_off + (uint32_t)row * row_stride + k0_bytes + (uint32_t)chunk * 16;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + blk * 1024), 16, voff, 0, 0, 0);
   }
 }
 
-// One 16-byte operand fragment: row `row` (multiple-of-32 base + lane % 32), k
-// chunk c (0..7) of the stage.
+// One 16-byte operand fragment: row `row`, logical k chunk c (0..7) of the stage.
 __device__ __forceinline__ bf16x8 frag_read(const char* lds, int row, int c) {
-  const int slot = c ^ (row & 7);
-  return *reinterpret_cast<const bf16x8*>(lds + row * kRowB + slot * 16);
+  return *reinterpret_cast<const bf16x8*>(lds + row * kRowB + swz(c, row) * 16);
 }
 
 template <int BM, int BN>
@@ -102,33 +110,118 @@ __device__ __forceinline__ void frags_mfma(const Frags<BM, BN>& f, Acc<BM, BN>& 
       acc.v[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc.v[fm][fn], 0, 0, 0);
 }
 
-// One LDS stage (64 k = 4 MFMA k-steps). The fragments of k-step kk+1 are
-// issued before the MFMAs of k-step kk (two fragment sets in registers), with
-// scheduling fences so the compiler keeps that order; the MFMAs of one k-step
-// write distinct accumulators and pipeline back to back.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+#define FG_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// Full K loop for one tile (K a multiple of 128, so the stage count is even).
+// rA: gathered rows (row stride K*2 bytes), a_off = byte offset of the tile's
+// first row; rB: weight rows [N][K], b_off likewise. lds0/lds1: the two stage
+// buffers (distinct objects, so the compiler can tell them apart when it places
+// its own waits).
+//
+// Stage k lives in slot k&1 and k-step 0 of its fragments is already in
+// registers when the stage starts. Per stage: read k-steps 1..3, MFMAs of
+// k-steps 0 and 1, wait for this wave's loads of stage k+1, one workgroup
+// barrier (publishes stage k+1 from every wave and retires slot k&1, whose
+// fragments are all in registers by now), refill slot k&1 with stage k+2, read
+// k-step 0 of stage k+1, MFMAs of k-steps 2 and 3. The LDS latency after the
+// barrier hides behind the last 32 MFMAs.
+// --- explicitly interleaved stage schedule -------------------------------
+// With one wave per SIMD nothing else fills the matrix pipe while a wave
+// issues memory instructions, so every LDS read and every global->LDS load is
+// issued in the shadow of one 32-cycle MFMA: the stage is a fixed sequence of
+// MFMA slots, each followed by at most one memory instruction, fenced so the
+// compiler keeps the order.
 template <int BM, int BN>
-__device__ __forceinline__ void stage_compute(const char* ldsA, const char* ldsB, Acc<BM, BN>& acc, int wm, int wn,
-                                              int lane) {
-  Frags<BM, BN> f0, f1;
-  frags_read<BM, BN>(ldsA, ldsB, f0, 0, wm, wn, lane);
+__device__ __forceinline__ void mfma_one(const Frags<BM, BN>& f, Acc<BM, BN>& acc, int i) {
+  using T = Tile<BM, BN>;
+  const int fm = i / T::FN, fn = i % T::FN;
+  acc.v[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc.v[fm][fn], 0, 0, 0);
+}
+
+// Element e of a k-step's fragment set, in the order the MFMAs consume them:
+// b[0..FN), then a[0..FM).
+template <int BM, int BN>
+__device__ __forceinline__ void frag_read_one(const char* ldsA, const char* ldsB, Frags<BM, BN>& f, int kk, int e,
+                                              int wm, int wn, int lane) {
+  using T = Tile<BM, BN>;
+  const int lr = lane & 31, kh = lane >> 5;
+  if (e < T::FN) f.b[e] = frag_read(ldsB, wn * T::WN + e * 32 + lr, kk * 2 + kh);
+  else f.a[e - T::FN] = frag_read(ldsA, wm * T::WM + (e - T::FN) * 32 + lr, kk * 2 + kh);
+}
+
+// Load q (0..LOADS) of this wave's share of a stage.
+template <int BM, int BN>
+__device__ __forceinline__ void stage_load_one(__amdgpu_buffer_rsrc_t rA, uint32_t a_off, __amdgpu_buffer_rsrc_t rB,
+                                               uint32_t b_off, uint32_t stride, uint32_t k0_bytes, char* lds,
+                                               int wave, int lane, int q) {
+  using T = Tile<BM, BN>;
+  const bool isA = q < T::LOADS_A;
+  const int blk = isA ? wave * T::LOADS_A + q : wave * T::LOADS_B + (q - T::LOADS_A);
+  const int row = blk * kRowsPerLoad + (lane >> 3);
+  const int chunk = swz(lane & 7, row);
+  const uint32_t voff = (isA ? a_off : b_off) + (uint32_t)row * stride + k0_bytes + (uint32_t)chunk * 16;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rB,
+                                           (lds_void*)(lds + (isA ? 0 : T::A_BYTES) + blk * 1024), 16, voff, 0, 0, 0);
+}
+
+// Stage k in `cur`, its k-step 0 fragments already in f0.
+//   phase A: MFMAs of k-steps 0 and 1; in their shadow the reads of k-steps
+//            1, 2, 3 (k-step 1's reads land in the first two thirds, before
+//            its MFMAs start);
+//   wait for this wave's loads of stage k+1; workgroup barrier (publishes
+//   stage k+1, retires `cur`, whose fragments are all in registers);
+//   phase B: MFMAs of k-steps 2 and 3; in their shadow the reads of k-step 0
+//            of stage k+1 (first, so they land early) and the refill of `cur`
+//            with stage k+2.
+template <int BM, int BN, bool has_next, bool refill>
+__device__ __forceinline__ void stage_body(const char* cur, const char* nxt,
+                                           Frags<BM, BN>& f0, Acc<BM, BN>& acc, int wm, int wn, int lane,
+                                           __amdgpu_buffer_rsrc_t rA, uint32_t a_off, __amdgpu_buffer_rsrc_t rB,
+                                           uint32_t b_off, uint32_t stride, uint32_t k2_bytes, char* cur_w, int wave) {
+  using T = Tile<BM, BN>;
+  constexpr int NM = T::FM * T::FN;        // MFMAs per k-step
+  constexpr int NR = T::FM + T::FN;        // fragment reads per k-step
+  constexpr int OPS_A = 3 * NR;
+  constexpr int OPS_B = NR + T::LOADS;
+  Frags<BM, BN> f1, f2, f3;
+  const char* curB = cur + T::A_BYTES;
+  // phase A
 #pragma unroll
-  for (int kk = 0; kk < kBK / 16; kk += 2) {
-    frags_read<BM, BN>(ldsA, ldsB, f1, kk + 1, wm, wn, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    frags_mfma<BM, BN>(f0, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kk + 2 < kBK / 16) frags_read<BM, BN>(ldsA, ldsB, f0, kk + 2, wm, wn, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    frags_mfma<BM, BN>(f1, acc);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int j = 0; j < 2 * NM; ++j) {
+    if (j < NM) mfma_one<BM, BN>(f0, acc, j);
+    else mfma_one<BM, BN>(f1, acc, j - NM);
+#pragma unroll
+    for (int o = (j * OPS_A) / (2 * NM); o < ((j + 1) * OPS_A) / (2 * NM); ++o) {
+      if (o < NR) frag_read_one<BM, BN>(cur, curB, f1, 1, o, wm, wn, lane);
+      else if (o < 2 * NR) frag_read_one<BM, BN>(cur, curB, f2, 2, o - NR, wm, wn, lane);
+      else frag_read_one<BM, BN>(cur, curB, f3, 3, o - 2 * NR, wm, wn, lane);
+    }
+    FG_SCHED_FENCE();
+  }
+  if constexpr (has_next) wait_vmcnt<0>();
+  __syncthreads();
+  // phase B
+#pragma unroll
+  for (int j = 0; j < 2 * NM; ++j) {
+    if (j < NM) mfma_one<BM, BN>(f2, acc, j);
+    else mfma_one<BM, BN>(f3, acc, j - NM);
+#pragma unroll
+    for (int o = (j * OPS_B) / (2 * NM); o < ((j + 1) * OPS_B) / (2 * NM); ++o) {
+      if (o < NR) {
+        if constexpr (has_next) frag_read_one<BM, BN>(nxt, nxt + T::A_BYTES, f0, 0, o, wm, wn, lane);
+      } else {
+        if constexpr (refill) stage_load_one<BM, BN>(rA, a_off, rB, b_off, stride, k2_bytes, cur_w, wave, lane, o - NR);
+      }
+    }
+    FG_SCHED_FENCE();
   }
 }
 
-// Full K loop for one tile (K a multiple of 128). rA: gathered rows (row stride
-// K*2 bytes), a_off = byte offset of the tile's first row; rB: weight rows
-// [N][K], b_off likewise. lds0/lds1: the two stage buffers. Each stage is
-// loaded one stage ahead; one workgroup barrier per stage both publishes the
-// stage just landed and retires the stage just read.
 template <int BM, int BN>
 __device__ __forceinline__ void tile_mainloop(__amdgpu_buffer_rsrc_t rA, uint32_t a_off,
                                               __amdgpu_buffer_rsrc_t rB, uint32_t b_off, int K,
@@ -141,26 +234,21 @@ __device__ __forceinline__ void tile_mainloop(__amdgpu_buffer_rsrc_t rA, uint32_
   const int nk = K / kBK;   // even
   stage_load<BM>(rA, a_off, stride, 0, lds0, wave, lane);
   stage_load<BN>(rB, b_off, stride, 0, lds0 + T::A_BYTES, wave, lane);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
   stage_load<BM>(rA, a_off, stride, kRowB, lds1, wave, lane);
   stage_load<BN>(rB, b_off, stride, kRowB, lds1 + T::A_BYTES, wave, lane);
-  for (int kt = 0; kt < nk; kt += 2) {
-    stage_compute<BM, BN>(lds0, lds0 + T::A_BYTES, acc, wm, wn, lane);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 2 < nk) {
-      stage_load<BM>(rA, a_off, stride, (uint32_t)(kt + 2) * kRowB, lds0, wave, lane);
-      stage_load<BN>(rB, b_off, stride, (uint32_t)(kt + 2) * kRowB, lds0 + T::A_BYTES, wave, lane);
-    }
-    stage_compute<BM, BN>(lds1, lds1 + T::A_BYTES, acc, wm, wn, lane);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (kt + 3 < nk) {
-      stage_load<BM>(rA, a_off, stride, (uint32_t)(kt + 3) * kRowB, lds1, wave, lane);
-      stage_load<BN>(rB, b_off, stride, (uint32_t)(kt + 3) * kRowB, lds1 + T::A_BYTES, wave, lane);
-    }
+  wait_vmcnt<T::LOADS>();
+  __syncthreads();
+  Frags<BM, BN> f0;
+  frags_read<BM, BN>(lds0, lds0 + T::A_BYTES, f0, 0, wm, wn, lane);
+  int kt = 0;
+  for (; kt < nk - 2; kt += 2) {
+    stage_body<BM, BN, true, true>(lds0, lds1, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
+                                   (uint32_t)(kt + 2) * kRowB, lds0, wave);
+    stage_body<BM, BN, true, true>(lds1, lds0, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
+                                   (uint32_t)(kt + 3) * kRowB, lds1, wave);
   }
+  stage_body<BM, BN, true, false>(lds0, lds1, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, lds0, wave);
+  stage_body<BM, BN, false, false>(lds1, lds0, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, lds1, wave);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -191,7 +279,7 @@ __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int
         v2i w;
         w[0] = pad ? 0 : (int)pack_bf16x2(c[4 * g + 0], c[4 * g + 1]);
         w[1] = pad ? 0 : (int)pack_bf16x2(c[4 * g + 2], c[4 * g + 3]);
-        __builtin_amdgcn_raw_buffer_store_b64(w, rO, row_off + (uint32_t)n * 2, 0, kPolNT);
+        __builtin_amdgcn_raw_buffer_store_b64(w, rO, row_off + (uint32_t)n * 2, 0, 0);
       }
     }
   }

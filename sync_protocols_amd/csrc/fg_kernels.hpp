@@ -4,7 +4,7 @@
 #pragma once
 
 #include "fg_gemm.hpp"
-#include "../../include/fg.h"
+#include "fg.h"
 
 namespace fg {
 
@@ -57,8 +57,43 @@ struct FusedArgs {
 // order in which the compute role consumes row blocks (§6 audit item 3); a
 // communication workgroup never waits on anything (§6 audit item 2).
 // ---------------------------------------------------------------------------
+// Copy one batch of RB gathered rows (g0 .. g0+RB-1), each at most 64*UPR
+// 16-byte vectors, branch-free: every row gets its own buffer descriptors, and
+// a padding row (or the part of a row beyond K) gets a zero-sized one, so its
+// loads read 0 and its stores are dropped by the buffer unit. All loads of the
+// batch are issued before its stores (RB*UPR vectors per lane in flight).
+template <int UPR, int RB>
+__device__ __forceinline__ void copy_batch(const FusedArgs& a, const uint16_t* const* sh_shard, int g0, int info,
+                                           int srow, uint32_t row_bytes, int lane) {
+  __amdgpu_buffer_rsrc_t rs[RB], rd[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const int rinfo = readlane(info, r);
+    const bool valid = rinfo >= 0;
+    const int s = valid ? (rinfo >> 24) : 0;
+    const int sr = readlane(srow, r);
+    const uint64_t base = (uint64_t)sh_shard[s];
+    const uint16_t* shard = (const uint16_t*)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(base >> 32)) << 32) |
+                                              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base));
+    rs[r] = buffer_rsrc(shard + (size_t)sr * a.K, valid ? row_bytes : 0u);
+    rd[r] = buffer_rsrc(a.gathered + (size_t)(g0 + r) * a.K, valid ? row_bytes : 0u);
+  }
+  v4i v[RB][UPR];
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int u = 0; u < UPR; ++u)
+      v[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rs[r], (uint32_t)(u * 64 + lane) * 16, 0, kPolNT);
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int u = 0; u < UPR; ++u)
+      store16_coherent(rd[r], (uint32_t)(u * 64 + lane) * 16, v[r][u]);
+}
+
 __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int cw = blockIdx.x;
   const bool strict = a.flags & kStrict;
 
@@ -73,10 +108,8 @@ __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
   const int m_pad = __builtin_amdgcn_readfirstlane(a.desc[0]);
   const int RB = a.rows_per_batch;
   const int n_batches = m_pad / RB;
-  const int K = a.K;
-  const int V = K / 8;                       // 16-byte vectors per row
-  const uint32_t row_bytes = (uint32_t)K * 2;
-  const __amdgpu_buffer_rsrc_t rG = buffer_rsrc(a.gathered, (uint32_t)m_pad * row_bytes);
+  const int upr = (a.K / 8 + 63) / 64;       // 64-lane units of 16 bytes per row
+  const uint32_t row_bytes = (uint32_t)a.K * 2;
   const int nw = a.n_comm * 4;
   const bool verify = a.flags & kVerify;
 
@@ -89,28 +122,12 @@ __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
       if (info >= 0) srow = a.src_row[(info >> 24) * a.rs_cap + (info & 0xFFFFFF)];
     }
     // bitwise row copy: 16-byte streaming loads, device-coherent 16-byte stores
-    for (int r = 0; r < RB; ++r) {
-      const int rinfo = readlane(info, r);
-      if (rinfo < 0) continue;   // padding row: never written
-      const int s = rinfo >> 24;
-      const int sr = readlane(srow, r);
-      const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(sh_shard[s], (uint32_t)a.shard_rows * row_bytes);
-      const uint32_t src = (uint32_t)sr * row_bytes;
-      const uint32_t dst = (uint32_t)(g0 + r) * row_bytes;
-      for (int c0 = 0; c0 < V; c0 += 64 * 8) {
-        v4i v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int c = c0 + u * 64 + lane;
-          if (c < V) v[u] = __builtin_amdgcn_raw_buffer_load_b128(rS, src + (uint32_t)c * 16, 0, kPolNT);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int c = c0 + u * 64 + lane;
-          if (c < V) store16_coherent(rG, dst + (uint32_t)c * 16, v[u]);
-        }
-      }
-    }
+    if (upr <= 1)       copy_batch<1, 16>(a, sh_shard, g0, info, srow, row_bytes, lane);
+    else if (upr <= 2)  copy_batch<2, 16>(a, sh_shard, g0, info, srow, row_bytes, lane);
+    else if (upr <= 4)  copy_batch<4, 8>(a, sh_shard, g0, info, srow, row_bytes, lane);
+    else if (upr <= 8)  copy_batch<8, 4>(a, sh_shard, g0, info, srow, row_bytes, lane);
+    else if (upr <= 16) copy_batch<16, 2>(a, sh_shard, g0, info, srow, row_bytes, lane);
+    else                copy_batch<32, 1>(a, sh_shard, g0, info, srow, row_bytes, lane);
     release_coherent(strict);
     // arrival count for the batch's row block (RB divides the row block)
     const uint64_t real = ballot(lane < RB && info >= 0);
