@@ -107,7 +107,8 @@ typedef struct {
   int32_t m_pad;              /* gathered rows, a multiple of FG_ROW_BLOCK */
   const int32_t* group_off;   /* host [n_groups+1] first gathered row of each group (NULL: one group) */
   /* TOPK */
-  const int32_t* topk;        /* device [n_shards][rows_per_shard][topk_k] chosen experts, distinct per token */
+  const int32_t* topk;        /* device [n_shards][rows_per_shard][topk_k] chosen experts, distinct per token;
+                                 rows_per_shard <= max_rows_per_shard */
   int32_t topk_k;
   int32_t expert_base;        /* this GPU owns experts [expert_base, expert_base + n_groups) */
 } fg_route;
@@ -140,7 +141,8 @@ typedef struct {
   const int32_t* elect;       /* [2][n_shards][chunk_cap] */
   const int32_t* pub_count;   /* [n_shards][chunk_cap] (VERIFY) */
   const int32_t* seed;        /* [rb_cap] */
-  const int32_t* inv_row;     /* [m_pad_cap] (shard << 24 | stream index) or -1 for padding */
+  const uint64_t* inv_row;    /* [m_pad_cap] versioned inverse map: (route_ver << 32) | (shard << 24 | stream
+                                 index); an entry with another version is a padding row */
   const int32_t* group_of_rb; /* [rb_cap] */
   const int32_t* src_row;     /* [n_shards][max_rows_per_shard] route in use */
   const int32_t* dst_row;     /* [n_shards][max_rows_per_shard] */
@@ -150,6 +152,7 @@ typedef struct {
   const int32_t* stress_slot; /* [P][C][KC] */
   const int32_t* stress_pub;  /* [P][C][KC] */
   int32_t chunk_cap, rb_cap, m_pad_cap;
+  uint32_t route_ver;         /* version of the route in use */
 } fg_views_t;
 
 /* Create a context on `hip_device`: validates the configuration, allocates and

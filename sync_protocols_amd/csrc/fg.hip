@@ -29,13 +29,16 @@ struct Plane {
   int* elect;      // [2][S * chunk_cap]
   int* pub_count;
   int* seed;
-  int* inv;
+  unsigned long long* inv;   // versioned inverse map
   int* group_of_rb;
   int* src_row;
   int* dst_row;
   int* stream_len;
   int* group_off;
   int* rbcount;
+  int* wgcount;
+  int* wgbase;
+  int* ticket;
   int* desc;
   int* err;        // [2]
   unsigned long long* stats;
@@ -61,6 +64,8 @@ struct fg_ctx {
   Plane p{};
   int* host_status = nullptr;
   int seq = 0, bseq = 0, sseq = 0, ppseq = 0;
+  uint32_t route_ver = 0;
+  int route_wg_cap = 0;
   fg_status sticky = FG_OK;
   bool stream_bound = false;
   hipStream_t stream = nullptr;
@@ -164,13 +169,30 @@ static fg_status launch_route(fg_ctx* ctx, const fg_route* route, int mode, int 
   }
   if (mode == FG_ROUTE_TOPK) { ra.topk = route->topk; ra.topk_k = route->topk_k; ra.expert_base = route->expert_base; }
   const int cur = ctx->seq & 1;
+  ctx->route_ver += 1;
+  ra.ver = ctx->route_ver;
   ra.src_row = ctx->p.src_row; ra.dst_row = ctx->p.dst_row; ra.stream_len = ctx->p.stream_len;
   ra.group_off_out = ctx->p.group_off; ra.inv = ctx->p.inv; ra.seed = ctx->p.seed;
   ra.group_of_rb = ctx->p.group_of_rb; ra.rbcount = ctx->p.rbcount;
+  ra.wgcount = ctx->p.wgcount; ra.wgbase = ctx->p.wgbase; ra.ticket = ctx->p.ticket;
   ra.counter_cur = ctx->p.counter + (size_t)cur * ctx->rb_cap;
   ra.elect_cur = ctx->p.elect + (size_t)cur * c.n_shards * ctx->chunk_cap;
   ra.desc = ctx->p.desc; ra.err = sink(ctx);
-  hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, st, ra);
+  auto blocks = [](long long work) { return (int)std::max(1LL, std::min(1024LL, (work + kRouteThreads - 1) / kRouteThreads)); };
+  if (mode == FG_ROUTE_CONTIG) {
+    const long long work = std::max<long long>({(long long)c.n_shards * rows, ctx->rb_cap,
+                                                (long long)c.n_shards * ctx->chunk_cap});
+    hipLaunchKernelGGL(route_contig_kernel, dim3(blocks(work)), dim3(kRouteThreads), 0, st, ra);
+  } else if (mode == FG_ROUTE_EXPLICIT) {
+    hipLaunchKernelGGL(route_explicit_kernel, dim3(blocks((long long)c.n_shards * c.max_rows_per_shard)),
+                       dim3(kRouteThreads), 0, st, ra);
+  } else {
+    ra.wpb = (rows + kRouteThreads - 1) / kRouteThreads;
+    const int n_wg = c.n_shards * ra.wpb;
+    hipLaunchKernelGGL(route_topk_count_kernel, dim3(n_wg), dim3(kRouteThreads), 0, st, ra);
+    HIPCHK(hipGetLastError());
+    hipLaunchKernelGGL(route_topk_place_kernel, dim3(n_wg), dim3(kRouteThreads), 0, st, ra);
+  }
   HIPCHK(hipGetLastError());
   return FG_OK;
 }
@@ -256,11 +278,14 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
   const size_t nrs = (size_t)S * cfg->max_rows_per_shard;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  ctx->route_wg_cap = S * ((cfg->max_rows_per_shard + kRouteThreads - 1) / kRouteThreads);
+  const size_t wgc = (size_t)ctx->route_wg_cap * (FG_MAX_GROUPS + 1) * 4;
   const size_t o_slot = take(nch * 4), o_counter = take(2 * (size_t)ctx->rb_cap * 4),
                o_elect = take(2 * nch * 4), o_pub = take(nch * 4), o_seed = take((size_t)ctx->rb_cap * 4),
-               o_inv = take((size_t)ctx->m_pad_cap * 4), o_grp = take((size_t)ctx->rb_cap * 4),
+               o_inv = take((size_t)ctx->m_pad_cap * 8), o_grp = take((size_t)ctx->rb_cap * 4),
                o_src = take(nrs * 4), o_dst = take(nrs * 4), o_slen = take((size_t)S * 4),
                o_goff = take((FG_MAX_GROUPS + 1) * 4), o_rbc = take((size_t)ctx->rb_cap * 4), o_desc = take(64),
+               o_wgc = take(wgc), o_wgb = take(wgc), o_tick = take(64),
                o_err = take(64), o_stats = take(ST_COUNT * 8), o_bslot = take((size_t)S * S * 4),
                o_pp = take(512), o_tdev = take(64), o_wg = take((size_t)grid_max * 32),
                o_sslot = take((size_t)ctx->s_slots * 4), o_select = take(2 * (size_t)ctx->s_slots * 4),
@@ -270,7 +295,8 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
   char* b = ctx->plane_mem;
   Plane& p = ctx->p;
   p.slot = (int*)(b + o_slot); p.counter = (int*)(b + o_counter); p.elect = (int*)(b + o_elect);
-  p.pub_count = (int*)(b + o_pub); p.seed = (int*)(b + o_seed); p.inv = (int*)(b + o_inv);
+  p.pub_count = (int*)(b + o_pub); p.seed = (int*)(b + o_seed); p.inv = (unsigned long long*)(b + o_inv);
+  p.wgcount = (int*)(b + o_wgc); p.wgbase = (int*)(b + o_wgb); p.ticket = (int*)(b + o_tick);
   p.group_of_rb = (int*)(b + o_grp); p.src_row = (int*)(b + o_src); p.dst_row = (int*)(b + o_dst);
   p.stream_len = (int*)(b + o_slen); p.group_off = (int*)(b + o_goff); p.rbcount = (int*)(b + o_rbc);
   p.desc = (int*)(b + o_desc); p.err = (int*)(b + o_err); p.stats = (unsigned long long*)(b + o_stats);
@@ -329,7 +355,7 @@ fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route*
   } else if (mode == FG_ROUTE_TOPK) {
     if (!route->topk || route->topk_k < 1 || route->topk_k > 64) return FG_EINVAL;
     rows = route->rows_per_shard;
-    if (rows < 1 || (long long)rows * c.n_shards > (1 << 20)) return FG_EINVAL;
+    if (rows < 1 || rows > c.max_rows_per_shard) return FG_EINVAL;
     if (c.n_groups < 1) return FG_EINVAL;
   } else {
     return FG_EINVAL;
@@ -374,7 +400,8 @@ fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route*
   a.counter_nxt = ctx->p.counter + (size_t)nxt * ctx->rb_cap;
   a.elect_cur = ctx->p.elect + (size_t)cur * c.n_shards * ctx->chunk_cap;
   a.elect_nxt = ctx->p.elect + (size_t)nxt * c.n_shards * ctx->chunk_cap;
-  a.pub_count = ctx->p.pub_count; a.seed = ctx->p.seed; a.inv = ctx->p.inv; a.group_of_rb = ctx->p.group_of_rb;
+  a.pub_count = ctx->p.pub_count; a.seed = ctx->p.seed; a.inv = ctx->p.inv; a.route_ver = ctx->route_ver;
+  a.group_of_rb = ctx->p.group_of_rb;
   a.src_row = ctx->p.src_row; a.stream_len = ctx->p.stream_len; a.desc = ctx->p.desc; a.stats = ctx->p.stats;
   a.wgtime = ctx->p.wgtime; a.err = sink(ctx); a.seq = ctx->seq;
   a.n_comm = ctx->n_comm; a.n_gemm = ctx->n_gemm;
@@ -450,7 +477,7 @@ fg_status fg_stress(fg_ctx* ctx, const int32_t* chunk_rows, const int32_t* delay
   a.P = ctx->cfg.stress_producers; a.C = ctx->cfg.stress_consumers; a.KC = ctx->cfg.stress_max_chunks;
   a.seq = ctx->sseq; a.flags = flags; a.timeout_ticks = timeout_ticks(ctx);
   a.payload_bytes = (uint32_t)((size_t)ctx->s_slots * FG_CHUNK_ROWS * 4);
-  hipLaunchKernelGGL(stress_kernel, dim3(a.P + a.C), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(stress_kernel, dim3(a.P + a.C), dim3(kStressThreads), 0, stream, a);
   HIPCHK(hipGetLastError());
   return FG_OK;
 }
@@ -510,7 +537,7 @@ fg_status fg_views(fg_ctx* ctx, fg_views_t* v) {
   if (!ctx || !v) return FG_EINVAL;
   const Plane& p = ctx->p;
   v->slot = p.slot; v->counter = p.counter; v->elect = p.elect; v->pub_count = p.pub_count; v->seed = p.seed;
-  v->inv_row = p.inv; v->group_of_rb = p.group_of_rb; v->src_row = p.src_row; v->dst_row = p.dst_row;
+  v->inv_row = (const uint64_t*)p.inv; v->route_ver = ctx->route_ver; v->group_of_rb = p.group_of_rb; v->src_row = p.src_row; v->dst_row = p.dst_row;
   v->stream_len = p.stream_len; v->group_off = p.group_off; v->bslot = p.bslot; v->stress_slot = p.s_slot;
   v->stress_pub = p.s_pub;
   v->chunk_cap = ctx->chunk_cap; v->rb_cap = ctx->rb_cap; v->m_pad_cap = ctx->m_pad_cap;

@@ -5,7 +5,7 @@
 //   out[m][n] = sum_k A[m][k] * W[k][n],  A = gathered rows (bf16, K contiguous),
 //   W stored as [N][K] (K contiguous), fp32 accumulation, bf16 RNE output.
 //
-// Tile BM x BN, four waves as 2 x 2, each wave (BM/2) x (BN/2) built from
+// Tile BM x BN, eight waves as 2 x 4 (two per SIMD), each wave (BM/2) x (BN/4) built from
 // v_mfma_f32_32x32x16_bf16 fragments. The weight tile is the MFMA "A" operand
 // and the gathered tile the "B" operand, so that each lane's four consecutive
 // accumulator values are four consecutive output columns of one row (8-byte
@@ -33,16 +33,22 @@ constexpr int kRowB = kBK * 2;      // bytes per tile row per stage: one 128-byt
 constexpr int kRowsPerLoad = 1024 / kRowB;   // rows covered by one 64-lane 16-byte load
 constexpr int kKSteps = kBK / 16;   // MFMA k-steps per stage
 
+constexpr int kWaves = 8;           // waves per workgroup: two per SIMD, so one wave's memory
+                                    // instructions issue while the other's MFMAs run
+
 template <int BM, int BN>
 struct Tile {
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int WGN = kWaves == 8 ? 4 : 2;     // waves along n
+  static constexpr int WGM = kWaves / WGN;            // waves along m
+  static constexpr int WM = BM / WGM, WN = BN / WGN;  // per-wave tile
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int A_BYTES = BM * kRowB;
   static constexpr int B_BYTES = BN * kRowB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LOADS_A = BM / kRowsPerLoad / 4;   // buffer_load_lds per wave per stage for A
-  static constexpr int LOADS_B = BN / kRowsPerLoad / 4;
+  static constexpr int LOADS_A = BM / kRowsPerLoad / kWaves;   // buffer_load_lds per wave per stage for A
+  static constexpr int LOADS_B = BN / kRowsPerLoad / kWaves;
   static constexpr int LOADS = LOADS_A + LOADS_B;
+  static_assert(FM >= 1 && FN >= 1 && LOADS_A >= 1 && LOADS_B >= 1, "tile too small for the wave layout");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -60,7 +66,7 @@ __device__ __forceinline__ int swz(int c, int r) { return c ^ ((r >> 1) & 7); }
 template <int ROWS>
 __device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t r, uint32_t row0_off, uint32_t row_stride,
                                            uint32_t k0_bytes, char* lds, int wave, int lane) {
-  constexpr int PER_WAVE = ROWS / kRowsPerLoad / 4;
+  constexpr int PER_WAVE = ROWS / kRowsPerLoad / kWaves;
   const int sub = lane >> 3;           // row within the 8-row block of one load
   const int slot = lane & 7;
 #pragma unroll
@@ -68,8 +74,8 @@ __device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t r, uint32_t ro
     const int blk = wave * PER_WAVE + q;
     const int row = blk * kRowsPerLoad + sub;
     const int chunk = swz(slot, row);  // the xor is its own inverse
-    const uint32_t voff = row0_off + (uint32_t)row * row_stride + k0_bytes + (uint32_t)chunk * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + blk * 1024), 16, voff, 0, 0, 0);
+    const uint32_t voff = row0_off + (uint32_t)row * row_stride + (uint32_t)chunk * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + blk * 1024), 16, voff, k0_bytes, 0, 0);
   }
 }
 
@@ -154,7 +160,8 @@ __device__ __forceinline__ void frag_read_one(const char* ldsA, const char* ldsB
   else f.a[e - T::FN] = frag_read(ldsA, wm * T::WM + (e - T::FN) * 32 + lr, kk * 2 + kh);
 }
 
-// Load q (0..LOADS) of this wave's share of a stage.
+// Load q (0..LOADS) of this wave's share of a stage; the stage's k offset is
+// the scalar offset of the buffer instruction.
 template <int BM, int BN>
 __device__ __forceinline__ void stage_load_one(__amdgpu_buffer_rsrc_t rA, uint32_t a_off, __amdgpu_buffer_rsrc_t rB,
                                                uint32_t b_off, uint32_t stride, uint32_t k0_bytes, char* lds,
@@ -164,20 +171,19 @@ __device__ __forceinline__ void stage_load_one(__amdgpu_buffer_rsrc_t rA, uint32
   const int blk = isA ? wave * T::LOADS_A + q : wave * T::LOADS_B + (q - T::LOADS_A);
   const int row = blk * kRowsPerLoad + (lane >> 3);
   const int chunk = swz(lane & 7, row);
-  const uint32_t voff = (isA ? a_off : b_off) + (uint32_t)row * stride + k0_bytes + (uint32_t)chunk * 16;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rB,
-                                           (lds_void*)(lds + (isA ? 0 : T::A_BYTES) + blk * 1024), 16, voff, 0, 0, 0);
+  const uint32_t voff = (isA ? a_off : b_off) + (uint32_t)row * stride + (uint32_t)chunk * 16;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rB, (lds_void*)(lds + (isA ? 0 : T::A_BYTES) + blk * 1024),
+                                           16, voff, k0_bytes, 0, 0);
 }
 
 // Stage k in `cur`, its k-step 0 fragments already in f0.
-//   phase A: MFMAs of k-steps 0 and 1; in their shadow the reads of k-steps
-//            1, 2, 3 (k-step 1's reads land in the first two thirds, before
-//            its MFMAs start);
+//   phase A: MFMAs of k-steps 0, 1, 2; the reads of k-step s+1 are issued in
+//            the shadow of k-step s's MFMAs (two fragment sets live at a time);
 //   wait for this wave's loads of stage k+1; workgroup barrier (publishes
-//   stage k+1, retires `cur`, whose fragments are all in registers);
-//   phase B: MFMAs of k-steps 2 and 3; in their shadow the reads of k-step 0
-//            of stage k+1 (first, so they land early) and the refill of `cur`
-//            with stage k+2.
+//   stage k+1 from every wave and retires `cur`: all of its fragments are in
+//   registers now);
+//   phase B: MFMAs of k-step 3; in their shadow the reads of k-step 0 of stage
+//            k+1 and the refill of `cur` with stage k+2.
 template <int BM, int BN, bool has_next, bool refill>
 __device__ __forceinline__ void stage_body(const char* cur, const char* nxt,
                                            Frags<BM, BN>& f0, Acc<BM, BN>& acc, int wm, int wn, int lane,
@@ -186,32 +192,41 @@ __device__ __forceinline__ void stage_body(const char* cur, const char* nxt,
   using T = Tile<BM, BN>;
   constexpr int NM = T::FM * T::FN;        // MFMAs per k-step
   constexpr int NR = T::FM + T::FN;        // fragment reads per k-step
-  constexpr int OPS_A = 3 * NR;
   constexpr int OPS_B = NR + T::LOADS;
-  Frags<BM, BN> f1, f2, f3;
   const char* curB = cur + T::A_BYTES;
-  // phase A
+  Frags<BM, BN> f1, f2, f3;
+  // phase A, k-step 0 (reads k-step 1)
 #pragma unroll
-  for (int j = 0; j < 2 * NM; ++j) {
-    if (j < NM) mfma_one<BM, BN>(f0, acc, j);
-    else mfma_one<BM, BN>(f1, acc, j - NM);
+  for (int j = 0; j < NM; ++j) {
+    mfma_one<BM, BN>(f0, acc, j);
 #pragma unroll
-    for (int o = (j * OPS_A) / (2 * NM); o < ((j + 1) * OPS_A) / (2 * NM); ++o) {
-      if (o < NR) frag_read_one<BM, BN>(cur, curB, f1, 1, o, wm, wn, lane);
-      else if (o < 2 * NR) frag_read_one<BM, BN>(cur, curB, f2, 2, o - NR, wm, wn, lane);
-      else frag_read_one<BM, BN>(cur, curB, f3, 3, o - 2 * NR, wm, wn, lane);
-    }
+    for (int o = (j * NR) / NM; o < ((j + 1) * NR) / NM; ++o) frag_read_one<BM, BN>(cur, curB, f1, 1, o, wm, wn, lane);
+    FG_SCHED_FENCE();
+  }
+  // k-step 1 (reads k-step 2)
+#pragma unroll
+  for (int j = 0; j < NM; ++j) {
+    mfma_one<BM, BN>(f1, acc, j);
+#pragma unroll
+    for (int o = (j * NR) / NM; o < ((j + 1) * NR) / NM; ++o) frag_read_one<BM, BN>(cur, curB, f2, 2, o, wm, wn, lane);
+    FG_SCHED_FENCE();
+  }
+  // k-step 2 (reads k-step 3)
+#pragma unroll
+  for (int j = 0; j < NM; ++j) {
+    mfma_one<BM, BN>(f2, acc, j);
+#pragma unroll
+    for (int o = (j * NR) / NM; o < ((j + 1) * NR) / NM; ++o) frag_read_one<BM, BN>(cur, curB, f3, 3, o, wm, wn, lane);
     FG_SCHED_FENCE();
   }
   if constexpr (has_next) wait_vmcnt<0>();
   __syncthreads();
-  // phase B
+  // phase B, k-step 3 (reads k-step 0 of stage k+1, refills `cur` with stage k+2)
 #pragma unroll
-  for (int j = 0; j < 2 * NM; ++j) {
-    if (j < NM) mfma_one<BM, BN>(f2, acc, j);
-    else mfma_one<BM, BN>(f3, acc, j - NM);
+  for (int j = 0; j < NM; ++j) {
+    mfma_one<BM, BN>(f3, acc, j);
 #pragma unroll
-    for (int o = (j * OPS_B) / (2 * NM); o < ((j + 1) * OPS_B) / (2 * NM); ++o) {
+    for (int o = (j * OPS_B) / NM; o < ((j + 1) * OPS_B) / NM; ++o) {
       if (o < NR) {
         if constexpr (has_next) frag_read_one<BM, BN>(nxt, nxt + T::A_BYTES, f0, 0, o, wm, wn, lane);
       } else {
@@ -229,7 +244,7 @@ __device__ __forceinline__ void tile_mainloop(__amdgpu_buffer_rsrc_t rA, uint32_
   using T = Tile<BM, BN>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / T::WGN, wn = wave % T::WGN;
   const uint32_t stride = (uint32_t)K * 2;
   const int nk = K / kBK;   // even
   stage_load<BM>(rA, a_off, stride, 0, lds0, wave, lane);
@@ -256,19 +271,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
 }
 
-// Store the tile: rows whose pad mask bit is set are written as zeros.
+// Store the tile: padding rows (no current inverse-map entry) are written as zeros.
 // rO: output rows [*, N] (row stride N*2 bytes); m0, n0: tile origin.
 template <int BM, int BN>
 __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int m0, int n0,
-                                           const Acc<BM, BN>& acc, const int* pad_rows_info) {
+                                           const Acc<BM, BN>& acc, const unsigned long long* inv, uint32_t ver) {
   using T = Tile<BM, BN>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / T::WGN, wn = wave % T::WGN;
   const int lr = lane & 31, kh = lane >> 5;
 #pragma unroll
   for (int fm = 0; fm < T::FM; ++fm) {
     const int m = m0 + wm * T::WM + fm * 32 + lr;
-    const bool pad = pad_rows_info[m] < 0;
+    const bool pad = (uint32_t)(inv[m] >> 32) != ver;   // versioned inverse map: stale = padding
     const uint32_t row_off = (uint32_t)m * (uint32_t)N * 2;
 #pragma unroll
     for (int fn = 0; fn < T::FN; ++fn) {

@@ -10,7 +10,7 @@ namespace fg {
 
 constexpr int kChunk = FG_CHUNK_ROWS;
 constexpr int kRB = FG_ROW_BLOCK;
-constexpr int kThreads = 256;
+constexpr int kThreads = 64 * kWaves;   // workgroup size of the fused kernel
 
 // per-call flag bits as seen by the device
 constexpr uint32_t kCommOnly = FG_CALL_COMM_ONLY;
@@ -21,6 +21,15 @@ constexpr uint32_t kDropPublish = FG_FAULT_DROP_PUBLISH;
 
 // Device statistics block (int64 counters, cumulative).
 enum { ST_PUBLISHES = 0, ST_GATE_POLLS, ST_SLOT_POLLS, ST_GATE_PASSES, ST_STALE, ST_COUNT };
+
+// Versioned inverse map: entry = (route version << 32) | (shard << 24 | stream index).
+__device__ __forceinline__ unsigned long long inv_pack(uint32_t ver, int v) {
+  return ((unsigned long long)ver << 32) | (uint32_t)v;
+}
+__device__ __forceinline__ int inv_read(const unsigned long long* inv, int g, uint32_t ver) {
+  const unsigned long long e = inv[g];
+  return (uint32_t)(e >> 32) == ver ? (int)(uint32_t)e : -1;
+}
 
 struct FusedArgs {
   const uint16_t* shards[FG_MAX_SHARDS];
@@ -36,7 +45,8 @@ struct FusedArgs {
   int* elect_nxt;
   int* pub_count;
   const int* seed;
-  const int* inv;
+  const unsigned long long* inv;   // versioned inverse map
+  uint32_t route_ver;
   const int* group_of_rb;
   const int* src_row;
   const int* stream_len;
@@ -110,15 +120,15 @@ __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
   const int n_batches = m_pad / RB;
   const int upr = (a.K / 8 + 63) / 64;       // 64-lane units of 16 bytes per row
   const uint32_t row_bytes = (uint32_t)a.K * 2;
-  const int nw = a.n_comm * 4;
+  const int nw = a.n_comm * kWaves;
   const bool verify = a.flags & kVerify;
 
-  for (int b = cw * 4 + wave; b < n_batches; b += nw) {
+  for (int b = cw * kWaves + wave; b < n_batches; b += nw) {
     const int g0 = b * RB;
     // lane r < RB describes gathered row g0 + r
     int info = -1, srow = 0;
     if (lane < RB) {
-      info = a.inv[g0 + lane];
+      info = inv_read(a.inv, g0 + lane, a.route_ver);
       if (info >= 0) srow = a.src_row[(info >> 24) * a.rs_cap + (info & 0xFFFFFF)];
     }
     // bitwise row copy: 16-byte streaming loads, device-coherent 16-byte stores
@@ -213,7 +223,7 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh_fl
 #pragma unroll
       for (int j = 0; j < Tile<BM, BN>::FN; ++j) acc.v[i][j] = f32x16{};
     tile_mainloop<BM, BN>(rA, (uint32_t)m0 * row_bytes, rB, (uint32_t)n0 * row_bytes, a.K, lds0, lds1, acc);
-    tile_store<BM, BN>(rO, a.N, m0, n0, acc, a.inv);
+    tile_store<BM, BN>(rO, a.N, m0, n0, acc, a.inv, a.route_ver);
     if (threadIdx.x == 0) ++*tiles_done;
   }
 }
@@ -244,14 +254,20 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Layout step (step a1). Single workgroup of 1024 threads; phases separated by
-// workgroup barriers. Writes the route tables, the inverse map, the padding
-// seeds and arms the current parity (counters = seed, election counts = 0).
+// Layout step (step a1): the route tables, the inverse map gathered row ->
+// (shard, stream index), the padding seed of every row block, and the arming
+// of the current parity (counters = seed, election counts = 0).
+//
+// The inverse map is versioned: entry = (route version << 32) | value, and an
+// entry whose version is not the current one reads as a padding row, so no
+// pass clears it between routes. Work that needs every workgroup's result is
+// done by the last workgroup to finish (agent-scope release by each, acquire
+// by the last), which also resets the shared scratch for the next call.
 // ---------------------------------------------------------------------------
 struct RouteArgs {
   int mode;                  // FG_ROUTE_*
   int n_shards, rs_cap, chunk_cap, rb_cap, m_pad_cap;
-  int rows_per_shard;        // CONTIG / TOPK
+  int rows_per_shard;        // CONTIG / EXPLICIT: rows of every shard; TOPK: tokens of every shard
   int m_pad;                 // CONTIG / EXPLICIT
   int n_groups;
   int group_off[FG_MAX_GROUPS + 1];   // EXPLICIT (host-given)
@@ -260,52 +276,50 @@ struct RouteArgs {
   const int* dst_in;
   const int* topk;           // TOPK device [S][T][KK]
   int topk_k, expert_base;
+  int wpb;                   // TOPK: workgroups per shard
+  uint32_t ver;              // route version stamped into the inverse map
   int* src_row;
   int* dst_row;
   int* stream_len;
   int* group_off_out;
-  int* inv;
+  unsigned long long* inv;
   int* seed;
   int* group_of_rb;
-  int* rbcount;
+  int* rbcount;              // EXPLICIT: real rows per row block (zero between calls)
   int* counter_cur;
   int* elect_cur;
   int* desc;
+  int* wgcount;              // TOPK: [n_wg][E + 1] per-workgroup expert counts, picks
+  int* wgbase;               // TOPK: [n_wg][E + 1] expert row bases, stream base
+  int* ticket;               // [0] last-workgroup ticket, [1] failure flag (zero between calls)
   ErrorSink err;
 };
 
-constexpr int kRouteThreads = 1024;
+constexpr int kRouteThreads = 256;
 
-__device__ int block_exclusive_scan(int v, int* sh, int* total) {
-  // sh: >= 32 ints of LDS scratch (16 waves)
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) sh[wave] = x;
+
+// True in every thread of the workgroup that finishes last.
+__device__ bool last_workgroup(int* ticket, int* sh) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < kRouteThreads / 64; ++w) { const int t = sh[w]; sh[w] = run; run += t; }
-    sh[16] = run;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int t = atomicAdd(ticket, 1);
+    *sh = (t == (int)gridDim.x - 1);
   }
   __syncthreads();
-  const int r = sh[wave] + x - v;
-  *total = sh[16];
-  __syncthreads();
-  return r;
+  const bool last = *sh;
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
 }
 
-__device__ void route_finish(const RouteArgs& a, int m_pad, const int* goff, int n_groups) {
-  // seeds, group of each row block, arming of the current parity
+// Seeds, group of each row block, arming; real(rb) gives the real rows of rb.
+template <class Real>
+__device__ void route_finish(const RouteArgs& a, int m_pad, const int* goff, int n_groups, Real real) {
   const int n_rb = m_pad / kRB;
-  for (int rb = threadIdx.x; rb < a.rb_cap; rb += kRouteThreads) {
+  for (int rb = threadIdx.x; rb < a.rb_cap; rb += blockDim.x) {
     int sd = 0, g = 0;
     if (rb < n_rb) {
-      sd = kRB - __hip_atomic_load(a.rbcount + rb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sd = kRB - real(rb);
       for (int j = 0; j < n_groups; ++j)
         if (rb * kRB >= goff[j] && rb * kRB < goff[j + 1]) g = j;
     }
@@ -313,124 +327,208 @@ __device__ void route_finish(const RouteArgs& a, int m_pad, const int* goff, int
     a.group_of_rb[rb] = g;
     a.counter_cur[rb] = sd;
   }
-  for (int i = threadIdx.x; i < a.n_shards * a.chunk_cap; i += kRouteThreads) a.elect_cur[i] = 0;
-  if (threadIdx.x <= n_groups) a.group_off_out[threadIdx.x] = goff[threadIdx.x];
+  for (int i = threadIdx.x; i < a.n_shards * a.chunk_cap; i += blockDim.x) a.elect_cur[i] = 0;
+  if ((int)threadIdx.x <= n_groups) a.group_off_out[threadIdx.x] = goff[threadIdx.x];
   if (threadIdx.x == 0) a.desc[0] = m_pad;
 }
 
-__device__ __forceinline__ bool is_local(int e, int E) { return e >= 0 && e < E; }
+// CONTIG: shard s row i -> gathered row s*R + i; everything is arithmetic, so
+// every thread works independently.
+__global__ __launch_bounds__(kRouteThreads) void route_contig_kernel(RouteArgs a) {
+  const int R = a.rows_per_shard, M = a.n_shards * R, m_pad = a.m_pad;
+  const int tid = blockIdx.x * blockDim.x + threadIdx.x, nth = gridDim.x * blockDim.x;
+  for (int g = tid; g < M; g += nth) {
+    const int s = g / R, i = g - s * R;
+    a.inv[g] = inv_pack(a.ver, (s << 24) | i);
+    a.src_row[s * a.rs_cap + i] = i;
+    a.dst_row[s * a.rs_cap + i] = g;
+  }
+  const int n_rb = m_pad / kRB;
+  for (int rb = tid; rb < a.rb_cap; rb += nth) {
+    const int real = rb < n_rb ? min(kRB, max(0, M - rb * kRB)) : kRB;
+    const int sd = kRB - real;
+    a.seed[rb] = sd;
+    a.group_of_rb[rb] = 0;
+    a.counter_cur[rb] = sd;
+  }
+  for (int i = tid; i < a.n_shards * a.chunk_cap; i += nth) a.elect_cur[i] = 0;
+  if (tid < a.n_shards) a.stream_len[tid] = R;
+  if (tid == 0) { a.group_off_out[0] = 0; a.group_off_out[1] = m_pad; a.desc[0] = m_pad; }
+}
 
-__global__ __launch_bounds__(kRouteThreads, 1) void route_kernel(RouteArgs a) {
-  __shared__ int sh[64];
+// EXPLICIT: one thread per stream entry; the last workgroup computes the seeds.
+__global__ __launch_bounds__(kRouteThreads) void route_explicit_kernel(RouteArgs a) {
+  __shared__ int sh_last;
+  __shared__ int sh_goff[FG_MAX_GROUPS + 1];
+  const int tid = blockIdx.x * blockDim.x + threadIdx.x, nth = gridDim.x * blockDim.x;
+  for (int f = tid; f < a.n_shards * a.rs_cap; f += nth) {
+    const int s = f / a.rs_cap, i = f - s * a.rs_cap;
+    if (i >= a.stream_len_in[s]) continue;
+    const int src = a.src_in[f], dst = a.dst_in[f];
+    if (dst < 0 || dst >= a.m_pad || src < 0 || src >= a.rows_per_shard) {
+      raise_error(a.err, kErrProtocol, 0x20000000 | s);
+      atomicOr(a.ticket + 1, 1);
+      continue;
+    }
+    a.src_row[f] = src;
+    a.dst_row[f] = dst;
+    const unsigned long long old = atomicExch(a.inv + dst, inv_pack(a.ver, (s << 24) | i));
+    if ((uint32_t)(old >> 32) == a.ver) {
+      raise_error(a.err, kErrProtocol, 0x30000000 | dst);
+      atomicOr(a.ticket + 1, 1);
+    }
+    atomicAdd(a.rbcount + dst / kRB, 1);
+  }
+  if (!last_workgroup(a.ticket, &sh_last)) return;
+  if ((int)threadIdx.x <= a.n_groups) sh_goff[threadIdx.x] = a.group_off[threadIdx.x];
+  if ((int)threadIdx.x < a.n_shards) a.stream_len[threadIdx.x] = a.stream_len_in[threadIdx.x];
+  __syncthreads();
+  const int fail = __hip_atomic_load(a.ticket + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  route_finish(a, fail ? 0 : a.m_pad, sh_goff, a.n_groups, [&](int rb) {
+    return __hip_atomic_load(a.rbcount + rb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  });
+  __syncthreads();
+  for (int rb = threadIdx.x; rb < a.rb_cap; rb += blockDim.x) a.rbcount[rb] = 0;
+  if (threadIdx.x == 0) { a.ticket[0] = 0; a.ticket[1] = 0; }
+}
+
+// TOPK, pass 1: per workgroup (a range of 256 tokens of one shard) the number
+// of tokens choosing each local expert and the number of local pairs; the last
+// workgroup scans them in global token order into expert row bases and stream
+// bases ("DeepEP FIFO pipeline" dispatch notify stage: counts fix the offsets),
+// the group offsets (each expert padded to a multiple of 128 rows) and seeds.
+__global__ __launch_bounds__(kRouteThreads) void route_topk_count_kernel(RouteArgs a) {
+  __shared__ int sh_cnt[FG_MAX_GROUPS + 1];
+  __shared__ int sh_last;
   __shared__ int sh_goff[FG_MAX_GROUPS + 1];
   __shared__ int sh_ne[FG_MAX_GROUPS];
-  __shared__ int sh_shard_base[FG_MAX_SHARDS + 1];
-  __shared__ int sh_fail;
-  const int tid = threadIdx.x;
-  if (tid == 0) sh_fail = 0;
-  for (int g = tid; g < a.m_pad_cap; g += kRouteThreads) a.inv[g] = -1;
-  for (int rb = tid; rb < a.rb_cap; rb += kRouteThreads) a.rbcount[rb] = 0;
-  if (a.mode == FG_ROUTE_CONTIG || a.mode == FG_ROUTE_EXPLICIT) {
-    const int m_pad = a.m_pad;
-    if (tid <= a.n_groups) sh_goff[tid] = (a.mode == FG_ROUTE_CONTIG) ? (tid == 0 ? 0 : m_pad) : a.group_off[tid];
-    __syncthreads();
-    for (int s = 0; s < a.n_shards; ++s) {
-      const int n = (a.mode == FG_ROUTE_CONTIG) ? a.rows_per_shard : a.stream_len_in[s];
-      if (tid == 0) a.stream_len[s] = n;
-      for (int i = tid; i < n; i += kRouteThreads) {
-        int src, dst;
-        if (a.mode == FG_ROUTE_CONTIG) { src = i; dst = s * a.rows_per_shard + i; }
-        else { src = a.src_in[s * a.rs_cap + i]; dst = a.dst_in[s * a.rs_cap + i]; }
-        if (dst < 0 || dst >= m_pad || src < 0 || src >= a.rows_per_shard) {
-          raise_error(a.err, kErrProtocol, 0x20000000 | s);
-          sh_fail = 1;
-          continue;
-        }
-        a.src_row[s * a.rs_cap + i] = src;
-        a.dst_row[s * a.rs_cap + i] = dst;
-        const int old = atomicExch(a.inv + dst, (s << 24) | i);
-        if (old != -1) { raise_error(a.err, kErrProtocol, 0x30000000 | dst); sh_fail = 1; }
-        atomicAdd(a.rbcount + dst / kRB, 1);
+  const int E = a.n_groups, KK = a.topk_k, T = a.rows_per_shard;
+  const int w = blockIdx.x, s = w / a.wpb, t = (w - s * a.wpb) * kRouteThreads + threadIdx.x;
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) sh_cnt[e] = 0;
+  __syncthreads();
+  if (t < T) {
+    const int* tk = a.topk + ((size_t)s * T + t) * KK;
+    unsigned long long mask = 0;
+    int picks = 0;
+    for (int k = 0; k < KK; ++k) {
+      const int e = tk[k] - a.expert_base;
+      if (e < 0 || e >= E) continue;
+      if ((mask >> e) & 1ull) {   // one token routed twice to one expert: not a valid top-k
+        raise_error(a.err, kErrProtocol, 0x48000000 | s);
+        atomicOr(a.ticket + 1, 1);
+        continue;
       }
+      mask |= 1ull << e;
+      ++picks;
+      atomicAdd(sh_cnt + e, 1);
     }
-    __syncthreads();
-    route_finish(a, sh_fail ? 0 : m_pad, sh_goff, a.n_groups);
-    return;
-  }
-  // ---- TOPK: expert-dispatch layout. Token g = s*T + t is handled by thread
-  // g / per; each thread walks its tokens in order, so every count below is an
-  // exclusive prefix in global token order.
-  const int S = a.n_shards, T = a.rows_per_shard, KK = a.topk_k, E = a.n_groups;
-  const int G = S * T;
-  const int per = (G + kRouteThreads - 1) / kRouteThreads;
-  const int g_lo = min(G, tid * per), g_hi = min(G, g_lo + per);
-  int picks = 0;
-  for (int g = g_lo; g < g_hi; ++g)
-    for (int k = 0; k < KK; ++k) picks += is_local(a.topk[(size_t)g * KK + k] - a.expert_base, E);
-  int total_pairs;
-  const int pick_base = block_exclusive_scan(picks, sh, &total_pairs);
-  {
-    int run = pick_base;
-    for (int g = g_lo; g < g_hi; ++g) {
-      if (g % T == 0) sh_shard_base[g / T] = run;
-      for (int k = 0; k < KK; ++k) run += is_local(a.topk[(size_t)g * KK + k] - a.expert_base, E);
-    }
-    if (tid == 0) sh_shard_base[S] = total_pairs;
+    atomicAdd(sh_cnt + E, picks);
   }
   __syncthreads();
-  if (tid < S) {
-    const int n = sh_shard_base[tid + 1] - sh_shard_base[tid];
-    a.stream_len[tid] = n;
-    if (n > a.rs_cap) { raise_error(a.err, kErrProtocol, 0x40000000 | tid); sh_fail = 1; }
-  }
-  if (tid == 0) sh_goff[0] = 0;
-  __syncthreads();
-  const bool cap_fail = sh_fail;
-  int off = 0;
-  for (int e = 0; e < E; ++e) {
-    int c = 0;
-    for (int g = g_lo; g < g_hi; ++g)
-      for (int k = 0; k < KK; ++k) c += (a.topk[(size_t)g * KK + k] - a.expert_base == e);
-    int n_e;
-    int rank = block_exclusive_scan(c, sh, &n_e);
-    const int seg = ((n_e + kRB - 1) / kRB) * kRB;
-    const bool overflow = off + seg > a.m_pad_cap;   // uniform across the block
-    if (overflow && tid == 0) raise_error(a.err, kErrProtocol, 0x50000000 | e);
-    if (!overflow && !cap_fail) {
-      int run_pick = pick_base;   // stream index (global) of the next local pair
-      for (int g = g_lo; g < g_hi; ++g) {
-        const int s = g / T, t = g - s * T;
-        for (int k = 0; k < KK; ++k) {
-          const int ek = a.topk[(size_t)g * KK + k] - a.expert_base;
-          if (!is_local(ek, E)) continue;
-          if (ek == e) {
-            const int i = run_pick - sh_shard_base[s];
-            const int dst = off + rank;
-            ++rank;
-            a.src_row[s * a.rs_cap + i] = t;
-            a.dst_row[s * a.rs_cap + i] = dst;
-            a.inv[dst] = (s << 24) | i;
-          }
-          ++run_pick;
-        }
-      }
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) a.wgcount[w * (E + 1) + e] = sh_cnt[e];
+  if (!last_workgroup(a.ticket, &sh_last)) return;
+  const int n_wg = gridDim.x;
+  // expert e: running row base in global token order (workgroup order)
+  if ((int)threadIdx.x < E) {
+    const int e = threadIdx.x;
+    int run = 0;
+    for (int v = 0; v < n_wg; ++v) {
+      a.wgbase[v * (E + 1) + e] = run;          // relative to the expert's offset, fixed below
+      run += a.wgcount[v * (E + 1) + e];
     }
-    if (tid == 0) { sh_ne[e] = n_e; sh_goff[e + 1] = off + seg; }
-    off += seg;
-    if (overflow) { if (tid == 0) sh_fail = 1; break; }
+    sh_ne[e] = run;
+  }
+  if ((int)threadIdx.x < a.n_shards) {
+    const int sh = threadIdx.x;
+    int run = 0;
+    for (int v = sh * a.wpb; v < (sh + 1) * a.wpb; ++v) {
+      a.wgbase[v * (E + 1) + E] = run;
+      run += a.wgcount[v * (E + 1) + E];
+    }
+    a.stream_len[sh] = run;
+    if (run > a.rs_cap) { raise_error(a.err, kErrProtocol, 0x40000000 | sh); atomicOr(a.ticket + 1, 1); }
   }
   __syncthreads();
-  const int m_pad = sh_fail ? 0 : off;
-  // real rows per row block: expert j's n_j real rows open its segment
-  for (int rb = tid; rb < m_pad / kRB; rb += kRouteThreads) {
+  if (threadIdx.x == 0) {
+    int off = 0;
+    sh_goff[0] = 0;
+    for (int e = 0; e < E; ++e) {
+      off += ((sh_ne[e] + kRB - 1) / kRB) * kRB;
+      sh_goff[e + 1] = off;
+    }
+    if (off > a.m_pad_cap) { raise_error(a.err, kErrProtocol, 0x50000000); atomicOr(a.ticket + 1, 1); }
+  }
+  __syncthreads();
+  for (int f = threadIdx.x; f < n_wg * E; f += blockDim.x) {
+    const int v = f / E, e = f - v * E;
+    a.wgbase[v * (E + 1) + e] += sh_goff[e];
+  }
+  const int fail = __hip_atomic_load(a.ticket + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  route_finish(a, fail ? 0 : sh_goff[E], sh_goff, E, [&](int rb) {
     int real = 0;
     for (int j = 0; j < E; ++j)
-      if (rb * kRB >= sh_goff[j] && rb * kRB < sh_goff[j + 1])
-        real = min(kRB, max(0, sh_ne[j] - (rb * kRB - sh_goff[j])));
-    a.rbcount[rb] = real;
-  }
+      if (rb * kRB >= sh_goff[j] && rb * kRB < sh_goff[j + 1]) real = min(kRB, max(0, sh_ne[j] - (rb * kRB - sh_goff[j])));
+    return real;
+  });
   __syncthreads();
-  route_finish(a, m_pad, sh_goff, E);
+  if (threadIdx.x == 0) { a.ticket[0] = 0; a.ticket[2] = fail; a.ticket[1] = 0; }
+}
+
+// TOPK, pass 2: place every local pair. Inside a workgroup the rank of a token
+// among those choosing expert e comes from wave ballots (tokens are in thread
+// order, i.e. global token order); the stream index from a scan of the local
+// pick counts.
+__global__ __launch_bounds__(kRouteThreads) void route_topk_place_kernel(RouteArgs a) {
+  __shared__ int sh_wave[FG_MAX_GROUPS + 1][kRouteThreads / 64];
+  const int E = a.n_groups, KK = a.topk_k, T = a.rows_per_shard;
+  const int w = blockIdx.x, s = w / a.wpb, t = (w - s * a.wpb) * kRouteThreads + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (__hip_atomic_load(a.ticket + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;  // layout failed
+  unsigned long long mask = 0;
+  const int* tk = a.topk + ((size_t)s * T + min(t, T - 1)) * KK;
+  if (t < T)
+    for (int k = 0; k < KK; ++k) {
+      const int e = tk[k] - a.expert_base;
+      if (e >= 0 && e < E) mask |= 1ull << e;
+    }
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  // per expert: rank inside the wave, wave totals to LDS
+  for (int e = 0; e <= E; ++e) {
+    const bool f = e < E ? ((mask >> e) & 1ull) : false;
+    const unsigned long long b = ballot(f);
+    if (lane == 0) sh_wave[e][wave] = __popcll(b);
+  }
+  // local picks of this token and their scan (stream positions)
+  const int picks = __popcll(mask);
+  int x = picks;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  __shared__ int sh_pick[kRouteThreads / 64];
+  if (lane == 63) sh_pick[wave] = x;
+  __syncthreads();
+  int pick_base = x - picks;
+  for (int v = 0; v < wave; ++v) pick_base += sh_pick[v];
+  const int stream0 = a.wgbase[w * (E + 1) + E] + pick_base;
+  for (int e = 0; e < E; ++e) {
+    const bool f = (mask >> e) & 1ull;
+    const unsigned long long b = ballot(f);
+    if (!f) continue;
+    int rank = a.wgbase[w * (E + 1) + e] + __popcll(b & lt);
+    for (int v = 0; v < wave; ++v) rank += sh_wave[e][v];
+    int j = 0;   // local picks ahead of expert e in this token's list
+    for (int k = 0; k < KK; ++k) {
+      const int ek = tk[k] - a.expert_base;
+      if (ek == e) break;
+      j += (ek >= 0 && ek < E);
+    }
+    const int i = stream0 + j;
+    a.src_row[s * a.rs_cap + i] = t;
+    a.dst_row[s * a.rs_cap + i] = rank;
+    a.inv[rank] = inv_pack(a.ver, (s << 24) | i);
+  }
 }
 
 // Small helpers: fill, poke (fault injection on a counter).
@@ -521,13 +619,15 @@ __device__ __forceinline__ int stress_word(int seq, int sid, int r) {
   return (int)(((uint32_t)seq << 20) ^ (uint32_t)(sid * kChunk + r));
 }
 
-__global__ __launch_bounds__(kThreads, 1) void stress_kernel(StressArgs a) {
+constexpr int kStressThreads = 256;   // four waves: a chunk's 64 rows are written 16 per wave
+
+__global__ __launch_bounds__(kStressThreads, 1) void stress_kernel(StressArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool strict = a.flags & kStrict;
   const __amdgpu_buffer_rsrc_t rP = buffer_rsrc(a.payload, a.payload_bytes);
   if ((int)blockIdx.x < a.P) {
     const int p = blockIdx.x;
-    for (int i = threadIdx.x; i < a.C * a.KC; i += kThreads) a.elect_nxt[p * a.C * a.KC + i] = 0;
+    for (int i = threadIdx.x; i < a.C * a.KC; i += kStressThreads) a.elect_nxt[p * a.C * a.KC + i] = 0;
     for (int c = 0; c < a.C; ++c) {
       for (int k = 0; k < a.KC; ++k) {
         const int sid = (p * a.C + c) * a.KC + k;

@@ -64,7 +64,7 @@ class FgViews(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("slot", "counter", "elect", "pub_count", "seed", "inv_row",
                                           "group_of_rb", "src_row", "dst_row", "stream_len", "group_off",
                                           "bslot", "stress_slot", "stress_pub")] + [
-        ("chunk_cap", C.c_int32), ("rb_cap", C.c_int32), ("m_pad_cap", C.c_int32)]
+        ("chunk_cap", C.c_int32), ("rb_cap", C.c_int32), ("m_pad_cap", C.c_int32), ("route_ver", C.c_uint32)]
 
 
 class FgError(RuntimeError):
@@ -193,6 +193,15 @@ class Context:
         """Copy `count` int32 of library-owned device memory to a CPU tensor."""
         torch.cuda.synchronize(self.device)
         return _as_device_tensor(ptr, count, self.device).clone().cpu()
+
+    def read_inverse_map(self) -> torch.Tensor:
+        """The inverse map of the route in use: gathered row -> (shard << 24 |
+        stream index), -1 for a padding row."""
+        v = self.views()
+        raw = self.read_i32(v.inv_row, 2 * v.m_pad_cap).view(torch.int64)
+        ver = raw.bitwise_right_shift(32).bitwise_and(0xFFFFFFFF)
+        val = raw.bitwise_and(0xFFFFFFFF)
+        return torch.where(ver == int(v.route_ver), val, torch.full_like(val, -1)).to(torch.int32)
 
 
 class _DevArray:

@@ -122,7 +122,7 @@ def control_plane(ctx: fg.Context, n_shards: int):
         elect=ctx.read_i32(v.elect, 2 * S * cc).numpy().reshape(2, S, cc),
         pub_count=ctx.read_i32(v.pub_count, S * cc).numpy().reshape(S, cc),
         seed=ctx.read_i32(v.seed, rbc).numpy(),
-        inv=ctx.read_i32(v.inv_row, v.m_pad_cap).numpy(),
+        inv=ctx.read_inverse_map().numpy(),
         stream_len=ctx.read_i32(v.stream_len, S).numpy(),
         group_off=ctx.read_i32(v.group_off, 65).numpy(),
         src_row=ctx.read_i32(v.src_row, S * ctx.cfg.max_rows_per_shard).numpy().reshape(S, -1),
