@@ -29,6 +29,37 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "fused gather-GEMM TFLOP/s + overlap efficiency; slot-signal latency (\u00b5s)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 1 << 29          # plain device copy used to calibrate the HBM byte counters
+
+
+def kernel_source_hash():
+    """sha256 of the HIP sources and the C header: traffic counters recorded for
+    other sources do not describe the kernel that runs."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sync_protocols_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "fg.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch of the fused kernel from the committed counter
+    summary, or None if there is none for this workload and these sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    return None if w is None else w.get("hbm_bytes_per_launch")
 
 
 def log(msg):
@@ -94,9 +125,11 @@ def setup_workload(name, torch, fg, W):
 
 
 def cpu_baseline(wl, budget_s=12.0):
-    """The oracle as it stands, on host cores, over a bounded sample of the
-    workload: layout + gather of all rows, then the float64 contraction of as
-    many gathered rows as fit the time budget. Returns TFLOP/s of the sample."""
+    """The oracle as it stands, on the host cores, over a bounded sample of the
+    workload: whole steps (layout, gather of every row, float64 contraction of
+    every real row), repeated until about `budget_s` of CPU work; if one step
+    would take much longer, the contraction is restricted to a prefix of the
+    real rows. Returns contraction TFLOP/s of the sample."""
     import numpy as np
     import oracle as O
     try:
@@ -105,41 +138,64 @@ def cpu_baseline(wl, budget_s=12.0):
     except Exception:
         cores = os.cpu_count() or 1
     c = wl["cfg"]
+    K, N = wl["K"], wl["N"]
 
     def bits(t):
         return t.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
 
-    t0 = time.perf_counter()
     if c["kind"] == "dense":
         d = wl["inputs"]["dense"]
-        if c["gather"] == "contiguous":
-            lay = O.layout_contiguous(c["n_shards"], c["rows"])
-        else:
-            lay = O.layout_permutation(d.perm.numpy(), c["n_shards"], c["rows"])
-        G = O.gather([bits(s) for s in d.shards], lay)
+        shards = [bits(s) for s in d.shards]
         wb = bits(d.w)[None]
+        perm = d.perm.numpy() if c["gather"] != "contiguous" else None
+
+        def layout():
+            if perm is None:
+                return O.layout_contiguous(c["n_shards"], c["rows"])
+            return O.layout_permutation(perm, c["n_shards"], c["rows"])
     else:
         e = wl["inputs"]["ep"]
-        lay = O.layout_topk(e.topk.numpy(), c["expert_base"], c["n_local"])
-        G = O.gather([bits(s) for s in e.shards], lay)
+        shards = [bits(s) for s in e.shards]
         wb = bits(e.w)
-    O.seeds(lay)
-    O.signal_counts(lay)
-    t_layout = time.perf_counter() - t0
-    K, N = wl["K"], wl["N"]
-    real_idx = np.nonzero(O.real_rows(lay))[0]
-    rows = 16
+        topk = e.topk.numpy()
+
+        def layout():
+            return O.layout_topk(topk, c["expert_base"], c["n_local"])
+
+    def one_step(rows):
+        lay = layout()
+        G = O.gather(shards, lay)
+        O.seeds(lay)
+        O.signal_counts(lay)
+        real_idx = np.nonzero(O.real_rows(lay))[0]
+        sel = real_idx if rows is None else real_idx[:rows]
+        O.gemm(G, wb, lay, rows=None if rows is None else sel)
+        return len(sel)
+
+    # warm-up (first-touch, thread pool start), then steps on 64 and 512 rows
+    # give the fixed and the per-row cost
+    one_step(64)
+    t0 = time.perf_counter()
+    one_step(64)
     t1 = time.perf_counter()
-    O.gemm(G, wb, lay, rows=real_idx[:rows])
-    dt = max(time.perf_counter() - t1, 1e-6)
-    rows = int(min(len(real_idx), max(rows, rows * (budget_s - t_layout) / dt)))
-    t1 = time.perf_counter()
-    O.gemm(G, wb, lay, rows=real_idx[:rows])
-    t_gemm = time.perf_counter() - t1
-    flop = 2.0 * rows * K * N
-    return dict(value=round(flop / t_gemm / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
-                sample=f"layout+gather of all {lay.m} rows ({t_layout:.2f} s) and the float64 contraction of "
-                       f"{rows} gathered rows x K={K} x N={N} ({t_gemm:.2f} s); value = contraction FLOP / its time")
+    one_step(512)
+    t2 = time.perf_counter()
+    per_row = max(((t2 - t1) - (t1 - t0)) / 448, 1e-9)
+    fixed = max((t1 - t0) - 64 * per_row, 0.0)
+    rows = None if fixed + wl["m_real"] * per_row <= budget_s else max(64, int((budget_s - fixed) / per_row))
+    t0 = time.perf_counter()
+    steps, done_rows = 0, 0
+    while True:
+        done_rows += one_step(rows)
+        steps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flop = 2.0 * done_rows * K * N
+    what = "every real row" if rows is None else f"the first {rows} real rows"
+    return dict(value=round(flop / dt / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"{steps} whole step(s) of the oracle (layout, gather of all rows, float64 contraction of "
+                       f"{what} x K={K} x N={N}) in {dt:.1f} s; value = contraction FLOP / wall time")
 
 
 def main():
@@ -152,6 +208,8 @@ def main():
     ap.add_argument("--tile-n", type=int, default=0)
     ap.add_argument("--no-extras", action="store_true", help="fused timing only (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of a known size (calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the path runs on a single MI355X "
@@ -167,6 +225,7 @@ def main():
     wl = setup_workload(args.workload, torch, fg, W)
     cfg = fg.make_config(wl["S"], wl["max_rows"], wl["K"], wl["N"], n_groups=wl["n_groups"],
                          n_comm_wg=args.n_comm, tile_n=args.tile_n)
+    log(f"bench: workload {args.workload}, {args.warmup} warmup + {args.steps} timed steps")
     ctx = fg.Context(cfg)
     cap = fg.capacity(cfg)
     gathered = torch.zeros(cap, wl["K"], dtype=torch.bfloat16, device="cuda:0")
@@ -182,26 +241,29 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # ---- timed region: exactly `steps` steps, events around each launch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # ---- timed region: exactly `steps` back-to-back steps between one pair of
+    # HIP events on the stream the kernels run on (torch's current stream, which
+    # the library is bound to). With a cached CONTIG layout a step is one launch
+    # of the fused kernel; otherwise the step's layout kernels are included.
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record()
     for i in range(args.steps):
-        ev[i][0].record()
         step()
-        ev[i][1].record()
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [a.elapsed_time(b) for a, b in ev]
     st = ctx.stats()
     if st.error_code:
         raise RuntimeError(f"device error {st.error_code} id {st.error_id}")
     ms_per_step = wall * 1000.0 / args.steps
-    avg_launch_ms = statistics.mean(per)
+    avg_launch_ms = e0.elapsed_time(e1) / args.steps
     value = flop * args.steps / wall / 1e12
 
     result = {
-        "metric": "fused gather-GEMM TFLOP/s + overlap efficiency; slot-signal latency (us)",
+        "metric": METRIC,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -212,12 +274,17 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": dict(workload=f"{args.workload}", **wl["info"], n_comm_wg=st.n_comm_wg,
-                       n_gemm_wg=st.n_gemm_wg),
+                       n_gemm_wg=st.n_gemm_wg, tiles_whole=st.tiles_whole, tiles_split=st.tiles_split,
+                       split_parts=st.split_parts),
     }
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
+    traffic = recorded_traffic(args.workload)
     result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                          "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                          "kernel": "fused_kernel", "avg_launch_us": round(avg_launch_ms * 1000, 2)}
+                          "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                          "traffic": None if traffic is None else int(traffic),
+                          "kernel": "fused_kernel", "avg_launch_us": round(avg_launch_ms * 1000, 2),
+                          "algorithmic_flop_per_launch": flop,
+                          "algorithmic_gather_bytes_per_launch": gather_bytes}
 
     if not args.no_extras:
         n_rep = max(10, args.steps)
@@ -283,7 +350,15 @@ def main():
                             "us_per_iter_no_delay": round(statistics.median(t_nodelay) * 1000, 2),
                             "us_per_iter_delays_0_20us": round(statistics.median(t_delay) * 1000, 2),
                             "signals_per_s_no_delay": round(signals / (statistics.median(t_nodelay) * 1e-3), 0)}
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)     # one elementwise kernel: reads and writes COPY_BYTES
+        torch.cuda.synchronize()
+        log(f"bench: copy calibration, 3 copies of {COPY_BYTES} bytes")
     if not args.no_cpu:
+        log("bench: oracle on the host cores")
         result["cpu_baseline"] = cpu_baseline(wl)
     ctx.close()
     print(json.dumps(result), flush=True)

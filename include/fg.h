@@ -47,6 +47,7 @@ extern "C" {
 
 #define FG_CHUNK_ROWS 64    /* "PCIe sync protocols" §4: one signal per 64 rows of a producer stream */
 #define FG_ROW_BLOCK 128    /* "PCIe sync protocols" §5: the GEMM gate releases 128 gathered rows */
+#define FG_COUNTER_STRIDE 64  /* int32 per arrival counter: each counter has a 256-byte line of its own */
 #define FG_MAX_SHARDS 64
 #define FG_MAX_GROUPS 64
 
@@ -68,6 +69,7 @@ enum {
   FG_CALL_VERIFY = 1u << 2,     /* count publishes per slot, polls and waits (observation counters) */
   FG_CALL_STRICT = 1u << 3,     /* formal agent-scope release fences on every signal (slow reference mode) */
   FG_CALL_SAME_ROUTE = 1u << 4, /* EXPLICIT/TOPK: route identical to the previous call, skip the layout step */
+  FG_CALL_TRACE = 1u << 5,      /* record per compute item and per row block timestamps (fg_views trace) */
   /* Fault injection (tests). Each makes a bounded wait or a check fail so that
    * the error path is exercised; every kernel still runs to completion. */
   FG_FAULT_SEED_LOW = 1u << 8,      /* seed of row block 0 one too low: its gate never opens -> FG_ETIMEOUT */
@@ -81,13 +83,19 @@ typedef struct {
   int32_t K;                   /* row width in bf16 elements; multiple of 128 */
   int32_t N;                   /* GEMM output width; multiple of 128 */
   int32_t n_groups;            /* 1 = one dense weight; >1 = one weight per group (expert) */
-  int32_t n_comm_wg;           /* communication workgroups (0 = default 16) */
-  int32_t n_gemm_wg;           /* compute workgroups (0 = CUs - n_comm_wg) */
+  int32_t n_comm_wg;           /* communication workgroups (0 = default 64); they join the compute role
+                                  once their rows are copied */
+  int32_t n_gemm_wg;           /* dedicated compute workgroups (0 = CUs - n_comm_wg) */
   int32_t tile_n;              /* GEMM tile width 128 or 256 (0 = default) */
   int64_t timeout_ns;          /* watchdog of every device-side wait (0 = 2 s) */
   int32_t stress_producers;    /* protocol-stress plane (0 = none): producers x consumers x chunks slots */
   int32_t stress_consumers;
   int32_t stress_max_chunks;
+  int32_t split_parts;         /* split-K tail, used when the tiles leave the last round of the grid
+                                  partial: k-ranges per tail tile, 1..8 (0 = default 4, 1 = no split) */
+  int32_t split_tiles;         /* split-K tail: at most this many tail tiles split (0 = default: one
+                                  part per workgroup of the grid); the library allocates
+                                  split_tiles * split_parts * 256 * tile_n * 4 bytes of partial sums */
   int32_t reserved;
 } fg_config;
 
@@ -126,18 +134,21 @@ typedef struct {
   double t_kernel_us;             /* last fused kernel: first start to last end (device clock) */
   double t_comm_span_us;          /* last fused kernel: communication role span */
   double t_gemm_span_us;          /* last fused kernel: compute role span */
-  double t_gemm_busy_us;          /* mean over compute WGs of (span - time spent waiting at gates) */
-  double t_gate_wait_us;          /* mean over compute WGs of time spent waiting at gates */
+  double t_gemm_busy_us;          /* compute-role time net of waits (gates, split-K part waits), summed
+                                     over workgroups, per whole-tile equivalent (a part counts 1/P) */
+  double t_gate_wait_us;          /* mean over workgroups that ran compute items of their wait time */
   double t_barrier_us;            /* last fg_barrier: device time per barrier */
   double t_rtt_us;                /* last fg_pingpong: device round trip */
   int32_t n_comm_wg, n_gemm_wg, cu_count, m_pad_cap;
+  int32_t tiles_whole, tiles_split; /* last fused kernel: whole tiles, tiles computed as split-K parts */
+  int32_t split_parts, reserved;
 } fg_stats_t;
 
 /* Read-only device views of the library-owned control plane (for tests that
  * compare it element by element with the host-recomputed table). */
 typedef struct {
   const int32_t* slot;        /* [n_shards][chunk_cap] */
-  const int32_t* counter;     /* [2][rb_cap] parity double-buffered */
+  const int32_t* counter;     /* [2][rb_cap][FG_COUNTER_STRIDE] parity double-buffered; value at [..][..][0] */
   const int32_t* elect;       /* [2][n_shards][chunk_cap] */
   const int32_t* pub_count;   /* [n_shards][chunk_cap] (VERIFY) */
   const int32_t* seed;        /* [rb_cap] */
@@ -153,6 +164,15 @@ typedef struct {
   const int32_t* stress_pub;  /* [P][C][KC] */
   int32_t chunk_cap, rb_cap, m_pad_cap;
   uint32_t route_ver;         /* version of the route in use */
+  /* Timing observation (device wall clock, wall_khz ticks per ms), written by
+   * the last fused kernel: */
+  const int64_t* wg_time;     /* [grid][8]: start, end, wait ticks, whole tiles, end of the copy role,
+                                 split parts, start of the compute role, parts per split tile */
+  const int64_t* trace;       /* FG_CALL_TRACE: [trace_cap][4] per compute item in ticket order:
+                                 workgroup, ticket taken, gate open, item done */
+  const int64_t* rb_time;     /* FG_CALL_TRACE: [rb_cap] time the row block's counter reached 128 */
+  int32_t grid, trace_cap;
+  int64_t wall_khz;
 } fg_views_t;
 
 /* Create a context on `hip_device`: validates the configuration, allocates and
@@ -169,9 +189,13 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out);
  * shards[s][src_row] -> gathered[dst_row] bitwise (device-coherent 16-byte
  * stores), add arrivals to the 128-row counters (seeded with the padding
  * count), elect the last writer of each 64-row chunk, which stores seq into the
- * chunk's single-writer slot; compute workgroups wait for each 128-row block's
- * counter to equal 128 and compute out[m][n] = sum_k gathered[m][k] * W_g(m)[k][n]
- * (fp32 accumulation, bf16 round-to-nearest-even output; padding rows = 0).
+ * chunk's single-writer slot; compute workgroups (and communication
+ * workgroups once their rows are copied) take tiles from a ticket counter,
+ * wait for each 128-row block's counter to equal 128 and compute
+ * out[m][n] = sum_k gathered[m][k] * W_g(m)[k][n] (fp32 accumulation, bf16
+ * round-to-nearest-even output; padding rows = 0). The last tiles are split
+ * into k-ranges whose fp32 partials are summed in a fixed order, so results
+ * are deterministic.
  *   shards:   host array of n_shards device pointers, bf16 [rows, K]
  *   route:    NULL = CONTIG with rows_per_shard = max_rows_per_shard
  *   W:        device bf16 [n_groups][N][K]: W_g[k][n] stored at W[g][n][k]

@@ -18,14 +18,18 @@ using namespace fg;
 
 namespace {
 
-constexpr int kDefaultComm = 16;
+// Copy workgroups: the gather is latency-bound per workgroup (load, write-through
+// store, acknowledgement, counter add), so many workgroups keep enough bytes in
+// flight; they join the compute role when their rows are copied.
+constexpr int kDefaultComm = 64;
+constexpr int kDefaultSplitParts = 4;
 constexpr int64_t kDefaultTimeoutNs = 2000000000LL;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Plane {
   int* slot;
-  int* counter;    // [2][rb_cap]
+  int* counter;    // [2][rb_cap][kCtr]
   int* elect;      // [2][S * chunk_cap]
   int* pub_count;
   int* seed;
@@ -39,6 +43,10 @@ struct Plane {
   int* wgcount;
   int* wgbase;
   int* ticket;
+  int* gtick;      // [2] x 64 ints: compute-item tickets, one per parity
+  int* skc;        // [2][split_tiles] split-K part counters
+  long long* trace;    // [trace_cap][4]
+  long long* rb_time;  // [rb_cap]
   int* desc;
   int* err;        // [2]
   unsigned long long* stats;
@@ -59,6 +67,9 @@ struct fg_ctx {
   int cu_count = 0;
   int chunk_cap = 0, rb_cap = 0, m_pad_cap = 0, s_slots = 0;
   int n_comm = 0, n_gemm = 0, tile_n = 256;
+  int split_parts = 1, split_tiles = 0, trace_cap = 0;
+  float* skws = nullptr;       // split-K partial sums
+  size_t skws_bytes = 0;
   int64_t wall_khz = 100000;
   char* plane_mem = nullptr;
   Plane p{};
@@ -104,6 +115,7 @@ static bool config_ok(const fg_config* c) {
   if (c->tile_n == 256 && c->N % 256 != 0) return false;
   if (c->n_comm_wg < 0 || c->n_gemm_wg < 0) return false;
   if (c->timeout_ns < 0) return false;
+  if (c->split_parts < 0 || c->split_parts > 8 || c->split_tiles < 0 || c->split_tiles > 4096) return false;
   if (c->stress_producers < 0 || c->stress_consumers < 0 || c->stress_max_chunks < 0) return false;
   const long long m = (long long)c->n_shards * c->max_rows_per_shard + (long long)c->n_groups * FG_ROW_BLOCK;
   if (m * c->K * 2 >= (1ll << 32)) return false;   // 32-bit buffer offsets
@@ -175,7 +187,7 @@ static fg_status launch_route(fg_ctx* ctx, const fg_route* route, int mode, int 
   ra.group_off_out = ctx->p.group_off; ra.inv = ctx->p.inv; ra.seed = ctx->p.seed;
   ra.group_of_rb = ctx->p.group_of_rb; ra.rbcount = ctx->p.rbcount;
   ra.wgcount = ctx->p.wgcount; ra.wgbase = ctx->p.wgbase; ra.ticket = ctx->p.ticket;
-  ra.counter_cur = ctx->p.counter + (size_t)cur * ctx->rb_cap;
+  ra.counter_cur = ctx->p.counter + (size_t)cur * ctx->rb_cap * kCtr;
   ra.elect_cur = ctx->p.elect + (size_t)cur * c.n_shards * ctx->chunk_cap;
   ra.desc = ctx->p.desc; ra.err = sink(ctx);
   auto blocks = [](long long work) { return (int)std::max(1LL, std::min(1024LL, (work + kRouteThreads - 1) / kRouteThreads)); };
@@ -274,20 +286,29 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
   ctx->rb_cap = ctx->m_pad_cap / FG_ROW_BLOCK;
   ctx->s_slots = cfg->stress_producers * cfg->stress_consumers * cfg->stress_max_chunks;
   const int grid_max = ctx->n_comm + ctx->n_gemm;
+  ctx->split_parts = cfg->split_parts ? cfg->split_parts : kDefaultSplitParts;
+  ctx->split_tiles = ctx->split_parts > 1 ? (cfg->split_tiles ? cfg->split_tiles
+                                                              : (grid_max + ctx->split_parts - 1) / ctx->split_parts)
+                                          : 0;
+  ctx->skws_bytes = (size_t)ctx->split_tiles * ctx->split_parts * 256 * ctx->tile_n * 4;
+  if (ctx->skws_bytes >= (1ull << 32)) { delete ctx; return FG_EINVAL; }
+  ctx->trace_cap = (ctx->m_pad_cap / 128) * (cfg->N / 128) + ctx->split_tiles * ctx->split_parts;
   const size_t nch = (size_t)S * ctx->chunk_cap;
   const size_t nrs = (size_t)S * cfg->max_rows_per_shard;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
   ctx->route_wg_cap = S * ((cfg->max_rows_per_shard + kRouteThreads - 1) / kRouteThreads);
   const size_t wgc = (size_t)ctx->route_wg_cap * (FG_MAX_GROUPS + 1) * 4;
-  const size_t o_slot = take(nch * 4), o_counter = take(2 * (size_t)ctx->rb_cap * 4),
+  const size_t o_slot = take(nch * 4), o_counter = take(2 * (size_t)ctx->rb_cap * kCtr * 4),
                o_elect = take(2 * nch * 4), o_pub = take(nch * 4), o_seed = take((size_t)ctx->rb_cap * 4),
                o_inv = take((size_t)ctx->m_pad_cap * 8), o_grp = take((size_t)ctx->rb_cap * 4),
                o_src = take(nrs * 4), o_dst = take(nrs * 4), o_slen = take((size_t)S * 4),
                o_goff = take((FG_MAX_GROUPS + 1) * 4), o_rbc = take((size_t)ctx->rb_cap * 4), o_desc = take(64),
-               o_wgc = take(wgc), o_wgb = take(wgc), o_tick = take(64),
+               o_wgc = take(wgc), o_wgb = take(wgc), o_tick = take(64), o_gtick = take(512),
+               o_skc = take(2 * (size_t)std::max(1, ctx->split_tiles) * 4),
+               o_trace = take((size_t)ctx->trace_cap * 32), o_rbt = take((size_t)ctx->rb_cap * 8),
                o_err = take(64), o_stats = take(ST_COUNT * 8), o_bslot = take((size_t)S * S * 4),
-               o_pp = take(512), o_tdev = take(64), o_wg = take((size_t)grid_max * 32),
+               o_pp = take(512), o_tdev = take(64), o_wg = take((size_t)grid_max * kWgTimeFields * 8),
                o_sslot = take((size_t)ctx->s_slots * 4), o_select = take(2 * (size_t)ctx->s_slots * 4),
                o_spub = take((size_t)ctx->s_slots * 4);
   if (hipMalloc(&ctx->plane_mem, off) != hipSuccess) { delete ctx; return FG_ENOMEM; }
@@ -297,6 +318,8 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
   p.slot = (int*)(b + o_slot); p.counter = (int*)(b + o_counter); p.elect = (int*)(b + o_elect);
   p.pub_count = (int*)(b + o_pub); p.seed = (int*)(b + o_seed); p.inv = (unsigned long long*)(b + o_inv);
   p.wgcount = (int*)(b + o_wgc); p.wgbase = (int*)(b + o_wgb); p.ticket = (int*)(b + o_tick);
+  p.gtick = (int*)(b + o_gtick); p.skc = (int*)(b + o_skc);
+  p.trace = (long long*)(b + o_trace); p.rb_time = (long long*)(b + o_rbt);
   p.group_of_rb = (int*)(b + o_grp); p.src_row = (int*)(b + o_src); p.dst_row = (int*)(b + o_dst);
   p.stream_len = (int*)(b + o_slen); p.group_off = (int*)(b + o_goff); p.rbcount = (int*)(b + o_rbc);
   p.desc = (int*)(b + o_desc); p.err = (int*)(b + o_err); p.stats = (unsigned long long*)(b + o_stats);
@@ -307,6 +330,11 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
     (void)hipFree(ctx->plane_mem); delete ctx; return FG_ENOMEM;
   }
   memset(ctx->host_status, 0, 64);
+  if (ctx->skws_bytes && hipMalloc(&ctx->skws, ctx->skws_bytes) != hipSuccess) {
+    ctx->skws = nullptr;
+    fg_destroy(ctx);
+    return FG_ENOMEM;
+  }
   if (hipDeviceSynchronize() != hipSuccess) { fg_destroy(ctx); return FG_EHIP; }
   *out = ctx;
   return FG_OK;
@@ -318,6 +346,7 @@ fg_status fg_destroy(fg_ctx* ctx) {
   if (ctx->stream_bound) (void)hipStreamSynchronize(ctx->stream);
   if (ctx->plane_mem) (void)hipFree(ctx->plane_mem);
   if (ctx->host_status) (void)hipHostFree(ctx->host_status);
+  if (ctx->skws) (void)hipFree(ctx->skws);
   delete ctx;
   return FG_OK;
 }
@@ -379,14 +408,14 @@ fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route*
     ctx->route_cached_mode = mode;
     ctx->route_cached_rows = rows;
   }
-  int* counter_cur = ctx->p.counter + (size_t)cur * ctx->rb_cap;
+  int* counter_cur = ctx->p.counter + (size_t)cur * ctx->rb_cap * kCtr;
   if (flags & (FG_FAULT_SEED_LOW | FG_FAULT_SEED_HIGH)) {
     hipLaunchKernelGGL(poke_kernel, dim3(1), dim3(64), 0, stream, counter_cur, (flags & FG_FAULT_SEED_HIGH) ? 1 : -1);
     HIPCHK(hipGetLastError());
   }
   if (flags & FG_CALL_GEMM_ONLY) {
     hipLaunchKernelGGL(fill_kernel, dim3(std::max(1, std::min(64, ctx->rb_cap / 256 + 1))), dim3(256), 0, stream,
-                       counter_cur, ctx->rb_cap, FG_ROW_BLOCK);
+                       counter_cur, ctx->rb_cap, FG_ROW_BLOCK, kCtr);
     HIPCHK(hipGetLastError());
   }
   FusedArgs a{};
@@ -397,7 +426,7 @@ fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route*
   a.shard_rows = rows;
   a.slot = ctx->p.slot;
   a.counter_cur = counter_cur;
-  a.counter_nxt = ctx->p.counter + (size_t)nxt * ctx->rb_cap;
+  a.counter_nxt = ctx->p.counter + (size_t)nxt * ctx->rb_cap * kCtr;
   a.elect_cur = ctx->p.elect + (size_t)cur * c.n_shards * ctx->chunk_cap;
   a.elect_nxt = ctx->p.elect + (size_t)nxt * c.n_shards * ctx->chunk_cap;
   a.pub_count = ctx->p.pub_count; a.seed = ctx->p.seed; a.inv = ctx->p.inv; a.route_ver = ctx->route_ver;
@@ -411,6 +440,15 @@ fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route*
   a.rows_per_batch = upr <= 2 ? 16 : upr <= 4 ? 8 : upr <= 8 ? 4 : upr <= 16 ? 2 : 1;
   a.flags = flags;
   a.timeout_ticks = timeout_ticks(ctx);
+  a.tick_cur = ctx->p.gtick + cur * 64;
+  a.tick_nxt = ctx->p.gtick + nxt * 64;
+  a.skc_cur = ctx->p.skc + (size_t)cur * std::max(1, ctx->split_tiles);
+  a.skc_nxt = ctx->p.skc + (size_t)nxt * std::max(1, ctx->split_tiles);
+  a.skws = ctx->skws;
+  a.skws_bytes = (uint32_t)ctx->skws_bytes;
+  a.split_tiles = ctx->split_tiles;
+  a.split_parts = ctx->split_parts;
+  a.trace = ctx->p.trace; a.rb_time = ctx->p.rb_time; a.trace_cap = ctx->trace_cap;
   ctx->last_grid = a.n_comm + a.n_gemm;
   ctx->last_m_pad = m_pad;
   const bool bm256 = (mode != FG_ROUTE_TOPK) && (m_pad % 256 == 0) &&
@@ -508,26 +546,44 @@ fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait) {
   if (ctx->host_stats[1]) out->t_rtt_us = td[1] * us_per_tick / (double)ctx->host_stats[1];
   if (ctx->last_grid) {
     const int g = ctx->last_grid;
-    long long* wg = new (std::nothrow) long long[(size_t)g * 4];
+    long long* wg = new (std::nothrow) long long[(size_t)g * kWgTimeFields];
     if (!wg) return FG_ENOMEM;
-    if (hipMemcpy(wg, ctx->p.wgtime, (size_t)g * 32, hipMemcpyDeviceToHost) != hipSuccess) { delete[] wg; return FG_EHIP; }
-    long long t0 = wg[0], t1 = wg[1], c0 = wg[0], c1 = wg[1], g0 = 0, g1 = 0;
+    if (hipMemcpy(wg, ctx->p.wgtime, (size_t)g * kWgTimeFields * 8, hipMemcpyDeviceToHost) != hipSuccess) {
+      delete[] wg;
+      return FG_EHIP;
+    }
+    long long t0 = wg[WT_START], t1 = wg[WT_END], c1 = 0, g0 = -1, g1 = 0;
     double busy = 0, waitt = 0;
-    int ng = 0;
+    long long tiles = 0, parts = 0, peff = 1;
+    int nw = 0;
     for (int i = 0; i < g; ++i) {
-      const long long* t = wg + (size_t)i * 4;
-      t0 = std::min(t0, t[0]); t1 = std::max(t1, t[1]);
-      if (i < ctx->n_comm) { c0 = std::min(c0, t[0]); c1 = std::max(c1, t[1]); }
-      else {
-        if (ng == 0) { g0 = t[0]; g1 = t[1]; }
-        g0 = std::min(g0, t[0]); g1 = std::max(g1, t[1]);
-        busy += (double)(t[1] - t[0] - t[2]); waitt += (double)t[2]; ++ng;
+      const long long* t = wg + (size_t)i * kWgTimeFields;
+      t0 = std::min(t0, t[WT_START]);
+      t1 = std::max(t1, t[WT_END]);
+      if (i < ctx->n_comm) c1 = std::max(c1, t[WT_COMM_END]);
+      if (t[WT_TILES] + t[WT_PARTS] > 0) {
+        g0 = g0 < 0 ? t[WT_GEMM_START] : std::min(g0, t[WT_GEMM_START]);
+        g1 = std::max(g1, t[WT_END]);
+        busy += (double)(t[WT_END] - t[WT_GEMM_START] - t[WT_GATE]);
+        waitt += (double)t[WT_GATE];
+        tiles += t[WT_TILES];
+        parts += t[WT_PARTS];
+        peff = std::max(peff, t[WT_P]);
+        ++nw;
       }
     }
     out->t_kernel_us = (t1 - t0) * us_per_tick;
-    out->t_comm_span_us = (c1 - c0) * us_per_tick;
-    out->t_gemm_span_us = (g1 - g0) * us_per_tick;
-    if (ng) { out->t_gemm_busy_us = busy / ng * us_per_tick; out->t_gate_wait_us = waitt / ng * us_per_tick; }
+    out->t_comm_span_us = c1 > t0 ? (c1 - t0) * us_per_tick : 0.0;
+    out->t_gemm_span_us = g0 >= 0 ? (g1 - g0) * us_per_tick : 0.0;
+    const long long P = std::max(1LL, peff);
+    const double units = (double)tiles + (double)parts / P;
+    if (nw) {
+      out->t_gemm_busy_us = units > 0 ? busy / units * us_per_tick : 0.0;
+      out->t_gate_wait_us = waitt / nw * us_per_tick;
+    }
+    out->tiles_whole = (int32_t)tiles;
+    out->tiles_split = (int32_t)(parts / P);
+    out->split_parts = (int32_t)P;
     delete[] wg;
   }
   return FG_OK;
@@ -541,6 +597,8 @@ fg_status fg_views(fg_ctx* ctx, fg_views_t* v) {
   v->stream_len = p.stream_len; v->group_off = p.group_off; v->bslot = p.bslot; v->stress_slot = p.s_slot;
   v->stress_pub = p.s_pub;
   v->chunk_cap = ctx->chunk_cap; v->rb_cap = ctx->rb_cap; v->m_pad_cap = ctx->m_pad_cap;
+  v->wg_time = (const int64_t*)p.wgtime; v->trace = (const int64_t*)p.trace; v->rb_time = (const int64_t*)p.rb_time;
+  v->grid = ctx->n_comm + ctx->n_gemm; v->trace_cap = ctx->trace_cap; v->wall_khz = ctx->wall_khz;
   return FG_OK;
 }
 

@@ -26,6 +26,7 @@ namespace fg {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 
 constexpr int kBK = 64;             // k per LDS stage
@@ -123,7 +124,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 #define FG_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// Full K loop for one tile (K a multiple of 128, so the stage count is even).
+// K loop for one tile (or one k-range of it; the stage count is even).
 // rA: gathered rows (row stride K*2 bytes), a_off = byte offset of the tile's
 // first row; rB: weight rows [N][K], b_off likewise. lds0/lds1: the two stage
 // buffers (distinct objects, so the compiler can tell them apart when it places
@@ -237,16 +238,17 @@ __device__ __forceinline__ void stage_body(const char* cur, const char* nxt,
   }
 }
 
+// nk: k-iterations of 64 to run (even, >= 2) starting at the byte offsets
+// a_off / b_off (which include the k origin); stride: row stride of both
+// buffers in bytes (K * 2).
 template <int BM, int BN>
 __device__ __forceinline__ void tile_mainloop(__amdgpu_buffer_rsrc_t rA, uint32_t a_off,
-                                              __amdgpu_buffer_rsrc_t rB, uint32_t b_off, int K,
+                                              __amdgpu_buffer_rsrc_t rB, uint32_t b_off, uint32_t stride, int nk,
                                               char* lds0, char* lds1, Acc<BM, BN>& acc) {
   using T = Tile<BM, BN>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / T::WGN, wn = wave % T::WGN;
-  const uint32_t stride = (uint32_t)K * 2;
-  const int nk = K / kBK;   // even
   stage_load<BM>(rA, a_off, stride, 0, lds0, wave, lane);
   stage_load<BN>(rB, b_off, stride, 0, lds0 + T::A_BYTES, wave, lane);
   stage_load<BM>(rA, a_off, stride, kRowB, lds1, wave, lane);
@@ -272,10 +274,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // Store the tile: padding rows (no current inverse-map entry) are written as zeros.
-// rO: output rows [*, N] (row stride N*2 bytes); m0, n0: tile origin.
+// rO: output rows [*, N] (row stride N*2 bytes); m0, n0: tile origin. Only the
+// wave fragments f (f = fm * FN + fn) with f % P == part are stored (P = 1:
+// all of them).
 template <int BM, int BN>
 __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int m0, int n0,
-                                           const Acc<BM, BN>& acc, const unsigned long long* inv, uint32_t ver) {
+                                           const Acc<BM, BN>& acc, const unsigned long long* inv, uint32_t ver,
+                                           int part = 0, int P = 1) {
   using T = Tile<BM, BN>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / T::WGN, wn = wave % T::WGN;
@@ -287,6 +292,7 @@ __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int
     const uint32_t row_off = (uint32_t)m * (uint32_t)N * 2;
 #pragma unroll
     for (int fn = 0; fn < T::FN; ++fn) {
+      if ((fm * T::FN + fn) % P != part) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + wn * T::WN + fn * 32 + 8 * g + 4 * kh;
@@ -298,6 +304,78 @@ __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int
       }
     }
   }
+}
+
+// --- split-K partial sums ------------------------------------------------
+// A tile's partial sum is kept in register order: for wave w and fragment f,
+// 16 floats per lane as four 1 KB rows (64 lanes x 16 bytes), so every store
+// and load is one fully coalesced 16-byte-per-lane access. One part's block is
+// BM * BN * 4 bytes.
+template <int BM, int BN>
+__device__ __forceinline__ uint32_t partial_off(int wave, int f, int g, int lane) {
+  using T = Tile<BM, BN>;
+  return (uint32_t)((((wave * (T::FM * T::FN) + f) * 4 + g) * 64 + lane) * 16);
+}
+
+// Store the fragments this part does NOT reduce itself (f % P != part) into
+// its block at byte offset `base`, with device-coherent write-through stores.
+template <int BM, int BN>
+__device__ __forceinline__ void partial_store(__amdgpu_buffer_rsrc_t rW, uint32_t base, const Acc<BM, BN>& acc,
+                                              int part, int P) {
+  using T = Tile<BM, BN>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < T::FN; ++fn) {
+      const int f = fm * T::FN + fn;
+      if (f % P == part) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // whole-vector bit casts only: a bit cast of a vector element lvalue
+        // reads element 0 with this compiler
+        const f32x16& c = acc.v[fm][fn];
+        const f32x4 x = {c[4 * g + 0], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
+        store16_coherent(rW, base + partial_off<BM, BN>(wave, f, g, lane), __builtin_bit_cast(v4i, x));
+      }
+    }
+}
+
+// Reduce the fragments this part owns (f % P == part): its own partial (in
+// registers) plus the other parts' in part order. The owner of a fragment is
+// fixed by f, so the order of the fp32 additions, and with it the result,
+// does not depend on which workgroup ran which part. `base` = byte offset of
+// part 0's block; blocks are `tile_bytes` apart. Loads use the device-coherent
+// policy: the blocks were written by other workgroups, possibly on other XCDs.
+template <int BM, int BN>
+__device__ __forceinline__ void partial_reduce(__amdgpu_buffer_rsrc_t rW, uint32_t base, uint32_t tile_bytes,
+                                               Acc<BM, BN>& acc, int part, int P) {
+  using T = Tile<BM, BN>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < T::FN; ++fn) {
+      const int f = fm * T::FN + fn;
+      if (f % P != part) continue;
+#pragma unroll 1
+      for (int q = 0; q < P; ++q) {
+        if (q == part) continue;
+        const uint32_t off = base + (uint32_t)q * tile_bytes;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 x = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rW, off + partial_off<BM, BN>(wave, f, g, lane), 0,
+                                                           kPolCoherentStream));
+          acc.v[fm][fn][4 * g + 0] += x[0];
+          acc.v[fm][fn][4 * g + 1] += x[1];
+          acc.v[fm][fn][4 * g + 2] += x[2];
+          acc.v[fm][fn][4 * g + 3] += x[3];
+        }
+      }
+    }
 }
 
 }  // namespace fg

@@ -10,6 +10,8 @@ namespace fg {
 
 constexpr int kChunk = FG_CHUNK_ROWS;
 constexpr int kRB = FG_ROW_BLOCK;
+constexpr int kCtr = FG_COUNTER_STRIDE;  // arrival counters sit 256 bytes apart: a gate's pollers and
+                                         // the copy role's adds then spread over memory channels
 constexpr int kThreads = 64 * kWaves;   // workgroup size of the fused kernel
 
 // per-call flag bits as seen by the device
@@ -18,6 +20,7 @@ constexpr uint32_t kGemmOnly = FG_CALL_GEMM_ONLY;
 constexpr uint32_t kVerify = FG_CALL_VERIFY;
 constexpr uint32_t kStrict = FG_CALL_STRICT;
 constexpr uint32_t kDropPublish = FG_FAULT_DROP_PUBLISH;
+constexpr uint32_t kTrace = FG_CALL_TRACE;
 
 // Device statistics block (int64 counters, cumulative).
 enum { ST_PUBLISHES = 0, ST_GATE_POLLS, ST_SLOT_POLLS, ST_GATE_PASSES, ST_STALE, ST_COUNT };
@@ -39,7 +42,7 @@ struct FusedArgs {
   int K, N, n_shards, chunk_cap, rs_cap, rb_cap, m_pad_cap;
   int shard_rows;            // rows of every source shard (bounds of the row loads)
   int* slot;
-  int* counter_cur;
+  int* counter_cur;          // [rb_cap][kCtr]
   int* counter_nxt;
   int* elect_cur;
   int* elect_nxt;
@@ -52,14 +55,29 @@ struct FusedArgs {
   const int* stream_len;
   const int* desc;           // [0] = m_pad of this iteration
   unsigned long long* stats;
-  long long* wgtime;         // [grid][4]: start, end, gate-wait ticks, tiles
+  long long* wgtime;         // [grid][kWgTimeFields], see WgTime
   ErrorSink err;
   int seq;
   int n_comm, n_gemm;
   int rows_per_batch;
   uint32_t flags;
   uint64_t timeout_ticks;
+  // compute schedule: tickets and the split-K tail
+  int* tick_cur;             // [1] next work item of this call (zero at kernel start)
+  int* tick_nxt;             // [1] the other parity, zeroed here for the next call
+  int* skc_cur;              // [split_tiles] parts finished per split tile (zero at kernel start)
+  int* skc_nxt;
+  float* skws;               // split_tiles x split_parts partial blocks of BM x BN floats
+  uint32_t skws_bytes;
+  int split_tiles;           // at most this many tail tiles are split
+  int split_parts;           // into this many k-ranges (1 = no split)
+  long long* trace;          // TRACE: [trace_cap][4] per item: workgroup, taken, gate open, done
+  long long* rb_time;        // TRACE: [rb_cap] time a row block's counter reached 128
+  int trace_cap;
 };
+
+// Per-workgroup timing record (device clock ticks).
+enum { WT_START = 0, WT_END, WT_GATE, WT_TILES, WT_COMM_END, WT_PARTS, WT_GEMM_START, WT_P, kWgTimeFields = 8 };
 
 // ---------------------------------------------------------------------------
 // Communication role ("PCIe sync protocols" §3 election + publish, §4 chunk
@@ -110,9 +128,11 @@ __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
   // Re-arm the other parity for the next iteration: nothing else touches it
   // during this kernel, and stream order publishes it to the next one.
   for (int i = cw * kThreads + threadIdx.x; i < a.rb_cap; i += a.n_comm * kThreads)
-    a.counter_nxt[i] = a.seed[i];
+    a.counter_nxt[(size_t)i * kCtr] = a.seed[i];
   for (int i = cw * kThreads + threadIdx.x; i < a.n_shards * a.chunk_cap; i += a.n_comm * kThreads)
     a.elect_nxt[i] = 0;
+  for (int i = cw * kThreads + threadIdx.x; i < a.split_tiles; i += a.n_comm * kThreads) a.skc_nxt[i] = 0;
+  if (cw == 0 && threadIdx.x == 0) a.tick_nxt[0] = 0;
   if (a.flags & kGemmOnly) return;
 
   const int m_pad = __builtin_amdgcn_readfirstlane(a.desc[0]);
@@ -144,8 +164,9 @@ __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
     const int n_real = __popcll(real);
     if (lane == 0 && n_real > 0) {
       const int rb = g0 / kRB;
-      const int old = fetch_add_relaxed(a.counter_cur + rb, n_real);
+      const int old = fetch_add_relaxed(a.counter_cur + (size_t)rb * kCtr, n_real);
       if (old + n_real > kRB) raise_error(a.err, kErrProtocol, rb);
+      if ((a.flags & kTrace) && old + n_real == kRB) a.rb_time[rb] = (long long)now_ticks();
     }
     // election: per chunk touched by the batch, one add of the rows it finished;
     // the add that completes the chunk elects this wave as its single publisher
@@ -176,55 +197,131 @@ __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
 }
 
 // ---------------------------------------------------------------------------
-// Compute role: for each tile in row-block-major order, wait until every row
-// block it reads has counter == 128 ("PCIe sync protocols" §5 gate), acquire,
-// run the MFMA tile.
+// Compute role ("PCIe sync protocols" §5 gate). Work items are handed out by
+// one ticket counter, in row-block-major tile order (the order in which the
+// communication role delivers row blocks). Items 0 .. n_whole-1 are whole
+// tiles; when the tiles do not fill a whole number of rounds of the grid, the
+// last R tiles of the order are split into P k-ranges ("parts"), one item
+// each, so that the tail of the schedule is spread over the grid instead of
+// leaving most workgroups idle. Every item first waits until each
+// row block it reads has counter == 128, acquires, and runs the MFMA tile.
+// A part stores the fragments it does not own to the partial workspace,
+// counts itself in the tile's part counter, waits until all P parts have
+// done so, then sums the partials of the fragments it owns and stores them.
+// Communication workgroups enter this role once their rows are copied.
+//
+// Deadlock freedom: parts of a tile are consecutive tickets, so at most one
+// tile at a time has parts not yet taken; its waiting holders are at most P-1
+// workgroups, and every other workgroup either computes (and finishes) or
+// waits on a tile whose parts are all taken. With P <= grid some workgroup is
+// always free to take the remaining parts.
 // ---------------------------------------------------------------------------
 template <int BM, int BN>
-__device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh_flag, long long* gate_ticks,
-                          int* tiles_done) {
-  const int gj = blockIdx.x - a.n_comm;
+__device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, long long* wt) {
   if (a.flags & kCommOnly) return;
+  using T = Tile<BM, BN>;
   const int m_pad = __builtin_amdgcn_readfirstlane(a.desc[0]);
   const int n_tn = a.N / BN;
   const int n_tiles = (m_pad / BM) * n_tn;
+  const int grid = gridDim.x;
+  const int nk2 = a.K / (2 * kBK);                       // k-iterations in pairs
+  const int P = min(min(a.split_parts, nk2), grid);     // grid >= P: see the deadlock note
+  // split only when the last round of whole tiles would be partial
+  const int R = (P > 1 && n_tiles > grid && n_tiles % grid != 0) ? min(a.split_tiles, n_tiles) : 0;
+  const int n_whole = n_tiles - R;
+  const int n_items = n_whole + R * P;
   const bool verify = a.flags & kVerify;
-  const bool skip_gate = false;
+  const bool strict = a.flags & kStrict;
   const uint32_t row_bytes = (uint32_t)a.K * 2;
+  const uint32_t tile_bytes = (uint32_t)(BM * BN * 4);
   const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(a.gathered, (uint32_t)m_pad * row_bytes);
   const __amdgpu_buffer_rsrc_t rO = buffer_rsrc(a.out, (uint32_t)m_pad * (uint32_t)a.N * 2);
-  for (int tile = gj; tile < n_tiles; tile += a.n_gemm) {
-    const int mt = tile / n_tn, nt = tile - mt * n_tn;
-    const int m0 = mt * BM, n0 = nt * BN;
+  const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(a.skws, a.skws_bytes);
+  long long gate = 0;
+  int tiles = 0, parts = 0;
+  const long long t_begin = (long long)now_ticks();
+  for (;;) {
     if (threadIdx.x == 0) {
-      int ok = 1;
-      if (!skip_gate) {
+      const long long t_take = (long long)now_ticks();
+      const int item = error_raised(a.err) ? n_items : fetch_add_relaxed(a.tick_cur, 1);
+      int ok = item < n_items;
+      if (ok) {
+        const int tile = item < n_whole ? item : n_whole + (item - n_whole) / P;
+        const int m0 = (tile / n_tn) * BM;
         const long long t0 = (long long)now_ticks();
         uint32_t polls = 0;
         for (int rb = m0 / kRB; rb < (m0 + BM) / kRB && ok; ++rb)
-          ok = wait_eq(a.counter_cur + rb, kRB, now_ticks() + a.timeout_ticks, a.err, rb, &polls);
-        *gate_ticks += (long long)now_ticks() - t0;
+          ok = wait_eq(a.counter_cur + (size_t)rb * kCtr, kRB, now_ticks() + a.timeout_ticks, a.err, rb, &polls,
+                       kBackoffLong);
+        const long long t_open = (long long)now_ticks();
+        gate += t_open - t0;
         if (verify) {
           atomicAdd(a.stats + ST_GATE_POLLS, (unsigned long long)polls);
           if (ok) atomicAdd(a.stats + ST_GATE_PASSES, 1ull);
         }
+        if ((a.flags & kTrace) && item < a.trace_cap) {
+          long long* tr = a.trace + (size_t)item * 4;
+          tr[0] = blockIdx.x; tr[1] = t_take; tr[2] = t_open; tr[3] = 0;
+        }
       }
-      *sh_flag = ok;
+      sh[0] = item;
+      sh[1] = ok;
     }
     __syncthreads();
-    if (!*sh_flag) break;
+    const int item = __builtin_amdgcn_readfirstlane(sh[0]);
+    if (!sh[1]) break;
     acquire_agent();
+    const bool whole = item < n_whole;
+    const int tile = whole ? item : n_whole + (item - n_whole) / P;
+    const int part = whole ? 0 : (item - n_whole) % P;
+    const int mt = tile / n_tn, nt = tile - mt * n_tn;
+    const int m0 = mt * BM, n0 = nt * BN;
     const int g = __builtin_amdgcn_readfirstlane(a.group_of_rb[m0 / kRB]);
-    const __amdgpu_buffer_rsrc_t rB =
-        buffer_rsrc(a.W + (size_t)g * a.N * a.K, (uint32_t)a.N * row_bytes);
+    const __amdgpu_buffer_rsrc_t rB = buffer_rsrc(a.W + (size_t)g * a.N * a.K, (uint32_t)a.N * row_bytes);
+    const int k0 = whole ? 0 : 2 * (nk2 * part / P);
+    const int k1 = whole ? 2 * nk2 : 2 * (nk2 * (part + 1) / P);
     Acc<BM, BN> acc;
 #pragma unroll
-    for (int i = 0; i < Tile<BM, BN>::FM; ++i)
+    for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < Tile<BM, BN>::FN; ++j) acc.v[i][j] = f32x16{};
-    tile_mainloop<BM, BN>(rA, (uint32_t)m0 * row_bytes, rB, (uint32_t)n0 * row_bytes, a.K, lds0, lds1, acc);
-    tile_store<BM, BN>(rO, a.N, m0, n0, acc, a.inv, a.route_ver);
-    if (threadIdx.x == 0) ++*tiles_done;
+      for (int j = 0; j < T::FN; ++j) acc.v[i][j] = f32x16{};
+    tile_mainloop<BM, BN>(rA, (uint32_t)m0 * row_bytes + (uint32_t)k0 * kRowB, rB,
+                          (uint32_t)n0 * row_bytes + (uint32_t)k0 * kRowB, row_bytes, k1 - k0, lds0, lds1, acc);
+    if (whole) {
+      tile_store<BM, BN>(rO, a.N, m0, n0, acc, a.inv, a.route_ver);
+      ++tiles;
+      if ((a.flags & kTrace) && threadIdx.x == 0 && item < a.trace_cap) a.trace[(size_t)item * 4 + 3] = now_ticks();
+      continue;
+    }
+    // split-K part
+    const int slot = tile - n_whole;
+    const uint32_t base = (uint32_t)slot * (uint32_t)P * tile_bytes;
+    partial_store<BM, BN>(rW, base + (uint32_t)part * tile_bytes, acc, part, P);
+    release_coherent(strict);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const long long t0 = (long long)now_ticks();
+      const int old = fetch_add_relaxed(a.skc_cur + slot, 1);
+      int ok = old < P;
+      if (!ok) raise_error(a.err, kErrProtocol, 0x20000000 | slot);
+      uint32_t polls = 0;
+      if (ok) ok = wait_eq(a.skc_cur + slot, P, now_ticks() + a.timeout_ticks, a.err, 0x20000000 | slot, &polls);
+      gate += (long long)now_ticks() - t0;
+      sh[2] = ok;
+    }
+    __syncthreads();
+    if (!sh[2]) break;
+    partial_reduce<BM, BN>(rW, base, tile_bytes, acc, part, P);
+    tile_store<BM, BN>(rO, a.N, m0, n0, acc, a.inv, a.route_ver, part, P);
+    ++parts;
+    if ((a.flags & kTrace) && threadIdx.x == 0 && item < a.trace_cap) a.trace[(size_t)item * 4 + 3] = now_ticks();
+  }
+  if (threadIdx.x == 0) {
+    wt[WT_GATE] = gate;
+    wt[WT_TILES] = tiles;
+    wt[WT_PARTS] = parts;
+    wt[WT_GEMM_START] = t_begin;
+    wt[WT_P] = P;
   }
 }
 
@@ -233,23 +330,24 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
   __shared__ __attribute__((aligned(16))) char lds0[Tile<BM, BN>::STAGE];
   __shared__ __attribute__((aligned(16))) char lds1[Tile<BM, BN>::STAGE];
   __shared__ const uint16_t* sh_shard[FG_MAX_SHARDS];
-  __shared__ int sh_flag;
-  long long t_start = (long long)now_ticks();
-  long long gate_ticks = 0;
-  int tiles = 0;
+  __shared__ int sh[3];
+  long long* wt = a.wgtime + (size_t)blockIdx.x * kWgTimeFields;
+  const long long t_start = (long long)now_ticks();
+  long long t_comm = 0;
+  if (threadIdx.x == 0) {
+    wt[WT_GATE] = 0; wt[WT_TILES] = 0; wt[WT_PARTS] = 0; wt[WT_GEMM_START] = 0; wt[WT_P] = 1;
+  }
   if (blockIdx.x < a.n_comm) {
     if (threadIdx.x < a.n_shards) sh_shard[threadIdx.x] = a.shards[threadIdx.x];
     __syncthreads();
     comm_role(a, sh_shard);
-  } else {
-    gemm_role<BM, BN>(a, lds0, lds1, &sh_flag, &gate_ticks, &tiles);
+    t_comm = (long long)now_ticks();
   }
+  gemm_role<BM, BN>(a, lds0, lds1, sh, wt);
   if (threadIdx.x == 0) {
-    long long* t = a.wgtime + (size_t)blockIdx.x * 4;
-    t[0] = t_start;
-    t[1] = (long long)now_ticks();
-    t[2] = gate_ticks;
-    t[3] = tiles;
+    wt[WT_START] = t_start;
+    wt[WT_END] = (long long)now_ticks();
+    wt[WT_COMM_END] = t_comm;
   }
 }
 
@@ -286,7 +384,7 @@ struct RouteArgs {
   int* seed;
   int* group_of_rb;
   int* rbcount;              // EXPLICIT: real rows per row block (zero between calls)
-  int* counter_cur;
+  int* counter_cur;          // [rb_cap][kCtr]
   int* elect_cur;
   int* desc;
   int* wgcount;              // TOPK: [n_wg][E + 1] per-workgroup expert counts, picks
@@ -325,7 +423,7 @@ __device__ void route_finish(const RouteArgs& a, int m_pad, const int* goff, int
     }
     a.seed[rb] = sd;
     a.group_of_rb[rb] = g;
-    a.counter_cur[rb] = sd;
+    a.counter_cur[(size_t)rb * kCtr] = sd;
   }
   for (int i = threadIdx.x; i < a.n_shards * a.chunk_cap; i += blockDim.x) a.elect_cur[i] = 0;
   if ((int)threadIdx.x <= n_groups) a.group_off_out[threadIdx.x] = goff[threadIdx.x];
@@ -349,7 +447,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_contig_kernel(RouteArgs a
     const int sd = kRB - real;
     a.seed[rb] = sd;
     a.group_of_rb[rb] = 0;
-    a.counter_cur[rb] = sd;
+    a.counter_cur[(size_t)rb * kCtr] = sd;
   }
   for (int i = tid; i < a.n_shards * a.chunk_cap; i += nth) a.elect_cur[i] = 0;
   if (tid < a.n_shards) a.stream_len[tid] = R;
@@ -532,8 +630,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_place_kernel(RouteAr
 }
 
 // Small helpers: fill, poke (fault injection on a counter).
-__global__ void fill_kernel(int* p, int n, int v) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
+// p[i * stride] = v for i < n
+__global__ void fill_kernel(int* p, int n, int v, int stride) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[(size_t)i * stride] = v;
 }
 __global__ void poke_kernel(int* p, int delta) {
   if (threadIdx.x == 0 && blockIdx.x == 0) p[0] += delta;

@@ -89,13 +89,24 @@ __device__ __forceinline__ int fetch_add_acq_rel(int* p, int v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Exponential s_sleep backoff, 64 to 512 clocks (s_sleep needs an immediate).
-__device__ __forceinline__ void backoff(int& lvl) {
-  if (lvl == 0) __builtin_amdgcn_s_sleep(1);
-  else if (lvl == 1) __builtin_amdgcn_s_sleep(2);
-  else if (lvl == 2) __builtin_amdgcn_s_sleep(4);
-  else __builtin_amdgcn_s_sleep(8);
-  lvl += (lvl < 3);
+// Exponential s_sleep backoff (s_sleep needs an immediate): 64 clocks doubling
+// up to 64 << max_lvl. Signal waits whose latency matters stop at 512 clocks
+// (kBackoffShort); gate waits, which last tens of microseconds and have many
+// waiters, go up to 4096 clocks (kBackoffLong) so that their polls do not load
+// the memory channel the producers' counter updates go to.
+constexpr int kBackoffShort = 3;
+constexpr int kBackoffLong = 6;
+__device__ __forceinline__ void backoff(int& lvl, int max_lvl) {
+  switch (lvl) {
+    case 0: __builtin_amdgcn_s_sleep(1); break;
+    case 1: __builtin_amdgcn_s_sleep(2); break;
+    case 2: __builtin_amdgcn_s_sleep(4); break;
+    case 3: __builtin_amdgcn_s_sleep(8); break;
+    case 4: __builtin_amdgcn_s_sleep(16); break;
+    case 5: __builtin_amdgcn_s_sleep(32); break;
+    default: __builtin_amdgcn_s_sleep(64); break;
+  }
+  lvl += (lvl < max_lvl);
 }
 
 // Error reporting shared by every kernel: first error wins; the code is also
@@ -122,7 +133,7 @@ constexpr int kErrProtocol = -6;
 // and backoff. Returns 1 on success, 0 on timeout / error elsewhere / overshoot.
 // On success the caller issues acquire_agent(). *polls counts the loads.
 __device__ __forceinline__ int wait_eq(const int* p, int target, uint64_t deadline,
-                                       const ErrorSink& e, int id, uint32_t* polls) {
+                                       const ErrorSink& e, int id, uint32_t* polls, int max_lvl = kBackoffShort) {
   int lvl = 0;
   uint32_t n = 0;
   while (true) {
@@ -134,7 +145,7 @@ __device__ __forceinline__ int wait_eq(const int* p, int target, uint64_t deadli
       if (now_ticks() > deadline) { raise_error(e, kErrTimeout, id); *polls += n; return 0; }
       if (error_raised(e)) { *polls += n; return 0; }
     }
-    backoff(lvl);
+    backoff(lvl, max_lvl);
   }
 }
 
@@ -152,7 +163,7 @@ __device__ __forceinline__ int wait_ge(const int* p, int seq, uint64_t deadline,
       if (now_ticks() > deadline) { raise_error(e, kErrTimeout, id); *polls += n; return 0; }
       if (error_raised(e)) { *polls += n; return 0; }
     }
-    backoff(lvl);
+    backoff(lvl, kBackoffShort);
   }
 }
 

@@ -23,6 +23,8 @@ CALL_GEMM_ONLY = 1 << 1
 CALL_VERIFY = 1 << 2
 CALL_STRICT = 1 << 3
 CALL_SAME_ROUTE = 1 << 4
+CALL_TRACE = 1 << 5
+COUNTER_STRIDE = 64      # int32 per arrival counter in the control plane (FG_COUNTER_STRIDE)
 FAULT_SEED_LOW = 1 << 8
 FAULT_SEED_HIGH = 1 << 9
 FAULT_DROP_PUBLISH = 1 << 10
@@ -38,7 +40,8 @@ class FgConfig(C.Structure):
                 ("N", C.c_int32), ("n_groups", C.c_int32), ("n_comm_wg", C.c_int32),
                 ("n_gemm_wg", C.c_int32), ("tile_n", C.c_int32), ("timeout_ns", C.c_int64),
                 ("stress_producers", C.c_int32), ("stress_consumers", C.c_int32),
-                ("stress_max_chunks", C.c_int32), ("reserved", C.c_int32)]
+                ("stress_max_chunks", C.c_int32), ("split_parts", C.c_int32), ("split_tiles", C.c_int32),
+                ("reserved", C.c_int32)]
 
 
 class FgRoute(C.Structure):
@@ -57,14 +60,17 @@ class FgStats(C.Structure):
                 ("t_gemm_busy_us", C.c_double), ("t_gate_wait_us", C.c_double),
                 ("t_barrier_us", C.c_double), ("t_rtt_us", C.c_double),
                 ("n_comm_wg", C.c_int32), ("n_gemm_wg", C.c_int32), ("cu_count", C.c_int32),
-                ("m_pad_cap", C.c_int32)]
+                ("m_pad_cap", C.c_int32), ("tiles_whole", C.c_int32), ("tiles_split", C.c_int32),
+                ("split_parts", C.c_int32), ("reserved", C.c_int32)]
 
 
 class FgViews(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("slot", "counter", "elect", "pub_count", "seed", "inv_row",
                                           "group_of_rb", "src_row", "dst_row", "stream_len", "group_off",
                                           "bslot", "stress_slot", "stress_pub")] + [
-        ("chunk_cap", C.c_int32), ("rb_cap", C.c_int32), ("m_pad_cap", C.c_int32), ("route_ver", C.c_uint32)]
+        ("chunk_cap", C.c_int32), ("rb_cap", C.c_int32), ("m_pad_cap", C.c_int32), ("route_ver", C.c_uint32),
+        ("wg_time", C.c_void_p), ("trace", C.c_void_p), ("rb_time", C.c_void_p), ("grid", C.c_int32),
+        ("trace_cap", C.c_int32), ("wall_khz", C.c_int64)]
 
 
 class FgError(RuntimeError):
@@ -124,9 +130,9 @@ def _ptr(t: torch.Tensor) -> C.c_void_p:
 
 
 def make_config(n_shards, max_rows_per_shard, K, N, n_groups=1, n_comm_wg=0, n_gemm_wg=0, tile_n=0,
-                timeout_ns=0, stress=(0, 0, 0)) -> FgConfig:
+                timeout_ns=0, stress=(0, 0, 0), split_parts=0, split_tiles=0) -> FgConfig:
     return FgConfig(n_shards, max_rows_per_shard, K, N, n_groups, n_comm_wg, n_gemm_wg, tile_n, timeout_ns,
-                    stress[0], stress[1], stress[2], 0)
+                    stress[0], stress[1], stress[2], split_parts, split_tiles, 0)
 
 
 def capacity(cfg: FgConfig) -> int:
@@ -193,6 +199,21 @@ class Context:
         """Copy `count` int32 of library-owned device memory to a CPU tensor."""
         torch.cuda.synchronize(self.device)
         return _as_device_tensor(ptr, count, self.device).clone().cpu()
+
+    def read_timeline(self) -> dict:
+        """Timing records of the last fused kernel, in microseconds from the
+        earliest workgroup start: per workgroup (fg_views wg_time) and, after a
+        call with CALL_TRACE, per compute item and per row block."""
+        v = self.views()
+        us = 1000.0 / v.wall_khz
+        wg = self.read_i32(v.wg_time, 2 * 8 * v.grid).view(torch.int64).reshape(v.grid, 8).numpy().copy()
+        t0 = wg[:, 0].min()
+        out = dict(wg=wg, t0=t0, us_per_tick=us)
+        if v.trace_cap:
+            tr = self.read_i32(v.trace, 2 * 4 * v.trace_cap).view(torch.int64).reshape(v.trace_cap, 4).numpy().copy()
+            out["trace"] = tr
+            out["rb_time"] = self.read_i32(v.rb_time, 2 * v.rb_cap).view(torch.int64).numpy().copy()
+        return out
 
     def read_inverse_map(self) -> torch.Tensor:
         """The inverse map of the route in use: gathered row -> (shard << 24 |

@@ -86,10 +86,12 @@ def ep_case(seed, n_shards, tokens, K, N, n_experts=64, topk=8, n_local=8, exper
                 expert_base=expert_base)
 
 
-def make_ctx(case: Case, *, n_comm=0, n_gemm=0, tile_n=0, timeout_ns=0, max_rows=None) -> fg.Context:
+def make_ctx(case: Case, *, n_comm=0, n_gemm=0, tile_n=0, timeout_ns=0, max_rows=None, split_parts=0,
+             split_tiles=0) -> fg.Context:
     max_rows = max_rows or max(int(case.lay.stream_len.max()), case.rows_per_shard)
     cfg = fg.make_config(len(case.shards), max_rows, case.K, case.N, n_groups=case.n_groups,
-                         n_comm_wg=n_comm, n_gemm_wg=n_gemm, tile_n=tile_n, timeout_ns=timeout_ns)
+                         n_comm_wg=n_comm, n_gemm_wg=n_gemm, tile_n=tile_n, timeout_ns=timeout_ns,
+                         split_parts=split_parts, split_tiles=split_tiles)
     return fg.Context(cfg)
 
 
@@ -118,7 +120,7 @@ def control_plane(ctx: fg.Context, n_shards: int):
     S, cc, rbc = n_shards, v.chunk_cap, v.rb_cap
     return dict(
         slot=ctx.read_i32(v.slot, S * cc).numpy().reshape(S, cc),
-        counter=ctx.read_i32(v.counter, 2 * rbc).numpy().reshape(2, rbc),
+        counter=ctx.read_i32(v.counter, 2 * rbc * fg.COUNTER_STRIDE).numpy().reshape(2, rbc, -1)[:, :, 0].copy(),
         elect=ctx.read_i32(v.elect, 2 * S * cc).numpy().reshape(2, S, cc),
         pub_count=ctx.read_i32(v.pub_count, S * cc).numpy().reshape(S, cc),
         seed=ctx.read_i32(v.seed, rbc).numpy(),

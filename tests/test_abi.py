@@ -52,3 +52,41 @@ def test_null_arguments_rejected_without_gpu():
     assert lib.fg_init(None, 0, None) == fg.EINVAL
     assert lib.fg_destroy(None) == fg.EINVAL
     assert lib.fg_stats(None, None, 0) == fg.EINVAL
+
+
+def _c_layout(tmp_path):
+    """sizeof / offsetof of every ABI struct field, from the C header compiled with gcc."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("gcc or the ROCm headers are not available")
+    structs = {"fg_config": fg.FgConfig, "fg_stats_t": fg.FgStats, "fg_route": fg.FgRoute, "fg_views_t": fg.FgViews}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "fg.h"', 'int main(void) {']
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ['  return 0;', '}']
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                    str(src), "-o", str(exe)], check=True, capture_output=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    return structs, dict((" ".join(l.split()[:2]), int(l.split()[2])) for l in out.splitlines())
+
+
+def test_binding_structs_match_the_header(tmp_path):
+    structs, c = _c_layout(tmp_path)
+    for cname, py in structs.items():
+        assert C.sizeof(py) == c[f"{cname} size"], cname
+        for fname, _ in py._fields_:
+            assert getattr(py, fname).offset == c[f"{cname} {fname}"], (cname, fname)
+
+
+def test_binding_constants_match_the_header():
+    src = open(os.path.join(ROOT, "include", "fg.h")).read()
+    defs = dict(re.findall(r"^#define (FG_\w+) (\d+)", src, re.M))
+    assert int(defs["FG_COUNTER_STRIDE"]) == fg.COUNTER_STRIDE
+    for name, val in re.findall(r"^\s+(FG_(?:CALL|FAULT)_\w+) = 1u << (\d+)", src, re.M):
+        assert getattr(fg, name[3:]) == 1 << int(val), name

@@ -1,0 +1,120 @@
+"""The compute schedule: ticket-dispatched tiles, communication workgroups that
+join the compute role, and the split-K tail (tail tiles cut into k-ranges whose
+fp32 partials are summed in a fixed order). Every case is checked against the
+CPU oracle element by element; the split path must also be deterministic."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sync_protocols_amd import fg
+from fg_harness import (bits, buffers, check_control_plane, check_gathered, check_out, check_route, control_plane,
+                        dense_case, ep_case, log, make_ctx, run_iters)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(case, ctx, iters, flags=fg.CALL_VERIFY):
+    gathered, out = buffers(ctx, case)
+    st = run_iters(ctx, case, gathered, out, iters, flags=flags)
+    cp = control_plane(ctx, len(case.shards))
+    check_route(case, cp)
+    check_control_plane(case, cp, iters, iters if flags & fg.CALL_VERIFY else None)
+    check_gathered(case, gathered, poisoned=True)
+    r = check_out(case, out)
+    return st, out, r
+
+
+def _expected_split(case, grid, P, split_tiles, bm, bn):
+    """(whole tiles, split tiles, parts per split tile) of the documented schedule:
+    a tail is split only when the tiles leave the grid's last round partial; the
+    parts are capped by the k-iteration pairs and by the grid."""
+    n_tiles = (case.lay.m_pad // bm) * (case.N // bn)
+    p_eff = min(P, case.K // 128, grid)
+    if p_eff <= 1 or n_tiles <= grid or n_tiles % grid == 0:
+        return n_tiles, 0, 1
+    r = min(split_tiles if split_tiles else -(-grid // P), n_tiles)
+    return n_tiles - r, r, p_eff
+
+
+@pytest.mark.parametrize("P,split_tiles", [(2, 0), (3, 0), (4, 0), (8, 0), (4, 32), (3, 5)])
+def test_split_tail_matches_oracle(P, split_tiles):
+    log(f"split-K tail: 4 x 512 rows (32 tiles), K=N=1024, grid 2+5, P={P}, split_tiles={split_tiles}")
+    case = dense_case(51, 4, 512, 1024, 1024)
+    ctx = make_ctx(case, n_comm=2, n_gemm=5, split_parts=P, split_tiles=split_tiles)
+    st, _, r = _check(case, ctx, 3)
+    whole, split, p_eff = _expected_split(case, 7, P, split_tiles, 256, 256)
+    assert (st.tiles_whole, st.tiles_split, st.split_parts) == (whole, split, p_eff)
+    assert split > 0
+    log(f"split ok: whole={st.tiles_whole} split={st.tiles_split} P={st.split_parts} max|d|={r['max_abs']:.3g}")
+    ctx.close()
+
+
+def test_split_tail_is_deterministic():
+    log("split-K tail: outputs of repeated calls are bit-identical")
+    case = dense_case(52, 4, 512, 1024, 1024)
+    ctx = make_ctx(case, n_comm=2, n_gemm=5, split_parts=4, split_tiles=32)
+    gathered, out = buffers(ctx, case)
+    outs = []
+    for _ in range(3):
+        run_iters(ctx, case, gathered, out, 1, flags=0)
+        outs.append(bits(out[:case.lay.m_pad]).copy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    check_out(case, out)
+    ctx.close()
+
+
+def test_split_parts_capped_by_k():
+    log("split-K tail with fewer k-iteration pairs than parts: K=256 -> 2 parts")
+    case = dense_case(53, 4, 512, 256, 1024)
+    ctx = make_ctx(case, n_comm=2, n_gemm=5, split_parts=4, split_tiles=32)
+    st, _, _ = _check(case, ctx, 2)
+    assert st.split_parts == 2 and st.tiles_split > 0
+    ctx.close()
+
+
+def test_no_split_whole_tiles_only():
+    log("split-K off (split_parts=1): whole tiles only")
+    case = dense_case(54, 4, 512, 1024, 1024)
+    ctx = make_ctx(case, n_comm=2, n_gemm=5, split_parts=1)
+    st, _, _ = _check(case, ctx, 2)
+    assert st.tiles_split == 0 and st.tiles_whole == 32
+    ctx.close()
+
+
+def test_split_tail_tile_n_128_ragged():
+    log("split-K tail, BN 128, ragged rows: 5 x 77 rows, K=512, N=384")
+    case = dense_case(55, 5, 77, 512, 384)
+    ctx = make_ctx(case, n_comm=1, n_gemm=3, tile_n=128, split_parts=4, split_tiles=6)
+    st, _, _ = _check(case, ctx, 3)
+    assert st.tiles_split > 0
+    ctx.close()
+
+
+def test_split_tail_expert_groups():
+    log("split-K tail on grouped expert tiles: 8 shards x 64 tokens, grid 1+3")
+    case = ep_case(56, 8, 64, 512, 256)
+    n_tiles = case.lay.m_pad // 128
+    grid = next(g for g in (4, 3, 5, 6, 7) if n_tiles > g and n_tiles % g)
+    ctx = make_ctx(case, n_comm=1, n_gemm=grid - 1, split_parts=4, split_tiles=8)
+    st, _, _ = _check(case, ctx, 3)
+    assert (st.tiles_whole, st.tiles_split, st.split_parts) == _expected_split(case, grid, 4, 8, 128, 256)
+    assert st.tiles_split > 0
+    ctx.close()
+
+
+def test_strict_split_tail():
+    log("split-K tail with formal release fences")
+    case = dense_case(57, 4, 512, 1024, 1024)
+    ctx = make_ctx(case, n_comm=2, n_gemm=5, split_parts=4, split_tiles=8)
+    _check(case, ctx, 2, flags=fg.CALL_VERIFY | fg.CALL_STRICT)
+    ctx.close()
+
+
+def test_comm_workgroups_join_compute():
+    log("one communication workgroup, one compute workgroup: the comm workgroup takes tiles after its rows")
+    case = dense_case(58, 2, 512, 512, 512)
+    ctx = make_ctx(case, n_comm=1, n_gemm=1, split_parts=1)
+    st, _, _ = _check(case, ctx, 2)
+    assert st.tiles_whole == (1024 // 256) * (512 // 256)
+    ctx.close()
