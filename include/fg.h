@@ -83,7 +83,7 @@ typedef struct {
   int32_t K;                   /* row width in bf16 elements; multiple of 128 */
   int32_t N;                   /* GEMM output width; multiple of 128 */
   int32_t n_groups;            /* 1 = one dense weight; >1 = one weight per group (expert) */
-  int32_t n_comm_wg;           /* communication workgroups (0 = default 64); they join the compute role
+  int32_t n_comm_wg;           /* communication workgroups (0 = default 128); they join the compute role
                                   once their rows are copied */
   int32_t n_gemm_wg;           /* dedicated compute workgroups (0 = CUs - n_comm_wg) */
   int32_t tile_n;              /* GEMM tile width 128 or 256 (0 = default) */
@@ -96,7 +96,8 @@ typedef struct {
   int32_t split_tiles;         /* split-K tail: at most this many tail tiles split (0 = default: one
                                   part per workgroup of the grid); the library allocates
                                   split_tiles * split_parts * 256 * tile_n * 4 bytes of partial sums */
-  int32_t reserved;
+  int32_t tile_order;          /* 0 = tiles grouped per XCD when the grid is a multiple of 8 (default);
+                                  1 = one row-block-major list */
 } fg_config;
 
 typedef enum {
@@ -141,7 +142,8 @@ typedef struct {
   double t_rtt_us;                /* last fg_pingpong: device round trip */
   int32_t n_comm_wg, n_gemm_wg, cu_count, m_pad_cap;
   int32_t tiles_whole, tiles_split; /* last fused kernel: whole tiles, tiles computed as split-K parts */
-  int32_t split_parts, reserved;
+  int32_t split_parts, reserved;  /* split_parts: k-ranges per split tile (1 when none is split) */
+  double clock_mhz;               /* last fused kernel: shader-clock cycles / wall time, over all workgroups */
 } fg_stats_t;
 
 /* Read-only device views of the library-owned control plane (for tests that
@@ -166,8 +168,9 @@ typedef struct {
   uint32_t route_ver;         /* version of the route in use */
   /* Timing observation (device wall clock, wall_khz ticks per ms), written by
    * the last fused kernel: */
-  const int64_t* wg_time;     /* [grid][8]: start, end, wait ticks, whole tiles, end of the copy role,
-                                 split parts, start of the compute role, parts per split tile */
+  const int64_t* wg_time;     /* [grid][12]: start, end, wait ticks, whole tiles, end of the copy role,
+                                 split parts, start of the compute role, parts per split tile, shader-clock
+                                 counter at start and at end, 2 unused */
   const int64_t* trace;       /* FG_CALL_TRACE: [trace_cap][4] per compute item in ticket order:
                                  workgroup, ticket taken, gate open, item done */
   const int64_t* rb_time;     /* FG_CALL_TRACE: [rb_cap] time the row block's counter reached 128 */

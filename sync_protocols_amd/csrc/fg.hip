@@ -21,7 +21,7 @@ namespace {
 // Copy workgroups: the gather is latency-bound per workgroup (load, write-through
 // store, acknowledgement, counter add), so many workgroups keep enough bytes in
 // flight; they join the compute role when their rows are copied.
-constexpr int kDefaultComm = 64;
+constexpr int kDefaultComm = 128;
 constexpr int kDefaultSplitParts = 4;
 constexpr int64_t kDefaultTimeoutNs = 2000000000LL;
 
@@ -43,7 +43,7 @@ struct Plane {
   int* wgcount;
   int* wgbase;
   int* ticket;
-  int* gtick;      // [2] x 64 ints: compute-item tickets, one per parity
+  int* gtick;      // [2] x kTickInts: compute-item tickets (global + one per XCD), one set per parity
   int* skc;        // [2][split_tiles] split-K part counters
   long long* trace;    // [trace_cap][4]
   long long* rb_time;  // [rb_cap]
@@ -116,6 +116,7 @@ static bool config_ok(const fg_config* c) {
   if (c->n_comm_wg < 0 || c->n_gemm_wg < 0) return false;
   if (c->timeout_ns < 0) return false;
   if (c->split_parts < 0 || c->split_parts > 8 || c->split_tiles < 0 || c->split_tiles > 4096) return false;
+  if (c->tile_order < 0 || c->tile_order > 1) return false;
   if (c->stress_producers < 0 || c->stress_consumers < 0 || c->stress_max_chunks < 0) return false;
   const long long m = (long long)c->n_shards * c->max_rows_per_shard + (long long)c->n_groups * FG_ROW_BLOCK;
   if (m * c->K * 2 >= (1ll << 32)) return false;   // 32-bit buffer offsets
@@ -304,7 +305,7 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
                o_inv = take((size_t)ctx->m_pad_cap * 8), o_grp = take((size_t)ctx->rb_cap * 4),
                o_src = take(nrs * 4), o_dst = take(nrs * 4), o_slen = take((size_t)S * 4),
                o_goff = take((FG_MAX_GROUPS + 1) * 4), o_rbc = take((size_t)ctx->rb_cap * 4), o_desc = take(64),
-               o_wgc = take(wgc), o_wgb = take(wgc), o_tick = take(64), o_gtick = take(512),
+               o_wgc = take(wgc), o_wgb = take(wgc), o_tick = take(64), o_gtick = take(2 * kTickInts * 4),
                o_skc = take(2 * (size_t)std::max(1, ctx->split_tiles) * 4),
                o_trace = take((size_t)ctx->trace_cap * 32), o_rbt = take((size_t)ctx->rb_cap * 8),
                o_err = take(64), o_stats = take(ST_COUNT * 8), o_bslot = take((size_t)S * S * 4),
@@ -440,8 +441,9 @@ fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route*
   a.rows_per_batch = upr <= 2 ? 16 : upr <= 4 ? 8 : upr <= 8 ? 4 : upr <= 16 ? 2 : 1;
   a.flags = flags;
   a.timeout_ticks = timeout_ticks(ctx);
-  a.tick_cur = ctx->p.gtick + cur * 64;
-  a.tick_nxt = ctx->p.gtick + nxt * 64;
+  a.tick_cur = ctx->p.gtick + cur * kTickInts;
+  a.tick_nxt = ctx->p.gtick + nxt * kTickInts;
+  a.tile_order = c.tile_order;
   a.skc_cur = ctx->p.skc + (size_t)cur * std::max(1, ctx->split_tiles);
   a.skc_nxt = ctx->p.skc + (size_t)nxt * std::max(1, ctx->split_tiles);
   a.skws = ctx->skws;
@@ -556,11 +558,14 @@ fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait) {
     double busy = 0, waitt = 0;
     long long tiles = 0, parts = 0, peff = 1;
     int nw = 0;
+    double cyc = 0, wall = 0;
     for (int i = 0; i < g; ++i) {
       const long long* t = wg + (size_t)i * kWgTimeFields;
       t0 = std::min(t0, t[WT_START]);
       t1 = std::max(t1, t[WT_END]);
       if (i < ctx->n_comm) c1 = std::max(c1, t[WT_COMM_END]);
+      cyc += (double)(t[WT_CLK1] - t[WT_CLK0]);
+      wall += (double)(t[WT_END] - t[WT_START]);
       if (t[WT_TILES] + t[WT_PARTS] > 0) {
         g0 = g0 < 0 ? t[WT_GEMM_START] : std::min(g0, t[WT_GEMM_START]);
         g1 = std::max(g1, t[WT_END]);
@@ -581,6 +586,7 @@ fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait) {
       out->t_gemm_busy_us = units > 0 ? busy / units * us_per_tick : 0.0;
       out->t_gate_wait_us = waitt / nw * us_per_tick;
     }
+    if (wall > 0) out->clock_mhz = cyc / wall * (double)ctx->wall_khz / 1000.0;
     out->tiles_whole = (int32_t)tiles;
     out->tiles_split = (int32_t)(parts / P);
     out->split_parts = (int32_t)P;

@@ -34,8 +34,12 @@ constexpr int kRowB = kBK * 2;      // bytes per tile row per stage: one 128-byt
 constexpr int kRowsPerLoad = 1024 / kRowB;   // rows covered by one 64-lane 16-byte load
 constexpr int kKSteps = kBK / 16;   // MFMA k-steps per stage
 
-constexpr int kWaves = 8;           // waves per workgroup: two per SIMD, so one wave's memory
-                                    // instructions issue while the other's MFMAs run
+#ifndef FG_WAVES
+#define FG_WAVES 8
+#endif
+constexpr int kWaves = FG_WAVES;    // waves per workgroup: 8 = two per SIMD, so one wave's memory
+                                    // instructions issue while the other's MFMAs run; 4 = one per SIMD
+                                    // with a 128 x 128 wave tile (fewer LDS reads per MFMA)
 
 template <int BM, int BN>
 struct Tile {
@@ -274,13 +278,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // Store the tile: padding rows (no current inverse-map entry) are written as zeros.
-// rO: output rows [*, N] (row stride N*2 bytes); m0, n0: tile origin. Only the
-// wave fragments f (f = fm * FN + fn) with f % P == part are stored (P = 1:
-// all of them).
+// rO: output rows [*, N] (row stride N*2 bytes); m0, n0: tile origin.
 template <int BM, int BN>
 __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int m0, int n0,
-                                           const Acc<BM, BN>& acc, const unsigned long long* inv, uint32_t ver,
-                                           int part = 0, int P = 1) {
+                                           const Acc<BM, BN>& acc, const unsigned long long* inv, uint32_t ver) {
   using T = Tile<BM, BN>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / T::WGN, wn = wave % T::WGN;
@@ -292,7 +293,6 @@ __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int
     const uint32_t row_off = (uint32_t)m * (uint32_t)N * 2;
 #pragma unroll
     for (int fn = 0; fn < T::FN; ++fn) {
-      if ((fm * T::FN + fn) % P != part) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + wn * T::WN + fn * 32 + 8 * g + 4 * kh;
@@ -317,11 +317,10 @@ __device__ __forceinline__ uint32_t partial_off(int wave, int f, int g, int lane
   return (uint32_t)((((wave * (T::FM * T::FN) + f) * 4 + g) * 64 + lane) * 16);
 }
 
-// Store the fragments this part does NOT reduce itself (f % P != part) into
-// its block at byte offset `base`, with device-coherent write-through stores.
+// Store all of this part's fragments into its block at byte offset `base`,
+// with device-coherent write-through stores (the accumulators are only read).
 template <int BM, int BN>
-__device__ __forceinline__ void partial_store(__amdgpu_buffer_rsrc_t rW, uint32_t base, const Acc<BM, BN>& acc,
-                                              int part, int P) {
+__device__ __forceinline__ void partial_store(__amdgpu_buffer_rsrc_t rW, uint32_t base, const Acc<BM, BN>& acc) {
   using T = Tile<BM, BN>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -330,7 +329,6 @@ __device__ __forceinline__ void partial_store(__amdgpu_buffer_rsrc_t rW, uint32_
 #pragma unroll
     for (int fn = 0; fn < T::FN; ++fn) {
       const int f = fm * T::FN + fn;
-      if (f % P == part) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         // whole-vector bit casts only: a bit cast of a vector element lvalue
@@ -342,40 +340,46 @@ __device__ __forceinline__ void partial_store(__amdgpu_buffer_rsrc_t rW, uint32_
     }
 }
 
-// Reduce the fragments this part owns (f % P == part): its own partial (in
-// registers) plus the other parts' in part order. The owner of a fragment is
-// fixed by f, so the order of the fp32 additions, and with it the result,
-// does not depend on which workgroup ran which part. `base` = byte offset of
-// part 0's block; blocks are `tile_bytes` apart. Loads use the device-coherent
-// policy: the blocks were written by other workgroups, possibly on other XCDs.
+// For the fragments this part owns (f % P == part): sum the P partials in
+// part order 0..P-1, round to bf16 and store them as tile_store does. The
+// order of the fp32 additions is fixed, so the result does not depend on
+// which workgroup ran which part. `base` = byte offset of part 0's block;
+// blocks are `tile_bytes` apart. Loads use the device-coherent policy: the
+// blocks were written by other workgroups, possibly on other XCDs.
 template <int BM, int BN>
-__device__ __forceinline__ void partial_reduce(__amdgpu_buffer_rsrc_t rW, uint32_t base, uint32_t tile_bytes,
-                                               Acc<BM, BN>& acc, int part, int P) {
+__device__ __forceinline__ void partial_sum_store(__amdgpu_buffer_rsrc_t rW, uint32_t base, uint32_t tile_bytes,
+                                                  int part, int P, __amdgpu_buffer_rsrc_t rO, int N, int m0, int n0,
+                                                  const unsigned long long* inv, uint32_t ver) {
   using T = Tile<BM, BN>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / T::WGN, wn = wave % T::WGN;
+  const int lr = lane & 31, kh = lane >> 5;
 #pragma unroll
-  for (int fm = 0; fm < T::FM; ++fm)
+  for (int fm = 0; fm < T::FM; ++fm) {
+    const int m = m0 + wm * T::WM + fm * 32 + lr;
+    const bool pad = (uint32_t)(inv[m] >> 32) != ver;
+    const uint32_t row_off = (uint32_t)m * (uint32_t)N * 2;
 #pragma unroll
     for (int fn = 0; fn < T::FN; ++fn) {
       const int f = fm * T::FN + fn;
       if (f % P != part) continue;
-#pragma unroll 1
-      for (int q = 0; q < P; ++q) {
-        if (q == part) continue;
-        const uint32_t off = base + (uint32_t)q * tile_bytes;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 x = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(rW, off + partial_off<BM, BN>(wave, f, g, lane), 0,
-                                                           kPolCoherentStream));
-          acc.v[fm][fn][4 * g + 0] += x[0];
-          acc.v[fm][fn][4 * g + 1] += x[1];
-          acc.v[fm][fn][4 * g + 2] += x[2];
-          acc.v[fm][fn][4 * g + 3] += x[3];
-        }
+      for (int g = 0; g < 4; ++g) {
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+        for (int q = 0; q < P; ++q)
+          sum += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rW, base + (uint32_t)q * tile_bytes + partial_off<BM, BN>(wave, f, g, lane),
+                                               0, kPolCoherentStream));
+        const int n = n0 + wn * T::WN + fn * 32 + 8 * g + 4 * kh;
+        v2i w;
+        w[0] = pad ? 0 : (int)pack_bf16x2(sum[0], sum[1]);
+        w[1] = pad ? 0 : (int)pack_bf16x2(sum[2], sum[3]);
+        __builtin_amdgcn_raw_buffer_store_b64(w, rO, row_off + (uint32_t)n * 2, 0, 0);
       }
     }
+  }
 }
 
 }  // namespace fg

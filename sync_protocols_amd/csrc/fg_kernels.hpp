@@ -13,6 +13,8 @@ constexpr int kRB = FG_ROW_BLOCK;
 constexpr int kCtr = FG_COUNTER_STRIDE;  // arrival counters sit 256 bytes apart: a gate's pollers and
                                          // the copy role's adds then spread over memory channels
 constexpr int kThreads = 64 * kWaves;   // workgroup size of the fused kernel
+constexpr int kXcds = 8;                // XCDs of the part; workgroup i runs on XCD i % 8
+constexpr int kTickInts = 1024;         // ticket block per parity: global ticket + one per XCD, 256 B apart
 
 // per-call flag bits as seen by the device
 constexpr uint32_t kCommOnly = FG_CALL_COMM_ONLY;
@@ -63,8 +65,9 @@ struct FusedArgs {
   uint32_t flags;
   uint64_t timeout_ticks;
   // compute schedule: tickets and the split-K tail
-  int* tick_cur;             // [1] next work item of this call (zero at kernel start)
-  int* tick_nxt;             // [1] the other parity, zeroed here for the next call
+  int* tick_cur;             // [kTickInts]: [0] next split-K part, [64 (1 + x)] next entry of list x
+  int* tick_nxt;             // the other parity, zeroed here for the next call
+  int tile_order;            // 0: XCD-grouped lists when the grid is a multiple of 8; 1: one list
   int* skc_cur;              // [split_tiles] parts finished per split tile (zero at kernel start)
   int* skc_nxt;
   float* skws;               // split_tiles x split_parts partial blocks of BM x BN floats
@@ -77,7 +80,10 @@ struct FusedArgs {
 };
 
 // Per-workgroup timing record (device clock ticks).
-enum { WT_START = 0, WT_END, WT_GATE, WT_TILES, WT_COMM_END, WT_PARTS, WT_GEMM_START, WT_P, kWgTimeFields = 8 };
+// WT_CLK0 / WT_CLK1: shader-clock counter (s_memtime) at start and end, for the
+// effective clock = cycles / wall time.
+enum { WT_START = 0, WT_END, WT_GATE, WT_TILES, WT_COMM_END, WT_PARTS, WT_GEMM_START, WT_P, WT_CLK0, WT_CLK1,
+       kWgTimeFields = 12 };
 
 // ---------------------------------------------------------------------------
 // Communication role ("PCIe sync protocols" §3 election + publish, §4 chunk
@@ -132,7 +138,7 @@ __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
   for (int i = cw * kThreads + threadIdx.x; i < a.n_shards * a.chunk_cap; i += a.n_comm * kThreads)
     a.elect_nxt[i] = 0;
   for (int i = cw * kThreads + threadIdx.x; i < a.split_tiles; i += a.n_comm * kThreads) a.skc_nxt[i] = 0;
-  if (cw == 0 && threadIdx.x == 0) a.tick_nxt[0] = 0;
+  if (cw == 0 && threadIdx.x <= kXcds) a.tick_nxt[threadIdx.x * 64] = 0;
   if (a.flags & kGemmOnly) return;
 
   const int m_pad = __builtin_amdgcn_readfirstlane(a.desc[0]);
@@ -197,39 +203,82 @@ __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
 }
 
 // ---------------------------------------------------------------------------
-// Compute role ("PCIe sync protocols" §5 gate). Work items are handed out by
-// one ticket counter, in row-block-major tile order (the order in which the
-// communication role delivers row blocks). Items 0 .. n_whole-1 are whole
-// tiles; when the tiles do not fill a whole number of rounds of the grid, the
-// last R tiles of the order are split into P k-ranges ("parts"), one item
-// each, so that the tail of the schedule is spread over the grid instead of
-// leaving most workgroups idle. Every item first waits until each
-// row block it reads has counter == 128, acquires, and runs the MFMA tile.
-// A part stores the fragments it does not own to the partial workspace,
-// counts itself in the tile's part counter, waits until all P parts have
-// done so, then sums the partials of the fragments it owns and stores them.
-// Communication workgroups enter this role once their rows are copied.
+// Compute role ("PCIe sync protocols" §5 gate).
 //
-// Deadlock freedom: parts of a tile are consecutive tickets, so at most one
-// tile at a time has parts not yet taken; its waiting holders are at most P-1
-// workgroups, and every other workgroup either computes (and finishes) or
+// Work lists. With a grid that is a multiple of the 8 XCDs (workgroup i runs
+// on XCD i % 8), XCD x owns the 256-row slabs s = x, x + 8, x + 16, ... and
+// hands out their tiles from its own ticket counter, in groups of GS slabs x
+// GN column tiles, GS * GN = workgroups per XCD: the tiles that run at the
+// same time on one XCD share A and W lines in that XCD's L2. Slabs are walked
+// in increasing order, the order in which the copy role delivers row blocks.
+// (Other grids use one list, x = 0, in row-block-major order.)
+//
+// Split-K tail. When the tiles leave the grid's last round partial, or the
+// XCD lists differ in length, the last r tiles of every XCD list are split
+// into P k-ranges ("parts"); all parts sit in one global ticket queue, tile by
+// tile, taken by any workgroup whose own list is empty. A part stores all
+// its fragments to the partial workspace, counts itself in the tile's part
+// counter, waits until all P parts have done so, then sums the P partials of
+// the fragments it owns, in part order (so deterministic), and stores them.
+//
+// Every item first waits until each row block it reads has counter == 128,
+// acquires, and runs the MFMA tile. Communication workgroups enter this role
+// once their rows are copied.
+//
+// Deadlock freedom: parts of a tile are consecutive tickets of the one part
+// queue, so at most one tile at a time has parts not yet taken; its waiting
+// holders are at most P-1 workgroups, and every other workgroup either
+// computes (and finishes), waits at a gate (whose supplier never waits), or
 // waits on a tile whose parts are all taken. With P <= grid some workgroup is
 // always free to take the remaining parts.
 // ---------------------------------------------------------------------------
+struct TileLists {
+  int nx;        // lists (8 or 1)
+  int n_tn;      // column tiles
+  int n_slabs;   // row slabs of BM rows
+  int GN, GS;    // group shape: GS slabs x GN column tiles
+  int r;         // split tiles taken from the end of every list
+  __device__ int slabs_of(int x) const { return (n_slabs - x + nx - 1) / nx; }
+  __device__ int len(int x) const { return slabs_of(x) * n_tn; }
+  // tile index (slab * n_tn + column tile) of entry j of list x
+  __device__ int tile(int x, int j) const {
+    const int ns = slabs_of(x);
+    const int g = j / (GS * n_tn);
+    const int gs = min(GS, ns - g * GS);
+    const int rr = j - g * GS * n_tn;
+    const int ng = rr / (gs * GN), r2 = rr - ng * gs * GN;
+    const int si = r2 / GN, nn = r2 - si * GN;
+    return (x + nx * (g * GS + si)) * n_tn + ng * GN + nn;
+  }
+};
+
 template <int BM, int BN>
 __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, long long* wt) {
   if (a.flags & kCommOnly) return;
   using T = Tile<BM, BN>;
   const int m_pad = __builtin_amdgcn_readfirstlane(a.desc[0]);
-  const int n_tn = a.N / BN;
-  const int n_tiles = (m_pad / BM) * n_tn;
   const int grid = gridDim.x;
   const int nk2 = a.K / (2 * kBK);                       // k-iterations in pairs
+  TileLists L;
+  L.n_tn = a.N / BN;
+  L.n_slabs = m_pad / BM;
+  L.nx = (a.tile_order == 0 && grid % kXcds == 0) ? kXcds : 1;
+  const int per_list = grid / L.nx;                      // workgroups per list
+  {
+    int gn = 1;
+    while (gn * 2 <= min(8, per_list) && L.n_tn % (gn * 2) == 0) gn *= 2;
+    L.GN = L.nx == 1 ? L.n_tn : gn;
+    L.GS = L.nx == 1 ? 1 : max(1, per_list / gn);
+  }
+  const int n_tiles = L.n_slabs * L.n_tn;
   const int P = min(min(a.split_parts, nk2), grid);     // grid >= P: see the deadlock note
-  // split only when the last round of whole tiles would be partial
-  const int R = (P > 1 && n_tiles > grid && n_tiles % grid != 0) ? min(a.split_tiles, n_tiles) : 0;
-  const int n_whole = n_tiles - R;
-  const int n_items = n_whole + R * P;
+  const bool ragged = (n_tiles % grid != 0) || (L.n_slabs % L.nx != 0);
+  const int min_len = (L.n_slabs / L.nx) * L.n_tn;       // the shortest list
+  int R = (P > 1 && n_tiles > grid && ragged) ? min(a.split_tiles, min_len * L.nx) : 0;
+  L.r = R / L.nx;
+  R = L.r * L.nx;
+  const int x = blockIdx.x % L.nx;
+  const int my_whole = L.len(x) - L.r;
   const bool verify = a.flags & kVerify;
   const bool strict = a.flags & kStrict;
   const uint32_t row_bytes = (uint32_t)a.K * 2;
@@ -237,17 +286,35 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
   const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(a.gathered, (uint32_t)m_pad * row_bytes);
   const __amdgpu_buffer_rsrc_t rO = buffer_rsrc(a.out, (uint32_t)m_pad * (uint32_t)a.N * 2);
   const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(a.skws, a.skws_bytes);
+  int* const my_tick = a.tick_cur + (L.nx == 1 ? 64 : 64 * (1 + x));
+  int* const part_tick = a.tick_cur;
   long long gate = 0;
   int tiles = 0, parts = 0;
+  bool own_done = false;                                 // thread 0 only
   const long long t_begin = (long long)now_ticks();
   for (;;) {
     if (threadIdx.x == 0) {
       const long long t_take = (long long)now_ticks();
-      const int item = error_raised(a.err) ? n_items : fetch_add_relaxed(a.tick_cur, 1);
-      int ok = item < n_items;
+      int tile = -1, q = -1;
+      if (!error_raised(a.err)) {
+        if (!own_done) {
+          const int j = fetch_add_relaxed(my_tick, 1);
+          if (j < my_whole) tile = L.tile(x, j);
+          else own_done = true;
+        }
+        if (tile < 0 && R > 0) {
+          q = fetch_add_relaxed(part_tick, 1);
+          if (q < R * P) {
+            const int slot = q / P, xs = slot % L.nx;
+            tile = L.tile(xs, L.len(xs) - L.r + slot / L.nx);
+          } else {
+            q = -1;
+          }
+        }
+      }
+      int ok = tile >= 0;
       if (ok) {
-        const int tile = item < n_whole ? item : n_whole + (item - n_whole) / P;
-        const int m0 = (tile / n_tn) * BM;
+        const int m0 = (tile / L.n_tn) * BM;
         const long long t0 = (long long)now_ticks();
         uint32_t polls = 0;
         for (int rb = m0 / kRB; rb < (m0 + BM) / kRB && ok; ++rb)
@@ -259,22 +326,24 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
           atomicAdd(a.stats + ST_GATE_POLLS, (unsigned long long)polls);
           if (ok) atomicAdd(a.stats + ST_GATE_PASSES, 1ull);
         }
-        if ((a.flags & kTrace) && item < a.trace_cap) {
-          long long* tr = a.trace + (size_t)item * 4;
+        const int tr_id = q < 0 ? tile : n_tiles + q;
+        if ((a.flags & kTrace) && tr_id < a.trace_cap) {
+          long long* tr = a.trace + (size_t)tr_id * 4;
           tr[0] = blockIdx.x; tr[1] = t_take; tr[2] = t_open; tr[3] = 0;
         }
       }
-      sh[0] = item;
+      sh[0] = tile;
       sh[1] = ok;
+      sh[3] = q;
     }
     __syncthreads();
-    const int item = __builtin_amdgcn_readfirstlane(sh[0]);
+    const int tile = __builtin_amdgcn_readfirstlane(sh[0]);
+    const int q = __builtin_amdgcn_readfirstlane(sh[3]);
     if (!sh[1]) break;
     acquire_agent();
-    const bool whole = item < n_whole;
-    const int tile = whole ? item : n_whole + (item - n_whole) / P;
-    const int part = whole ? 0 : (item - n_whole) % P;
-    const int mt = tile / n_tn, nt = tile - mt * n_tn;
+    const bool whole = q < 0;
+    const int part = whole ? 0 : q % P;
+    const int mt = tile / L.n_tn, nt = tile - mt * L.n_tn;
     const int m0 = mt * BM, n0 = nt * BN;
     const int g = __builtin_amdgcn_readfirstlane(a.group_of_rb[m0 / kRB]);
     const __amdgpu_buffer_rsrc_t rB = buffer_rsrc(a.W + (size_t)g * a.N * a.K, (uint32_t)a.N * row_bytes);
@@ -287,16 +356,17 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
       for (int j = 0; j < T::FN; ++j) acc.v[i][j] = f32x16{};
     tile_mainloop<BM, BN>(rA, (uint32_t)m0 * row_bytes + (uint32_t)k0 * kRowB, rB,
                           (uint32_t)n0 * row_bytes + (uint32_t)k0 * kRowB, row_bytes, k1 - k0, lds0, lds1, acc);
+    const int tr_id = whole ? tile : n_tiles + q;
     if (whole) {
       tile_store<BM, BN>(rO, a.N, m0, n0, acc, a.inv, a.route_ver);
       ++tiles;
-      if ((a.flags & kTrace) && threadIdx.x == 0 && item < a.trace_cap) a.trace[(size_t)item * 4 + 3] = now_ticks();
+      if ((a.flags & kTrace) && threadIdx.x == 0 && tr_id < a.trace_cap) a.trace[(size_t)tr_id * 4 + 3] = now_ticks();
       continue;
     }
     // split-K part
-    const int slot = tile - n_whole;
+    const int slot = q / P;
     const uint32_t base = (uint32_t)slot * (uint32_t)P * tile_bytes;
-    partial_store<BM, BN>(rW, base + (uint32_t)part * tile_bytes, acc, part, P);
+    partial_store<BM, BN>(rW, base + (uint32_t)part * tile_bytes, acc);
     release_coherent(strict);
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -311,17 +381,16 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
     }
     __syncthreads();
     if (!sh[2]) break;
-    partial_reduce<BM, BN>(rW, base, tile_bytes, acc, part, P);
-    tile_store<BM, BN>(rO, a.N, m0, n0, acc, a.inv, a.route_ver, part, P);
+    partial_sum_store<BM, BN>(rW, base, tile_bytes, part, P, rO, a.N, m0, n0, a.inv, a.route_ver);
     ++parts;
-    if ((a.flags & kTrace) && threadIdx.x == 0 && item < a.trace_cap) a.trace[(size_t)item * 4 + 3] = now_ticks();
+    if ((a.flags & kTrace) && threadIdx.x == 0 && tr_id < a.trace_cap) a.trace[(size_t)tr_id * 4 + 3] = now_ticks();
   }
   if (threadIdx.x == 0) {
     wt[WT_GATE] = gate;
     wt[WT_TILES] = tiles;
     wt[WT_PARTS] = parts;
     wt[WT_GEMM_START] = t_begin;
-    wt[WT_P] = P;
+    wt[WT_P] = R > 0 ? P : 1;
   }
 }
 
@@ -330,9 +399,10 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
   __shared__ __attribute__((aligned(16))) char lds0[Tile<BM, BN>::STAGE];
   __shared__ __attribute__((aligned(16))) char lds1[Tile<BM, BN>::STAGE];
   __shared__ const uint16_t* sh_shard[FG_MAX_SHARDS];
-  __shared__ int sh[3];
+  __shared__ int sh[4];
   long long* wt = a.wgtime + (size_t)blockIdx.x * kWgTimeFields;
   const long long t_start = (long long)now_ticks();
+  const long long c_start = (long long)__builtin_amdgcn_s_memtime();
   long long t_comm = 0;
   if (threadIdx.x == 0) {
     wt[WT_GATE] = 0; wt[WT_TILES] = 0; wt[WT_PARTS] = 0; wt[WT_GEMM_START] = 0; wt[WT_P] = 1;
@@ -345,9 +415,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
   }
   gemm_role<BM, BN>(a, lds0, lds1, sh, wt);
   if (threadIdx.x == 0) {
+    wt[WT_CLK1] = (long long)__builtin_amdgcn_s_memtime();
     wt[WT_START] = t_start;
     wt[WT_END] = (long long)now_ticks();
     wt[WT_COMM_END] = t_comm;
+    wt[WT_CLK0] = c_start;
   }
 }
 

@@ -41,7 +41,7 @@ class FgConfig(C.Structure):
                 ("n_gemm_wg", C.c_int32), ("tile_n", C.c_int32), ("timeout_ns", C.c_int64),
                 ("stress_producers", C.c_int32), ("stress_consumers", C.c_int32),
                 ("stress_max_chunks", C.c_int32), ("split_parts", C.c_int32), ("split_tiles", C.c_int32),
-                ("reserved", C.c_int32)]
+                ("tile_order", C.c_int32)]
 
 
 class FgRoute(C.Structure):
@@ -61,7 +61,7 @@ class FgStats(C.Structure):
                 ("t_barrier_us", C.c_double), ("t_rtt_us", C.c_double),
                 ("n_comm_wg", C.c_int32), ("n_gemm_wg", C.c_int32), ("cu_count", C.c_int32),
                 ("m_pad_cap", C.c_int32), ("tiles_whole", C.c_int32), ("tiles_split", C.c_int32),
-                ("split_parts", C.c_int32), ("reserved", C.c_int32)]
+                ("split_parts", C.c_int32), ("reserved", C.c_int32), ("clock_mhz", C.c_double)]
 
 
 class FgViews(C.Structure):
@@ -130,9 +130,9 @@ def _ptr(t: torch.Tensor) -> C.c_void_p:
 
 
 def make_config(n_shards, max_rows_per_shard, K, N, n_groups=1, n_comm_wg=0, n_gemm_wg=0, tile_n=0,
-                timeout_ns=0, stress=(0, 0, 0), split_parts=0, split_tiles=0) -> FgConfig:
+                timeout_ns=0, stress=(0, 0, 0), split_parts=0, split_tiles=0, tile_order=0) -> FgConfig:
     return FgConfig(n_shards, max_rows_per_shard, K, N, n_groups, n_comm_wg, n_gemm_wg, tile_n, timeout_ns,
-                    stress[0], stress[1], stress[2], split_parts, split_tiles, 0)
+                    stress[0], stress[1], stress[2], split_parts, split_tiles, tile_order)
 
 
 def capacity(cfg: FgConfig) -> int:
@@ -206,7 +206,7 @@ class Context:
         call with CALL_TRACE, per compute item and per row block."""
         v = self.views()
         us = 1000.0 / v.wall_khz
-        wg = self.read_i32(v.wg_time, 2 * 8 * v.grid).view(torch.int64).reshape(v.grid, 8).numpy().copy()
+        wg = self.read_i32(v.wg_time, 2 * 12 * v.grid).view(torch.int64).reshape(v.grid, 12).numpy().copy()
         t0 = wg[:, 0].min()
         out = dict(wg=wg, t0=t0, us_per_tick=us)
         if v.trace_cap:

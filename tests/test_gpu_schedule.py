@@ -118,3 +118,47 @@ def test_comm_workgroups_join_compute():
     st, _, _ = _check(case, ctx, 2)
     assert st.tiles_whole == (1024 // 256) * (512 // 256)
     ctx.close()
+
+
+def _expected_xcd(case, grid, P, split_tiles, bm, bn):
+    """(whole, split, parts) of the XCD-grouped schedule: 8 lists of slabs
+    x, x+8, ...; split tiles come from the end of every list, r per list."""
+    n_tn = case.N // bn
+    n_slabs = case.lay.m_pad // bm
+    n_tiles = n_slabs * n_tn
+    p_eff = min(P, case.K // 128, grid)
+    ragged = n_tiles % grid != 0 or n_slabs % 8 != 0
+    min_len = (n_slabs // 8) * n_tn
+    auto = -(-grid // P)
+    R = min(split_tiles or auto, min_len * 8) if (p_eff > 1 and n_tiles > grid and ragged) else 0
+    R = (R // 8) * 8
+    return n_tiles - R, R, (p_eff if R else 1)
+
+
+@pytest.mark.parametrize("rows,n_comm,n_gemm,split_tiles", [(1024, 2, 14, 0), (1024, 1, 7, 0), (640, 2, 14, 16),
+                                                             (640, 2, 14, 0), (896, 4, 12, 24)])
+def test_xcd_grouped_lists(rows, n_comm, n_gemm, split_tiles):
+    grid = n_comm + n_gemm
+    log(f"XCD-grouped lists: 4 x {rows} rows, K=512, N=1024, grid {n_comm}+{n_gemm}, split_tiles={split_tiles}")
+    case = dense_case(60 + rows // 128, 4, rows, 512, 1024)
+    ctx = make_ctx(case, n_comm=n_comm, n_gemm=n_gemm, split_parts=4, split_tiles=split_tiles)
+    st, _, _ = _check(case, ctx, 3)
+    assert (st.tiles_whole, st.tiles_split, st.split_parts) == _expected_xcd(case, grid, 4, split_tiles, 256, 256)
+    ctx.close()
+
+
+def test_xcd_grouped_expert_groups():
+    log("XCD-grouped lists on grouped expert tiles: 8 shards x 128 tokens, grid 2+14")
+    case = ep_case(70, 8, 128, 512, 512)
+    ctx = make_ctx(case, n_comm=2, n_gemm=14, split_parts=4, split_tiles=16)
+    st, _, _ = _check(case, ctx, 3)
+    assert (st.tiles_whole, st.tiles_split, st.split_parts) == _expected_xcd(case, 16, 4, 16, 128, 256)
+    ctx.close()
+
+
+def test_single_list_order_at_full_grid():
+    log("one row-block-major list (tile_order=1) on the default grid: TP-like 4 x 512 rows, K=N=1024")
+    case = dense_case(71, 4, 512, 1024, 1024)
+    cfg_ctx = make_ctx(case, tile_order=1)
+    _check(case, cfg_ctx, 2)
+    cfg_ctx.close()
