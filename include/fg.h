@@ -93,11 +93,15 @@ typedef struct {
   int32_t stress_max_chunks;
   int32_t split_parts;         /* split-K tail, used when the tiles leave the last round of the grid
                                   partial: k-ranges per tail tile, 1..8 (0 = default 4, 1 = no split) */
-  int32_t split_tiles;         /* split-K tail: at most this many tail tiles split (0 = default: one
-                                  part per workgroup of the grid); the library allocates
-                                  split_tiles * split_parts * 256 * tile_n * 4 bytes of partial sums */
+  int32_t split_tiles;         /* split-K tail: at most this many tail tiles split; a value given here
+                                  also splits when the tiles fill whole rounds (0 = default: one part per
+                                  workgroup of the grid, only for a partial last round); the library
+                                  allocates split_tiles * split_parts * 256 * tile_n * 4 bytes of partials */
   int32_t tile_order;          /* 0 = tiles grouped per XCD when the grid is a multiple of 8 (default);
                                   1 = one row-block-major list */
+  int32_t copy_rows;           /* rows per copy batch of one wave: 1, 2, 4, 8 or 16, capped so that at most
+                                  32 16-byte vectors per lane are in flight (0 = the cap) */
+  int32_t reserved;
 } fg_config;
 
 typedef enum {
@@ -176,6 +180,10 @@ typedef struct {
   const int64_t* rb_time;     /* FG_CALL_TRACE: [rb_cap] time the row block's counter reached 128 */
   int32_t grid, trace_cap;
   int64_t wall_khz;
+  const int32_t* desc;        /* [2]: gathered rows m_pad and row slabs n_slabs of the route in use */
+  const int32_t* slab;        /* [n_slabs] compute row slabs: first row | 1 for a 128-row slab (else 256 rows);
+                                 every group is cut into 256-row slabs plus one 128-row slab if its size is an
+                                 odd number of 128-row blocks */
 } fg_views_t;
 
 /* Create a context on `hip_device`: validates the configuration, allocates and

@@ -47,7 +47,8 @@ struct Plane {
   int* skc;        // [2][split_tiles] split-K part counters
   long long* trace;    // [trace_cap][4]
   long long* rb_time;  // [rb_cap]
-  int* desc;
+  int* desc;       // [0] m_pad, [1] row slabs
+  int* slab;       // [rb_cap] row slab table
   int* err;        // [2]
   unsigned long long* stats;
   int* bslot;
@@ -85,7 +86,6 @@ struct fg_ctx {
   int route_cached_rows = -1;
   int last_grid = 0;
   int last_m_pad = 0;
-  int last_bm = 0;
   unsigned long long host_stats[ST_COUNT] = {};
 };
 
@@ -117,6 +117,8 @@ static bool config_ok(const fg_config* c) {
   if (c->timeout_ns < 0) return false;
   if (c->split_parts < 0 || c->split_parts > 8 || c->split_tiles < 0 || c->split_tiles > 4096) return false;
   if (c->tile_order < 0 || c->tile_order > 1) return false;
+  if (c->copy_rows != 0 && c->copy_rows != 1 && c->copy_rows != 2 && c->copy_rows != 4 && c->copy_rows != 8 &&
+      c->copy_rows != 16) return false;
   if (c->stress_producers < 0 || c->stress_consumers < 0 || c->stress_max_chunks < 0) return false;
   const long long m = (long long)c->n_shards * c->max_rows_per_shard + (long long)c->n_groups * FG_ROW_BLOCK;
   if (m * c->K * 2 >= (1ll << 32)) return false;   // 32-bit buffer offsets
@@ -125,9 +127,9 @@ static bool config_ok(const fg_config* c) {
   return true;
 }
 
-template <int BM, int BN>
+template <int BN>
 static hipError_t occupancy(int* per_cu) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, fused_kernel<BM, BN>, kThreads, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, fused_kernel<BN>, kThreads, 0);
 }
 
 static fg_status map_device_error(int code) {
@@ -190,7 +192,7 @@ static fg_status launch_route(fg_ctx* ctx, const fg_route* route, int mode, int 
   ra.wgcount = ctx->p.wgcount; ra.wgbase = ctx->p.wgbase; ra.ticket = ctx->p.ticket;
   ra.counter_cur = ctx->p.counter + (size_t)cur * ctx->rb_cap * kCtr;
   ra.elect_cur = ctx->p.elect + (size_t)cur * c.n_shards * ctx->chunk_cap;
-  ra.desc = ctx->p.desc; ra.err = sink(ctx);
+  ra.desc = ctx->p.desc; ra.slab = ctx->p.slab; ra.err = sink(ctx);
   auto blocks = [](long long work) { return (int)std::max(1LL, std::min(1024LL, (work + kRouteThreads - 1) / kRouteThreads)); };
   if (mode == FG_ROUTE_CONTIG) {
     const long long work = std::max<long long>({(long long)c.n_shards * rows, ctx->rb_cap,
@@ -210,11 +212,10 @@ static fg_status launch_route(fg_ctx* ctx, const fg_route* route, int mode, int 
   return FG_OK;
 }
 
-template <int BM, int BN>
-static fg_status launch_fused(fg_ctx* ctx, const FusedArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((fused_kernel<BM, BN>), dim3(a.n_comm + a.n_gemm), dim3(kThreads), 0, st, a);
+template <int BN>
+static fg_status launch_fused(const FusedArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((fused_kernel<BN>), dim3(a.n_comm + a.n_gemm), dim3(kThreads), 0, st, a);
   HIPCHK(hipGetLastError());
-  ctx->last_bm = BM;
   return FG_OK;
 }
 
@@ -267,13 +268,8 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
   {
     int per_cu = 0, worst = 1 << 30;
     hipError_t e = hipSuccess;
-    if (ctx->tile_n == 256) {
-      e = occupancy<256, 256>(&per_cu); worst = std::min(worst, per_cu);
-      if (e == hipSuccess) { e = occupancy<128, 256>(&per_cu); worst = std::min(worst, per_cu); }
-    } else {
-      e = occupancy<256, 128>(&per_cu); worst = std::min(worst, per_cu);
-      if (e == hipSuccess) { e = occupancy<128, 128>(&per_cu); worst = std::min(worst, per_cu); }
-    }
+    e = ctx->tile_n == 256 ? occupancy<256>(&per_cu) : occupancy<128>(&per_cu);
+    worst = std::min(worst, per_cu);
     if (e != hipSuccess) { delete ctx; return FG_EHIP; }
     if ((long long)worst * ctx->cu_count < ctx->n_comm + ctx->n_gemm) { delete ctx; return FG_ERESIDENCY; }
   }
@@ -304,7 +300,7 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
                o_elect = take(2 * nch * 4), o_pub = take(nch * 4), o_seed = take((size_t)ctx->rb_cap * 4),
                o_inv = take((size_t)ctx->m_pad_cap * 8), o_grp = take((size_t)ctx->rb_cap * 4),
                o_src = take(nrs * 4), o_dst = take(nrs * 4), o_slen = take((size_t)S * 4),
-               o_goff = take((FG_MAX_GROUPS + 1) * 4), o_rbc = take((size_t)ctx->rb_cap * 4), o_desc = take(64),
+               o_goff = take((FG_MAX_GROUPS + 1) * 4), o_rbc = take((size_t)ctx->rb_cap * 4), o_desc = take(64), o_slab = take((size_t)ctx->rb_cap * 4),
                o_wgc = take(wgc), o_wgb = take(wgc), o_tick = take(64), o_gtick = take(2 * kTickInts * 4),
                o_skc = take(2 * (size_t)std::max(1, ctx->split_tiles) * 4),
                o_trace = take((size_t)ctx->trace_cap * 32), o_rbt = take((size_t)ctx->rb_cap * 8),
@@ -323,7 +319,7 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
   p.trace = (long long*)(b + o_trace); p.rb_time = (long long*)(b + o_rbt);
   p.group_of_rb = (int*)(b + o_grp); p.src_row = (int*)(b + o_src); p.dst_row = (int*)(b + o_dst);
   p.stream_len = (int*)(b + o_slen); p.group_off = (int*)(b + o_goff); p.rbcount = (int*)(b + o_rbc);
-  p.desc = (int*)(b + o_desc); p.err = (int*)(b + o_err); p.stats = (unsigned long long*)(b + o_stats);
+  p.desc = (int*)(b + o_desc); p.slab = (int*)(b + o_slab); p.err = (int*)(b + o_err); p.stats = (unsigned long long*)(b + o_stats);
   p.bslot = (int*)(b + o_bslot); p.pp = (int*)(b + o_pp); p.tdev = (long long*)(b + o_tdev);
   p.wgtime = (long long*)(b + o_wg); p.s_slot = (int*)(b + o_sslot); p.s_elect = (int*)(b + o_select);
   p.s_pub = (int*)(b + o_spub);
@@ -432,13 +428,14 @@ fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route*
   a.elect_nxt = ctx->p.elect + (size_t)nxt * c.n_shards * ctx->chunk_cap;
   a.pub_count = ctx->p.pub_count; a.seed = ctx->p.seed; a.inv = ctx->p.inv; a.route_ver = ctx->route_ver;
   a.group_of_rb = ctx->p.group_of_rb;
-  a.src_row = ctx->p.src_row; a.stream_len = ctx->p.stream_len; a.desc = ctx->p.desc; a.stats = ctx->p.stats;
+  a.src_row = ctx->p.src_row; a.stream_len = ctx->p.stream_len; a.desc = ctx->p.desc; a.slab = ctx->p.slab; a.stats = ctx->p.stats;
   a.wgtime = ctx->p.wgtime; a.err = sink(ctx); a.seq = ctx->seq;
   a.n_comm = ctx->n_comm; a.n_gemm = ctx->n_gemm;
   // rows per communication batch: matches the copy template chosen on the
   // device (about 32 KB of loads in flight per wave)
   const int upr = (c.K / 8 + 63) / 64;
-  a.rows_per_batch = upr <= 2 ? 16 : upr <= 4 ? 8 : upr <= 8 ? 4 : upr <= 16 ? 2 : 1;
+  const int rb_max = upr <= 2 ? 16 : upr <= 4 ? 8 : upr <= 8 ? 4 : upr <= 16 ? 2 : 1;
+  a.rows_per_batch = c.copy_rows ? std::min(c.copy_rows, rb_max) : rb_max;
   a.flags = flags;
   a.timeout_ticks = timeout_ticks(ctx);
   a.tick_cur = ctx->p.gtick + cur * kTickInts;
@@ -450,17 +447,11 @@ fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route*
   a.skws_bytes = (uint32_t)ctx->skws_bytes;
   a.split_tiles = ctx->split_tiles;
   a.split_parts = ctx->split_parts;
+  a.split_forced = c.split_tiles != 0;
   a.trace = ctx->p.trace; a.rb_time = ctx->p.rb_time; a.trace_cap = ctx->trace_cap;
   ctx->last_grid = a.n_comm + a.n_gemm;
   ctx->last_m_pad = m_pad;
-  const bool bm256 = (mode != FG_ROUTE_TOPK) && (m_pad % 256 == 0) &&
-                     !(mode == FG_ROUTE_EXPLICIT && route->group_off && c.n_groups > 1);
-  if (ctx->tile_n == 256) {
-    s = bm256 ? launch_fused<256, 256>(ctx, a, stream) : launch_fused<128, 256>(ctx, a, stream);
-  } else {
-    s = bm256 ? launch_fused<256, 128>(ctx, a, stream) : launch_fused<128, 128>(ctx, a, stream);
-  }
-  return s;
+  return ctx->tile_n == 256 ? launch_fused<256>(a, stream) : launch_fused<128>(a, stream);
 }
 
 fg_status fg_barrier(fg_ctx* ctx, int32_t rounds, hipStream_t stream) {
@@ -605,6 +596,7 @@ fg_status fg_views(fg_ctx* ctx, fg_views_t* v) {
   v->chunk_cap = ctx->chunk_cap; v->rb_cap = ctx->rb_cap; v->m_pad_cap = ctx->m_pad_cap;
   v->wg_time = (const int64_t*)p.wgtime; v->trace = (const int64_t*)p.trace; v->rb_time = (const int64_t*)p.rb_time;
   v->grid = ctx->n_comm + ctx->n_gemm; v->trace_cap = ctx->trace_cap; v->wall_khz = ctx->wall_khz;
+  v->desc = p.desc; v->slab = p.slab;
   return FG_OK;
 }
 

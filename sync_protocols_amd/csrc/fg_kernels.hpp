@@ -55,7 +55,8 @@ struct FusedArgs {
   const int* group_of_rb;
   const int* src_row;
   const int* stream_len;
-  const int* desc;           // [0] = m_pad of this iteration
+  const int* desc;           // [0] = m_pad of this iteration, [1] = number of row slabs
+  const int* slab;           // [n_slabs] row slab: first row | 1 if the slab has 128 rows (else 256)
   unsigned long long* stats;
   long long* wgtime;         // [grid][kWgTimeFields], see WgTime
   ErrorSink err;
@@ -74,6 +75,7 @@ struct FusedArgs {
   uint32_t skws_bytes;
   int split_tiles;           // at most this many tail tiles are split
   int split_parts;           // into this many k-ranges (1 = no split)
+  int split_forced;          // split a tail even when the tiles fill whole rounds (split_tiles given)
   long long* trace;          // TRACE: [trace_cap][4] per item: workgroup, taken, gate open, done
   long long* rb_time;        // TRACE: [rb_cap] time a row block's counter reached 128
   int trace_cap;
@@ -125,6 +127,17 @@ __device__ __forceinline__ void copy_batch(const FusedArgs& a, const uint16_t* c
       store16_coherent(rd[r], (uint32_t)(u * 64 + lane) * 16, v[r][u]);
 }
 
+// Batch of RB rows (RB in {1, 2, 4, 8, 16}, at most 32 vectors per lane in flight).
+template <int UPR>
+__device__ __forceinline__ void copy_rows(int RB, const FusedArgs& a, const uint16_t* const* sh_shard, int g0,
+                                          int info, int srow, uint32_t row_bytes, int lane) {
+  if (RB == 1) copy_batch<UPR, 1>(a, sh_shard, g0, info, srow, row_bytes, lane);
+  else if (RB == 2) { if constexpr (UPR * 2 <= 32) copy_batch<UPR, 2>(a, sh_shard, g0, info, srow, row_bytes, lane); }
+  else if (RB == 4) { if constexpr (UPR * 4 <= 32) copy_batch<UPR, 4>(a, sh_shard, g0, info, srow, row_bytes, lane); }
+  else if (RB == 8) { if constexpr (UPR * 8 <= 32) copy_batch<UPR, 8>(a, sh_shard, g0, info, srow, row_bytes, lane); }
+  else { if constexpr (UPR * 16 <= 32) copy_batch<UPR, 16>(a, sh_shard, g0, info, srow, row_bytes, lane); }
+}
+
 __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -158,12 +171,12 @@ __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
       if (info >= 0) srow = a.src_row[(info >> 24) * a.rs_cap + (info & 0xFFFFFF)];
     }
     // bitwise row copy: 16-byte streaming loads, device-coherent 16-byte stores
-    if (upr <= 1)       copy_batch<1, 16>(a, sh_shard, g0, info, srow, row_bytes, lane);
-    else if (upr <= 2)  copy_batch<2, 16>(a, sh_shard, g0, info, srow, row_bytes, lane);
-    else if (upr <= 4)  copy_batch<4, 8>(a, sh_shard, g0, info, srow, row_bytes, lane);
-    else if (upr <= 8)  copy_batch<8, 4>(a, sh_shard, g0, info, srow, row_bytes, lane);
-    else if (upr <= 16) copy_batch<16, 2>(a, sh_shard, g0, info, srow, row_bytes, lane);
-    else                copy_batch<32, 1>(a, sh_shard, g0, info, srow, row_bytes, lane);
+    if (upr <= 1)       copy_rows<1>(RB, a, sh_shard, g0, info, srow, row_bytes, lane);
+    else if (upr <= 2)  copy_rows<2>(RB, a, sh_shard, g0, info, srow, row_bytes, lane);
+    else if (upr <= 4)  copy_rows<4>(RB, a, sh_shard, g0, info, srow, row_bytes, lane);
+    else if (upr <= 8)  copy_rows<8>(RB, a, sh_shard, g0, info, srow, row_bytes, lane);
+    else if (upr <= 16) copy_rows<16>(RB, a, sh_shard, g0, info, srow, row_bytes, lane);
+    else                copy_rows<32>(RB, a, sh_shard, g0, info, srow, row_bytes, lane);
     release_coherent(strict);
     // arrival count for the batch's row block (RB divides the row block)
     const uint64_t real = ballot(lane < RB && info >= 0);
@@ -235,7 +248,7 @@ __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
 struct TileLists {
   int nx;        // lists (8 or 1)
   int n_tn;      // column tiles
-  int n_slabs;   // row slabs of BM rows
+  int n_slabs;   // row slabs (256 rows, or 128 at the end of a group)
   int GN, GS;    // group shape: GS slabs x GN column tiles
   int r;         // split tiles taken from the end of every list
   __device__ int slabs_of(int x) const { return (n_slabs - x + nx - 1) / nx; }
@@ -252,16 +265,64 @@ struct TileLists {
   }
 };
 
+// One work item on a BM-row slab: the tile (whole) or one k-range of it
+// (part q of P, split slot `slot`). Returns false if a wait failed.
 template <int BM, int BN>
+__device__ __forceinline__ bool run_item(const FusedArgs& a, char* lds0, char* lds1, int* sh, int m0, int n0,
+                                         int g, int q, int P, int nk2, bool strict, long long& gate,
+                                         __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rO,
+                                         __amdgpu_buffer_rsrc_t rW) {
+  using T = Tile<BM, BN>;
+  const bool whole = q < 0;
+  const int part = whole ? 0 : q % P;
+  const uint32_t row_bytes = (uint32_t)a.K * 2;
+  const __amdgpu_buffer_rsrc_t rB = buffer_rsrc(a.W + (size_t)g * a.N * a.K, (uint32_t)a.N * row_bytes);
+  const int k0 = whole ? 0 : 2 * (nk2 * part / P);
+  const int k1 = whole ? 2 * nk2 : 2 * (nk2 * (part + 1) / P);
+  Acc<BM, BN> acc;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) acc.v[i][j] = f32x16{};
+  tile_mainloop<BM, BN>(rA, (uint32_t)m0 * row_bytes + (uint32_t)k0 * kRowB, rB,
+                        (uint32_t)n0 * row_bytes + (uint32_t)k0 * kRowB, row_bytes, k1 - k0, lds0, lds1, acc);
+  if (whole) {
+    tile_store<BM, BN>(rO, a.N, m0, n0, acc, a.inv, a.route_ver);
+    return true;
+  }
+  // split-K part: blocks of one split tile are 256 x BN floats apart (the
+  // largest slab), so one workspace layout serves both slab heights
+  const int slot = q / P;
+  const uint32_t stride = (uint32_t)(256 * BN * 4);
+  const uint32_t base = (uint32_t)slot * (uint32_t)P * stride;
+  partial_store<BM, BN>(rW, base + (uint32_t)part * stride, acc);
+  release_coherent(strict);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const long long t0 = (long long)now_ticks();
+    const int old = fetch_add_relaxed(a.skc_cur + slot, 1);
+    int ok = old < P;
+    if (!ok) raise_error(a.err, kErrProtocol, 0x20000000 | slot);
+    uint32_t polls = 0;
+    if (ok) ok = wait_eq(a.skc_cur + slot, P, now_ticks() + a.timeout_ticks, a.err, 0x20000000 | slot, &polls);
+    gate += (long long)now_ticks() - t0;
+    sh[2] = ok;
+  }
+  __syncthreads();
+  if (!sh[2]) return false;
+  partial_sum_store<BM, BN>(rW, base, stride, part, P, rO, a.N, m0, n0, a.inv, a.route_ver);
+  return true;
+}
+
+template <int BN>
 __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, long long* wt) {
   if (a.flags & kCommOnly) return;
-  using T = Tile<BM, BN>;
   const int m_pad = __builtin_amdgcn_readfirstlane(a.desc[0]);
   const int grid = gridDim.x;
   const int nk2 = a.K / (2 * kBK);                       // k-iterations in pairs
   TileLists L;
   L.n_tn = a.N / BN;
-  L.n_slabs = m_pad / BM;
+  L.n_slabs = __builtin_amdgcn_readfirstlane(a.desc[1]);
   L.nx = (a.tile_order == 0 && grid % kXcds == 0) ? kXcds : 1;
   const int per_list = grid / L.nx;                      // workgroups per list
   {
@@ -272,7 +333,7 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
   }
   const int n_tiles = L.n_slabs * L.n_tn;
   const int P = min(min(a.split_parts, nk2), grid);     // grid >= P: see the deadlock note
-  const bool ragged = (n_tiles % grid != 0) || (L.n_slabs % L.nx != 0);
+  const bool ragged = (n_tiles % grid != 0) || (L.n_slabs % L.nx != 0) || a.split_forced;
   const int min_len = (L.n_slabs / L.nx) * L.n_tn;       // the shortest list
   int R = (P > 1 && n_tiles > grid && ragged) ? min(a.split_tiles, min_len * L.nx) : 0;
   L.r = R / L.nx;
@@ -282,7 +343,6 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
   const bool verify = a.flags & kVerify;
   const bool strict = a.flags & kStrict;
   const uint32_t row_bytes = (uint32_t)a.K * 2;
-  const uint32_t tile_bytes = (uint32_t)(BM * BN * 4);
   const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(a.gathered, (uint32_t)m_pad * row_bytes);
   const __amdgpu_buffer_rsrc_t rO = buffer_rsrc(a.out, (uint32_t)m_pad * (uint32_t)a.N * 2);
   const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(a.skws, a.skws_bytes);
@@ -295,7 +355,7 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
   for (;;) {
     if (threadIdx.x == 0) {
       const long long t_take = (long long)now_ticks();
-      int tile = -1, q = -1;
+      int tile = -1, q = -1, entry = 0;
       if (!error_raised(a.err)) {
         if (!own_done) {
           const int j = fetch_add_relaxed(my_tick, 1);
@@ -314,10 +374,11 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
       }
       int ok = tile >= 0;
       if (ok) {
-        const int m0 = (tile / L.n_tn) * BM;
+        entry = a.slab[tile / L.n_tn];
+        const int m0 = entry & ~1, bm = (entry & 1) ? 128 : 256;
         const long long t0 = (long long)now_ticks();
         uint32_t polls = 0;
-        for (int rb = m0 / kRB; rb < (m0 + BM) / kRB && ok; ++rb)
+        for (int rb = m0 / kRB; rb < (m0 + bm) / kRB && ok; ++rb)
           ok = wait_eq(a.counter_cur + (size_t)rb * kCtr, kRB, now_ticks() + a.timeout_ticks, a.err, rb, &polls,
                        kBackoffLong);
         const long long t_open = (long long)now_ticks();
@@ -335,54 +396,21 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
       sh[0] = tile;
       sh[1] = ok;
       sh[3] = q;
+      sh[4] = entry;
     }
     __syncthreads();
     const int tile = __builtin_amdgcn_readfirstlane(sh[0]);
     const int q = __builtin_amdgcn_readfirstlane(sh[3]);
+    const int entry = __builtin_amdgcn_readfirstlane(sh[4]);
     if (!sh[1]) break;
     acquire_agent();
-    const bool whole = q < 0;
-    const int part = whole ? 0 : q % P;
-    const int mt = tile / L.n_tn, nt = tile - mt * L.n_tn;
-    const int m0 = mt * BM, n0 = nt * BN;
+    const int m0 = entry & ~1, n0 = (tile - (tile / L.n_tn) * L.n_tn) * BN;
     const int g = __builtin_amdgcn_readfirstlane(a.group_of_rb[m0 / kRB]);
-    const __amdgpu_buffer_rsrc_t rB = buffer_rsrc(a.W + (size_t)g * a.N * a.K, (uint32_t)a.N * row_bytes);
-    const int k0 = whole ? 0 : 2 * (nk2 * part / P);
-    const int k1 = whole ? 2 * nk2 : 2 * (nk2 * (part + 1) / P);
-    Acc<BM, BN> acc;
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < T::FN; ++j) acc.v[i][j] = f32x16{};
-    tile_mainloop<BM, BN>(rA, (uint32_t)m0 * row_bytes + (uint32_t)k0 * kRowB, rB,
-                          (uint32_t)n0 * row_bytes + (uint32_t)k0 * kRowB, row_bytes, k1 - k0, lds0, lds1, acc);
-    const int tr_id = whole ? tile : n_tiles + q;
-    if (whole) {
-      tile_store<BM, BN>(rO, a.N, m0, n0, acc, a.inv, a.route_ver);
-      ++tiles;
-      if ((a.flags & kTrace) && threadIdx.x == 0 && tr_id < a.trace_cap) a.trace[(size_t)tr_id * 4 + 3] = now_ticks();
-      continue;
-    }
-    // split-K part
-    const int slot = q / P;
-    const uint32_t base = (uint32_t)slot * (uint32_t)P * tile_bytes;
-    partial_store<BM, BN>(rW, base + (uint32_t)part * tile_bytes, acc);
-    release_coherent(strict);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const long long t0 = (long long)now_ticks();
-      const int old = fetch_add_relaxed(a.skc_cur + slot, 1);
-      int ok = old < P;
-      if (!ok) raise_error(a.err, kErrProtocol, 0x20000000 | slot);
-      uint32_t polls = 0;
-      if (ok) ok = wait_eq(a.skc_cur + slot, P, now_ticks() + a.timeout_ticks, a.err, 0x20000000 | slot, &polls);
-      gate += (long long)now_ticks() - t0;
-      sh[2] = ok;
-    }
-    __syncthreads();
-    if (!sh[2]) break;
-    partial_sum_store<BM, BN>(rW, base, tile_bytes, part, P, rO, a.N, m0, n0, a.inv, a.route_ver);
-    ++parts;
+    const bool ok = (entry & 1) ? run_item<128, BN>(a, lds0, lds1, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW)
+                                : run_item<256, BN>(a, lds0, lds1, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW);
+    if (!ok) break;
+    if (q < 0) ++tiles; else ++parts;
+    const int tr_id = q < 0 ? tile : n_tiles + q;
     if ((a.flags & kTrace) && threadIdx.x == 0 && tr_id < a.trace_cap) a.trace[(size_t)tr_id * 4 + 3] = now_ticks();
   }
   if (threadIdx.x == 0) {
@@ -394,12 +422,12 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
   }
 }
 
-template <int BM, int BN>
+template <int BN>
 __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds0[Tile<BM, BN>::STAGE];
-  __shared__ __attribute__((aligned(16))) char lds1[Tile<BM, BN>::STAGE];
+  __shared__ __attribute__((aligned(16))) char lds0[Tile<256, BN>::STAGE];
+  __shared__ __attribute__((aligned(16))) char lds1[Tile<256, BN>::STAGE];
   __shared__ const uint16_t* sh_shard[FG_MAX_SHARDS];
-  __shared__ int sh[4];
+  __shared__ int sh[5];
   long long* wt = a.wgtime + (size_t)blockIdx.x * kWgTimeFields;
   const long long t_start = (long long)now_ticks();
   const long long c_start = (long long)__builtin_amdgcn_s_memtime();
@@ -413,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
     comm_role(a, sh_shard);
     t_comm = (long long)now_ticks();
   }
-  gemm_role<BM, BN>(a, lds0, lds1, sh, wt);
+  gemm_role<BN>(a, lds0, lds1, sh, wt);
   if (threadIdx.x == 0) {
     wt[WT_CLK1] = (long long)__builtin_amdgcn_s_memtime();
     wt[WT_START] = t_start;
@@ -459,6 +487,7 @@ struct RouteArgs {
   int* counter_cur;          // [rb_cap][kCtr]
   int* elect_cur;
   int* desc;
+  int* slab;                 // row slab table (see FusedArgs)
   int* wgcount;              // TOPK: [n_wg][E + 1] per-workgroup expert counts, picks
   int* wgbase;               // TOPK: [n_wg][E + 1] expert row bases, stream base
   int* ticket;               // [0] last-workgroup ticket, [1] failure flag (zero between calls)
@@ -482,7 +511,29 @@ __device__ bool last_workgroup(int* ticket, int* sh) {
   return last;
 }
 
-// Seeds, group of each row block, arming; real(rb) gives the real rows of rb.
+// Row slabs of the compute role (one workgroup): every group [goff[g],
+// goff[g+1]) (multiples of 128 rows) is cut into 256-row slabs and, when its
+// size is an odd number of row blocks, one last 128-row slab, so that no slab
+// straddles two groups. Entry = first row | (128-row slab ? 1 : 0).
+__device__ void build_slabs(const int* goff, int n_groups, int* slab, int* desc) {
+  __shared__ int sh_base[FG_MAX_GROUPS + 1];
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int g = 0; g < n_groups; ++g) {
+      sh_base[g] = n;
+      const int S = goff[g + 1] - goff[g];
+      n += S / 256 + (S % 256 ? 1 : 0);
+    }
+    desc[1] = n;
+  }
+  __syncthreads();
+  for (int g = 0; g < n_groups; ++g) {
+    const int S = goff[g + 1] - goff[g], n256 = S / 256, ns = n256 + (S % 256 ? 1 : 0);
+    for (int j = threadIdx.x; j < ns; j += blockDim.x) slab[sh_base[g] + j] = (goff[g] + 256 * j) | (j == n256 ? 1 : 0);
+  }
+}
+
+// Seeds, group of each row block, arming, row slabs; real(rb) gives the real rows of rb.
 template <class Real>
 __device__ void route_finish(const RouteArgs& a, int m_pad, const int* goff, int n_groups, Real real) {
   const int n_rb = m_pad / kRB;
@@ -500,6 +551,7 @@ __device__ void route_finish(const RouteArgs& a, int m_pad, const int* goff, int
   for (int i = threadIdx.x; i < a.n_shards * a.chunk_cap; i += blockDim.x) a.elect_cur[i] = 0;
   if ((int)threadIdx.x <= n_groups) a.group_off_out[threadIdx.x] = goff[threadIdx.x];
   if (threadIdx.x == 0) a.desc[0] = m_pad;
+  build_slabs(goff, m_pad > 0 ? n_groups : 0, a.slab, a.desc);
 }
 
 // CONTIG: shard s row i -> gathered row s*R + i; everything is arithmetic, so
@@ -522,8 +574,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_contig_kernel(RouteArgs a
     a.counter_cur[(size_t)rb * kCtr] = sd;
   }
   for (int i = tid; i < a.n_shards * a.chunk_cap; i += nth) a.elect_cur[i] = 0;
+  const int n256 = m_pad / 256, n_slabs = n256 + (m_pad % 256 ? 1 : 0);
+  for (int j = tid; j < n_slabs; j += nth) a.slab[j] = (256 * j) | (j == n256 ? 1 : 0);
   if (tid < a.n_shards) a.stream_len[tid] = R;
-  if (tid == 0) { a.group_off_out[0] = 0; a.group_off_out[1] = m_pad; a.desc[0] = m_pad; }
+  if (tid == 0) { a.group_off_out[0] = 0; a.group_off_out[1] = m_pad; a.desc[0] = m_pad; a.desc[1] = n_slabs; }
 }
 
 // EXPLICIT: one thread per stream entry; the last workgroup computes the seeds.

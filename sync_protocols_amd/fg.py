@@ -41,7 +41,7 @@ class FgConfig(C.Structure):
                 ("n_gemm_wg", C.c_int32), ("tile_n", C.c_int32), ("timeout_ns", C.c_int64),
                 ("stress_producers", C.c_int32), ("stress_consumers", C.c_int32),
                 ("stress_max_chunks", C.c_int32), ("split_parts", C.c_int32), ("split_tiles", C.c_int32),
-                ("tile_order", C.c_int32)]
+                ("tile_order", C.c_int32), ("copy_rows", C.c_int32), ("reserved", C.c_int32)]
 
 
 class FgRoute(C.Structure):
@@ -70,7 +70,7 @@ class FgViews(C.Structure):
                                           "bslot", "stress_slot", "stress_pub")] + [
         ("chunk_cap", C.c_int32), ("rb_cap", C.c_int32), ("m_pad_cap", C.c_int32), ("route_ver", C.c_uint32),
         ("wg_time", C.c_void_p), ("trace", C.c_void_p), ("rb_time", C.c_void_p), ("grid", C.c_int32),
-        ("trace_cap", C.c_int32), ("wall_khz", C.c_int64)]
+        ("trace_cap", C.c_int32), ("wall_khz", C.c_int64), ("desc", C.c_void_p), ("slab", C.c_void_p)]
 
 
 class FgError(RuntimeError):
@@ -130,9 +130,10 @@ def _ptr(t: torch.Tensor) -> C.c_void_p:
 
 
 def make_config(n_shards, max_rows_per_shard, K, N, n_groups=1, n_comm_wg=0, n_gemm_wg=0, tile_n=0,
-                timeout_ns=0, stress=(0, 0, 0), split_parts=0, split_tiles=0, tile_order=0) -> FgConfig:
+                timeout_ns=0, stress=(0, 0, 0), split_parts=0, split_tiles=0, tile_order=0,
+                copy_rows=0) -> FgConfig:
     return FgConfig(n_shards, max_rows_per_shard, K, N, n_groups, n_comm_wg, n_gemm_wg, tile_n, timeout_ns,
-                    stress[0], stress[1], stress[2], split_parts, split_tiles, tile_order)
+                    stress[0], stress[1], stress[2], split_parts, split_tiles, tile_order, copy_rows, 0)
 
 
 def capacity(cfg: FgConfig) -> int:

@@ -127,9 +127,23 @@ def control_plane(ctx: fg.Context, n_shards: int):
         inv=ctx.read_inverse_map().numpy(),
         stream_len=ctx.read_i32(v.stream_len, S).numpy(),
         group_off=ctx.read_i32(v.group_off, 65).numpy(),
+        desc=ctx.read_i32(v.desc, 2).numpy(),
+        slab=ctx.read_i32(v.slab, v.rb_cap).numpy(),
         src_row=ctx.read_i32(v.src_row, S * ctx.cfg.max_rows_per_shard).numpy().reshape(S, -1),
         dst_row=ctx.read_i32(v.dst_row, S * ctx.cfg.max_rows_per_shard).numpy().reshape(S, -1),
         chunk_cap=cc, rb_cap=rbc)
+
+
+def expected_slabs(lay) -> np.ndarray:
+    """Row slabs of the compute role for a layout: every group cut into 256-row
+    slabs plus a 128-row slab when its size is an odd number of row blocks;
+    entry = first row | 1 for a 128-row slab."""
+    out = []
+    for g in range(lay.n_groups):
+        a, b = int(lay.group_off[g]), int(lay.group_off[g + 1])
+        for m0 in range(a, b, 256):
+            out.append(m0 | (1 if b - m0 == 128 else 0))
+    return np.array(out, dtype=np.int64)
 
 
 def check_route(case: Case, cp) -> None:
@@ -140,6 +154,9 @@ def check_route(case: Case, cp) -> None:
         assert np.array_equal(cp["src_row"][s, :n], lay.src_row[s]), f"src_row shard {s}"
         assert np.array_equal(cp["dst_row"][s, :n], lay.dst_row[s]), f"dst_row shard {s}"
     assert np.array_equal(cp["group_off"][:lay.n_groups + 1], lay.group_off), "group offsets"
+    want = expected_slabs(lay)
+    assert int(cp["desc"][0]) == lay.m_pad and int(cp["desc"][1]) == len(want), "m_pad / slab count"
+    assert np.array_equal(cp["slab"][:len(want)], want), "row slab table"
     assert np.array_equal(cp["seed"][:lay.n_rb], O.seeds(lay)), "padding seeds"
     real = O.real_rows(lay)
     assert np.array_equal(cp["inv"][:lay.m_pad] >= 0, real), "padding rows of the inverse map"

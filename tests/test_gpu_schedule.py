@@ -9,7 +9,7 @@ import torch
 import oracle as O
 from sync_protocols_amd import fg
 from fg_harness import (bits, buffers, check_control_plane, check_gathered, check_out, check_route, control_plane,
-                        dense_case, ep_case, log, make_ctx, run_iters)
+                        dense_case, ep_case, expected_slabs, log, make_ctx, run_iters)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,9 +29,9 @@ def _expected_split(case, grid, P, split_tiles, bm, bn):
     """(whole tiles, split tiles, parts per split tile) of the documented schedule:
     a tail is split only when the tiles leave the grid's last round partial; the
     parts are capped by the k-iteration pairs and by the grid."""
-    n_tiles = (case.lay.m_pad // bm) * (case.N // bn)
+    n_tiles = len(expected_slabs(case.lay)) * (case.N // bn)
     p_eff = min(P, case.K // 128, grid)
-    if p_eff <= 1 or n_tiles <= grid or n_tiles % grid == 0:
+    if p_eff <= 1 or n_tiles <= grid or (n_tiles % grid == 0 and not split_tiles):
         return n_tiles, 0, 1
     r = min(split_tiles if split_tiles else -(-grid // P), n_tiles)
     return n_tiles - r, r, p_eff
@@ -94,7 +94,7 @@ def test_split_tail_tile_n_128_ragged():
 def test_split_tail_expert_groups():
     log("split-K tail on grouped expert tiles: 8 shards x 64 tokens, grid 1+3")
     case = ep_case(56, 8, 64, 512, 256)
-    n_tiles = case.lay.m_pad // 128
+    n_tiles = len(expected_slabs(case.lay))
     grid = next(g for g in (4, 3, 5, 6, 7) if n_tiles > g and n_tiles % g)
     ctx = make_ctx(case, n_comm=1, n_gemm=grid - 1, split_parts=4, split_tiles=8)
     st, _, _ = _check(case, ctx, 3)
@@ -124,10 +124,10 @@ def _expected_xcd(case, grid, P, split_tiles, bm, bn):
     """(whole, split, parts) of the XCD-grouped schedule: 8 lists of slabs
     x, x+8, ...; split tiles come from the end of every list, r per list."""
     n_tn = case.N // bn
-    n_slabs = case.lay.m_pad // bm
+    n_slabs = len(expected_slabs(case.lay))
     n_tiles = n_slabs * n_tn
     p_eff = min(P, case.K // 128, grid)
-    ragged = n_tiles % grid != 0 or n_slabs % 8 != 0
+    ragged = n_tiles % grid != 0 or n_slabs % 8 != 0 or split_tiles != 0
     min_len = (n_slabs // 8) * n_tn
     auto = -(-grid // P)
     R = min(split_tiles or auto, min_len * 8) if (p_eff > 1 and n_tiles > grid and ragged) else 0
@@ -136,7 +136,7 @@ def _expected_xcd(case, grid, P, split_tiles, bm, bn):
 
 
 @pytest.mark.parametrize("rows,n_comm,n_gemm,split_tiles", [(1024, 2, 14, 0), (1024, 1, 7, 0), (640, 2, 14, 16),
-                                                             (640, 2, 14, 0), (896, 4, 12, 24)])
+                                                             (640, 2, 14, 0), (896, 4, 12, 24), (1024, 2, 14, 16)])
 def test_xcd_grouped_lists(rows, n_comm, n_gemm, split_tiles):
     grid = n_comm + n_gemm
     log(f"XCD-grouped lists: 4 x {rows} rows, K=512, N=1024, grid {n_comm}+{n_gemm}, split_tiles={split_tiles}")
