@@ -91,12 +91,14 @@ typedef struct {
   int32_t stress_producers;    /* protocol-stress plane (0 = none): producers x consumers x chunks slots */
   int32_t stress_consumers;
   int32_t stress_max_chunks;
-  int32_t split_parts;         /* split-K tail, used when the tiles leave the last round of the grid
-                                  partial: k-ranges per tail tile, 1..8 (0 = default 4, 1 = no split) */
-  int32_t split_tiles;         /* split-K tail: at most this many tail tiles split; a value given here
-                                  also splits when the tiles fill whole rounds (0 = default: one part per
-                                  workgroup of the grid, only for a partial last round); the library
-                                  allocates split_tiles * split_parts * 256 * tile_n * 4 bytes of partials */
+  int32_t split_parts;         /* split-K tail: at most this many k-ranges per split tile, 1..8 (0 = 8,
+                                  1 = no split). By default every tile list keeps a whole number of rounds
+                                  of whole tiles and its leftover tiles are split into
+                                  P = min(split_parts, K / 128, grid / leftover tiles) ranges */
+  int32_t split_tiles;         /* 0 = the default above; > 0: split this many tiles (taken evenly from the
+                                  end of the tile lists) into split_parts ranges, even when the tiles fill
+                                  whole rounds. Partial workspace: max(grid, split_tiles * split_parts) blocks
+                                  of 256 * tile_n fp32, allocated by fg_init */
   int32_t tile_order;          /* 0 = tiles grouped per XCD when the grid is a multiple of 8 (default);
                                   1 = one row-block-major list */
   int32_t copy_rows;           /* rows per copy batch of one wave: 1, 2, 4, 8 or 16, capped so that at most
@@ -175,8 +177,9 @@ typedef struct {
   const int64_t* wg_time;     /* [grid][12]: start, end, wait ticks, whole tiles, end of the copy role,
                                  split parts, start of the compute role, parts per split tile, shader-clock
                                  counter at start and at end, 2 unused */
-  const int64_t* trace;       /* FG_CALL_TRACE: [trace_cap][4] per compute item in ticket order:
-                                 workgroup, ticket taken, gate open, item done */
+  const int64_t* trace;       /* FG_CALL_TRACE: [trace_cap][8] per compute item (whole tile t at row t,
+                                 split-K part q at row n_tiles + q): workgroup, ticket taken, gate open, item
+                                 done; parts also: k loop done, partial stored, all parts counted; 1 unused */
   const int64_t* rb_time;     /* FG_CALL_TRACE: [rb_cap] time the row block's counter reached 128 */
   int32_t grid, trace_cap;
   int64_t wall_khz;

@@ -22,7 +22,7 @@ namespace {
 // store, acknowledgement, counter add), so many workgroups keep enough bytes in
 // flight; they join the compute role when their rows are copied.
 constexpr int kDefaultComm = 128;
-constexpr int kDefaultSplitParts = 4;
+constexpr int kDefaultSplitParts = 8;
 constexpr int64_t kDefaultTimeoutNs = 2000000000LL;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -44,7 +44,7 @@ struct Plane {
   int* wgbase;
   int* ticket;
   int* gtick;      // [2] x kTickInts: compute-item tickets (global + one per XCD), one set per parity
-  int* skc;        // [2][split_tiles] split-K part counters
+  int* skc;        // [2][split_slots] split-K part counters
   long long* trace;    // [trace_cap][4]
   long long* rb_time;  // [rb_cap]
   int* desc;       // [0] m_pad, [1] row slabs
@@ -68,7 +68,7 @@ struct fg_ctx {
   int cu_count = 0;
   int chunk_cap = 0, rb_cap = 0, m_pad_cap = 0, s_slots = 0;
   int n_comm = 0, n_gemm = 0, tile_n = 256;
-  int split_parts = 1, split_tiles = 0, trace_cap = 0;
+  int split_parts = 1, split_tiles = 0, split_slots = 1, split_blocks = 0, trace_cap = 0;
   float* skws = nullptr;       // split-K partial sums
   size_t skws_bytes = 0;
   int64_t wall_khz = 100000;
@@ -283,13 +283,17 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
   ctx->rb_cap = ctx->m_pad_cap / FG_ROW_BLOCK;
   ctx->s_slots = cfg->stress_producers * cfg->stress_consumers * cfg->stress_max_chunks;
   const int grid_max = ctx->n_comm + ctx->n_gemm;
+  // split-K tail capacity: by default at most grid/2 split tiles and grid
+  // partial blocks (P <= grid / split tiles); a given split_tiles adds
+  // split_tiles tiles of split_parts blocks each
   ctx->split_parts = cfg->split_parts ? cfg->split_parts : kDefaultSplitParts;
-  ctx->split_tiles = ctx->split_parts > 1 ? (cfg->split_tiles ? cfg->split_tiles
-                                                              : (grid_max + ctx->split_parts - 1) / ctx->split_parts)
-                                          : 0;
-  ctx->skws_bytes = (size_t)ctx->split_tiles * ctx->split_parts * 256 * ctx->tile_n * 4;
-  if (ctx->skws_bytes >= (1ull << 32)) { delete ctx; return FG_EINVAL; }
-  ctx->trace_cap = (ctx->m_pad_cap / 128) * (cfg->N / 128) + ctx->split_tiles * ctx->split_parts;
+  ctx->split_tiles = ctx->split_parts > 1 ? cfg->split_tiles : 0;
+  ctx->split_slots = std::max({1, grid_max / 2, ctx->split_tiles});
+  ctx->split_blocks = ctx->split_parts > 1 ? std::max(grid_max, ctx->split_tiles * ctx->split_parts) : 0;
+  ctx->skws_bytes = (size_t)ctx->split_blocks * 256 * ctx->tile_n * 4;
+  // 32-bit buffer offsets; offsets from 0xFFFFFFF0 up read as zeros in the partial sums
+  if (ctx->skws_bytes >= 0xFFFFFFF0ull) { delete ctx; return FG_EINVAL; }
+  ctx->trace_cap = (ctx->m_pad_cap / 128) * (cfg->N / 128) + ctx->split_blocks;
   const size_t nch = (size_t)S * ctx->chunk_cap;
   const size_t nrs = (size_t)S * cfg->max_rows_per_shard;
   size_t off = 0;
@@ -302,8 +306,8 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
                o_src = take(nrs * 4), o_dst = take(nrs * 4), o_slen = take((size_t)S * 4),
                o_goff = take((FG_MAX_GROUPS + 1) * 4), o_rbc = take((size_t)ctx->rb_cap * 4), o_desc = take(64), o_slab = take((size_t)ctx->rb_cap * 4),
                o_wgc = take(wgc), o_wgb = take(wgc), o_tick = take(64), o_gtick = take(2 * kTickInts * 4),
-               o_skc = take(2 * (size_t)std::max(1, ctx->split_tiles) * 4),
-               o_trace = take((size_t)ctx->trace_cap * 32), o_rbt = take((size_t)ctx->rb_cap * 8),
+               o_skc = take(2 * (size_t)ctx->split_slots * 4),
+               o_trace = take((size_t)ctx->trace_cap * kTraceFields * 8), o_rbt = take((size_t)ctx->rb_cap * 8),
                o_err = take(64), o_stats = take(ST_COUNT * 8), o_bslot = take((size_t)S * S * 4),
                o_pp = take(512), o_tdev = take(64), o_wg = take((size_t)grid_max * kWgTimeFields * 8),
                o_sslot = take((size_t)ctx->s_slots * 4), o_select = take(2 * (size_t)ctx->s_slots * 4),
@@ -441,13 +445,14 @@ fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route*
   a.tick_cur = ctx->p.gtick + cur * kTickInts;
   a.tick_nxt = ctx->p.gtick + nxt * kTickInts;
   a.tile_order = c.tile_order;
-  a.skc_cur = ctx->p.skc + (size_t)cur * std::max(1, ctx->split_tiles);
-  a.skc_nxt = ctx->p.skc + (size_t)nxt * std::max(1, ctx->split_tiles);
+  a.skc_cur = ctx->p.skc + (size_t)cur * ctx->split_slots;
+  a.skc_nxt = ctx->p.skc + (size_t)nxt * ctx->split_slots;
   a.skws = ctx->skws;
   a.skws_bytes = (uint32_t)ctx->skws_bytes;
   a.split_tiles = ctx->split_tiles;
+  a.split_slots = ctx->split_slots;
   a.split_parts = ctx->split_parts;
-  a.split_forced = c.split_tiles != 0;
+  a.split_forced = ctx->split_tiles != 0;
   a.trace = ctx->p.trace; a.rb_time = ctx->p.rb_time; a.trace_cap = ctx->trace_cap;
   ctx->last_grid = a.n_comm + a.n_gemm;
   ctx->last_m_pad = m_pad;

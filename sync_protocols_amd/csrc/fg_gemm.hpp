@@ -366,12 +366,19 @@ __device__ __forceinline__ void partial_sum_store(__amdgpu_buffer_rsrc_t rW, uin
       if (f % P != part) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-        for (int q = 0; q < P; ++q)
-          sum += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rW, base + (uint32_t)q * tile_bytes + partial_off<BM, BN>(wave, f, g, lane),
-                                               0, kPolCoherentStream));
+        // eight independent loads first (their latencies overlap); those of
+        // parts q >= P point past the end of the buffer, where the buffer
+        // unit returns zeros; then the sum in part order
+        const uint32_t o = partial_off<BM, BN>(wave, f, g, lane);
+        f32x4 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          v[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rW, q < P ? base + (uint32_t)q * tile_bytes + o : 0xFFFFFFF0u, 0,
+                                               kPolCoherentStream));
+        f32x4 sum = v[0];
+#pragma unroll
+        for (int q = 1; q < 8; ++q) sum += v[q];
         const int n = n0 + wn * T::WN + fn * 32 + 8 * g + 4 * kh;
         v2i w;
         w[0] = pad ? 0 : (int)pack_bf16x2(sum[0], sum[1]);

@@ -15,6 +15,7 @@ constexpr int kCtr = FG_COUNTER_STRIDE;  // arrival counters sit 256 bytes apart
 constexpr int kThreads = 64 * kWaves;   // workgroup size of the fused kernel
 constexpr int kXcds = 8;                // XCDs of the part; workgroup i runs on XCD i % 8
 constexpr int kTickInts = 1024;         // ticket block per parity: global ticket + one per XCD, 256 B apart
+constexpr int kTraceFields = 8;
 
 // per-call flag bits as seen by the device
 constexpr uint32_t kCommOnly = FG_CALL_COMM_ONLY;
@@ -69,14 +70,16 @@ struct FusedArgs {
   int* tick_cur;             // [kTickInts]: [0] next split-K part, [64 (1 + x)] next entry of list x
   int* tick_nxt;             // the other parity, zeroed here for the next call
   int tile_order;            // 0: XCD-grouped lists when the grid is a multiple of 8; 1: one list
-  int* skc_cur;              // [split_tiles] parts finished per split tile (zero at kernel start)
+  int* skc_cur;              // [split_slots] parts finished per split tile (zero at kernel start)
   int* skc_nxt;
-  float* skws;               // split_tiles x split_parts partial blocks of BM x BN floats
+  float* skws;               // partial blocks of 256 x BN floats, P consecutive blocks per split tile
   uint32_t skws_bytes;
-  int split_tiles;           // at most this many tail tiles are split
+  int split_tiles;           // given split tile count (split_forced), else 0
+  int split_slots;           // capacity of the part counters
   int split_parts;           // into this many k-ranges (1 = no split)
   int split_forced;          // split a tail even when the tiles fill whole rounds (split_tiles given)
-  long long* trace;          // TRACE: [trace_cap][4] per item: workgroup, taken, gate open, done
+  long long* trace;          // TRACE: [trace_cap][kTraceFields] per item: workgroup, taken, gate open,
+                             // done; parts also: k loop done, partial stored, all parts counted
   long long* rb_time;        // TRACE: [rb_cap] time a row block's counter reached 128
   int trace_cap;
 };
@@ -150,7 +153,7 @@ __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
     a.counter_nxt[(size_t)i * kCtr] = a.seed[i];
   for (int i = cw * kThreads + threadIdx.x; i < a.n_shards * a.chunk_cap; i += a.n_comm * kThreads)
     a.elect_nxt[i] = 0;
-  for (int i = cw * kThreads + threadIdx.x; i < a.split_tiles; i += a.n_comm * kThreads) a.skc_nxt[i] = 0;
+  for (int i = cw * kThreads + threadIdx.x; i < a.split_slots; i += a.n_comm * kThreads) a.skc_nxt[i] = 0;
   if (cw == 0 && threadIdx.x <= kXcds) a.tick_nxt[threadIdx.x * 64] = 0;
   if (a.flags & kGemmOnly) return;
 
@@ -250,9 +253,19 @@ struct TileLists {
   int n_tn;      // column tiles
   int n_slabs;   // row slabs (256 rows, or 128 at the end of a group)
   int GN, GS;    // group shape: GS slabs x GN column tiles
-  int r;         // split tiles taken from the end of every list
+  int per_list;  // workgroups per list
+  int forced_r;  // split tiles per list when given (>= 0), else -1: leftover of each list
+  bool split;    // the tail is split
   __device__ int slabs_of(int x) const { return (n_slabs - x + nx - 1) / nx; }
   __device__ int len(int x) const { return slabs_of(x) * n_tn; }
+  // split tiles taken from the end of list x
+  __device__ int r(int x) const { return !split ? 0 : forced_r >= 0 ? forced_r : len(x) % per_list; }
+  // tile of split slot `slot` (slots of list 0 first, then list 1, ...)
+  __device__ int split_tile(int slot) const {
+    int x = 0, base = 0;
+    while (x + 1 < nx && slot >= base + r(x)) { base += r(x); ++x; }
+    return tile(x, len(x) - r(x) + (slot - base));
+  }
   // tile index (slab * n_tn + column tile) of entry j of list x
   __device__ int tile(int x, int j) const {
     const int ns = slabs_of(x);
@@ -271,7 +284,7 @@ template <int BM, int BN>
 __device__ __forceinline__ bool run_item(const FusedArgs& a, char* lds0, char* lds1, int* sh, int m0, int n0,
                                          int g, int q, int P, int nk2, bool strict, long long& gate,
                                          __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rO,
-                                         __amdgpu_buffer_rsrc_t rW) {
+                                         __amdgpu_buffer_rsrc_t rW, long long* tr) {
   using T = Tile<BM, BN>;
   const bool whole = q < 0;
   const int part = whole ? 0 : q % P;
@@ -295,17 +308,20 @@ __device__ __forceinline__ bool run_item(const FusedArgs& a, char* lds0, char* l
   const int slot = q / P;
   const uint32_t stride = (uint32_t)(256 * BN * 4);
   const uint32_t base = (uint32_t)slot * (uint32_t)P * stride;
+  if (tr && threadIdx.x == 0) tr[4] = now_ticks();
   partial_store<BM, BN>(rW, base + (uint32_t)part * stride, acc);
   release_coherent(strict);
   __syncthreads();
   if (threadIdx.x == 0) {
     const long long t0 = (long long)now_ticks();
+    if (tr) tr[5] = t0;
     const int old = fetch_add_relaxed(a.skc_cur + slot, 1);
     int ok = old < P;
     if (!ok) raise_error(a.err, kErrProtocol, 0x20000000 | slot);
     uint32_t polls = 0;
     if (ok) ok = wait_eq(a.skc_cur + slot, P, now_ticks() + a.timeout_ticks, a.err, 0x20000000 | slot, &polls);
     gate += (long long)now_ticks() - t0;
+    if (tr) tr[6] = now_ticks();
     sh[2] = ok;
   }
   __syncthreads();
@@ -332,14 +348,27 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
     L.GS = L.nx == 1 ? 1 : max(1, per_list / gn);
   }
   const int n_tiles = L.n_slabs * L.n_tn;
-  const int P = min(min(a.split_parts, nk2), grid);     // grid >= P: see the deadlock note
-  const bool ragged = (n_tiles % grid != 0) || (L.n_slabs % L.nx != 0) || a.split_forced;
-  const int min_len = (L.n_slabs / L.nx) * L.n_tn;       // the shortest list
-  int R = (P > 1 && n_tiles > grid && ragged) ? min(a.split_tiles, min_len * L.nx) : 0;
-  L.r = R / L.nx;
-  R = L.r * L.nx;
+  // Split-K tail. Default: every list keeps a whole number of rounds of whole
+  // tiles (a multiple of its workgroups); its leftover tiles are split into
+  // P = min(parts cap, k pairs, grid / leftover) k-ranges, so that the parts
+  // fill about one round of the grid. With split_tiles given (split_forced),
+  // split_tiles / lists tiles are taken from the end of every list, P = cap.
+  int R = 0, P = 1;
+  {
+    const int min_len = (L.n_slabs / L.nx) * L.n_tn;   // the shortest list
+    L.per_list = per_list;
+    L.forced_r = a.split_forced ? min(a.split_tiles / L.nx, min_len) : -1;
+    L.split = true;
+    int rsum = 0;
+    for (int xx = 0; xx < L.nx; ++xx) rsum += L.r(xx);
+    if (rsum > 0 && n_tiles > grid) {
+      P = min(min(a.split_parts, nk2), a.split_forced ? grid : grid / rsum);   // P <= grid: deadlock note
+      R = P > 1 ? rsum : 0;
+    }
+    if (R == 0) { P = 1; L.split = false; }
+  }
   const int x = blockIdx.x % L.nx;
-  const int my_whole = L.len(x) - L.r;
+  const int my_whole = L.len(x) - L.r(x);
   const bool verify = a.flags & kVerify;
   const bool strict = a.flags & kStrict;
   const uint32_t row_bytes = (uint32_t)a.K * 2;
@@ -365,8 +394,7 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
         if (tile < 0 && R > 0) {
           q = fetch_add_relaxed(part_tick, 1);
           if (q < R * P) {
-            const int slot = q / P, xs = slot % L.nx;
-            tile = L.tile(xs, L.len(xs) - L.r + slot / L.nx);
+            tile = L.split_tile(q / P);
           } else {
             q = -1;
           }
@@ -389,8 +417,8 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
         }
         const int tr_id = q < 0 ? tile : n_tiles + q;
         if ((a.flags & kTrace) && tr_id < a.trace_cap) {
-          long long* tr = a.trace + (size_t)tr_id * 4;
-          tr[0] = blockIdx.x; tr[1] = t_take; tr[2] = t_open; tr[3] = 0;
+          long long* tr = a.trace + (size_t)tr_id * kTraceFields;
+          tr[0] = blockIdx.x; tr[1] = t_take; tr[2] = t_open; tr[3] = 0; tr[4] = 0; tr[5] = 0; tr[6] = 0;
         }
       }
       sh[0] = tile;
@@ -406,12 +434,14 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
     acquire_agent();
     const int m0 = entry & ~1, n0 = (tile - (tile / L.n_tn) * L.n_tn) * BN;
     const int g = __builtin_amdgcn_readfirstlane(a.group_of_rb[m0 / kRB]);
-    const bool ok = (entry & 1) ? run_item<128, BN>(a, lds0, lds1, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW)
-                                : run_item<256, BN>(a, lds0, lds1, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW);
+    const int tr_id = q < 0 ? tile : n_tiles + q;
+    long long* tr = ((a.flags & kTrace) && q >= 0 && tr_id < a.trace_cap) ? a.trace + (size_t)tr_id * kTraceFields
+                                                                            : nullptr;
+    const bool ok = (entry & 1) ? run_item<128, BN>(a, lds0, lds1, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr)
+                                : run_item<256, BN>(a, lds0, lds1, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr);
     if (!ok) break;
     if (q < 0) ++tiles; else ++parts;
-    const int tr_id = q < 0 ? tile : n_tiles + q;
-    if ((a.flags & kTrace) && threadIdx.x == 0 && tr_id < a.trace_cap) a.trace[(size_t)tr_id * 4 + 3] = now_ticks();
+    if ((a.flags & kTrace) && threadIdx.x == 0 && tr_id < a.trace_cap) a.trace[(size_t)tr_id * kTraceFields + 3] = now_ticks();
   }
   if (threadIdx.x == 0) {
     wt[WT_GATE] = gate;

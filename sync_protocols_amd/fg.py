@@ -211,7 +211,7 @@ class Context:
         t0 = wg[:, 0].min()
         out = dict(wg=wg, t0=t0, us_per_tick=us)
         if v.trace_cap:
-            tr = self.read_i32(v.trace, 2 * 4 * v.trace_cap).view(torch.int64).reshape(v.trace_cap, 4).numpy().copy()
+            tr = self.read_i32(v.trace, 2 * 8 * v.trace_cap).view(torch.int64).reshape(v.trace_cap, 8).numpy().copy()
             out["trace"] = tr
             out["rb_time"] = self.read_i32(v.rb_time, 2 * v.rb_cap).view(torch.int64).numpy().copy()
         return out

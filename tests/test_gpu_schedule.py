@@ -25,28 +25,51 @@ def _check(case, ctx, iters, flags=fg.CALL_VERIFY):
     return st, out, r
 
 
-def _expected_split(case, grid, P, split_tiles, bm, bn):
-    """(whole tiles, split tiles, parts per split tile) of the documented schedule:
-    a tail is split only when the tiles leave the grid's last round partial; the
-    parts are capped by the k-iteration pairs and by the grid."""
-    n_tiles = len(expected_slabs(case.lay)) * (case.N // bn)
-    p_eff = min(P, case.K // 128, grid)
-    if p_eff <= 1 or n_tiles <= grid or (n_tiles % grid == 0 and not split_tiles):
-        return n_tiles, 0, 1
-    r = min(split_tiles if split_tiles else -(-grid // P), n_tiles)
-    return n_tiles - r, r, p_eff
+def _schedule(case, grid, split_parts, split_tiles, bn=256, tile_order=0):
+    """(whole tiles, split tiles, parts per split tile) of the documented
+    schedule. Lists: 8 (XCD-grouped, when the grid is a multiple of 8 and
+    tile_order = 0) or 1. Default: list x splits its leftover len_x mod
+    (workgroups per list) tiles into P = min(split_parts, K / 128, grid / R)
+    parts; with split_tiles given, split_tiles / lists tiles of every list,
+    P = min(split_parts, K / 128, grid)."""
+    n_tn = case.N // bn
+    n_slabs = len(expected_slabs(case.lay))
+    n_tiles = n_slabs * n_tn
+    nx = 8 if (tile_order == 0 and grid % 8 == 0) else 1
+    per_list = grid // nx
+    lens = [((n_slabs - x + nx - 1) // nx) * n_tn for x in range(nx)]
+    min_len = (n_slabs // nx) * n_tn
+    r = [min(split_tiles // nx, min_len)] * nx if split_tiles else [l % per_list for l in lens]
+    R, P = sum(r), 1
+    if R > 0 and n_tiles > grid:
+        P = min(split_parts, case.K // 128, grid if split_tiles else grid // R)
+    if P <= 1:
+        R, P = 0, 1
+    return n_tiles - R, R, P
 
 
-@pytest.mark.parametrize("P,split_tiles", [(2, 0), (3, 0), (4, 0), (8, 0), (4, 32), (3, 5)])
+@pytest.mark.parametrize("P,split_tiles", [(2, 4), (3, 4), (4, 4), (8, 4), (4, 32), (3, 5)])
 def test_split_tail_matches_oracle(P, split_tiles):
     log(f"split-K tail: 4 x 512 rows (32 tiles), K=N=1024, grid 2+5, P={P}, split_tiles={split_tiles}")
     case = dense_case(51, 4, 512, 1024, 1024)
     ctx = make_ctx(case, n_comm=2, n_gemm=5, split_parts=P, split_tiles=split_tiles)
     st, _, r = _check(case, ctx, 3)
-    whole, split, p_eff = _expected_split(case, 7, P, split_tiles, 256, 256)
-    assert (st.tiles_whole, st.tiles_split, st.split_parts) == (whole, split, p_eff)
-    assert split > 0
+    assert (st.tiles_whole, st.tiles_split, st.split_parts) == _schedule(case, 7, P, split_tiles)
+    assert st.tiles_split > 0
     log(f"split ok: whole={st.tiles_whole} split={st.tiles_split} P={st.split_parts} max|d|={r['max_abs']:.3g}")
+    ctx.close()
+
+
+@pytest.mark.parametrize("rows,N,n_comm,n_gemm", [(640, 768, 2, 14), (896, 768, 4, 12), (512, 1280, 1, 2)])
+def test_default_split_of_leftover_tiles(rows, N, n_comm, n_gemm):
+    grid = n_comm + n_gemm
+    log(f"default split of each list's leftover tiles: 4 x {rows} rows, K=1024, N={N}, grid {n_comm}+{n_gemm}")
+    case = dense_case(80 + rows // 128, 4, rows, 1024, N)
+    ctx = make_ctx(case, n_comm=n_comm, n_gemm=n_gemm, split_parts=8)
+    st, _, _ = _check(case, ctx, 3)
+    want = _schedule(case, grid, 8, 0)
+    assert (st.tiles_whole, st.tiles_split, st.split_parts) == want
+    assert want[1] > 0
     ctx.close()
 
 
@@ -69,6 +92,7 @@ def test_split_parts_capped_by_k():
     case = dense_case(53, 4, 512, 256, 1024)
     ctx = make_ctx(case, n_comm=2, n_gemm=5, split_parts=4, split_tiles=32)
     st, _, _ = _check(case, ctx, 2)
+    assert (st.tiles_whole, st.tiles_split, st.split_parts) == _schedule(case, 7, 4, 32)
     assert st.split_parts == 2 and st.tiles_split > 0
     ctx.close()
 
@@ -98,7 +122,7 @@ def test_split_tail_expert_groups():
     grid = next(g for g in (4, 3, 5, 6, 7) if n_tiles > g and n_tiles % g)
     ctx = make_ctx(case, n_comm=1, n_gemm=grid - 1, split_parts=4, split_tiles=8)
     st, _, _ = _check(case, ctx, 3)
-    assert (st.tiles_whole, st.tiles_split, st.split_parts) == _expected_split(case, grid, 4, 8, 128, 256)
+    assert (st.tiles_whole, st.tiles_split, st.split_parts) == _schedule(case, grid, 4, 8)
     assert st.tiles_split > 0
     ctx.close()
 
@@ -120,21 +144,6 @@ def test_comm_workgroups_join_compute():
     ctx.close()
 
 
-def _expected_xcd(case, grid, P, split_tiles, bm, bn):
-    """(whole, split, parts) of the XCD-grouped schedule: 8 lists of slabs
-    x, x+8, ...; split tiles come from the end of every list, r per list."""
-    n_tn = case.N // bn
-    n_slabs = len(expected_slabs(case.lay))
-    n_tiles = n_slabs * n_tn
-    p_eff = min(P, case.K // 128, grid)
-    ragged = n_tiles % grid != 0 or n_slabs % 8 != 0 or split_tiles != 0
-    min_len = (n_slabs // 8) * n_tn
-    auto = -(-grid // P)
-    R = min(split_tiles or auto, min_len * 8) if (p_eff > 1 and n_tiles > grid and ragged) else 0
-    R = (R // 8) * 8
-    return n_tiles - R, R, (p_eff if R else 1)
-
-
 @pytest.mark.parametrize("rows,n_comm,n_gemm,split_tiles", [(1024, 2, 14, 0), (1024, 1, 7, 0), (640, 2, 14, 16),
                                                              (640, 2, 14, 0), (896, 4, 12, 24), (1024, 2, 14, 16)])
 def test_xcd_grouped_lists(rows, n_comm, n_gemm, split_tiles):
@@ -143,7 +152,7 @@ def test_xcd_grouped_lists(rows, n_comm, n_gemm, split_tiles):
     case = dense_case(60 + rows // 128, 4, rows, 512, 1024)
     ctx = make_ctx(case, n_comm=n_comm, n_gemm=n_gemm, split_parts=4, split_tiles=split_tiles)
     st, _, _ = _check(case, ctx, 3)
-    assert (st.tiles_whole, st.tiles_split, st.split_parts) == _expected_xcd(case, grid, 4, split_tiles, 256, 256)
+    assert (st.tiles_whole, st.tiles_split, st.split_parts) == _schedule(case, grid, 4, split_tiles)
     ctx.close()
 
 
@@ -152,7 +161,7 @@ def test_xcd_grouped_expert_groups():
     case = ep_case(70, 8, 128, 512, 512)
     ctx = make_ctx(case, n_comm=2, n_gemm=14, split_parts=4, split_tiles=16)
     st, _, _ = _check(case, ctx, 3)
-    assert (st.tiles_whole, st.tiles_split, st.split_parts) == _expected_xcd(case, 16, 4, 16, 128, 256)
+    assert (st.tiles_whole, st.tiles_split, st.split_parts) == _schedule(case, 16, 4, 16)
     ctx.close()
 
 
