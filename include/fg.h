@@ -183,10 +183,11 @@ typedef struct {
   const int64_t* rb_time;     /* FG_CALL_TRACE: [rb_cap] time the row block's counter reached 128 */
   int32_t grid, trace_cap;
   int64_t wall_khz;
-  const int32_t* desc;        /* [2]: gathered rows m_pad and row slabs n_slabs of the route in use */
+  const int32_t* desc;        /* [3]: gathered rows m_pad, row slabs n_slabs and groups of the route in use */
   const int32_t* slab;        /* [n_slabs] compute row slabs: first row | 1 for a 128-row slab (else 256 rows);
                                  every group is cut into 256-row slabs plus one 128-row slab if its size is an
                                  odd number of 128-row blocks */
+  const int32_t* group_slab;  /* [groups + 1] first slab of each group (the last entry is n_slabs) */
 } fg_views_t;
 
 /* Create a context on `hip_device`: validates the configuration, allocates and

@@ -49,6 +49,7 @@ struct Plane {
   long long* rb_time;  // [rb_cap]
   int* desc;       // [0] m_pad, [1] row slabs
   int* slab;       // [rb_cap] row slab table
+  int* gslab;      // [FG_MAX_GROUPS + 1] first slab of each group
   int* err;        // [2]
   unsigned long long* stats;
   int* bslot;
@@ -192,7 +193,7 @@ static fg_status launch_route(fg_ctx* ctx, const fg_route* route, int mode, int 
   ra.wgcount = ctx->p.wgcount; ra.wgbase = ctx->p.wgbase; ra.ticket = ctx->p.ticket;
   ra.counter_cur = ctx->p.counter + (size_t)cur * ctx->rb_cap * kCtr;
   ra.elect_cur = ctx->p.elect + (size_t)cur * c.n_shards * ctx->chunk_cap;
-  ra.desc = ctx->p.desc; ra.slab = ctx->p.slab; ra.err = sink(ctx);
+  ra.desc = ctx->p.desc; ra.slab = ctx->p.slab; ra.gslab = ctx->p.gslab; ra.err = sink(ctx);
   auto blocks = [](long long work) { return (int)std::max(1LL, std::min(1024LL, (work + kRouteThreads - 1) / kRouteThreads)); };
   if (mode == FG_ROUTE_CONTIG) {
     const long long work = std::max<long long>({(long long)c.n_shards * rows, ctx->rb_cap,
@@ -304,7 +305,7 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
                o_elect = take(2 * nch * 4), o_pub = take(nch * 4), o_seed = take((size_t)ctx->rb_cap * 4),
                o_inv = take((size_t)ctx->m_pad_cap * 8), o_grp = take((size_t)ctx->rb_cap * 4),
                o_src = take(nrs * 4), o_dst = take(nrs * 4), o_slen = take((size_t)S * 4),
-               o_goff = take((FG_MAX_GROUPS + 1) * 4), o_rbc = take((size_t)ctx->rb_cap * 4), o_desc = take(64), o_slab = take((size_t)ctx->rb_cap * 4),
+               o_goff = take((FG_MAX_GROUPS + 1) * 4), o_rbc = take((size_t)ctx->rb_cap * 4), o_desc = take(64), o_slab = take((size_t)ctx->rb_cap * 4), o_gslab = take((FG_MAX_GROUPS + 1) * 4),
                o_wgc = take(wgc), o_wgb = take(wgc), o_tick = take(64), o_gtick = take(2 * kTickInts * 4),
                o_skc = take(2 * (size_t)ctx->split_slots * 4),
                o_trace = take((size_t)ctx->trace_cap * kTraceFields * 8), o_rbt = take((size_t)ctx->rb_cap * 8),
@@ -323,7 +324,7 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
   p.trace = (long long*)(b + o_trace); p.rb_time = (long long*)(b + o_rbt);
   p.group_of_rb = (int*)(b + o_grp); p.src_row = (int*)(b + o_src); p.dst_row = (int*)(b + o_dst);
   p.stream_len = (int*)(b + o_slen); p.group_off = (int*)(b + o_goff); p.rbcount = (int*)(b + o_rbc);
-  p.desc = (int*)(b + o_desc); p.slab = (int*)(b + o_slab); p.err = (int*)(b + o_err); p.stats = (unsigned long long*)(b + o_stats);
+  p.desc = (int*)(b + o_desc); p.slab = (int*)(b + o_slab); p.gslab = (int*)(b + o_gslab); p.err = (int*)(b + o_err); p.stats = (unsigned long long*)(b + o_stats);
   p.bslot = (int*)(b + o_bslot); p.pp = (int*)(b + o_pp); p.tdev = (long long*)(b + o_tdev);
   p.wgtime = (long long*)(b + o_wg); p.s_slot = (int*)(b + o_sslot); p.s_elect = (int*)(b + o_select);
   p.s_pub = (int*)(b + o_spub);
@@ -432,7 +433,7 @@ fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route*
   a.elect_nxt = ctx->p.elect + (size_t)nxt * c.n_shards * ctx->chunk_cap;
   a.pub_count = ctx->p.pub_count; a.seed = ctx->p.seed; a.inv = ctx->p.inv; a.route_ver = ctx->route_ver;
   a.group_of_rb = ctx->p.group_of_rb;
-  a.src_row = ctx->p.src_row; a.stream_len = ctx->p.stream_len; a.desc = ctx->p.desc; a.slab = ctx->p.slab; a.stats = ctx->p.stats;
+  a.src_row = ctx->p.src_row; a.stream_len = ctx->p.stream_len; a.desc = ctx->p.desc; a.slab = ctx->p.slab; a.gslab = ctx->p.gslab; a.stats = ctx->p.stats;
   a.wgtime = ctx->p.wgtime; a.err = sink(ctx); a.seq = ctx->seq;
   a.n_comm = ctx->n_comm; a.n_gemm = ctx->n_gemm;
   // rows per communication batch: matches the copy template chosen on the
@@ -601,7 +602,7 @@ fg_status fg_views(fg_ctx* ctx, fg_views_t* v) {
   v->chunk_cap = ctx->chunk_cap; v->rb_cap = ctx->rb_cap; v->m_pad_cap = ctx->m_pad_cap;
   v->wg_time = (const int64_t*)p.wgtime; v->trace = (const int64_t*)p.trace; v->rb_time = (const int64_t*)p.rb_time;
   v->grid = ctx->n_comm + ctx->n_gemm; v->trace_cap = ctx->trace_cap; v->wall_khz = ctx->wall_khz;
-  v->desc = p.desc; v->slab = p.slab;
+  v->desc = p.desc; v->slab = p.slab; v->group_slab = p.gslab;
   return FG_OK;
 }
 

@@ -56,8 +56,9 @@ struct FusedArgs {
   const int* group_of_rb;
   const int* src_row;
   const int* stream_len;
-  const int* desc;           // [0] = m_pad of this iteration, [1] = number of row slabs
+  const int* desc;           // [0] = m_pad of this iteration, [1] = number of row slabs, [2] = groups
   const int* slab;           // [n_slabs] row slab: first row | 1 if the slab has 128 rows (else 256)
+  const int* gslab;          // [groups + 1] first slab of each group
   unsigned long long* stats;
   long long* wgtime;         // [grid][kWgTimeFields], see WgTime
   ErrorSink err;
@@ -222,12 +223,14 @@ __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
 // Compute role ("PCIe sync protocols" §5 gate).
 //
 // Work lists. With a grid that is a multiple of the 8 XCDs (workgroup i runs
-// on XCD i % 8), XCD x owns the 256-row slabs s = x, x + 8, x + 16, ... and
-// hands out their tiles from its own ticket counter, in groups of GS slabs x
-// GN column tiles, GS * GN = workgroups per XCD: the tiles that run at the
-// same time on one XCD share A and W lines in that XCD's L2. Slabs are walked
-// in increasing order, the order in which the copy role delivers row blocks.
-// (Other grids use one list, x = 0, in row-block-major order.)
+// on XCD i % 8), XCD x owns the row slabs s = x, x + 8, x + 16, ... (with
+// exactly 8 groups, e.g. 8 local experts: the slabs of group x, so that one
+// XCD streams one expert's weights) and hands out their tiles from its own
+// ticket counter, in groups of GS slabs x GN column tiles, GS * GN =
+// workgroups per XCD: the tiles that run at the same time on one XCD share A
+// and W lines in that XCD's L2. Slabs are walked in increasing order, the
+// order in which the copy role delivers row blocks. (Other grids use one
+// list, x = 0, in row-block-major order.)
 //
 // Split-K tail. When the tiles leave the grid's last round partial, or the
 // XCD lists differ in length, the last r tiles of every XCD list are split
@@ -252,11 +255,14 @@ struct TileLists {
   int nx;        // lists (8 or 1)
   int n_tn;      // column tiles
   int n_slabs;   // row slabs (256 rows, or 128 at the end of a group)
+  bool by_group; // list x = the slabs of group x (8 groups on 8 XCDs), else slabs x, x + nx, ...
+  const int* gslab;
   int GN, GS;    // group shape: GS slabs x GN column tiles
   int per_list;  // workgroups per list
   int forced_r;  // split tiles per list when given (>= 0), else -1: leftover of each list
   bool split;    // the tail is split
-  __device__ int slabs_of(int x) const { return (n_slabs - x + nx - 1) / nx; }
+  __device__ int slabs_of(int x) const { return by_group ? gslab[x + 1] - gslab[x] : (n_slabs - x + nx - 1) / nx; }
+  __device__ int slab_at(int x, int i) const { return by_group ? gslab[x] + i : x + nx * i; }
   __device__ int len(int x) const { return slabs_of(x) * n_tn; }
   // split tiles taken from the end of list x
   __device__ int r(int x) const { return !split ? 0 : forced_r >= 0 ? forced_r : len(x) % per_list; }
@@ -274,7 +280,7 @@ struct TileLists {
     const int rr = j - g * GS * n_tn;
     const int ng = rr / (gs * GN), r2 = rr - ng * gs * GN;
     const int si = r2 / GN, nn = r2 - si * GN;
-    return (x + nx * (g * GS + si)) * n_tn + ng * GN + nn;
+    return slab_at(x, g * GS + si) * n_tn + ng * GN + nn;
   }
 };
 
@@ -340,6 +346,8 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
   L.n_tn = a.N / BN;
   L.n_slabs = __builtin_amdgcn_readfirstlane(a.desc[1]);
   L.nx = (a.tile_order == 0 && grid % kXcds == 0) ? kXcds : 1;
+  L.gslab = a.gslab;
+  L.by_group = L.nx == kXcds && __builtin_amdgcn_readfirstlane(a.desc[2]) == kXcds;
   const int per_list = grid / L.nx;                      // workgroups per list
   {
     int gn = 1;
@@ -355,7 +363,8 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
   // split_tiles / lists tiles are taken from the end of every list, P = cap.
   int R = 0, P = 1;
   {
-    const int min_len = (L.n_slabs / L.nx) * L.n_tn;   // the shortest list
+    int min_len = L.len(0);                            // the shortest list
+    for (int xx = 1; xx < L.nx; ++xx) min_len = min(min_len, L.len(xx));
     L.per_list = per_list;
     L.forced_r = a.split_forced ? min(a.split_tiles / L.nx, min_len) : -1;
     L.split = true;
@@ -518,6 +527,7 @@ struct RouteArgs {
   int* elect_cur;
   int* desc;
   int* slab;                 // row slab table (see FusedArgs)
+  int* gslab;                // first slab of each group
   int* wgcount;              // TOPK: [n_wg][E + 1] per-workgroup expert counts, picks
   int* wgbase;               // TOPK: [n_wg][E + 1] expert row bases, stream base
   int* ticket;               // [0] last-workgroup ticket, [1] failure flag (zero between calls)
@@ -545,7 +555,7 @@ __device__ bool last_workgroup(int* ticket, int* sh) {
 // goff[g+1]) (multiples of 128 rows) is cut into 256-row slabs and, when its
 // size is an odd number of row blocks, one last 128-row slab, so that no slab
 // straddles two groups. Entry = first row | (128-row slab ? 1 : 0).
-__device__ void build_slabs(const int* goff, int n_groups, int* slab, int* desc) {
+__device__ void build_slabs(const int* goff, int n_groups, int* slab, int* gslab, int* desc) {
   __shared__ int sh_base[FG_MAX_GROUPS + 1];
   if (threadIdx.x == 0) {
     int n = 0;
@@ -554,13 +564,16 @@ __device__ void build_slabs(const int* goff, int n_groups, int* slab, int* desc)
       const int S = goff[g + 1] - goff[g];
       n += S / 256 + (S % 256 ? 1 : 0);
     }
+    sh_base[n_groups] = n;
     desc[1] = n;
+    desc[2] = n_groups;
   }
   __syncthreads();
   for (int g = 0; g < n_groups; ++g) {
     const int S = goff[g + 1] - goff[g], n256 = S / 256, ns = n256 + (S % 256 ? 1 : 0);
     for (int j = threadIdx.x; j < ns; j += blockDim.x) slab[sh_base[g] + j] = (goff[g] + 256 * j) | (j == n256 ? 1 : 0);
   }
+  if ((int)threadIdx.x <= n_groups) gslab[threadIdx.x] = sh_base[threadIdx.x];
 }
 
 // Seeds, group of each row block, arming, row slabs; real(rb) gives the real rows of rb.
@@ -581,7 +594,7 @@ __device__ void route_finish(const RouteArgs& a, int m_pad, const int* goff, int
   for (int i = threadIdx.x; i < a.n_shards * a.chunk_cap; i += blockDim.x) a.elect_cur[i] = 0;
   if ((int)threadIdx.x <= n_groups) a.group_off_out[threadIdx.x] = goff[threadIdx.x];
   if (threadIdx.x == 0) a.desc[0] = m_pad;
-  build_slabs(goff, m_pad > 0 ? n_groups : 0, a.slab, a.desc);
+  build_slabs(goff, m_pad > 0 ? n_groups : 0, a.slab, a.gslab, a.desc);
 }
 
 // CONTIG: shard s row i -> gathered row s*R + i; everything is arithmetic, so
@@ -607,7 +620,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_contig_kernel(RouteArgs a
   const int n256 = m_pad / 256, n_slabs = n256 + (m_pad % 256 ? 1 : 0);
   for (int j = tid; j < n_slabs; j += nth) a.slab[j] = (256 * j) | (j == n256 ? 1 : 0);
   if (tid < a.n_shards) a.stream_len[tid] = R;
-  if (tid == 0) { a.group_off_out[0] = 0; a.group_off_out[1] = m_pad; a.desc[0] = m_pad; a.desc[1] = n_slabs; }
+  if (tid == 0) {
+    a.group_off_out[0] = 0; a.group_off_out[1] = m_pad;
+    a.desc[0] = m_pad; a.desc[1] = n_slabs; a.desc[2] = 1;
+    a.gslab[0] = 0; a.gslab[1] = n_slabs;
+  }
 }
 
 // EXPLICIT: one thread per stream entry; the last workgroup computes the seeds.

@@ -70,7 +70,8 @@ class FgViews(C.Structure):
                                           "bslot", "stress_slot", "stress_pub")] + [
         ("chunk_cap", C.c_int32), ("rb_cap", C.c_int32), ("m_pad_cap", C.c_int32), ("route_ver", C.c_uint32),
         ("wg_time", C.c_void_p), ("trace", C.c_void_p), ("rb_time", C.c_void_p), ("grid", C.c_int32),
-        ("trace_cap", C.c_int32), ("wall_khz", C.c_int64), ("desc", C.c_void_p), ("slab", C.c_void_p)]
+        ("trace_cap", C.c_int32), ("wall_khz", C.c_int64), ("desc", C.c_void_p), ("slab", C.c_void_p),
+        ("group_slab", C.c_void_p)]
 
 
 class FgError(RuntimeError):

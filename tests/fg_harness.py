@@ -127,11 +127,18 @@ def control_plane(ctx: fg.Context, n_shards: int):
         inv=ctx.read_inverse_map().numpy(),
         stream_len=ctx.read_i32(v.stream_len, S).numpy(),
         group_off=ctx.read_i32(v.group_off, 65).numpy(),
-        desc=ctx.read_i32(v.desc, 2).numpy(),
+        desc=ctx.read_i32(v.desc, 3).numpy(),
         slab=ctx.read_i32(v.slab, v.rb_cap).numpy(),
+        group_slab=ctx.read_i32(v.group_slab, 65).numpy(),
         src_row=ctx.read_i32(v.src_row, S * ctx.cfg.max_rows_per_shard).numpy().reshape(S, -1),
         dst_row=ctx.read_i32(v.dst_row, S * ctx.cfg.max_rows_per_shard).numpy().reshape(S, -1),
         chunk_cap=cc, rb_cap=rbc)
+
+
+def expected_group_slabs(lay) -> np.ndarray:
+    """First slab of each group, then the slab count."""
+    counts = [(int(lay.group_off[g + 1]) - int(lay.group_off[g]) + 255) // 256 for g in range(lay.n_groups)]
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
 
 
 def expected_slabs(lay) -> np.ndarray:
@@ -157,6 +164,9 @@ def check_route(case: Case, cp) -> None:
     want = expected_slabs(lay)
     assert int(cp["desc"][0]) == lay.m_pad and int(cp["desc"][1]) == len(want), "m_pad / slab count"
     assert np.array_equal(cp["slab"][:len(want)], want), "row slab table"
+    assert int(cp["desc"][2]) == lay.n_groups, "group count"
+    gs = expected_group_slabs(lay)
+    assert np.array_equal(cp["group_slab"][:len(gs)], gs), "first slab of each group"
     assert np.array_equal(cp["seed"][:lay.n_rb], O.seeds(lay)), "padding seeds"
     real = O.real_rows(lay)
     assert np.array_equal(cp["inv"][:lay.m_pad] >= 0, real), "padding rows of the inverse map"

@@ -9,7 +9,7 @@ import torch
 import oracle as O
 from sync_protocols_amd import fg
 from fg_harness import (bits, buffers, check_control_plane, check_gathered, check_out, check_route, control_plane,
-                        dense_case, ep_case, expected_slabs, log, make_ctx, run_iters)
+                        dense_case, ep_case, expected_group_slabs, expected_slabs, log, make_ctx, run_iters)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,8 +37,12 @@ def _schedule(case, grid, split_parts, split_tiles, bn=256, tile_order=0):
     n_tiles = n_slabs * n_tn
     nx = 8 if (tile_order == 0 and grid % 8 == 0) else 1
     per_list = grid // nx
-    lens = [((n_slabs - x + nx - 1) // nx) * n_tn for x in range(nx)]
-    min_len = (n_slabs // nx) * n_tn
+    if nx == 8 and case.lay.n_groups == 8:      # list x = the slabs of group x
+        gs = expected_group_slabs(case.lay)
+        lens = [int(gs[x + 1] - gs[x]) * n_tn for x in range(8)]
+    else:
+        lens = [((n_slabs - x + nx - 1) // nx) * n_tn for x in range(nx)]
+    min_len = min(lens) if split_tiles else 0
     r = [min(split_tiles // nx, min_len)] * nx if split_tiles else [l % per_list for l in lens]
     R, P = sum(r), 1
     if R > 0 and n_tiles > grid:
