@@ -29,10 +29,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 
-constexpr int kBK = 64;             // k per LDS stage
-constexpr int kRowB = kBK * 2;      // bytes per tile row per stage: one 128-byte line
+#ifndef FG_BK
+#define FG_BK 64
+#endif
+constexpr int kBK = FG_BK;          // k per LDS stage: 64 (two stages of 128-byte rows) or 32 (a ring of
+                                    // four stages of 64-byte rows: same LDS, three stages of load lead)
+constexpr int kRowB = kBK * 2;      // bytes per tile row per stage
 constexpr int kRowsPerLoad = 1024 / kRowB;   // rows covered by one 64-lane 16-byte load
 constexpr int kKSteps = kBK / 16;   // MFMA k-steps per stage
+constexpr int kStages = kBK == 64 ? 2 : 4;
+constexpr int kChunks = kRowB / 16;          // 16-byte chunks per row and stage
+static_assert(kBK == 64 || kBK == 32, "stage depth");
 
 #ifndef FG_WAVES
 #define FG_WAVES 8
@@ -62,8 +69,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 // ds_read_b128 sixteen lanes (256 bytes, all 64 banks) at a time; the 16 rows
 // read together (same c) must land in 16 distinct 16-byte bank groups. With
 // 128-byte rows, rows of equal parity share a half of the bank space, so the
-// slot is permuted by (r >> 1) & 7.
-__device__ __forceinline__ int swz(int c, int r) { return c ^ ((r >> 1) & 7); }
+// slot is permuted by (r >> 1) & 7; with 64-byte rows, rows r mod 4 share a
+// quarter, permuted by (r >> 2) & 3.
+__device__ __forceinline__ int swz(int c, int r) { return c ^ ((r / (256 / kRowB)) & (kChunks - 1)); }
 
 // Issue this wave's share of one stage: ROWS rows starting at byte offset
 // row0_off of the buffer, k slice [k0, k0 + 64), into LDS at `lds`. Each row
@@ -72,8 +80,8 @@ template <int ROWS>
 __device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t r, uint32_t row0_off, uint32_t row_stride,
                                            uint32_t k0_bytes, char* lds, int wave, int lane) {
   constexpr int PER_WAVE = ROWS / kRowsPerLoad / kWaves;
-  const int sub = lane >> 3;           // row within the 8-row block of one load
-  const int slot = lane & 7;
+  const int sub = lane / kChunks;      // row within the block of one load
+  const int slot = lane % kChunks;
 #pragma unroll
   for (int q = 0; q < PER_WAVE; ++q) {
     const int blk = wave * PER_WAVE + q;
@@ -174,8 +182,8 @@ __device__ __forceinline__ void stage_load_one(__amdgpu_buffer_rsrc_t rA, uint32
   using T = Tile<BM, BN>;
   const bool isA = q < T::LOADS_A;
   const int blk = isA ? wave * T::LOADS_A + q : wave * T::LOADS_B + (q - T::LOADS_A);
-  const int row = blk * kRowsPerLoad + (lane >> 3);
-  const int chunk = swz(lane & 7, row);
+  const int row = blk * kRowsPerLoad + lane / kChunks;
+  const int chunk = swz(lane % kChunks, row);
   const uint32_t voff = (isA ? a_off : b_off) + (uint32_t)row * stride + (uint32_t)chunk * 16;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rB, (lds_void*)(lds + (isA ? 0 : T::A_BYTES) + blk * 1024),
                                            16, voff, k0_bytes, 0, 0);
@@ -242,34 +250,109 @@ __device__ __forceinline__ void stage_body(const char* cur, const char* nxt,
   }
 }
 
+// Ring stage of the 32-k variant: stage k in `cur`, its k-step 0 fragments in
+// f0. Phase A: MFMAs of k-step 0, reads of k-step 1 in their shadow; wait
+// until this wave's loads of stage k+1 are done (WAIT later stages may still be
+// in flight), one workgroup barrier (publishes stage k+1, and every wave has
+// read `cur`); phase B: MFMAs of k-step 1, in their shadow the reads of k-step
+// 0 of stage k+1 and the refill of `cur` with stage k+4. Loads therefore lead
+// their use by three stages.
+template <int BM, int BN, bool has_next, bool refill, int WAIT>
+__device__ __forceinline__ void stage_body4(const char* cur, const char* nxt, Frags<BM, BN>& f0, Acc<BM, BN>& acc,
+                                            int wm, int wn, int lane, __amdgpu_buffer_rsrc_t rA, uint32_t a_off,
+                                            __amdgpu_buffer_rsrc_t rB, uint32_t b_off, uint32_t stride,
+                                            uint32_t k4_bytes, char* cur_w, int wave) {
+  using T = Tile<BM, BN>;
+  constexpr int NM = T::FM * T::FN;
+  constexpr int NR = T::FM + T::FN;
+  constexpr int OPS_B = NR + T::LOADS;
+  const char* curB = cur + T::A_BYTES;
+  Frags<BM, BN> f1;
+#pragma unroll
+  for (int j = 0; j < NM; ++j) {
+    mfma_one<BM, BN>(f0, acc, j);
+#pragma unroll
+    for (int o = (j * NR) / NM; o < ((j + 1) * NR) / NM; ++o) frag_read_one<BM, BN>(cur, curB, f1, 1, o, wm, wn, lane);
+    FG_SCHED_FENCE();
+  }
+  if constexpr (has_next) wait_vmcnt<WAIT * T::LOADS>();
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < NM; ++j) {
+    mfma_one<BM, BN>(f1, acc, j);
+#pragma unroll
+    for (int o = (j * OPS_B) / NM; o < ((j + 1) * OPS_B) / NM; ++o) {
+      if (o < NR) {
+        if constexpr (has_next) frag_read_one<BM, BN>(nxt, nxt + T::A_BYTES, f0, 0, o, wm, wn, lane);
+      } else {
+        if constexpr (refill) stage_load_one<BM, BN>(rA, a_off, rB, b_off, stride, k4_bytes, cur_w, wave, lane, o - NR);
+      }
+    }
+    FG_SCHED_FENCE();
+  }
+}
+
 // nk: k-iterations of 64 to run (even, >= 2) starting at the byte offsets
 // a_off / b_off (which include the k origin); stride: row stride of both
-// buffers in bytes (K * 2).
+// buffers in bytes (K * 2). l0..l3: the LDS stage buffers (distinct objects,
+// so the compiler can tell them apart when it places its own waits); the
+// 64-k variant uses l0 and l1.
 template <int BM, int BN>
 __device__ __forceinline__ void tile_mainloop(__amdgpu_buffer_rsrc_t rA, uint32_t a_off,
-                                              __amdgpu_buffer_rsrc_t rB, uint32_t b_off, uint32_t stride, int nk,
-                                              char* lds0, char* lds1, Acc<BM, BN>& acc) {
+                                              __amdgpu_buffer_rsrc_t rB, uint32_t b_off, uint32_t stride, int nk64,
+                                              char* l0, char* l1, char* l2, char* l3, Acc<BM, BN>& acc) {
   using T = Tile<BM, BN>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / T::WGN, wn = wave % T::WGN;
-  stage_load<BM>(rA, a_off, stride, 0, lds0, wave, lane);
-  stage_load<BN>(rB, b_off, stride, 0, lds0 + T::A_BYTES, wave, lane);
-  stage_load<BM>(rA, a_off, stride, kRowB, lds1, wave, lane);
-  stage_load<BN>(rB, b_off, stride, kRowB, lds1 + T::A_BYTES, wave, lane);
-  wait_vmcnt<T::LOADS>();
-  __syncthreads();
   Frags<BM, BN> f0;
-  frags_read<BM, BN>(lds0, lds0 + T::A_BYTES, f0, 0, wm, wn, lane);
-  int kt = 0;
-  for (; kt < nk - 2; kt += 2) {
-    stage_body<BM, BN, true, true>(lds0, lds1, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
-                                   (uint32_t)(kt + 2) * kRowB, lds0, wave);
-    stage_body<BM, BN, true, true>(lds1, lds0, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
-                                   (uint32_t)(kt + 3) * kRowB, lds1, wave);
+  if constexpr (kBK == 64) {
+    const int nk = nk64;   // even
+    char* const lds0 = l0;
+    char* const lds1 = l1;
+    stage_load<BM>(rA, a_off, stride, 0, lds0, wave, lane);
+    stage_load<BN>(rB, b_off, stride, 0, lds0 + T::A_BYTES, wave, lane);
+    stage_load<BM>(rA, a_off, stride, kRowB, lds1, wave, lane);
+    stage_load<BN>(rB, b_off, stride, kRowB, lds1 + T::A_BYTES, wave, lane);
+    wait_vmcnt<T::LOADS>();
+    __syncthreads();
+    frags_read<BM, BN>(lds0, lds0 + T::A_BYTES, f0, 0, wm, wn, lane);
+    int kt = 0;
+    for (; kt < nk - 2; kt += 2) {
+      stage_body<BM, BN, true, true>(lds0, lds1, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
+                                     (uint32_t)(kt + 2) * kRowB, lds0, wave);
+      stage_body<BM, BN, true, true>(lds1, lds0, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
+                                     (uint32_t)(kt + 3) * kRowB, lds1, wave);
+    }
+    stage_body<BM, BN, true, false>(lds0, lds1, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, lds0, wave);
+    stage_body<BM, BN, false, false>(lds1, lds0, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, lds1, wave);
+  } else {
+    const int nk = 2 * nk64;   // stages of 32 k; a multiple of 4
+    char* const L[4] = {l0, l1, l2, l3};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      stage_load<BM>(rA, a_off, stride, (uint32_t)i * kRowB, L[i], wave, lane);
+      stage_load<BN>(rB, b_off, stride, (uint32_t)i * kRowB, L[i] + T::A_BYTES, wave, lane);
+    }
+    wait_vmcnt<3 * T::LOADS>();
+    __syncthreads();
+    frags_read<BM, BN>(l0, l0 + T::A_BYTES, f0, 0, wm, wn, lane);
+    int kt = 0;
+    for (; kt < nk - 4; kt += 4) {
+      stage_body4<BM, BN, true, true, 2>(l0, l1, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
+                                         (uint32_t)(kt + 4) * kRowB, l0, wave);
+      stage_body4<BM, BN, true, true, 2>(l1, l2, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
+                                         (uint32_t)(kt + 5) * kRowB, l1, wave);
+      stage_body4<BM, BN, true, true, 2>(l2, l3, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
+                                         (uint32_t)(kt + 6) * kRowB, l2, wave);
+      stage_body4<BM, BN, true, true, 2>(l3, l0, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
+                                         (uint32_t)(kt + 7) * kRowB, l3, wave);
+    }
+    stage_body4<BM, BN, true, false, 2>(l0, l1, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, l0, wave);
+    stage_body4<BM, BN, true, false, 1>(l1, l2, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, l1, wave);
+    stage_body4<BM, BN, true, false, 0>(l2, l3, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, l2, wave);
+    stage_body4<BM, BN, false, false, 0>(l3, l0, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, l3, wave);
   }
-  stage_body<BM, BN, true, false>(lds0, lds1, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, lds0, wave);
-  stage_body<BM, BN, false, false>(lds1, lds0, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, lds1, wave);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -287,7 +287,7 @@ struct TileLists {
 // One work item on a BM-row slab: the tile (whole) or one k-range of it
 // (part q of P, split slot `slot`). Returns false if a wait failed.
 template <int BM, int BN>
-__device__ __forceinline__ bool run_item(const FusedArgs& a, char* lds0, char* lds1, int* sh, int m0, int n0,
+__device__ __forceinline__ bool run_item(const FusedArgs& a, char* const* lds, int* sh, int m0, int n0,
                                          int g, int q, int P, int nk2, bool strict, long long& gate,
                                          __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rO,
                                          __amdgpu_buffer_rsrc_t rW, long long* tr) {
@@ -303,8 +303,10 @@ __device__ __forceinline__ bool run_item(const FusedArgs& a, char* lds0, char* l
   for (int i = 0; i < T::FM; ++i)
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) acc.v[i][j] = f32x16{};
-  tile_mainloop<BM, BN>(rA, (uint32_t)m0 * row_bytes + (uint32_t)k0 * kRowB, rB,
-                        (uint32_t)n0 * row_bytes + (uint32_t)k0 * kRowB, row_bytes, k1 - k0, lds0, lds1, acc);
+  // k0, k1 count k-iterations of 64 (128 bytes of a row)
+  tile_mainloop<BM, BN>(rA, (uint32_t)m0 * row_bytes + (uint32_t)k0 * 128u, rB,
+                        (uint32_t)n0 * row_bytes + (uint32_t)k0 * 128u, row_bytes, k1 - k0, lds[0], lds[1], lds[2],
+                        lds[3], acc);
   if (whole) {
     tile_store<BM, BN>(rO, a.N, m0, n0, acc, a.inv, a.route_ver);
     return true;
@@ -337,11 +339,11 @@ __device__ __forceinline__ bool run_item(const FusedArgs& a, char* lds0, char* l
 }
 
 template <int BN>
-__device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, long long* wt) {
+__device__ void gemm_role(const FusedArgs& a, char* const* lds, int* sh, long long* wt) {
   if (a.flags & kCommOnly) return;
   const int m_pad = __builtin_amdgcn_readfirstlane(a.desc[0]);
   const int grid = gridDim.x;
-  const int nk2 = a.K / (2 * kBK);                       // k-iterations in pairs
+  const int nk2 = a.K / 128;                             // pairs of 64-wide k-iterations
   TileLists L;
   L.n_tn = a.N / BN;
   L.n_slabs = __builtin_amdgcn_readfirstlane(a.desc[1]);
@@ -446,8 +448,8 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
     const int tr_id = q < 0 ? tile : n_tiles + q;
     long long* tr = ((a.flags & kTrace) && q >= 0 && tr_id < a.trace_cap) ? a.trace + (size_t)tr_id * kTraceFields
                                                                             : nullptr;
-    const bool ok = (entry & 1) ? run_item<128, BN>(a, lds0, lds1, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr)
-                                : run_item<256, BN>(a, lds0, lds1, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr);
+    const bool ok = (entry & 1) ? run_item<128, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr)
+                                : run_item<256, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr);
     if (!ok) break;
     if (q < 0) ++tiles; else ++parts;
     if ((a.flags & kTrace) && threadIdx.x == 0 && tr_id < a.trace_cap) a.trace[(size_t)tr_id * kTraceFields + 3] = now_ticks();
@@ -463,8 +465,13 @@ __device__ void gemm_role(const FusedArgs& a, char* lds0, char* lds1, int* sh, l
 
 template <int BN>
 __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
+  // one array per LDS stage (distinct objects for the compiler's wait placement)
+  constexpr int kS23 = kStages == 4 ? Tile<256, BN>::STAGE : 16;
   __shared__ __attribute__((aligned(16))) char lds0[Tile<256, BN>::STAGE];
   __shared__ __attribute__((aligned(16))) char lds1[Tile<256, BN>::STAGE];
+  __shared__ __attribute__((aligned(16))) char lds2[kS23];
+  __shared__ __attribute__((aligned(16))) char lds3[kS23];
+  char* const lds[4] = {lds0, lds1, lds2, lds3};
   __shared__ const uint16_t* sh_shard[FG_MAX_SHARDS];
   __shared__ int sh[5];
   long long* wt = a.wgtime + (size_t)blockIdx.x * kWgTimeFields;
@@ -480,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
     comm_role(a, sh_shard);
     t_comm = (long long)now_ticks();
   }
-  gemm_role<BN>(a, lds0, lds1, sh, wt);
+  gemm_role<BN>(a, lds, sh, wt);
   if (threadIdx.x == 0) {
     wt[WT_CLK1] = (long long)__builtin_amdgcn_s_memtime();
     wt[WT_START] = t_start;
