@@ -468,6 +468,74 @@ def gemm_check(out_bits, C64, K, sigma_x, sigma_w, real_mask=None) -> dict:
 
 
 # ---------------------------------------------------------------------------
+# Combine: the reverse of the expert dispatch ("PCIe sync protocols" §3: the
+# producers' rows are pushed to the destination's staging buffer and the last
+# writer of each 64-row chunk, elected by a local count, publishes its slot;
+# the destination then sums each token's expert rows with its gate weights)
+# ---------------------------------------------------------------------------
+
+def combine_picks(topk, expert_base: int, n_local: int) -> list:
+    """Per shard s, the stream of local picks in stream order (reading R11:
+    tokens ascending, then their top-k choices in list order), as (t, k) pairs.
+    Stream entry i of shard s is the i-th pair; it is the same stream as
+    ``layout_topk``'s."""
+    topk = np.asarray(topk, dtype=np.int64)
+    S, T, KK = topk.shape
+    out = []
+    for s in range(S):
+        pairs = []
+        for t in range(T):
+            for k in range(KK):
+                if 0 <= int(topk[s, t, k]) - expert_base < n_local:
+                    pairs.append((t, k))
+        out.append(pairs)
+    return out
+
+
+def combine_staging(out_bits, lay: Layout) -> list:
+    """Pushed rows, per shard in stream order: staging[s][i] = out[dst_row[s][i]]
+    bitwise (reading R25: the staging buffer is the destination rank's receive
+    buffer, indexed by the destination's stream entry)."""
+    out_bits = np.asarray(out_bits)
+    return [out_bits[np.asarray(lay.dst_row[s], dtype=np.int64)] for s in range(lay.n_shards)]
+
+
+def combine(out_bits, weights, topk, expert_base: int, n_local: int, lay: Layout) -> np.ndarray:
+    """y[s][t][n] = sum over the local picks (t, k) of shard s of
+    weights[s][t][k] * out[g(s, t, k)][n], in float64 with bf16 outputs and fp32
+    weights decoded exactly; tokens without a local pick give 0 (reading R25:
+    on this GPU only the local experts' contributions are summed). g(s, t, k) is
+    the gathered row the dispatch gave pick (t, k) of shard s."""
+    out = bf16_to_f64(out_bits)
+    w = np.asarray(weights, dtype=np.float32).astype(np.float64)
+    picks = combine_picks(topk, expert_base, n_local)
+    S, T, _ = np.asarray(topk).shape
+    N = out.shape[1]
+    y = np.zeros((S, T, N), dtype=np.float64)
+    for s in range(S):
+        for i, (t, k) in enumerate(picks[s]):
+            g = int(lay.dst_row[s][i])
+            y[s, t] += w[s, t, k] * out[g]
+    return y
+
+
+def combine_tolerance(out_bits, weights, topk, expert_base: int, n_local: int, lay: Layout) -> np.ndarray:
+    """Per element bound for a float32 weighted sum of at most KK terms rounded
+    once to bf16 (reading R26): half a bf16 ulp of the exact sum plus
+    KK * 2^-23 times the sum of the terms' magnitudes (float32 products and adds)."""
+    out = np.abs(bf16_to_f64(out_bits))
+    w = np.abs(np.asarray(weights, dtype=np.float32).astype(np.float64))
+    picks = combine_picks(topk, expert_base, n_local)
+    S, T, KK = np.asarray(topk).shape
+    mag = np.zeros((S, T, out.shape[1]), dtype=np.float64)
+    for s in range(S):
+        for i, (t, k) in enumerate(picks[s]):
+            mag[s, t] += w[s, t, k] * out[int(lay.dst_row[s][i])]
+    y = combine(out_bits, weights, topk, expert_base, n_local, lay)
+    return 0.5 * bf16_ulp(y) + KK * 2.0 ** -23 * mag
+
+
+# ---------------------------------------------------------------------------
 # Protocol stress workload (PCIe sync protocols §3: tens of thousands of
 # signals per round over dozens of rounds; §4 chunked slots)
 # ---------------------------------------------------------------------------

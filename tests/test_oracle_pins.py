@@ -390,3 +390,78 @@ def test_workload_distributions():
     assert w.shape == (512, 256) and abs(w.std().item() - 0.02) < 0.001
     p = W.dense_inputs(3, 2, 64, 8, 8, gather="permutation").perm
     assert sorted(p.tolist()) == list(range(128))
+
+
+# ----------------------------------------------------------------- combine
+
+def _golden(name):
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        return json.load(f)
+
+
+def test_combine_hand_worked_example():
+    g = _golden("combine_tiny.json")
+    topk = np.array(g["topk"])
+    lay = O.layout_topk(topk, g["expert_base"], g["n_local"], row_block=g["row_block"])
+    assert lay.m_pad == g["m_pad"]
+    assert [list(map(int, d)) for d in lay.dst_row] == g["dst_row"]
+    picks = O.combine_picks(topk, g["expert_base"], g["n_local"])
+    assert [[list(p) for p in ps] for ps in picks] == g["picks"]
+    out_bits = O.f64_to_bf16(np.array(g["out"], dtype=np.float64))
+    y = O.combine(out_bits, np.array(g["weights"], dtype=np.float32), topk, g["expert_base"], g["n_local"], lay)
+    assert np.array_equal(y, np.array(g["y"]))
+    st = O.combine_staging(out_bits, lay)
+    for s in range(2):
+        assert np.array_equal(st[s], out_bits[np.array(g["dst_row"][s])])
+
+
+def test_combine_after_identity_dispatch_is_identity():
+    """Dispatch with every expert local, an identity expert (out row = its gathered
+    row) and weights that sum to 1 over each token's picks: combine returns each
+    token's own row exactly."""
+    rng = np.random.default_rng(7)
+    S, T, KK, E = 3, 40, 4, 8
+    topk = np.stack([np.stack([rng.permutation(E)[:KK] for _ in range(T)]) for _ in range(S)])
+    lay = O.layout_topk(topk, 0, E, row_block=16)
+    x = [O.f64_to_bf16(rng.standard_normal((T, 24))) for _ in range(S)]
+    G = O.gather(x, lay)
+    w = np.array([0.5, 0.25, 0.125, 0.125], dtype=np.float32)[None, None, :].repeat(S, 0).repeat(T, 1)
+    y = O.combine(G, w, topk, 0, E, lay)
+    for s in range(S):
+        assert np.array_equal(y[s], O.bf16_to_f64(x[s]))
+
+
+def test_combine_partial_locality_and_tolerance_teeth():
+    rng = np.random.default_rng(8)
+    S, T, KK, E = 2, 30, 4, 16
+    topk = np.stack([np.stack([rng.permutation(E)[:KK] for _ in range(T)]) for _ in range(S)])
+    lay = O.layout_topk(topk, 4, 4, row_block=8)
+    out = O.f64_to_bf16(rng.standard_normal((lay.m_pad, 16)))
+    w = rng.random((S, T, KK)).astype(np.float32)
+    y = O.combine(out, w, topk, 4, 4, lay)
+    # brute force over the top-k lists directly
+    gpos = {}
+    for s in range(S):
+        for i, d in enumerate(lay.dst_row[s]):
+            gpos[(s, i)] = int(d)
+    picks = O.combine_picks(topk, 4, 4)
+    for s in range(S):
+        for t in range(T):
+            want = np.zeros(16)
+            for i, (tt, k) in enumerate(picks[s]):
+                if tt == t:
+                    assert 4 <= topk[s, t, k] < 8
+                    want += float(w[s, t, k]) * O.bf16_to_f64(out[gpos[(s, i)]])
+            assert np.allclose(y[s, t], want, rtol=0, atol=1e-12)
+            if not any(4 <= e < 8 for e in topk[s, t]):
+                assert np.all(y[s, t] == 0)
+    tol = O.combine_tolerance(out, w, topk, 4, 4, lay)
+    assert np.all(tol > 0)
+    yb = O.bf16_to_f64(O.f64_to_bf16(y))
+    assert np.all(np.abs(yb - y) <= tol)
+    bad = yb.copy()
+    idx = np.unravel_index(np.argmax(np.abs(y)), y.shape)
+    bad[idx] += 3 * tol[idx]
+    assert not np.all(np.abs(bad - y) <= tol)
