@@ -103,7 +103,8 @@ typedef struct {
                                   1 = one row-block-major list */
   int32_t copy_rows;           /* rows per copy batch of one wave: 1, 2, 4, 8 or 16, capped so that at most
                                   32 16-byte vectors per lane are in flight (0 = the cap) */
-  int32_t reserved;
+  int32_t combine_wg;          /* workgroups of the combine kernel (0 = 2 per compute unit); any count is
+                                  safe, the kernel assumes no residency */
 } fg_config;
 
 typedef enum {
@@ -148,7 +149,8 @@ typedef struct {
   double t_rtt_us;                /* last fg_pingpong: device round trip */
   int32_t n_comm_wg, n_gemm_wg, cu_count, m_pad_cap;
   int32_t tiles_whole, tiles_split; /* last fused kernel: whole tiles, tiles computed as split-K parts */
-  int32_t split_parts, reserved;  /* split_parts: k-ranges per split tile (1 when none is split) */
+  int32_t split_parts;            /* k-ranges per split tile (1 when none is split) */
+  int32_t combine_seq;            /* last combine sequence number issued (monotonic, never reset) */
   double clock_mhz;               /* last fused kernel: shader-clock cycles / wall time, over all workgroups */
 } fg_stats_t;
 
@@ -188,6 +190,13 @@ typedef struct {
                                  every group is cut into 256-row slabs plus one 128-row slab if its size is an
                                  odd number of 128-row blocks */
   const int32_t* group_slab;  /* [groups + 1] first slab of each group (the last entry is n_slabs) */
+  /* Combine plane (fg_combine) and the per-entry tables of the TOPK route: */
+  const int32_t* combine_slot;  /* [n_shards][chunk_cap] */
+  const int32_t* combine_elect; /* [2][n_shards][chunk_cap] parity double-buffered */
+  const int32_t* combine_pub;   /* [n_shards][chunk_cap] (VERIFY) */
+  const int32_t* src_k;         /* [n_shards][max_rows_per_shard] top-k position of each stream entry */
+  const int32_t* tok_first;     /* [n_shards][max_rows_per_shard + 1] first stream entry of each token;
+                                   entry [tokens] = the stream length */
 } fg_views_t;
 
 /* Create a context on `hip_device`: validates the configuration, allocates and
@@ -247,6 +256,36 @@ fg_status fg_pingpong(fg_ctx* ctx, int32_t round_trips, int32_t sys_scope, hipSt
  *   flags:      FG_CALL_STRICT / FG_FAULT_DROP_PUBLISH */
 fg_status fg_stress(fg_ctx* ctx, const int32_t* chunk_rows, const int32_t* delays_ns,
                     int32_t* payload, uint32_t flags, hipStream_t stream);
+
+/* Combine, the reverse of the expert dispatch ("PCIe sync protocols" §3 the
+ * pushed rows, the local count and the last writer's slot store; §4 one slot
+ * per 64 entries of a stream). Runs on the TOPK route of the last
+ * fg_gather_gemm call (FG_EINVAL for any other route). cseq = ++cseq; one
+ * kernel whose workgroups first push every stream entry i of every shard s,
+ * staging[s][i] = out[dst_row[s][i]] bitwise (device-coherent 16-byte stores),
+ * and count the rows of each 64-entry chunk; the add that completes a chunk
+ * elects its single publisher, which stores cseq into the chunk's combine
+ * slot. Then, per token t of shard s, after the slots of the chunks holding
+ * its entries carry cseq:
+ *   y[s][t][n] = bf16_rne( sum over the token's local picks k, in k order, of
+ *                          weights[s][t][k] * staging[s][i(t,k)][n] )
+ * in fp32; a token with no local pick gets a zero row. Only this GPU's experts
+ * are summed.
+ *   out:     device bf16 [m_pad][N] expert outputs in gathered-row order (as
+ *            written by fg_gather_gemm)
+ *   weights: device fp32 [n_shards][tokens][topk_k] gate weights
+ *   staging: host array of n_shards device pointers, bf16 [max_rows_per_shard][N]
+ *            (each shard's receive buffer, indexed by stream entry; written)
+ *   y:       host array of n_shards device pointers, bf16 [tokens][N] (written)
+ *   flags:   FG_CALL_COMM_ONLY (push only), FG_CALL_GEMM_ONLY (weighted sums
+ *            only, from a staging buffer an earlier call filled; no slot
+ *            waits), FG_CALL_VERIFY (publisher counts, polls), FG_CALL_STRICT,
+ *            FG_FAULT_DROP_PUBLISH (publisher of chunk (0,0) skips its slot
+ *            store: the waits on it time out -> FG_ETIMEOUT)
+ * Errors: FG_EINVAL (route, NULLs, stream), FG_ESTATE, FG_ETIMEOUT /
+ * FG_EPROTOCOL from an earlier call, FG_EHIP. */
+fg_status fg_combine(fg_ctx* ctx, const void* out, const float* weights, void* const* staging,
+                     void* const* y, uint32_t flags, hipStream_t stream);
 
 /* Copy the observation counters to *out. wait != 0 first synchronises the
  * bound stream (needed for device-computed fields and timings). */

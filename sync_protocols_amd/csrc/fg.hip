@@ -12,7 +12,7 @@
 #include <cstring>
 #include <new>
 
-#include "fg_kernels.hpp"
+#include "fg_combine.hpp"
 
 using namespace fg;
 
@@ -59,6 +59,12 @@ struct Plane {
   int* s_slot;
   int* s_elect;    // [2][P*C*KC]
   int* s_pub;
+  int* src_k;      // [S][rs_cap] TOPK: top-k position of each stream entry
+  int* tok_first;  // [S][rs_cap + 1] TOPK: first stream entry of each token
+  int* cslot;      // combine plane: slots, election counts x2, publisher counts, tickets x2
+  int* celect;
+  int* cpub;
+  int* ctick;
 };
 
 }  // namespace
@@ -76,7 +82,8 @@ struct fg_ctx {
   char* plane_mem = nullptr;
   Plane p{};
   int* host_status = nullptr;
-  int seq = 0, bseq = 0, sseq = 0, ppseq = 0;
+  int seq = 0, bseq = 0, sseq = 0, ppseq = 0, cseq = 0;
+  int topk_rows = 0, topk_k = 0;   // tokens per shard and k of the last TOPK route
   uint32_t route_ver = 0;
   int route_wg_cap = 0;
   fg_status sticky = FG_OK;
@@ -120,6 +127,7 @@ static bool config_ok(const fg_config* c) {
   if (c->tile_order < 0 || c->tile_order > 1) return false;
   if (c->copy_rows != 0 && c->copy_rows != 1 && c->copy_rows != 2 && c->copy_rows != 4 && c->copy_rows != 8 &&
       c->copy_rows != 16) return false;
+  if (c->combine_wg < 0 || c->combine_wg > 65536) return false;
   if (c->stress_producers < 0 || c->stress_consumers < 0 || c->stress_max_chunks < 0) return false;
   const long long m = (long long)c->n_shards * c->max_rows_per_shard + (long long)c->n_groups * FG_ROW_BLOCK;
   if (m * c->K * 2 >= (1ll << 32)) return false;   // 32-bit buffer offsets
@@ -183,7 +191,11 @@ static fg_status launch_route(fg_ctx* ctx, const fg_route* route, int mode, int 
     }
     ra.src_in = route->src_row; ra.dst_in = route->dst_row;
   }
-  if (mode == FG_ROUTE_TOPK) { ra.topk = route->topk; ra.topk_k = route->topk_k; ra.expert_base = route->expert_base; }
+  if (mode == FG_ROUTE_TOPK) {
+    ra.topk = route->topk; ra.topk_k = route->topk_k; ra.expert_base = route->expert_base;
+    ctx->topk_rows = rows; ctx->topk_k = route->topk_k;
+  }
+  ra.src_k = ctx->p.src_k; ra.tok_first = ctx->p.tok_first;
   const int cur = ctx->seq & 1;
   ctx->route_ver += 1;
   ra.ver = ctx->route_ver;
@@ -312,7 +324,9 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
                o_err = take(64), o_stats = take(ST_COUNT * 8), o_bslot = take((size_t)S * S * 4),
                o_pp = take(512), o_tdev = take(64), o_wg = take((size_t)grid_max * kWgTimeFields * 8),
                o_sslot = take((size_t)ctx->s_slots * 4), o_select = take(2 * (size_t)ctx->s_slots * 4),
-               o_spub = take((size_t)ctx->s_slots * 4);
+               o_spub = take((size_t)ctx->s_slots * 4), o_srck = take(nrs * 4),
+               o_tokf = take((size_t)S * (cfg->max_rows_per_shard + 1) * 4), o_cslot = take(nch * 4),
+               o_celect = take(2 * nch * 4), o_cpub = take(nch * 4), o_ctick = take(2 * kCombTickInts * 4);
   if (hipMalloc(&ctx->plane_mem, off) != hipSuccess) { delete ctx; return FG_ENOMEM; }
   if (hipMemset(ctx->plane_mem, 0, off) != hipSuccess) { (void)hipFree(ctx->plane_mem); delete ctx; return FG_EHIP; }
   char* b = ctx->plane_mem;
@@ -328,6 +342,8 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
   p.bslot = (int*)(b + o_bslot); p.pp = (int*)(b + o_pp); p.tdev = (long long*)(b + o_tdev);
   p.wgtime = (long long*)(b + o_wg); p.s_slot = (int*)(b + o_sslot); p.s_elect = (int*)(b + o_select);
   p.s_pub = (int*)(b + o_spub);
+  p.src_k = (int*)(b + o_srck); p.tok_first = (int*)(b + o_tokf); p.cslot = (int*)(b + o_cslot);
+  p.celect = (int*)(b + o_celect); p.cpub = (int*)(b + o_cpub); p.ctick = (int*)(b + o_ctick);
   if (hipHostMalloc((void**)&ctx->host_status, 64, hipHostMallocCoherent) != hipSuccess) {
     (void)hipFree(ctx->plane_mem); delete ctx; return FG_ENOMEM;
   }
@@ -519,12 +535,43 @@ fg_status fg_stress(fg_ctx* ctx, const int32_t* chunk_rows, const int32_t* delay
   return FG_OK;
 }
 
+fg_status fg_combine(fg_ctx* ctx, const void* out, const float* weights, void* const* staging, void* const* y,
+                     uint32_t flags, hipStream_t stream) {
+  if (!ctx) return FG_EINVAL;
+  fg_status s = check_sticky(ctx);
+  if (s != FG_OK) return s;
+  const fg_config& c = ctx->cfg;
+  if (!out || !weights || !staging || !y) return FG_EINVAL;
+  for (int i = 0; i < c.n_shards; ++i) if (!staging[i] || !y[i]) return FG_EINVAL;
+  if ((flags & FG_CALL_COMM_ONLY) && (flags & FG_CALL_GEMM_ONLY)) return FG_EINVAL;
+  if (ctx->route_cached_mode != FG_ROUTE_TOPK || ctx->topk_rows < 1) return FG_EINVAL;
+  if (bind_stream(ctx, stream) != FG_OK) return FG_EINVAL;
+  HIPCHK(hipSetDevice(ctx->device));
+  ctx->cseq += 1;
+  const int cur = ctx->cseq & 1, nxt = cur ^ 1;
+  const size_t nch = (size_t)c.n_shards * ctx->chunk_cap;
+  CombineArgs a{};
+  a.out = (const uint16_t*)out; a.weights = weights;
+  for (int i = 0; i < c.n_shards; ++i) { a.staging[i] = (uint16_t*)staging[i]; a.y[i] = (uint16_t*)y[i]; }
+  a.N = c.N; a.n_shards = c.n_shards; a.T = ctx->topk_rows; a.KK = ctx->topk_k; a.rs_cap = c.max_rows_per_shard;
+  a.chunk_cap = ctx->chunk_cap;
+  a.desc = ctx->p.desc; a.stream_len = ctx->p.stream_len; a.dst_row = ctx->p.dst_row; a.src_k = ctx->p.src_k;
+  a.tok_first = ctx->p.tok_first;
+  a.cslot = ctx->p.cslot; a.celect_cur = ctx->p.celect + cur * nch; a.celect_nxt = ctx->p.celect + nxt * nch;
+  a.cpub = ctx->p.cpub; a.tick_cur = ctx->p.ctick + cur * kCombTickInts; a.tick_nxt = ctx->p.ctick + nxt * kCombTickInts;
+  a.stats = ctx->p.stats; a.err = sink(ctx); a.seq = ctx->cseq; a.flags = flags; a.timeout_ticks = timeout_ticks(ctx);
+  const int grid = c.combine_wg ? c.combine_wg : 2 * ctx->cu_count;
+  hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kCombThreads), 0, stream, a);
+  HIPCHK(hipGetLastError());
+  return FG_OK;
+}
+
 fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait) {
   if (!ctx || !out) return FG_EINVAL;
   HIPCHK(hipSetDevice(ctx->device));
   if (wait && ctx->stream_bound) HIPCHK(hipStreamSynchronize(ctx->stream));
   memset(out, 0, sizeof(*out));
-  out->seq = ctx->seq; out->bseq = ctx->bseq; out->stress_seq = ctx->sseq;
+  out->seq = ctx->seq; out->bseq = ctx->bseq; out->stress_seq = ctx->sseq; out->combine_seq = ctx->cseq;
   out->n_comm_wg = ctx->n_comm; out->n_gemm_wg = ctx->n_gemm; out->cu_count = ctx->cu_count;
   out->m_pad_cap = ctx->m_pad_cap;
   if (!wait) { out->m_pad = ctx->last_m_pad; return FG_OK; }
@@ -603,6 +650,8 @@ fg_status fg_views(fg_ctx* ctx, fg_views_t* v) {
   v->wg_time = (const int64_t*)p.wgtime; v->trace = (const int64_t*)p.trace; v->rb_time = (const int64_t*)p.rb_time;
   v->grid = ctx->n_comm + ctx->n_gemm; v->trace_cap = ctx->trace_cap; v->wall_khz = ctx->wall_khz;
   v->desc = p.desc; v->slab = p.slab; v->group_slab = p.gslab;
+  v->combine_slot = p.cslot; v->combine_elect = p.celect; v->combine_pub = p.cpub; v->src_k = p.src_k;
+  v->tok_first = p.tok_first;
   return FG_OK;
 }
 

@@ -1,0 +1,291 @@
+// Combine: the reverse of the expert dispatch, with the same signalling.
+//
+// "PCIe sync protocols" §3 (layer-1 combine: the producer pushes its rows into
+// the receiver's buffer, counts them locally and the last writer of each chunk
+// stores seq into the chunk's single-writer slot) and §4 (one signal per 64
+// entries of a stream). Here the producer side is this GPU's expert outputs,
+// laid out in gathered-row order by the dispatch, and the receiver side is one
+// staging buffer per source shard, indexed by that shard's stream entries; the
+// shard's side then forms, per token, the gate-weighted sum of its local picks.
+//
+// One kernel, two phases taken from ticket counters:
+//  * push items (16 stream entries of one shard, 4 per wave): copy
+//    out[dst_row[s][i]] -> staging[s][i] bitwise with device-coherent stores,
+//    release, add the wave's rows to the chunk's election count; the add that
+//    completes the chunk elects the wave, whose leader stores seq in the slot;
+//  * reduce items (16 tokens of one shard, 4 per wave): wait until the slot of
+//    every chunk holding the tokens' entries carries seq, acquire, and write
+//    y[s][t] = bf16(sum over the token's entries e, in k order, of
+//    w[s][t][k(e)] * staging[s][e]) with fp32 products and sums.
+// A workgroup takes reduce items only after the push queue is exhausted, so
+// every push item is held by a running workgroup that never waits: no
+// residency assumption is needed for freedom from deadlock ("PCIe sync
+// protocols" §6: every wait has a supplier that does not wait).
+#pragma once
+
+#include "fg_kernels.hpp"
+
+namespace fg {
+
+constexpr int kCombWaves = 4;
+constexpr int kCombThreads = 64 * kCombWaves;
+constexpr int kPushEntries = 16;                          // stream entries per push item
+constexpr int kPushPerWave = kPushEntries / kCombWaves;
+constexpr int kRedTokens = 16;                            // tokens per reduce item
+constexpr int kRedPerWave = kRedTokens / kCombWaves;
+constexpr int kCombU = 2;                                 // 16-byte vectors per lane and row per column step
+constexpr int kCombTickInts = 128;                        // [0] push ticket, [64] reduce ticket
+
+static_assert(kChunk % kPushEntries == 0, "a push item lies inside one chunk");
+static_assert(kPushPerWave <= 64 && kRedPerWave * 16 <= 64, "lane layout");
+
+struct CombineArgs {
+  const uint16_t* out;            // [m_pad][N] expert outputs, gathered-row order
+  const float* weights;           // [S][T][KK] gate weights
+  uint16_t* staging[FG_MAX_SHARDS];  // per shard [rs_cap][N], stream-entry order
+  uint16_t* y[FG_MAX_SHARDS];     // per shard [T][N]
+  int N, n_shards, T, KK, rs_cap, chunk_cap;
+  const int* desc;                // [0] = m_pad of the route in use
+  const int* stream_len;
+  const int* dst_row;             // [S][rs_cap]
+  const int* src_k;               // [S][rs_cap] top-k position of each stream entry
+  const int* tok_first;           // [S][rs_cap + 1] first stream entry of each token, [T] = stream length
+  int* cslot;                     // [S][chunk_cap]
+  int* celect_cur;                // [S][chunk_cap]
+  int* celect_nxt;
+  int* cpub;
+  int* tick_cur;                  // [kCombTickInts]
+  int* tick_nxt;
+  unsigned long long* stats;
+  ErrorSink err;
+  int seq;
+  uint32_t flags;
+  uint64_t timeout_ticks;
+};
+
+__device__ __forceinline__ const uint16_t* uniform_ptr(const void* p) {
+  const uint64_t b = (uint64_t)p;
+  return (const uint16_t*)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b));
+}
+
+// One wave: push entries eb .. eb + kPushPerWave - 1 of shard s.
+__device__ __forceinline__ void combine_push(const CombineArgs& a, const uint16_t* stg, int s, int eb, int n_s,
+                                             uint32_t out_bytes, int lane) {
+  const bool strict = a.flags & kStrict;
+  const uint32_t row_bytes = (uint32_t)a.N * 2;
+  int g = -1;
+  if (lane < kPushPerWave && eb + lane < n_s) {
+    g = a.dst_row[s * a.rs_cap + eb + lane];
+    if (g < 0 || (uint32_t)g * row_bytes >= out_bytes) {
+      raise_error(a.err, kErrProtocol, 0x60000000 | s);
+      g = -1;
+    }
+  }
+  __amdgpu_buffer_rsrc_t rs[kPushPerWave], rd[kPushPerWave];
+#pragma unroll
+  for (int r = 0; r < kPushPerWave; ++r) {
+    const int gr = readlane(g, r);
+    const bool valid = gr >= 0;
+    rs[r] = buffer_rsrc(a.out + (size_t)(valid ? gr : 0) * a.N, valid ? row_bytes : 0u);
+    rd[r] = buffer_rsrc(stg + (size_t)(eb + r) * a.N, valid ? row_bytes : 0u);
+  }
+  const int nvec = a.N / 8;
+  for (int c0 = 0; c0 < nvec; c0 += 64 * 2 * kCombU) {
+    v4i v[kPushPerWave][2 * kCombU];
+#pragma unroll
+    for (int r = 0; r < kPushPerWave; ++r)
+#pragma unroll
+      for (int u = 0; u < 2 * kCombU; ++u)
+        v[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rs[r], (uint32_t)(c0 + u * 64 + lane) * 16, 0, kPolNT);
+#pragma unroll
+    for (int r = 0; r < kPushPerWave; ++r)
+#pragma unroll
+      for (int u = 0; u < 2 * kCombU; ++u) store16_coherent(rd[r], (uint32_t)(c0 + u * 64 + lane) * 16, v[r][u]);
+  }
+  release_coherent(strict);
+  const int n_done = __popcll(ballot(g >= 0));
+  if (lane == 0 && n_done > 0) {
+    const int c = eb / kChunk, ch = s * a.chunk_cap + c;
+    const int old = strict ? fetch_add_acq_rel(a.celect_cur + ch, n_done) : fetch_add_relaxed(a.celect_cur + ch, n_done);
+    const int expect = min(kChunk, n_s - kChunk * c);
+    if (old + n_done == expect) {
+      if (!((a.flags & kDropPublish) && ch == 0)) slot_publish(a.cslot + ch, a.seq, strict);
+      if (a.flags & kVerify) {
+        atomicAdd(a.cpub + ch, 1);
+        atomicAdd(a.stats + ST_PUBLISHES, 1ull);
+      }
+    } else if (old + n_done > expect) {
+      raise_error(a.err, kErrProtocol, 0x10000000 | ch);
+    }
+  }
+}
+
+__device__ __forceinline__ void bf16x8_fma(float* acc, v4i x, float w) {
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const uint32_t b = (uint32_t)x[h];
+    acc[2 * h] += w * __builtin_bit_cast(float, b << 16);
+    acc[2 * h + 1] += w * __builtin_bit_cast(float, b & 0xFFFF0000u);
+  }
+}
+
+// One wave: tokens tb .. tb + kRedPerWave - 1 of shard s (entries already acquired).
+__device__ __forceinline__ void combine_reduce(const CombineArgs& a, const uint16_t* stg, uint16_t* yb, int s, int tb,
+                                               int lane) {
+  const uint32_t row_bytes = (uint32_t)a.N * 2;
+  const int* tf_s = a.tok_first + (size_t)s * (a.rs_cap + 1);
+  int tf = 0;
+  if (lane <= kRedPerWave) tf = tf_s[min(tb + lane, a.T)];
+  int ea[kRedPerWave], ne[kRedPerWave];
+  int maxn = 0;
+  // the tables come from the layout step; clamping keeps every access inside
+  // the buffers even if a failed layout left them stale (it also raised an error)
+  tf = min(max(tf, 0), a.rs_cap);
+#pragma unroll
+  for (int r = 0; r < kRedPerWave; ++r) {
+    ea[r] = readlane(tf, r);
+    ne[r] = tb + r < a.T ? max(0, readlane(tf, r + 1) - ea[r]) : 0;
+    maxn = max(maxn, ne[r]);
+  }
+  // gate weight of entry j of token r in lane 16 r + j (j < 16); entries 16..
+  // of a token (more than 16 local picks) load their weight when used
+  float wl = 0.f;
+  {
+    const int r = lane >> 4, j = lane & 15;
+    const int my_ea = __shfl(tf, r, 64);
+    const int my_ne = tb + r < a.T ? __shfl(tf, r + 1, 64) - my_ea : 0;
+    if (j < my_ne) {
+      const int k = min(max(a.src_k[s * a.rs_cap + my_ea + j], 0), a.KK - 1);
+      wl = a.weights[((size_t)s * a.T + tb + r) * a.KK + k];
+    }
+  }
+  const int nvec = a.N / 8;
+  for (int c0 = 0; c0 < nvec; c0 += 64 * kCombU) {
+    float acc[kRedPerWave][kCombU][8];
+#pragma unroll
+    for (int r = 0; r < kRedPerWave; ++r)
+#pragma unroll
+      for (int u = 0; u < kCombU; ++u)
+#pragma unroll
+        for (int h = 0; h < 8; ++h) acc[r][u][h] = 0.f;
+    for (int j = 0; j < maxn; ++j) {
+      v4i v[kRedPerWave][kCombU];
+      float w[kRedPerWave];
+#pragma unroll
+      for (int r = 0; r < kRedPerWave; ++r) {
+        const bool valid = j < ne[r];
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(stg + (size_t)(valid ? ea[r] + j : 0) * a.N, valid ? row_bytes : 0u);
+#pragma unroll
+        for (int u = 0; u < kCombU; ++u)
+          v[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(c0 + u * 64 + lane) * 16, 0, kPolNT);
+        float wr = 0.f;
+        if (valid) {
+          if (j < 16) {
+            wr = __builtin_bit_cast(float, readlane(__builtin_bit_cast(int, wl), 16 * r + j));
+          } else {
+            const int k = min(max(a.src_k[s * a.rs_cap + ea[r] + j], 0), a.KK - 1);
+            wr = a.weights[((size_t)s * a.T + tb + r) * a.KK + k];
+          }
+        }
+        w[r] = wr;
+      }
+#pragma unroll
+      for (int r = 0; r < kRedPerWave; ++r)
+#pragma unroll
+        for (int u = 0; u < kCombU; ++u) bf16x8_fma(acc[r][u], v[r][u], w[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < kRedPerWave; ++r) {
+      const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(yb + (size_t)min(tb + r, a.T - 1) * a.N, tb + r < a.T ? row_bytes : 0u);
+#pragma unroll
+      for (int u = 0; u < kCombU; ++u) {
+        v4i o;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) o[h] = (int)pack_bf16x2(acc[r][u][2 * h], acc[r][u][2 * h + 1]);
+        store16_stream(ro, (uint32_t)(c0 + u * 64 + lane) * 16, o);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
+  __shared__ const uint16_t* sh_stg[FG_MAX_SHARDS];
+  __shared__ uint16_t* sh_y[FG_MAX_SHARDS];
+  __shared__ int sh_base[FG_MAX_SHARDS + 1];     // push items before shard s
+  __shared__ int sh_item[2];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = gridDim.x;
+  // arm the other parity for the next call (nothing else touches it here)
+  for (int i = blockIdx.x * kCombThreads + threadIdx.x; i < a.n_shards * a.chunk_cap; i += G * kCombThreads)
+    a.celect_nxt[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x < 2) a.tick_nxt[threadIdx.x * 64] = 0;
+  if ((int)threadIdx.x < a.n_shards) {
+    sh_stg[threadIdx.x] = a.staging[threadIdx.x];
+    sh_y[threadIdx.x] = a.y[threadIdx.x];
+  }
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int s = 0; s < a.n_shards; ++s) {
+      sh_base[s] = n;
+      n += (a.stream_len[s] + kPushEntries - 1) / kPushEntries;
+    }
+    sh_base[a.n_shards] = n;
+  }
+  __syncthreads();
+  const int m_pad = __builtin_amdgcn_readfirstlane(a.desc[0]);
+  const uint32_t out_bytes = (uint32_t)m_pad * (uint32_t)a.N * 2;
+  const int n_push = sh_base[a.n_shards];
+  const bool verify = a.flags & kVerify;
+
+  if (!(a.flags & kGemmOnly)) {
+    for (int phase = 0;; phase ^= 1) {
+      if (threadIdx.x == 0) sh_item[phase] = error_raised(a.err) ? n_push : fetch_add_relaxed(a.tick_cur, 1);
+      __syncthreads();
+      const int it = __builtin_amdgcn_readfirstlane(sh_item[phase]);
+      if (it >= n_push) break;
+      int s = 0;
+      while (s + 1 < a.n_shards && sh_base[s + 1] <= it) ++s;
+      s = __builtin_amdgcn_readfirstlane(s);
+      const int n_s = __builtin_amdgcn_readfirstlane(a.stream_len[s]);
+      const int e0 = (it - sh_base[s]) * kPushEntries;
+      combine_push(a, uniform_ptr(sh_stg[s]), s, e0 + wave * kPushPerWave, n_s, out_bytes, lane);
+    }
+  }
+  if (a.flags & kCommOnly) return;
+  __syncthreads();   // every wave has read the last push ticket before sh_item is reused
+
+  const int ntb = (a.T + kRedTokens - 1) / kRedTokens;
+  const int n_red = a.n_shards * ntb;
+  const bool wait = !(a.flags & kGemmOnly);
+  for (int phase = 0;; phase ^= 1) {
+    if (threadIdx.x == 0) {
+      int it = error_raised(a.err) ? -1 : fetch_add_relaxed(a.tick_cur + 64, 1);
+      if (it >= n_red) it = -1;
+      if (it >= 0 && wait) {
+        const int s = it / ntb, t0 = (it - s * ntb) * kRedTokens, t1 = min(t0 + kRedTokens, a.T);
+        const int* tf_s = a.tok_first + (size_t)s * (a.rs_cap + 1);
+        const int e_lo = min(max(tf_s[t0], 0), a.rs_cap), e_hi = min(max(tf_s[t1], 0), a.rs_cap);
+        uint32_t polls = 0;
+        const uint64_t deadline = now_ticks() + a.timeout_ticks;
+        for (int c = e_lo / kChunk; c * kChunk < e_hi; ++c)
+          if (!wait_ge(a.cslot + s * a.chunk_cap + c, a.seq, deadline, a.err, 0x70000000 | (s * a.chunk_cap + c),
+                       &polls)) {
+            it = -1;
+            break;
+          }
+        if (verify) atomicAdd(a.stats + ST_SLOT_POLLS, (unsigned long long)polls);
+      }
+      sh_item[phase] = it;
+    }
+    __syncthreads();
+    const int it = __builtin_amdgcn_readfirstlane(sh_item[phase]);
+    if (it < 0) break;
+    acquire_agent();
+    const int s = it / ntb, t0 = (it - s * ntb) * kRedTokens;
+    combine_reduce(a, uniform_ptr(sh_stg[s]), (uint16_t*)uniform_ptr(sh_y[s]), s, t0 + wave * kRedPerWave, lane);
+  }
+}
+
+}  // namespace fg

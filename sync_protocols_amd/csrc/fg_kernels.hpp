@@ -537,6 +537,8 @@ struct RouteArgs {
   int* gslab;                // first slab of each group
   int* wgcount;              // TOPK: [n_wg][E + 1] per-workgroup expert counts, picks
   int* wgbase;               // TOPK: [n_wg][E + 1] expert row bases, stream base
+  int* src_k;                // TOPK: [S][rs_cap] top-k position of each stream entry
+  int* tok_first;            // TOPK: [S][rs_cap + 1] first stream entry of each token; [T] = stream length
   int* ticket;               // [0] last-workgroup ticket, [1] failure flag (zero between calls)
   ErrorSink err;
 };
@@ -724,6 +726,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_count_kernel(RouteAr
       run += a.wgcount[v * (E + 1) + E];
     }
     a.stream_len[sh] = run;
+    a.tok_first[(size_t)sh * (a.rs_cap + 1) + T] = run;
     if (run > a.rs_cap) { raise_error(a.err, kErrProtocol, 0x40000000 | sh); atomicOr(a.ticket + 1, 1); }
   }
   __syncthreads();
@@ -790,20 +793,22 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_place_kernel(RouteAr
   int pick_base = x - picks;
   for (int v = 0; v < wave; ++v) pick_base += sh_pick[v];
   const int stream0 = a.wgbase[w * (E + 1) + E] + pick_base;
+  if (t < T) a.tok_first[(size_t)s * (a.rs_cap + 1) + t] = stream0;
   for (int e = 0; e < E; ++e) {
     const bool f = (mask >> e) & 1ull;
     const unsigned long long b = ballot(f);
     if (!f) continue;
     int rank = a.wgbase[w * (E + 1) + e] + __popcll(b & lt);
     for (int v = 0; v < wave; ++v) rank += sh_wave[e][v];
-    int j = 0;   // local picks ahead of expert e in this token's list
+    int j = 0, kk = 0;   // local picks ahead of expert e in this token's list; e's position in it
     for (int k = 0; k < KK; ++k) {
       const int ek = tk[k] - a.expert_base;
-      if (ek == e) break;
+      if (ek == e) { kk = k; break; }
       j += (ek >= 0 && ek < E);
     }
     const int i = stream0 + j;
     a.src_row[s * a.rs_cap + i] = t;
+    a.src_k[s * a.rs_cap + i] = kk;
     a.dst_row[s * a.rs_cap + i] = rank;
     a.inv[rank] = inv_pack(a.ver, (s << 24) | i);
   }

@@ -31,7 +31,7 @@ FAULT_DROP_PUBLISH = 1 << 10
 
 ROUTE_CONTIG, ROUTE_EXPLICIT, ROUTE_TOPK = 0, 1, 2
 
-EXPORTS = ("fg_init", "fg_gather_gemm", "fg_barrier", "fg_pingpong", "fg_stress", "fg_stats",
+EXPORTS = ("fg_init", "fg_gather_gemm", "fg_barrier", "fg_pingpong", "fg_stress", "fg_combine", "fg_stats",
            "fg_views", "fg_capacity", "fg_destroy", "fg_strerror")
 
 
@@ -41,7 +41,7 @@ class FgConfig(C.Structure):
                 ("n_gemm_wg", C.c_int32), ("tile_n", C.c_int32), ("timeout_ns", C.c_int64),
                 ("stress_producers", C.c_int32), ("stress_consumers", C.c_int32),
                 ("stress_max_chunks", C.c_int32), ("split_parts", C.c_int32), ("split_tiles", C.c_int32),
-                ("tile_order", C.c_int32), ("copy_rows", C.c_int32), ("reserved", C.c_int32)]
+                ("tile_order", C.c_int32), ("copy_rows", C.c_int32), ("combine_wg", C.c_int32)]
 
 
 class FgRoute(C.Structure):
@@ -61,7 +61,7 @@ class FgStats(C.Structure):
                 ("t_barrier_us", C.c_double), ("t_rtt_us", C.c_double),
                 ("n_comm_wg", C.c_int32), ("n_gemm_wg", C.c_int32), ("cu_count", C.c_int32),
                 ("m_pad_cap", C.c_int32), ("tiles_whole", C.c_int32), ("tiles_split", C.c_int32),
-                ("split_parts", C.c_int32), ("reserved", C.c_int32), ("clock_mhz", C.c_double)]
+                ("split_parts", C.c_int32), ("combine_seq", C.c_int32), ("clock_mhz", C.c_double)]
 
 
 class FgViews(C.Structure):
@@ -71,7 +71,8 @@ class FgViews(C.Structure):
         ("chunk_cap", C.c_int32), ("rb_cap", C.c_int32), ("m_pad_cap", C.c_int32), ("route_ver", C.c_uint32),
         ("wg_time", C.c_void_p), ("trace", C.c_void_p), ("rb_time", C.c_void_p), ("grid", C.c_int32),
         ("trace_cap", C.c_int32), ("wall_khz", C.c_int64), ("desc", C.c_void_p), ("slab", C.c_void_p),
-        ("group_slab", C.c_void_p)]
+        ("group_slab", C.c_void_p), ("combine_slot", C.c_void_p), ("combine_elect", C.c_void_p),
+        ("combine_pub", C.c_void_p), ("src_k", C.c_void_p), ("tok_first", C.c_void_p)]
 
 
 class FgError(RuntimeError):
@@ -97,6 +98,7 @@ def load_library() -> C.CDLL:
     lib.fg_barrier.argtypes = [vp, C.c_int32, vp]
     lib.fg_pingpong.argtypes = [vp, C.c_int32, C.c_int32, vp]
     lib.fg_stress.argtypes = [vp, vp, vp, vp, C.c_uint32, vp]
+    lib.fg_combine.argtypes = [vp, vp, vp, C.POINTER(vp), C.POINTER(vp), C.c_uint32, vp]
     lib.fg_stats.argtypes = [vp, C.POINTER(FgStats), C.c_int]
     lib.fg_views.argtypes = [vp, C.POINTER(FgViews)]
     lib.fg_capacity.argtypes = [C.POINTER(FgConfig), C.POINTER(C.c_int32)]
@@ -132,9 +134,9 @@ def _ptr(t: torch.Tensor) -> C.c_void_p:
 
 def make_config(n_shards, max_rows_per_shard, K, N, n_groups=1, n_comm_wg=0, n_gemm_wg=0, tile_n=0,
                 timeout_ns=0, stress=(0, 0, 0), split_parts=0, split_tiles=0, tile_order=0,
-                copy_rows=0) -> FgConfig:
+                copy_rows=0, combine_wg=0) -> FgConfig:
     return FgConfig(n_shards, max_rows_per_shard, K, N, n_groups, n_comm_wg, n_gemm_wg, tile_n, timeout_ns,
-                    stress[0], stress[1], stress[2], split_parts, split_tiles, tile_order, copy_rows, 0)
+                    stress[0], stress[1], stress[2], split_parts, split_tiles, tile_order, copy_rows, combine_wg)
 
 
 def capacity(cfg: FgConfig) -> int:
@@ -185,6 +187,14 @@ class Context:
     def stress(self, chunk_rows, delays_ns, payload, flags: int = 0, stream=None) -> int:
         return self._lib.fg_stress(self._h, _ptr(chunk_rows), _ptr(delays_ns), _ptr(payload), flags,
                                    _stream_ptr(stream))
+
+    def combine(self, out, weights, staging, y, flags: int = 0, stream=None) -> int:
+        """fg_combine on the TOPK route of the last gather_gemm; staging and y are
+        lists of per-shard device tensors. Returns the fg_status code."""
+        st = (C.c_void_p * len(staging))(*[t.data_ptr() for t in staging])
+        ys = (C.c_void_p * len(y))(*[t.data_ptr() for t in y])
+        self._keep_c = [st, ys]
+        return self._lib.fg_combine(self._h, _ptr(out), _ptr(weights), st, ys, flags, _stream_ptr(stream))
 
     def stats(self, wait: bool = True) -> FgStats:
         st = FgStats()

@@ -92,6 +92,18 @@ def ep_inputs(seed: int, n_shards: int = 8, tokens: int = 1024, K: int = 7168,
     return EPInputs(shards, topk_t, w, expert_base, n_local, sigma_x, sigma_w)
 
 
+def combine_inputs(seed: int, rows: int, N: int, n_shards: int, tokens: int, topk: int,
+                   sigma: float = 1.0):
+    """Inputs of the combine step: expert outputs bf16 [rows, N] ~N(0, sigma) in
+    gathered-row order, and gate weights fp32 [n_shards, tokens, topk] drawn
+    U(0, 1) and normalised to sum 1 over each token's top-k list."""
+    g = _gen(seed)
+    out = _normal_bf16(g, (rows, N), sigma)
+    u = torch.rand(n_shards, tokens, topk, generator=g, dtype=torch.float32)
+    w = (u / u.sum(dim=-1, keepdim=True)).contiguous()
+    return out, w
+
+
 def stress_inputs(seed: int, producers: int = 64, consumers: int = 64,
                   max_chunks: int = 4, signals: int = 10000, iters: int = 50,
                   max_delay_ns: int = 20000) -> StressInputs:
