@@ -198,6 +198,77 @@ def cpu_baseline(wl, budget_s=12.0):
                        f"{what} x K={K} x N={N}) in {dt:.1f} s; value = contraction FLOP / wall time")
 
 
+def combine_bench(args, wl, ctx, gathered, out, torch, fg, W):
+    """The combine step on the EP workload (8 x 1024 tokens, top-8 of 64 experts,
+    8 local, N = 2048): T_total (push + weighted sums in one kernel), push alone,
+    sums alone (each the mean of back-to-back calls between one event pair),
+    overlap, and the HBM rate over the algorithmic bytes
+    3 * M * N * 2 (expert rows read, staging written, staging read) +
+    S * T * N * 2 (outputs written) + M * 4 (gate weights)."""
+    if wl["name"] != "ep":
+        wl = setup_workload("ep", torch, fg, W)
+        cfg = fg.make_config(wl["S"], wl["max_rows"], wl["K"], wl["N"], n_groups=wl["n_groups"])
+        ctx = fg.Context(cfg)
+        cap = fg.capacity(cfg)
+        gathered = torch.zeros(cap, wl["K"], dtype=torch.bfloat16, device="cuda:0")
+        out = torch.zeros(cap, wl["N"], dtype=torch.bfloat16, device="cuda:0")
+        own = True
+    else:
+        own = False
+    c = wl["cfg"]
+    S, T, KK, N = wl["S"], c["tokens"], c["topk"], wl["N"]
+    rc = ctx.gather_gemm(wl["shards"], wl["w"], gathered, out, route=wl["route"])
+    if rc != fg.OK:
+        raise RuntimeError(f"fg_gather_gemm: {fg.strerror(rc)}")
+    _, weights = W.combine_inputs(c["seed"] + 1, 1, N, S, T, KK)
+    weights = weights.to("cuda:0")
+    staging = [torch.empty(ctx.cfg.max_rows_per_shard, N, dtype=torch.bfloat16, device="cuda:0") for _ in range(S)]
+    ys = [torch.empty(T, N, dtype=torch.bfloat16, device="cuda:0") for _ in range(S)]
+
+    def comb(flags=0):
+        r = ctx.combine(out, weights, staging, ys, flags=flags)
+        if r != fg.OK:
+            raise RuntimeError(f"fg_combine: {fg.strerror(r)}")
+
+    def back_to_back(flags, n):
+        """Mean device time (us) of n back-to-back calls between one event pair."""
+        comb(flags)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            comb(flags)
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / n
+
+    for _ in range(5):
+        comb()
+    torch.cuda.synchronize()
+    n_rep = max(50, args.steps)
+    Tt = back_to_back(0, n_rep)
+    Tp = back_to_back(fg.CALL_COMM_ONLY, n_rep)
+    Ts = back_to_back(fg.CALL_GEMM_ONLY, n_rep)
+    t_single = _events_time(comb, 20, torch)
+    st = ctx.stats()
+    if st.error_code:
+        raise RuntimeError(f"device error {st.error_code} id {st.error_id}")
+    M = wl["m_real"]
+    alg = 3.0 * M * N * 2 + float(S) * T * N * 2 + M * 4.0
+    if own:
+        ctx.close()
+    gbs = alg / (Tt * 1e-6) / 1e9
+    return {"workload": "ep", "M": M, "tokens": S * T, "N": N, "kernel": "combine_kernel",
+            "T_total_us": round(Tt, 2),
+            "T_single_call_incl_launch_us": round(statistics.median(t_single) * 1000, 2),
+            "T_push_alone_us": round(Tp, 2), "T_sums_alone_us": round(Ts, 2),
+            "overlap_efficiency": round((Tp + Ts - Tt) / min(Tp, Ts), 4),
+            "algorithmic_bytes_per_launch": alg,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -350,6 +421,7 @@ def main():
                             "us_per_iter_no_delay": round(statistics.median(t_nodelay) * 1000, 2),
                             "us_per_iter_delays_0_20us": round(statistics.median(t_delay) * 1000, 2),
                             "signals_per_s_no_delay": round(signals / (statistics.median(t_nodelay) * 1e-3), 0)}
+        result["combine"] = combine_bench(args, wl, ctx, gathered, out, torch, fg, W)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0").fill_(1)
         dst = torch.empty_like(src)

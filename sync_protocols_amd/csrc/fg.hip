@@ -61,10 +61,9 @@ struct Plane {
   int* s_pub;
   int* src_k;      // [S][rs_cap] TOPK: top-k position of each stream entry
   int* tok_first;  // [S][rs_cap + 1] TOPK: first stream entry of each token
-  int* cslot;      // combine plane: slots, election counts x2, publisher counts, tickets x2
+  int* cslot;      // combine plane: slots, election counts x2, publisher counts
   int* celect;
   int* cpub;
-  int* ctick;
 };
 
 }  // namespace
@@ -84,6 +83,7 @@ struct fg_ctx {
   int* host_status = nullptr;
   int seq = 0, bseq = 0, sseq = 0, ppseq = 0, cseq = 0;
   int topk_rows = 0, topk_k = 0;   // tokens per shard and k of the last TOPK route
+  int combine_wg = 0;
   uint32_t route_ver = 0;
   int route_wg_cap = 0;
   fg_status sticky = FG_OK;
@@ -286,6 +286,17 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
     if (e != hipSuccess) { delete ctx; return FG_EHIP; }
     if ((long long)worst * ctx->cu_count < ctx->n_comm + ctx->n_gemm) { delete ctx; return FG_ERESIDENCY; }
   }
+  // combine kernel: its waves wait on pushes done by other waves, so the whole
+  // grid must be resident (same audit)
+  ctx->combine_wg = cfg->combine_wg ? cfg->combine_wg : 2 * ctx->cu_count;
+  {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, combine_kernel, kCombThreads, 0) != hipSuccess) {
+      delete ctx;
+      return FG_EHIP;
+    }
+    if ((long long)per_cu * ctx->cu_count < ctx->combine_wg) { delete ctx; return FG_ERESIDENCY; }
+  }
   if (cfg->stress_producers + cfg->stress_consumers > ctx->cu_count ||
       cfg->stress_consumers >= ctx->cu_count) { delete ctx; return FG_ERESIDENCY; }
   if (cfg->n_shards > ctx->cu_count) { delete ctx; return FG_ERESIDENCY; }
@@ -326,7 +337,7 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
                o_sslot = take((size_t)ctx->s_slots * 4), o_select = take(2 * (size_t)ctx->s_slots * 4),
                o_spub = take((size_t)ctx->s_slots * 4), o_srck = take(nrs * 4),
                o_tokf = take((size_t)S * (cfg->max_rows_per_shard + 1) * 4), o_cslot = take(nch * 4),
-               o_celect = take(2 * nch * 4), o_cpub = take(nch * 4), o_ctick = take(2 * kCombTickInts * 4);
+               o_celect = take(2 * nch * 4), o_cpub = take(nch * 4);
   if (hipMalloc(&ctx->plane_mem, off) != hipSuccess) { delete ctx; return FG_ENOMEM; }
   if (hipMemset(ctx->plane_mem, 0, off) != hipSuccess) { (void)hipFree(ctx->plane_mem); delete ctx; return FG_EHIP; }
   char* b = ctx->plane_mem;
@@ -343,7 +354,7 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
   p.wgtime = (long long*)(b + o_wg); p.s_slot = (int*)(b + o_sslot); p.s_elect = (int*)(b + o_select);
   p.s_pub = (int*)(b + o_spub);
   p.src_k = (int*)(b + o_srck); p.tok_first = (int*)(b + o_tokf); p.cslot = (int*)(b + o_cslot);
-  p.celect = (int*)(b + o_celect); p.cpub = (int*)(b + o_cpub); p.ctick = (int*)(b + o_ctick);
+  p.celect = (int*)(b + o_celect); p.cpub = (int*)(b + o_cpub);
   if (hipHostMalloc((void**)&ctx->host_status, 64, hipHostMallocCoherent) != hipSuccess) {
     (void)hipFree(ctx->plane_mem); delete ctx; return FG_ENOMEM;
   }
@@ -558,10 +569,9 @@ fg_status fg_combine(fg_ctx* ctx, const void* out, const float* weights, void* c
   a.desc = ctx->p.desc; a.stream_len = ctx->p.stream_len; a.dst_row = ctx->p.dst_row; a.src_k = ctx->p.src_k;
   a.tok_first = ctx->p.tok_first;
   a.cslot = ctx->p.cslot; a.celect_cur = ctx->p.celect + cur * nch; a.celect_nxt = ctx->p.celect + nxt * nch;
-  a.cpub = ctx->p.cpub; a.tick_cur = ctx->p.ctick + cur * kCombTickInts; a.tick_nxt = ctx->p.ctick + nxt * kCombTickInts;
+  a.cpub = ctx->p.cpub;
   a.stats = ctx->p.stats; a.err = sink(ctx); a.seq = ctx->cseq; a.flags = flags; a.timeout_ticks = timeout_ticks(ctx);
-  const int grid = c.combine_wg ? c.combine_wg : 2 * ctx->cu_count;
-  hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(kCombThreads), 0, stream, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(ctx->combine_wg), dim3(kCombThreads), 0, stream, a);
   HIPCHK(hipGetLastError());
   return FG_OK;
 }

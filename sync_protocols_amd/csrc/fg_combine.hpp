@@ -8,19 +8,20 @@
 // staging buffer per source shard, indexed by that shard's stream entries; the
 // shard's side then forms, per token, the gate-weighted sum of its local picks.
 //
-// One kernel, two phases taken from ticket counters:
-//  * push items (16 stream entries of one shard, 4 per wave): copy
+// One kernel, two phases; every wave takes items i, i + waves, ... of each:
+//  * push items (4 stream entries of one shard per wave): copy
 //    out[dst_row[s][i]] -> staging[s][i] bitwise with device-coherent stores,
 //    release, add the wave's rows to the chunk's election count; the add that
 //    completes the chunk elects the wave, whose leader stores seq in the slot;
-//  * reduce items (16 tokens of one shard, 4 per wave): wait until the slot of
+//  * reduce items (4 tokens of one shard per wave): wait until the slot of
 //    every chunk holding the tokens' entries carries seq, acquire, and write
 //    y[s][t] = bf16(sum over the token's entries e, in k order, of
 //    w[s][t][k(e)] * staging[s][e]) with fp32 products and sums.
-// A workgroup takes reduce items only after the push queue is exhausted, so
-// every push item is held by a running workgroup that never waits: no
-// residency assumption is needed for freedom from deadlock ("PCIe sync
-// protocols" §6: every wait has a supplier that does not wait).
+// A wave starts its reduce items only after its push items, and the host
+// checks that the whole grid is co-resident, so every wait has a running
+// supplier that does not wait ("PCIe sync protocols" §6 audit). Static item
+// assignment keeps atomics off the item hand-out: one ticket counter shared by
+// every workgroup serialises at its memory channel.
 #pragma once
 
 #include "fg_kernels.hpp"
@@ -29,15 +30,22 @@ namespace fg {
 
 constexpr int kCombWaves = 4;
 constexpr int kCombThreads = 64 * kCombWaves;
-constexpr int kPushEntries = 16;                          // stream entries per push item
-constexpr int kPushPerWave = kPushEntries / kCombWaves;
-constexpr int kRedTokens = 16;                            // tokens per reduce item
-constexpr int kRedPerWave = kRedTokens / kCombWaves;
-constexpr int kCombU = 2;                                 // 16-byte vectors per lane and row per column step
-constexpr int kCombTickInts = 128;                        // [0] push ticket, [64] reduce ticket
+// Build-time shape of the work items (defaults measured fastest on the EP workload).
+#ifndef FG_COMB_PUSH
+#define FG_COMB_PUSH 4
+#endif
+#ifndef FG_COMB_TOKENS
+#define FG_COMB_TOKENS 4
+#endif
+#ifndef FG_COMB_U
+#define FG_COMB_U 4
+#endif
+constexpr int kPushPerWave = FG_COMB_PUSH;                // stream entries per push item (one wave)
+constexpr int kRedPerWave = FG_COMB_TOKENS;               // tokens per reduce item (one wave)
+constexpr int kCombU = FG_COMB_U;                         // 16-byte vectors per lane and row per column step
 
-static_assert(kChunk % kPushEntries == 0, "a push item lies inside one chunk");
-static_assert(kPushPerWave <= 64 && kRedPerWave * 16 <= 64, "lane layout");
+static_assert(kChunk % kPushPerWave == 0, "a push item lies inside one chunk");
+static_assert(kPushPerWave <= 64 && kRedPerWave * 16 <= 64 && kRedPerWave < 64, "lane layout");
 
 struct CombineArgs {
   const uint16_t* out;            // [m_pad][N] expert outputs, gathered-row order
@@ -54,8 +62,6 @@ struct CombineArgs {
   int* celect_cur;                // [S][chunk_cap]
   int* celect_nxt;
   int* cpub;
-  int* tick_cur;                  // [kCombTickInts]
-  int* tick_nxt;
   unsigned long long* stats;
   ErrorSink err;
   int seq;
@@ -130,35 +136,42 @@ __device__ __forceinline__ void bf16x8_fma(float* acc, v4i x, float w) {
   }
 }
 
-// One wave: tokens tb .. tb + kRedPerWave - 1 of shard s (entries already acquired).
-__device__ __forceinline__ void combine_reduce(const CombineArgs& a, const uint16_t* stg, uint16_t* yb, int s, int tb,
-                                               int lane) {
-  const uint32_t row_bytes = (uint32_t)a.N * 2;
-  const int* tf_s = a.tok_first + (size_t)s * (a.rs_cap + 1);
+// First stream entry of tokens tb .. tb + kRedPerWave of shard s, in lanes
+// 0 .. kRedPerWave. The tables come from the layout step; clamping keeps every
+// access inside the buffers even if a failed layout left them stale (it also
+// raised an error).
+__device__ __forceinline__ int reduce_first_entries(const CombineArgs& a, int s, int tb, int lane) {
   int tf = 0;
-  if (lane <= kRedPerWave) tf = tf_s[min(tb + lane, a.T)];
+  if (lane <= kRedPerWave) tf = a.tok_first[(size_t)s * (a.rs_cap + 1) + min(tb + lane, a.T)];
+  return tf;
+}
+
+// Gate weight of entry j of token r in lane 16 r + j (j < 16); entries 16.. of
+// a token (more than 16 local picks) load their weight when used.
+__device__ __forceinline__ float reduce_weights(const CombineArgs& a, int s, int tb, int tf, int lane) {
+  const int r = lane >> 4, j = lane & 15;
+  const int my_ea = __shfl(tf, r, 64);
+  const int my_ne = (r < kRedPerWave && tb + r < a.T) ? __shfl(tf, r + 1, 64) - my_ea : 0;
+  float wl = 0.f;
+  if (j < my_ne) {
+    const int k = min(max(a.src_k[s * a.rs_cap + my_ea + j], 0), a.KK - 1);
+    wl = a.weights[((size_t)s * a.T + tb + r) * a.KK + k];
+  }
+  return wl;
+}
+
+// One wave: y rows of tokens tb .. tb + kRedPerWave - 1 of shard s from the
+// (acquired) staging rows; tf and wl from the two functions above.
+__device__ __forceinline__ void combine_reduce(const CombineArgs& a, const uint16_t* stg, uint16_t* yb, int s, int tb,
+                                               int tf, float wl, int lane) {
+  const uint32_t row_bytes = (uint32_t)a.N * 2;
   int ea[kRedPerWave], ne[kRedPerWave];
   int maxn = 0;
-  // the tables come from the layout step; clamping keeps every access inside
-  // the buffers even if a failed layout left them stale (it also raised an error)
-  tf = min(max(tf, 0), a.rs_cap);
 #pragma unroll
   for (int r = 0; r < kRedPerWave; ++r) {
     ea[r] = readlane(tf, r);
     ne[r] = tb + r < a.T ? max(0, readlane(tf, r + 1) - ea[r]) : 0;
     maxn = max(maxn, ne[r]);
-  }
-  // gate weight of entry j of token r in lane 16 r + j (j < 16); entries 16..
-  // of a token (more than 16 local picks) load their weight when used
-  float wl = 0.f;
-  {
-    const int r = lane >> 4, j = lane & 15;
-    const int my_ea = __shfl(tf, r, 64);
-    const int my_ne = tb + r < a.T ? __shfl(tf, r + 1, 64) - my_ea : 0;
-    if (j < my_ne) {
-      const int k = min(max(a.src_k[s * a.rs_cap + my_ea + j], 0), a.KK - 1);
-      wl = a.weights[((size_t)s * a.T + tb + r) * a.KK + k];
-    }
   }
   const int nvec = a.N / 8;
   for (int c0 = 0; c0 < nvec; c0 += 64 * kCombU) {
@@ -213,14 +226,12 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
   __shared__ const uint16_t* sh_stg[FG_MAX_SHARDS];
   __shared__ uint16_t* sh_y[FG_MAX_SHARDS];
   __shared__ int sh_base[FG_MAX_SHARDS + 1];     // push items before shard s
-  __shared__ int sh_item[2];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x;
   // arm the other parity for the next call (nothing else touches it here)
   for (int i = blockIdx.x * kCombThreads + threadIdx.x; i < a.n_shards * a.chunk_cap; i += G * kCombThreads)
     a.celect_nxt[i] = 0;
-  if (blockIdx.x == 0 && threadIdx.x < 2) a.tick_nxt[threadIdx.x * 64] = 0;
   if ((int)threadIdx.x < a.n_shards) {
     sh_stg[threadIdx.x] = a.staging[threadIdx.x];
     sh_y[threadIdx.x] = a.y[threadIdx.x];
@@ -229,62 +240,57 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
     int n = 0;
     for (int s = 0; s < a.n_shards; ++s) {
       sh_base[s] = n;
-      n += (a.stream_len[s] + kPushEntries - 1) / kPushEntries;
+      n += (a.stream_len[s] + kPushPerWave - 1) / kPushPerWave;
     }
     sh_base[a.n_shards] = n;
   }
   __syncthreads();
+  if (error_raised(a.err)) return;
   const int m_pad = __builtin_amdgcn_readfirstlane(a.desc[0]);
   const uint32_t out_bytes = (uint32_t)m_pad * (uint32_t)a.N * 2;
   const int n_push = sh_base[a.n_shards];
-  const bool verify = a.flags & kVerify;
+  const int nw = G * kCombWaves, wid = blockIdx.x * kCombWaves + wave;
+  const int ntb = (a.T + kRedPerWave - 1) / kRedPerWave;
+  const int n_red = a.n_shards * ntb;
+  // the route tables are ready before the kernel starts: the first entries of
+  // this wave's first reduce item load while the push phase runs
+  int tf_next = 0;
+  if (wid < n_red) tf_next = reduce_first_entries(a, wid / ntb, (wid % ntb) * kRedPerWave, lane);
 
   if (!(a.flags & kGemmOnly)) {
-    for (int phase = 0;; phase ^= 1) {
-      if (threadIdx.x == 0) sh_item[phase] = error_raised(a.err) ? n_push : fetch_add_relaxed(a.tick_cur, 1);
-      __syncthreads();
-      const int it = __builtin_amdgcn_readfirstlane(sh_item[phase]);
-      if (it >= n_push) break;
+    for (int it = wid; it < n_push; it += nw) {
       int s = 0;
       while (s + 1 < a.n_shards && sh_base[s + 1] <= it) ++s;
       s = __builtin_amdgcn_readfirstlane(s);
       const int n_s = __builtin_amdgcn_readfirstlane(a.stream_len[s]);
-      const int e0 = (it - sh_base[s]) * kPushEntries;
-      combine_push(a, uniform_ptr(sh_stg[s]), s, e0 + wave * kPushPerWave, n_s, out_bytes, lane);
+      combine_push(a, uniform_ptr(sh_stg[s]), s, (it - sh_base[s]) * kPushPerWave, n_s, out_bytes, lane);
     }
   }
   if (a.flags & kCommOnly) return;
-  __syncthreads();   // every wave has read the last push ticket before sh_item is reused
 
-  const int ntb = (a.T + kRedTokens - 1) / kRedTokens;
-  const int n_red = a.n_shards * ntb;
   const bool wait = !(a.flags & kGemmOnly);
-  for (int phase = 0;; phase ^= 1) {
-    if (threadIdx.x == 0) {
-      int it = error_raised(a.err) ? -1 : fetch_add_relaxed(a.tick_cur + 64, 1);
-      if (it >= n_red) it = -1;
-      if (it >= 0 && wait) {
-        const int s = it / ntb, t0 = (it - s * ntb) * kRedTokens, t1 = min(t0 + kRedTokens, a.T);
-        const int* tf_s = a.tok_first + (size_t)s * (a.rs_cap + 1);
-        const int e_lo = min(max(tf_s[t0], 0), a.rs_cap), e_hi = min(max(tf_s[t1], 0), a.rs_cap);
+  const bool verify = a.flags & kVerify;
+  for (int it = wid; it < n_red; it += nw) {
+    const int s = it / ntb, tb = (it - s * ntb) * kRedPerWave;
+    const int tf = min(max(tf_next, 0), a.rs_cap);
+    // gate weights first: their loads run while the slots are polled
+    const float wl = reduce_weights(a, s, tb, tf, lane);
+    if (it + nw < n_red) tf_next = reduce_first_entries(a, (it + nw) / ntb, ((it + nw) % ntb) * kRedPerWave, lane);
+    if (wait) {
+      int ok = 1;
+      const int e_lo = readlane(tf, 0), e_hi = readlane(tf, min(kRedPerWave, a.T - tb));
+      if (lane == 0) {
         uint32_t polls = 0;
         const uint64_t deadline = now_ticks() + a.timeout_ticks;
-        for (int c = e_lo / kChunk; c * kChunk < e_hi; ++c)
-          if (!wait_ge(a.cslot + s * a.chunk_cap + c, a.seq, deadline, a.err, 0x70000000 | (s * a.chunk_cap + c),
-                       &polls)) {
-            it = -1;
-            break;
-          }
+        for (int c = e_lo / kChunk; c * kChunk < e_hi && ok; ++c)
+          ok = wait_ge(a.cslot + s * a.chunk_cap + c, a.seq, deadline, a.err, 0x70000000 | (s * a.chunk_cap + c),
+                       &polls);
         if (verify) atomicAdd(a.stats + ST_SLOT_POLLS, (unsigned long long)polls);
       }
-      sh_item[phase] = it;
+      if (!readlane(ok, 0)) break;
+      acquire_agent();
     }
-    __syncthreads();
-    const int it = __builtin_amdgcn_readfirstlane(sh_item[phase]);
-    if (it < 0) break;
-    acquire_agent();
-    const int s = it / ntb, t0 = (it - s * ntb) * kRedTokens;
-    combine_reduce(a, uniform_ptr(sh_stg[s]), (uint16_t*)uniform_ptr(sh_y[s]), s, t0 + wave * kRedPerWave, lane);
+    combine_reduce(a, uniform_ptr(sh_stg[s]), (uint16_t*)uniform_ptr(sh_y[s]), s, tb, tf, wl, lane);
   }
 }
 

@@ -672,27 +672,48 @@ __global__ __launch_bounds__(kRouteThreads) void route_explicit_kernel(RouteArgs
   if (threadIdx.x == 0) { a.ticket[0] = 0; a.ticket[1] = 0; }
 }
 
-// TOPK, pass 1: per workgroup (a range of 256 tokens of one shard) the number
-// of tokens choosing each local expert and the number of local pairs; the last
-// workgroup scans them in global token order into expert row bases and stream
-// bases ("DeepEP FIFO pipeline" dispatch notify stage: counts fix the offsets),
-// the group offsets (each expert padded to a multiple of 128 rows) and seeds.
+// TOPK layout, both passes: each workgroup takes 256 consecutive tokens of one
+// shard and first copies their top-k lists into LDS, one byte per choice: the
+// local expert index, or 0xFF for an expert this GPU does not own.
+constexpr int kRouteTileInts = 4096;   // per-workgroup counts staged through LDS by the last workgroup
+
+__device__ __forceinline__ int stage_topk(const RouteArgs& a, uint8_t* sh_tk, int s, int t0) {
+  const int E = a.n_groups, KK = a.topk_k, T = a.rows_per_shard;
+  const int ntok = min(kRouteThreads, T - t0);
+  const int* src = a.topk + ((size_t)s * T + t0) * KK;
+  for (int i = threadIdx.x; i < ntok * KK; i += blockDim.x) {
+    const int e = src[i] - a.expert_base;
+    sh_tk[i] = (e >= 0 && e < E) ? (uint8_t)e : (uint8_t)0xFF;
+  }
+  return ntok;
+}
+
+// TOPK, pass 1: per workgroup the number of its tokens choosing each local
+// expert and its number of local pairs; the last workgroup scans them in
+// global token order (workgroup order) into relative expert row bases and
+// per-shard stream bases ("DeepEP FIFO pipeline" dispatch notify stage: counts
+// fix the offsets), then the group offsets (each expert padded to a multiple of
+// 128 rows) and seeds. The counts pass through LDS in tiles, so the scan runs
+// on LDS reads, not on a chain of global loads.
 __global__ __launch_bounds__(kRouteThreads) void route_topk_count_kernel(RouteArgs a) {
+  __shared__ uint8_t sh_tk[kRouteThreads * 64];
   __shared__ int sh_cnt[FG_MAX_GROUPS + 1];
   __shared__ int sh_last;
   __shared__ int sh_goff[FG_MAX_GROUPS + 1];
   __shared__ int sh_ne[FG_MAX_GROUPS];
+  __shared__ int sh_tile[kRouteTileInts];
   const int E = a.n_groups, KK = a.topk_k, T = a.rows_per_shard;
-  const int w = blockIdx.x, s = w / a.wpb, t = (w - s * a.wpb) * kRouteThreads + threadIdx.x;
+  const int w = blockIdx.x, s = w / a.wpb, t0 = (w - s * a.wpb) * kRouteThreads, t = t0 + threadIdx.x;
   for (int e = threadIdx.x; e <= E; e += blockDim.x) sh_cnt[e] = 0;
+  stage_topk(a, sh_tk, s, t0);
   __syncthreads();
   if (t < T) {
-    const int* tk = a.topk + ((size_t)s * T + t) * KK;
+    const uint8_t* tk = sh_tk + threadIdx.x * KK;
     unsigned long long mask = 0;
     int picks = 0;
     for (int k = 0; k < KK; ++k) {
-      const int e = tk[k] - a.expert_base;
-      if (e < 0 || e >= E) continue;
+      const int e = tk[k];
+      if (e == 0xFF) continue;
       if ((mask >> e) & 1ull) {   // one token routed twice to one expert: not a valid top-k
         raise_error(a.err, kErrProtocol, 0x48000000 | s);
         atomicOr(a.ticket + 1, 1);
@@ -708,26 +729,37 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_count_kernel(RouteAr
   for (int e = threadIdx.x; e <= E; e += blockDim.x) a.wgcount[w * (E + 1) + e] = sh_cnt[e];
   if (!last_workgroup(a.ticket, &sh_last)) return;
   const int n_wg = gridDim.x;
-  // expert e: running row base in global token order (workgroup order)
-  if ((int)threadIdx.x < E) {
-    const int e = threadIdx.x;
-    int run = 0;
-    for (int v = 0; v < n_wg; ++v) {
-      a.wgbase[v * (E + 1) + e] = run;          // relative to the expert's offset, fixed below
-      run += a.wgcount[v * (E + 1) + e];
+  // column e < E: running row base of expert e in workgroup order (relative to
+  // the expert's group offset); column E: running stream base inside a shard
+  const int rows_per_tile = kRouteTileInts / (E + 1);
+  int run = 0;
+  for (int v0 = 0; v0 < n_wg; v0 += rows_per_tile) {
+    const int nrows = min(rows_per_tile, n_wg - v0);
+    for (int i = threadIdx.x; i < nrows * (E + 1); i += blockDim.x) sh_tile[i] = a.wgcount[v0 * (E + 1) + i];
+    __syncthreads();
+    if ((int)threadIdx.x <= E) {
+      const int e = threadIdx.x;
+      for (int r = 0; r < nrows; ++r) {
+        const int v = v0 + r;
+        if (e == E && v % a.wpb == 0 && v > 0) {   // a new shard starts: close the previous one
+          const int sp = v / a.wpb - 1;
+          a.stream_len[sp] = run;
+          a.tok_first[(size_t)sp * (a.rs_cap + 1) + T] = run;
+          if (run > a.rs_cap) { raise_error(a.err, kErrProtocol, 0x40000000 | sp); atomicOr(a.ticket + 1, 1); }
+          run = 0;
+        }
+        a.wgbase[v * (E + 1) + e] = run;
+        run += sh_tile[r * (E + 1) + e];
+      }
     }
-    sh_ne[e] = run;
+    __syncthreads();
   }
-  if ((int)threadIdx.x < a.n_shards) {
-    const int sh = threadIdx.x;
-    int run = 0;
-    for (int v = sh * a.wpb; v < (sh + 1) * a.wpb; ++v) {
-      a.wgbase[v * (E + 1) + E] = run;
-      run += a.wgcount[v * (E + 1) + E];
-    }
-    a.stream_len[sh] = run;
-    a.tok_first[(size_t)sh * (a.rs_cap + 1) + T] = run;
-    if (run > a.rs_cap) { raise_error(a.err, kErrProtocol, 0x40000000 | sh); atomicOr(a.ticket + 1, 1); }
+  if ((int)threadIdx.x < E) sh_ne[threadIdx.x] = run;
+  if ((int)threadIdx.x == E) {
+    const int sp = a.n_shards - 1;
+    a.stream_len[sp] = run;
+    a.tok_first[(size_t)sp * (a.rs_cap + 1) + T] = run;
+    if (run > a.rs_cap) { raise_error(a.err, kErrProtocol, 0x40000000 | sp); atomicOr(a.ticket + 1, 1); }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -740,10 +772,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_count_kernel(RouteAr
     if (off > a.m_pad_cap) { raise_error(a.err, kErrProtocol, 0x50000000); atomicOr(a.ticket + 1, 1); }
   }
   __syncthreads();
-  for (int f = threadIdx.x; f < n_wg * E; f += blockDim.x) {
-    const int v = f / E, e = f - v * E;
-    a.wgbase[v * (E + 1) + e] += sh_goff[e];
-  }
   const int fail = __hip_atomic_load(a.ticket + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   route_finish(a, fail ? 0 : sh_goff[E], sh_goff, E, [&](int rb) {
     int real = 0;
@@ -758,25 +786,32 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_count_kernel(RouteAr
 // TOPK, pass 2: place every local pair. Inside a workgroup the rank of a token
 // among those choosing expert e comes from wave ballots (tokens are in thread
 // order, i.e. global token order); the stream index from a scan of the local
-// pick counts.
+// pick counts; the bases of pass 1 and the group offsets are read once.
 __global__ __launch_bounds__(kRouteThreads) void route_topk_place_kernel(RouteArgs a) {
+  __shared__ uint8_t sh_tk[kRouteThreads * 64];
   __shared__ int sh_wave[FG_MAX_GROUPS + 1][kRouteThreads / 64];
+  __shared__ int sh_pick[kRouteThreads / 64];
+  __shared__ int sh_base[FG_MAX_GROUPS + 1];
   const int E = a.n_groups, KK = a.topk_k, T = a.rows_per_shard;
-  const int w = blockIdx.x, s = w / a.wpb, t = (w - s * a.wpb) * kRouteThreads + threadIdx.x;
+  const int w = blockIdx.x, s = w / a.wpb, t0 = (w - s * a.wpb) * kRouteThreads, t = t0 + threadIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (__hip_atomic_load(a.ticket + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;  // layout failed
+  stage_topk(a, sh_tk, s, t0);
+  // absolute row base of each expert for this workgroup, stream base in [E]
+  if ((int)threadIdx.x <= E)
+    sh_base[threadIdx.x] = a.wgbase[w * (E + 1) + threadIdx.x] + ((int)threadIdx.x < E ? a.group_off_out[threadIdx.x] : 0);
+  __syncthreads();
+  const uint8_t* tk = sh_tk + threadIdx.x * KK;
   unsigned long long mask = 0;
-  const int* tk = a.topk + ((size_t)s * T + min(t, T - 1)) * KK;
   if (t < T)
     for (int k = 0; k < KK; ++k) {
-      const int e = tk[k] - a.expert_base;
-      if (e >= 0 && e < E) mask |= 1ull << e;
+      const int e = tk[k];
+      if (e != 0xFF) mask |= 1ull << e;
     }
   const unsigned long long lt = (1ull << lane) - 1ull;
   // per expert: rank inside the wave, wave totals to LDS
-  for (int e = 0; e <= E; ++e) {
-    const bool f = e < E ? ((mask >> e) & 1ull) : false;
-    const unsigned long long b = ballot(f);
+  for (int e = 0; e < E; ++e) {
+    const unsigned long long b = ballot((mask >> e) & 1ull);
     if (lane == 0) sh_wave[e][wave] = __popcll(b);
   }
   // local picks of this token and their scan (stream positions)
@@ -787,24 +822,23 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_place_kernel(RouteAr
     const int y = __shfl_up(x, d, 64);
     if (lane >= d) x += y;
   }
-  __shared__ int sh_pick[kRouteThreads / 64];
   if (lane == 63) sh_pick[wave] = x;
   __syncthreads();
   int pick_base = x - picks;
   for (int v = 0; v < wave; ++v) pick_base += sh_pick[v];
-  const int stream0 = a.wgbase[w * (E + 1) + E] + pick_base;
+  const int stream0 = sh_base[E] + pick_base;
   if (t < T) a.tok_first[(size_t)s * (a.rs_cap + 1) + t] = stream0;
   for (int e = 0; e < E; ++e) {
     const bool f = (mask >> e) & 1ull;
     const unsigned long long b = ballot(f);
     if (!f) continue;
-    int rank = a.wgbase[w * (E + 1) + e] + __popcll(b & lt);
+    int rank = sh_base[e] + __popcll(b & lt);
     for (int v = 0; v < wave; ++v) rank += sh_wave[e][v];
     int j = 0, kk = 0;   // local picks ahead of expert e in this token's list; e's position in it
     for (int k = 0; k < KK; ++k) {
-      const int ek = tk[k] - a.expert_base;
+      const int ek = tk[k];
       if (ek == e) { kk = k; break; }
-      j += (ek >= 0 && ek < E);
+      j += (ek != 0xFF);
     }
     const int i = stream0 + j;
     a.src_row[s * a.rs_cap + i] = t;

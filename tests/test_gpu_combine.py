@@ -146,6 +146,27 @@ def test_combine_ragged_widths_and_tokens(N):
     r.close()
 
 
+@pytest.mark.parametrize("combine_wg", [1, 3, 37])
+def test_combine_small_grids_stride_over_items(combine_wg):
+    log(f"combine with {combine_wg} workgroups: every wave loops over many push and sum items")
+    case = ep_case(2011, 4, 300, 128, 256, n_experts=16, topk=4, n_local=4)
+    r = CombineRun(case, ctx_kw=dict(combine_wg=combine_wg))
+    r.dispatch()
+    for t in range(2):
+        r.combine(3800 + t, flags=fg.CALL_VERIFY)
+    r.check_plane(2, verify_iters=2)
+    r.close()
+
+
+def test_combine_grid_beyond_residency_rejected():
+    log("combine grid larger than the resident capacity -> FG_ERESIDENCY at init")
+    case = ep_case(2012, 2, 64, 128, 256, n_experts=16, topk=4, n_local=4)
+    cfg = fg.make_config(2, 64, 128, 256, n_groups=4, combine_wg=65536)
+    with pytest.raises(fg.FgError) as e:
+        fg.Context(cfg)
+    assert e.value.code == fg.ERESIDENCY
+
+
 def test_combine_more_than_sixteen_local_picks():
     log("combine: every token picks 20 of 32 local experts (weights beyond the first 16 picks)")
     g = np.random.default_rng(2003)
