@@ -103,8 +103,8 @@ typedef struct {
                                   1 = one row-block-major list */
   int32_t copy_rows;           /* rows per copy batch of one wave: 1, 2, 4, 8 or 16, capped so that at most
                                   32 16-byte vectors per lane are in flight (0 = the cap) */
-  int32_t combine_wg;          /* workgroups of the combine kernel (0 = 2 per compute unit); any count is
-                                  safe, the kernel assumes no residency */
+  int32_t combine_wg;          /* workgroups of the combine kernel (0 = 2 per compute unit); the grid must
+                                  be co-resident (checked by fg_init: FG_ERESIDENCY) */
 } fg_config;
 
 typedef enum {
@@ -191,8 +191,8 @@ typedef struct {
                                  odd number of 128-row blocks */
   const int32_t* group_slab;  /* [groups + 1] first slab of each group (the last entry is n_slabs) */
   /* Combine plane (fg_combine) and the per-entry tables of the TOPK route: */
-  const int32_t* combine_slot;  /* [n_shards][chunk_cap] */
-  const int32_t* combine_elect; /* [2][n_shards][chunk_cap] parity double-buffered */
+  const int32_t* combine_slot;  /* [n_shards][chunk_cap][FG_COUNTER_STRIDE], value at [..][..][0] */
+  const int32_t* combine_elect; /* [2][n_shards][chunk_cap][FG_COUNTER_STRIDE] parity double-buffered */
   const int32_t* combine_pub;   /* [n_shards][chunk_cap] (VERIFY) */
   const int32_t* src_k;         /* [n_shards][max_rows_per_shard] top-k position of each stream entry */
   const int32_t* tok_first;     /* [n_shards][max_rows_per_shard + 1] first stream entry of each token;

@@ -336,8 +336,8 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
                o_pp = take(512), o_tdev = take(64), o_wg = take((size_t)grid_max * kWgTimeFields * 8),
                o_sslot = take((size_t)ctx->s_slots * 4), o_select = take(2 * (size_t)ctx->s_slots * 4),
                o_spub = take((size_t)ctx->s_slots * 4), o_srck = take(nrs * 4),
-               o_tokf = take((size_t)S * (cfg->max_rows_per_shard + 1) * 4), o_cslot = take(nch * 4),
-               o_celect = take(2 * nch * 4), o_cpub = take(nch * 4);
+               o_tokf = take((size_t)S * (cfg->max_rows_per_shard + 1) * 4), o_cslot = take(nch * kCombStride * 4),
+               o_celect = take(2 * nch * kCombStride * 4), o_cpub = take(nch * 4);
   if (hipMalloc(&ctx->plane_mem, off) != hipSuccess) { delete ctx; return FG_ENOMEM; }
   if (hipMemset(ctx->plane_mem, 0, off) != hipSuccess) { (void)hipFree(ctx->plane_mem); delete ctx; return FG_EHIP; }
   char* b = ctx->plane_mem;
@@ -568,7 +568,7 @@ fg_status fg_combine(fg_ctx* ctx, const void* out, const float* weights, void* c
   a.chunk_cap = ctx->chunk_cap;
   a.desc = ctx->p.desc; a.stream_len = ctx->p.stream_len; a.dst_row = ctx->p.dst_row; a.src_k = ctx->p.src_k;
   a.tok_first = ctx->p.tok_first;
-  a.cslot = ctx->p.cslot; a.celect_cur = ctx->p.celect + cur * nch; a.celect_nxt = ctx->p.celect + nxt * nch;
+  a.cslot = ctx->p.cslot; a.celect_cur = ctx->p.celect + cur * nch * kCombStride; a.celect_nxt = ctx->p.celect + nxt * nch * kCombStride;
   a.cpub = ctx->p.cpub;
   a.stats = ctx->p.stats; a.err = sink(ctx); a.seq = ctx->cseq; a.flags = flags; a.timeout_ticks = timeout_ticks(ctx);
   hipLaunchKernelGGL(combine_kernel, dim3(ctx->combine_wg), dim3(kCombThreads), 0, stream, a);

@@ -8,20 +8,23 @@
 // staging buffer per source shard, indexed by that shard's stream entries; the
 // shard's side then forms, per token, the gate-weighted sum of its local picks.
 //
-// One kernel, two phases; every wave takes items i, i + waves, ... of each:
+// One kernel; every wave takes push items i, i + waves, ..., then reduce items
+// i, i + waves, ... (both in shard-major order):
 //  * push items (4 stream entries of one shard per wave): copy
 //    out[dst_row[s][i]] -> staging[s][i] bitwise with device-coherent stores,
 //    release, add the wave's rows to the chunk's election count; the add that
 //    completes the chunk elects the wave, whose leader stores seq in the slot;
 //  * reduce items (4 tokens of one shard per wave): wait until the slot of
-//    every chunk holding the tokens' entries carries seq, acquire, and write
+//    every chunk holding the tokens' entries carries seq, then write
 //    y[s][t] = bf16(sum over the token's entries e, in k order, of
-//    w[s][t][k(e)] * staging[s][e]) with fp32 products and sums.
+//    w[s][t][k(e)] * staging[s][e]) with fp32 products and sums, the staging
+//    rows read with device-scope loads.
 // A wave starts its reduce items only after its push items, and the host
 // checks that the whole grid is co-resident, so every wait has a running
-// supplier that does not wait ("PCIe sync protocols" §6 audit). Static item
-// assignment keeps atomics off the item hand-out: one ticket counter shared by
-// every workgroup serialises at its memory channel.
+// supplier that does not wait ("PCIe sync protocols" §6 audit). Static item assignment keeps atomics off the item
+// hand-out: one ticket counter shared by every workgroup serialises at its
+// memory channel. Slots and election counts sit one per 256-byte line, so the
+// pollers of one slot do not load the channel of its neighbours.
 #pragma once
 
 #include "fg_kernels.hpp"
@@ -40,6 +43,7 @@ constexpr int kCombThreads = 64 * kCombWaves;
 #ifndef FG_COMB_U
 #define FG_COMB_U 4
 #endif
+constexpr int kCombStride = FG_COUNTER_STRIDE;            // ints per combine slot / election count (own line)
 constexpr int kPushPerWave = FG_COMB_PUSH;                // stream entries per push item (one wave)
 constexpr int kRedPerWave = FG_COMB_TOKENS;               // tokens per reduce item (one wave)
 constexpr int kCombU = FG_COMB_U;                         // 16-byte vectors per lane and row per column step
@@ -113,10 +117,11 @@ __device__ __forceinline__ void combine_push(const CombineArgs& a, const uint16_
   const int n_done = __popcll(ballot(g >= 0));
   if (lane == 0 && n_done > 0) {
     const int c = eb / kChunk, ch = s * a.chunk_cap + c;
-    const int old = strict ? fetch_add_acq_rel(a.celect_cur + ch, n_done) : fetch_add_relaxed(a.celect_cur + ch, n_done);
+    int* const el = a.celect_cur + (size_t)ch * kCombStride;
+    const int old = strict ? fetch_add_acq_rel(el, n_done) : fetch_add_relaxed(el, n_done);
     const int expect = min(kChunk, n_s - kChunk * c);
     if (old + n_done == expect) {
-      if (!((a.flags & kDropPublish) && ch == 0)) slot_publish(a.cslot + ch, a.seq, strict);
+      if (!((a.flags & kDropPublish) && ch == 0)) slot_publish(a.cslot + (size_t)ch * kCombStride, a.seq, strict);
       if (a.flags & kVerify) {
         atomicAdd(a.cpub + ch, 1);
         atomicAdd(a.stats + ST_PUBLISHES, 1ull);
@@ -161,7 +166,7 @@ __device__ __forceinline__ float reduce_weights(const CombineArgs& a, int s, int
 }
 
 // One wave: y rows of tokens tb .. tb + kRedPerWave - 1 of shard s from the
-// (acquired) staging rows; tf and wl from the two functions above.
+// published staging rows; tf and wl from the two functions above.
 __device__ __forceinline__ void combine_reduce(const CombineArgs& a, const uint16_t* stg, uint16_t* yb, int s, int tb,
                                                int tf, float wl, int lane) {
   const uint32_t row_bytes = (uint32_t)a.N * 2;
@@ -191,7 +196,7 @@ __device__ __forceinline__ void combine_reduce(const CombineArgs& a, const uint1
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(stg + (size_t)(valid ? ea[r] + j : 0) * a.N, valid ? row_bytes : 0u);
 #pragma unroll
         for (int u = 0; u < kCombU; ++u)
-          v[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(c0 + u * 64 + lane) * 16, 0, kPolNT);
+          v[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(c0 + u * 64 + lane) * 16, 0, kPolSC1 | kPolNT);
         float wr = 0.f;
         if (valid) {
           if (j < 16) {
@@ -231,7 +236,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
   const int G = gridDim.x;
   // arm the other parity for the next call (nothing else touches it here)
   for (int i = blockIdx.x * kCombThreads + threadIdx.x; i < a.n_shards * a.chunk_cap; i += G * kCombThreads)
-    a.celect_nxt[i] = 0;
+    a.celect_nxt[(size_t)i * kCombStride] = 0;
   if ((int)threadIdx.x < a.n_shards) {
     sh_stg[threadIdx.x] = a.staging[threadIdx.x];
     sh_y[threadIdx.x] = a.y[threadIdx.x];
@@ -270,6 +275,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
 
   const bool wait = !(a.flags & kGemmOnly);
   const bool verify = a.flags & kVerify;
+  const bool strict = a.flags & kStrict;
   for (int it = wid; it < n_red; it += nw) {
     const int s = it / ntb, tb = (it - s * ntb) * kRedPerWave;
     const int tf = min(max(tf_next, 0), a.rs_cap);
@@ -282,13 +288,17 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
       if (lane == 0) {
         uint32_t polls = 0;
         const uint64_t deadline = now_ticks() + a.timeout_ticks;
-        for (int c = e_lo / kChunk; c * kChunk < e_hi && ok; ++c)
-          ok = wait_ge(a.cslot + s * a.chunk_cap + c, a.seq, deadline, a.err, 0x70000000 | (s * a.chunk_cap + c),
-                       &polls);
+        for (int c = e_lo / kChunk; c * kChunk < e_hi && ok; ++c) {
+          const int ch = s * a.chunk_cap + c;
+          ok = wait_ge(a.cslot + (size_t)ch * kCombStride, a.seq, deadline, a.err, 0x70000000 | ch, &polls);
+        }
         if (verify) atomicAdd(a.stats + ST_SLOT_POLLS, (unsigned long long)polls);
       }
       if (!readlane(ok, 0)) break;
-      acquire_agent();
+      // the staging rows are read with device-scope loads, issued after the
+      // poll returned seq (the rows were written through before seq was
+      // stored); the formal acquire fence is the strict variant
+      if (strict) acquire_agent();
     }
     combine_reduce(a, uniform_ptr(sh_stg[s]), (uint16_t*)uniform_ptr(sh_y[s]), s, tb, tf, wl, lane);
   }

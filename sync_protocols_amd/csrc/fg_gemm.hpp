@@ -71,12 +71,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 // 128-byte rows, rows of equal parity share a half of the bank space, so the
 // slot is permuted by (r >> 1) & 7; with 64-byte rows, rows r mod 4 share a
 // quarter, permuted by (r >> 2) & 3.
+constexpr int kPolA = kPolSC1;   // gathered-row loads: device scope (see stage_load)
+
 __device__ __forceinline__ int swz(int c, int r) { return c ^ ((r / (256 / kRowB)) & (kChunks - 1)); }
 
 // Issue this wave's share of one stage: ROWS rows starting at byte offset
 // row0_off of the buffer, k slice [k0, k0 + 64), into LDS at `lds`. Each row
 // of the stage is one full 128-byte line (8 lanes x 16 bytes).
-template <int ROWS>
+// POL is the cache policy of the loads: the gathered rows (written in the same
+// kernel by other workgroups, possibly on other XCDs) are read with
+// device-scope loads, the weights with the default policy.
+template <int ROWS, int POL>
 __device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t r, uint32_t row0_off, uint32_t row_stride,
                                            uint32_t k0_bytes, char* lds, int wave, int lane) {
   constexpr int PER_WAVE = ROWS / kRowsPerLoad / kWaves;
@@ -88,7 +93,7 @@ __device__ __forceinline__ void stage_load(__amdgpu_buffer_rsrc_t r, uint32_t ro
     const int row = blk * kRowsPerLoad + sub;
     const int chunk = swz(slot, row);  // the xor is its own inverse
     const uint32_t voff = row0_off + (uint32_t)row * row_stride + (uint32_t)chunk * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + blk * 1024), 16, voff, k0_bytes, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + blk * 1024), 16, voff, k0_bytes, 0, POL);
   }
 }
 
@@ -185,8 +190,10 @@ __device__ __forceinline__ void stage_load_one(__amdgpu_buffer_rsrc_t rA, uint32
   const int row = blk * kRowsPerLoad + lane / kChunks;
   const int chunk = swz(lane % kChunks, row);
   const uint32_t voff = (isA ? a_off : b_off) + (uint32_t)row * stride + (uint32_t)chunk * 16;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(isA ? rA : rB, (lds_void*)(lds + (isA ? 0 : T::A_BYTES) + blk * 1024),
-                                           16, voff, k0_bytes, 0, 0);
+  if (isA)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(lds + blk * 1024), 16, voff, k0_bytes, 0, kPolA);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(lds + T::A_BYTES + blk * 1024), 16, voff, k0_bytes, 0, 0);
 }
 
 // Stage k in `cur`, its k-step 0 fragments already in f0.
@@ -310,10 +317,10 @@ __device__ __forceinline__ void tile_mainloop(__amdgpu_buffer_rsrc_t rA, uint32_
     const int nk = nk64;   // even
     char* const lds0 = l0;
     char* const lds1 = l1;
-    stage_load<BM>(rA, a_off, stride, 0, lds0, wave, lane);
-    stage_load<BN>(rB, b_off, stride, 0, lds0 + T::A_BYTES, wave, lane);
-    stage_load<BM>(rA, a_off, stride, kRowB, lds1, wave, lane);
-    stage_load<BN>(rB, b_off, stride, kRowB, lds1 + T::A_BYTES, wave, lane);
+    stage_load<BM, kPolA>(rA, a_off, stride, 0, lds0, wave, lane);
+    stage_load<BN, 0>(rB, b_off, stride, 0, lds0 + T::A_BYTES, wave, lane);
+    stage_load<BM, kPolA>(rA, a_off, stride, kRowB, lds1, wave, lane);
+    stage_load<BN, 0>(rB, b_off, stride, kRowB, lds1 + T::A_BYTES, wave, lane);
     wait_vmcnt<T::LOADS>();
     __syncthreads();
     frags_read<BM, BN>(lds0, lds0 + T::A_BYTES, f0, 0, wm, wn, lane);
@@ -331,8 +338,8 @@ __device__ __forceinline__ void tile_mainloop(__amdgpu_buffer_rsrc_t rA, uint32_
     char* const L[4] = {l0, l1, l2, l3};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      stage_load<BM>(rA, a_off, stride, (uint32_t)i * kRowB, L[i], wave, lane);
-      stage_load<BN>(rB, b_off, stride, (uint32_t)i * kRowB, L[i] + T::A_BYTES, wave, lane);
+      stage_load<BM, kPolA>(rA, a_off, stride, (uint32_t)i * kRowB, L[i], wave, lane);
+      stage_load<BN, 0>(rB, b_off, stride, (uint32_t)i * kRowB, L[i] + T::A_BYTES, wave, lane);
     }
     wait_vmcnt<3 * T::LOADS>();
     __syncthreads();

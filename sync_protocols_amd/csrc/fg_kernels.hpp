@@ -442,7 +442,9 @@ __device__ void gemm_role(const FusedArgs& a, char* const* lds, int* sh, long lo
     const int q = __builtin_amdgcn_readfirstlane(sh[3]);
     const int entry = __builtin_amdgcn_readfirstlane(sh[4]);
     if (!sh[1]) break;
-    acquire_agent();
+    // the tile reads the gathered rows with device-scope loads issued after the
+    // gate poll returned 128; the formal acquire fence is the strict variant
+    if (strict) acquire_agent();
     const int m0 = entry & ~1, n0 = (tile - (tile / L.n_tn) * L.n_tn) * BN;
     const int g = __builtin_amdgcn_readfirstlane(a.group_of_rb[m0 / kRB]);
     const int tr_id = q < 0 ? tile : n_tiles + q;

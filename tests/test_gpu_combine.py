@@ -104,8 +104,9 @@ class CombineRun:
         S, cc = self.S, v.chunk_cap
         lay = self.case.lay
         want = O.state_after(lay, t, cc)
-        slot = self.ctx.read_i32(v.combine_slot, S * cc).numpy().reshape(S, cc)
-        elect = self.ctx.read_i32(v.combine_elect, 2 * S * cc).numpy().reshape(2, S, cc)
+        cs = fg.COUNTER_STRIDE
+        slot = self.ctx.read_i32(v.combine_slot, S * cc * cs).numpy().reshape(S, cc, cs)[:, :, 0]
+        elect = self.ctx.read_i32(v.combine_elect, 2 * S * cc * cs).numpy().reshape(2, S, cc, cs)[:, :, :, 0]
         assert np.array_equal(slot, want.slot), "combine slots"
         assert np.array_equal(elect, want.elect), "combine election counts (both parities)"
         if verify_iters is not None:
@@ -226,10 +227,24 @@ def test_combine_follows_a_route_change():
     r.combine(3501)
     v = r.ctx.views()
     S, cc = r.S, v.chunk_cap
-    slot = r.ctx.read_i32(v.combine_slot, S * cc).numpy().reshape(S, cc)
+    cs = fg.COUNTER_STRIDE
+    slot = r.ctx.read_i32(v.combine_slot, S * cc * cs).numpy().reshape(S, cc, cs)[:, :, 0]
     for s in range(S):
         n_ch = -(-int(b.lay.stream_len[s]) // 64)
         assert np.all(slot[s, :n_ch] == 2), "every chunk of the new route published in call 2"
+    r.close()
+
+
+def test_combine_strict_fences_same_bits():
+    log("combine with formal release / acquire fences gives the same bits as the default")
+    case = ep_case(2013, 4, 180, 128, 512, n_experts=16, topk=4, n_local=4)
+    r = CombineRun(case)
+    r.dispatch()
+    r.combine(3900)
+    y1 = [bits(y).copy() for y in r.y]
+    r.combine(3900, flags=fg.CALL_STRICT | fg.CALL_VERIFY)
+    for a, b in zip(y1, r.y):
+        assert np.array_equal(a, bits(b))
     r.close()
 
 
