@@ -152,6 +152,8 @@ typedef struct {
   int32_t split_parts;            /* k-ranges per split tile (1 when none is split) */
   int32_t combine_seq;            /* last combine sequence number issued (monotonic, never reset) */
   double clock_mhz;               /* last fused kernel: shader-clock cycles / wall time, over all workgroups */
+  int64_t litmus_stale;           /* fg_litmus: words read with a value other than the round's, cumulative */
+  int64_t litmus_words;           /* fg_litmus: words checked, cumulative */
 } fg_stats_t;
 
 /* Read-only device views of the library-owned control plane (for tests that
@@ -286,6 +288,21 @@ fg_status fg_stress(fg_ctx* ctx, const int32_t* chunk_rows, const int32_t* delay
  * FG_EPROTOCOL from an earlier call, FG_EHIP. */
 fg_status fg_combine(fg_ctx* ctx, const void* out, const float* weights, void* const* staging,
                      void* const* y, uint32_t flags, hipStream_t stream);
+
+/* Message-passing litmus test of how signalled data is read (an isolated
+ * debug entry, "PCIe sync protocols" §7, for the data-then-signal chain of
+ * §3): `rounds` rounds (1..1e6) in one kernel of two workgroups on different
+ * XCDs. Each round the writer stores a 16 KB block with device-scope
+ * write-through stores, waits for their acknowledgement and stores the round
+ * number into a flag; the reader, whose caches hold the block's previous
+ * contents, polls the flag and reads the block again:
+ *   mode 0: device-scope loads, as the library reads signalled data;
+ *   mode 1: plain loads (expected to see stale words: shows the test's reach);
+ *   mode 2: plain loads after the formal agent-scope acquire fence.
+ * Words that differ from the round number accumulate in
+ * fg_stats.litmus_stale (out of fg_stats.litmus_words). Every wait has the
+ * context's watchdog. */
+fg_status fg_litmus(fg_ctx* ctx, int32_t rounds, int32_t mode, hipStream_t stream);
 
 /* Copy the observation counters to *out. wait != 0 first synchronises the
  * bound stream (needed for device-computed fields and timings). */

@@ -64,6 +64,7 @@ struct Plane {
   int* cslot;      // combine plane: slots, election counts x2, publisher counts
   int* celect;
   int* cpub;
+  int* litmus;     // message-passing litmus test: 16 KB block, flag, ready, stale count
 };
 
 }  // namespace
@@ -81,7 +82,8 @@ struct fg_ctx {
   char* plane_mem = nullptr;
   Plane p{};
   int* host_status = nullptr;
-  int seq = 0, bseq = 0, sseq = 0, ppseq = 0, cseq = 0;
+  int seq = 0, bseq = 0, sseq = 0, ppseq = 0, cseq = 0, lseq = 0;
+  long long litmus_words = 0;
   int topk_rows = 0, topk_k = 0;   // tokens per shard and k of the last TOPK route
   int combine_wg = 0;
   uint32_t route_ver = 0;
@@ -337,7 +339,7 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
                o_sslot = take((size_t)ctx->s_slots * 4), o_select = take(2 * (size_t)ctx->s_slots * 4),
                o_spub = take((size_t)ctx->s_slots * 4), o_srck = take(nrs * 4),
                o_tokf = take((size_t)S * (cfg->max_rows_per_shard + 1) * 4), o_cslot = take(nch * kCombStride * 4),
-               o_celect = take(2 * nch * kCombStride * 4), o_cpub = take(nch * 4);
+               o_celect = take(2 * nch * kCombStride * 4), o_cpub = take(nch * 4), o_lit = take(kLitmusBytes + 768);
   if (hipMalloc(&ctx->plane_mem, off) != hipSuccess) { delete ctx; return FG_ENOMEM; }
   if (hipMemset(ctx->plane_mem, 0, off) != hipSuccess) { (void)hipFree(ctx->plane_mem); delete ctx; return FG_EHIP; }
   char* b = ctx->plane_mem;
@@ -354,7 +356,7 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
   p.wgtime = (long long*)(b + o_wg); p.s_slot = (int*)(b + o_sslot); p.s_elect = (int*)(b + o_select);
   p.s_pub = (int*)(b + o_spub);
   p.src_k = (int*)(b + o_srck); p.tok_first = (int*)(b + o_tokf); p.cslot = (int*)(b + o_cslot);
-  p.celect = (int*)(b + o_celect); p.cpub = (int*)(b + o_cpub);
+  p.celect = (int*)(b + o_celect); p.cpub = (int*)(b + o_cpub); p.litmus = (int*)(b + o_lit);
   if (hipHostMalloc((void**)&ctx->host_status, 64, hipHostMallocCoherent) != hipSuccess) {
     (void)hipFree(ctx->plane_mem); delete ctx; return FG_ENOMEM;
   }
@@ -576,12 +578,32 @@ fg_status fg_combine(fg_ctx* ctx, const void* out, const float* weights, void* c
   return FG_OK;
 }
 
+fg_status fg_litmus(fg_ctx* ctx, int32_t rounds, int32_t mode, hipStream_t stream) {
+  if (!ctx || rounds < 1 || rounds > 1000000 || mode < 0 || mode > 2) return FG_EINVAL;
+  fg_status s = check_sticky(ctx);
+  if (s != FG_OK) return s;
+  if (bind_stream(ctx, stream) != FG_OK) return FG_EINVAL;
+  HIPCHK(hipSetDevice(ctx->device));
+  int* data = ctx->p.litmus;
+  int* flag = data + kLitmusBytes / 4;
+  int* ready = flag + 64;
+  unsigned long long* stale = (unsigned long long*)(ready + 64);
+  auto* k = mode == 0 ? litmus_kernel<0> : mode == 1 ? litmus_kernel<1> : litmus_kernel<2>;
+  hipLaunchKernelGGL(k, dim3(2), dim3(64), 0, stream, data, flag, ready, stale, ctx->lseq, rounds, sink(ctx),
+                     timeout_ticks(ctx));
+  HIPCHK(hipGetLastError());
+  ctx->lseq += rounds;
+  ctx->litmus_words += (long long)rounds * (kLitmusBytes / 4);
+  return FG_OK;
+}
+
 fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait) {
   if (!ctx || !out) return FG_EINVAL;
   HIPCHK(hipSetDevice(ctx->device));
   if (wait && ctx->stream_bound) HIPCHK(hipStreamSynchronize(ctx->stream));
   memset(out, 0, sizeof(*out));
   out->seq = ctx->seq; out->bseq = ctx->bseq; out->stress_seq = ctx->sseq; out->combine_seq = ctx->cseq;
+  out->litmus_words = ctx->litmus_words;
   out->n_comm_wg = ctx->n_comm; out->n_gemm_wg = ctx->n_gemm; out->cu_count = ctx->cu_count;
   out->m_pad_cap = ctx->m_pad_cap;
   if (!wait) { out->m_pad = ctx->last_m_pad; return FG_OK; }
@@ -593,6 +615,11 @@ fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait) {
   HIPCHK(hipMemcpy(st, ctx->p.stats, sizeof(st), hipMemcpyDeviceToHost));
   HIPCHK(hipMemcpy(td, ctx->p.tdev, sizeof(td), hipMemcpyDeviceToHost));
   out->error_code = err[0]; out->error_id = err[1];
+  {
+    unsigned long long ls = 0;
+    HIPCHK(hipMemcpy(&ls, ctx->p.litmus + kLitmusBytes / 4 + 128, 8, hipMemcpyDeviceToHost));
+    out->litmus_stale = (int64_t)ls;
+  }
   out->m_pad = desc;
   out->publishes = (int64_t)st[ST_PUBLISHES]; out->gate_polls = (int64_t)st[ST_GATE_POLLS];
   out->slot_polls = (int64_t)st[ST_SLOT_POLLS]; out->gate_passes = (int64_t)st[ST_GATE_PASSES];

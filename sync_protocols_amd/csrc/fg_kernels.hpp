@@ -913,6 +913,65 @@ __global__ __launch_bounds__(64, 1) void pingpong_kernel(int* a_slot, int* b_slo
 }
 
 // ---------------------------------------------------------------------------
+// Message-passing litmus test of the acquire side (an isolated debug entry,
+// "PCIe sync protocols" §7; the data-then-signal chain of §3). Workgroup 0
+// (XCD 0) writes a 16 KB block with device-scope write-through stores, waits
+// for their acknowledgement and stores round k into a flag; workgroup 1 (XCD 1)
+// first reads the block with plain loads, so that its L1 and L2 hold the old
+// contents, tells the writer, polls the flag, then reads the block again with
+// the policy under test and counts the words that are not k.
+//   MODE 0: device-scope loads (how the library reads signalled data);
+//   MODE 1: plain loads (shows that the test sees the reader's caches);
+//   MODE 2: plain loads after the formal agent-scope acquire fence.
+// ---------------------------------------------------------------------------
+constexpr int kLitmusVec = 16;                                // 16-byte vectors per lane
+constexpr uint32_t kLitmusBytes = 64u * kLitmusVec * 16u;     // 16 KB block
+
+template <int MODE>
+__global__ __launch_bounds__(64, 1) void litmus_kernel(int* data, int* flag, int* ready,
+                                                        unsigned long long* stale_out, int base, int rounds,
+                                                        ErrorSink e, uint64_t timeout) {
+  const int lane = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t r = buffer_rsrc(data, kLitmusBytes);
+  unsigned long long stale = 0;
+  for (int i = 1; i <= rounds; ++i) {
+    const int k = base + i;
+    if (blockIdx.x == 1) {
+#pragma unroll
+      for (int u = 0; u < kLitmusVec; ++u) {
+        const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(u * 64 + lane) * 16, 0, 0);
+        asm volatile("" : : "v"(v));   // the old contents must really be loaded
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (lane == 0) __hip_atomic_store(ready, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int ok = 1;
+      uint32_t polls = 0;
+      if (lane == 0) ok = wait_ge(flag, k, now_ticks() + timeout, e, 0x71000001, &polls);
+      if (!readlane(ok, 0)) break;
+      if (MODE == 2) acquire_agent();
+#pragma unroll
+      for (int u = 0; u < kLitmusVec; ++u) {
+        const v4i v = MODE == 0 ? __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(u * 64 + lane) * 16, 0, kPolSC1)
+                                : __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(u * 64 + lane) * 16, 0, 0);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) stale += (v[h] != k);
+      }
+    } else if (blockIdx.x == 0) {
+      int ok = 1;
+      uint32_t polls = 0;
+      if (lane == 0) ok = wait_ge(ready, k, now_ticks() + timeout, e, 0x71000000, &polls);
+      if (!readlane(ok, 0)) break;
+      const v4i val = {k, k, k, k};
+#pragma unroll
+      for (int u = 0; u < kLitmusVec; ++u) store16_coherent(r, (uint32_t)(u * 64 + lane) * 16, val);
+      release_coherent(false);
+      if (lane == 0) slot_publish(flag, k, false);
+    }
+  }
+  if (blockIdx.x == 1 && stale) atomicAdd(stale_out, stale);
+}
+
+// ---------------------------------------------------------------------------
 // Protocol stress ("PCIe sync protocols" §3 validation scale, §4 chunked slots).
 // Workgroups [0, P) are producers, [P, P + C) consumers. Slot id
 // sid = (p * C + c) * KC + k. Producer waves split a chunk's rows 16 each and

@@ -31,7 +31,7 @@ FAULT_DROP_PUBLISH = 1 << 10
 
 ROUTE_CONTIG, ROUTE_EXPLICIT, ROUTE_TOPK = 0, 1, 2
 
-EXPORTS = ("fg_init", "fg_gather_gemm", "fg_barrier", "fg_pingpong", "fg_stress", "fg_combine", "fg_stats",
+EXPORTS = ("fg_init", "fg_gather_gemm", "fg_barrier", "fg_pingpong", "fg_stress", "fg_combine", "fg_litmus", "fg_stats",
            "fg_views", "fg_capacity", "fg_destroy", "fg_strerror")
 
 
@@ -61,7 +61,8 @@ class FgStats(C.Structure):
                 ("t_barrier_us", C.c_double), ("t_rtt_us", C.c_double),
                 ("n_comm_wg", C.c_int32), ("n_gemm_wg", C.c_int32), ("cu_count", C.c_int32),
                 ("m_pad_cap", C.c_int32), ("tiles_whole", C.c_int32), ("tiles_split", C.c_int32),
-                ("split_parts", C.c_int32), ("combine_seq", C.c_int32), ("clock_mhz", C.c_double)]
+                ("split_parts", C.c_int32), ("combine_seq", C.c_int32), ("clock_mhz", C.c_double),
+                ("litmus_stale", C.c_int64), ("litmus_words", C.c_int64)]
 
 
 class FgViews(C.Structure):
@@ -99,6 +100,7 @@ def load_library() -> C.CDLL:
     lib.fg_pingpong.argtypes = [vp, C.c_int32, C.c_int32, vp]
     lib.fg_stress.argtypes = [vp, vp, vp, vp, C.c_uint32, vp]
     lib.fg_combine.argtypes = [vp, vp, vp, C.POINTER(vp), C.POINTER(vp), C.c_uint32, vp]
+    lib.fg_litmus.argtypes = [vp, C.c_int32, C.c_int32, vp]
     lib.fg_stats.argtypes = [vp, C.POINTER(FgStats), C.c_int]
     lib.fg_views.argtypes = [vp, C.POINTER(FgViews)]
     lib.fg_capacity.argtypes = [C.POINTER(FgConfig), C.POINTER(C.c_int32)]
@@ -195,6 +197,9 @@ class Context:
         ys = (C.c_void_p * len(y))(*[t.data_ptr() for t in y])
         self._keep_c = [st, ys]
         return self._lib.fg_combine(self._h, _ptr(out), _ptr(weights), st, ys, flags, _stream_ptr(stream))
+
+    def litmus(self, rounds: int, mode: int = 0, stream=None) -> int:
+        return self._lib.fg_litmus(self._h, rounds, mode, _stream_ptr(stream))
 
     def stats(self, wait: bool = True) -> FgStats:
         st = FgStats()

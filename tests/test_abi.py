@@ -52,6 +52,8 @@ def test_null_arguments_rejected_without_gpu():
     assert lib.fg_init(None, 0, None) == fg.EINVAL
     assert lib.fg_destroy(None) == fg.EINVAL
     assert lib.fg_stats(None, None, 0) == fg.EINVAL
+    assert lib.fg_litmus(None, 10, 0, None) == fg.EINVAL
+    assert lib.fg_combine(None, None, None, None, None, 0, None) == fg.EINVAL
 
 
 def _c_layout(tmp_path):

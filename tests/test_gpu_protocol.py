@@ -175,3 +175,23 @@ def test_invalid_arguments():
     torch.cuda.synchronize()
     assert ctx.stats().error_code == 0
     ctx.close()
+
+
+def test_litmus_device_scope_loads_see_signalled_data():
+    log("litmus: writer on XCD 0, reader on XCD 1 with the old block cached; device-scope loads after the flag")
+    ctx = fg.Context(fg.make_config(2, 256, 256, 256))
+    assert ctx.litmus(5000, 0) == fg.OK
+    st0 = ctx.stats()
+    assert st0.error_code == 0
+    assert st0.litmus_words == 5000 * 4096
+    assert st0.litmus_stale == 0, "a device-scope load returned a word from before the signal"
+    assert ctx.litmus(2000, 1) == fg.OK
+    st1 = ctx.stats()
+    log(f"plain loads without a fence: {st1.litmus_stale - st0.litmus_stale} stale words of {2000 * 4096} "
+        "(the reader's caches are in reach of the test)")
+    assert ctx.litmus(5000, 2) == fg.OK
+    st2 = ctx.stats()
+    assert st2.error_code == 0
+    assert st2.litmus_stale == st1.litmus_stale, "plain loads after the acquire fence returned stale words"
+    assert ctx.litmus(0, 0) == fg.EINVAL and ctx.litmus(10, 3) == fg.EINVAL
+    ctx.close()
