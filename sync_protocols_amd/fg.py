@@ -198,6 +198,20 @@ class Context:
         self._keep_c = [st, ys]
         return self._lib.fg_combine(self._h, _ptr(out), _ptr(weights), st, ys, flags, _stream_ptr(stream))
 
+    def prepare_combine(self, out, weights, staging, y, stream=None):
+        """fg_combine with its arguments marshalled once: returns f(flags=0) ->
+        fg_status. The tensors must stay alive (and in place) while f is used."""
+        st = (C.c_void_p * len(staging))(*[t.data_ptr() for t in staging])
+        ys = (C.c_void_p * len(y))(*[t.data_ptr() for t in y])
+        args = (self._h, _ptr(out), _ptr(weights), st, ys)
+        sp = _stream_ptr(stream)
+        fn = self._lib.fg_combine
+
+        def call(flags: int = 0) -> int:
+            return fn(*args, flags, sp)
+        call._keep = (st, ys, out, weights, staging, y)
+        return call
+
     def litmus(self, rounds: int, mode: int = 0, stream=None) -> int:
         return self._lib.fg_litmus(self._h, rounds, mode, _stream_ptr(stream))
 
