@@ -362,6 +362,132 @@ def simulate_iteration(lay: Layout, state: ProtocolState, t: int, batches, order
     return SimResult(state, pubs, arr, gates, early_g, early_p)
 
 
+# ---------------------------------------------------------------------------
+# Two-stage dispatch ("PCIe sync protocols" §4 chunk watermark: each producer
+# stream is cut into 64-row chunks and the chunk's slot is the watermark the
+# receiver waits on; §6 audit item 2: the receiver's scatter waits only on the
+# remote watermarks and reads its own shard directly). Stage 1 pushes every
+# stream row of a remote shard into that shard's staging buffer in stream
+# order and publishes the chunk watermarks; stage 2 scatters rows into the
+# gathered buffer, after the watermark of their chunk, and counts arrivals
+# into the seeded 128-row counters of §5.
+# ---------------------------------------------------------------------------
+
+def push_staging(shards_bits, lay: Layout, self_shard: int = -1) -> list:
+    """staging[s][i] = shard_s[src_row[s][i]] bitwise for every shard other
+    than ``self_shard`` (reading R27); the self shard has no staging rows."""
+    out = []
+    for s in range(lay.n_shards):
+        if s == self_shard:
+            out.append(None)
+            continue
+        X = np.asarray(shards_bits[s])
+        out.append(X[np.asarray(lay.src_row[s], dtype=np.int64)])
+    return out
+
+
+def state_after_two_stage(lay: Layout, t: int, chunk_cap: int, self_shard: int = -1) -> ProtocolState:
+    """Control plane after t iterations of the two-stage dispatch (reading R27):
+    the pushes publish the slot of every chunk of every remote shard, as the
+    one-stage copy does, and the scatter brings every 128-row counter to 128;
+    the self shard is never pushed, so its slots, election counts and
+    publisher counts stay 0."""
+    st = state_after(lay, t, chunk_cap)
+    if 0 <= self_shard < lay.n_shards:
+        st.slot[self_shard] = 0
+        st.elect[:, self_shard] = 0
+        st.pub_count[self_shard] = 0
+    return st
+
+
+@dataclasses.dataclass
+class TwoStageResult:
+    state: ProtocolState
+    staged: list             # staging rows written, per shard (bool per stream entry)
+    publishes: int
+    early_scatter: int       # a row scattered from staging before the row was pushed
+    early_gates: int         # a gate opened while one of its real rows was unscattered
+    deferred: int            # scatter steps that found a watermark not yet published
+
+
+def simulate_two_stage(lay: Layout, state: ProtocolState, t: int, push_batches, scatter_batches, events,
+                       self_shard: int = -1) -> TwoStageResult:
+    """One iteration, event by event. ``push_batches``: lists of (s, i) stream
+    entries of remote shards, each inside one chunk; ``scatter_batches``: lists
+    of gathered rows; ``events``: a sequence of ("push", b) and ("scatter", b).
+      push b: write the batch's staging rows, add its row count to the chunk's
+        election count; the add that completes the chunk stores t into its slot;
+      scatter b: if a remote row of the batch has a chunk whose slot is not yet
+        t, the step is deferred to the end of the sequence (the watermark wait);
+        otherwise copy every row (remote rows from staging, self-shard rows from
+        the shard) into the gathered buffer and add the rows per block to the
+        counters; a gate opens when its counter reaches 128.
+    At the end the other parity is re-armed (reading R4)."""
+    p = t & 1
+    exp = chunk_table(lay)
+    inv = {}
+    for s in range(lay.n_shards):
+        for i, d in enumerate(lay.dst_row[s]):
+            inv[int(d)] = (s, i)
+    staged = [np.zeros(len(lay.src_row[s]), dtype=bool) for s in range(lay.n_shards)]
+    written = np.zeros(lay.m_pad, dtype=bool)
+    real = real_rows(lay)
+    opened = np.zeros(lay.n_rb, dtype=bool)
+    pubs = early_s = early_g = deferred = 0
+    queue = list(events)
+    k = 0
+    stall = 0            # deferrals since the last step that ran
+    while k < len(queue):
+        kind, b = queue[k]
+        k += 1
+        if kind == "push":
+            stall = 0
+            rows = push_batches[b]
+            for (s, i) in rows:
+                staged[s][i] = True
+            s, c = rows[0][0], rows[0][1] // lay.chunk_rows
+            old = state.elect[p, s, c]
+            state.elect[p, s, c] = old + len(rows)
+            if old + len(rows) == exp[s][c]:
+                state.slot[s, c] = t
+                state.pub_count[s, c] += 1
+                pubs += 1
+            continue
+        rows = scatter_batches[b]
+        ready = True
+        for g in rows:
+            s, i = inv[g]
+            if s != self_shard and state.slot[s, i // lay.chunk_rows] != t:
+                ready = False
+        if not ready:
+            deferred += 1
+            stall += 1
+            queue.append((kind, b))
+            if stall > len(queue) - k:      # a full pass over the pending steps ran nothing
+                raise RuntimeError("scatter waits on a watermark no push publishes")
+            continue
+        stall = 0
+        per_rb = {}
+        for g in rows:
+            s, i = inv[g]
+            if s != self_shard and not staged[s][i]:
+                early_s += 1
+            written[g] = True
+            r = g // lay.row_block
+            per_rb[r] = per_rb.get(r, 0) + 1
+        for r, n in per_rb.items():
+            state.counter[p, r] += n
+            if state.counter[p, r] == lay.row_block and not opened[r]:
+                opened[r] = True
+                blk = slice(r * lay.row_block, (r + 1) * lay.row_block)
+                if np.any(real[blk] & ~written[blk]):
+                    early_g += 1
+    q = (t + 1) & 1
+    state.counter[q] = seeds(lay)
+    state.elect[q] = 0
+    return TwoStageResult(state, staged, pubs, early_s, early_g, deferred)
+
+
 def election_brute_force(parts) -> int:
     """A chunk of sum(parts) rows finished by len(parts) waves, wave w adding
     parts[w]: over every completion order, count the adds that see

@@ -465,3 +465,100 @@ def test_combine_partial_locality_and_tolerance_teeth():
     idx = np.unravel_index(np.argmax(np.abs(y)), y.shape)
     bad[idx] += 3 * tol[idx]
     assert not np.all(np.abs(bad - y) <= tol)
+
+
+# ------------------------------------------------------------ two-stage dispatch
+
+def _push_batches(lay, rng, self_shard, max_rows=3):
+    """Random push batches of remote stream entries, each inside one chunk."""
+    out = []
+    for s in range(lay.n_shards):
+        if s == self_shard:
+            continue
+        n = int(lay.stream_len[s])
+        for c0 in range(0, n, lay.chunk_rows):
+            i = c0
+            end = min(n, c0 + lay.chunk_rows)
+            while i < end:
+                k = int(rng.integers(1, max_rows + 1))
+                out.append([(s, j) for j in range(i, min(end, i + k))])
+                i += k
+    return out
+
+
+def _scatter_batches(lay, rng, max_rows=5):
+    rows = [int(d) for s in range(lay.n_shards) for d in lay.dst_row[s]]
+    rows.sort()
+    out, j = [], 0
+    while j < len(rows):
+        k = int(rng.integers(1, max_rows + 1))
+        out.append(rows[j:j + k])
+        j += k
+    return out
+
+
+def test_push_staging_special_cases():
+    rng = np.random.default_rng(31)
+    shards = [O.f64_to_bf16(rng.standard_normal((9, 4))) for _ in range(3)]
+    lay = O.layout_contiguous(3, 9)
+    st = O.push_staging(shards, lay)
+    for s in range(3):
+        assert np.array_equal(st[s], shards[s])          # contiguous: the stream is the shard itself
+    st = O.push_staging(shards, lay, self_shard=1)
+    assert st[1] is None and np.array_equal(st[2], shards[2])
+    g = _golden("ep_route_tiny.json")
+    lay = O.layout_topk(np.array(g["topk"]), g["expert_base"], g["n_local"], row_block=g["row_block"],
+                        chunk_rows=g["chunk_rows"])
+    sh = [O.f64_to_bf16(rng.standard_normal((3, 2))) for _ in range(2)]
+    st = O.push_staging(sh, lay)
+    for s in range(2):
+        for i, t in enumerate(g["src_row"][s]):           # stream entry i carries token src_row[s][i]
+            assert np.array_equal(st[s][i], sh[s][t])
+    # the scatter of the staged rows rebuilds the one-stage gather
+    G = O.gather(sh, lay)
+    for s in range(2):
+        for i, d in enumerate(g["dst_row"][s]):
+            assert np.array_equal(G[d], st[s][i])
+
+
+@pytest.mark.parametrize("self_shard", [-1, 0, 2])
+def test_two_stage_simulation_matches_closed_form(self_shard):
+    rng = np.random.default_rng(40 + self_shard)
+    for lay in _layouts_small():
+        if self_shard >= lay.n_shards:
+            continue
+        cap = int(max(-(-lay.stream_len // lay.chunk_rows)))
+        state = O.state_after_two_stage(lay, 0, cap, self_shard)
+        remote_chunks = sum(-(-int(lay.stream_len[s]) // lay.chunk_rows)
+                            for s in range(lay.n_shards) if s != self_shard)
+        for t in range(1, 4):
+            pb = _push_batches(lay, rng, self_shard)
+            sb = _scatter_batches(lay, rng)
+            events = [("push", b) for b in range(len(pb))] + [("scatter", b) for b in range(len(sb))]
+            events = [events[k] for k in rng.permutation(len(events))]
+            r = O.simulate_two_stage(lay, state, t, pb, sb, events, self_shard)
+            assert r.early_scatter == 0 and r.early_gates == 0
+            assert r.publishes == remote_chunks
+            want = O.state_after_two_stage(lay, t, cap, self_shard)
+            assert np.array_equal(r.state.slot, want.slot)
+            assert np.array_equal(r.state.counter, want.counter)
+            assert np.array_equal(r.state.elect, want.elect)
+            assert np.array_equal(r.state.pub_count, want.pub_count)
+            for s in range(lay.n_shards):
+                assert np.all(r.staged[s]) == (s != self_shard) or int(lay.stream_len[s]) == 0
+
+
+def test_two_stage_missing_push_never_releases_the_scatter():
+    lay = O.layout_contiguous(2, 40, row_block=16, chunk_rows=8)
+    rng = np.random.default_rng(9)
+    cap = int(max(-(-lay.stream_len // lay.chunk_rows)))
+    pb = _push_batches(lay, rng, -1)
+    sb = _scatter_batches(lay, rng)
+    events = [("push", b) for b in range(1, len(pb))] + [("scatter", b) for b in range(len(sb))]
+    with pytest.raises(RuntimeError):
+        O.simulate_two_stage(lay, O.state_after_two_stage(lay, 0, cap), 1, pb, sb, events)
+    # the self shard's rows need no push: dropping its batches changes nothing
+    pb1 = _push_batches(lay, rng, 0)
+    events = [("push", b) for b in range(len(pb1))] + [("scatter", b) for b in range(len(sb))]
+    r = O.simulate_two_stage(lay, O.state_after_two_stage(lay, 0, cap, 0), 1, pb1, sb, events, self_shard=0)
+    assert r.early_scatter == 0 and np.all(r.state.counter[1] == lay.row_block)
