@@ -234,6 +234,26 @@ fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route*
                          const void* W, void* gathered, void* out, uint32_t flags,
                          hipStream_t stream);
 
+/* The same iteration as fg_gather_gemm with the dispatch in two stages
+ * ("PCIe sync protocols" §4 chunk watermark; §6 audit item 2: the receiver's
+ * scatter waits only on remote watermarks and reads its own shard directly).
+ * Stage 1, push: every stream entry i of every shard s other than self_shard
+ * is copied shards[s][src_row[s][i]] -> staging[s][i] bitwise (write-through
+ * stores); the wave that completes a 64-entry chunk, elected by a local count,
+ * stores seq into the chunk's slot (the watermark). Stage 2, scatter: gathered
+ * rows, in gathered-row order, are copied from staging (remote shards, after
+ * their chunk's slot carries seq) or from the shard (self_shard, no wait) and
+ * counted into the seeded 128-row counters; the compute role gates on those
+ * counters as in fg_gather_gemm. The slots, election counts and publisher
+ * counts of self_shard are not touched.
+ *   staging:    host array of n_shards device pointers, bf16 [max_rows_per_shard][K]
+ *               (written; the entry of self_shard may be NULL)
+ *   self_shard: -1 (every shard is remote) or 0..n_shards-1
+ * Other arguments, flags and errors as fg_gather_gemm. */
+fg_status fg_gather_gemm_staged(fg_ctx* ctx, const void* const* shards, const fg_route* route,
+                                const void* W, void* const* staging, int32_t self_shard, void* gathered,
+                                void* out, uint32_t flags, hipStream_t stream);
+
 /* `rounds` consecutive all-rank barriers over n_shards virtual ranks in one
  * kernel ("PCIe sync protocols" §2): rank i's lane j stores bseq into
  * bslot[j][i] (its own slot on every rank), then waits until

@@ -382,8 +382,9 @@ fg_status fg_destroy(fg_ctx* ctx) {
   return FG_OK;
 }
 
-fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route* route, const void* W,
-                         void* gathered, void* out, uint32_t flags, hipStream_t stream) {
+static fg_status gather_gemm_impl(fg_ctx* ctx, const void* const* shards, const fg_route* route, const void* W,
+                                  void* const* staging, int self_shard, void* gathered, void* out, uint32_t flags,
+                                  hipStream_t stream) {
   if (!ctx) return FG_EINVAL;
   fg_status s = check_sticky(ctx);
   if (s != FG_OK) return s;
@@ -484,9 +485,28 @@ fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route*
   a.split_parts = ctx->split_parts;
   a.split_forced = ctx->split_tiles != 0;
   a.trace = ctx->p.trace; a.rb_time = ctx->p.rb_time; a.trace_cap = ctx->trace_cap;
+  a.two_stage = staging != nullptr;
+  a.self_shard = staging ? self_shard : -1;
+  if (staging)
+    for (int i = 0; i < c.n_shards; ++i) a.staging[i] = (uint16_t*)staging[i];
   ctx->last_grid = a.n_comm + a.n_gemm;
   ctx->last_m_pad = m_pad;
   return ctx->tile_n == 256 ? launch_fused<256>(a, stream) : launch_fused<128>(a, stream);
+}
+
+fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route* route, const void* W,
+                         void* gathered, void* out, uint32_t flags, hipStream_t stream) {
+  return gather_gemm_impl(ctx, shards, route, W, nullptr, -1, gathered, out, flags, stream);
+}
+
+fg_status fg_gather_gemm_staged(fg_ctx* ctx, const void* const* shards, const fg_route* route, const void* W,
+                                void* const* staging, int32_t self_shard, void* gathered, void* out,
+                                uint32_t flags, hipStream_t stream) {
+  if (!ctx || !staging) return FG_EINVAL;
+  if (self_shard < -1 || self_shard >= ctx->cfg.n_shards) return FG_EINVAL;
+  for (int i = 0; i < ctx->cfg.n_shards; ++i)
+    if (i != self_shard && !staging[i]) return FG_EINVAL;
+  return gather_gemm_impl(ctx, shards, route, W, staging, self_shard, gathered, out, flags, stream);
 }
 
 fg_status fg_barrier(fg_ctx* ctx, int32_t rounds, hipStream_t stream) {

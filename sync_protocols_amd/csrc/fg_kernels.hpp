@@ -83,6 +83,11 @@ struct FusedArgs {
                              // done; parts also: k loop done, partial stored, all parts counted
   long long* rb_time;        // TRACE: [rb_cap] time a row block's counter reached 128
   int trace_cap;
+  // two-stage dispatch: pushes into per-shard staging buffers, then a
+  // watermark-gated scatter into the gathered buffer
+  int two_stage;
+  int self_shard;            // shard read directly by the scatter (-1 = none)
+  uint16_t* staging[FG_MAX_SHARDS];   // [rs_cap][K] per shard, stream order
 };
 
 // Per-workgroup timing record (device clock ticks).
@@ -142,20 +147,23 @@ __device__ __forceinline__ void copy_rows(int RB, const FusedArgs& a, const uint
   else { if constexpr (UPR * 16 <= 32) copy_batch<UPR, 16>(a, sh_shard, g0, info, srow, row_bytes, lane); }
 }
 
-__device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+// Re-arm the other parity for the next iteration: nothing else touches it
+// during this kernel, and stream order publishes it to the next one.
+__device__ void arm_next(const FusedArgs& a) {
   const int cw = blockIdx.x;
-  const bool strict = a.flags & kStrict;
-
-  // Re-arm the other parity for the next iteration: nothing else touches it
-  // during this kernel, and stream order publishes it to the next one.
   for (int i = cw * kThreads + threadIdx.x; i < a.rb_cap; i += a.n_comm * kThreads)
     a.counter_nxt[(size_t)i * kCtr] = a.seed[i];
   for (int i = cw * kThreads + threadIdx.x; i < a.n_shards * a.chunk_cap; i += a.n_comm * kThreads)
     a.elect_nxt[i] = 0;
   for (int i = cw * kThreads + threadIdx.x; i < a.split_slots; i += a.n_comm * kThreads) a.skc_nxt[i] = 0;
   if (cw == 0 && threadIdx.x <= kXcds) a.tick_nxt[threadIdx.x * 64] = 0;
+}
+
+__device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cw = blockIdx.x;
+  const bool strict = a.flags & kStrict;
   if (a.flags & kGemmOnly) return;
 
   const int m_pad = __builtin_amdgcn_readfirstlane(a.desc[0]);
@@ -215,6 +223,154 @@ __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
         }
       }
       pending &= ~mask;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Two-stage dispatch ("PCIe sync protocols" §4 chunk watermark, §6 audit item
+// 2). Copy rows between per-row addresses: lane r < RB holds row r's source
+// and destination address (valid = false: a zero-sized descriptor, so loads
+// read 0 and stores are dropped).
+// ---------------------------------------------------------------------------
+template <int UPR, int RB>
+__device__ __forceinline__ void copy_batch_addr(uint64_t src, uint64_t dst, bool valid, uint32_t row_bytes, int lane) {
+  __amdgpu_buffer_rsrc_t rs[RB], rd[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    const bool v = readlane((int)valid, r) != 0;
+    const uint64_t sp = ((uint64_t)(uint32_t)readlane((int)(src >> 32), r) << 32) | (uint32_t)readlane((int)src, r);
+    const uint64_t dp = ((uint64_t)(uint32_t)readlane((int)(dst >> 32), r) << 32) | (uint32_t)readlane((int)dst, r);
+    rs[r] = buffer_rsrc((const void*)sp, v ? row_bytes : 0u);
+    rd[r] = buffer_rsrc((const void*)dp, v ? row_bytes : 0u);
+  }
+  v4i v[RB][UPR];
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int u = 0; u < UPR; ++u)
+      v[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rs[r], (uint32_t)(u * 64 + lane) * 16, 0, kPolSC1 | kPolNT);
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int u = 0; u < UPR; ++u) store16_coherent(rd[r], (uint32_t)(u * 64 + lane) * 16, v[r][u]);
+}
+
+template <int UPR>
+__device__ __forceinline__ void copy_rows_addr(int RB, uint64_t src, uint64_t dst, bool valid, uint32_t row_bytes,
+                                               int lane) {
+  if (RB == 1) copy_batch_addr<UPR, 1>(src, dst, valid, row_bytes, lane);
+  else if (RB == 2) { if constexpr (UPR * 2 <= 32) copy_batch_addr<UPR, 2>(src, dst, valid, row_bytes, lane); }
+  else if (RB == 4) { if constexpr (UPR * 4 <= 32) copy_batch_addr<UPR, 4>(src, dst, valid, row_bytes, lane); }
+  else if (RB == 8) { if constexpr (UPR * 8 <= 32) copy_batch_addr<UPR, 8>(src, dst, valid, row_bytes, lane); }
+  else { if constexpr (UPR * 16 <= 32) copy_batch_addr<UPR, 16>(src, dst, valid, row_bytes, lane); }
+}
+
+__device__ __forceinline__ void copy_addr(int upr, int RB, uint64_t src, uint64_t dst, bool valid,
+                                          uint32_t row_bytes, int lane) {
+  if (upr <= 1)       copy_rows_addr<1>(RB, src, dst, valid, row_bytes, lane);
+  else if (upr <= 2)  copy_rows_addr<2>(RB, src, dst, valid, row_bytes, lane);
+  else if (upr <= 4)  copy_rows_addr<4>(RB, src, dst, valid, row_bytes, lane);
+  else if (upr <= 8)  copy_rows_addr<8>(RB, src, dst, valid, row_bytes, lane);
+  else if (upr <= 16) copy_rows_addr<16>(RB, src, dst, valid, row_bytes, lane);
+  else                copy_rows_addr<32>(RB, src, dst, valid, row_bytes, lane);
+}
+
+// Stage 1, push: every wave takes batches i, i + waves, ... of RB consecutive
+// stream entries of one remote shard (RB divides 64, so a batch lies inside
+// one chunk), copies shard_s[src_row] -> staging[s][entry] with write-through
+// stores, releases, and adds its rows to the chunk's election count; the add
+// that completes the chunk stores seq into the chunk's slot (the watermark).
+// Stage 2, scatter: the batches of gathered rows in gathered-row order, as the
+// one-stage copy walks them; a remote row is read from staging after its
+// chunk's slot carries seq (one poll per distinct chunk of the batch), a row
+// of the self shard straight from the shard; then the rows are counted into
+// their 128-row block's counter. A wave scatters only after all its pushes,
+// so every watermark wait has a supplier that never waits.
+__device__ void comm_two_stage(const FusedArgs& a, const uint16_t* const* sh_shard, uint16_t* const* sh_stage,
+                               const int* sh_pbase) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool strict = a.flags & kStrict;
+  const bool verify = a.flags & kVerify;
+  const int RB = a.rows_per_batch;
+  const int upr = (a.K / 8 + 63) / 64;
+  const uint32_t row_bytes = (uint32_t)a.K * 2;
+  const int nw = a.n_comm * kWaves, wid = blockIdx.x * kWaves + wave;
+  const int n_push = sh_pbase[a.n_shards];
+  for (int it = wid; it < n_push; it += nw) {
+    int s = 0;
+    while (s + 1 < a.n_shards && sh_pbase[s + 1] <= it) ++s;
+    s = __builtin_amdgcn_readfirstlane(s);
+    const int n_s = __builtin_amdgcn_readfirstlane(a.stream_len[s]);
+    const int e0 = (it - sh_pbase[s]) * RB;
+    const bool valid = lane < RB && e0 + lane < n_s;
+    int srow = 0;
+    if (valid) srow = min(max(a.src_row[s * a.rs_cap + e0 + lane], 0), a.shard_rows - 1);
+    const uint64_t src = (uint64_t)(sh_shard[s] + (size_t)srow * a.K);
+    const uint64_t dst = (uint64_t)(sh_stage[s] + (size_t)(e0 + lane) * a.K);
+    copy_addr(upr, RB, src, dst, valid, row_bytes, lane);
+    release_coherent(strict);
+    const int n_done = __popcll(ballot(valid));
+    if (lane == 0 && n_done > 0) {
+      const int c = e0 / kChunk, ch = s * a.chunk_cap + c;
+      const int old = strict ? fetch_add_acq_rel(a.elect_cur + ch, n_done) : fetch_add_relaxed(a.elect_cur + ch, n_done);
+      const int expect = min(kChunk, n_s - kChunk * c);
+      if (old + n_done == expect) {
+        if (!((a.flags & kDropPublish) && ch == 0)) slot_publish(a.slot + ch, a.seq, strict);
+        if (verify) {
+          atomicAdd(a.pub_count + ch, 1);
+          atomicAdd(a.stats + ST_PUBLISHES, 1ull);
+        }
+      } else if (old + n_done > expect) {
+        raise_error(a.err, kErrProtocol, 0x10000000 | ch);
+      }
+    }
+  }
+  const int m_pad = __builtin_amdgcn_readfirstlane(a.desc[0]);
+  const int n_batches = m_pad / RB;
+  for (int b = wid; b < n_batches; b += nw) {
+    const int g0 = b * RB;
+    int info = -1, s = 0, i = 0;
+    if (lane < RB) {
+      info = inv_read(a.inv, g0 + lane, a.route_ver);
+      if (info >= 0) { s = info >> 24; i = info & 0xFFFFFF; }
+    }
+    // watermark waits: one poll per distinct remote chunk of the batch
+    const int chunk = (info >= 0 && s != a.self_shard) ? s * a.chunk_cap + i / kChunk : -1;
+    uint64_t pending = ballot(chunk >= 0);
+    int ok = 1;
+    while (pending) {
+      const int leader = __ffsll((long long)pending) - 1;
+      const int ch = readlane(chunk, leader);
+      if (lane == 0) {
+        uint32_t polls = 0;
+        ok = wait_ge(a.slot + ch, a.seq, now_ticks() + a.timeout_ticks, a.err, 0x30000000 | ch, &polls);
+        if (verify) atomicAdd(a.stats + ST_SLOT_POLLS, (unsigned long long)polls);
+      }
+      if (!readlane(ok, 0)) break;
+      pending &= ~ballot(chunk == ch);
+    }
+    if (!readlane(ok, 0)) break;
+    if (strict) acquire_agent();
+    uint64_t src = 0;
+    if (info >= 0) {
+      if (s == a.self_shard) {
+        const int srow = min(max(a.src_row[s * a.rs_cap + i], 0), a.shard_rows - 1);
+        src = (uint64_t)(sh_shard[s] + (size_t)srow * a.K);
+      } else {
+        src = (uint64_t)(sh_stage[s] + (size_t)i * a.K);
+      }
+    }
+    const uint64_t dst = (uint64_t)(a.gathered + (size_t)(g0 + lane) * a.K);
+    copy_addr(upr, RB, src, dst, info >= 0, row_bytes, lane);
+    release_coherent(strict);
+    const int n_real = __popcll(ballot(lane < RB && info >= 0));
+    if (lane == 0 && n_real > 0) {
+      const int rb = g0 / kRB;
+      const int old = fetch_add_relaxed(a.counter_cur + (size_t)rb * kCtr, n_real);
+      if (old + n_real > kRB) raise_error(a.err, kErrProtocol, rb);
+      if ((a.flags & kTrace) && old + n_real == kRB) a.rb_time[rb] = (long long)now_ticks();
     }
   }
 }
@@ -484,9 +640,27 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
     wt[WT_GATE] = 0; wt[WT_TILES] = 0; wt[WT_PARTS] = 0; wt[WT_GEMM_START] = 0; wt[WT_P] = 1;
   }
   if (blockIdx.x < a.n_comm) {
-    if (threadIdx.x < a.n_shards) sh_shard[threadIdx.x] = a.shards[threadIdx.x];
+    __shared__ uint16_t* sh_stage[FG_MAX_SHARDS];
+    __shared__ int sh_pbase[FG_MAX_SHARDS + 1];   // push batches before shard s (two-stage)
+    if (threadIdx.x < a.n_shards) {
+      sh_shard[threadIdx.x] = a.shards[threadIdx.x];
+      sh_stage[threadIdx.x] = a.staging[threadIdx.x];
+    }
+    if (a.two_stage && threadIdx.x == 0) {
+      int n = 0;
+      for (int s = 0; s < a.n_shards; ++s) {
+        sh_pbase[s] = n;
+        if (s != a.self_shard) n += (a.stream_len[s] + a.rows_per_batch - 1) / a.rows_per_batch;
+      }
+      sh_pbase[a.n_shards] = n;
+    }
     __syncthreads();
-    comm_role(a, sh_shard);
+    arm_next(a);
+    if (a.two_stage) {
+      if (!(a.flags & kGemmOnly)) comm_two_stage(a, sh_shard, sh_stage, sh_pbase);
+    } else {
+      comm_role(a, sh_shard);
+    }
     t_comm = (long long)now_ticks();
   }
   gemm_role<BN>(a, lds, sh, wt);

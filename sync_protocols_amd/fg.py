@@ -31,7 +31,7 @@ FAULT_DROP_PUBLISH = 1 << 10
 
 ROUTE_CONTIG, ROUTE_EXPLICIT, ROUTE_TOPK = 0, 1, 2
 
-EXPORTS = ("fg_init", "fg_gather_gemm", "fg_barrier", "fg_pingpong", "fg_stress", "fg_combine", "fg_litmus", "fg_stats",
+EXPORTS = ("fg_init", "fg_gather_gemm", "fg_gather_gemm_staged", "fg_barrier", "fg_pingpong", "fg_stress", "fg_combine", "fg_litmus", "fg_stats",
            "fg_views", "fg_capacity", "fg_destroy", "fg_strerror")
 
 
@@ -96,6 +96,8 @@ def load_library() -> C.CDLL:
     vp = C.c_void_p
     lib.fg_init.argtypes = [C.POINTER(FgConfig), C.c_int, C.POINTER(vp)]
     lib.fg_gather_gemm.argtypes = [vp, C.POINTER(vp), C.POINTER(FgRoute), vp, vp, vp, C.c_uint32, vp]
+    lib.fg_gather_gemm_staged.argtypes = [vp, C.POINTER(vp), C.POINTER(FgRoute), vp, C.POINTER(vp), C.c_int32,
+                                          vp, vp, C.c_uint32, vp]
     lib.fg_barrier.argtypes = [vp, C.c_int32, vp]
     lib.fg_pingpong.argtypes = [vp, C.c_int32, C.c_int32, vp]
     lib.fg_stress.argtypes = [vp, vp, vp, vp, C.c_uint32, vp]
@@ -179,6 +181,17 @@ class Context:
         self._keep = [arr, route]
         return self._lib.fg_gather_gemm(self._h, arr, C.byref(route) if route is not None else None,
                                         _ptr(w), _ptr(gathered), _ptr(out), flags, _stream_ptr(stream))
+
+    def gather_gemm_staged(self, shards, w, staging, gathered, out, *, self_shard: int = -1,
+                           route: FgRoute | None = None, flags: int = 0, stream=None) -> int:
+        """Two-stage dispatch; staging is a list of per-shard device tensors (None
+        allowed for self_shard). Returns the fg_status code."""
+        arr = (C.c_void_p * len(shards))(*[s.data_ptr() for s in shards])
+        st = (C.c_void_p * len(staging))(*[0 if t is None else t.data_ptr() for t in staging])
+        self._keep = [arr, st, route]
+        return self._lib.fg_gather_gemm_staged(self._h, arr, C.byref(route) if route is not None else None,
+                                               _ptr(w), st, self_shard, _ptr(gathered), _ptr(out), flags,
+                                               _stream_ptr(stream))
 
     def barrier(self, rounds: int = 1, stream=None) -> int:
         return self._lib.fg_barrier(self._h, rounds, _stream_ptr(stream))
