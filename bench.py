@@ -100,6 +100,7 @@ def setup_workload(name, torch, fg, W):
             dst = d.perm.reshape(S, R).contiguous().to(dev)
             route = fg.route_explicit([R] * S, src, dst, S * R, R)
         m_real = S * R
+        stream_len = [R] * S
         n_groups = 1
         max_rows = R
         info = dict(n_shards=S, rows_per_shard=R, M=m_real, K=K, N=N, gather=c["gather"])
@@ -115,12 +116,13 @@ def setup_workload(name, torch, fg, W):
         route = fg.route_topk(topk, c["tokens"], c["expert_base"])
         local = ((e.topk >= c["expert_base"]) & (e.topk < c["expert_base"] + c["n_local"]))
         m_real = int(local.sum())
+        stream_len = [int(x) for x in local.reshape(S, -1).sum(dim=1)]
         n_groups = c["n_local"]
         max_rows = c["tokens"] * min(c["topk"], c["n_local"])
         info = dict(n_shards=S, tokens_per_shard=c["tokens"], M=m_real, K=K, N=N, topk=c["topk"],
                     experts=c["n_experts"], local_experts=c["n_local"])
         inputs = dict(ep=e)
-    return dict(name=name, shards=shards, w=w, route=route, m_real=m_real, n_groups=n_groups,
+    return dict(name=name, shards=shards, w=w, route=route, m_real=m_real, stream_len=stream_len, n_groups=n_groups,
                 max_rows=max_rows, K=K, N=N, S=S, info=info, inputs=inputs, iters=c["iters"], cfg=c)
 
 
@@ -196,6 +198,53 @@ def cpu_baseline(wl, budget_s=12.0):
     return dict(value=round(flop / dt / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
                 sample=f"{steps} whole step(s) of the oracle (layout, gather of all rows, float64 contraction of "
                        f"{what} x K={K} x N={N}) in {dt:.1f} s; value = contraction FLOP / wall time")
+
+
+def two_stage_bench(args, wl, ctx, gathered, out, torch, fg):
+    """The two-stage dispatch (fg_gather_gemm_staged) on the same workload and
+    context, with shard 0 as the self shard: T_total and the copy roles alone
+    (push + scatter), each the mean of back-to-back steps between one event
+    pair; algorithmic copy bytes = push (2 x remote rows x K x 2) + scatter
+    (2 x M x K x 2)."""
+    S, K = wl["S"], wl["K"]
+    staging = [None if s == 0 else torch.empty(ctx.cfg.max_rows_per_shard, K, dtype=torch.bfloat16, device="cuda:0")
+               for s in range(S)]
+
+    def step(flags=0):
+        rc = ctx.gather_gemm_staged(wl["shards"], wl["w"], staging, gathered, out, self_shard=0, route=wl["route"],
+                                    flags=flags)
+        if rc != fg.OK:
+            raise RuntimeError(f"fg_gather_gemm_staged: {fg.strerror(rc)}")
+
+    def back_to_back(flags, n):
+        step(flags)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            step(flags)
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / n
+
+    for _ in range(3):
+        step()
+    n = max(10, args.steps)
+    Tt = back_to_back(0, n)
+    Tc = back_to_back(fg.CALL_COMM_ONLY, n)
+    st = ctx.stats()
+    if st.error_code:
+        raise RuntimeError(f"device error {st.error_code} id {st.error_id}")
+    M = wl["m_real"]
+    remote = M - wl["stream_len"][0]
+    copy_bytes = 2.0 * remote * K * 2 + 2.0 * M * K * 2
+    flop = 2.0 * M * K * wl["N"]
+    step()
+    torch.cuda.synchronize()
+    return {"self_shard": 0, "T_total_us": round(Tt, 2), "T_copy_alone_us": round(Tc, 2),
+            "TFLOPs": round(flop / (Tt * 1e-6) / 1e12, 2), "copy_bytes": copy_bytes,
+            "copy_GBps": round(copy_bytes / (Tc * 1e-6) / 1e9, 1)}
 
 
 def combine_bench(args, wl, ctx, gathered, out, torch, fg, W):
@@ -423,6 +472,7 @@ def main():
                             "us_per_iter_no_delay": round(statistics.median(t_nodelay) * 1000, 2),
                             "us_per_iter_delays_0_20us": round(statistics.median(t_delay) * 1000, 2),
                             "signals_per_s_no_delay": round(signals / (statistics.median(t_nodelay) * 1e-3), 0)}
+        result["two_stage"] = two_stage_bench(args, wl, ctx, gathered, out, torch, fg)
         result["combine"] = combine_bench(args, wl, ctx, gathered, out, torch, fg, W)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0").fill_(1)
