@@ -488,6 +488,141 @@ def simulate_two_stage(lay: Layout, state: ProtocolState, t: int, push_batches, 
     return TwoStageResult(state, staged, pubs, early_s, early_g, deferred)
 
 
+# ---------------------------------------------------------------------------
+# Streaming FIFO ring ("DeepEP FIFO pipeline": a bounded ring per channel, the
+# sender waits until tail - head < capacity, writes slot tail mod capacity and
+# advances tail; the receiver polls tail, consumes, and returns credit by
+# advancing head; the sender's last tail carries a finish flag packed with it).
+# Reading R28: each shard's stream of 64-row chunks is dealt to n_channels
+# rings (chunk c to ring c mod n_channels, in increasing c); each ring has one
+# producer and one consumer and ring_chunks chunk slots. The consumer scatters
+# a consumed chunk into the gathered buffer and counts its rows into the
+# seeded 128-row counters. A self shard is read straight from the shard.
+# ---------------------------------------------------------------------------
+
+RING_FINISH = 1 << 32
+
+
+def ring_chunks_of(lay: Layout, n_channels: int) -> list:
+    """chunks[s][k] = the chunk indices ring (s, k) carries, in order."""
+    out = []
+    for s in range(lay.n_shards):
+        n = -(-int(lay.stream_len[s]) // lay.chunk_rows)
+        out.append([list(range(k, n, n_channels)) for k in range(n_channels)])
+    return out
+
+
+def ring_state_after(lay: Layout, n_channels: int, t: int, self_shard: int = -1):
+    """(tail, head) words after t iterations, [2][S * n_channels] each, parity
+    double-buffered as in reading R4: iteration t leaves parity t & 1 with
+    tail = finish | chunks and head = chunks for every ring of a remote shard
+    (0 for the self shard's rings, which are never used) and re-arms the other
+    parity to 0."""
+    S = lay.n_shards
+    tail = np.zeros((2, S * n_channels), dtype=np.int64)
+    head = np.zeros((2, S * n_channels), dtype=np.int64)
+    if t >= 1:
+        ch = ring_chunks_of(lay, n_channels)
+        for s in range(S):
+            if s == self_shard:
+                continue
+            for k in range(n_channels):
+                tail[t & 1, s * n_channels + k] = RING_FINISH | len(ch[s][k])
+                head[t & 1, s * n_channels + k] = len(ch[s][k])
+    return tail, head
+
+
+@dataclasses.dataclass
+class RingResult:
+    gathered_rows: np.ndarray   # bool per gathered row: written by a consumer
+    counter: np.ndarray         # [n_rb] arrival counters after the iteration
+    tail: np.ndarray            # [S * n_channels]
+    head: np.ndarray
+    max_occupancy: int          # largest tail - head seen on any ring
+    overwrites: int             # a slot rewritten before its chunk was consumed
+    early_reads: int            # a consumer read a slot before its chunk was written
+    early_gates: int
+    steps: int
+
+
+def simulate_ring(lay: Layout, n_channels: int, ring_chunks: int, rng, self_shard: int = -1,
+                  credit_limit=None) -> RingResult:
+    """One iteration, one ring step at a time in a random order. A producer step
+    of ring r writes its next chunk j into slot j mod ring_chunks if
+    tail - head < credit_limit (the capacity unless a mistake is planted), then
+    sets tail = j + 1 (with the finish flag on the ring's last chunk, or at once
+    for a ring with no chunk). A consumer step reads chunk j from its slot if
+    tail > j, scatters its rows, counts them per 128-row block and sets
+    head = j + 1. Self-shard rings have no producer: their consumer reads the
+    shard directly. Raises if no step can run while work remains."""
+    cap = ring_chunks if credit_limit is None else credit_limit
+    S = lay.n_shards
+    ch = ring_chunks_of(lay, n_channels)
+    R = S * n_channels
+    tail = np.zeros(R, dtype=np.int64)
+    head = np.zeros(R, dtype=np.int64)
+    slot = {}                                   # (ring, slot index) -> chunk index written there
+    written_rows = np.zeros(lay.m_pad, dtype=bool)
+    counter = seeds(lay).astype(np.int64).copy()
+    real = real_rows(lay)
+    opened = np.zeros(lay.n_rb, dtype=bool)
+    occ = over = early = early_g = steps = 0
+    cons = np.zeros(R, dtype=np.int64)          # chunks consumed per ring
+    for s in range(S):
+        for k in range(n_channels):
+            r = s * n_channels + k
+            if s != self_shard and not ch[s][k]:
+                tail[r] = RING_FINISH
+    while True:
+        moves = []
+        for r in range(R):
+            s, k = divmod(r, n_channels)
+            n = len(ch[s][k])
+            if s != self_shard and (tail[r] & 0xFFFFFFFF) < n and (tail[r] & 0xFFFFFFFF) - head[r] < cap:
+                moves.append(("p", r))
+            if cons[r] < n and (s == self_shard or (tail[r] & 0xFFFFFFFF) > cons[r]):
+                moves.append(("c", r))
+        if not moves:
+            break
+        kind, r = moves[int(rng.integers(len(moves)))]
+        s, k = divmod(r, n_channels)
+        n = len(ch[s][k])
+        steps += 1
+        if kind == "p":
+            j = int(tail[r] & 0xFFFFFFFF)
+            key = (r, j % ring_chunks)
+            if key in slot and slot[key] >= cons[r]:
+                over += 1                        # that chunk was not consumed yet
+            slot[key] = j
+            tail[r] = (j + 1) | (RING_FINISH if j + 1 == n else 0)
+            occ = max(occ, j + 1 - int(head[r]))
+            continue
+        j = int(cons[r])
+        if s != self_shard and slot.get((r, j % ring_chunks)) != j:
+            early += 1
+        c = ch[s][k][j]
+        lo, hi = c * lay.chunk_rows, min(int(lay.stream_len[s]), (c + 1) * lay.chunk_rows)
+        per_rb = {}
+        for i in range(lo, hi):
+            d = int(lay.dst_row[s][i])
+            written_rows[d] = True
+            per_rb[d // lay.row_block] = per_rb.get(d // lay.row_block, 0) + 1
+        for rb, m in per_rb.items():
+            counter[rb] += m
+            if counter[rb] == lay.row_block and not opened[rb]:
+                opened[rb] = True
+                blk = slice(rb * lay.row_block, (rb + 1) * lay.row_block)
+                if np.any(real[blk] & ~written_rows[blk]):
+                    early_g += 1
+        cons[r] = j + 1
+        if s != self_shard:
+            head[r] = j + 1
+    done = all(cons[s * n_channels + k] == len(ch[s][k]) for s in range(S) for k in range(n_channels))
+    if not done:
+        raise RuntimeError("the ring stalled with chunks left")
+    return RingResult(written_rows, counter, tail, head, occ, over, early, early_g, steps)
+
+
 def election_brute_force(parts) -> int:
     """A chunk of sum(parts) rows finished by len(parts) waves, wave w adding
     parts[w]: over every completion order, count the adds that see

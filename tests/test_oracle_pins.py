@@ -562,3 +562,48 @@ def test_two_stage_missing_push_never_releases_the_scatter():
     events = [("push", b) for b in range(len(pb1))] + [("scatter", b) for b in range(len(sb))]
     r = O.simulate_two_stage(lay, O.state_after_two_stage(lay, 0, cap, 0), 1, pb1, sb, events, self_shard=0)
     assert r.early_scatter == 0 and np.all(r.state.counter[1] == lay.row_block)
+
+
+# ------------------------------------------------------------ streaming FIFO ring
+
+@pytest.mark.parametrize("n_channels,ring_chunks,self_shard", [(1, 1, -1), (2, 1, 0), (3, 2, -1), (2, 3, 2)])
+def test_ring_simulation_matches_closed_form(n_channels, ring_chunks, self_shard):
+    rng = np.random.default_rng(60 + 7 * n_channels + ring_chunks)
+    for lay in _layouts_small():
+        if self_shard >= lay.n_shards:
+            continue
+        for trial in range(3):
+            r = O.simulate_ring(lay, n_channels, ring_chunks, rng, self_shard)
+            assert r.overwrites == 0 and r.early_reads == 0 and r.early_gates == 0
+            assert r.max_occupancy <= ring_chunks
+            assert np.array_equal(r.gathered_rows, O.real_rows(lay))
+            assert np.all(r.counter == lay.row_block)
+            tail, head = O.ring_state_after(lay, n_channels, 1, self_shard)
+            assert np.array_equal(r.tail, tail[1]) and np.array_equal(r.head, head[1])
+            assert not tail[0].any() and not head[0].any()
+    # every chunk of a remote shard travels through exactly one ring, in order
+    lay = list(_layouts_small())[2]
+    ch = O.ring_chunks_of(lay, n_channels)
+    for s in range(lay.n_shards):
+        allc = sorted(c for k in range(n_channels) for c in ch[s][k])
+        assert allc == list(range(-(-int(lay.stream_len[s]) // lay.chunk_rows)))
+        for k in range(n_channels):
+            assert ch[s][k] == sorted(ch[s][k]) and all(c % n_channels == k for c in ch[s][k])
+
+
+def test_ring_planted_credit_mistake_overwrites():
+    lay = O.layout_contiguous(2, 200, row_block=16, chunk_rows=8)
+    rng = np.random.default_rng(71)
+    over = sum(O.simulate_ring(lay, 2, 2, rng, credit_limit=3).overwrites for _ in range(10))
+    assert over > 0, "one credit too many must let a producer overwrite an unconsumed slot"
+    with pytest.raises(RuntimeError):
+        O.simulate_ring(lay, 2, 0, rng)     # no slot: the producer never gets a credit
+
+
+def test_ring_empty_rings_finish_at_once():
+    lay = O.layout_contiguous(2, 10, row_block=16, chunk_rows=8)     # 2 chunks per shard, 4 rings per shard
+    rng = np.random.default_rng(72)
+    r = O.simulate_ring(lay, 4, 1, rng)
+    tail, head = O.ring_state_after(lay, 4, 1)
+    assert np.array_equal(r.tail, tail[1])
+    assert sum(1 for x in tail[1] if x == O.RING_FINISH) == 4        # rings 2, 3 of each shard carry nothing
