@@ -199,6 +199,10 @@ typedef struct {
   const int32_t* src_k;         /* [n_shards][max_rows_per_shard] top-k position of each stream entry */
   const int32_t* tok_first;     /* [n_shards][max_rows_per_shard + 1] first stream entry of each token;
                                    entry [tokens] = the stream length */
+  /* FIFO rings (fg_gather_gemm_ring), parity double-buffered: */
+  const uint64_t* ring_tail;    /* [2][ring_cap][32], value at [..][r][0] = finish << 32 | tail */
+  const int32_t* ring_head;     /* [2][ring_cap][FG_COUNTER_STRIDE], value at [..][r][0] */
+  int32_t ring_cap, reserved2;  /* ring_cap: rings the copy workgroups can serve (n_comm_wg / 2) */
 } fg_views_t;
 
 /* Create a context on `hip_device`: validates the configuration, allocates and
@@ -253,6 +257,32 @@ fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route*
 fg_status fg_gather_gemm_staged(fg_ctx* ctx, const void* const* shards, const fg_route* route,
                                 const void* W, void* const* staging, int32_t self_shard, void* gathered,
                                 void* out, uint32_t flags, hipStream_t stream);
+
+/* The same iteration as fg_gather_gemm_staged with bounded staging memory: a
+ * streaming FIFO ring per (shard, channel) ("DeepEP FIFO pipeline": head/tail
+ * credits, slot = index mod capacity, a finish flag packed beside the tail).
+ * Shard s's stream of 64-row chunks is dealt to n_channels rings, chunk c to
+ * ring c mod n_channels. Copy workgroup r produces ring r: it writes the ring's
+ * j-th chunk shards[s][src_row] rows into slot j mod ring_chunks once the
+ * consumer's head shows chunk j - ring_chunks drained, then stores the tail
+ * (j + 1, with the finish bit on the last chunk). Copy workgroup rings + r
+ * consumes it: it waits for the tail, scatters the chunk into the gathered
+ * buffer, counts the rows into the seeded 128-row counters and advances the
+ * head. Rings of self_shard have no producer; their consumer reads the shard.
+ * The compute role gates on the counters as in fg_gather_gemm.
+ *   ring:        device bf16 [n_shards][n_channels][ring_chunks][64][K]
+ *                (fg_ring_bytes gives its size)
+ *   n_channels:  rings per shard, n_shards * n_channels <= n_comm_wg / 2
+ *   ring_chunks: 64-row slots per ring, >= 1
+ *   self_shard:  -1 (every shard is remote) or 0..n_shards-1
+ * Other arguments, flags and errors as fg_gather_gemm; FG_EINVAL when the
+ * rings need more copy workgroups than the context has. */
+fg_status fg_gather_gemm_ring(fg_ctx* ctx, const void* const* shards, const fg_route* route, const void* W,
+                              void* ring, int32_t n_channels, int32_t ring_chunks, int32_t self_shard,
+                              void* gathered, void* out, uint32_t flags, hipStream_t stream);
+
+/* Bytes of the ring buffer fg_gather_gemm_ring needs for this configuration. */
+fg_status fg_ring_bytes(const fg_config* cfg, int32_t n_channels, int32_t ring_chunks, int64_t* bytes);
 
 /* `rounds` consecutive all-rank barriers over n_shards virtual ranks in one
  * kernel ("PCIe sync protocols" §2): rank i's lane j stores bseq into

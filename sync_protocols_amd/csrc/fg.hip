@@ -65,6 +65,8 @@ struct Plane {
   int* celect;
   int* cpub;
   int* litmus;     // message-passing litmus test: 16 KB block, flag, ready, stale count
+  unsigned long long* rtail;   // [2][ring_cap][kRingTailStride] FIFO ring tails (finish << 32 | tail)
+  int* rhead;                  // [2][ring_cap][kCtr] FIFO ring heads
 };
 
 }  // namespace
@@ -86,6 +88,7 @@ struct fg_ctx {
   long long litmus_words = 0;
   int topk_rows = 0, topk_k = 0;   // tokens per shard and k of the last TOPK route
   int combine_wg = 0;
+  int ring_cap = 0;            // rings the copy workgroups can serve (a producer and a consumer each)
   uint32_t route_ver = 0;
   int route_wg_cap = 0;
   fg_status sticky = FG_OK;
@@ -340,6 +343,9 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
                o_spub = take((size_t)ctx->s_slots * 4), o_srck = take(nrs * 4),
                o_tokf = take((size_t)S * (cfg->max_rows_per_shard + 1) * 4), o_cslot = take(nch * kCombStride * 4),
                o_celect = take(2 * nch * kCombStride * 4), o_cpub = take(nch * 4), o_lit = take(kLitmusBytes + 768);
+  ctx->ring_cap = std::max(1, ctx->n_comm / 2);
+  const size_t o_rtail = take(2 * (size_t)ctx->ring_cap * kRingTailStride * 8),
+               o_rhead = take(2 * (size_t)ctx->ring_cap * kCtr * 4);
   if (hipMalloc(&ctx->plane_mem, off) != hipSuccess) { delete ctx; return FG_ENOMEM; }
   if (hipMemset(ctx->plane_mem, 0, off) != hipSuccess) { (void)hipFree(ctx->plane_mem); delete ctx; return FG_EHIP; }
   char* b = ctx->plane_mem;
@@ -357,6 +363,7 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
   p.s_pub = (int*)(b + o_spub);
   p.src_k = (int*)(b + o_srck); p.tok_first = (int*)(b + o_tokf); p.cslot = (int*)(b + o_cslot);
   p.celect = (int*)(b + o_celect); p.cpub = (int*)(b + o_cpub); p.litmus = (int*)(b + o_lit);
+  p.rtail = (unsigned long long*)(b + o_rtail); p.rhead = (int*)(b + o_rhead);
   if (hipHostMalloc((void**)&ctx->host_status, 64, hipHostMallocCoherent) != hipSuccess) {
     (void)hipFree(ctx->plane_mem); delete ctx; return FG_ENOMEM;
   }
@@ -382,9 +389,14 @@ fg_status fg_destroy(fg_ctx* ctx) {
   return FG_OK;
 }
 
+struct RingCall {
+  void* ring = nullptr;
+  int n_channels = 0, ring_chunks = 0;
+};
+
 static fg_status gather_gemm_impl(fg_ctx* ctx, const void* const* shards, const fg_route* route, const void* W,
                                   void* const* staging, int self_shard, void* gathered, void* out, uint32_t flags,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, const RingCall& rc = RingCall()) {
   if (!ctx) return FG_EINVAL;
   fg_status s = check_sticky(ctx);
   if (s != FG_OK) return s;
@@ -463,7 +475,7 @@ static fg_status gather_gemm_impl(fg_ctx* ctx, const void* const* shards, const 
   a.elect_nxt = ctx->p.elect + (size_t)nxt * c.n_shards * ctx->chunk_cap;
   a.pub_count = ctx->p.pub_count; a.seed = ctx->p.seed; a.inv = ctx->p.inv; a.route_ver = ctx->route_ver;
   a.group_of_rb = ctx->p.group_of_rb;
-  a.src_row = ctx->p.src_row; a.stream_len = ctx->p.stream_len; a.desc = ctx->p.desc; a.slab = ctx->p.slab; a.gslab = ctx->p.gslab; a.stats = ctx->p.stats;
+  a.src_row = ctx->p.src_row; a.dst_row = ctx->p.dst_row; a.stream_len = ctx->p.stream_len; a.desc = ctx->p.desc; a.slab = ctx->p.slab; a.gslab = ctx->p.gslab; a.stats = ctx->p.stats;
   a.wgtime = ctx->p.wgtime; a.err = sink(ctx); a.seq = ctx->seq;
   a.n_comm = ctx->n_comm; a.n_gemm = ctx->n_gemm;
   // rows per communication batch: matches the copy template chosen on the
@@ -486,7 +498,16 @@ static fg_status gather_gemm_impl(fg_ctx* ctx, const void* const* shards, const 
   a.split_forced = ctx->split_tiles != 0;
   a.trace = ctx->p.trace; a.rb_time = ctx->p.rb_time; a.trace_cap = ctx->trace_cap;
   a.two_stage = staging != nullptr;
-  a.self_shard = staging ? self_shard : -1;
+  a.self_shard = (staging || rc.ring) ? self_shard : -1;
+  a.ring_mode = rc.ring != nullptr;
+  a.ring = (uint16_t*)rc.ring;
+  a.n_channels = rc.ring ? rc.n_channels : 1;
+  a.ring_chunks = rc.ring ? rc.ring_chunks : 1;
+  a.ring_cap = ctx->ring_cap;
+  a.rtail_cur = ctx->p.rtail + (size_t)cur * ctx->ring_cap * kRingTailStride;
+  a.rtail_nxt = ctx->p.rtail + (size_t)nxt * ctx->ring_cap * kRingTailStride;
+  a.rhead_cur = ctx->p.rhead + (size_t)cur * ctx->ring_cap * kCtr;
+  a.rhead_nxt = ctx->p.rhead + (size_t)nxt * ctx->ring_cap * kCtr;
   if (staging)
     for (int i = 0; i < c.n_shards; ++i) a.staging[i] = (uint16_t*)staging[i];
   ctx->last_grid = a.n_comm + a.n_gemm;
@@ -507,6 +528,26 @@ fg_status fg_gather_gemm_staged(fg_ctx* ctx, const void* const* shards, const fg
   for (int i = 0; i < ctx->cfg.n_shards; ++i)
     if (i != self_shard && !staging[i]) return FG_EINVAL;
   return gather_gemm_impl(ctx, shards, route, W, staging, self_shard, gathered, out, flags, stream);
+}
+
+fg_status fg_ring_bytes(const fg_config* cfg, int32_t n_channels, int32_t ring_chunks, int64_t* bytes) {
+  if (!config_ok(cfg) || !bytes || n_channels < 1 || ring_chunks < 1) return FG_EINVAL;
+  *bytes = (int64_t)cfg->n_shards * n_channels * ring_chunks * FG_CHUNK_ROWS * cfg->K * 2;
+  return FG_OK;
+}
+
+fg_status fg_gather_gemm_ring(fg_ctx* ctx, const void* const* shards, const fg_route* route, const void* W,
+                              void* ring, int32_t n_channels, int32_t ring_chunks, int32_t self_shard,
+                              void* gathered, void* out, uint32_t flags, hipStream_t stream) {
+  if (!ctx || !ring || n_channels < 1 || ring_chunks < 1) return FG_EINVAL;
+  if (self_shard < -1 || self_shard >= ctx->cfg.n_shards) return FG_EINVAL;
+  // a producer and a consumer copy workgroup per ring
+  if ((long long)ctx->cfg.n_shards * n_channels > ctx->ring_cap) return FG_EINVAL;
+  RingCall rc;
+  rc.ring = ring;
+  rc.n_channels = n_channels;
+  rc.ring_chunks = ring_chunks;
+  return gather_gemm_impl(ctx, shards, route, W, nullptr, self_shard, gathered, out, flags, stream, rc);
 }
 
 fg_status fg_barrier(fg_ctx* ctx, int32_t rounds, hipStream_t stream) {
@@ -709,6 +750,7 @@ fg_status fg_views(fg_ctx* ctx, fg_views_t* v) {
   v->desc = p.desc; v->slab = p.slab; v->group_slab = p.gslab;
   v->combine_slot = p.cslot; v->combine_elect = p.celect; v->combine_pub = p.cpub; v->src_k = p.src_k;
   v->tok_first = p.tok_first;
+  v->ring_tail = (const uint64_t*)p.rtail; v->ring_head = p.rhead; v->ring_cap = ctx->ring_cap;
   return FG_OK;
 }
 

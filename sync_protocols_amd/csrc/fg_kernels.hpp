@@ -55,6 +55,7 @@ struct FusedArgs {
   uint32_t route_ver;
   const int* group_of_rb;
   const int* src_row;
+  const int* dst_row;        // [S][rs_cap] gathered row of each stream entry
   const int* stream_len;
   const int* desc;           // [0] = m_pad of this iteration, [1] = number of row slabs, [2] = groups
   const int* slab;           // [n_slabs] row slab: first row | 1 if the slab has 128 rows (else 256)
@@ -88,7 +89,18 @@ struct FusedArgs {
   int two_stage;
   int self_shard;            // shard read directly by the scatter (-1 = none)
   uint16_t* staging[FG_MAX_SHARDS];   // [rs_cap][K] per shard, stream order
+  // streaming FIFO ring: n_channels rings per shard of ring_chunks 64-row slots
+  int ring_mode;
+  int n_channels, ring_chunks, ring_cap;
+  uint16_t* ring;            // [S][n_channels][ring_chunks][64][K]
+  unsigned long long* rtail_cur;   // [ring_cap][kRingTailStride]: finish << 32 | tail
+  unsigned long long* rtail_nxt;
+  int* rhead_cur;            // [ring_cap][kCtr]
+  int* rhead_nxt;
 };
+
+constexpr int kRingTailStride = 32;                    // u64 words per tail (one 256-byte line)
+constexpr unsigned long long kRingFinish = 1ull << 32;
 
 // Per-workgroup timing record (device clock ticks).
 // WT_CLK0 / WT_CLK1: shader-clock counter (s_memtime) at start and end, for the
@@ -157,6 +169,10 @@ __device__ void arm_next(const FusedArgs& a) {
     a.elect_nxt[i] = 0;
   for (int i = cw * kThreads + threadIdx.x; i < a.split_slots; i += a.n_comm * kThreads) a.skc_nxt[i] = 0;
   if (cw == 0 && threadIdx.x <= kXcds) a.tick_nxt[threadIdx.x * 64] = 0;
+  for (int i = cw * kThreads + threadIdx.x; i < a.ring_cap; i += a.n_comm * kThreads) {
+    a.rtail_nxt[(size_t)i * kRingTailStride] = 0;
+    a.rhead_nxt[(size_t)i * kCtr] = 0;
+  }
 }
 
 __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
@@ -372,6 +388,160 @@ __device__ void comm_two_stage(const FusedArgs& a, const uint16_t* const* sh_sha
       if (old + n_real > kRB) raise_error(a.err, kErrProtocol, rb);
       if ((a.flags & kTrace) && old + n_real == kRB) a.rb_time[rb] = (long long)now_ticks();
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming FIFO ring ("DeepEP FIFO pipeline": head/tail credits, slot = index
+// mod capacity, finish flag packed beside the tail). Ring r = (shard s =
+// r / n_channels, channel k = r % n_channels) carries the 64-row chunks
+// c = k, k + n_channels, ... of shard s's stream. Copy workgroup r is its
+// producer, copy workgroup rings + r its consumer; both walk the ring's chunks
+// in order, so the producer of chunk j waits only on the consumer of chunk
+// j - ring_chunks and the consumer of chunk j only on the producer of chunk j.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int ring_chunk_count(const FusedArgs& a, int s, int k) {
+  const int n_chunks = (a.stream_len[s] + kChunk - 1) / kChunk;
+  return n_chunks > k ? (n_chunks - k + a.n_channels - 1) / a.n_channels : 0;
+}
+
+__device__ void ring_producer(const FusedArgs& a, const uint16_t* const* sh_shard, int r, int* sh) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool strict = a.flags & kStrict;
+  const int s = r / a.n_channels, k = r - s * a.n_channels;
+  if (s == a.self_shard) return;
+  const int n_s = __builtin_amdgcn_readfirstlane(a.stream_len[s]);
+  const int n_j = __builtin_amdgcn_readfirstlane(ring_chunk_count(a, s, k));
+  unsigned long long* tail = a.rtail_cur + (size_t)r * kRingTailStride;
+  if (n_j == 0) {
+    if (threadIdx.x == 0) __hip_atomic_store(tail, kRingFinish, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const int RB = a.rows_per_batch;
+  const int upr = (a.K / 8 + 63) / 64;
+  const uint32_t row_bytes = (uint32_t)a.K * 2;
+  const uint16_t* ring = a.ring + (size_t)r * a.ring_chunks * kChunk * a.K;
+  constexpr int kRowsPerWave = kChunk / kWaves;
+  for (int j = 0; j < n_j; ++j) {
+    if (j >= a.ring_chunks) {
+      // credit: the consumer has drained chunk j - ring_chunks from this slot
+      if (threadIdx.x == 0) {
+        uint32_t polls = 0;
+        sh[0] = wait_ge(a.rhead_cur + (size_t)r * kCtr, j - a.ring_chunks + 1, now_ticks() + a.timeout_ticks, a.err,
+                        0x72000000 | r, &polls);
+      }
+      __syncthreads();
+      const int ok = sh[0];
+      __syncthreads();
+      if (!ok) return;
+    }
+    const int c = k + j * a.n_channels;
+    const uint16_t* slot = ring + (size_t)(j % a.ring_chunks) * kChunk * a.K;
+    for (int b0 = 0; b0 < kRowsPerWave; b0 += RB) {
+      const int row = wave * kRowsPerWave + b0 + lane;      // row of the chunk, lane < RB
+      const int e = c * kChunk + row;
+      const bool valid = lane < RB && b0 + lane < kRowsPerWave && e < n_s;
+      int srow = 0;
+      if (valid) srow = min(max(a.src_row[s * a.rs_cap + e], 0), a.shard_rows - 1);
+      const uint64_t src = (uint64_t)(sh_shard[s] + (size_t)srow * a.K);
+      const uint64_t dst = (uint64_t)(slot + (size_t)min(row, kChunk - 1) * a.K);
+      copy_addr(upr, RB, src, dst, valid, row_bytes, lane);
+    }
+    release_coherent(strict);
+    __syncthreads();      // every wave's rows of the chunk are acknowledged
+    if (threadIdx.x == 0) {
+      const unsigned long long w = (unsigned long long)(j + 1) | (j + 1 == n_j ? kRingFinish : 0ull);
+      if (strict) __hip_atomic_store(tail, w, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      else __hip_atomic_store(tail, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Bounded wait on a ring tail: returns 1 once tail > j, 2 once the finish flag
+// is set with tail == j (the ring is drained), 0 on timeout / error elsewhere.
+__device__ __forceinline__ int wait_tail(const unsigned long long* p, int j, uint64_t deadline, const ErrorSink& e,
+                                         int id) {
+  int lvl = 0;
+  uint32_t n = 0;
+  while (true) {
+    const unsigned long long v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ++n;
+    if ((int)(v & 0xFFFFFFFFull) > j) return 1;
+    if ((v & kRingFinish) && (int)(v & 0xFFFFFFFFull) == j) return 2;
+    if ((n & 15) == 0) {
+      if (now_ticks() > deadline) { raise_error(e, kErrTimeout, id); return 0; }
+      if (error_raised(e)) return 0;
+    }
+    backoff(lvl, kBackoffShort);
+  }
+}
+
+__device__ void ring_consumer(const FusedArgs& a, const uint16_t* const* sh_shard, int r, int* sh) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool strict = a.flags & kStrict;
+  const int s = r / a.n_channels, k = r - s * a.n_channels;
+  const bool self = s == a.self_shard;
+  const int n_s = __builtin_amdgcn_readfirstlane(a.stream_len[s]);
+  const int n_j = __builtin_amdgcn_readfirstlane(ring_chunk_count(a, s, k));
+  const unsigned long long* tail = a.rtail_cur + (size_t)r * kRingTailStride;
+  const int RB = a.rows_per_batch;
+  const int upr = (a.K / 8 + 63) / 64;
+  const uint32_t row_bytes = (uint32_t)a.K * 2;
+  const uint16_t* ring = a.ring + (size_t)r * a.ring_chunks * kChunk * a.K;
+  constexpr int kRowsPerWave = kChunk / kWaves;
+  for (int j = 0;; ++j) {
+    if (self) {
+      if (j >= n_j) return;
+    } else {
+      if (threadIdx.x == 0) sh[0] = wait_tail(tail, j, now_ticks() + a.timeout_ticks, a.err, 0x73000000 | r);
+      __syncthreads();
+      const int st = sh[0];
+      __syncthreads();
+      if (st != 1) return;                 // drained (2) or failed (0)
+      if (j >= n_j) {                      // more chunks than the stream has
+        if (threadIdx.x == 0) raise_error(a.err, kErrProtocol, 0x74000000 | r);
+        return;
+      }
+      if (strict) acquire_agent();
+    }
+    const int c = k + j * a.n_channels;
+    const uint16_t* slot = ring + (size_t)(j % a.ring_chunks) * kChunk * a.K;
+    for (int b0 = 0; b0 < kRowsPerWave; b0 += RB) {
+      const int row = wave * kRowsPerWave + b0 + lane;
+      const int e = c * kChunk + row;
+      const bool valid = lane < RB && b0 + lane < kRowsPerWave && e < n_s;
+      int d = -1;
+      uint64_t src = 0;
+      if (valid) {
+        d = a.dst_row[s * a.rs_cap + e];
+        if (d < 0 || d >= a.m_pad_cap) d = -1;
+        if (self) src = (uint64_t)(sh_shard[s] + (size_t)min(max(a.src_row[s * a.rs_cap + e], 0), a.shard_rows - 1) * a.K);
+        else src = (uint64_t)(slot + (size_t)row * a.K);
+      }
+      const uint64_t dst = (uint64_t)(a.gathered + (size_t)max(d, 0) * a.K);
+      copy_addr(upr, RB, src, dst, d >= 0, row_bytes, lane);
+      release_coherent(strict);
+      // arrivals: one add per distinct row block of the batch
+      const int rb = d >= 0 ? d / kRB : -1;
+      uint64_t pending = ballot(rb >= 0);
+      while (pending) {
+        const int leader = __ffsll((long long)pending) - 1;
+        const int blk = readlane(rb, leader);
+        const uint64_t mask = ballot(rb == blk) & pending;
+        if (lane == leader) {
+          const int cnt = __popcll(mask);
+          const int old = fetch_add_relaxed(a.counter_cur + (size_t)blk * kCtr, cnt);
+          if (old + cnt > kRB) raise_error(a.err, kErrProtocol, blk);
+          if ((a.flags & kTrace) && old + cnt == kRB) a.rb_time[blk] = (long long)now_ticks();
+        }
+        pending &= ~mask;
+      }
+    }
+    __syncthreads();      // every wave has read its rows of the slot
+    if (!self && threadIdx.x == 0)
+      __hip_atomic_store(a.rhead_cur + (size_t)r * kCtr, j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -656,7 +826,14 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
     }
     __syncthreads();
     arm_next(a);
-    if (a.two_stage) {
+    const int rings = a.n_shards * a.n_channels;
+    if (a.ring_mode) {
+      __shared__ int sh_ring[2];
+      if (!(a.flags & kGemmOnly)) {
+        if ((int)blockIdx.x < rings) ring_producer(a, sh_shard, blockIdx.x, sh_ring);
+        else if ((int)blockIdx.x < 2 * rings) ring_consumer(a, sh_shard, blockIdx.x - rings, sh_ring);
+      }
+    } else if (a.two_stage) {
       if (!(a.flags & kGemmOnly)) comm_two_stage(a, sh_shard, sh_stage, sh_pbase);
     } else {
       comm_role(a, sh_shard);

@@ -31,7 +31,7 @@ FAULT_DROP_PUBLISH = 1 << 10
 
 ROUTE_CONTIG, ROUTE_EXPLICIT, ROUTE_TOPK = 0, 1, 2
 
-EXPORTS = ("fg_init", "fg_gather_gemm", "fg_gather_gemm_staged", "fg_barrier", "fg_pingpong", "fg_stress", "fg_combine", "fg_litmus", "fg_stats",
+EXPORTS = ("fg_init", "fg_gather_gemm", "fg_gather_gemm_staged", "fg_gather_gemm_ring", "fg_ring_bytes", "fg_barrier", "fg_pingpong", "fg_stress", "fg_combine", "fg_litmus", "fg_stats",
            "fg_views", "fg_capacity", "fg_destroy", "fg_strerror")
 
 
@@ -73,7 +73,8 @@ class FgViews(C.Structure):
         ("wg_time", C.c_void_p), ("trace", C.c_void_p), ("rb_time", C.c_void_p), ("grid", C.c_int32),
         ("trace_cap", C.c_int32), ("wall_khz", C.c_int64), ("desc", C.c_void_p), ("slab", C.c_void_p),
         ("group_slab", C.c_void_p), ("combine_slot", C.c_void_p), ("combine_elect", C.c_void_p),
-        ("combine_pub", C.c_void_p), ("src_k", C.c_void_p), ("tok_first", C.c_void_p)]
+        ("combine_pub", C.c_void_p), ("src_k", C.c_void_p), ("tok_first", C.c_void_p),
+        ("ring_tail", C.c_void_p), ("ring_head", C.c_void_p), ("ring_cap", C.c_int32), ("reserved2", C.c_int32)]
 
 
 class FgError(RuntimeError):
@@ -98,6 +99,9 @@ def load_library() -> C.CDLL:
     lib.fg_gather_gemm.argtypes = [vp, C.POINTER(vp), C.POINTER(FgRoute), vp, vp, vp, C.c_uint32, vp]
     lib.fg_gather_gemm_staged.argtypes = [vp, C.POINTER(vp), C.POINTER(FgRoute), vp, C.POINTER(vp), C.c_int32,
                                           vp, vp, C.c_uint32, vp]
+    lib.fg_gather_gemm_ring.argtypes = [vp, C.POINTER(vp), C.POINTER(FgRoute), vp, vp, C.c_int32, C.c_int32,
+                                        C.c_int32, vp, vp, C.c_uint32, vp]
+    lib.fg_ring_bytes.argtypes = [C.POINTER(FgConfig), C.c_int32, C.c_int32, C.POINTER(C.c_int64)]
     lib.fg_barrier.argtypes = [vp, C.c_int32, vp]
     lib.fg_pingpong.argtypes = [vp, C.c_int32, C.c_int32, vp]
     lib.fg_stress.argtypes = [vp, vp, vp, vp, C.c_uint32, vp]
@@ -141,6 +145,12 @@ def make_config(n_shards, max_rows_per_shard, K, N, n_groups=1, n_comm_wg=0, n_g
                 copy_rows=0, combine_wg=0) -> FgConfig:
     return FgConfig(n_shards, max_rows_per_shard, K, N, n_groups, n_comm_wg, n_gemm_wg, tile_n, timeout_ns,
                     stress[0], stress[1], stress[2], split_parts, split_tiles, tile_order, copy_rows, combine_wg)
+
+
+def ring_bytes(cfg: FgConfig, n_channels: int, ring_chunks: int) -> int:
+    out = C.c_int64(0)
+    _check(load_library().fg_ring_bytes(C.byref(cfg), n_channels, ring_chunks, C.byref(out)), "fg_ring_bytes")
+    return out.value
 
 
 def capacity(cfg: FgConfig) -> int:
@@ -192,6 +202,16 @@ class Context:
         return self._lib.fg_gather_gemm_staged(self._h, arr, C.byref(route) if route is not None else None,
                                                _ptr(w), st, self_shard, _ptr(gathered), _ptr(out), flags,
                                                _stream_ptr(stream))
+
+    def gather_gemm_ring(self, shards, w, ring, gathered, out, *, n_channels: int, ring_chunks: int,
+                         self_shard: int = -1, route: FgRoute | None = None, flags: int = 0, stream=None) -> int:
+        """Dispatch through bounded FIFO rings (ring: a device tensor of at least
+        ring_bytes(...) bytes). Returns the fg_status code."""
+        arr = (C.c_void_p * len(shards))(*[s.data_ptr() for s in shards])
+        self._keep = [arr, route]
+        return self._lib.fg_gather_gemm_ring(self._h, arr, C.byref(route) if route is not None else None,
+                                             _ptr(w), _ptr(ring), n_channels, ring_chunks, self_shard,
+                                             _ptr(gathered), _ptr(out), flags, _stream_ptr(stream))
 
     def barrier(self, rounds: int = 1, stream=None) -> int:
         return self._lib.fg_barrier(self._h, rounds, _stream_ptr(stream))
