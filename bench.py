@@ -247,6 +247,53 @@ def two_stage_bench(args, wl, ctx, gathered, out, torch, fg):
             "copy_GBps": round(copy_bytes / (Tc * 1e-6) / 1e9, 1)}
 
 
+def ring_bench(args, wl, ctx, gathered, out, torch, fg):
+    """The dispatch through bounded FIFO rings (fg_gather_gemm_ring) on the same
+    workload and context, shard 0 as the self shard, as many rings per shard
+    as the copy workgroups serve, one 64-row slot each: T_total and the copy
+    roles alone, each the mean of back-to-back steps, and the ring memory
+    against the whole streams."""
+    S, K = wl["S"], wl["K"]
+    n_ch = max(1, ctx.views().ring_cap // S)
+    slots = 1
+    nbytes = fg.ring_bytes(ctx.cfg, n_ch, slots)
+    ring = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda:0")
+
+    def step(flags=0):
+        rc = ctx.gather_gemm_ring(wl["shards"], wl["w"], ring, gathered, out, n_channels=n_ch, ring_chunks=slots,
+                                  self_shard=0, route=wl["route"], flags=flags)
+        if rc != fg.OK:
+            raise RuntimeError(f"fg_gather_gemm_ring: {fg.strerror(rc)}")
+
+    def back_to_back(flags, n):
+        step(flags)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            step(flags)
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / n
+
+    for _ in range(3):
+        step()
+    n = max(10, args.steps)
+    Tt = back_to_back(0, n)
+    Tc = back_to_back(fg.CALL_COMM_ONLY, n)
+    st = ctx.stats()
+    if st.error_code:
+        raise RuntimeError(f"device error {st.error_code} id {st.error_id}")
+    flop = 2.0 * wl["m_real"] * K * wl["N"]
+    stream_bytes = sum(wl["stream_len"][1:]) * K * 2.0
+    step()
+    torch.cuda.synchronize()
+    return {"self_shard": 0, "rings_per_shard": n_ch, "slots_per_ring": slots, "ring_MB": round(nbytes / 1e6, 1),
+            "remote_streams_MB": round(stream_bytes / 1e6, 1), "T_total_us": round(Tt, 2),
+            "T_copy_alone_us": round(Tc, 2), "TFLOPs": round(flop / (Tt * 1e-6) / 1e12, 2)}
+
+
 def combine_bench(args, wl, ctx, gathered, out, torch, fg, W):
     """The combine step on the EP workload (8 x 1024 tokens, top-8 of 64 experts,
     8 local, N = 2048): T_total (push + weighted sums in one kernel), push alone,
@@ -473,6 +520,7 @@ def main():
                             "us_per_iter_delays_0_20us": round(statistics.median(t_delay) * 1000, 2),
                             "signals_per_s_no_delay": round(signals / (statistics.median(t_nodelay) * 1e-3), 0)}
         result["two_stage"] = two_stage_bench(args, wl, ctx, gathered, out, torch, fg)
+        result["ring"] = ring_bench(args, wl, ctx, gathered, out, torch, fg)
         result["combine"] = combine_bench(args, wl, ctx, gathered, out, torch, fg, W)
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0").fill_(1)
