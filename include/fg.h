@@ -70,6 +70,9 @@ enum {
   FG_CALL_STRICT = 1u << 3,     /* formal agent-scope release fences on every signal (slow reference mode) */
   FG_CALL_SAME_ROUTE = 1u << 4, /* EXPLICIT/TOPK: route identical to the previous call, skip the layout step */
   FG_CALL_TRACE = 1u << 5,      /* record per compute item and per row block timestamps (fg_views trace) */
+  FG_CALL_LAYOUT_TWO_PASS = 1u << 6, /* TOPK: run the layout as two kernels (count + scan, then place) even
+                                        when its grid fits on the device at once (the one-kernel layout waits
+                                        for the scan inside the kernel) */
   /* Fault injection (tests). Each makes a bounded wait or a check fail so that
    * the error path is exercised; every kernel still runs to completion. */
   FG_FAULT_SEED_LOW = 1u << 8,      /* seed of row block 0 one too low: its gate never opens -> FG_ETIMEOUT */

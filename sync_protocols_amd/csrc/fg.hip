@@ -89,6 +89,7 @@ struct fg_ctx {
   int topk_rows = 0, topk_k = 0;   // tokens per shard and k of the last TOPK route
   int combine_wg = 0;
   int ring_cap = 0;            // rings the copy workgroups can serve (a producer and a consumer each)
+  int route_resident = 0;      // layout workgroups that can be resident at once (one-kernel layout)
   uint32_t route_ver = 0;
   int route_wg_cap = 0;
   fg_status sticky = FG_OK;
@@ -179,7 +180,8 @@ static uint64_t timeout_ticks(const fg_ctx* ctx) {
   return (uint64_t)(ns / 1000000.0 * ctx->wall_khz);
 }
 
-static fg_status launch_route(fg_ctx* ctx, const fg_route* route, int mode, int rows, int m_pad, hipStream_t st) {
+static fg_status launch_route(fg_ctx* ctx, const fg_route* route, int mode, int rows, int m_pad, hipStream_t st,
+                              uint32_t flags) {
   RouteArgs ra{};
   const fg_config& c = ctx->cfg;
   ra.mode = mode;
@@ -222,9 +224,16 @@ static fg_status launch_route(fg_ctx* ctx, const fg_route* route, int mode, int 
   } else {
     ra.wpb = (rows + kRouteThreads - 1) / kRouteThreads;
     const int n_wg = c.n_shards * ra.wpb;
-    hipLaunchKernelGGL(route_topk_count_kernel, dim3(n_wg), dim3(kRouteThreads), 0, st, ra);
-    HIPCHK(hipGetLastError());
-    hipLaunchKernelGGL(route_topk_place_kernel, dim3(n_wg), dim3(kRouteThreads), 0, st, ra);
+    ra.n_wg = n_wg;
+    ra.timeout_ticks = timeout_ticks(ctx);
+    if (n_wg <= ctx->route_resident && !(flags & FG_CALL_LAYOUT_TWO_PASS)) {
+      // one kernel: the layout grid is co-resident, so its workgroups can wait for the scan
+      hipLaunchKernelGGL(route_topk_kernel, dim3(n_wg), dim3(kRouteThreads), 0, st, ra);
+    } else {
+      hipLaunchKernelGGL(route_topk_count_kernel, dim3(n_wg), dim3(kRouteThreads), 0, st, ra);
+      HIPCHK(hipGetLastError());
+      hipLaunchKernelGGL(route_topk_place_kernel, dim3(n_wg), dim3(kRouteThreads), 0, st, ra);
+    }
   }
   HIPCHK(hipGetLastError());
   return FG_OK;
@@ -301,6 +310,14 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
       return FG_EHIP;
     }
     if ((long long)per_cu * ctx->cu_count < ctx->combine_wg) { delete ctx; return FG_ERESIDENCY; }
+  }
+  {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, route_topk_kernel, kRouteThreads, 0) != hipSuccess) {
+      delete ctx;
+      return FG_EHIP;
+    }
+    ctx->route_resident = per_cu * ctx->cu_count;
   }
   if (cfg->stress_producers + cfg->stress_consumers > ctx->cu_count ||
       cfg->stress_consumers >= ctx->cu_count) { delete ctx; return FG_ERESIDENCY; }
@@ -441,13 +458,13 @@ static fg_status gather_gemm_impl(fg_ctx* ctx, const void* const* shards, const 
   const bool same = flags & FG_CALL_SAME_ROUTE;
   if (mode == FG_ROUTE_CONTIG) {
     if (ctx->route_cached_mode != FG_ROUTE_CONTIG || ctx->route_cached_rows != rows) {
-      if ((s = launch_route(ctx, route, mode, rows, m_pad, stream)) != FG_OK) return s;
+      if ((s = launch_route(ctx, route, mode, rows, m_pad, stream, flags)) != FG_OK) return s;
       ctx->route_cached_mode = FG_ROUTE_CONTIG;
       ctx->route_cached_rows = rows;
     }
   } else {
     if (!same || ctx->route_cached_mode != mode) {
-      if ((s = launch_route(ctx, route, mode, rows, m_pad, stream)) != FG_OK) return s;
+      if ((s = launch_route(ctx, route, mode, rows, m_pad, stream, flags)) != FG_OK) return s;
     }
     ctx->route_cached_mode = mode;
     ctx->route_cached_rows = rows;

@@ -874,6 +874,8 @@ struct RouteArgs {
   const int* topk;           // TOPK device [S][T][KK]
   int topk_k, expert_base;
   int wpb;                   // TOPK: workgroups per shard
+  int n_wg;                  // TOPK: workgroups of the layout grid
+  uint64_t timeout_ticks;    // TOPK in one kernel: watchdog of the wait for the scan
   uint32_t ver;              // route version stamped into the inverse map
   int* src_row;
   int* dst_row;
@@ -892,7 +894,8 @@ struct RouteArgs {
   int* wgbase;               // TOPK: [n_wg][E + 1] expert row bases, stream base
   int* src_k;                // TOPK: [S][rs_cap] top-k position of each stream entry
   int* tok_first;            // TOPK: [S][rs_cap + 1] first stream entry of each token; [T] = stream length
-  int* ticket;               // [0] last-workgroup ticket, [1] failure flag (zero between calls)
+  int* ticket;               // [0] last-workgroup ticket, [1] failure flag (zero between calls),
+                             // [2] failure of the last layout, [3] route version whose scan is done
   ErrorSink err;
 };
 
@@ -1028,7 +1031,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_explicit_kernel(RouteArgs
 // TOPK layout, both passes: each workgroup takes 256 consecutive tokens of one
 // shard and first copies their top-k lists into LDS, one byte per choice: the
 // local expert index, or 0xFF for an expert this GPU does not own.
-constexpr int kRouteTileInts = 4096;   // per-workgroup counts staged through LDS by the last workgroup
 
 __device__ __forceinline__ int stage_topk(const RouteArgs& a, uint8_t* sh_tk, int s, int t0) {
   const int E = a.n_groups, KK = a.topk_k, T = a.rows_per_shard;
@@ -1041,29 +1043,14 @@ __device__ __forceinline__ int stage_topk(const RouteArgs& a, uint8_t* sh_tk, in
   return ntok;
 }
 
-// TOPK, pass 1: per workgroup the number of its tokens choosing each local
-// expert and its number of local pairs; the last workgroup scans them in
-// global token order (workgroup order) into relative expert row bases and
-// per-shard stream bases ("DeepEP FIFO pipeline" dispatch notify stage: counts
-// fix the offsets), then the group offsets (each expert padded to a multiple of
-// 128 rows) and seeds. The counts pass through LDS in tiles, so the scan runs
-// on LDS reads, not on a chain of global loads.
-__global__ __launch_bounds__(kRouteThreads) void route_topk_count_kernel(RouteArgs a) {
-  __shared__ uint8_t sh_tk[kRouteThreads * 64];
-  __shared__ int sh_cnt[FG_MAX_GROUPS + 1];
-  __shared__ int sh_last;
-  __shared__ int sh_goff[FG_MAX_GROUPS + 1];
-  __shared__ int sh_ne[FG_MAX_GROUPS];
-  __shared__ int sh_tile[kRouteTileInts];
-  const int E = a.n_groups, KK = a.topk_k, T = a.rows_per_shard;
-  const int w = blockIdx.x, s = w / a.wpb, t0 = (w - s * a.wpb) * kRouteThreads, t = t0 + threadIdx.x;
-  for (int e = threadIdx.x; e <= E; e += blockDim.x) sh_cnt[e] = 0;
-  stage_topk(a, sh_tk, s, t0);
-  __syncthreads();
+// TOPK, counting: per workgroup the number of its tokens choosing each local
+// expert and its number of local pairs (one wave ballot and one LDS add per
+// wave and expert); top-k lists already staged in sh_tk.
+__device__ void topk_count(const RouteArgs& a, const uint8_t* sh_tk, int* sh_cnt, int w, int s, int t0) {
+  const int E = a.n_groups, KK = a.topk_k, T = a.rows_per_shard, t = t0 + threadIdx.x;
+  unsigned long long mask = 0;
   if (t < T) {
     const uint8_t* tk = sh_tk + threadIdx.x * KK;
-    unsigned long long mask = 0;
-    int picks = 0;
     for (int k = 0; k < KK; ++k) {
       const int e = tk[k];
       if (e == 0xFF) continue;
@@ -1073,46 +1060,59 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_count_kernel(RouteAr
         continue;
       }
       mask |= 1ull << e;
-      ++picks;
-      atomicAdd(sh_cnt + e, 1);
     }
-    atomicAdd(sh_cnt + E, picks);
   }
+  const int lane = threadIdx.x & 63;
+  int total = 0;
+  for (int e = 0; e < E; ++e) {
+    const int n = __popcll(ballot((mask >> e) & 1ull));
+    total += n;
+    if (lane == 0 && n) atomicAdd(sh_cnt + e, n);
+  }
+  if (lane == 0 && total) atomicAdd(sh_cnt + E, total);
   __syncthreads();
   for (int e = threadIdx.x; e <= E; e += blockDim.x) a.wgcount[w * (E + 1) + e] = sh_cnt[e];
-  if (!last_workgroup(a.ticket, &sh_last)) return;
-  const int n_wg = gridDim.x;
-  // column e < E: running row base of expert e in workgroup order (relative to
-  // the expert's group offset); column E: running stream base inside a shard
-  const int rows_per_tile = kRouteTileInts / (E + 1);
-  int run = 0;
-  for (int v0 = 0; v0 < n_wg; v0 += rows_per_tile) {
-    const int nrows = min(rows_per_tile, n_wg - v0);
-    for (int i = threadIdx.x; i < nrows * (E + 1); i += blockDim.x) sh_tile[i] = a.wgcount[v0 * (E + 1) + i];
-    __syncthreads();
-    if ((int)threadIdx.x <= E) {
-      const int e = threadIdx.x;
-      for (int r = 0; r < nrows; ++r) {
-        const int v = v0 + r;
-        if (e == E && v % a.wpb == 0 && v > 0) {   // a new shard starts: close the previous one
-          const int sp = v / a.wpb - 1;
-          a.stream_len[sp] = run;
-          a.tok_first[(size_t)sp * (a.rs_cap + 1) + T] = run;
-          if (run > a.rs_cap) { raise_error(a.err, kErrProtocol, 0x40000000 | sp); atomicOr(a.ticket + 1, 1); }
-          run = 0;
+}
+
+// TOPK, the last workgroup: scans the counts in global token order (workgroup
+// order) into relative expert row bases and per-shard stream bases ("DeepEP
+// FIFO pipeline" dispatch notify stage: counts fix the offsets), then the group
+// offsets (each expert padded to a multiple of 128 rows), seeds, arming and the
+// slab table; resets the last-workgroup ticket and records failure in ticket[2].
+// Column e < E is an exclusive scan over the workgroups, 64 at a time, one
+// wave per column; column E one thread per shard over its workgroups.
+__device__ void topk_scan_finish(const RouteArgs& a, int* sh_goff, int* sh_ne) {
+  const int E = a.n_groups, T = a.rows_per_shard;
+  const int n_wg = a.n_wg;
+  {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    for (int e = wave; e < E; e += nwaves) {
+      int carry = 0;
+      for (int v0 = 0; v0 < n_wg; v0 += 64) {
+        const int v = v0 + lane;
+        const int x = v < n_wg ? a.wgcount[v * (E + 1) + e] : 0;
+        int incl = x;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int y = __shfl_up(incl, d, 64);
+          if (lane >= d) incl += y;
         }
-        a.wgbase[v * (E + 1) + e] = run;
-        run += sh_tile[r * (E + 1) + e];
+        if (v < n_wg) a.wgbase[v * (E + 1) + e] = carry + incl - x;
+        carry += __shfl(incl, 63, 64);
       }
+      if (lane == 0) sh_ne[e] = carry;
     }
-    __syncthreads();
-  }
-  if ((int)threadIdx.x < E) sh_ne[threadIdx.x] = run;
-  if ((int)threadIdx.x == E) {
-    const int sp = a.n_shards - 1;
-    a.stream_len[sp] = run;
-    a.tok_first[(size_t)sp * (a.rs_cap + 1) + T] = run;
-    if (run > a.rs_cap) { raise_error(a.err, kErrProtocol, 0x40000000 | sp); atomicOr(a.ticket + 1, 1); }
+    if ((int)threadIdx.x < a.n_shards) {
+      const int sp = threadIdx.x;
+      int run = 0;
+      for (int v = sp * a.wpb; v < (sp + 1) * a.wpb; ++v) {
+        a.wgbase[v * (E + 1) + E] = run;
+        run += a.wgcount[v * (E + 1) + E];
+      }
+      a.stream_len[sp] = run;
+      a.tok_first[(size_t)sp * (a.rs_cap + 1) + T] = run;
+      if (run > a.rs_cap) { raise_error(a.err, kErrProtocol, 0x40000000 | sp); atomicOr(a.ticket + 1, 1); }
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -1136,38 +1136,33 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_count_kernel(RouteAr
   if (threadIdx.x == 0) { a.ticket[0] = 0; a.ticket[2] = fail; a.ticket[1] = 0; }
 }
 
-// TOPK, pass 2: place every local pair. Inside a workgroup the rank of a token
+// TOPK, placing every local pair of this workgroup's tokens (lists in sh_tk,
+// sh_base = absolute expert row bases, [E] = stream base). The rank of a token
 // among those choosing expert e comes from wave ballots (tokens are in thread
 // order, i.e. global token order); the stream index from a scan of the local
-// pick counts; the bases of pass 1 and the group offsets are read once.
-__global__ __launch_bounds__(kRouteThreads) void route_topk_place_kernel(RouteArgs a) {
-  __shared__ uint8_t sh_tk[kRouteThreads * 64];
-  __shared__ int sh_wave[FG_MAX_GROUPS + 1][kRouteThreads / 64];
-  __shared__ int sh_pick[kRouteThreads / 64];
-  __shared__ int sh_base[FG_MAX_GROUPS + 1];
-  const int E = a.n_groups, KK = a.topk_k, T = a.rows_per_shard;
-  const int w = blockIdx.x, s = w / a.wpb, t0 = (w - s * a.wpb) * kRouteThreads, t = t0 + threadIdx.x;
+// pick counts.
+__device__ void topk_place(const RouteArgs& a, const uint8_t* sh_tk, const int* sh_base, int (*sh_wave)[kRouteThreads / 64],
+                           int* sh_pick, uint8_t* sh_kpos, int s, int t0) {
+  const int E = a.n_groups, KK = a.topk_k, T = a.rows_per_shard, t = t0 + threadIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (__hip_atomic_load(a.ticket + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;  // layout failed
-  stage_topk(a, sh_tk, s, t0);
-  // absolute row base of each expert for this workgroup, stream base in [E]
-  if ((int)threadIdx.x <= E)
-    sh_base[threadIdx.x] = a.wgbase[w * (E + 1) + threadIdx.x] + ((int)threadIdx.x < E ? a.group_off_out[threadIdx.x] : 0);
-  __syncthreads();
   const uint8_t* tk = sh_tk + threadIdx.x * KK;
-  unsigned long long mask = 0;
+  // one pass over the list: the experts chosen, the list positions holding a
+  // local expert, and each local expert's position (sh_kpos[e][thread])
+  unsigned long long mask = 0, lpos = 0;
   if (t < T)
     for (int k = 0; k < KK; ++k) {
       const int e = tk[k];
-      if (e != 0xFF) mask |= 1ull << e;
+      if (e != 0xFF) {
+        mask |= 1ull << e;
+        lpos |= 1ull << k;
+        sh_kpos[e * kRouteThreads + threadIdx.x] = (uint8_t)k;
+      }
     }
   const unsigned long long lt = (1ull << lane) - 1ull;
-  // per expert: rank inside the wave, wave totals to LDS
   for (int e = 0; e < E; ++e) {
     const unsigned long long b = ballot((mask >> e) & 1ull);
     if (lane == 0) sh_wave[e][wave] = __popcll(b);
   }
-  // local picks of this token and their scan (stream positions)
   const int picks = __popcll(mask);
   int x = picks;
 #pragma unroll
@@ -1187,18 +1182,102 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_place_kernel(RouteAr
     if (!f) continue;
     int rank = sh_base[e] + __popcll(b & lt);
     for (int v = 0; v < wave; ++v) rank += sh_wave[e][v];
-    int j = 0, kk = 0;   // local picks ahead of expert e in this token's list; e's position in it
-    for (int k = 0; k < KK; ++k) {
-      const int ek = tk[k];
-      if (ek == e) { kk = k; break; }
-      j += (ek != 0xFF);
-    }
-    const int i = stream0 + j;
+    const int kk = sh_kpos[e * kRouteThreads + threadIdx.x];        // e's position in the token's list
+    const int i = stream0 + __popcll(lpos & ((1ull << kk) - 1ull));  // after the local picks ahead of it
     a.src_row[s * a.rs_cap + i] = t;
     a.src_k[s * a.rs_cap + i] = kk;
     a.dst_row[s * a.rs_cap + i] = rank;
     a.inv[rank] = inv_pack(a.ver, (s << 24) | i);
   }
+}
+
+// Absolute bases of workgroup w into sh_base (the group offsets are final).
+__device__ __forceinline__ int topk_base_load(const RouteArgs& a, int w) {
+  const int E = a.n_groups;
+  int base = 0;
+  if ((int)threadIdx.x <= E)
+    base = a.wgbase[w * (E + 1) + threadIdx.x] + ((int)threadIdx.x < E ? a.group_off_out[threadIdx.x] : 0);
+  return base;
+}
+
+// TOPK in one kernel (the grid is co-resident, checked by the host): count,
+// the last workgroup scans and publishes the route version in ticket[3], the
+// others wait for it (a bounded wait on a supplier that never waits) and
+// place their pairs from the lists still in LDS.
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(RouteArgs a) {
+  __shared__ uint8_t sh_tk[kRouteThreads * 64];
+  __shared__ int sh_cnt[FG_MAX_GROUPS + 1];
+  __shared__ int sh_last;
+  __shared__ int sh_goff[FG_MAX_GROUPS + 1];
+  __shared__ int sh_ne[FG_MAX_GROUPS];
+  __shared__ int sh_wave[FG_MAX_GROUPS + 1][kRouteThreads / 64];
+  __shared__ int sh_pick[kRouteThreads / 64];
+  __shared__ int sh_base[FG_MAX_GROUPS + 1];
+  __shared__ uint8_t sh_kpos[FG_MAX_GROUPS * kRouteThreads];
+  __shared__ int sh_ok;
+  const int E = a.n_groups;
+  const int w = blockIdx.x, s = w / a.wpb, t0 = (w - s * a.wpb) * kRouteThreads;
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) sh_cnt[e] = 0;
+  stage_topk(a, sh_tk, s, t0);
+  __syncthreads();
+  topk_count(a, sh_tk, sh_cnt, w, s, t0);
+  if (last_workgroup(a.ticket, &sh_last)) {
+    topk_scan_finish(a, sh_goff, sh_ne);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_store(a.ticket + 3, (int)a.ver, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sh_ok = 1;
+    }
+  } else if (threadIdx.x == 0) {
+    uint32_t polls = 0;
+    sh_ok = wait_ge(a.ticket + 3, (int)a.ver, now_ticks() + a.timeout_ticks, a.err, 0x75000000, &polls);
+  }
+  __syncthreads();
+  if (!sh_ok) return;
+  acquire_agent();
+  if (__hip_atomic_load(a.ticket + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;   // layout failed
+  const int base = topk_base_load(a, w);
+  if ((int)threadIdx.x <= E) sh_base[threadIdx.x] = base;
+  __syncthreads();
+  topk_place(a, sh_tk, sh_base, sh_wave, sh_pick, sh_kpos, s, t0);
+}
+
+// TOPK in two kernels, for grids that are not co-resident: pass 1 counts and
+// the last workgroup scans; pass 2 places.
+__global__ __launch_bounds__(kRouteThreads) void route_topk_count_kernel(RouteArgs a) {
+  __shared__ uint8_t sh_tk[kRouteThreads * 64];
+  __shared__ int sh_cnt[FG_MAX_GROUPS + 1];
+  __shared__ int sh_last;
+  __shared__ int sh_goff[FG_MAX_GROUPS + 1];
+  __shared__ int sh_ne[FG_MAX_GROUPS];
+  const int E = a.n_groups;
+  const int w = blockIdx.x, s = w / a.wpb, t0 = (w - s * a.wpb) * kRouteThreads;
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) sh_cnt[e] = 0;
+  stage_topk(a, sh_tk, s, t0);
+  __syncthreads();
+  topk_count(a, sh_tk, sh_cnt, w, s, t0);
+  if (!last_workgroup(a.ticket, &sh_last)) return;
+  topk_scan_finish(a, sh_goff, sh_ne);
+}
+
+__global__ __launch_bounds__(kRouteThreads) void route_topk_place_kernel(RouteArgs a) {
+  __shared__ uint8_t sh_tk[kRouteThreads * 64];
+  __shared__ int sh_wave[FG_MAX_GROUPS + 1][kRouteThreads / 64];
+  __shared__ int sh_pick[kRouteThreads / 64];
+  __shared__ int sh_base[FG_MAX_GROUPS + 1];
+  __shared__ uint8_t sh_kpos[FG_MAX_GROUPS * kRouteThreads];
+  const int E = a.n_groups;
+  const int w = blockIdx.x, s = w / a.wpb, t0 = (w - s * a.wpb) * kRouteThreads;
+  // the failure flag, this workgroup's bases and its top-k lists are loaded
+  // together (one memory round trip); nothing is written before the flag is seen
+  const int failed = __hip_atomic_load(a.ticket + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int base = topk_base_load(a, w);
+  stage_topk(a, sh_tk, s, t0);
+  if ((int)threadIdx.x <= E) sh_base[threadIdx.x] = base;
+  __syncthreads();
+  if (failed) return;   // layout failed: the tables stay as they are
+  topk_place(a, sh_tk, sh_base, sh_wave, sh_pick, sh_kpos, s, t0);
 }
 
 // Small helpers: fill, poke (fault injection on a counter).

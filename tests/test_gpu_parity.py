@@ -83,6 +83,12 @@ def test_ep_topk_small():
     log(f"ep small ok: m_pad={case.lay.m_pad} max|d|={r['max_abs']:.3g}")
 
 
+def test_ep_topk_two_pass_layout():
+    log("EP top-k with the layout as two kernels (count + scan, then place): same tables and results")
+    case = ep_case(1103, 4, 300, 256, 256, n_experts=16, topk=4, n_local=4, expert_base=4)
+    _run_and_check(case, 3, flags=fg.CALL_LAYOUT_TWO_PASS)
+
+
 def test_ep_topk_other_base():
     log("expert dispatch: local experts 24..31, 4 shards x 200 tokens")
     case = ep_case(37, 4, 200, 256, 256, expert_base=24)
