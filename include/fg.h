@@ -73,6 +73,10 @@ enum {
   FG_CALL_LAYOUT_TWO_PASS = 1u << 6, /* TOPK: run the layout as two kernels (count + scan, then place) even
                                         when its grid fits on the device at once (the one-kernel layout waits
                                         for the scan inside the kernel) */
+  FG_CALL_GATE_WATERMARK = 1u << 7,  /* CONTIG routes of fg_gather_gemm only ("PCIe sync protocols" §4): the
+                                        compute role gates each tile on the slots (chunk watermarks) of the
+                                        64-row chunks its rows come from instead of the 128-row counters
+                                        (which are still counted, so the control plane is the same) */
   /* Fault injection (tests). Each makes a bounded wait or a check fail so that
    * the error path is exercised; every kernel still runs to completion. */
   FG_FAULT_SEED_LOW = 1u << 8,      /* seed of row block 0 one too low: its gate never opens -> FG_ETIMEOUT */

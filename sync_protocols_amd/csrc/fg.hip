@@ -422,6 +422,8 @@ static fg_status gather_gemm_impl(fg_ctx* ctx, const void* const* shards, const 
   for (int i = 0; i < c.n_shards; ++i) if (!shards[i]) return FG_EINVAL;
   if ((flags & FG_CALL_COMM_ONLY) && (flags & FG_CALL_GEMM_ONLY)) return FG_EINVAL;
   const int mode = route ? route->mode : FG_ROUTE_CONTIG;
+  // watermark gating needs the contiguous layout and the one-stage copy (whose slots cover the rows)
+  if ((flags & FG_CALL_GATE_WATERMARK) && (mode != FG_ROUTE_CONTIG || staging || rc.ring)) return FG_EINVAL;
   int rows = c.max_rows_per_shard, m_pad = 0;
   if (mode == FG_ROUTE_CONTIG) {
     if (route) rows = route->rows_per_shard;

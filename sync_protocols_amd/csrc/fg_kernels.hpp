@@ -24,6 +24,7 @@ constexpr uint32_t kVerify = FG_CALL_VERIFY;
 constexpr uint32_t kStrict = FG_CALL_STRICT;
 constexpr uint32_t kDropPublish = FG_FAULT_DROP_PUBLISH;
 constexpr uint32_t kTrace = FG_CALL_TRACE;
+constexpr uint32_t kGateWatermark = FG_CALL_GATE_WATERMARK;
 
 // Device statistics block (int64 counters, cumulative).
 enum { ST_PUBLISHES = 0, ST_GATE_POLLS, ST_SLOT_POLLS, ST_GATE_PASSES, ST_STALE, ST_COUNT };
@@ -743,9 +744,22 @@ __device__ void gemm_role(const FusedArgs& a, char* const* lds, int* sh, long lo
         const int m0 = entry & ~1, bm = (entry & 1) ? 128 : 256;
         const long long t0 = (long long)now_ticks();
         uint32_t polls = 0;
-        for (int rb = m0 / kRB; rb < (m0 + bm) / kRB && ok; ++rb)
-          ok = wait_eq(a.counter_cur + (size_t)rb * kCtr, kRB, now_ticks() + a.timeout_ticks, a.err, rb, &polls,
-                       kBackoffLong);
+        if ((a.flags & kGateWatermark) && !(a.flags & kGemmOnly)) {   // compute only: nothing to wait for
+          // contiguous layout: gathered row g is row g % R of shard g / R, so
+          // the tile's rows are covered by whole 64-row chunks of the shard
+          // streams; wait for each chunk's slot (its watermark) to carry seq
+          const int R = a.shard_rows, M = a.n_shards * R;
+          for (int g = m0; g < min(m0 + bm, M) && ok;) {
+            const int s = g / R, c = (g - s * R) / kChunk;
+            ok = wait_ge(a.slot + s * a.chunk_cap + c, a.seq, now_ticks() + a.timeout_ticks, a.err,
+                         0x31000000 | (s * a.chunk_cap + c), &polls);
+            g = s * R + min(R, (c + 1) * kChunk);
+          }
+        } else if (!(a.flags & kGateWatermark)) {
+          for (int rb = m0 / kRB; rb < (m0 + bm) / kRB && ok; ++rb)
+            ok = wait_eq(a.counter_cur + (size_t)rb * kCtr, kRB, now_ticks() + a.timeout_ticks, a.err, rb, &polls,
+                         kBackoffLong);
+        }
         const long long t_open = (long long)now_ticks();
         gate += t_open - t0;
         if (verify) {

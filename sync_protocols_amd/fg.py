@@ -25,6 +25,7 @@ CALL_STRICT = 1 << 3
 CALL_SAME_ROUTE = 1 << 4
 CALL_TRACE = 1 << 5
 CALL_LAYOUT_TWO_PASS = 1 << 6
+CALL_GATE_WATERMARK = 1 << 7
 COUNTER_STRIDE = 64      # int32 per arrival counter in the control plane (FG_COUNTER_STRIDE)
 FAULT_SEED_LOW = 1 << 8
 FAULT_SEED_HIGH = 1 << 9

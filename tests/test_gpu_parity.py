@@ -83,6 +83,31 @@ def test_ep_topk_small():
     log(f"ep small ok: m_pad={case.lay.m_pad} max|d|={r['max_abs']:.3g}")
 
 
+@pytest.mark.parametrize("n_shards,rows", [(4, 256), (3, 100), (5, 77)])
+def test_contiguous_watermark_gating(n_shards, rows):
+    log(f"contiguous {n_shards} x {rows} rows, the GEMM gated on the 64-row chunk watermarks")
+    case = dense_case(70 + rows, n_shards, rows, 256, 256)
+    _run_and_check(case, 3, flags=fg.CALL_GATE_WATERMARK)
+
+
+def test_watermark_gating_full_tp_sampled():
+    log("TP size, GEMM gated on chunk watermarks: 4 x 2048 rows, K=N=4096, sampled rows")
+    c = W.CONFIGS["tp"]
+    case = dense_case(c["seed"], c["n_shards"], c["rows"], c["K"], c["N"])
+    rng = np.random.default_rng(11)
+    _run_and_check(case, 2, flags=fg.CALL_GATE_WATERMARK, full_out=False,
+                   sample_rows=np.sort(rng.choice(case.lay.m_pad, 48, replace=False)))
+
+
+def test_watermark_gating_needs_contiguous_route():
+    log("watermark gating is refused for other routes")
+    case = dense_case(75, 2, 128, 256, 256, gather="permutation")
+    ctx = make_ctx(case)
+    g, o = buffers(ctx, case)
+    assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route, flags=fg.CALL_GATE_WATERMARK) == fg.EINVAL
+    ctx.close()
+
+
 def test_ep_topk_two_pass_layout():
     log("EP top-k with the layout as two kernels (count + scan, then place): same tables and results")
     case = ep_case(1103, 4, 300, 256, 256, n_experts=16, topk=4, n_local=4, expert_base=4)
