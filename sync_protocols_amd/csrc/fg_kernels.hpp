@@ -115,54 +115,9 @@ enum { WT_START = 0, WT_END, WT_GATE, WT_TILES, WT_COMM_END, WT_PARTS, WT_GEMM_S
 // order in which the compute role consumes row blocks (§6 audit item 3); a
 // communication workgroup never waits on anything (§6 audit item 2).
 // ---------------------------------------------------------------------------
-// Copy one batch of RB gathered rows (g0 .. g0+RB-1), each at most 64*UPR
-// 16-byte vectors, branch-free: every row gets its own buffer descriptors, and
-// a padding row (or the part of a row beyond K) gets a zero-sized one, so its
-// loads read 0 and its stores are dropped by the buffer unit. All loads of the
-// batch are issued before its stores (RB*UPR vectors per lane in flight).
-template <int UPR, int RB>
-__device__ __forceinline__ void copy_batch(const FusedArgs& a, const uint16_t* const* sh_shard, int g0, int info,
-                                           int srow, uint32_t row_bytes, int lane) {
-  __amdgpu_buffer_rsrc_t rs[RB], rd[RB];
-#pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    const int rinfo = readlane(info, r);
-    const bool valid = rinfo >= 0;
-    const int s = valid ? (rinfo >> 24) : 0;
-    const int sr = readlane(srow, r);
-    const uint64_t base = (uint64_t)sh_shard[s];
-    const uint16_t* shard = (const uint16_t*)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(base >> 32)) << 32) |
-                                              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base));
-    rs[r] = buffer_rsrc(shard + (size_t)sr * a.K, valid ? row_bytes : 0u);
-    rd[r] = buffer_rsrc(a.gathered + (size_t)(g0 + r) * a.K, valid ? row_bytes : 0u);
-  }
-  v4i v[RB][UPR];
-#pragma unroll
-  for (int r = 0; r < RB; ++r)
-#pragma unroll
-    for (int u = 0; u < UPR; ++u)
-      v[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rs[r], (uint32_t)(u * 64 + lane) * 16, 0, kPolNT);
-#pragma unroll
-  for (int r = 0; r < RB; ++r)
-#pragma unroll
-    for (int u = 0; u < UPR; ++u)
-      store16_coherent(rd[r], (uint32_t)(u * 64 + lane) * 16, v[r][u]);
-}
-
-// Batch of RB rows (RB in {1, 2, 4, 8, 16}, at most 32 vectors per lane in flight).
-template <int UPR>
-__device__ __forceinline__ void copy_rows(int RB, const FusedArgs& a, const uint16_t* const* sh_shard, int g0,
-                                          int info, int srow, uint32_t row_bytes, int lane) {
-  if (RB == 1) copy_batch<UPR, 1>(a, sh_shard, g0, info, srow, row_bytes, lane);
-  else if (RB == 2) { if constexpr (UPR * 2 <= 32) copy_batch<UPR, 2>(a, sh_shard, g0, info, srow, row_bytes, lane); }
-  else if (RB == 4) { if constexpr (UPR * 4 <= 32) copy_batch<UPR, 4>(a, sh_shard, g0, info, srow, row_bytes, lane); }
-  else if (RB == 8) { if constexpr (UPR * 8 <= 32) copy_batch<UPR, 8>(a, sh_shard, g0, info, srow, row_bytes, lane); }
-  else { if constexpr (UPR * 16 <= 32) copy_batch<UPR, 16>(a, sh_shard, g0, info, srow, row_bytes, lane); }
-}
-
 // Re-arm the other parity for the next iteration: nothing else touches it
 // during this kernel, and stream order publishes it to the next one.
-__device__ void arm_next(const FusedArgs& a) {
+__device__ __forceinline__ void arm_next(const FusedArgs& a) {
   const int cw = blockIdx.x;
   for (int i = cw * kThreads + threadIdx.x; i < a.rb_cap; i += a.n_comm * kThreads)
     a.counter_nxt[(size_t)i * kCtr] = a.seed[i];
@@ -176,7 +131,141 @@ __device__ void arm_next(const FusedArgs& a) {
   }
 }
 
-__device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
+// Lane r < RB of a batch describes gathered row b * RB + r. Its inverse-map
+// word is loaded a batch ahead of its use, by every lane and from an index
+// kept in range, so that the load sits on no branch: a value that reaches a
+// join on one path only makes the compiler wait for it there.
+__device__ __forceinline__ unsigned long long batch_inv_word(const FusedArgs& a, int b, int RB, int n_batches,
+                                                             int lane) {
+  return a.inv[min(b, n_batches - 1) * RB + min(lane, RB - 1)];
+}
+// The word's inverse entry (-1: padding, a lane past the batch, or no batch).
+__device__ __forceinline__ int batch_info(const FusedArgs& a, unsigned long long w, int b, int RB, int n_batches,
+                                          int lane) {
+  return lane < RB && b < n_batches && (uint32_t)(w >> 32) == a.route_ver ? (int)(uint32_t)w : -1;
+}
+// Source row of an inverse entry (any value for -1), loaded on no branch.
+__device__ __forceinline__ int batch_srow(const FusedArgs& a, int info) {
+  return a.src_row[info >= 0 ? (info >> 24) * a.rs_cap + (info & 0xFFFFFF) : 0];
+}
+
+// The batches b, b + nw, ... of RB gathered rows (each at most 64 * UPR
+// 16-byte vectors, RB * UPR <= 32 vectors per lane in flight) of one wave,
+// software-pipelined so that a batch costs two dependent memory round trips
+// instead of six: the next batch's loads leave as soon as this batch's stores
+// are acknowledged and its signals are issued, and the signals' return values
+// (needed only for the election and the overshoot check) are examined once
+// those loads are in flight; the inverse-map words of the batch after next
+// are fetched alongside.
+// Per batch: stores, release (every store acknowledged), one add to the row
+// block's arrival counter, one add per chunk touched (from the first lane of
+// the chunk, all chunks in one instruction), and the publish of each chunk
+// whose add completed it. A padding row (or the part of a row beyond K) gets
+// zero-sized descriptors, so its loads read 0 and its stores are dropped by the
+// buffer unit; so do the register rows RB .. RM-1 when a batch is shorter than
+// the register set (lanes >= RB describe no row).
+// The atomics' results are left undefined on the lanes that do not issue them
+// (and read only on the lanes that do), so no join copies them before the next
+// batch's loads are out.
+template <int UPR, bool strict>
+__device__ __forceinline__ void comm_batches(const FusedArgs& a, const uint16_t* const* sh_shard, int RB, int b,
+                                             int nw, int n_batches, uint32_t row_bytes, int lane, bool verify) {
+  constexpr int RM = 32 / UPR < 16 ? 32 / UPR : 16;   // rows of the register set
+  v4i v[RM][UPR];
+  auto load = [&](int binfo, int bsrow) {
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      const int rinfo = readlane(binfo, r);
+      const bool valid = rinfo >= 0;
+      const int s = valid ? (rinfo >> 24) : 0;
+      const int sr = readlane(bsrow, r);
+      const uint64_t base = (uint64_t)sh_shard[s];
+      const uint16_t* shard =
+          (const uint16_t*)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(base >> 32)) << 32) |
+                            (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base));
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(shard + (size_t)sr * a.K, valid ? row_bytes : 0u);
+#pragma unroll
+      for (int u = 0; u < UPR; ++u)
+        v[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(u * 64 + lane) * 16, 0, kPolNT);
+    }
+  };
+  // lane s holds shard s's stream length (the size of its last chunk), so
+  // that the election check reads it with a lane shuffle, not a dependent load
+  const int slen = lane < a.n_shards ? a.stream_len[lane] : 0;
+  int info = batch_info(a, batch_inv_word(a, b, RB, n_batches, lane), b, RB, n_batches, lane);
+  load(info, batch_srow(a, info));
+  int nb = b + nw;                                     // the batch to load next
+  unsigned long long nword = batch_inv_word(a, nb, RB, n_batches, lane);
+  while (true) {
+    // the call flags, re-read each pass through an opaque copy: as loop
+    // invariants they invite the compiler to clone the loop once per flag
+    const uint32_t fl = opaque_u32(a.flags);
+    const int ninfo = batch_info(a, nword, nb, RB, n_batches, lane);
+    const int nsrow = batch_srow(a, ninfo);
+    const int g0 = b * RB;
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      const bool valid = readlane(info, r) >= 0;
+      const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(a.gathered + (size_t)(g0 + r) * a.K, valid ? row_bytes : 0u);
+#pragma unroll
+      for (int u = 0; u < UPR; ++u) store16_coherent(rd, (uint32_t)(u * 64 + lane) * 16, v[r][u]);
+    }
+    release_coherent(strict);
+    // signals of batch b
+    const int n_real = __popcll(ballot(lane < RB && info >= 0));
+    int old_c, old_e, cnt = 0;
+    // (an opaque zero in the address keeps the compiler from rewriting this
+    // one-lane add as a wave-wide one whose result it needs at once)
+    if (lane == 0 && n_real > 0)
+      old_c = fetch_add_relaxed(a.counter_cur + (size_t)(g0 / kRB) * kCtr + opaque_zero(), n_real);
+    const int src_s = info >= 0 ? info >> 24 : 0, src_c = (info & 0xFFFFFF) / kChunk;
+    const int chunk = (lane < RB && info >= 0) ? src_s * a.chunk_cap + src_c : -1;
+    const int expect = min(kChunk, __shfl(slen, src_s) - kChunk * src_c);
+    bool leader = false;
+    uint64_t pending = ballot(chunk >= 0);
+    while (pending) {
+      const int l = __ffsll((long long)pending) - 1;
+      const int ch = readlane(chunk, l);
+      const uint64_t mask = ballot(chunk == ch) & pending;
+      if (lane == l) { leader = true; cnt = __popcll(mask); }
+      pending &= ~mask;
+    }
+    if (leader)
+      old_e = strict ? fetch_add_acq_rel(a.elect_cur + chunk, cnt) : fetch_add_relaxed(a.elect_cur + chunk, cnt);
+    // the next batch goes out before those values are examined
+    const bool more = nb < n_batches;
+    if (more) load(ninfo, nsrow);
+    const unsigned long long nnword = batch_inv_word(a, nb + nw, RB, n_batches, lane);
+    if (lane == 0 && n_real > 0) {
+      const int blk = g0 / kRB;
+      if (old_c + n_real > kRB) raise_error(a.err, kErrProtocol, blk);
+      if ((fl & kTrace) && old_c + n_real == kRB) a.rb_time[blk] = (long long)now_ticks();
+    }
+    if (leader) {
+      if (old_e + cnt == expect) {
+        if (!((fl & kDropPublish) && chunk == 0)) slot_publish(a.slot + chunk, a.seq, strict);
+        if (fl & kVerify) {
+          atomicAdd(a.pub_count + chunk, 1);
+          atomicAdd(a.stats + ST_PUBLISHES, 1ull);
+        }
+      } else if (old_e + cnt > expect) {
+        raise_error(a.err, kErrProtocol, 0x10000000 | chunk);
+      }
+    }
+    if (!more) break;
+    b = nb; info = ninfo; nb += nw; nword = nnword;
+  }
+}
+
+template <int UPR>
+__device__ __forceinline__ void comm_batches_any(bool strict, const FusedArgs& a, const uint16_t* const* sh_shard,
+                                                 int RB, int b, int nw, int n_batches, uint32_t row_bytes, int lane,
+                                                 bool verify) {
+  if (strict) comm_batches<UPR, true>(a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
+  else comm_batches<UPR, false>(a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
+}
+
+__device__ __forceinline__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int cw = blockIdx.x;
@@ -190,58 +279,15 @@ __device__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
   const uint32_t row_bytes = (uint32_t)a.K * 2;
   const int nw = a.n_comm * kWaves;
   const bool verify = a.flags & kVerify;
-
-  for (int b = cw * kWaves + wave; b < n_batches; b += nw) {
-    const int g0 = b * RB;
-    // lane r < RB describes gathered row g0 + r
-    int info = -1, srow = 0;
-    if (lane < RB) {
-      info = inv_read(a.inv, g0 + lane, a.route_ver);
-      if (info >= 0) srow = a.src_row[(info >> 24) * a.rs_cap + (info & 0xFFFFFF)];
-    }
-    // bitwise row copy: 16-byte streaming loads, device-coherent 16-byte stores
-    if (upr <= 1)       copy_rows<1>(RB, a, sh_shard, g0, info, srow, row_bytes, lane);
-    else if (upr <= 2)  copy_rows<2>(RB, a, sh_shard, g0, info, srow, row_bytes, lane);
-    else if (upr <= 4)  copy_rows<4>(RB, a, sh_shard, g0, info, srow, row_bytes, lane);
-    else if (upr <= 8)  copy_rows<8>(RB, a, sh_shard, g0, info, srow, row_bytes, lane);
-    else if (upr <= 16) copy_rows<16>(RB, a, sh_shard, g0, info, srow, row_bytes, lane);
-    else                copy_rows<32>(RB, a, sh_shard, g0, info, srow, row_bytes, lane);
-    release_coherent(strict);
-    // arrival count for the batch's row block (RB divides the row block)
-    const uint64_t real = ballot(lane < RB && info >= 0);
-    const int n_real = __popcll(real);
-    if (lane == 0 && n_real > 0) {
-      const int rb = g0 / kRB;
-      const int old = fetch_add_relaxed(a.counter_cur + (size_t)rb * kCtr, n_real);
-      if (old + n_real > kRB) raise_error(a.err, kErrProtocol, rb);
-      if ((a.flags & kTrace) && old + n_real == kRB) a.rb_time[rb] = (long long)now_ticks();
-    }
-    // election: per chunk touched by the batch, one add of the rows it finished;
-    // the add that completes the chunk elects this wave as its single publisher
-    const int chunk = (lane < RB && info >= 0) ? (info >> 24) * a.chunk_cap + ((info & 0xFFFFFF) / kChunk) : -1;
-    uint64_t pending = ballot(chunk >= 0);
-    while (pending) {
-      const int leader = __ffsll((long long)pending) - 1;
-      const int ch = readlane(chunk, leader);
-      const uint64_t mask = ballot(chunk == ch) & pending;
-      if (lane == leader) {
-        const int cnt = __popcll(mask);
-        const int old = strict ? fetch_add_acq_rel(a.elect_cur + ch, cnt) : fetch_add_relaxed(a.elect_cur + ch, cnt);
-        const int s = ch / a.chunk_cap, c = ch - s * a.chunk_cap;
-        const int expect = min(kChunk, a.stream_len[s] - kChunk * c);
-        if (old + cnt == expect) {
-          if (!((a.flags & kDropPublish) && ch == 0)) slot_publish(a.slot + ch, a.seq, strict);
-          if (verify) {
-            atomicAdd(a.pub_count + ch, 1);
-            atomicAdd(a.stats + ST_PUBLISHES, 1ull);
-          }
-        } else if (old + cnt > expect) {
-          raise_error(a.err, kErrProtocol, 0x10000000 | ch);
-        }
-      }
-      pending &= ~mask;
-    }
-  }
+  const int b = cw * kWaves + wave;
+  if (b >= n_batches) return;
+  // bitwise row copy: 16-byte streaming loads, device-coherent 16-byte stores
+  if (upr <= 1)       comm_batches_any<1>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
+  else if (upr <= 2)  comm_batches_any<2>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
+  else if (upr <= 4)  comm_batches_any<4>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
+  else if (upr <= 8)  comm_batches_any<8>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
+  else if (upr <= 16) comm_batches_any<16>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
+  else                comm_batches_any<32>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
 }
 
 // ---------------------------------------------------------------------------
@@ -304,7 +350,7 @@ __device__ __forceinline__ void copy_addr(int upr, int RB, uint64_t src, uint64_
 // of the self shard straight from the shard; then the rows are counted into
 // their 128-row block's counter. A wave scatters only after all its pushes,
 // so every watermark wait has a supplier that never waits.
-__device__ void comm_two_stage(const FusedArgs& a, const uint16_t* const* sh_shard, uint16_t* const* sh_stage,
+__device__ __forceinline__ void comm_two_stage(const FusedArgs& a, const uint16_t* const* sh_shard, uint16_t* const* sh_stage,
                                const int* sh_pbase) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -406,7 +452,7 @@ __device__ __forceinline__ int ring_chunk_count(const FusedArgs& a, int s, int k
   return n_chunks > k ? (n_chunks - k + a.n_channels - 1) / a.n_channels : 0;
 }
 
-__device__ void ring_producer(const FusedArgs& a, const uint16_t* const* sh_shard, int r, int* sh) {
+__device__ __forceinline__ void ring_producer(const FusedArgs& a, const uint16_t* const* sh_shard, int r, int* sh) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool strict = a.flags & kStrict;
@@ -478,7 +524,7 @@ __device__ __forceinline__ int wait_tail(const unsigned long long* p, int j, uin
   }
 }
 
-__device__ void ring_consumer(const FusedArgs& a, const uint16_t* const* sh_shard, int r, int* sh) {
+__device__ __forceinline__ void ring_consumer(const FusedArgs& a, const uint16_t* const* sh_shard, int r, int* sh) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool strict = a.flags & kStrict;
@@ -666,7 +712,7 @@ __device__ __forceinline__ bool run_item(const FusedArgs& a, char* const* lds, i
 }
 
 template <int BN>
-__device__ void gemm_role(const FusedArgs& a, char* const* lds, int* sh, long long* wt) {
+__device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, int* sh, long long* wt) {
   if (a.flags & kCommOnly) return;
   const int m_pad = __builtin_amdgcn_readfirstlane(a.desc[0]);
   const int grid = gridDim.x;
@@ -806,7 +852,8 @@ __device__ void gemm_role(const FusedArgs& a, char* const* lds, int* sh, long lo
 }
 
 template <int BN>
-__global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs) {
+  const FusedArgs& a = kernel_arg<FusedArgs>();
   // one array per LDS stage (distinct objects for the compiler's wait placement)
   constexpr int kS23 = kStages == 4 ? Tile<256, BN>::STAGE : 16;
   __shared__ __attribute__((aligned(16))) char lds0[Tile<256, BN>::STAGE];

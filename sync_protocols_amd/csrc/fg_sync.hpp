@@ -64,11 +64,18 @@ __device__ __forceinline__ v4i load16_stream(const v4i* p) { return __builtin_no
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 
 // Release of this wave's earlier device-coherent stores (see the header note).
+// The wait is the compiler's own s_waitcnt (vmcnt 0, the other counters left
+// alone), so that its wait placement knows every earlier vector memory result
+// has arrived; the empty asm statements keep memory operations from moving
+// across it.
+constexpr int kWaitVmcnt0 = 0x0F70;   // vmcnt = 0, expcnt = 7, lgkmcnt = 15 (no wait on those)
 __device__ __forceinline__ void release_coherent(bool strict) {
   if (strict) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    asm volatile("" ::: "memory");
   }
 }
 
@@ -85,6 +92,32 @@ __device__ __forceinline__ void slot_publish(int* slot, int seq, bool strict) {
     __hip_atomic_store(slot, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   else
     __hip_atomic_store(slot, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A kernel's single by-value argument, read in place from the kernel argument
+// segment (constant memory, scalar loads). Read through the parameter, the
+// argument is first copied into a private local; when the compiler cannot
+// show every use to be a read it keeps that copy, and every field read from
+// it becomes a per-lane value.
+template <typename T>
+__device__ __forceinline__ const T& kernel_arg() {
+  return *(const T*)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
+// A zero the compiler cannot see through (a per-lane value to its divergence
+// analysis): added to an address, it keeps a single-lane atomic from being
+// rewritten into a wave-wide one that needs the result at once.
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
+// A uniform value the compiler cannot prove loop-invariant.
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
+  uint32_t y;
+  asm volatile("s_mov_b32 %0, %1" : "=s"(y) : "s"(x));
+  return y;
 }
 
 __device__ __forceinline__ int fetch_add_relaxed(int* p, int v) {
