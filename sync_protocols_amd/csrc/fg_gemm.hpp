@@ -44,6 +44,10 @@ static_assert(kBK == 64 || kBK == 32, "stage depth");
 #ifndef FG_WAVES
 #define FG_WAVES 8
 #endif
+#ifndef FG_PINGPONG
+#define FG_PINGPONG 0
+#endif
+constexpr bool kPingPong = FG_PINGPONG != 0 && FG_WAVES == 8;   // the ping-pong stage schedule below
 constexpr int kWaves = FG_WAVES;    // waves per workgroup: 8 = two per SIMD, so one wave's memory
                                     // instructions issue while the other's MFMAs run; 4 = one per SIMD
                                     // with a 128 x 128 wave tile (fewer LDS reads per MFMA)
@@ -299,6 +303,114 @@ __device__ __forceinline__ void stage_body4(const char* cur, const char* nxt, Fr
   }
 }
 
+// --- ping-pong schedule ----------------------------------------------------
+// The eight waves form two groups of four (group g = waves 4g .. 4g+3; with
+// waves placed on the SIMDs in turn, every SIMD holds one wave of each group),
+// and group g computes output rows [g BM/2, (g+1) BM/2) of the tile. Time is
+// cut into phases ended by workgroup barriers; group 1 runs one phase behind
+// group 0, so in every phase one group issues its MFMAs (16 per wave: two
+// k-steps) while the other group reads the fragments of its next two k-steps
+// from LDS and issues global->LDS loads. On each SIMD the matrix pipe is then
+// fed by one wave while the other wave's memory instructions issue, instead of
+// both waves interleaving both kinds.
+// Stage t is read in phases 4t .. 4t+3 (group 0 halves in 4t and 4t+2, group 1
+// in 4t+1 and 4t+3); the other slot, free from phase 4t on (stage t-1 was last
+// read in 4t-1), is refilled with stage t+1 during stage t. Loads follow their
+// readers: group 0 loads its own A rows and all of B in phase 4t, group 1 its
+// own A rows in phase 4t+1; each wave waits for its loads after its last MFMAs
+// of stage t, before the barrier that ends phase 4t+3 (group 0) or 4t+4
+// (group 1), so every load leads its first reader by four or more phases.
+// Every wave waits for its fragment reads before the barrier that ends its
+// memory phase, so no slot is refilled while a read of it is outstanding.
+constexpr int kWaitLgkm0 = 0xC07F;   // s_waitcnt immediate: lgkmcnt = 0, vmcnt and expcnt left alone
+
+__device__ __forceinline__ void pp_barrier() {
+  FG_SCHED_FENCE();
+  __builtin_amdgcn_s_barrier();
+  FG_SCHED_FENCE();
+}
+
+// Rows [r0, r0 + ROWS) of an operand for one stage, spread over the four
+// waves of a group (w = wave index within the group).
+template <int ROWS, int POL>
+__device__ __forceinline__ void group_load(__amdgpu_buffer_rsrc_t r, uint32_t row0_off, uint32_t row_stride,
+                                           uint32_t k0_bytes, char* lds, int r0, int w, int lane) {
+  constexpr int PER_WAVE = ROWS / kRowsPerLoad / 4;
+  static_assert(PER_WAVE >= 1 && ROWS % (kRowsPerLoad * 4) == 0, "group share");
+  const int sub = lane / kChunks;
+  const int slot = lane % kChunks;
+#pragma unroll
+  for (int q = 0; q < PER_WAVE; ++q) {
+    const int blk = (r0 / kRowsPerLoad) + w * PER_WAVE + q;
+    const int row = blk * kRowsPerLoad + sub;
+    const int chunk = swz(slot, row);
+    const uint32_t voff = row0_off + (uint32_t)row * row_stride + (uint32_t)chunk * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + blk * 1024), 16, voff, k0_bytes, 0, POL);
+  }
+}
+
+// Stage t in `cur` (its loads complete and published); `nxt` is refilled with
+// stage t+1 when `refill` (t >= 1: stage 1 comes with the prologue).
+template <int BM, int BN>
+__device__ __forceinline__ void pp_stage(const char* cur, char* nxt, bool refill, int grp, Acc<BM, BN>& acc, int wm,
+                                         int wn, int lane, __amdgpu_buffer_rsrc_t rA, uint32_t a_off,
+                                         __amdgpu_buffer_rsrc_t rB, uint32_t b_off, uint32_t stride,
+                                         uint32_t k_bytes) {
+  using T = Tile<BM, BN>;
+  const char* curB = cur + T::A_BYTES;
+  Frags<BM, BN> f0, f1;
+  // memory: k-steps 0 and 1; this group's loads of stage t+1
+  frags_read<BM, BN>(cur, curB, f0, 0, wm, wn, lane);
+  frags_read<BM, BN>(cur, curB, f1, 1, wm, wn, lane);
+  if (refill) {
+    group_load<BM / 2, kPolA>(rA, a_off, stride, k_bytes, nxt, grp * (BM / 2), wn, lane);
+    if (grp == 0) group_load<BN, 0>(rB, b_off, stride, k_bytes, nxt + T::A_BYTES, 0, wn, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  pp_barrier();
+  // compute: k-steps 0 and 1
+  frags_mfma<BM, BN>(f0, acc);
+  frags_mfma<BM, BN>(f1, acc);
+  pp_barrier();
+  // memory: k-steps 2 and 3
+  frags_read<BM, BN>(cur, curB, f0, 2, wm, wn, lane);
+  frags_read<BM, BN>(cur, curB, f1, 3, wm, wn, lane);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  pp_barrier();
+  // compute: k-steps 2 and 3, then this wave's loads of stage t+1
+  frags_mfma<BM, BN>(f0, acc);
+  frags_mfma<BM, BN>(f1, acc);
+  if (refill) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  pp_barrier();
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void tile_mainloop_pp(__amdgpu_buffer_rsrc_t rA, uint32_t a_off,
+                                                 __amdgpu_buffer_rsrc_t rB, uint32_t b_off, uint32_t stride, int nk,
+                                                 char* l0, char* l1, Acc<BM, BN>& acc) {
+  using T = Tile<BM, BN>;
+  static_assert(T::WGM == 2 && T::WGN == 4, "two groups of four waves, group = row half");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / T::WGN, wn = wave % T::WGN;
+  const int grp = wm;
+  stage_load<BM, kPolA>(rA, a_off, stride, 0, l0, wave, lane);
+  stage_load<BN, 0>(rB, b_off, stride, 0, l0 + T::A_BYTES, wave, lane);
+  stage_load<BM, kPolA>(rA, a_off, stride, kRowB, l1, wave, lane);
+  stage_load<BN, 0>(rB, b_off, stride, kRowB, l1 + T::A_BYTES, wave, lane);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  pp_barrier();
+  if (grp == 1) pp_barrier();
+  // nk is even; stage t lives in l0 for even t, l1 for odd t
+  for (int t = 0; t < nk; t += 2) {
+    pp_stage<BM, BN>(l0, l1, t >= 1 && t + 1 < nk, grp, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
+                     (uint32_t)(t + 1) * kRowB);
+    pp_stage<BM, BN>(l1, l0, t + 2 < nk, grp, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
+                     (uint32_t)(t + 2) * kRowB);
+  }
+  if (grp == 0) pp_barrier();
+}
+
 // nk: k-iterations of 64 to run (even, >= 2) starting at the byte offsets
 // a_off / b_off (which include the k origin); stride: row stride of both
 // buffers in bytes (K * 2). l0..l3: the LDS stage buffers (distinct objects,
@@ -313,7 +425,9 @@ __device__ __forceinline__ void tile_mainloop(__amdgpu_buffer_rsrc_t rA, uint32_
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / T::WGN, wn = wave % T::WGN;
   Frags<BM, BN> f0;
-  if constexpr (kBK == 64) {
+  if constexpr (kBK == 64 && kPingPong) {
+    tile_mainloop_pp<BM, BN>(rA, a_off, rB, b_off, stride, nk64, l0, l1, acc);
+  } else if constexpr (kBK == 64) {
     const int nk = nk64;   // even
     char* const lds0 = l0;
     char* const lds1 = l1;
