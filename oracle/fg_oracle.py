@@ -10,9 +10,9 @@ Pages cited (titles abbreviated):
   "NVLink atomic publish" = hardware atomic publish and monotonic counters over NVLink
   "DeepEP FIFO pipeline" = DeepEP v2 FIFO / streaming pipeline analysis
 
-Where the pages leave a step open, the reading taken is named in the docstring
-of the function that takes it (R-numbers refer to the list of readings kept with
-the design notes).
+Where the pages leave a step open, the reading taken is stated in the docstring
+of the function that takes it, under a label (R1, R2, ...) that later
+docstrings use to refer back to it.
 
 Every function here is pinned by tests against closed forms, invariants, hand
 worked examples, library special cases or brute force, except the latency

@@ -107,7 +107,7 @@ __device__ __forceinline__ void combine_push(const CombineArgs& a, const uint16_
     for (int r = 0; r < kPushPerWave; ++r)
 #pragma unroll
       for (int u = 0; u < 2 * kCombU; ++u)
-        v[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rs[r], (uint32_t)(c0 + u * 64 + lane) * 16, 0, kPolNT);
+        v[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rs[r], (uint32_t)(c0 + u * 64 + lane) * 16, 0, 0);
 #pragma unroll
     for (int r = 0; r < kPushPerWave; ++r)
 #pragma unroll

@@ -579,7 +579,7 @@ __device__ __forceinline__ void partial_sum_store(__amdgpu_buffer_rsrc_t rW, uin
         for (int q = 0; q < 8; ++q)
           v[q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                                rW, q < P ? base + (uint32_t)q * tile_bytes + o : 0xFFFFFFF0u, 0,
-                                               kPolCoherentStream));
+                                               kPolCoherentStore));
         f32x4 sum = v[0];
 #pragma unroll
         for (int q = 1; q < 8; ++q) sum += v[q];
