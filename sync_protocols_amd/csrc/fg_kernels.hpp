@@ -313,7 +313,7 @@ __device__ __forceinline__ void copy_batch_addr(uint64_t src, uint64_t dst, bool
   for (int r = 0; r < RB; ++r)
 #pragma unroll
     for (int u = 0; u < UPR; ++u)
-      v[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rs[r], (uint32_t)(u * 64 + lane) * 16, 0, kPolSC1 | kPolNT);
+      v[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rs[r], (uint32_t)(u * 64 + lane) * 16, 0, kPolSC1);
 #pragma unroll
   for (int r = 0; r < RB; ++r)
 #pragma unroll
