@@ -90,7 +90,8 @@ typedef struct {
   int32_t K;                   /* row width in bf16 elements; multiple of 128 */
   int32_t N;                   /* GEMM output width; multiple of 128 */
   int32_t n_groups;            /* 1 = one dense weight; >1 = one weight per group (expert) */
-  int32_t n_comm_wg;           /* communication workgroups (0 = default 128); they join the compute role
+  int32_t n_comm_wg;           /* communication workgroups (0 = three quarters of the compute units, 192 on
+                                  MI355X); they join the compute role
                                   once their rows are copied */
   int32_t n_gemm_wg;           /* dedicated compute workgroups (0 = CUs - n_comm_wg) */
   int32_t tile_n;              /* GEMM tile width 128 or 256 (0 = default) */
