@@ -62,7 +62,6 @@ __device__ __forceinline__ void store16_stream(__amdgpu_buffer_rsrc_t r, uint32_
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kPolNT);
 }
 
-__device__ __forceinline__ v4i load16_stream(const v4i* p) { return __builtin_nontemporal_load(p); }
 
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 
