@@ -169,7 +169,7 @@ __device__ __forceinline__ int batch_srow(const FusedArgs& a, int info) {
 // batch's loads are out.
 template <int UPR, bool strict>
 __device__ __forceinline__ void comm_batches(const FusedArgs& a, const uint16_t* const* sh_shard, int RB, int b,
-                                             int nw, int n_batches, uint32_t row_bytes, int lane, bool verify) {
+                                             int nw, int n_batches, uint32_t row_bytes, int lane) {
   constexpr int RM = 32 / UPR < 16 ? 32 / UPR : 16;   // rows of the register set
   v4i v[RM][UPR];
   auto load = [&](int binfo, int bsrow) {
@@ -189,8 +189,9 @@ __device__ __forceinline__ void comm_batches(const FusedArgs& a, const uint16_t*
         v[r][u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(u * 64 + lane) * 16, 0, 0);
     }
   };
-  // lane s holds shard s's stream length (the size of its last chunk), so
-  // that the election check reads it with a lane shuffle, not a dependent load
+  // lane s holds shard s's stream length (which fixes the size of its last
+  // chunk), so that the election check reads it with a lane shuffle rather
+  // than a dependent load
   const int slen = lane < a.n_shards ? a.stream_len[lane] : 0;
   int info = batch_info(a, batch_inv_word(a, b, RB, n_batches, lane), b, RB, n_batches, lane);
   load(info, batch_srow(a, info));
@@ -259,10 +260,9 @@ __device__ __forceinline__ void comm_batches(const FusedArgs& a, const uint16_t*
 
 template <int UPR>
 __device__ __forceinline__ void comm_batches_any(bool strict, const FusedArgs& a, const uint16_t* const* sh_shard,
-                                                 int RB, int b, int nw, int n_batches, uint32_t row_bytes, int lane,
-                                                 bool verify) {
-  if (strict) comm_batches<UPR, true>(a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
-  else comm_batches<UPR, false>(a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
+                                                 int RB, int b, int nw, int n_batches, uint32_t row_bytes, int lane) {
+  if (strict) comm_batches<UPR, true>(a, sh_shard, RB, b, nw, n_batches, row_bytes, lane);
+  else comm_batches<UPR, false>(a, sh_shard, RB, b, nw, n_batches, row_bytes, lane);
 }
 
 __device__ __forceinline__ void comm_role(const FusedArgs& a, const uint16_t* const* sh_shard) {
@@ -278,17 +278,16 @@ __device__ __forceinline__ void comm_role(const FusedArgs& a, const uint16_t* co
   const int upr = (a.K / 8 + 63) / 64;       // 64-lane units of 16 bytes per row
   const uint32_t row_bytes = (uint32_t)a.K * 2;
   const int nw = a.n_comm * kWaves;
-  const bool verify = a.flags & kVerify;
   const int b = cw * kWaves + wave;
   if (b >= n_batches) return;
   // bitwise row copy: 16-byte loads (default cache policy: the non-temporal hint made the
   // copy 20 % slower), device-coherent 16-byte stores
-  if (upr <= 1)       comm_batches_any<1>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
-  else if (upr <= 2)  comm_batches_any<2>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
-  else if (upr <= 4)  comm_batches_any<4>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
-  else if (upr <= 8)  comm_batches_any<8>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
-  else if (upr <= 16) comm_batches_any<16>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
-  else                comm_batches_any<32>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane, verify);
+  if (upr <= 1)       comm_batches_any<1>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane);
+  else if (upr <= 2)  comm_batches_any<2>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane);
+  else if (upr <= 4)  comm_batches_any<4>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane);
+  else if (upr <= 8)  comm_batches_any<8>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane);
+  else if (upr <= 16) comm_batches_any<16>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane);
+  else                comm_batches_any<32>(strict, a, sh_shard, RB, b, nw, n_batches, row_bytes, lane);
 }
 
 // ---------------------------------------------------------------------------
