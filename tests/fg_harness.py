@@ -87,12 +87,12 @@ def ep_case(seed, n_shards, tokens, K, N, n_experts=64, topk=8, n_local=8, exper
 
 
 def make_ctx(case: Case, *, n_comm=0, n_gemm=0, tile_n=0, timeout_ns=0, max_rows=None, split_parts=0,
-             split_tiles=0, tile_order=0, combine_wg=0) -> fg.Context:
+             split_tiles=0, tile_order=0, combine_wg=0, copy_rows=0) -> fg.Context:
     max_rows = max_rows or max(int(case.lay.stream_len.max()), case.rows_per_shard)
     cfg = fg.make_config(len(case.shards), max_rows, case.K, case.N, n_groups=case.n_groups,
                          n_comm_wg=n_comm, n_gemm_wg=n_gemm, tile_n=tile_n, timeout_ns=timeout_ns,
                          split_parts=split_parts, split_tiles=split_tiles, tile_order=tile_order,
-                         combine_wg=combine_wg)
+                         combine_wg=combine_wg, copy_rows=copy_rows)
     return fg.Context(cfg)
 
 

@@ -64,6 +64,16 @@ def test_ragged_odd_row_blocks():
     _run_and_check(case, 3)
 
 
+@pytest.mark.parametrize("K,copy_rows", [(256, 1), (256, 4), (1024, 1), (1024, 2), (4096, 2), (7168, 1)])
+def test_copy_batches_shorter_than_register_set(K, copy_rows):
+    """Copy batches of fewer rows than the register set holds (the copy_rows
+    setting): the unused register rows must neither load nor store, and every
+    row block and chunk still gets its signals."""
+    log(f"copy batches of {copy_rows} rows: 3 x 200 rows (ragged), K={K}, N=256, 8 copy workgroups")
+    case = dense_case(90 + copy_rows, 3, 200, K, 256)
+    _run_and_check(case, 3, ctx_kw=dict(copy_rows=copy_rows, n_comm=8, n_gemm=24))
+
+
 def test_explicit_route_equals_contiguous():
     log("explicit route carrying the contiguous layout")
     case = dense_case(34, 4, 256, 256, 512, use_explicit=True)
