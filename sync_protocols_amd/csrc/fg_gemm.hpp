@@ -481,11 +481,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
 }
 
+// Version words (the upper half of the inverse-map entry) of the rows this
+// lane stores, loaded when the tile starts so that the store does not wait for
+// them: row m is padding when its word is not the current route version.
+template <int BM, int BN>
+__device__ __forceinline__ void tile_row_versions(const unsigned long long* inv, int m0, uint32_t (&ver_w)[Tile<BM, BN>::FM]) {
+  using T = Tile<BM, BN>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / T::WGN;
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(inv);
+#pragma unroll
+  for (int fm = 0; fm < T::FM; ++fm) ver_w[fm] = words[2 * (m0 + wm * T::WM + fm * 32 + (lane & 31)) + 1];
+}
+
 // Store the tile: padding rows (no current inverse-map entry) are written as zeros.
-// rO: output rows [*, N] (row stride N*2 bytes); m0, n0: tile origin.
+// rO: output rows [*, N] (row stride N*2 bytes); m0, n0: tile origin; ver_w:
+// the rows' version words (tile_row_versions).
 template <int BM, int BN>
 __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int m0, int n0,
-                                           const Acc<BM, BN>& acc, const unsigned long long* inv, uint32_t ver) {
+                                           const Acc<BM, BN>& acc, const uint32_t (&ver_w)[Tile<BM, BN>::FM],
+                                           uint32_t ver) {
   using T = Tile<BM, BN>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / T::WGN, wn = wave % T::WGN;
@@ -493,7 +508,7 @@ __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int
 #pragma unroll
   for (int fm = 0; fm < T::FM; ++fm) {
     const int m = m0 + wm * T::WM + fm * 32 + lr;
-    const bool pad = (uint32_t)(inv[m] >> 32) != ver;   // versioned inverse map: stale = padding
+    const bool pad = ver_w[fm] != ver;   // versioned inverse map: stale = padding
     const uint32_t row_off = (uint32_t)m * (uint32_t)N * 2;
 #pragma unroll
     for (int fn = 0; fn < T::FN; ++fn) {

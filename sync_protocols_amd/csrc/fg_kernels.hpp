@@ -676,12 +676,14 @@ __device__ __forceinline__ bool run_item(const FusedArgs& a, char* const* lds, i
   for (int i = 0; i < T::FM; ++i)
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) acc.v[i][j] = f32x16{};
+  uint32_t ver_w[T::FM];
+  if (whole) tile_row_versions<BM, BN>(a.inv, m0, ver_w);
   // k0, k1 count k-iterations of 64 (128 bytes of a row)
   tile_mainloop<BM, BN>(rA, (uint32_t)m0 * row_bytes + (uint32_t)k0 * 128u, rB,
                         (uint32_t)n0 * row_bytes + (uint32_t)k0 * 128u, row_bytes, k1 - k0, lds[0], lds[1], lds[2],
                         lds[3], acc);
   if (whole) {
-    tile_store<BM, BN>(rO, a.N, m0, n0, acc, a.inv, a.route_ver);
+    tile_store<BM, BN>(rO, a.N, m0, n0, acc, ver_w, a.route_ver);
     return true;
   }
   // split-K part: blocks of one split tile are 256 x BN floats apart (the
@@ -785,11 +787,23 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
         }
       }
       int ok = tile >= 0;
+      int grp = 0;
       if (ok) {
         entry = a.slab[tile / L.n_tn];
         const int m0 = entry & ~1, bm = (entry & 1) ? 128 : 256;
         const long long t0 = (long long)now_ticks();
         uint32_t polls = 0;
+        // the item's weight group and the first poll of each of its row
+        // blocks' counters go out together: one round trip when the gates are
+        // open, instead of one per load
+        grp = a.group_of_rb[m0 / kRB];
+        const bool counters = !(a.flags & kGateWatermark);
+        int c0 = kRB, c1 = kRB;
+        if (counters) {
+          c0 = poll_relaxed(a.counter_cur + (size_t)(m0 / kRB) * kCtr);
+          if (bm == 256) c1 = poll_relaxed(a.counter_cur + (size_t)(m0 / kRB + 1) * kCtr);
+          polls += bm / kRB;
+        }
         if ((a.flags & kGateWatermark) && !(a.flags & kGemmOnly)) {   // compute only: nothing to wait for
           // contiguous layout: gathered row g is row g % R of shard g / R, so
           // the tile's rows are covered by whole 64-row chunks of the shard
@@ -801,10 +815,15 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
                          0x31000000 | (s * a.chunk_cap + c), &polls);
             g = s * R + min(R, (c + 1) * kChunk);
           }
-        } else if (!(a.flags & kGateWatermark)) {
-          for (int rb = m0 / kRB; rb < (m0 + bm) / kRB && ok; ++rb)
-            ok = wait_eq(a.counter_cur + (size_t)rb * kCtr, kRB, now_ticks() + a.timeout_ticks, a.err, rb, &polls,
-                         kBackoffLong);
+        } else if (counters) {
+          // a block not yet complete (or overshot) goes to the bounded wait,
+          // which also reports an overshoot
+          if (c0 != kRB)
+            ok = wait_eq(a.counter_cur + (size_t)(m0 / kRB) * kCtr, kRB, now_ticks() + a.timeout_ticks, a.err,
+                         m0 / kRB, &polls, kBackoffLong);
+          if (ok && c1 != kRB)
+            ok = wait_eq(a.counter_cur + (size_t)(m0 / kRB + 1) * kCtr, kRB, now_ticks() + a.timeout_ticks, a.err,
+                         m0 / kRB + 1, &polls, kBackoffLong);
         }
         const long long t_open = (long long)now_ticks();
         gate += t_open - t0;
@@ -822,17 +841,18 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
       sh[1] = ok;
       sh[3] = q;
       sh[4] = entry;
+      sh[5] = grp;
     }
     __syncthreads();
     const int tile = __builtin_amdgcn_readfirstlane(sh[0]);
     const int q = __builtin_amdgcn_readfirstlane(sh[3]);
     const int entry = __builtin_amdgcn_readfirstlane(sh[4]);
+    const int g = __builtin_amdgcn_readfirstlane(sh[5]);
     if (!sh[1]) break;
     // the tile reads the gathered rows with device-scope loads issued after the
     // gate poll returned 128; the formal acquire fence is the strict variant
     if (strict) acquire_agent();
     const int m0 = entry & ~1, n0 = (tile - (tile / L.n_tn) * L.n_tn) * BN;
-    const int g = __builtin_amdgcn_readfirstlane(a.group_of_rb[m0 / kRB]);
     const int tr_id = q < 0 ? tile : n_tiles + q;
     long long* tr = ((a.flags & kTrace) && q >= 0 && tr_id < a.trace_cap) ? a.trace + (size_t)tr_id * kTraceFields
                                                                             : nullptr;
@@ -862,7 +882,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs) {
   __shared__ __attribute__((aligned(16))) char lds3[kS23];
   char* const lds[4] = {lds0, lds1, lds2, lds3};
   __shared__ const uint16_t* sh_shard[FG_MAX_SHARDS];
-  __shared__ int sh[5];
+  __shared__ int sh[6];   // item broadcast: tile, ok, part ok, part, slab entry, group
   long long* wt = a.wgtime + (size_t)blockIdx.x * kWgTimeFields;
   const long long t_start = (long long)now_ticks();
   const long long c_start = (long long)__builtin_amdgcn_s_memtime();
