@@ -477,8 +477,10 @@ __device__ __forceinline__ void tile_mainloop(__amdgpu_buffer_rsrc_t rA, uint32_
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 l = (__bf16)lo, h = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+  // one v_cvt_pk_bf16_f32 (round to nearest even) for the pair
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // Version words (the upper half of the inverse-map entry) of the rows this
@@ -494,13 +496,12 @@ __device__ __forceinline__ void tile_row_versions(const unsigned long long* inv,
   for (int fm = 0; fm < T::FM; ++fm) ver_w[fm] = words[2 * (m0 + wm * T::WM + fm * 32 + (lane & 31)) + 1];
 }
 
-// Store the tile: padding rows (no current inverse-map entry) are written as zeros.
-// rO: output rows [*, N] (row stride N*2 bytes); m0, n0: tile origin; ver_w:
-// the rows' version words (tile_row_versions).
+// Direct store of the accumulators, 8 bytes per lane: rows as in tile_store,
+// for the variants whose stage buffers cannot hold a wave block per wave.
 template <int BM, int BN>
-__device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int m0, int n0,
-                                           const Acc<BM, BN>& acc, const uint32_t (&ver_w)[Tile<BM, BN>::FM],
-                                           uint32_t ver) {
+__device__ __forceinline__ void tile_store_direct(__amdgpu_buffer_rsrc_t rO, int N, int m0, int n0,
+                                                  const Acc<BM, BN>& acc, const uint32_t (&ver_w)[Tile<BM, BN>::FM],
+                                                  uint32_t ver) {
   using T = Tile<BM, BN>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / T::WGN, wn = wave % T::WGN;
@@ -508,7 +509,7 @@ __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int
 #pragma unroll
   for (int fm = 0; fm < T::FM; ++fm) {
     const int m = m0 + wm * T::WM + fm * 32 + lr;
-    const bool pad = ver_w[fm] != ver;   // versioned inverse map: stale = padding
+    const bool pad = ver_w[fm] != ver;
     const uint32_t row_off = (uint32_t)m * (uint32_t)N * 2;
 #pragma unroll
     for (int fn = 0; fn < T::FN; ++fn) {
@@ -520,6 +521,105 @@ __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int
         w[0] = pad ? 0 : (int)pack_bf16x2(c[4 * g + 0], c[4 * g + 1]);
         w[1] = pad ? 0 : (int)pack_bf16x2(c[4 * g + 2], c[4 * g + 3]);
         __builtin_amdgcn_raw_buffer_store_b64(w, rO, row_off + (uint32_t)n * 2, 0, 0);
+      }
+    }
+  }
+}
+
+// Store the tile: padding rows (no current inverse-map entry) are written as zeros.
+// rO: output rows [*, N] (row stride N*2 bytes); m0, n0: tile origin; ver_w:
+// the rows' version words (tile_row_versions); l0, l1: the two LDS stage
+// buffers, free once the K loop's last barrier has passed (waves 0-3 use l0,
+// waves 4-7 l1).
+//
+// A lane's accumulators hold 4 consecutive columns of one row per register
+// group, so stored directly every 8-byte store instruction would touch 32
+// rows (32 partial lines). Instead each wave rounds its (BM/2) x (BN/4) block to
+// bf16 into a private LDS block and reads it back with BN/32 lanes per row:
+// every global store instruction then writes whole rows of the wave's block
+// (8 x 128 bytes for BN = 256).
+// LDS block: one 32-row sub-block per fragment row fm, rows of BN/2 bytes;
+// logical 16-byte chunk c of row r sits in slot c ^ ((r / (256 / row bytes)) &
+// (chunks - 1)) as in swz, and in rows 16..31 the two 8-byte halves of every
+// chunk trade places. A write instruction (half-wave passes of 32 rows x 8
+// bytes of one chunk) then covers all 64 banks once, and a read pass (16 lanes
+// x 16 bytes) covers whole rows in distinct bank ranges. The rows of one read
+// are all below or all above row 16, so its halves are swapped back by the
+// choice of registers. Where a stage buffer cannot hold four waves' blocks
+// (the 32-k variant), the waves reuse one 32-row sub-block: LDS operations of
+// one wave complete in issue order, which keeps the reuse safe. The stage
+// buffers are next written by the following item's loads, after the
+// scheduler's workgroup barrier.
+template <int BM, int BN>
+__device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int m0, int n0,
+                                           const Acc<BM, BN>& acc, const uint32_t (&ver_w)[Tile<BM, BN>::FM],
+                                           uint32_t ver, char* l0, char* l1) {
+  using T = Tile<BM, BN>;
+  constexpr int RB = T::WN * 2;          // bytes per row of the wave's block
+  constexpr int CPR = RB / 16;           // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;          // rows per 64-lane 16-byte access
+  constexpr int D = 256 / RB;            // rows per 256-byte bank period
+  constexpr int SUB = 32 * RB;           // bytes of one 32-row sub-block
+  constexpr int NSUB = 4 * T::FM * SUB <= Tile<256, BN>::STAGE ? T::FM : 1;
+  static_assert(RPI == 8 || RPI == 16, "read-back rows per access");
+  if constexpr (kWaves != 8 || 4 * SUB > Tile<256, BN>::STAGE) {
+    tile_store_direct<BM, BN>(rO, N, m0, n0, acc, ver_w, ver);   // the 4-wave variant
+    return;
+  }
+  // the lane's offsets are computed here, not hoisted out of the tile loop,
+  // where they would hold registers through the K loop
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / T::WGN, wn = wave % T::WGN;
+  const int lr = lane & 31, kh = lane >> 5;
+  char* const blk = (wave < 4 ? l0 : l1) + (wave & 3) * (NSUB * SUB);
+  const int sw = ((lr / D) & (CPR - 1)) * 16;                   // write: slot permutation of row lr
+  char* const wrow = blk + lr * RB + (kh ^ (lr >> 4)) * 8;
+  const int rr = lane / CPR, rc = lane % CPR;                   // read: row within the access, chunk
+  // read offset of row i * RPI + rr, chunk rc: the row's slot permutation is
+  // (rr / D) xor a constant of i ((i * RPI / D) & (CPR - 1))
+  const int rslot = rc ^ (rr / D);
+  const int rbase = rr * RB;
+  const uint32_t row_bytes = (uint32_t)N * 2;
+  const uint32_t out_lane = (uint32_t)(m0 + wm * T::WM + rr) * row_bytes + (uint32_t)(n0 + wn * T::WN + rc * 8) * 2;
+#pragma unroll
+  for (int fm = 0; fm < T::FM; ++fm) {
+    char* const sub = wrow + (fm % NSUB) * SUB;
+    const bool pad = ver_w[fm] != ver;   // versioned inverse map: stale = padding
+#pragma unroll
+    for (int fn = 0; fn < T::FN; ++fn) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& c = acc.v[fm][fn];
+        v2i w;
+        w[0] = pad ? 0 : (int)pack_bf16x2(c[4 * g + 0], c[4 * g + 1]);
+        w[1] = pad ? 0 : (int)pack_bf16x2(c[4 * g + 2], c[4 * g + 3]);
+        *reinterpret_cast<v2i*>(sub + (((fn * 4 + g) * 16) ^ sw)) = w;
+      }
+    }
+    if constexpr (NSUB == T::FM) {
+      if (fm + 1 < T::FM) continue;   // all blocks written: read them back below
+    }
+    constexpr int F0 = NSUB == T::FM ? 0 : -1;   // first fragment row to read back
+#pragma unroll
+    for (int f = (F0 < 0 ? fm : 0); f <= fm; ++f) {
+      v4i x[32 / RPI];
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int k = (i * RPI / D) & (CPR - 1);
+        x[i] = *reinterpret_cast<const v4i*>(blk + (f % NSUB) * SUB + i * RPI * RB + rbase + (rslot ^ k) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const bool swapped = ((i * RPI) >> 4) & 1;
+        const v4i v = swapped ? v4i{x[i][2], x[i][3], x[i][0], x[i][1]} : x[i];
+        // the whole offset goes in the VGPR operand, soffset stays 0: a
+        // 16-byte store with a register soffset, followed at once by a VALU
+        // write of its data registers, stored the new values in some lanes
+        // (measured), and the compiler guards that hazard only for a
+        // constant soffset
+        __builtin_amdgcn_raw_buffer_store_b128(v, rO, out_lane + (uint32_t)(f * 32 + i * RPI) * row_bytes, 0, 0);
       }
     }
   }

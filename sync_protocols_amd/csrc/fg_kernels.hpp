@@ -683,7 +683,7 @@ __device__ __forceinline__ bool run_item(const FusedArgs& a, char* const* lds, i
                         (uint32_t)n0 * row_bytes + (uint32_t)k0 * 128u, row_bytes, k1 - k0, lds[0], lds[1], lds[2],
                         lds[3], acc);
   if (whole) {
-    tile_store<BM, BN>(rO, a.N, m0, n0, acc, ver_w, a.route_ver);
+    tile_store<BM, BN>(rO, a.N, m0, n0, acc, ver_w, a.route_ver, lds[0], lds[1]);
     return true;
   }
   // split-K part: blocks of one split tile are 256 x BN floats apart (the

@@ -58,6 +58,23 @@ def test_ragged_rows_128_tile():
     _run_and_check(case, 3, ctx_kw=dict(tile_n=128))
 
 
+@pytest.mark.parametrize("tile_n", [256, 128])
+def test_every_output_element_of_full_tiles_each_call(tile_n):
+    """Whole 256-row tiles in every column tile, every output element checked
+    after each of five calls: the tile's store path writes each wave's rows
+    through LDS in 16-byte pieces, and a wrong row, chunk or half-chunk there
+    shows up as scattered elements, which sampled checks would miss."""
+    log(f"contiguous: 4 x 512 rows, K=256, N=1024, BN {tile_n}: five calls, full check after each")
+    case = dense_case(35, 4, 512, 256, 1024)
+    ctx = make_ctx(case, tile_n=tile_n)
+    gathered, out = buffers(ctx, case)
+    for _ in range(5):
+        run_iters(ctx, case, gathered, out, 1, flags=fg.CALL_VERIFY)
+        check_gathered(case, gathered, poisoned=True)
+        check_out(case, out)
+    ctx.close()
+
+
 def test_ragged_odd_row_blocks():
     log("ragged contiguous: 3 x 100 rows (m_pad 384 -> BM 128 tiles), K=256, N=256")
     case = dense_case(33, 3, 100, 256, 256)
