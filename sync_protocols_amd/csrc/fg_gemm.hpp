@@ -152,12 +152,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // its own waits).
 //
 // Stage k lives in slot k&1 and k-step 0 of its fragments is already in
-// registers when the stage starts. Per stage: read k-steps 1..3, MFMAs of
-// k-steps 0 and 1, wait for this wave's loads of stage k+1, one workgroup
-// barrier (publishes stage k+1 from every wave and retires slot k&1, whose
-// fragments are all in registers by now), refill slot k&1 with stage k+2, read
-// k-step 0 of stage k+1, MFMAs of k-steps 2 and 3. The LDS latency after the
-// barrier hides behind the last 32 MFMAs.
+// registers when the stage starts. Per stage: read k-steps 1..3 and load the
+// weight rows of stage k+1 into the other slot during the MFMAs of k-steps 0
+// to 2, wait for this wave's loads of stage k+1, one workgroup barrier
+// (publishes stage k+1 from every wave and retires slot k&1, whose fragments
+// are all in registers by now), load the gathered rows of stage k+2 into slot
+// k&1 and read k-step 0 of stage k+1 during the MFMAs of k-step 3.
 // --- explicitly interleaved stage schedule -------------------------------
 // With one wave per SIMD nothing else fills the matrix pipe while a wave
 // issues memory instructions, so every LDS read and every global->LDS load is
@@ -200,39 +200,70 @@ __device__ __forceinline__ void stage_load_one(__amdgpu_buffer_rsrc_t rA, uint32
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)(lds + T::A_BYTES + blk * 1024), 16, voff, k0_bytes, 0, 0);
 }
 
+// Memory operations of one MFMA window: NR fragment reads and NL global->LDS
+// loads, interleaved (a load after every read while both last) so that loads
+// are not issued in bursts. mix_load(o) says whether op o is a load; its index
+// among the loads (or reads) is mix_index(o).
+template <int NR, int NL>
+struct Mix {
+  static constexpr int P = NR < NL ? NR : NL;
+  static constexpr int OPS = NR + NL;
+  __device__ static constexpr bool load(int o) { return o < 2 * P ? (o & 1) : NL > NR; }
+  __device__ static constexpr int index(int o) { return o < 2 * P ? o / 2 : P + (o - 2 * P); }
+};
+
 // Stage k in `cur`, its k-step 0 fragments already in f0.
 //   phase A: MFMAs of k-steps 0, 1, 2; the reads of k-step s+1 are issued in
 //            the shadow of k-step s's MFMAs (two fragment sets live at a time);
+//            in the shadow of k-steps 0 and 1, the weight half of stage k+1's
+//            loads into `nxt` (that slot's previous stage was retired by the
+//            last barrier, and it is first read in phase B);
 //   wait for this wave's loads of stage k+1; workgroup barrier (publishes
 //   stage k+1 from every wave and retires `cur`: all of its fragments are in
 //   registers now);
 //   phase B: MFMAs of k-step 3; in their shadow the reads of k-step 0 of stage
-//            k+1 and the refill of `cur` with stage k+2.
+//            k+1 and the gathered-row half of stage k+2's loads into `cur`.
+// A stage's loads take about half of it at the unit's 64 bytes per clock; the
+// split keeps that many loads from queueing behind one another in phase B,
+// where each wave would stall at the issue of its next load and leave the
+// matrix pipe idle.
 template <int BM, int BN, bool has_next, bool refill>
 __device__ __forceinline__ void stage_body(const char* cur, const char* nxt,
                                            Frags<BM, BN>& f0, Acc<BM, BN>& acc, int wm, int wn, int lane,
                                            __amdgpu_buffer_rsrc_t rA, uint32_t a_off, __amdgpu_buffer_rsrc_t rB,
-                                           uint32_t b_off, uint32_t stride, uint32_t k2_bytes, char* cur_w, int wave) {
+                                           uint32_t b_off, uint32_t stride, uint32_t k1_bytes, uint32_t k2_bytes,
+                                           char* cur_w, char* nxt_w, int wave) {
   using T = Tile<BM, BN>;
   constexpr int NM = T::FM * T::FN;        // MFMAs per k-step
   constexpr int NR = T::FM + T::FN;        // fragment reads per k-step
-  constexpr int OPS_B = NR + T::LOADS;
+  constexpr int LB0 = T::LOADS_B / 2;      // weight loads in k-step 0's shadow, the rest in k-step 1's
+  using M0 = Mix<NR, has_next ? LB0 : 0>;
+  using M1 = Mix<NR, has_next ? T::LOADS_B - LB0 : 0>;
+  using MB = Mix<NR, refill ? T::LOADS_A : 0>;
   const char* curB = cur + T::A_BYTES;
   Frags<BM, BN> f1, f2, f3;
-  // phase A, k-step 0 (reads k-step 1)
+  // phase A, k-step 0 (reads k-step 1, weight loads of stage k+1)
 #pragma unroll
   for (int j = 0; j < NM; ++j) {
     mfma_one<BM, BN>(f0, acc, j);
 #pragma unroll
-    for (int o = (j * NR) / NM; o < ((j + 1) * NR) / NM; ++o) frag_read_one<BM, BN>(cur, curB, f1, 1, o, wm, wn, lane);
+    for (int o = (j * M0::OPS) / NM; o < ((j + 1) * M0::OPS) / NM; ++o) {
+      if (M0::load(o)) stage_load_one<BM, BN>(rA, a_off, rB, b_off, stride, k1_bytes, nxt_w, wave, lane,
+                                              T::LOADS_A + M0::index(o));
+      else frag_read_one<BM, BN>(cur, curB, f1, 1, M0::index(o), wm, wn, lane);
+    }
     FG_SCHED_FENCE();
   }
-  // k-step 1 (reads k-step 2)
+  // k-step 1 (reads k-step 2, the other weight loads of stage k+1)
 #pragma unroll
   for (int j = 0; j < NM; ++j) {
     mfma_one<BM, BN>(f1, acc, j);
 #pragma unroll
-    for (int o = (j * NR) / NM; o < ((j + 1) * NR) / NM; ++o) frag_read_one<BM, BN>(cur, curB, f2, 2, o, wm, wn, lane);
+    for (int o = (j * M1::OPS) / NM; o < ((j + 1) * M1::OPS) / NM; ++o) {
+      if (M1::load(o)) stage_load_one<BM, BN>(rA, a_off, rB, b_off, stride, k1_bytes, nxt_w, wave, lane,
+                                              T::LOADS_A + LB0 + M1::index(o));
+      else frag_read_one<BM, BN>(cur, curB, f2, 2, M1::index(o), wm, wn, lane);
+    }
     FG_SCHED_FENCE();
   }
   // k-step 2 (reads k-step 3)
@@ -245,17 +276,14 @@ __device__ __forceinline__ void stage_body(const char* cur, const char* nxt,
   }
   if constexpr (has_next) wait_vmcnt<0>();
   __syncthreads();
-  // phase B, k-step 3 (reads k-step 0 of stage k+1, refills `cur` with stage k+2)
+  // phase B, k-step 3 (reads k-step 0 of stage k+1, gathered-row loads of stage k+2 into `cur`)
 #pragma unroll
   for (int j = 0; j < NM; ++j) {
     mfma_one<BM, BN>(f3, acc, j);
 #pragma unroll
-    for (int o = (j * OPS_B) / NM; o < ((j + 1) * OPS_B) / NM; ++o) {
-      if (o < NR) {
-        if constexpr (has_next) frag_read_one<BM, BN>(nxt, nxt + T::A_BYTES, f0, 0, o, wm, wn, lane);
-      } else {
-        if constexpr (refill) stage_load_one<BM, BN>(rA, a_off, rB, b_off, stride, k2_bytes, cur_w, wave, lane, o - NR);
-      }
+    for (int o = (j * MB::OPS) / NM; o < ((j + 1) * MB::OPS) / NM; ++o) {
+      if (MB::load(o)) stage_load_one<BM, BN>(rA, a_off, rB, b_off, stride, k2_bytes, cur_w, wave, lane, MB::index(o));
+      else if constexpr (has_next) frag_read_one<BM, BN>(nxt, nxt + T::A_BYTES, f0, 0, MB::index(o), wm, wn, lane);
     }
     FG_SCHED_FENCE();
   }
@@ -431,22 +459,24 @@ __device__ __forceinline__ void tile_mainloop(__amdgpu_buffer_rsrc_t rA, uint32_
     const int nk = nk64;   // even
     char* const lds0 = l0;
     char* const lds1 = l1;
+    // stage 0 whole, stage 1's gathered rows; its weight rows follow in stage 0's phase A
     stage_load<BM, kPolA>(rA, a_off, stride, 0, lds0, wave, lane);
     stage_load<BN, 0>(rB, b_off, stride, 0, lds0 + T::A_BYTES, wave, lane);
     stage_load<BM, kPolA>(rA, a_off, stride, kRowB, lds1, wave, lane);
-    stage_load<BN, 0>(rB, b_off, stride, kRowB, lds1 + T::A_BYTES, wave, lane);
-    wait_vmcnt<T::LOADS>();
+    wait_vmcnt<T::LOADS_A>();
     __syncthreads();
     frags_read<BM, BN>(lds0, lds0 + T::A_BYTES, f0, 0, wm, wn, lane);
     int kt = 0;
     for (; kt < nk - 2; kt += 2) {
       stage_body<BM, BN, true, true>(lds0, lds1, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
-                                     (uint32_t)(kt + 2) * kRowB, lds0, wave);
+                                     (uint32_t)(kt + 1) * kRowB, (uint32_t)(kt + 2) * kRowB, lds0, lds1, wave);
       stage_body<BM, BN, true, true>(lds1, lds0, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
-                                     (uint32_t)(kt + 3) * kRowB, lds1, wave);
+                                     (uint32_t)(kt + 2) * kRowB, (uint32_t)(kt + 3) * kRowB, lds1, lds0, wave);
     }
-    stage_body<BM, BN, true, false>(lds0, lds1, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, lds0, wave);
-    stage_body<BM, BN, false, false>(lds1, lds0, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, lds1, wave);
+    stage_body<BM, BN, true, false>(lds0, lds1, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
+                                    (uint32_t)(nk - 1) * kRowB, 0, lds0, lds1, wave);
+    stage_body<BM, BN, false, false>(lds1, lds0, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, 0, lds1,
+                                     lds0, wave);
   } else {
     const int nk = 2 * nk64;   // stages of 32 k; a multiple of 4
     char* const L[4] = {l0, l1, l2, l3};
