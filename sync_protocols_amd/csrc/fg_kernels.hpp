@@ -646,14 +646,17 @@ struct TileLists {
     return tile(x, len(x) - r(x) + (slot - base));
   }
   // tile index (slab * n_tn + column tile) of entry j of list x
-  __device__ int tile(int x, int j) const {
-    const int ns = slabs_of(x);
+  __device__ int tile(int x, int j) const { return tile_in(x, slabs_of(x), by_group ? gslab[x] : 0, j); }
+  // the same, given list x's slab count and (grouped lists) first slab, so that
+  // a workgroup's own list needs no table load per item
+  __device__ int tile_in(int x, int ns, int base, int j) const {
     const int g = j / (GS * n_tn);
     const int gs = min(GS, ns - g * GS);
     const int rr = j - g * GS * n_tn;
     const int ng = rr / (gs * GN), r2 = rr - ng * gs * GN;
     const int si = r2 / GN, nn = r2 - si * GN;
-    return slab_at(x, g * GS + si) * n_tn + ng * GN + nn;
+    const int si2 = g * GS + si;
+    return (by_group ? base + si2 : x + nx * si2) * n_tn + ng * GN + nn;
   }
 };
 
@@ -663,7 +666,7 @@ template <int BM, int BN>
 __device__ __forceinline__ bool run_item(const FusedArgs& a, char* const* lds, int* sh, int m0, int n0,
                                          int g, int q, int P, int nk2, bool strict, long long& gate,
                                          __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rO,
-                                         __amdgpu_buffer_rsrc_t rW, long long* tr) {
+                                         __amdgpu_buffer_rsrc_t rW, long long* tr, int* pf_tick, int& pf_j) {
   using T = Tile<BM, BN>;
   const bool whole = q < 0;
   const int part = whole ? 0 : q % P;
@@ -683,6 +686,10 @@ __device__ __forceinline__ bool run_item(const FusedArgs& a, char* const* lds, i
                         (uint32_t)n0 * row_bytes + (uint32_t)k0 * 128u, row_bytes, k1 - k0, lds[0], lds[1], lds[2],
                         lds[3], acc);
   if (whole) {
+    // thread 0 (when pf_tick is given): the next ticket goes out before the
+    // stores; the opaque zero keeps the atomic optimizer from rewriting the add
+    // into a wave-wide one whose result it needs at once
+    if (pf_tick) pf_j = fetch_add_relaxed(pf_tick + opaque_zero(), 1);
     tile_store<BM, BN>(rO, a.N, m0, n0, acc, ver_w, a.route_ver, lds[0], lds[1]);
     return true;
   }
@@ -723,7 +730,12 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
   L.n_tn = a.N / BN;
   L.n_slabs = __builtin_amdgcn_readfirstlane(a.desc[1]);
   L.nx = (a.tile_order == 0 && grid % kXcds == 0) ? kXcds : 1;
-  L.gslab = a.gslab;
+  // the group slab offsets (nine words) are read from LDS: the split tail
+  // walks them once per list for every part it hands out
+  __shared__ int sh_gslab[kXcds + 1];
+  if (threadIdx.x <= kXcds) sh_gslab[threadIdx.x] = a.gslab[threadIdx.x];
+  __syncthreads();
+  L.gslab = sh_gslab;
   L.by_group = L.nx == kXcds && __builtin_amdgcn_readfirstlane(a.desc[2]) == kXcds;
   const int per_list = grid / L.nx;                      // workgroups per list
   {
@@ -755,6 +767,7 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
   }
   const int x = blockIdx.x % L.nx;
   const int my_whole = L.len(x) - L.r(x);
+  const int my_ns = L.slabs_of(x), my_base = L.by_group ? L.gslab[x] : 0;
   const bool verify = a.flags & kVerify;
   const bool strict = a.flags & kStrict;
   const uint32_t row_bytes = (uint32_t)a.K * 2;
@@ -766,24 +779,33 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
   long long gate = 0;
   int tiles = 0, parts = 0;
   bool own_done = false;                                 // thread 0 only
+  // thread 0: the ticket of the next whole tile, taken when the current tile's
+  // K loop ends, so that its round trip overlaps the tile's store instead of
+  // following it; taken any earlier, a busy workgroup would hold tiles that
+  // others, joining later, could run sooner (valid while pf_valid; other lanes
+  // leave it undefined, so that no copy of the pending value forces a wait)
+  bool pf_valid = false;
+  int pf_j;
   const long long t_begin = (long long)now_ticks();
   for (;;) {
     if (threadIdx.x == 0) {
       const long long t_take = (long long)now_ticks();
       int tile = -1, q = -1, entry = 0;
-      if (!error_raised(a.err)) {
-        if (!own_done) {
-          const int j = fetch_add_relaxed(my_tick, 1);
-          if (j < my_whole) tile = L.tile(x, j);
-          else own_done = true;
-        }
-        if (tile < 0 && R > 0) {
-          q = fetch_add_relaxed(part_tick, 1);
-          if (q < R * P) {
-            tile = L.split_tile(q / P);
-          } else {
-            q = -1;
-          }
+      // the error flag is read with the item's first loads and examined once
+      // they are out (an item taken after an error is dropped)
+      const int err_word = poll_relaxed(a.err.dev + opaque_zero());   // stays a per-lane value until used
+      if (!own_done) {
+        const int j = pf_valid ? pf_j : fetch_add_relaxed(my_tick, 1);
+        pf_valid = false;
+        if (j < my_whole) tile = L.tile_in(x, my_ns, my_base, j);
+        else own_done = true;
+      }
+      if (tile < 0 && R > 0) {
+        q = fetch_add_relaxed(part_tick, 1);
+        if (q < R * P) {
+          tile = L.split_tile(q / P);
+        } else {
+          q = -1;
         }
       }
       int ok = tile >= 0;
@@ -804,6 +826,7 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
           if (bm == 256) c1 = poll_relaxed(a.counter_cur + (size_t)(m0 / kRB + 1) * kCtr);
           polls += bm / kRB;
         }
+        if (err_word != 0) ok = 0;
         if ((a.flags & kGateWatermark) && !(a.flags & kGemmOnly)) {   // compute only: nothing to wait for
           // contiguous layout: gathered row g is row g % R of shard g / R, so
           // the tile's rows are covered by whole 64-row chunks of the shard
@@ -818,7 +841,7 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
         } else if (counters) {
           // a block not yet complete (or overshot) goes to the bounded wait,
           // which also reports an overshoot
-          if (c0 != kRB)
+          if (ok && c0 != kRB)
             ok = wait_eq(a.counter_cur + (size_t)(m0 / kRB) * kCtr, kRB, now_ticks() + a.timeout_ticks, a.err,
                          m0 / kRB, &polls, kBackoffLong);
           if (ok && c1 != kRB)
@@ -856,8 +879,12 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
     const int tr_id = q < 0 ? tile : n_tiles + q;
     long long* tr = ((a.flags & kTrace) && q >= 0 && tr_id < a.trace_cap) ? a.trace + (size_t)tr_id * kTraceFields
                                                                             : nullptr;
-    const bool ok = (entry & 1) ? run_item<128, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr)
-                                : run_item<256, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr);
+    int* const pf_tick = (threadIdx.x == 0 && q < 0 && !own_done) ? my_tick : nullptr;
+    const bool ok = (entry & 1) ? run_item<128, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr,
+                                                    pf_tick, pf_j)
+                                : run_item<256, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr,
+                                                    pf_tick, pf_j);
+    if (pf_tick) pf_valid = true;
     if (!ok) break;
     if (q < 0) ++tiles; else ++parts;
     if ((a.flags & kTrace) && threadIdx.x == 0 && tr_id < a.trace_cap) a.trace[(size_t)tr_id * kTraceFields + 3] = now_ticks();
