@@ -35,16 +35,24 @@ COPY_BYTES = 1 << 29          # plain device copy used to calibrate the HBM byte
 
 
 def kernel_source_hash():
-    """sha256 of the HIP sources and the C header: traffic counters recorded for
-    other sources do not describe the kernel that runs."""
+    """sha256 of the code of the HIP sources and the C header (comments and
+    white space removed): traffic counters recorded for other code do not
+    describe the kernel that runs; an edited comment does not change it."""
     import hashlib
+    import re
+
+    def code(text):
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        return " ".join(text.split()).encode()
+
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sync_protocols_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
-    with open(os.path.join(ROOT, "include", "fg.h"), "rb") as f:
-        h.update(f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + code(f.read()))
+    with open(os.path.join(ROOT, "include", "fg.h"), encoding="utf-8") as f:
+        h.update(code(f.read()))
     return h.hexdigest()
 
 

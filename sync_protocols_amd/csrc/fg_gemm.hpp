@@ -8,8 +8,9 @@
 // Tile BM x BN, eight waves as 2 x 4 (two per SIMD), each wave (BM/2) x (BN/4) built from
 // v_mfma_f32_32x32x16_bf16 fragments. The weight tile is the MFMA "A" operand
 // and the gathered tile the "B" operand, so that each lane's four consecutive
-// accumulator values are four consecutive output columns of one row (8-byte
-// stores). Lane layout (measured on the part): A/B operand lane l holds row/col
+// accumulator values are four consecutive output columns of one row; the
+// epilogue (tile_store) regroups them through LDS into 16-byte pieces of whole
+// rows. Lane layout (measured on the part): A/B operand lane l holds row/col
 // l % 32 and k = 8 * (l / 32) + 0..7; result register v of lane l is
 // D[8 * (v / 4) + 4 * (l / 32) + v % 4][l % 32].
 //
