@@ -592,65 +592,65 @@ __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int
   constexpr int D = 256 / RB;            // rows per 256-byte bank period
   constexpr int SUB = 32 * RB;           // bytes of one 32-row sub-block
   constexpr int NSUB = 4 * T::FM * SUB <= Tile<256, BN>::STAGE ? T::FM : 1;
-  static_assert(RPI == 8 || RPI == 16, "read-back rows per access");
   if constexpr (kWaves != 8 || 4 * SUB > Tile<256, BN>::STAGE) {
     tile_store_direct<BM, BN>(rO, N, m0, n0, acc, ver_w, ver);   // the 4-wave variant
-    return;
-  }
-  // the lane's offsets are computed here, not hoisted out of the tile loop,
-  // where they would hold registers through the K loop
-  int lane = threadIdx.x & 63;
-  asm volatile("" : "+v"(lane));
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / T::WGN, wn = wave % T::WGN;
-  const int lr = lane & 31, kh = lane >> 5;
-  char* const blk = (wave < 4 ? l0 : l1) + (wave & 3) * (NSUB * SUB);
-  const int sw = ((lr / D) & (CPR - 1)) * 16;                   // write: slot permutation of row lr
-  char* const wrow = blk + lr * RB + (kh ^ (lr >> 4)) * 8;
-  const int rr = lane / CPR, rc = lane % CPR;                   // read: row within the access, chunk
-  // read offset of row i * RPI + rr, chunk rc: the row's slot permutation is
-  // (rr / D) xor a constant of i ((i * RPI / D) & (CPR - 1))
-  const int rslot = rc ^ (rr / D);
-  const int rbase = rr * RB;
-  const uint32_t row_bytes = (uint32_t)N * 2;
-  const uint32_t out_lane = (uint32_t)(m0 + wm * T::WM + rr) * row_bytes + (uint32_t)(n0 + wn * T::WN + rc * 8) * 2;
+  } else {
+    static_assert(RPI == 8 || RPI == 16, "read-back rows per access");
+    // the lane's offsets are computed here, not hoisted out of the tile loop,
+    // where they would hold registers through the K loop
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / T::WGN, wn = wave % T::WGN;
+    const int lr = lane & 31, kh = lane >> 5;
+    char* const blk = (wave < 4 ? l0 : l1) + (wave & 3) * (NSUB * SUB);
+    const int sw = ((lr / D) & (CPR - 1)) * 16;                   // write: slot permutation of row lr
+    char* const wrow = blk + lr * RB + (kh ^ (lr >> 4)) * 8;
+    const int rr = lane / CPR, rc = lane % CPR;                   // read: row within the access, chunk
+    // read offset of row i * RPI + rr, chunk rc: the row's slot permutation is
+    // (rr / D) xor a constant of i ((i * RPI / D) & (CPR - 1))
+    const int rslot = rc ^ (rr / D);
+    const int rbase = rr * RB;
+    const uint32_t row_bytes = (uint32_t)N * 2;
+    const uint32_t out_lane = (uint32_t)(m0 + wm * T::WM + rr) * row_bytes + (uint32_t)(n0 + wn * T::WN + rc * 8) * 2;
 #pragma unroll
-  for (int fm = 0; fm < T::FM; ++fm) {
-    char* const sub = wrow + (fm % NSUB) * SUB;
-    const bool pad = ver_w[fm] != ver;   // versioned inverse map: stale = padding
+    for (int fm = 0; fm < T::FM; ++fm) {
+      char* const sub = wrow + (fm % NSUB) * SUB;
+      const bool pad = ver_w[fm] != ver;   // versioned inverse map: stale = padding
 #pragma unroll
-    for (int fn = 0; fn < T::FN; ++fn) {
+      for (int fn = 0; fn < T::FN; ++fn) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x16& c = acc.v[fm][fn];
-        v2i w;
-        w[0] = pad ? 0 : (int)pack_bf16x2(c[4 * g + 0], c[4 * g + 1]);
-        w[1] = pad ? 0 : (int)pack_bf16x2(c[4 * g + 2], c[4 * g + 3]);
-        *reinterpret_cast<v2i*>(sub + (((fn * 4 + g) * 16) ^ sw)) = w;
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& c = acc.v[fm][fn];
+          v2i w;
+          w[0] = pad ? 0 : (int)pack_bf16x2(c[4 * g + 0], c[4 * g + 1]);
+          w[1] = pad ? 0 : (int)pack_bf16x2(c[4 * g + 2], c[4 * g + 3]);
+          *reinterpret_cast<v2i*>(sub + (((fn * 4 + g) * 16) ^ sw)) = w;
+        }
       }
-    }
-    if constexpr (NSUB == T::FM) {
-      if (fm + 1 < T::FM) continue;   // all blocks written: read them back below
-    }
-    constexpr int F0 = NSUB == T::FM ? 0 : -1;   // first fragment row to read back
-#pragma unroll
-    for (int f = (F0 < 0 ? fm : 0); f <= fm; ++f) {
-      v4i x[32 / RPI];
-#pragma unroll
-      for (int i = 0; i < 32 / RPI; ++i) {
-        const int k = (i * RPI / D) & (CPR - 1);
-        x[i] = *reinterpret_cast<const v4i*>(blk + (f % NSUB) * SUB + i * RPI * RB + rbase + (rslot ^ k) * 16);
+      if constexpr (NSUB == T::FM) {
+        if (fm + 1 < T::FM) continue;   // all blocks written: read them back below
       }
+      constexpr int F0 = NSUB == T::FM ? 0 : -1;   // first fragment row to read back
 #pragma unroll
-      for (int i = 0; i < 32 / RPI; ++i) {
-        const bool swapped = ((i * RPI) >> 4) & 1;
-        const v4i v = swapped ? v4i{x[i][2], x[i][3], x[i][0], x[i][1]} : x[i];
-        // the whole offset goes in the VGPR operand, soffset stays 0: a
-        // 16-byte store with a register soffset, followed at once by a VALU
-        // write of its data registers, stored the new values in some lanes
-        // (measured), and the compiler guards that hazard only for a
-        // constant soffset
-        __builtin_amdgcn_raw_buffer_store_b128(v, rO, out_lane + (uint32_t)(f * 32 + i * RPI) * row_bytes, 0, 0);
+      for (int f = (F0 < 0 ? fm : 0); f <= fm; ++f) {
+        v4i x[32 / RPI];
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+          const int k = (i * RPI / D) & (CPR - 1);
+          x[i] = *reinterpret_cast<const v4i*>(blk + (f % NSUB) * SUB + i * RPI * RB + rbase + (rslot ^ k) * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+          const bool swapped = ((i * RPI) >> 4) & 1;
+          const v4i v = swapped ? v4i{x[i][2], x[i][3], x[i][0], x[i][1]} : x[i];
+          // the whole offset goes in the VGPR operand, soffset stays 0: a
+          // 16-byte store with a register soffset, followed at once by a VALU
+          // write of its data registers, stored the new values in some lanes
+          // (measured), and the compiler guards that hazard only for a
+          // constant soffset
+          __builtin_amdgcn_raw_buffer_store_b128(v, rO, out_lane + (uint32_t)(f * 32 + i * RPI) * row_bytes, 0, 0);
+        }
       }
     }
   }
