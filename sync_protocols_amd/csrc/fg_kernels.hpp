@@ -736,7 +736,13 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
   if (threadIdx.x <= kXcds) sh_gslab[threadIdx.x] = a.gslab[threadIdx.x];
   __syncthreads();
   L.gslab = sh_gslab;
-  L.by_group = L.nx == kXcds && __builtin_amdgcn_readfirstlane(a.desc[2]) == kXcds;
+  const int n_groups = __builtin_amdgcn_readfirstlane(a.desc[2]);
+  L.by_group = L.nx == kXcds && n_groups == kXcds;
+  // one group (the dense routes): the slab table holds 256-row slabs in order,
+  // the last one of 128 rows when m_pad is an odd multiple of 128, and every row
+  // block is in group 0, so an item's slab entry and group are computed here
+  // instead of loaded (one round trip less before each item)
+  const bool one_group = n_groups == 1;
   const int per_list = grid / L.nx;                      // workgroups per list
   {
     int gn = 1;
@@ -811,14 +817,15 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
       int ok = tile >= 0;
       int grp = 0;
       if (ok) {
-        entry = a.slab[tile / L.n_tn];
+        const int si = tile / L.n_tn;
+        entry = one_group ? ((si << 8) | (si == (m_pad >> 8) ? 1 : 0)) : a.slab[si];
         const int m0 = entry & ~1, bm = (entry & 1) ? 128 : 256;
         const long long t0 = (long long)now_ticks();
         uint32_t polls = 0;
         // the item's weight group and the first poll of each of its row
         // blocks' counters go out together: one round trip when the gates are
         // open, instead of one per load
-        grp = a.group_of_rb[m0 / kRB];
+        grp = one_group ? 0 : a.group_of_rb[m0 / kRB];
         const bool counters = !(a.flags & kGateWatermark);
         int c0 = kRB, c1 = kRB;
         if (counters) {
