@@ -1057,8 +1057,11 @@ __device__ void build_slabs(const int* goff, int n_groups, int* slab, int* gslab
 }
 
 // Seeds, group of each row block, arming, row slabs; real(rb) gives the real rows of rb.
+// failed: the route was rejected (m_pad is then 0 and goff may be invalid, so no
+// slab is built and the descriptor reports no groups); an empty valid route
+// keeps its groups, all of them empty.
 template <class Real>
-__device__ void route_finish(const RouteArgs& a, int m_pad, const int* goff, int n_groups, Real real) {
+__device__ void route_finish(const RouteArgs& a, int m_pad, const int* goff, int n_groups, bool failed, Real real) {
   const int n_rb = m_pad / kRB;
   for (int rb = threadIdx.x; rb < a.rb_cap; rb += blockDim.x) {
     int sd = 0, g = 0;
@@ -1074,7 +1077,7 @@ __device__ void route_finish(const RouteArgs& a, int m_pad, const int* goff, int
   for (int i = threadIdx.x; i < a.n_shards * a.chunk_cap; i += blockDim.x) a.elect_cur[i] = 0;
   if ((int)threadIdx.x <= n_groups) a.group_off_out[threadIdx.x] = goff[threadIdx.x];
   if (threadIdx.x == 0) a.desc[0] = m_pad;
-  build_slabs(goff, m_pad > 0 ? n_groups : 0, a.slab, a.gslab, a.desc);
+  build_slabs(goff, failed ? 0 : n_groups, a.slab, a.gslab, a.desc);
 }
 
 // CONTIG: shard s row i -> gathered row s*R + i; everything is arithmetic, so
@@ -1135,7 +1138,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_explicit_kernel(RouteArgs
   if ((int)threadIdx.x < a.n_shards) a.stream_len[threadIdx.x] = a.stream_len_in[threadIdx.x];
   __syncthreads();
   const int fail = __hip_atomic_load(a.ticket + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  route_finish(a, fail ? 0 : a.m_pad, sh_goff, a.n_groups, [&](int rb) {
+  route_finish(a, fail ? 0 : a.m_pad, sh_goff, a.n_groups, fail != 0, [&](int rb) {
     return __hip_atomic_load(a.rbcount + rb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   });
   __syncthreads();
@@ -1241,7 +1244,7 @@ __device__ void topk_scan_finish(const RouteArgs& a, int* sh_goff, int* sh_ne) {
   }
   __syncthreads();
   const int fail = __hip_atomic_load(a.ticket + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  route_finish(a, fail ? 0 : sh_goff[E], sh_goff, E, [&](int rb) {
+  route_finish(a, fail ? 0 : sh_goff[E], sh_goff, E, fail != 0, [&](int rb) {
     int real = 0;
     for (int j = 0; j < E; ++j)
       if (rb * kRB >= sh_goff[j] && rb * kRB < sh_goff[j + 1]) real = min(kRB, max(0, sh_ne[j] - (rb * kRB - sh_goff[j])));

@@ -1,0 +1,60 @@
+"""Seeded random configurations through the C ABI, each checked element by
+element against the oracle: dense routes (contiguous, explicit, permutation)
+and top-k expert routes, ragged row counts, both tile widths, and varied copy
+and compute workgroup counts and copy batch sizes. Every case is drawn from a
+fixed seed, so a failure names a reproducible configuration."""
+import numpy as np
+import pytest
+
+from sync_protocols_amd import fg
+from fg_harness import (buffers, check_control_plane, check_gathered, check_out, check_route, control_plane,
+                        dense_case, ep_case, log, make_ctx, run_iters)
+
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _draw(seed):
+    rng = np.random.default_rng(seed)
+    kind = ["contig", "explicit", "perm", "ep"][seed % 4]
+    K = int(rng.choice([128, 256, 384, 640, 1024]))
+    tile_n = int(rng.choice([128, 256]))
+    N = tile_n * int(rng.integers(1, 5))
+    n_comm = int(rng.choice([0, 8, 24]))
+    n_gemm = int(rng.choice([0, 16, 40])) if n_comm else 0
+    copy_rows = int(rng.choice([0, 1, 2, 4]))
+    if kind == "ep":
+        n_experts = int(rng.choice([8, 16]))
+        topk = int(rng.integers(1, 4))
+        n_local = int(rng.choice([2, 4, 8]))
+        shape = dict(n_shards=int(rng.integers(1, 7)), tokens=int(rng.integers(1, 200)), n_experts=n_experts,
+                     topk=topk, n_local=min(n_local, n_experts))
+    else:
+        shape = dict(n_shards=int(rng.integers(1, 9)), rows=int(rng.integers(1, 700)))
+    return kind, K, N, tile_n, n_comm, n_gemm, copy_rows, shape
+
+
+@pytest.mark.parametrize("seed", list(range(100, 116)))
+def test_random_configuration(seed):
+    kind, K, N, tile_n, n_comm, n_gemm, copy_rows, shape = _draw(seed)
+    log(f"seed {seed}: {kind} {shape} K={K} N={N} tile_n={tile_n} n_comm={n_comm} n_gemm={n_gemm} "
+        f"copy_rows={copy_rows}")
+    if kind == "ep":
+        case = ep_case(seed, shape["n_shards"], shape["tokens"], K, N, n_experts=shape["n_experts"],
+                       topk=shape["topk"], n_local=shape["n_local"])
+    else:
+        case = dense_case(seed, shape["n_shards"], shape["rows"], K, N,
+                          gather="permutation" if kind == "perm" else "contiguous",
+                          use_explicit=kind == "explicit")
+    ctx = make_ctx(case, n_comm=n_comm, n_gemm=n_gemm, tile_n=tile_n, copy_rows=copy_rows)
+    gathered, out = buffers(ctx, case)
+    iters = 2
+    st = run_iters(ctx, case, gathered, out, iters, flags=fg.CALL_VERIFY)
+    cp = control_plane(ctx, len(case.shards))
+    check_route(case, cp)
+    check_control_plane(case, cp, iters, iters)
+    check_gathered(case, gathered, poisoned=True)
+    check_out(case, out)
+    assert st.publishes == iters * O.signal_counts(case.lay)["publishes"]
+    ctx.close()
