@@ -1,8 +1,10 @@
 """Seeded random configurations through the C ABI, each checked element by
 element against the oracle: dense routes (contiguous, explicit, permutation)
 and top-k expert routes, ragged row counts, both tile widths, and varied copy
-and compute workgroup counts and copy batch sizes. Every case is drawn from a
-fixed seed, so a failure names a reproducible configuration."""
+and compute workgroup counts and copy batch sizes; the wider set adds up to 64
+experts, longer rows and forced split-K tails. Every case is drawn from a fixed
+seed, so a failure names a reproducible configuration (seed 115 is a top-k
+route with no local pick: an empty layout)."""
 import numpy as np
 import pytest
 
@@ -35,11 +37,29 @@ def _draw(seed):
     return kind, K, N, tile_n, n_comm, n_gemm, copy_rows, shape
 
 
-@pytest.mark.parametrize("seed", list(range(100, 116)))
-def test_random_configuration(seed):
-    kind, K, N, tile_n, n_comm, n_gemm, copy_rows, shape = _draw(seed)
+def _draw_wide(seed):
+    rng = np.random.default_rng(seed)
+    kind = ["contig", "explicit", "perm", "ep"][seed % 4]
+    K = int(rng.choice([128, 256, 384, 640, 1024, 2048]))
+    tile_n = int(rng.choice([128, 256]))
+    N = tile_n * int(rng.integers(1, 7))
+    n_comm = int(rng.choice([0, 8, 24, 64]))
+    n_gemm = int(rng.choice([0, 16, 40])) if n_comm else 0
+    copy_rows = int(rng.choice([0, 1, 2, 4]))
+    split_parts = int(rng.choice([0, 0, 2, 4]))
+    split_tiles = int(rng.choice([0, 0, 8])) if split_parts else 0
+    if kind == "ep":
+        n_experts = int(rng.choice([8, 16, 64]))
+        shape = dict(n_shards=int(rng.integers(1, 9)), tokens=int(rng.integers(1, 400)), n_experts=n_experts,
+                     topk=int(rng.integers(1, 5)), n_local=int(min(n_experts, rng.choice([1, 2, 4, 8, 16]))))
+    else:
+        shape = dict(n_shards=int(rng.integers(1, 9)), rows=int(rng.integers(1, 1500)))
+    return kind, K, N, tile_n, n_comm, n_gemm, copy_rows, shape, dict(split_parts=split_parts, split_tiles=split_tiles)
+
+
+def _check(seed, kind, K, N, tile_n, n_comm, n_gemm, copy_rows, shape, split):
     log(f"seed {seed}: {kind} {shape} K={K} N={N} tile_n={tile_n} n_comm={n_comm} n_gemm={n_gemm} "
-        f"copy_rows={copy_rows}")
+        f"copy_rows={copy_rows} {split}")
     if kind == "ep":
         case = ep_case(seed, shape["n_shards"], shape["tokens"], K, N, n_experts=shape["n_experts"],
                        topk=shape["topk"], n_local=shape["n_local"])
@@ -47,7 +67,7 @@ def test_random_configuration(seed):
         case = dense_case(seed, shape["n_shards"], shape["rows"], K, N,
                           gather="permutation" if kind == "perm" else "contiguous",
                           use_explicit=kind == "explicit")
-    ctx = make_ctx(case, n_comm=n_comm, n_gemm=n_gemm, tile_n=tile_n, copy_rows=copy_rows)
+    ctx = make_ctx(case, n_comm=n_comm, n_gemm=n_gemm, tile_n=tile_n, copy_rows=copy_rows, **split)
     gathered, out = buffers(ctx, case)
     iters = 2
     st = run_iters(ctx, case, gathered, out, iters, flags=fg.CALL_VERIFY)
@@ -58,3 +78,14 @@ def test_random_configuration(seed):
     check_out(case, out)
     assert st.publishes == iters * O.signal_counts(case.lay)["publishes"]
     ctx.close()
+
+
+@pytest.mark.parametrize("seed", list(range(100, 116)))
+def test_random_configuration(seed):
+    _check(seed, *_draw(seed), {})
+
+
+@pytest.mark.parametrize("seed", list(range(200, 224)))
+def test_random_configuration_wide(seed):
+    *rest, split = _draw_wide(seed)
+    _check(seed, *rest, split)
