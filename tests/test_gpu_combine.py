@@ -305,3 +305,28 @@ def test_combine_invalid_arguments():
     torch.cuda.synchronize()
     assert r.ctx.stats().error_code == 0
     r.close()
+
+
+@pytest.mark.parametrize("seed", list(range(400, 412)))
+def test_combine_random_configuration(seed):
+    """Seeded random combine configurations: shards, tokens, row widths, expert
+    counts, top-k, the local expert window and its base, and the combine grid;
+    two calls, staging rows, outputs and the combine control plane checked."""
+    rng = np.random.default_rng(seed)
+    S = int(rng.integers(1, 9))
+    T = int(rng.integers(1, 400))
+    n_experts = int(rng.choice([8, 16, 64]))
+    topk = int(rng.integers(1, min(8, n_experts) + 1))
+    n_local = int(rng.integers(1, min(16, n_experts) + 1))
+    base = int(rng.integers(0, n_experts - n_local + 1))
+    N = 128 * int(rng.integers(1, 24))
+    combine_wg = int(rng.choice([0, 1, 7, 64]))
+    log(f"seed {seed}: combine {S} shards x {T} tokens, top-{topk} of {n_experts}, {n_local} local at {base}, "
+        f"N={N}, combine_wg={combine_wg}")
+    case = ep_case(seed, S, T, 128, N, n_experts=n_experts, topk=topk, n_local=n_local, expert_base=base)
+    r = CombineRun(case, ctx_kw=dict(combine_wg=combine_wg))
+    r.dispatch()
+    for t in range(2):
+        r.combine(seed * 10 + t, flags=fg.CALL_VERIFY)
+    r.check_plane(2, verify_iters=2)
+    r.close()
