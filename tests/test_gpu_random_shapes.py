@@ -2,7 +2,8 @@
 element against the oracle: dense routes (contiguous, explicit, permutation)
 and top-k expert routes, ragged row counts, both tile widths, and varied copy
 and compute workgroup counts and copy batch sizes; the wider set adds up to 64
-experts, longer rows and forced split-K tails. Every case is drawn from a fixed
+experts, longer rows, forced split-K tails and the call flags (strict fences,
+watermark gating, the two-pass layout, tracing). Every case is drawn from a fixed
 seed, so a failure names a reproducible configuration (seed 115 is a top-k
 route with no local pick: an empty layout)."""
 import numpy as np
@@ -57,9 +58,25 @@ def _draw_wide(seed):
     return kind, K, N, tile_n, n_comm, n_gemm, copy_rows, shape, dict(split_parts=split_parts, split_tiles=split_tiles)
 
 
-def _check(seed, kind, K, N, tile_n, n_comm, n_gemm, copy_rows, shape, split):
+def _flags(seed, kind):
+    """Extra call flags of the wider set: strict fences, watermark gating
+    (contiguous routes only), the two-pass top-k layout, per-item tracing."""
+    rng = np.random.default_rng(seed + 7)
+    flags = 0
+    if rng.random() < 0.5:
+        flags |= fg.CALL_STRICT
+    if kind == "contig" and rng.random() < 0.6:
+        flags |= fg.CALL_GATE_WATERMARK
+    if kind == "ep" and rng.random() < 0.5:
+        flags |= fg.CALL_LAYOUT_TWO_PASS
+    if rng.random() < 0.3:
+        flags |= fg.CALL_TRACE
+    return flags
+
+
+def _check(seed, kind, K, N, tile_n, n_comm, n_gemm, copy_rows, shape, split, flags=0):
     log(f"seed {seed}: {kind} {shape} K={K} N={N} tile_n={tile_n} n_comm={n_comm} n_gemm={n_gemm} "
-        f"copy_rows={copy_rows} {split}")
+        f"copy_rows={copy_rows} {split} flags={flags:#x}")
     if kind == "ep":
         case = ep_case(seed, shape["n_shards"], shape["tokens"], K, N, n_experts=shape["n_experts"],
                        topk=shape["topk"], n_local=shape["n_local"])
@@ -70,7 +87,7 @@ def _check(seed, kind, K, N, tile_n, n_comm, n_gemm, copy_rows, shape, split):
     ctx = make_ctx(case, n_comm=n_comm, n_gemm=n_gemm, tile_n=tile_n, copy_rows=copy_rows, **split)
     gathered, out = buffers(ctx, case)
     iters = 2
-    st = run_iters(ctx, case, gathered, out, iters, flags=fg.CALL_VERIFY)
+    st = run_iters(ctx, case, gathered, out, iters, flags=fg.CALL_VERIFY | flags)
     cp = control_plane(ctx, len(case.shards))
     check_route(case, cp)
     check_control_plane(case, cp, iters, iters)
@@ -88,4 +105,4 @@ def test_random_configuration(seed):
 @pytest.mark.parametrize("seed", list(range(200, 224)))
 def test_random_configuration_wide(seed):
     *rest, split = _draw_wide(seed)
-    _check(seed, *rest, split)
+    _check(seed, *rest, split, _flags(seed, rest[0]))
