@@ -61,10 +61,13 @@ def f64_to_bf16(x) -> np.ndarray:
 
 
 def bf16_ulp(x) -> np.ndarray:
-    """Spacing of the bf16 grid at |x| (8 significant bits)."""
+    """Spacing of the bf16 grid at |x| (8 significant bits): 2**(e - 8) for
+    |x| = m * 2**e with m in [0.5, 1); from 2**-126 down to zero the grid is the
+    subnormal step 2**-133. frexp reports e = 0 for zero, so zero is mapped to
+    the subnormal exponent explicitly."""
     ax = np.abs(np.asarray(x, dtype=np.float64))
     _, e = np.frexp(ax)
-    e = np.maximum(e, -125)
+    e = np.where(ax == 0.0, -125, np.maximum(e, -125))
     return np.ldexp(1.0, (e - 8).astype(np.int32))
 
 

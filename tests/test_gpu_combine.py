@@ -92,11 +92,15 @@ class CombineRun:
         y64 = O.combine(ob, w, self.topk_np, c.expert_base, c.n_groups, c.lay)
         tol = O.combine_tolerance(ob, w, self.topk_np, c.expert_base, c.n_groups, c.lay)
         worst = 0.0
+        lo, hi = c.expert_base, c.expert_base + c.n_groups
         for s in range(self.S):
             yb = O.bf16_to_f64(bits(self.y[s]))
             d = np.abs(yb - y64[s])
             assert np.all(d <= tol[s]), f"shard {s}: max excess {float((d - tol[s]).max()):.3g}"
             worst = max(worst, float((d / tol[s]).max()))
+            # tokens with no local pick: exactly zero rows
+            none = ~np.any((self.topk_np[s] >= lo) & (self.topk_np[s] < hi), axis=1)
+            assert np.all(yb[none] == 0.0), f"shard {s}: a token without a local pick has a nonzero row"
         return worst
 
     def check_plane(self, t, verify_iters=None):

@@ -41,6 +41,26 @@ def test_bf16_hand_cases():
         assert int(O.f64_to_bf16(np.array([_num(val)]))[0]) == int(hexbits, 16), (val, _why)
 
 
+def test_bf16_ulp_hand_cases():
+    # grid spacing worked out from the format; zero's neighbour is the
+    # smallest subnormal, so ulp(0) is 2^-133 like the rest of the subnormals
+    g = _golden("bf16_cases.json")
+    for val, want, why in g["ulp"]:
+        got = float(O.bf16_ulp(np.array([_num(val)]))[0])
+        assert got == _num(want), (val, got, why)
+
+
+def test_bf16_ulp_is_the_gap_to_the_next_pattern():
+    # every finite non-negative pattern except the largest: ulp equals the
+    # distance to the next larger bf16 (a brute-force check over the format)
+    b = np.arange(0, 0x7F7F, dtype=np.uint16)
+    v = O.bf16_to_f64(b)
+    nxt = O.bf16_to_f64(b + np.uint16(1))
+    # at a power of two the step above is the new binade's; ulp(x) is the
+    # spacing of the binade that holds x, which is the gap to the next pattern
+    assert np.array_equal(O.bf16_ulp(v), nxt - v)
+
+
 def test_bf16_encode_matches_torch_on_float32_values():
     # For inputs exactly representable in float32 a single RNE step equals
     # torch's float32 -> bfloat16 conversion (an independent library routine).
@@ -323,6 +343,22 @@ def test_gemm_check_has_teeth():
     assert not O.gemm_check(out2, C2, 4096, 1.0, 0.02, mask[:, None].repeat(32, 1))["ok"]
 
 
+def test_gemm_check_is_tight_at_exact_zeros():
+    # where the fp64 result is exactly 0 (a real row whose products cancel)
+    # the allowance is the stated tolerance plus half a subnormal step, so an
+    # error a little above the tolerance fails there as it does elsewhere
+    K = 256
+    tol = O.gemm_tolerance(K, 1.0, 0.02)
+    C = np.zeros((4, 8))
+    C[0, 0] = 1.0
+    ok = O.f64_to_bf16(C)
+    assert O.gemm_check(ok, C, K, 1.0, 0.02)["ok"]
+    bad = C.copy()
+    bad[2, 3] = 1.25 * tol            # the result there is 0
+    r = O.gemm_check(O.f64_to_bf16(bad), C, K, 1.0, 0.02)
+    assert not r["ok"] and r["n_bad"] == 1
+
+
 def test_gemm_tolerance_value():
     # 2 % of the output standard deviation sqrt(K) * 1 * 0.02 at K = 4096
     assert abs(O.gemm_tolerance(4096, 1.0, 0.02) - 0.0256) < 1e-15
@@ -464,6 +500,15 @@ def test_combine_partial_locality_and_tolerance_teeth():
     bad = yb.copy()
     idx = np.unravel_index(np.argmax(np.abs(y)), y.shape)
     bad[idx] += 3 * tol[idx]
+    assert not np.all(np.abs(bad - y) <= tol)
+    # a token with no local pick sums nothing: its row is exactly 0 and the
+    # bound there admits no nonzero bf16 value (the smallest is 2^-133)
+    empty = [(s, t) for s in range(S) for t in range(T) if not any(4 <= e < 8 for e in topk[s, t])]
+    assert empty
+    s0, t0 = empty[0]
+    assert np.all(tol[s0, t0] < 2.0 ** -133)
+    bad = yb.copy()
+    bad[s0, t0, 5] = 2.0 ** -133
     assert not np.all(np.abs(bad - y) <= tol)
 
 
