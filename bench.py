@@ -1,18 +1,23 @@
 """Benchmark of the fused producer/consumer gather-GEMM on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload tp|large|ep|tiny]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large|tp|ep|tiny]
 
 A step is one pass of the hot path over one batch: layout (route) step, one
 persistent kernel that moves the rows, counts arrivals, elects publishers,
 publishes slots, gates and runs the bf16 contraction. Inputs are resident in
 HBM before timing starts. Prints ONE JSON line.
 
-Beside the fused throughput it reports the three timings of the measurement
-method ("Know your platform" §5: T_comp alone with the same workgroups, T_comm
-alone, T_total), overlap efficiency and compute interference, the gather's
-HBM rate, slot-signal latency (ping-pong round trip, slot barrier), the
-protocol-stress signal rate, the roofline of the fused kernel and the CPU
-oracle timed on a bounded sample on the host cores.
+The headline workload is the largest single-GPU configuration: 8 shards x
+4096 rows scattered by a seeded permutation (M = 32768), K = N = 8192, bf16.
+Beside its fused throughput the line reports the three timings of the
+measurement method ("Know your platform" §5: T_comp alone with the same
+workgroups, T_comm alone, T_total), overlap efficiency and compute
+interference, the gather's HBM rate, a sweep of the copy-workgroup count
+("Know your platform" §4), the publish-to-gate-observe latency from a traced
+call, the same fields for the TP share and the EP dispatch workloads,
+slot-signal latency (ping-pong round trip, slot barrier), the protocol-stress
+signal rate, the two-stage, ring and combine entry points, the roofline of the
+fused kernel and the CPU oracle timed on a bounded sample on the host cores.
 """
 from __future__ import annotations
 
@@ -375,19 +380,175 @@ def combine_bench(args, wl, ctx, gathered, out, torch, fg, W):
                          "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def observe_latency(ctx, step, fg, torch):
+    """Publish -> gate-observe latency from one traced call: for every whole
+    tile whose row blocks completed after its workgroup took it (so that the
+    workgroup was waiting), the time from the last of its blocks' counters
+    reaching 128 (stamped by the copy wave whose add completed it) to the gate
+    opening in the compute workgroup. Both stamps are on the device wall clock."""
+    import numpy as np
+    step(fg.CALL_TRACE)
+    torch.cuda.synchronize()
+    st = ctx.stats()
+    tl = ctx.read_timeline()
+    v = ctx.views()
+    desc = ctx.read_i32(v.desc, 3).numpy()
+    n_slabs = int(desc[1])
+    slab = ctx.read_i32(v.slab, max(1, n_slabs)).numpy()[:n_slabs]
+    tile_n = 256 if ctx.cfg.tile_n in (0, 256) and ctx.cfg.N % 256 == 0 else 128
+    n_tn = ctx.cfg.N // tile_n
+    tr, rbt, us = tl["trace"], tl["rb_time"], tl["us_per_tick"]
+    lat = []
+    for t in range(n_slabs * n_tn):
+        entry = int(slab[t // n_tn])
+        m0, bm = entry & ~1, 128 if entry & 1 else 256
+        rbs = [m0 // 128] + ([m0 // 128 + 1] if bm == 256 else [])
+        ready = max(int(rbt[r]) for r in rbs)
+        if ready > int(tr[t, 1]) and int(tr[t, 2]) >= ready:
+            lat.append((int(tr[t, 2]) - ready) * us)
+    out = {"tiles": n_slabs * n_tn, "tiles_that_waited": len(lat),
+           "max_wait_us": round(st.max_wait_ns / 1000.0, 2)}
+    if lat:
+        a = np.array(lat)
+        out.update(p50_us=round(float(np.percentile(a, 50)), 3), p99_us=round(float(np.percentile(a, 99)), 3),
+                   max_us=round(float(a.max()), 3))
+    return out
+
+
+def back_to_back_us(step, flags, n, torch):
+    """Mean device time (us) of n back-to-back calls between one event pair on
+    the current stream, after one untimed call."""
+    step(flags)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        step(flags)
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / n
+
+
+def overlap_fields(ctx, step, n_rep, flop, gather_bytes, fg, torch):
+    """The three timings of "Know your platform" §5, each the median of
+    separately synchronized calls with the same grid: T_comp alone (GEMM_ONLY,
+    gates pre-opened), T_comm alone (COMM_ONLY), T_total (fused); overlap
+    efficiency = (T_comp + T_comm - T_total) / min(T_comp, T_comm); compute
+    interference = per-tile busy time fused / GEMM only."""
+    t_total = _events_time(lambda: step(), n_rep, torch)
+    st_f = ctx.stats()
+    busy_fused = st_f.t_gemm_busy_us
+    t_comp = _events_time(lambda: step(fg.CALL_GEMM_ONLY), n_rep, torch)
+    busy_alone = ctx.stats().t_gemm_busy_us
+    t_comm = _events_time(lambda: step(fg.CALL_COMM_ONLY), n_rep, torch)
+    step()  # leave the buffers in the fused state
+    torch.cuda.synchronize()
+    med = lambda xs: statistics.median(xs) * 1000.0  # noqa: E731  (us)
+    Tt, Tc, Tm = med(t_total), med(t_comp), med(t_comm)
+    return {
+        "T_comp_alone_us": round(Tc, 2), "T_comm_alone_us": round(Tm, 2), "T_total_us": round(Tt, 2),
+        "T_total_p10_p90_us": [round(_pct(t_total, 10) * 1000, 2), round(_pct(t_total, 90) * 1000, 2)],
+        "overlap_efficiency": round((Tc + Tm - Tt) / min(Tc, Tm), 4),
+        "compute_interference": round(busy_fused / busy_alone, 4) if busy_alone else None,
+        "wall_interference": round(Tt / Tc, 4),
+        "gather_GBps": round(gather_bytes / (Tm * 1e-6) / 1e9, 1),
+        "gather_frac_hbm": round(gather_bytes / (Tm * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "gemm_alone_TFLOPs": round(flop / (Tc * 1e-6) / 1e12, 2),
+        "gemm_alone_frac": round(flop / (Tc * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "gate_wait_us_mean": round(st_f.t_gate_wait_us, 2),
+        "clock_mhz_fused": round(st_f.clock_mhz, 0),
+    }
+
+
+class Bench:
+    """One workload on one context: inputs resident on the device, the step."""
+
+    def __init__(self, name, fg, W, torch, n_comm=0, tile_n=0):
+        self.name = name
+        self.fg, self.torch = fg, torch
+        self.wl = setup_workload(name, torch, fg, W)
+        wl = self.wl
+        self.cfg = fg.make_config(wl["S"], wl["max_rows"], wl["K"], wl["N"], n_groups=wl["n_groups"],
+                                  n_comm_wg=n_comm, tile_n=tile_n)
+        self.ctx = fg.Context(self.cfg)
+        cap = fg.capacity(self.cfg)
+        self.gathered = torch.zeros(cap, wl["K"], dtype=torch.bfloat16, device="cuda:0")
+        self.out = torch.zeros(cap, wl["N"], dtype=torch.bfloat16, device="cuda:0")
+        self.flop = 2.0 * wl["m_real"] * wl["K"] * wl["N"]
+        self.gather_bytes = 2.0 * wl["m_real"] * wl["K"] * 2
+
+    def step(self, flags=0, ctx=None):
+        c = ctx or self.ctx
+        rc = c.gather_gemm(self.wl["shards"], self.wl["w"], self.gathered, self.out, route=self.wl["route"],
+                           flags=flags)
+        if rc != self.fg.OK:
+            raise RuntimeError(f"fg_gather_gemm: {self.fg.strerror(rc)}")
+
+    def check(self, ctx=None):
+        st = (ctx or self.ctx).stats()
+        if st.error_code:
+            raise RuntimeError(f"device error {st.error_code} id {st.error_id}")
+        return st
+
+    def close(self):
+        self.ctx.close()
+
+
+def n_comm_sweep(b, t_comp_us, counts, torch, fg):
+    """Sweep of the copy-workgroup count ("Know your platform" §4: the share of
+    compute units given to communication must be swept): per count a context
+    of its own on the same buffers, T_total as the mean of back-to-back fused
+    steps and T_comm alone as the mean of back-to-back copy-only steps, overlap
+    efficiency against the same T_comp alone (its grid does not change)."""
+    out = []
+    for n in counts:
+        cfg = fg.make_config(b.wl["S"], b.wl["max_rows"], b.wl["K"], b.wl["N"], n_groups=b.wl["n_groups"],
+                             n_comm_wg=n)
+        ctx = fg.Context(cfg)
+        step = lambda flags=0: b.step(flags, ctx)  # noqa: E731
+        for _ in range(3):
+            step()
+        tt = back_to_back_us(step, 0, 10, torch)
+        tm = back_to_back_us(step, fg.CALL_COMM_ONLY, 5, torch)
+        b.check(ctx)
+        ctx.close()
+        out.append({"n_comm_wg": n, "T_total_us": round(tt, 1), "T_comm_alone_us": round(tm, 1),
+                    "TFLOPs": round(b.flop / (tt * 1e-6) / 1e12, 1),
+                    "overlap_efficiency": round((t_comp_us + tm - tt) / min(t_comp_us, tm), 3)})
+    b.step()
+    torch.cuda.synchronize()
+    return out
+
+
+def secondary(name, steps, fg, W, torch):
+    """Fused throughput (back-to-back steps after a warm-up), the three timings
+    and overlap, and the publish-to-observe latency of another workload."""
+    b = Bench(name, fg, W, torch)
+    for _ in range(20):
+        b.step()
+    t = back_to_back_us(b.step, 0, steps, torch)
+    res = {"config": dict(workload=name, **b.wl["info"]), "T_step_us": round(t, 2),
+           "TFLOPs": round(b.flop / (t * 1e-6) / 1e12, 2),
+           "frac_bf16_peak": round(b.flop / (t * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    res["overlap"] = overlap_fields(b.ctx, b.step, 10, b.flop, b.gather_bytes, fg, torch)
+    res["publish_observe"] = observe_latency(b.ctx, b.step, fg, torch)
+    b.check()
+    return b, res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The first 75-100 back-to-back steps after an idle GPU run 5-30 % slower
-    # while the clock settles under the load; 150 warm-up steps (about 40 ms on
-    # TP) put the timed region in the steady state that continuous use sees.
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=150)
-    ap.add_argument("--workload", default="tp", choices=["tp", "large", "ep", "tiny"])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="large", choices=["large", "tp", "ep", "tiny"])
     ap.add_argument("--n-comm", type=int, default=0)
     ap.add_argument("--tile-n", type=int, default=0)
     ap.add_argument("--no-extras", action="store_true", help="fused timing only (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--mode", default="fused", choices=["fused", "gemm_only", "comm_only"],
+                    help="timed steps in this mode (profiling runs of the compute or copy role alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of a known size (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -402,24 +563,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
-    wl = setup_workload(args.workload, torch, fg, W)
-    cfg = fg.make_config(wl["S"], wl["max_rows"], wl["K"], wl["N"], n_groups=wl["n_groups"],
-                         n_comm_wg=args.n_comm, tile_n=args.tile_n)
-    log(f"bench: workload {args.workload}, {args.warmup} warmup + {args.steps} timed steps")
-    ctx = fg.Context(cfg)
-    cap = fg.capacity(cfg)
-    gathered = torch.zeros(cap, wl["K"], dtype=torch.bfloat16, device="cuda:0")
-    out = torch.zeros(cap, wl["N"], dtype=torch.bfloat16, device="cuda:0")
-    flop = 2.0 * wl["m_real"] * wl["K"] * wl["N"]
-    gather_bytes = 2.0 * wl["m_real"] * wl["K"] * 2
-
-    def step(flags=0):
-        rc = ctx.gather_gemm(wl["shards"], wl["w"], gathered, out, route=wl["route"], flags=flags)
-        if rc != fg.OK:
-            raise RuntimeError(f"fg_gather_gemm: {fg.strerror(rc)}")
-
+    log(f"bench: workload {args.workload}, {args.warmup} warmup + {args.steps} timed steps ({args.mode})")
+    b = Bench(args.workload, fg, W, torch, n_comm=args.n_comm, tile_n=args.tile_n)
+    wl, ctx = b.wl, b.ctx
+    mode_flags = {"fused": 0, "gemm_only": fg.CALL_GEMM_ONLY, "comm_only": fg.CALL_COMM_ONLY}[args.mode]
+    if mode_flags == fg.CALL_GEMM_ONLY:
+        b.step()   # the gathered rows the compute role reads
     for _ in range(args.warmup):
-        step()
+        b.step(mode_flags)
     torch.cuda.synchronize()
     # ---- timed region: exactly `steps` back-to-back steps between one pair of
     # HIP events on the stream the kernels run on (torch's current stream, which
@@ -431,16 +582,14 @@ def main():
     t0 = time.perf_counter()
     e0.record()
     for i in range(args.steps):
-        step()
+        b.step(mode_flags)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    st = ctx.stats()
-    if st.error_code:
-        raise RuntimeError(f"device error {st.error_code} id {st.error_id}")
+    st = b.check()
     ms_per_step = wall * 1000.0 / args.steps
     avg_launch_ms = e0.elapsed_time(e1) / args.steps
-    value = flop * args.steps / wall / 1e12
+    value = b.flop * args.steps / wall / 1e12
 
     result = {
         "metric": METRIC,
@@ -457,40 +606,37 @@ def main():
                        n_gemm_wg=st.n_gemm_wg, tiles_whole=st.tiles_whole, tiles_split=st.tiles_split,
                        split_parts=st.split_parts),
     }
-    achieved = flop / (avg_launch_ms * 1e-3) / 1e12
+    if args.mode != "fused":
+        result["mode"] = args.mode
+    achieved = b.flop / (avg_launch_ms * 1e-3) / 1e12
     traffic = recorded_traffic(args.workload)
     result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                           "traffic": None if traffic is None else int(traffic),
                           "kernel": "fused_kernel", "avg_launch_us": round(avg_launch_ms * 1000, 2),
-                          "algorithmic_flop_per_launch": flop,
-                          "algorithmic_gather_bytes_per_launch": gather_bytes}
+                          "algorithmic_flop_per_launch": b.flop,
+                          "algorithmic_gather_bytes_per_launch": b.gather_bytes,
+                          "clock_mhz": round(st.clock_mhz, 0)}
 
-    if not args.no_extras:
+    if not args.no_extras and args.mode == "fused":
         n_rep = max(10, args.steps)
-        t_total = _events_time(lambda: step(), n_rep, torch)
-        st_f = ctx.stats()
-        busy_fused = st_f.t_gemm_busy_us
-        t_comp = _events_time(lambda: step(fg.CALL_GEMM_ONLY), n_rep, torch)
-        st_c = ctx.stats()
-        busy_alone = st_c.t_gemm_busy_us
-        t_comm = _events_time(lambda: step(fg.CALL_COMM_ONLY), n_rep, torch)
-        step()  # leave the buffers in the fused state
-        torch.cuda.synchronize()
-        med = lambda xs: statistics.median(xs) * 1000.0  # noqa: E731  (us)
-        Tt, Tc, Tm = med(t_total), med(t_comp), med(t_comm)
-        ov = (Tc + Tm - Tt) / min(Tc, Tm)
-        result["overlap"] = {
-            "T_comp_alone_us": round(Tc, 2), "T_comm_alone_us": round(Tm, 2), "T_total_us": round(Tt, 2),
-            "T_total_p10_p90_us": [round(_pct(t_total, 10) * 1000, 2), round(_pct(t_total, 90) * 1000, 2)],
-            "overlap_efficiency": round(ov, 4),
-            "compute_interference": round(busy_fused / busy_alone, 4) if busy_alone else None,
-            "wall_interference": round(Tt / Tc, 4),
-            "gather_GBps": round(gather_bytes / (Tm * 1e-6) / 1e9, 1),
-            "gather_frac_hbm": round(gather_bytes / (Tm * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-            "gemm_alone_TFLOPs": round(flop / (Tc * 1e-6) / 1e12, 2),
-            "gate_wait_us_mean": round(st_f.t_gate_wait_us, 2),
-        }
+        ov = overlap_fields(ctx, b.step, n_rep, b.flop, b.gather_bytes, fg, torch)
+        result["overlap"] = ov
+        result["publish_observe"] = observe_latency(ctx, b.step, fg, torch)
+        log("bench: copy-workgroup sweep")
+        result["n_comm_sweep"] = n_comm_sweep(b, ov["T_comp_alone_us"], [16, 32, 64, 128, 192, 224], torch, fg)
+        others = {}
+        tp_b = ep_b = None
+        for name in ("tp", "ep"):
+            if name == args.workload:
+                continue
+            log(f"bench: secondary workload {name}")
+            sb, others[name] = secondary(name, 50, fg, W, torch)
+            if name == "tp":
+                tp_b = sb
+            else:
+                ep_b = sb
+        result["workloads"] = others
         # slot-signal latency
         lat = fg.Context(fg.make_config(8, 256, 256, 256))
         assert lat.pingpong(10000, False) == 0
@@ -526,13 +672,17 @@ def main():
         sctx.close()
         signals = int((s_in.chunk_rows > 0).sum())
         result["stress"] = {"signals_per_iter": signals, "iters": sc["iters"] + 11, "stale": int(sst.stale),
-                            "errors": int(sst.error_code),
+                            "errors": int(sst.error_code), "timeouts": int(sst.timeouts),
                             "us_per_iter_no_delay": round(statistics.median(t_nodelay) * 1000, 2),
                             "us_per_iter_delays_0_20us": round(statistics.median(t_delay) * 1000, 2),
                             "signals_per_s_no_delay": round(signals / (statistics.median(t_nodelay) * 1e-3), 0)}
-        result["two_stage"] = two_stage_bench(args, wl, ctx, gathered, out, torch, fg)
-        result["ring"] = ring_bench(args, wl, ctx, gathered, out, torch, fg)
-        result["combine"] = combine_bench(args, wl, ctx, gathered, out, torch, fg, W)
+        if tp_b is not None:
+            result["two_stage"] = two_stage_bench(args, tp_b.wl, tp_b.ctx, tp_b.gathered, tp_b.out, torch, fg)
+            result["ring"] = ring_bench(args, tp_b.wl, tp_b.ctx, tp_b.gathered, tp_b.out, torch, fg)
+            tp_b.close()
+        if ep_b is not None:
+            result["combine"] = combine_bench(args, ep_b.wl, ep_b.ctx, ep_b.gathered, ep_b.out, torch, fg, W)
+            ep_b.close()
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0").fill_(1)
         dst = torch.empty_like(src)
@@ -543,7 +693,7 @@ def main():
     if not args.no_cpu:
         log("bench: oracle on the host cores")
         result["cpu_baseline"] = cpu_baseline(wl)
-    ctx.close()
+    b.close()
     print(json.dumps(result), flush=True)
 
 

@@ -139,6 +139,12 @@ typedef struct {
 
 typedef struct fg_ctx fg_ctx;
 
+/* Observation counters of the library ("NVLink atomic publish" §7: a hidden
+ * observation counter beside the protocol, read by the host, and the package
+ * as a small primitive library; "PCIe sync protocols" §7: the host compares
+ * what the device did with a table it recomputes, here expected_publishes
+ * against publishes). Cumulative fields count from fg_init; "last" fields
+ * describe the last fused kernel. */
 typedef struct {
   int32_t seq, bseq, stress_seq;  /* last sequence numbers issued (monotonic, never reset) */
   int32_t m_pad;                  /* gathered rows of the last gather-GEMM (device-computed for TOPK) */
@@ -162,6 +168,15 @@ typedef struct {
   double clock_mhz;               /* last fused kernel: shader-clock cycles / wall time, over all workgroups */
   int64_t litmus_stale;           /* fg_litmus: words read with a value other than the round's, cumulative */
   int64_t litmus_words;           /* fg_litmus: words checked, cumulative */
+  int64_t expected_publishes;     /* VERIFY: publishes the calls should have made, one per active 64-row chunk of
+                                     every stream they publish (device-computed from the route in use), cumulative;
+                                     equal to publishes when every chunk had exactly one publisher */
+  int64_t timeouts;               /* device-side waits that hit their watchdog, cumulative (any entry point) */
+  int64_t max_wait_ns;            /* last fused kernel: longest single wait of a compute workgroup (a gate, or a
+                                     split-K part waiting for its siblings) */
+  int32_t first_timeout_id;       /* id of the first wait that timed out (-1: none); error_id names the first
+                                     error of any kind */
+  int32_t reserved3;
 } fg_stats_t;
 
 /* Read-only device views of the library-owned control plane (for tests that
@@ -362,17 +377,41 @@ fg_status fg_combine(fg_ctx* ctx, const void* out, const float* weights, void* c
  * context's watchdog. */
 fg_status fg_litmus(fg_ctx* ctx, int32_t rounds, int32_t mode, hipStream_t stream);
 
-/* Copy the observation counters to *out. wait != 0 first synchronises the
- * bound stream (needed for device-computed fields and timings). */
+/* Copy the observation counters to *out ("NVLink atomic publish" §7: the
+ * observation counter and the small library around the protocol; fields as
+ * documented in fg_stats_t). wait != 0 first synchronises the bound stream,
+ * which the device-computed fields and timings need; wait == 0 returns only
+ * the host-side sequence numbers and sizes. Callable on a context in the
+ * error state. Errors: FG_EINVAL (NULL), FG_EHIP, FG_ENOMEM. */
 fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait);
 
-/* Device pointers of the control plane (valid until fg_destroy). */
+/* Read-only device pointers of the control plane, valid until fg_destroy
+ * ("PCIe sync protocols" §7: the host recomputes the expected table and
+ * compares it with the device state element by element; "NVLink atomic
+ * publish" §3.1: the control plane lives apart from the data). The caller
+ * must not write through them. Errors: FG_EINVAL (NULL). */
 fg_status fg_views(fg_ctx* ctx, fg_views_t* out);
 
-/* Minimum number of gathered / output rows the caller must allocate. */
+/* Minimum number of gathered / output rows the caller must allocate for a
+ * configuration: the real rows plus the padding of every group to a multiple
+ * of FG_ROW_BLOCK ("PCIe sync protocols" §5: padding rows are pre-counted by
+ * the seed, so the gathered buffer holds whole 128-row blocks). Errors:
+ * FG_EINVAL (invalid configuration or NULL). */
 fg_status fg_capacity(const fg_config* cfg, int32_t* m_pad_cap);
 
+/* Synchronise the bound stream and free the context's control plane, split-K
+ * workspace and status word; the caller's buffers are not touched. The
+ * counterpart of fg_init ("NVLink atomic publish" §7: the protocol packaged
+ * as a small library that owns only its control plane). Errors: FG_EINVAL
+ * (NULL). */
 fg_status fg_destroy(fg_ctx* ctx);
+
+/* Static text of a status code (never NULL; "unknown" for other values).
+ * The codes are the error conventions of every entry point: a device-side
+ * wait that hit its watchdog ("DeepEP FIFO pipeline": every spin bounded by a
+ * timeout), a counter past its target ("PCIe sync protocols" §5: the gate
+ * compares for equality with the row block), or a context left in the error
+ * state. */
 const char* fg_strerror(fg_status s);
 
 #ifdef __cplusplus

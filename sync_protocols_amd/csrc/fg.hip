@@ -108,6 +108,18 @@ struct fg_ctx {
     if (e_ != hipSuccess) return FG_EHIP;           \
   } while (0)
 
+// After a call has advanced a sequence number whose parity arms the control
+// plane, a failed launch leaves that plane one parity behind: the context is
+// then unusable and answers FG_ESTATE from the next call on.
+#define HIPCHK_STICKY(ctx, x)                       \
+  do {                                              \
+    hipError_t e_ = (x);                            \
+    if (e_ != hipSuccess) {                         \
+      (ctx)->sticky = FG_EHIP;                      \
+      return FG_EHIP;                               \
+    }                                               \
+  } while (0)
+
 static int round_up(int x, int b) { return (x + b - 1) / b * b; }
 
 static int m_pad_capacity(const fg_config& c) {
@@ -414,6 +426,10 @@ struct RingCall {
   int n_channels = 0, ring_chunks = 0;
 };
 
+static fg_status gather_gemm_launch(fg_ctx* ctx, const void* const* shards, const fg_route* route, const void* W,
+                                    void* const* staging, int self_shard, void* gathered, void* out, uint32_t flags,
+                                    hipStream_t stream, const RingCall& rc, int mode, int rows, int m_pad);
+
 static fg_status gather_gemm_impl(fg_ctx* ctx, const void* const* shards, const fg_route* route, const void* W,
                                   void* const* staging, int self_shard, void* gathered, void* out, uint32_t flags,
                                   hipStream_t stream, const RingCall& rc = RingCall()) {
@@ -457,7 +473,20 @@ static fg_status gather_gemm_impl(fg_ctx* ctx, const void* const* shards, const 
   }
   if (bind_stream(ctx, stream) != FG_OK) return FG_EINVAL;
   HIPCHK(hipSetDevice(ctx->device));
+  s = gather_gemm_launch(ctx, shards, route, W, staging, self_shard, gathered, out, flags, stream, rc, mode, rows,
+                         m_pad);
+  // once seq has advanced the parity arming assumes this call's kernel ran:
+  // a launch that failed leaves the control plane one parity behind, so the
+  // context is unusable from here on
+  if (s == FG_EHIP) ctx->sticky = FG_EHIP;
+  return s;
+}
 
+static fg_status gather_gemm_launch(fg_ctx* ctx, const void* const* shards, const fg_route* route, const void* W,
+                                    void* const* staging, int self_shard, void* gathered, void* out, uint32_t flags,
+                                    hipStream_t stream, const RingCall& rc, int mode, int rows, int m_pad) {
+  const fg_config& c = ctx->cfg;
+  fg_status s = FG_OK;
   ctx->seq += 1;
   const int cur = ctx->seq & 1, nxt = cur ^ 1;
   const bool same = flags & FG_CALL_SAME_ROUTE;
@@ -626,8 +655,9 @@ fg_status fg_stress(fg_ctx* ctx, const int32_t* chunk_rows, const int32_t* delay
   a.P = ctx->cfg.stress_producers; a.C = ctx->cfg.stress_consumers; a.KC = ctx->cfg.stress_max_chunks;
   a.seq = ctx->sseq; a.flags = flags; a.timeout_ticks = timeout_ticks(ctx);
   a.payload_bytes = (uint32_t)((size_t)ctx->s_slots * FG_CHUNK_ROWS * 4);
+  a.wall_khz = ctx->wall_khz;
   hipLaunchKernelGGL(stress_kernel, dim3(a.P + a.C), dim3(kStressThreads), 0, stream, a);
-  HIPCHK(hipGetLastError());
+  HIPCHK_STICKY(ctx, hipGetLastError());
   return FG_OK;
 }
 
@@ -657,7 +687,7 @@ fg_status fg_combine(fg_ctx* ctx, const void* out, const float* weights, void* c
   a.cpub = ctx->p.cpub;
   a.stats = ctx->p.stats; a.err = sink(ctx); a.seq = ctx->cseq; a.flags = flags; a.timeout_ticks = timeout_ticks(ctx);
   hipLaunchKernelGGL(combine_kernel, dim3(ctx->combine_wg), dim3(kCombThreads), 0, stream, a);
-  HIPCHK(hipGetLastError());
+  HIPCHK_STICKY(ctx, hipGetLastError());
   return FG_OK;
 }
 
@@ -690,14 +720,16 @@ fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait) {
   out->n_comm_wg = ctx->n_comm; out->n_gemm_wg = ctx->n_gemm; out->cu_count = ctx->cu_count;
   out->m_pad_cap = ctx->m_pad_cap;
   if (!wait) { out->m_pad = ctx->last_m_pad; return FG_OK; }
-  int err[2] = {0, 0}, desc = 0;
+  int err[4] = {0, 0, 0, 0}, desc = 0;
   unsigned long long st[ST_COUNT];
   long long td[4];
-  HIPCHK(hipMemcpy(err, ctx->p.err, 8, hipMemcpyDeviceToHost));
+  HIPCHK(hipMemcpy(err, ctx->p.err, sizeof(err), hipMemcpyDeviceToHost));
   HIPCHK(hipMemcpy(&desc, ctx->p.desc, 4, hipMemcpyDeviceToHost));
   HIPCHK(hipMemcpy(st, ctx->p.stats, sizeof(st), hipMemcpyDeviceToHost));
   HIPCHK(hipMemcpy(td, ctx->p.tdev, sizeof(td), hipMemcpyDeviceToHost));
   out->error_code = err[0]; out->error_id = err[1];
+  out->timeouts = err[2];
+  out->first_timeout_id = err[2] ? err[3] : -1;
   {
     unsigned long long ls = 0;
     HIPCHK(hipMemcpy(&ls, ctx->p.litmus + kLitmusBytes / 4 + 128, 8, hipMemcpyDeviceToHost));
@@ -707,6 +739,7 @@ fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait) {
   out->publishes = (int64_t)st[ST_PUBLISHES]; out->gate_polls = (int64_t)st[ST_GATE_POLLS];
   out->slot_polls = (int64_t)st[ST_SLOT_POLLS]; out->gate_passes = (int64_t)st[ST_GATE_PASSES];
   out->stale = (int64_t)st[ST_STALE];
+  out->expected_publishes = (int64_t)st[ST_EXPECTED];
   const double us_per_tick = 1000.0 / (double)ctx->wall_khz;
   if (ctx->host_stats[0]) out->t_barrier_us = td[0] * us_per_tick / (double)ctx->host_stats[0];
   if (ctx->host_stats[1]) out->t_rtt_us = td[1] * us_per_tick / (double)ctx->host_stats[1];
@@ -718,7 +751,7 @@ fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait) {
       delete[] wg;
       return FG_EHIP;
     }
-    long long t0 = wg[WT_START], t1 = wg[WT_END], c1 = 0, g0 = -1, g1 = 0;
+    long long t0 = wg[WT_START], t1 = wg[WT_END], c1 = 0, g0 = -1, g1 = 0, wmax = 0;
     double busy = 0, waitt = 0;
     long long tiles = 0, parts = 0, peff = 1;
     int nw = 0;
@@ -729,6 +762,7 @@ fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait) {
       t1 = std::max(t1, t[WT_END]);
       if (i < ctx->n_comm) c1 = std::max(c1, t[WT_COMM_END]);
       cyc += (double)(t[WT_CLK1] - t[WT_CLK0]);
+      wmax = std::max(wmax, t[WT_MAXWAIT]);
       wall += (double)(t[WT_END] - t[WT_START]);
       if (t[WT_TILES] + t[WT_PARTS] > 0) {
         g0 = g0 < 0 ? t[WT_GEMM_START] : std::min(g0, t[WT_GEMM_START]);
@@ -742,6 +776,7 @@ fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait) {
       }
     }
     out->t_kernel_us = (t1 - t0) * us_per_tick;
+    out->max_wait_ns = (int64_t)(wmax * us_per_tick * 1000.0);
     out->t_comm_span_us = c1 > t0 ? (c1 - t0) * us_per_tick : 0.0;
     out->t_gemm_span_us = g0 >= 0 ? (g1 - g0) * us_per_tick : 0.0;
     const long long P = std::max(1LL, peff);

@@ -243,11 +243,15 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(CombineArgs a) {
   }
   if (threadIdx.x == 0) {
     int n = 0;
+    unsigned long long want = 0;
     for (int s = 0; s < a.n_shards; ++s) {
       sh_base[s] = n;
       n += (a.stream_len[s] + kPushPerWave - 1) / kPushPerWave;
+      want += (a.stream_len[s] + kChunk - 1) / kChunk;
     }
     sh_base[a.n_shards] = n;
+    // VERIFY: one publish per active 64-entry chunk of every stream
+    if (blockIdx.x == 0 && (a.flags & kVerify) && !(a.flags & kGemmOnly)) atomicAdd(a.stats + ST_EXPECTED, want);
   }
   __syncthreads();
   if (error_raised(a.err)) return;

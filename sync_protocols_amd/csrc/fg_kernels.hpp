@@ -27,7 +27,10 @@ constexpr uint32_t kTrace = FG_CALL_TRACE;
 constexpr uint32_t kGateWatermark = FG_CALL_GATE_WATERMARK;
 
 // Device statistics block (int64 counters, cumulative).
-enum { ST_PUBLISHES = 0, ST_GATE_POLLS, ST_SLOT_POLLS, ST_GATE_PASSES, ST_STALE, ST_COUNT };
+// ST_EXPECTED: the publishes a VERIFY call should make (one per active chunk of
+// the streams it copies), added by the call itself so that the host can
+// compare it with ST_PUBLISHES whatever route the device computed.
+enum { ST_PUBLISHES = 0, ST_GATE_POLLS, ST_SLOT_POLLS, ST_GATE_PASSES, ST_STALE, ST_EXPECTED, ST_COUNT };
 
 // Versioned inverse map: entry = (route version << 32) | (shard << 24 | stream index).
 __device__ __forceinline__ unsigned long long inv_pack(uint32_t ver, int v) {
@@ -106,8 +109,10 @@ constexpr unsigned long long kRingFinish = 1ull << 32;
 // Per-workgroup timing record (device clock ticks).
 // WT_CLK0 / WT_CLK1: shader-clock counter (s_memtime) at start and end, for the
 // effective clock = cycles / wall time.
+// WT_MAXWAIT: the longest single wait of the compute role (a gate, or the wait
+// of a split-K part for its siblings).
 enum { WT_START = 0, WT_END, WT_GATE, WT_TILES, WT_COMM_END, WT_PARTS, WT_GEMM_START, WT_P, WT_CLK0, WT_CLK1,
-       kWgTimeFields = 12 };
+       WT_MAXWAIT, kWgTimeFields = 12 };
 
 // ---------------------------------------------------------------------------
 // Communication role ("PCIe sync protocols" §3 election + publish, §4 chunk
@@ -782,7 +787,7 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
   const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(a.skws, a.skws_bytes);
   int* const my_tick = a.tick_cur + (L.nx == 1 ? 64 : 64 * (1 + x));
   int* const part_tick = a.tick_cur;
-  long long gate = 0;
+  long long gate = 0, max_wait = 0;
   int tiles = 0, parts = 0;
   bool own_done = false;                                 // thread 0 only
   // thread 0: the ticket of the next whole tile, taken when the current tile's
@@ -857,6 +862,7 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
         }
         const long long t_open = (long long)now_ticks();
         gate += t_open - t0;
+        max_wait = max(max_wait, t_open - t0);
         if (verify) {
           atomicAdd(a.stats + ST_GATE_POLLS, (unsigned long long)polls);
           if (ok) atomicAdd(a.stats + ST_GATE_PASSES, 1ull);
@@ -887,17 +893,20 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
     long long* tr = ((a.flags & kTrace) && q >= 0 && tr_id < a.trace_cap) ? a.trace + (size_t)tr_id * kTraceFields
                                                                             : nullptr;
     int* const pf_tick = (threadIdx.x == 0 && q < 0 && !own_done) ? my_tick : nullptr;
+    const long long gate_before = gate;
     const bool ok = (entry & 1) ? run_item<128, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr,
                                                     pf_tick, pf_j)
                                 : run_item<256, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr,
                                                     pf_tick, pf_j);
     if (pf_tick) pf_valid = true;
+    max_wait = max(max_wait, gate - gate_before);   // a split-K part's wait for its siblings
     if (!ok) break;
     if (q < 0) ++tiles; else ++parts;
     if ((a.flags & kTrace) && threadIdx.x == 0 && tr_id < a.trace_cap) a.trace[(size_t)tr_id * kTraceFields + 3] = now_ticks();
   }
   if (threadIdx.x == 0) {
     wt[WT_GATE] = gate;
+    wt[WT_MAXWAIT] = max_wait;
     wt[WT_TILES] = tiles;
     wt[WT_PARTS] = parts;
     wt[WT_GEMM_START] = t_begin;
@@ -941,6 +950,15 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs) {
     }
     __syncthreads();
     arm_next(a);
+    // VERIFY: the publishes this call should make, one per active 64-row chunk
+    // of every stream whose slots it publishes (all shards in the one-stage
+    // copy, the remote ones in the two-stage push; the ring publishes none)
+    if (blockIdx.x == 0 && threadIdx.x == 0 && (a.flags & kVerify) && !(a.flags & kGemmOnly) && !a.ring_mode) {
+      unsigned long long want = 0;
+      for (int s2 = 0; s2 < a.n_shards; ++s2)
+        if (!(a.two_stage && s2 == a.self_shard)) want += (a.stream_len[s2] + kChunk - 1) / kChunk;
+      atomicAdd(a.stats + ST_EXPECTED, want);
+    }
     const int rings = a.n_shards * a.n_channels;
     if (a.ring_mode) {
       __shared__ int sh_ring[2];
@@ -1429,34 +1447,46 @@ __global__ __launch_bounds__(64, 1) void barrier_kernel(int* bslot, int n, int b
   if (me == 0 && lane == 0) t_out[0] = (long long)now_ticks() - t0;
 }
 
-// Slot ping-pong between workgroup 0 and workgroup 1 (different XCDs).
+// Slot ping-pong between workgroup 0 and workgroup 1 (different XCDs). Every
+// poll is followed by the shortest s_sleep (64 clocks): the wait backs off
+// like every other wait, but does not double, since the round trip it
+// measures is a few hundred nanoseconds and a longer sleep would be measured
+// with it.
+template <int SYS>
+__device__ __forceinline__ int pp_load(const int* p) {
+  return SYS ? __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : poll_relaxed(p);
+}
+template <int SYS>
+__device__ __forceinline__ void pp_store(int* p, int v) {
+  if (SYS) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  else __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// one lane: wait until *p >= seq; false on timeout
+template <int SYS>
+__device__ __forceinline__ bool pp_wait(const int* p, int seq, uint64_t timeout, const ErrorSink& e, int id) {
+  const uint64_t dl = now_ticks() + timeout;
+  while (pp_load<SYS>(p) < seq) {
+    if (now_ticks() > dl) { raise_error(e, kErrTimeout, id); return false; }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
+}
+
 template <int SYS>
 __global__ __launch_bounds__(64, 1) void pingpong_kernel(int* a_slot, int* b_slot, int base, int rounds, ErrorSink e,
                                                          uint64_t timeout, long long* t_out) {
   if (threadIdx.x != 0) return;
   const long long t0 = (long long)now_ticks();
-  uint32_t polls = 0;
   for (int r = 1; r <= rounds; ++r) {
     const int seq = base + r;
     if (blockIdx.x == 0) {
-      if (SYS) __hip_atomic_store(a_slot, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      else __hip_atomic_store(a_slot, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint64_t dl = now_ticks() + timeout;
-      int lvl = 0;
-      while ((SYS ? __hip_atomic_load(b_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : poll_relaxed(b_slot)) < seq) {
-        if (now_ticks() > dl) { raise_error(e, kErrTimeout, 0x70000000); return; }
-        (void)lvl;
-      }
+      pp_store<SYS>(a_slot, seq);
+      if (!pp_wait<SYS>(b_slot, seq, timeout, e, 0x70000000)) return;
     } else {
-      const uint64_t dl = now_ticks() + timeout;
-      while ((SYS ? __hip_atomic_load(a_slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : poll_relaxed(a_slot)) < seq) {
-        if (now_ticks() > dl) { raise_error(e, kErrTimeout, 0x70000001); return; }
-      }
-      if (SYS) __hip_atomic_store(b_slot, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      else __hip_atomic_store(b_slot, seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!pp_wait<SYS>(a_slot, seq, timeout, e, 0x70000001)) return;
+      pp_store<SYS>(b_slot, seq);
     }
   }
-  (void)polls;
   if (blockIdx.x == 0) t_out[0] = (long long)now_ticks() - t0;
 }
 
@@ -1540,6 +1570,7 @@ struct StressArgs {
   uint32_t flags;
   uint64_t timeout_ticks;
   uint32_t payload_bytes;
+  int64_t wall_khz;          // device wall-clock ticks per millisecond
 };
 
 __device__ __forceinline__ int stress_word(int seq, int sid, int r) {
@@ -1560,9 +1591,9 @@ __global__ __launch_bounds__(kStressThreads, 1) void stress_kernel(StressArgs a)
         const int sid = (p * a.C + c) * a.KC + k;
         const int n = a.chunk_rows[sid];
         if (n <= 0) continue;
-        // producer delay (bounded: at most the given nanoseconds, 100 MHz clock)
+        // producer delay, spun on the device wall clock at its queried rate
         const int d_ns = min(max(a.delays_ns[sid], 0), 10000000);   // clamp to [0, 10 ms]
-        const uint64_t until = now_ticks() + (uint64_t)(d_ns / 10);
+        const uint64_t until = now_ticks() + (uint64_t)((long long)d_ns * a.wall_khz / 1000000);
         while (now_ticks() < until) __builtin_amdgcn_s_sleep(1);
         const int r = wave * 16 + lane;
         const int nw = max(0, min(16, n - wave * 16));

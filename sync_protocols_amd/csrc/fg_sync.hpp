@@ -152,12 +152,21 @@ __device__ __forceinline__ void backoff(int& lvl, int max_lvl) {
 
 // Error reporting shared by every kernel: first error wins; the code is also
 // stored (system scope, the only system-scope write) into a host-visible word.
+// Watchdog timeouts are also counted, and the id of the first wait that timed
+// out is kept apart from the first error of any kind ("NVLink atomic publish"
+// §7: observation counters of the library).
 struct ErrorSink {
-  int* dev;          // [0] = code, [1] = id of the wait or slot that failed
+  int* dev;          // [0] = code, [1] = id of the wait or slot that failed,
+                     // [2] = waits that timed out (cumulative), [3] = id of the first of them
   int* host;         // host-visible status word (pinned, coherent)
 };
 
+constexpr int kErrTimeoutCode = -5;   // fg_status FG_ETIMEOUT
+
 __device__ __forceinline__ void raise_error(const ErrorSink& e, int code, int id) {
+  if (code == kErrTimeoutCode) {
+    if (atomicAdd(e.dev + 2, 1) == 0) __hip_atomic_store(e.dev + 3, id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (atomicCAS(e.dev, 0, code) == 0) {
     __hip_atomic_store(e.dev + 1, id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(e.host, code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -167,7 +176,7 @@ __device__ __forceinline__ void raise_error(const ErrorSink& e, int code, int id
 __device__ __forceinline__ bool error_raised(const ErrorSink& e) { return poll_relaxed(e.dev) != 0; }
 
 // Wait outcome codes (match fg_status values in the public header).
-constexpr int kErrTimeout = -5;
+constexpr int kErrTimeout = kErrTimeoutCode;
 constexpr int kErrProtocol = -6;
 
 // Bounded wait, one lane: spin until *p == target (a gate) using relaxed polls

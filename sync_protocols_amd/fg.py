@@ -64,7 +64,9 @@ class FgStats(C.Structure):
                 ("n_comm_wg", C.c_int32), ("n_gemm_wg", C.c_int32), ("cu_count", C.c_int32),
                 ("m_pad_cap", C.c_int32), ("tiles_whole", C.c_int32), ("tiles_split", C.c_int32),
                 ("split_parts", C.c_int32), ("combine_seq", C.c_int32), ("clock_mhz", C.c_double),
-                ("litmus_stale", C.c_int64), ("litmus_words", C.c_int64)]
+                ("litmus_stale", C.c_int64), ("litmus_words", C.c_int64),
+                ("expected_publishes", C.c_int64), ("timeouts", C.c_int64), ("max_wait_ns", C.c_int64),
+                ("first_timeout_id", C.c_int32), ("reserved3", C.c_int32)]
 
 
 class FgViews(C.Structure):

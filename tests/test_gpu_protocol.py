@@ -60,10 +60,21 @@ def test_stress_full_config():
     delays = st_in.delays_ns.to(DEV)
     P, C, KC = st_in.chunk_rows.shape
     payload = torch.zeros(C * P * KC * 64, dtype=torch.int32, device=DEV)
+    active = st_in.chunk_rows.numpy() > 0
     for t in range(c["iters"]):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         assert ctx.stress(cr, delays[t].contiguous(), payload) == 0
+        e1.record()
+        e1.synchronize()
+        # a producer spins its delays one chunk after another, so the call takes
+        # at least the largest per-producer sum of delays (the wall clock's rate
+        # is the device's own)
+        d_ns = st_in.delays_ns[t].numpy().astype(np.int64) * active
+        floor_ms = float(d_ns.reshape(P, -1).sum(axis=1).max()) * 1e-6
+        assert e0.elapsed_time(e1) >= 0.95 * floor_ms, (t, e0.elapsed_time(e1), floor_ms)
     st = ctx.stats()
-    assert st.error_code == 0 and st.stale == 0
+    assert st.error_code == 0 and st.stale == 0 and st.timeouts == 0
     want = O.stress_expected(st_in.chunk_rows.numpy(), c["iters"])
     v = ctx.views()
     slots = ctx.read_i32(v.stress_slot, P * C * KC).numpy().reshape(P, C, KC)
@@ -102,6 +113,8 @@ def test_dropped_publish_times_out_in_stress():
     assert ctx.stress(cr, d, payload, flags=fg.FAULT_DROP_PUBLISH) == 0
     st = ctx.stats()
     assert st.error_code == fg.ETIMEOUT
+    # the consumer waiting on slot 0 (producer 0, consumer 0, chunk 0) times out
+    assert st.timeouts >= 1 and st.first_timeout_id == 0
     assert ctx.stress(cr, d, payload) == fg.ETIMEOUT     # reported by the next call
     assert ctx.stress(cr, d, payload) == fg.ESTATE       # then sticky
     ctx.close()
@@ -115,6 +128,8 @@ def test_seed_low_times_out():
     assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route, flags=fg.FAULT_SEED_LOW) == 0
     st = ctx.stats()
     assert st.error_code == fg.ETIMEOUT and st.error_id == 0
+    # every compute workgroup gating on row block 0 times out; the first is block 0
+    assert st.timeouts >= 1 and st.first_timeout_id == 0
     assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route) == fg.ETIMEOUT
     assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route) == fg.ESTATE
     ctx.close()
@@ -128,6 +143,7 @@ def test_seed_high_overshoots():
     assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route, flags=fg.FAULT_SEED_HIGH) == 0
     st = ctx.stats()
     assert st.error_code == fg.EPROTOCOL
+    assert st.first_timeout_id == -1   # an overshoot is not a timeout
     assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route) == fg.EPROTOCOL
     ctx.close()
 

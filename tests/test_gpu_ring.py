@@ -87,14 +87,12 @@ def test_ring_strict_fences():
     _run(case, 2, n_channels=2, ring_chunks=1, flags=fg.CALL_STRICT)
 
 
-def test_ring_tp_full_size_sampled():
+def test_ring_tp_full_size():
     log("ring at the TP size: 4 x 2048 rows, K=N=4096, 8 rings per shard of 2 slots (1/4 of the streams), "
-        "self shard 0")
+        "self shard 0, 3 calls; every output element")
     c = W.CONFIGS["tp"]
     case = dense_case(c["seed"], c["n_shards"], c["rows"], c["K"], c["N"])
-    rng = np.random.default_rng(8)
-    _run(case, 2, n_channels=8, ring_chunks=2, self_shard=0,
-         sample_rows=np.sort(rng.choice(case.lay.m_pad, 48, replace=False)))
+    _run(case, 3, n_channels=8, ring_chunks=2, self_shard=0)
 
 
 def test_ring_arguments():

@@ -110,12 +110,11 @@ def test_two_stage_comm_only_then_gemm_only():
     ctx.close()
 
 
-def test_two_stage_tp_full_size_sampled():
-    log("two-stage at the TP size: 4 x 2048 rows, K=N=4096, self shard 0; gathered bit-exact, sampled rows")
+def test_two_stage_tp_full_size():
+    log("two-stage at the TP size: 4 x 2048 rows, K=N=4096, self shard 0, 3 calls; every output element")
     c = W.CONFIGS["tp"]
     case = dense_case(c["seed"], c["n_shards"], c["rows"], c["K"], c["N"])
-    rng = np.random.default_rng(7)
-    _run(case, 2, self_shard=0, sample_rows=np.sort(rng.choice(case.lay.m_pad, 48, replace=False)))
+    _run(case, 3, self_shard=0)
 
 
 def test_two_stage_dropped_watermark_times_out():
