@@ -207,7 +207,8 @@ typedef struct {
   const int64_t* trace;       /* FG_CALL_TRACE: [trace_cap][8] per compute item (whole tile t at row t,
                                  split-K part q at row n_tiles + q): workgroup, ticket taken, gate open, item
                                  done; parts also: k loop done, partial stored, all parts counted; 1 unused */
-  const int64_t* rb_time;     /* FG_CALL_TRACE: [rb_cap] time the row block's counter reached 128 */
+  const int64_t* rb_time;     /* FG_CALL_TRACE: [rb_cap] issue time of the add that brought the row block's
+                                 counter to 128 (its publish) */
   int32_t grid, trace_cap;
   int64_t wall_khz;
   const int32_t* desc;        /* [3]: gathered rows m_pad, row slabs n_slabs and groups of the route in use */

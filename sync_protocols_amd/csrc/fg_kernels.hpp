@@ -220,6 +220,9 @@ __device__ __forceinline__ void comm_batches(const FusedArgs& a, const uint16_t*
     // signals of batch b
     const int n_real = __popcll(ballot(lane < RB && info >= 0));
     int old_c, old_e, cnt = 0;
+    // TRACE: the publish time of the block is the issue of the add that
+    // completes it (its result, which says so, is examined a round trip later)
+    const long long t_pub = (fl & kTrace) ? (long long)now_ticks() : 0;
     // (an opaque zero in the address keeps the compiler from rewriting this
     // one-lane add as a wave-wide one whose result it needs at once)
     if (lane == 0 && n_real > 0)
@@ -245,7 +248,7 @@ __device__ __forceinline__ void comm_batches(const FusedArgs& a, const uint16_t*
     if (lane == 0 && n_real > 0) {
       const int blk = g0 / kRB;
       if (old_c + n_real > kRB) raise_error(a.err, kErrProtocol, blk);
-      if ((fl & kTrace) && old_c + n_real == kRB) a.rb_time[blk] = (long long)now_ticks();
+      if ((fl & kTrace) && old_c + n_real == kRB) a.rb_time[blk] = t_pub;
     }
     if (leader) {
       if (old_e + cnt == expect) {
@@ -436,9 +439,10 @@ __device__ __forceinline__ void comm_two_stage(const FusedArgs& a, const uint16_
     const int n_real = __popcll(ballot(lane < RB && info >= 0));
     if (lane == 0 && n_real > 0) {
       const int rb = g0 / kRB;
+      const long long t_pub = (long long)now_ticks();   // issue of the add (publish time under TRACE)
       const int old = fetch_add_relaxed(a.counter_cur + (size_t)rb * kCtr, n_real);
       if (old + n_real > kRB) raise_error(a.err, kErrProtocol, rb);
-      if ((a.flags & kTrace) && old + n_real == kRB) a.rb_time[rb] = (long long)now_ticks();
+      if ((a.flags & kTrace) && old + n_real == kRB) a.rb_time[rb] = t_pub;
     }
   }
 }
@@ -584,9 +588,10 @@ __device__ __forceinline__ void ring_consumer(const FusedArgs& a, const uint16_t
         const uint64_t mask = ballot(rb == blk) & pending;
         if (lane == leader) {
           const int cnt = __popcll(mask);
+          const long long t_pub = (long long)now_ticks();   // issue of the add (publish time under TRACE)
           const int old = fetch_add_relaxed(a.counter_cur + (size_t)blk * kCtr, cnt);
           if (old + cnt > kRB) raise_error(a.err, kErrProtocol, blk);
-          if ((a.flags & kTrace) && old + cnt == kRB) a.rb_time[blk] = (long long)now_ticks();
+          if ((a.flags & kTrace) && old + cnt == kRB) a.rb_time[blk] = t_pub;
         }
         pending &= ~mask;
       }
