@@ -378,6 +378,32 @@ fg_status fg_combine(fg_ctx* ctx, const void* out, const float* weights, void* c
  * context's watchdog. */
 fg_status fg_litmus(fg_ctx* ctx, int32_t rounds, int32_t mode, hipStream_t stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * iteration as fg_gather_gemm with no context: the call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); the control plane
+ * lives in a file-scope device array of the library, 4 MiB per GPU, held until
+ * the process ends (8 shards x 4096 rows at K = N = 8192 fit; a configuration
+ * whose control plane does not fit returns FG_EINVAL). The split-K tail is not
+ * used (leftover tiles run whole) and nothing is traced.
+ *   cfg, hip_device: configuration and device of this call; shapes may change
+ *                    from call to call
+ *   shards, route, W, gathered, out: as fg_gather_gemm (CONTIG, EXPLICIT or
+ *                    TOPK routes)
+ *   status:          device int32, set to 0 at the start of the call; a device-side
+ *                    error (a wait that timed out, a counter that overshot) stores
+ *                    its fg_status code there; read it after the stream's work ends
+ *   flags:           0, FG_CALL_STRICT or FG_CALL_GATE_WATERMARK (others: FG_EINVAL)
+ * Every call on one GPU uses that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (other streams, other host threads)
+ * race and must be serialised by the caller. The slots keep their monotonic
+ * sequence numbers across calls; everything else is cleared by the call.
+ * Errors: FG_EINVAL (shapes, NULLs, flags, control plane too large), FG_EHIP,
+ * FG_ERESIDENCY. */
+fg_status fg_gather_gemm_noalloc(const fg_config* cfg, int hip_device, const void* const* shards,
+                                 const fg_route* route, const void* W, void* gathered, void* out, int32_t* status,
+                                 uint32_t flags, hipStream_t stream);
+
 /* Copy the observation counters to *out ("NVLink atomic publish" §7: the
  * observation counter and the small library around the protocol; fields as
  * documented in fg_stats_t). wait != 0 first synchronises the bound stream,

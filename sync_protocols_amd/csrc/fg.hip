@@ -92,6 +92,7 @@ struct fg_ctx {
   uint32_t route_ver = 0;
   int route_wg_cap = 0;
   fg_status sticky = FG_OK;
+  bool no_alloc = false;       // state of fg_gather_gemm_noalloc: the status word is the caller's device word
   bool stream_bound = false;
   hipStream_t stream = nullptr;
   // cached CONTIG route (so that repeated all-gathers skip the layout step)
@@ -167,6 +168,7 @@ static fg_status map_device_error(int code) {
 // A device-side error recorded by an earlier launch becomes sticky here.
 static fg_status check_sticky(fg_ctx* ctx) {
   if (ctx->sticky != FG_OK) return FG_ESTATE;
+  if (ctx->no_alloc) return FG_OK;   // device-side errors go to the caller's status word
   const int code = __atomic_load_n(ctx->host_status, __ATOMIC_ACQUIRE);
   if (code != 0) {
     ctx->sticky = map_device_error(code);
@@ -257,6 +259,144 @@ static fg_status launch_fused(const FusedArgs& a, hipStream_t st) {
   return FG_OK;
 }
 
+// Scratch of fg_gather_gemm_noalloc: the control plane of one call (slots,
+// arrival counters and election counts of both parities, route tables,
+// tickets, statistics); 4 MiB covers 8 shards x 4096 rows at K = N = 8192.
+constexpr size_t kScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kNoAllocMaxDevices = 64;
+struct NoAllocDevice {
+  bool ready = false;
+  char* ptr = nullptr;   // device address of this GPU's copy of `scratch`
+  fg_ctx ctx;            // sequence numbers, route version and the per-call sizes
+};
+NoAllocDevice g_noalloc[kNoAllocMaxDevices];
+}  // namespace
+
+// Context set-up shared by fg_init and the no-allocation entry point:
+// device attributes, the grid split, the residency audit ("PCIe sync
+// protocols" §6 items 1 and 2) and the derived capacities. no_alloc: no
+// split-K workspace (split_parts 1) and no trace.
+static fg_status ctx_setup(fg_ctx* ctx, const fg_config* cfg, int hip_device, bool no_alloc) {
+  ctx->cfg = *cfg;
+  ctx->device = hip_device;
+  int wall = 0;
+  if (hipDeviceGetAttribute(&ctx->cu_count, hipDeviceAttributeMultiprocessorCount, hip_device) != hipSuccess ||
+      hipDeviceGetAttribute(&wall, hipDeviceAttributeWallClockRate, hip_device) != hipSuccess) {
+    return FG_EHIP;
+  }
+  if (wall > 0) ctx->wall_khz = wall;
+  // default: three quarters of the compute units copy first (192 of 256): the
+  // copy is bandwidth-bound, and more copy workgroups bring the first row
+  // blocks in sooner and join the compute role earlier (measured fused time on
+  // TP / EP / Large: 243 / 311 / 3574 us at 128, 237 / 304 / 3553 us at 192)
+  ctx->n_comm = cfg->n_comm_wg ? cfg->n_comm_wg : std::max(1, ctx->cu_count * 3 / 4);
+  ctx->n_gemm = cfg->n_gemm_wg ? cfg->n_gemm_wg : ctx->cu_count - ctx->n_comm;
+  ctx->tile_n = cfg->tile_n ? cfg->tile_n : (cfg->N % 256 == 0 ? 256 : 128);
+  // "PCIe sync protocols" §6 audit: every spinning workgroup must leave room
+  // for the suppliers, and the whole persistent grid must be resident at once.
+  if (ctx->n_gemm < 1 || ctx->n_gemm >= ctx->cu_count || ctx->n_comm < 1) return FG_ERESIDENCY;
+  {
+    int per_cu = 0, worst = 1 << 30;
+    hipError_t e = hipSuccess;
+    e = ctx->tile_n == 256 ? occupancy<256>(&per_cu) : occupancy<128>(&per_cu);
+    worst = std::min(worst, per_cu);
+    if (e != hipSuccess) return FG_EHIP;
+    if ((long long)worst * ctx->cu_count < ctx->n_comm + ctx->n_gemm) return FG_ERESIDENCY;
+  }
+  // combine kernel: its waves wait on pushes done by other waves, so the whole
+  // grid must be resident (same audit)
+  ctx->combine_wg = cfg->combine_wg ? cfg->combine_wg : 2 * ctx->cu_count;
+  {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, combine_kernel, kCombThreads, 0) != hipSuccess) {
+      return FG_EHIP;
+    }
+    if ((long long)per_cu * ctx->cu_count < ctx->combine_wg) return FG_ERESIDENCY;
+  }
+  {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, route_topk_kernel, kRouteThreads, 0) != hipSuccess) {
+      return FG_EHIP;
+    }
+    ctx->route_resident = per_cu * ctx->cu_count;
+  }
+  if (cfg->stress_producers + cfg->stress_consumers > ctx->cu_count ||
+      cfg->stress_consumers >= ctx->cu_count) return FG_ERESIDENCY;
+  if (cfg->n_shards > ctx->cu_count) return FG_ERESIDENCY;
+
+  const int S = cfg->n_shards;
+  ctx->chunk_cap = (cfg->max_rows_per_shard + FG_CHUNK_ROWS - 1) / FG_CHUNK_ROWS;
+  ctx->m_pad_cap = m_pad_capacity(*cfg);
+  ctx->rb_cap = ctx->m_pad_cap / FG_ROW_BLOCK;
+  ctx->s_slots = cfg->stress_producers * cfg->stress_consumers * cfg->stress_max_chunks;
+  const int grid_max = ctx->n_comm + ctx->n_gemm;
+  // split-K tail capacity: by default at most grid/2 split tiles and grid
+  // partial blocks (P <= grid / split tiles); a given split_tiles adds
+  // split_tiles tiles of split_parts blocks each
+  ctx->split_parts = no_alloc ? 1 : cfg->split_parts ? cfg->split_parts : kDefaultSplitParts;
+  ctx->split_tiles = ctx->split_parts > 1 ? cfg->split_tiles : 0;
+  ctx->split_slots = std::max({1, grid_max / 2, ctx->split_tiles});
+  ctx->split_blocks = ctx->split_parts > 1 ? std::max(grid_max, ctx->split_tiles * ctx->split_parts) : 0;
+  ctx->skws_bytes = (size_t)ctx->split_blocks * 256 * ctx->tile_n * 4;
+  // 32-bit buffer offsets; offsets from 0xFFFFFFF0 up read as zeros in the partial sums
+  if (ctx->skws_bytes >= 0xFFFFFFF0ull) return FG_EINVAL;
+  ctx->trace_cap = no_alloc ? 0 : (ctx->m_pad_cap / 128) * (cfg->N / 128) + ctx->split_blocks;
+  return FG_OK;
+}
+
+// Offsets of the control-plane arrays, each on a 256-byte boundary ("NVLink
+// atomic publish" §3.1); with a base address the context's pointers are set.
+// Returns the plane's size in bytes.
+static size_t plane_layout(fg_ctx* ctx, char* base) {
+  const fg_config* cfg = &ctx->cfg;
+  const int S = cfg->n_shards;
+  const int grid_max = ctx->n_comm + ctx->n_gemm;
+  const size_t nch = (size_t)S * ctx->chunk_cap;
+  const size_t nrs = (size_t)S * cfg->max_rows_per_shard;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+  ctx->route_wg_cap = S * ((cfg->max_rows_per_shard + kRouteThreads - 1) / kRouteThreads);
+  const size_t wgc = (size_t)ctx->route_wg_cap * (FG_MAX_GROUPS + 1) * 4;
+  const size_t o_slot = take(nch * 4), o_counter = take(2 * (size_t)ctx->rb_cap * kCtr * 4),
+               o_elect = take(2 * nch * 4), o_pub = take(nch * 4), o_seed = take((size_t)ctx->rb_cap * 4),
+               o_inv = take((size_t)ctx->m_pad_cap * 8), o_grp = take((size_t)ctx->rb_cap * 4),
+               o_src = take(nrs * 4), o_dst = take(nrs * 4), o_slen = take((size_t)S * 4),
+               o_goff = take((FG_MAX_GROUPS + 1) * 4), o_rbc = take((size_t)ctx->rb_cap * 4), o_desc = take(64), o_slab = take((size_t)ctx->rb_cap * 4), o_gslab = take((FG_MAX_GROUPS + 1) * 4),
+               o_wgc = take(wgc), o_wgb = take(wgc), o_tick = take(64), o_gtick = take(2 * kTickInts * 4),
+               o_skc = take(2 * (size_t)ctx->split_slots * 4),
+               o_trace = take((size_t)ctx->trace_cap * kTraceFields * 8), o_rbt = take((size_t)ctx->rb_cap * 8),
+               o_err = take(64), o_stats = take(ST_COUNT * 8), o_bslot = take((size_t)S * S * 4),
+               o_pp = take(512), o_tdev = take(64), o_wg = take((size_t)grid_max * kWgTimeFields * 8),
+               o_sslot = take((size_t)ctx->s_slots * 4), o_select = take(2 * (size_t)ctx->s_slots * 4),
+               o_spub = take((size_t)ctx->s_slots * 4), o_srck = take(nrs * 4),
+               o_tokf = take((size_t)S * (cfg->max_rows_per_shard + 1) * 4), o_cslot = take(nch * kCombStride * 4),
+               o_celect = take(2 * nch * kCombStride * 4), o_cpub = take(nch * 4), o_lit = take(kLitmusBytes + 768);
+  ctx->ring_cap = std::max(1, ctx->n_comm / 2);
+  const size_t o_rtail = take(2 * (size_t)ctx->ring_cap * kRingTailStride * 8),
+               o_rhead = take(2 * (size_t)ctx->ring_cap * kCtr * 4);
+  if (!base) return off;
+  char* b = base;
+  Plane& p = ctx->p;
+  p.slot = (int*)(b + o_slot); p.counter = (int*)(b + o_counter); p.elect = (int*)(b + o_elect);
+  p.pub_count = (int*)(b + o_pub); p.seed = (int*)(b + o_seed); p.inv = (unsigned long long*)(b + o_inv);
+  p.wgcount = (int*)(b + o_wgc); p.wgbase = (int*)(b + o_wgb); p.ticket = (int*)(b + o_tick);
+  p.gtick = (int*)(b + o_gtick); p.skc = (int*)(b + o_skc);
+  p.trace = (long long*)(b + o_trace); p.rb_time = (long long*)(b + o_rbt);
+  p.group_of_rb = (int*)(b + o_grp); p.src_row = (int*)(b + o_src); p.dst_row = (int*)(b + o_dst);
+  p.stream_len = (int*)(b + o_slen); p.group_off = (int*)(b + o_goff); p.rbcount = (int*)(b + o_rbc);
+  p.desc = (int*)(b + o_desc); p.slab = (int*)(b + o_slab); p.gslab = (int*)(b + o_gslab); p.err = (int*)(b + o_err); p.stats = (unsigned long long*)(b + o_stats);
+  p.bslot = (int*)(b + o_bslot); p.pp = (int*)(b + o_pp); p.tdev = (long long*)(b + o_tdev);
+  p.wgtime = (long long*)(b + o_wg); p.s_slot = (int*)(b + o_sslot); p.s_elect = (int*)(b + o_select);
+  p.s_pub = (int*)(b + o_spub);
+  p.src_k = (int*)(b + o_srck); p.tok_first = (int*)(b + o_tokf); p.cslot = (int*)(b + o_cslot);
+  p.celect = (int*)(b + o_celect); p.cpub = (int*)(b + o_cpub); p.litmus = (int*)(b + o_lit);
+  p.rtail = (unsigned long long*)(b + o_rtail); p.rhead = (int*)(b + o_rhead);
+  return off;
+}
+
 extern "C" {
 
 const char* fg_strerror(fg_status s) {
@@ -288,114 +428,12 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out) {
   HIPCHK(hipSetDevice(hip_device));
   fg_ctx* ctx = new (std::nothrow) fg_ctx();
   if (!ctx) return FG_ENOMEM;
-  ctx->cfg = *cfg;
-  ctx->device = hip_device;
-  int wall = 0;
-  if (hipDeviceGetAttribute(&ctx->cu_count, hipDeviceAttributeMultiprocessorCount, hip_device) != hipSuccess ||
-      hipDeviceGetAttribute(&wall, hipDeviceAttributeWallClockRate, hip_device) != hipSuccess) {
-    delete ctx;
-    return FG_EHIP;
-  }
-  if (wall > 0) ctx->wall_khz = wall;
-  // default: three quarters of the compute units copy first (192 of 256): the
-  // copy is bandwidth-bound, and more copy workgroups bring the first row
-  // blocks in sooner and join the compute role earlier (measured fused time on
-  // TP / EP / Large: 243 / 311 / 3574 us at 128, 237 / 304 / 3553 us at 192)
-  ctx->n_comm = cfg->n_comm_wg ? cfg->n_comm_wg : std::max(1, ctx->cu_count * 3 / 4);
-  ctx->n_gemm = cfg->n_gemm_wg ? cfg->n_gemm_wg : ctx->cu_count - ctx->n_comm;
-  ctx->tile_n = cfg->tile_n ? cfg->tile_n : (cfg->N % 256 == 0 ? 256 : 128);
-  // "PCIe sync protocols" §6 audit: every spinning workgroup must leave room
-  // for the suppliers, and the whole persistent grid must be resident at once.
-  if (ctx->n_gemm < 1 || ctx->n_gemm >= ctx->cu_count || ctx->n_comm < 1) { delete ctx; return FG_ERESIDENCY; }
-  {
-    int per_cu = 0, worst = 1 << 30;
-    hipError_t e = hipSuccess;
-    e = ctx->tile_n == 256 ? occupancy<256>(&per_cu) : occupancy<128>(&per_cu);
-    worst = std::min(worst, per_cu);
-    if (e != hipSuccess) { delete ctx; return FG_EHIP; }
-    if ((long long)worst * ctx->cu_count < ctx->n_comm + ctx->n_gemm) { delete ctx; return FG_ERESIDENCY; }
-  }
-  // combine kernel: its waves wait on pushes done by other waves, so the whole
-  // grid must be resident (same audit)
-  ctx->combine_wg = cfg->combine_wg ? cfg->combine_wg : 2 * ctx->cu_count;
-  {
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, combine_kernel, kCombThreads, 0) != hipSuccess) {
-      delete ctx;
-      return FG_EHIP;
-    }
-    if ((long long)per_cu * ctx->cu_count < ctx->combine_wg) { delete ctx; return FG_ERESIDENCY; }
-  }
-  {
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, route_topk_kernel, kRouteThreads, 0) != hipSuccess) {
-      delete ctx;
-      return FG_EHIP;
-    }
-    ctx->route_resident = per_cu * ctx->cu_count;
-  }
-  if (cfg->stress_producers + cfg->stress_consumers > ctx->cu_count ||
-      cfg->stress_consumers >= ctx->cu_count) { delete ctx; return FG_ERESIDENCY; }
-  if (cfg->n_shards > ctx->cu_count) { delete ctx; return FG_ERESIDENCY; }
-
-  const int S = cfg->n_shards;
-  ctx->chunk_cap = (cfg->max_rows_per_shard + FG_CHUNK_ROWS - 1) / FG_CHUNK_ROWS;
-  ctx->m_pad_cap = m_pad_capacity(*cfg);
-  ctx->rb_cap = ctx->m_pad_cap / FG_ROW_BLOCK;
-  ctx->s_slots = cfg->stress_producers * cfg->stress_consumers * cfg->stress_max_chunks;
-  const int grid_max = ctx->n_comm + ctx->n_gemm;
-  // split-K tail capacity: by default at most grid/2 split tiles and grid
-  // partial blocks (P <= grid / split tiles); a given split_tiles adds
-  // split_tiles tiles of split_parts blocks each
-  ctx->split_parts = cfg->split_parts ? cfg->split_parts : kDefaultSplitParts;
-  ctx->split_tiles = ctx->split_parts > 1 ? cfg->split_tiles : 0;
-  ctx->split_slots = std::max({1, grid_max / 2, ctx->split_tiles});
-  ctx->split_blocks = ctx->split_parts > 1 ? std::max(grid_max, ctx->split_tiles * ctx->split_parts) : 0;
-  ctx->skws_bytes = (size_t)ctx->split_blocks * 256 * ctx->tile_n * 4;
-  // 32-bit buffer offsets; offsets from 0xFFFFFFF0 up read as zeros in the partial sums
-  if (ctx->skws_bytes >= 0xFFFFFFF0ull) { delete ctx; return FG_EINVAL; }
-  ctx->trace_cap = (ctx->m_pad_cap / 128) * (cfg->N / 128) + ctx->split_blocks;
-  const size_t nch = (size_t)S * ctx->chunk_cap;
-  const size_t nrs = (size_t)S * cfg->max_rows_per_shard;
-  size_t off = 0;
-  auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-  ctx->route_wg_cap = S * ((cfg->max_rows_per_shard + kRouteThreads - 1) / kRouteThreads);
-  const size_t wgc = (size_t)ctx->route_wg_cap * (FG_MAX_GROUPS + 1) * 4;
-  const size_t o_slot = take(nch * 4), o_counter = take(2 * (size_t)ctx->rb_cap * kCtr * 4),
-               o_elect = take(2 * nch * 4), o_pub = take(nch * 4), o_seed = take((size_t)ctx->rb_cap * 4),
-               o_inv = take((size_t)ctx->m_pad_cap * 8), o_grp = take((size_t)ctx->rb_cap * 4),
-               o_src = take(nrs * 4), o_dst = take(nrs * 4), o_slen = take((size_t)S * 4),
-               o_goff = take((FG_MAX_GROUPS + 1) * 4), o_rbc = take((size_t)ctx->rb_cap * 4), o_desc = take(64), o_slab = take((size_t)ctx->rb_cap * 4), o_gslab = take((FG_MAX_GROUPS + 1) * 4),
-               o_wgc = take(wgc), o_wgb = take(wgc), o_tick = take(64), o_gtick = take(2 * kTickInts * 4),
-               o_skc = take(2 * (size_t)ctx->split_slots * 4),
-               o_trace = take((size_t)ctx->trace_cap * kTraceFields * 8), o_rbt = take((size_t)ctx->rb_cap * 8),
-               o_err = take(64), o_stats = take(ST_COUNT * 8), o_bslot = take((size_t)S * S * 4),
-               o_pp = take(512), o_tdev = take(64), o_wg = take((size_t)grid_max * kWgTimeFields * 8),
-               o_sslot = take((size_t)ctx->s_slots * 4), o_select = take(2 * (size_t)ctx->s_slots * 4),
-               o_spub = take((size_t)ctx->s_slots * 4), o_srck = take(nrs * 4),
-               o_tokf = take((size_t)S * (cfg->max_rows_per_shard + 1) * 4), o_cslot = take(nch * kCombStride * 4),
-               o_celect = take(2 * nch * kCombStride * 4), o_cpub = take(nch * 4), o_lit = take(kLitmusBytes + 768);
-  ctx->ring_cap = std::max(1, ctx->n_comm / 2);
-  const size_t o_rtail = take(2 * (size_t)ctx->ring_cap * kRingTailStride * 8),
-               o_rhead = take(2 * (size_t)ctx->ring_cap * kCtr * 4);
-  if (hipMalloc(&ctx->plane_mem, off) != hipSuccess) { delete ctx; return FG_ENOMEM; }
-  if (hipMemset(ctx->plane_mem, 0, off) != hipSuccess) { (void)hipFree(ctx->plane_mem); delete ctx; return FG_EHIP; }
-  char* b = ctx->plane_mem;
-  Plane& p = ctx->p;
-  p.slot = (int*)(b + o_slot); p.counter = (int*)(b + o_counter); p.elect = (int*)(b + o_elect);
-  p.pub_count = (int*)(b + o_pub); p.seed = (int*)(b + o_seed); p.inv = (unsigned long long*)(b + o_inv);
-  p.wgcount = (int*)(b + o_wgc); p.wgbase = (int*)(b + o_wgb); p.ticket = (int*)(b + o_tick);
-  p.gtick = (int*)(b + o_gtick); p.skc = (int*)(b + o_skc);
-  p.trace = (long long*)(b + o_trace); p.rb_time = (long long*)(b + o_rbt);
-  p.group_of_rb = (int*)(b + o_grp); p.src_row = (int*)(b + o_src); p.dst_row = (int*)(b + o_dst);
-  p.stream_len = (int*)(b + o_slen); p.group_off = (int*)(b + o_goff); p.rbcount = (int*)(b + o_rbc);
-  p.desc = (int*)(b + o_desc); p.slab = (int*)(b + o_slab); p.gslab = (int*)(b + o_gslab); p.err = (int*)(b + o_err); p.stats = (unsigned long long*)(b + o_stats);
-  p.bslot = (int*)(b + o_bslot); p.pp = (int*)(b + o_pp); p.tdev = (long long*)(b + o_tdev);
-  p.wgtime = (long long*)(b + o_wg); p.s_slot = (int*)(b + o_sslot); p.s_elect = (int*)(b + o_select);
-  p.s_pub = (int*)(b + o_spub);
-  p.src_k = (int*)(b + o_srck); p.tok_first = (int*)(b + o_tokf); p.cslot = (int*)(b + o_cslot);
-  p.celect = (int*)(b + o_celect); p.cpub = (int*)(b + o_cpub); p.litmus = (int*)(b + o_lit);
-  p.rtail = (unsigned long long*)(b + o_rtail); p.rhead = (int*)(b + o_rhead);
+  const fg_status st = ctx_setup(ctx, cfg, hip_device, false);
+  if (st != FG_OK) { delete ctx; return st; }
+  const size_t bytes = plane_layout(ctx, nullptr);
+  if (hipMalloc(&ctx->plane_mem, bytes) != hipSuccess) { delete ctx; return FG_ENOMEM; }
+  if (hipMemset(ctx->plane_mem, 0, bytes) != hipSuccess) { (void)hipFree(ctx->plane_mem); delete ctx; return FG_EHIP; }
+  plane_layout(ctx, ctx->plane_mem);
   if (hipHostMalloc((void**)&ctx->host_status, 64, hipHostMallocCoherent) != hipSuccess) {
     (void)hipFree(ctx->plane_mem); delete ctx; return FG_ENOMEM;
   }
@@ -809,6 +847,58 @@ fg_status fg_views(fg_ctx* ctx, fg_views_t* v) {
   v->tok_first = p.tok_first;
   v->ring_tail = (const uint64_t*)p.rtail; v->ring_head = p.rhead; v->ring_cap = ctx->ring_cap;
   return FG_OK;
+}
+
+// ---------------------------------------------------------------------------
+// fg_gather_gemm without allocation. The control plane lives in `scratch`, a
+// file-scope device array: every GPU the library runs on holds its own copy
+// until the process ends. Host code never passes the array's name to a kernel
+// (in host code it names a host-side stand-in): the device address of each
+// GPU's copy is looked up once per device with hipGetSymbolAddress and kept in
+// g_noalloc[device].ptr, which is what the kernels and fills receive.
+// ---------------------------------------------------------------------------
+fg_status fg_gather_gemm_noalloc(const fg_config* cfg, int hip_device, const void* const* shards,
+                                 const fg_route* route, const void* W, void* gathered, void* out, int32_t* status,
+                                 uint32_t flags, hipStream_t stream) {
+  if (!config_ok(cfg) || !status) return FG_EINVAL;
+  if (flags & ~(uint32_t)(FG_CALL_STRICT | FG_CALL_GATE_WATERMARK)) return FG_EINVAL;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess) return FG_EHIP;
+  if (hip_device < 0 || hip_device >= ndev || hip_device >= kNoAllocMaxDevices) return FG_EINVAL;
+  HIPCHK(hipSetDevice(hip_device));
+  NoAllocDevice& d = g_noalloc[hip_device];
+  if (!d.ready) {
+    void* ptr = nullptr;
+    HIPCHK(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) return FG_EHIP;
+    d.ptr = (char*)ptr;
+    d.ready = true;
+  }
+  fg_ctx* ctx = &d.ctx;
+  // the sequence number and the route version carry over from the last call
+  // on this device (monotonic, never reset); everything else is per call
+  const fg_status st = ctx_setup(ctx, cfg, hip_device, true);
+  if (st != FG_OK) return st;
+  const size_t bytes = plane_layout(ctx, nullptr);
+  if (bytes > kScratchBytes) return FG_EINVAL;
+  plane_layout(ctx, d.ptr);
+  ctx->no_alloc = true;
+  ctx->sticky = FG_OK;
+  ctx->stream_bound = false;
+  ctx->route_cached_mode = -1;        // the layout step runs on every call
+  ctx->plane_mem = nullptr;
+  ctx->skws = nullptr;
+  ctx->host_status = status;          // device word: the kernels store their first error code here
+  // clear what must start at zero (everything but the slots, whose monotonic
+  // sequence numbers stay) and the caller's status word, with fill kernels
+  const size_t slot_end = align256((size_t)cfg->n_shards * ctx->chunk_cap * 4);
+  const int n_words = (int)((bytes - slot_end) / 4);
+  hipLaunchKernelGGL(fill_kernel, dim3(std::max(1, std::min(1024, n_words / 256 + 1))), dim3(256), 0, stream,
+                     (int*)(d.ptr + slot_end), n_words, 0, 1);
+  HIPCHK(hipGetLastError());
+  hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(64), 0, stream, (int*)status, 1, 0, 1);
+  HIPCHK(hipGetLastError());
+  return gather_gemm_impl(ctx, shards, route, W, nullptr, -1, gathered, out, flags, stream);
 }
 
 }  // extern "C"

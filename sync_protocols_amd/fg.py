@@ -33,8 +33,9 @@ FAULT_DROP_PUBLISH = 1 << 10
 
 ROUTE_CONTIG, ROUTE_EXPLICIT, ROUTE_TOPK = 0, 1, 2
 
-EXPORTS = ("fg_init", "fg_gather_gemm", "fg_gather_gemm_staged", "fg_gather_gemm_ring", "fg_ring_bytes", "fg_barrier", "fg_pingpong", "fg_stress", "fg_combine", "fg_litmus", "fg_stats",
-           "fg_views", "fg_capacity", "fg_destroy", "fg_strerror")
+EXPORTS = ("fg_init", "fg_gather_gemm", "fg_gather_gemm_staged", "fg_gather_gemm_ring", "fg_ring_bytes", "fg_barrier",
+           "fg_pingpong", "fg_stress", "fg_combine", "fg_litmus", "fg_stats", "fg_views", "fg_capacity",
+           "fg_gather_gemm_noalloc", "fg_destroy", "fg_strerror")
 
 
 class FgConfig(C.Structure):
@@ -114,6 +115,8 @@ def load_library() -> C.CDLL:
     lib.fg_stats.argtypes = [vp, C.POINTER(FgStats), C.c_int]
     lib.fg_views.argtypes = [vp, C.POINTER(FgViews)]
     lib.fg_capacity.argtypes = [C.POINTER(FgConfig), C.POINTER(C.c_int32)]
+    lib.fg_gather_gemm_noalloc.argtypes = [C.POINTER(FgConfig), C.c_int, C.POINTER(vp), C.POINTER(FgRoute), vp,
+                                           vp, vp, vp, C.c_uint32, vp]
     lib.fg_destroy.argtypes = [vp]
     lib.fg_strerror.argtypes = [C.c_int]
     lib.fg_strerror.restype = C.c_char_p
@@ -155,6 +158,17 @@ def ring_bytes(cfg: FgConfig, n_channels: int, ring_chunks: int) -> int:
     out = C.c_int64(0)
     _check(load_library().fg_ring_bytes(C.byref(cfg), n_channels, ring_chunks, C.byref(out)), "fg_ring_bytes")
     return out.value
+
+
+def gather_gemm_noalloc(cfg: FgConfig, shards, w, gathered, out, status, *, route: FgRoute | None = None,
+                        flags: int = 0, device: int = 0, stream=None) -> int:
+    """fg_gather_gemm_noalloc: one iteration with no context and no allocation
+    (status: a device int32 tensor the call clears and the kernels set on a
+    device-side error). Returns the fg_status code of the launch."""
+    arr = (C.c_void_p * len(shards))(*[s.data_ptr() for s in shards])
+    return load_library().fg_gather_gemm_noalloc(C.byref(cfg), device, arr,
+                                                 C.byref(route) if route is not None else None, _ptr(w),
+                                                 _ptr(gathered), _ptr(out), _ptr(status), flags, _stream_ptr(stream))
 
 
 def capacity(cfg: FgConfig) -> int:
