@@ -464,13 +464,13 @@ def overlap_fields(ctx, step, n_rep, flop, gather_bytes, fg, torch):
 class Bench:
     """One workload on one context: inputs resident on the device, the step."""
 
-    def __init__(self, name, fg, W, torch, n_comm=0, tile_n=0):
+    def __init__(self, name, fg, W, torch, n_comm=0, tile_n=0, copy_mode=0):
         self.name = name
         self.fg, self.torch = fg, torch
         self.wl = setup_workload(name, torch, fg, W)
         wl = self.wl
         self.cfg = fg.make_config(wl["S"], wl["max_rows"], wl["K"], wl["N"], n_groups=wl["n_groups"],
-                                  n_comm_wg=n_comm, tile_n=tile_n)
+                                  n_comm_wg=n_comm, tile_n=tile_n, copy_mode=copy_mode)
         self.ctx = fg.Context(self.cfg)
         cap = fg.capacity(self.cfg)
         self.gathered = torch.zeros(cap, wl["K"], dtype=torch.bfloat16, device="cuda:0")
@@ -497,14 +497,16 @@ class Bench:
 
 def n_comm_sweep(b, t_comp_us, counts, torch, fg):
     """Sweep of the copy-workgroup count ("Know your platform" §4: the share of
-    compute units given to communication must be swept): per count a context
-    of its own on the same buffers, T_total as the mean of back-to-back fused
-    steps and T_comm alone as the mean of back-to-back copy-only steps, overlap
-    efficiency against the same T_comp alone (its grid does not change)."""
+    compute units given to communication must be swept), in the copy-workgroup
+    mode (copy_mode 0: n_comm_wg workgroups copy every row, then compute): per
+    count a context of its own on the same buffers, T_total as the mean of
+    back-to-back fused steps and T_comm alone as the mean of back-to-back
+    copy-only steps, overlap efficiency against the same T_comp alone (its grid
+    does not change)."""
     out = []
     for n in counts:
         cfg = fg.make_config(b.wl["S"], b.wl["max_rows"], b.wl["K"], b.wl["N"], n_groups=b.wl["n_groups"],
-                             n_comm_wg=n)
+                             n_comm_wg=n, copy_mode=fg.COPY_WORKGROUPS)
         ctx = fg.Context(cfg)
         step = lambda flags=0: b.step(flags, ctx)  # noqa: E731
         for _ in range(3):
@@ -519,6 +521,26 @@ def n_comm_sweep(b, t_comp_us, counts, torch, fg):
     b.step()
     torch.cuda.synchronize()
     return out
+
+
+def other_copy_mode(b, t_comp_us, mode, torch, fg):
+    """The fused step with the other copy mode on the same buffers and grid:
+    T_total (median of separately synchronized calls), TFLOP/s and the ratio
+    to the same T_comp alone."""
+    cfg = fg.make_config(b.wl["S"], b.wl["max_rows"], b.wl["K"], b.wl["N"], n_groups=b.wl["n_groups"],
+                         copy_mode=mode)
+    ctx = fg.Context(cfg)
+    step = lambda flags=0: b.step(flags, ctx)  # noqa: E731
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    ts = _events_time(step, 20, torch)
+    st = b.check(ctx)
+    ctx.close()
+    t = statistics.median(ts) * 1000.0
+    return {"copy": "in tiles" if st.copy_in_tiles else "copy workgroups", "lead_rows": st.lead_rows,
+            "T_total_us": round(t, 2), "TFLOPs": round(b.flop / (t * 1e-6) / 1e12, 1),
+            "T_total_over_T_comp": round(t / t_comp_us, 4)}
 
 
 def secondary(name, steps, fg, W, torch):
@@ -544,9 +566,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large", choices=["large", "tp", "ep", "tiny"])
     ap.add_argument("--n-comm", type=int, default=0)
+    ap.add_argument("--copy-mode", type=int, default=0, choices=[0, 1],
+                    help="0: copy workgroups; 1: rows copied in the compute tiles where the shape allows")
     ap.add_argument("--tile-n", type=int, default=0)
     ap.add_argument("--no-extras", action="store_true", help="fused timing only (for profiling runs)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="headline workload's fields only (no other workloads, latency, stress or other entry points)")
     ap.add_argument("--mode", default="fused", choices=["fused", "gemm_only", "comm_only"],
                     help="timed steps in this mode (profiling runs of the compute or copy role alone)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -564,7 +590,7 @@ def main():
     torch.cuda.set_device(0)
 
     log(f"bench: workload {args.workload}, {args.warmup} warmup + {args.steps} timed steps ({args.mode})")
-    b = Bench(args.workload, fg, W, torch, n_comm=args.n_comm, tile_n=args.tile_n)
+    b = Bench(args.workload, fg, W, torch, n_comm=args.n_comm, tile_n=args.tile_n, copy_mode=args.copy_mode)
     wl, ctx = b.wl, b.ctx
     mode_flags = {"fused": 0, "gemm_only": fg.CALL_GEMM_ONLY, "comm_only": fg.CALL_COMM_ONLY}[args.mode]
     if mode_flags == fg.CALL_GEMM_ONLY:
@@ -602,9 +628,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": dict(workload=f"{args.workload}", **wl["info"], n_comm_wg=st.n_comm_wg,
-                       n_gemm_wg=st.n_gemm_wg, tiles_whole=st.tiles_whole, tiles_split=st.tiles_split,
-                       split_parts=st.split_parts),
+        "config": dict(workload=f"{args.workload}", **wl["info"],
+                       copy="in tiles" if st.copy_in_tiles else "copy workgroups",
+                       lead_rows=st.lead_rows, n_comm_wg=st.n_comm_wg if not st.copy_in_tiles else None,
+                       tiles_whole=st.tiles_whole, tiles_split=st.tiles_split, split_parts=st.split_parts),
     }
     if args.mode != "fused":
         result["mode"] = args.mode
@@ -625,6 +652,8 @@ def main():
         result["publish_observe"] = observe_latency(ctx, b.step, fg, torch)
         log("bench: copy-workgroup sweep")
         result["n_comm_sweep"] = n_comm_sweep(b, ov["T_comp_alone_us"], [16, 32, 64, 128, 192, 224], torch, fg)
+        result["other_copy_mode"] = other_copy_mode(b, ov["T_comp_alone_us"], 1 - args.copy_mode, torch, fg)
+    if not args.no_extras and args.mode == "fused" and not args.no_secondary:
         others = {}
         tp_b = ep_b = None
         for name in ("tp", "ep"):

@@ -113,6 +113,15 @@ typedef struct {
                                   32 16-byte vectors per lane are in flight (0 = the cap) */
   int32_t combine_wg;          /* workgroups of the combine kernel (0 = 2 per compute unit); the grid must
                                   be co-resident (checked by fg_init: FG_ERESIDENCY) */
+  int32_t copy_mode;           /* who moves the rows of fg_gather_gemm ("PCIe sync protocols" §3-§5):
+                                  0 = copy workgroups (default): n_comm_wg workgroups copy every row first
+                                      and then join the compute role;
+                                  1 = in tiles where the shape allows: every workgroup copies the lead rows
+                                      that the first round of tiles reads, then each tile copies rows of a
+                                      later round's slabs inside its K loop, in the shadow of its MFMAs,
+                                      and counts and publishes them (one-group CONTIG or EXPLICIT routes,
+                                      K a multiple of 512 and >= 1536, per-XCD tile lists, no forced split,
+                                      no watermark gating); otherwise as 0 */
 } fg_config;
 
 typedef enum {
@@ -176,7 +185,9 @@ typedef struct {
                                      split-K part waiting for its siblings) */
   int32_t first_timeout_id;       /* id of the first wait that timed out (-1: none); error_id names the first
                                      error of any kind */
-  int32_t reserved3;
+  int32_t copy_in_tiles;          /* last fused kernel: 1 if its rows were copied in tiles (copy_mode 1) */
+  int32_t lead_rows;              /* last fused kernel: rows every workgroup copied first (in-tile copy) */
+  int32_t reserved4;
 } fg_stats_t;
 
 /* Read-only device views of the library-owned control plane (for tests that
@@ -227,6 +238,8 @@ typedef struct {
   const uint64_t* ring_tail;    /* [2][ring_cap][32], value at [..][r][0] = finish << 32 | tail */
   const int32_t* ring_head;     /* [2][ring_cap][FG_COUNTER_STRIDE], value at [..][r][0] */
   int32_t ring_cap, reserved2;  /* ring_cap: rings the copy workgroups can serve (n_comm_wg / 2) */
+  const int32_t* src_of;        /* [m_pad_cap] source row of each gathered row of the route in use (valid where
+                                   the inverse map has a current entry) */
 } fg_views_t;
 
 /* Create a context on `hip_device`: validates the configuration, allocates and

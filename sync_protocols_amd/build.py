@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIB_DIR, "libfg.so")
 SOURCES = [os.path.join(CSRC, "fg.hip")]
-HEADERS = [os.path.join(CSRC, n) for n in ("fg_sync.hpp", "fg_gemm.hpp", "fg_kernels.hpp", "fg_combine.hpp")] + [
+HEADERS = [os.path.join(CSRC, n) for n in ("fg_sync.hpp", "fg_gemm.hpp", "fg_plan.hpp", "fg_kernels.hpp", "fg_combine.hpp")] + [
     os.path.join(ROOT, "include", "fg.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -33,6 +33,7 @@ struct Plane {
   int* pub_count;
   int* seed;
   unsigned long long* inv;   // versioned inverse map
+  int* src_of;     // [m_pad_cap] source row of each gathered row
   int* group_of_rb;
   int* src_row;
   int* dst_row;
@@ -100,6 +101,7 @@ struct fg_ctx {
   int route_cached_rows = -1;
   int last_grid = 0;
   int last_m_pad = 0;
+  int last_tcopy = 0, last_lead_rows = 0;
   unsigned long long host_stats[ST_COUNT] = {};
 };
 
@@ -146,6 +148,7 @@ static bool config_ok(const fg_config* c) {
   if (c->copy_rows != 0 && c->copy_rows != 1 && c->copy_rows != 2 && c->copy_rows != 4 && c->copy_rows != 8 &&
       c->copy_rows != 16) return false;
   if (c->combine_wg < 0 || c->combine_wg > 65536) return false;
+  if (c->copy_mode < 0 || c->copy_mode > 1) return false;
   if (c->stress_producers < 0 || c->stress_consumers < 0 || c->stress_max_chunks < 0) return false;
   const long long m = (long long)c->n_shards * c->max_rows_per_shard + (long long)c->n_groups * FG_ROW_BLOCK;
   if (m * c->K * 2 >= (1ll << 32)) return false;   // 32-bit buffer offsets
@@ -220,7 +223,7 @@ static fg_status launch_route(fg_ctx* ctx, const fg_route* route, int mode, int 
   ctx->route_ver += 1;
   ra.ver = ctx->route_ver;
   ra.src_row = ctx->p.src_row; ra.dst_row = ctx->p.dst_row; ra.stream_len = ctx->p.stream_len;
-  ra.group_off_out = ctx->p.group_off; ra.inv = ctx->p.inv; ra.seed = ctx->p.seed;
+  ra.group_off_out = ctx->p.group_off; ra.inv = ctx->p.inv; ra.src_of = ctx->p.src_of; ra.seed = ctx->p.seed;
   ra.group_of_rb = ctx->p.group_of_rb; ra.rbcount = ctx->p.rbcount;
   ra.wgcount = ctx->p.wgcount; ra.wgbase = ctx->p.wgbase; ra.ticket = ctx->p.ticket;
   ra.counter_cur = ctx->p.counter + (size_t)cur * ctx->rb_cap * kCtr;
@@ -362,7 +365,8 @@ static size_t plane_layout(fg_ctx* ctx, char* base) {
   const size_t wgc = (size_t)ctx->route_wg_cap * (FG_MAX_GROUPS + 1) * 4;
   const size_t o_slot = take(nch * 4), o_counter = take(2 * (size_t)ctx->rb_cap * kCtr * 4),
                o_elect = take(2 * nch * 4), o_pub = take(nch * 4), o_seed = take((size_t)ctx->rb_cap * 4),
-               o_inv = take((size_t)ctx->m_pad_cap * 8), o_grp = take((size_t)ctx->rb_cap * 4),
+               o_inv = take((size_t)ctx->m_pad_cap * 8), o_srcof = take((size_t)ctx->m_pad_cap * 4),
+               o_grp = take((size_t)ctx->rb_cap * 4),
                o_src = take(nrs * 4), o_dst = take(nrs * 4), o_slen = take((size_t)S * 4),
                o_goff = take((FG_MAX_GROUPS + 1) * 4), o_rbc = take((size_t)ctx->rb_cap * 4), o_desc = take(64), o_slab = take((size_t)ctx->rb_cap * 4), o_gslab = take((FG_MAX_GROUPS + 1) * 4),
                o_wgc = take(wgc), o_wgb = take(wgc), o_tick = take(64), o_gtick = take(2 * kTickInts * 4),
@@ -382,6 +386,7 @@ static size_t plane_layout(fg_ctx* ctx, char* base) {
   Plane& p = ctx->p;
   p.slot = (int*)(b + o_slot); p.counter = (int*)(b + o_counter); p.elect = (int*)(b + o_elect);
   p.pub_count = (int*)(b + o_pub); p.seed = (int*)(b + o_seed); p.inv = (unsigned long long*)(b + o_inv);
+  p.src_of = (int*)(b + o_srcof);
   p.wgcount = (int*)(b + o_wgc); p.wgbase = (int*)(b + o_wgb); p.ticket = (int*)(b + o_tick);
   p.gtick = (int*)(b + o_gtick); p.skc = (int*)(b + o_skc);
   p.trace = (long long*)(b + o_trace); p.rb_time = (long long*)(b + o_rbt);
@@ -563,6 +568,7 @@ static fg_status gather_gemm_launch(fg_ctx* ctx, const void* const* shards, cons
   a.elect_cur = ctx->p.elect + (size_t)cur * c.n_shards * ctx->chunk_cap;
   a.elect_nxt = ctx->p.elect + (size_t)nxt * c.n_shards * ctx->chunk_cap;
   a.pub_count = ctx->p.pub_count; a.seed = ctx->p.seed; a.inv = ctx->p.inv; a.route_ver = ctx->route_ver;
+  a.src_of = ctx->p.src_of;
   a.group_of_rb = ctx->p.group_of_rb;
   a.src_row = ctx->p.src_row; a.dst_row = ctx->p.dst_row; a.stream_len = ctx->p.stream_len; a.desc = ctx->p.desc; a.slab = ctx->p.slab; a.gslab = ctx->p.gslab; a.stats = ctx->p.stats;
   a.wgtime = ctx->p.wgtime; a.err = sink(ctx); a.seq = ctx->seq;
@@ -599,6 +605,28 @@ static fg_status gather_gemm_launch(fg_ctx* ctx, const void* const* shards, cons
   a.rhead_nxt = ctx->p.rhead + (size_t)nxt * ctx->ring_cap * kCtr;
   if (staging)
     for (int i = 0; i < c.n_shards; ++i) a.staging[i] = (uint16_t*)staging[i];
+  // in-tile copy (copy_mode 1) where the shape allows it: a one-group dense
+  // route, per-XCD tile lists without a forced split, whole 1 KB segments per
+  // row and at least three per row (the copy of a row spans that many stages),
+  // the one-stage copy and counter gates. Every workgroup then copies the lead
+  // rows first (the grid's copy role), and the compute items copy the rest.
+  {
+    const int grid = a.n_comm + a.n_gemm;
+    const bool one_group = mode == FG_ROUTE_CONTIG || (mode == FG_ROUTE_EXPLICIT && (!route->group_off ||
+                                                                                     c.n_groups == 1));
+    const bool ok = c.copy_mode == 1 && one_group && !staging && !rc.ring && !(flags & FG_CALL_GATE_WATERMARK) &&
+                    grid % kXcds == 0 && c.tile_order == 0 && !a.split_forced && c.K % 512 == 0 && c.K >= 1536;
+    if (ok) {
+      const int per_list = grid / kXcds, n_tn = c.N / ctx->tile_n;
+      const long long lead = plan_lead_slabs(per_list, n_tn);
+      a.tcopy = 1;
+      a.lead_rows = (int)std::min<long long>(m_pad, 2048LL * lead);
+      a.n_comm = grid;
+      a.n_gemm = 0;
+    }
+    ctx->last_tcopy = a.tcopy;
+    ctx->last_lead_rows = a.tcopy ? a.lead_rows : 0;
+  }
   ctx->last_grid = a.n_comm + a.n_gemm;
   ctx->last_m_pad = m_pad;
   return ctx->tile_n == 256 ? launch_fused<256>(a, stream) : launch_fused<128>(a, stream);
@@ -756,6 +784,7 @@ fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait) {
   out->seq = ctx->seq; out->bseq = ctx->bseq; out->stress_seq = ctx->sseq; out->combine_seq = ctx->cseq;
   out->litmus_words = ctx->litmus_words;
   out->n_comm_wg = ctx->n_comm; out->n_gemm_wg = ctx->n_gemm; out->cu_count = ctx->cu_count;
+  out->copy_in_tiles = ctx->last_tcopy; out->lead_rows = ctx->last_lead_rows;
   out->m_pad_cap = ctx->m_pad_cap;
   if (!wait) { out->m_pad = ctx->last_m_pad; return FG_OK; }
   int err[4] = {0, 0, 0, 0}, desc = 0;
@@ -846,6 +875,7 @@ fg_status fg_views(fg_ctx* ctx, fg_views_t* v) {
   v->combine_slot = p.cslot; v->combine_elect = p.celect; v->combine_pub = p.cpub; v->src_k = p.src_k;
   v->tok_first = p.tok_first;
   v->ring_tail = (const uint64_t*)p.rtail; v->ring_head = p.rhead; v->ring_cap = ctx->ring_cap;
+  v->src_of = p.src_of;
   return FG_OK;
 }
 

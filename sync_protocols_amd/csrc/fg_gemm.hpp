@@ -228,22 +228,39 @@ struct Mix {
 // split keeps that many loads from queueing behind one another in phase B,
 // where each wave would stall at the issue of its next load and leave the
 // matrix pipe idle.
-template <int BM, int BN, bool has_next, bool refill>
-__device__ __forceinline__ void stage_body(const char* cur, const char* nxt,
-                                           Frags<BM, BN>& f0, Acc<BM, BN>& acc, int wm, int wn, int lane,
-                                           __amdgpu_buffer_rsrc_t rA, uint32_t a_off, __amdgpu_buffer_rsrc_t rB,
-                                           uint32_t b_off, uint32_t stride, uint32_t k1_bytes, uint32_t k2_bytes,
-                                           char* cur_w, char* nxt_w, int wave) {
+// The hook (the in-tile copy of rows for later tiles) adds memory
+// instructions to the stages: store<P>(k) and load<P>(k) right after the
+// first MFMA of phase B (P = the stage's parity), in that MFMA's shadow, and
+// mid(k) between phase A's wait for this wave's loads and its workgroup
+// barrier, where the compiler waits for every memory operation anyway, so
+// that what mid issues leaves nothing pending for the rest of the loop.
+struct NoHook {
+  template <int P>
+  __device__ __forceinline__ void store(int) {}
+  template <int P>
+  __device__ __forceinline__ void load(int) {}
+  __device__ __forceinline__ void mid(int) {}
+};
+
+// Phase A of stage k (in `cur`, its k-step 0 fragments in f0): the MFMAs of
+// k-steps 0-2, the reads of k-steps 1-3 (f3 holds k-step 3's on return), the
+// weight half of stage k+1's loads into `nxt_w` during k-steps 0 and 1; then
+// (has_next) the wait for this wave's loads and the hook's mid, and the
+// workgroup barrier, which publishes stage k+1 and retires `cur`.
+template <int BM, int BN, bool has_next, class Hook>
+__device__ __forceinline__ void phase_a(const char* cur, Frags<BM, BN>& f0, Frags<BM, BN>& f3, Acc<BM, BN>& acc,
+                                        int wm, int wn, int lane, __amdgpu_buffer_rsrc_t rA, uint32_t a_off,
+                                        __amdgpu_buffer_rsrc_t rB, uint32_t b_off, uint32_t stride,
+                                        uint32_t k1_bytes, char* nxt_w, int wave, Hook& hook, int kst) {
   using T = Tile<BM, BN>;
   constexpr int NM = T::FM * T::FN;        // MFMAs per k-step
   constexpr int NR = T::FM + T::FN;        // fragment reads per k-step
   constexpr int LB0 = T::LOADS_B / 2;      // weight loads in k-step 0's shadow, the rest in k-step 1's
   using M0 = Mix<NR, has_next ? LB0 : 0>;
   using M1 = Mix<NR, has_next ? T::LOADS_B - LB0 : 0>;
-  using MB = Mix<NR, refill ? T::LOADS_A : 0>;
   const char* curB = cur + T::A_BYTES;
-  Frags<BM, BN> f1, f2, f3;
-  // phase A, k-step 0 (reads k-step 1, weight loads of stage k+1)
+  Frags<BM, BN> f1, f2;
+  // k-step 0 (reads k-step 1, weight loads of stage k+1)
 #pragma unroll
   for (int j = 0; j < NM; ++j) {
     mfma_one<BM, BN>(f0, acc, j);
@@ -275,12 +292,35 @@ __device__ __forceinline__ void stage_body(const char* cur, const char* nxt,
     for (int o = (j * NR) / NM; o < ((j + 1) * NR) / NM; ++o) frag_read_one<BM, BN>(cur, curB, f3, 3, o, wm, wn, lane);
     FG_SCHED_FENCE();
   }
-  if constexpr (has_next) wait_vmcnt<0>();
+  if constexpr (has_next) {
+    wait_vmcnt<0>();
+    hook.mid(kst);   // only after the wait for this wave's memory operations
+  }
   __syncthreads();
-  // phase B, k-step 3 (reads k-step 0 of stage k+1, gathered-row loads of stage k+2 into `cur`)
+}
+
+// Phase B of stage k: the MFMAs of k-step 3 (f3); in their shadow the hook's
+// copy instructions, the reads of k-step 0 of stage k+1 from `nxt` into f0
+// (has_next) and the gathered-row half of stage k+2's loads into `cur_w`
+// (refill), the slot phase A's barrier retired.
+template <int BM, int BN, bool has_next, bool refill, int PAR, class Hook>
+__device__ __forceinline__ void phase_b(const char* nxt, Frags<BM, BN>& f3, Frags<BM, BN>& f0, Acc<BM, BN>& acc,
+                                        int wm, int wn, int lane, __amdgpu_buffer_rsrc_t rA, uint32_t a_off,
+                                        __amdgpu_buffer_rsrc_t rB, uint32_t b_off, uint32_t stride,
+                                        uint32_t k2_bytes, char* cur_w, int wave, Hook& hook, int kst) {
+  using T = Tile<BM, BN>;
+  constexpr int NM = T::FM * T::FN;
+  constexpr int NR = T::FM + T::FN;
+  using MB = Mix<NR, refill ? T::LOADS_A : 0>;
 #pragma unroll
   for (int j = 0; j < NM; ++j) {
     mfma_one<BM, BN>(f3, acc, j);
+    if (j == 0) {
+      FG_SCHED_FENCE();
+      hook.template store<PAR>(kst);
+      hook.template load<PAR>(kst);
+      FG_SCHED_FENCE();
+    }
 #pragma unroll
     for (int o = (j * MB::OPS) / NM; o < ((j + 1) * MB::OPS) / NM; ++o) {
       if (MB::load(o)) stage_load_one<BM, BN>(rA, a_off, rB, b_off, stride, k2_bytes, cur_w, wave, lane, MB::index(o));
@@ -445,10 +485,10 @@ __device__ __forceinline__ void tile_mainloop_pp(__amdgpu_buffer_rsrc_t rA, uint
 // buffers in bytes (K * 2). l0..l3: the LDS stage buffers (distinct objects,
 // so the compiler can tell them apart when it places its own waits); the
 // 64-k variant uses l0 and l1.
-template <int BM, int BN>
+template <int BM, int BN, class Hook>
 __device__ __forceinline__ void tile_mainloop(__amdgpu_buffer_rsrc_t rA, uint32_t a_off,
                                               __amdgpu_buffer_rsrc_t rB, uint32_t b_off, uint32_t stride, int nk64,
-                                              char* l0, char* l1, char* l2, char* l3, Acc<BM, BN>& acc) {
+                                              char* l0, char* l1, char* l2, char* l3, Acc<BM, BN>& acc, Hook& hook) {
   using T = Tile<BM, BN>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -467,17 +507,32 @@ __device__ __forceinline__ void tile_mainloop(__amdgpu_buffer_rsrc_t rA, uint32_
     wait_vmcnt<T::LOADS_A>();
     __syncthreads();
     frags_read<BM, BN>(lds0, lds0 + T::A_BYTES, f0, 0, wm, wn, lane);
+    // Rotated so that every iteration ends with phase A's workgroup barrier,
+    // before which the compiler waits for all memory operations: nothing the
+    // copy hook issues in phase B is still in flight where the loop's paths
+    // meet, which would make the compiler wait for every load at the top of
+    // the next stage.
+    Frags<BM, BN> f3;
+    phase_a<BM, BN, true>(lds0, f0, f3, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, (uint32_t)1 * kRowB, lds1,
+                          wave, hook, 0);
     int kt = 0;
     for (; kt < nk - 2; kt += 2) {
-      stage_body<BM, BN, true, true>(lds0, lds1, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
-                                     (uint32_t)(kt + 1) * kRowB, (uint32_t)(kt + 2) * kRowB, lds0, lds1, wave);
-      stage_body<BM, BN, true, true>(lds1, lds0, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
-                                     (uint32_t)(kt + 2) * kRowB, (uint32_t)(kt + 3) * kRowB, lds1, lds0, wave);
+      phase_b<BM, BN, true, true, 0>(lds1, f3, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
+                                     (uint32_t)(kt + 2) * kRowB, lds0, wave, hook, kt);
+      phase_a<BM, BN, true>(lds1, f0, f3, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
+                            (uint32_t)(kt + 2) * kRowB, lds0, wave, hook, kt + 1);
+      phase_b<BM, BN, true, true, 1>(lds0, f3, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
+                                     (uint32_t)(kt + 3) * kRowB, lds1, wave, hook, kt + 1);
+      phase_a<BM, BN, true>(lds0, f0, f3, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
+                            (uint32_t)(kt + 3) * kRowB, lds1, wave, hook, kt + 2);
     }
-    stage_body<BM, BN, true, false>(lds0, lds1, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride,
-                                    (uint32_t)(nk - 1) * kRowB, 0, lds0, lds1, wave);
-    stage_body<BM, BN, false, false>(lds1, lds0, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, 0, lds1,
-                                     lds0, wave);
+    // stages nk - 2 (phase A done) and nk - 1
+    phase_b<BM, BN, true, false, 0>(lds1, f3, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, lds0, wave,
+                                    hook, nk - 2);
+    phase_a<BM, BN, false>(lds1, f0, f3, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, lds0, wave, hook,
+                           nk - 1);
+    phase_b<BM, BN, false, false, 1>(lds0, f3, f0, acc, wm, wn, lane, rA, a_off, rB, b_off, stride, 0, lds1, wave,
+                                     hook, nk - 1);
   } else {
     const int nk = 2 * nk64;   // stages of 32 k; a multiple of 4
     char* const L[4] = {l0, l1, l2, l3};

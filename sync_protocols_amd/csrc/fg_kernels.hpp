@@ -4,6 +4,7 @@
 #pragma once
 
 #include "fg_gemm.hpp"
+#include "fg_plan.hpp"
 #include "fg.h"
 
 namespace fg {
@@ -56,7 +57,12 @@ struct FusedArgs {
   int* pub_count;
   const int* seed;
   const unsigned long long* inv;   // versioned inverse map
+  const int* src_of;         // [m_pad_cap] source row of each gathered row (with the inverse map)
   uint32_t route_ver;
+  // in-tile copy: every workgroup copies the rows [0, lead_rows) first, the
+  // compute items copy the other rows inside their K loops (fg_plan.hpp)
+  int tcopy;
+  int lead_rows;
   const int* group_of_rb;
   const int* src_row;
   const int* dst_row;        // [S][rs_cap] gathered row of each stream entry
@@ -282,7 +288,10 @@ __device__ __forceinline__ void comm_role(const FusedArgs& a, const uint16_t* co
 
   const int m_pad = __builtin_amdgcn_readfirstlane(a.desc[0]);
   const int RB = a.rows_per_batch;
-  const int n_batches = m_pad / RB;
+  // in-tile copy: the copy role takes only the lead rows, which the first
+  // round of compute items reads; the items copy the rest
+  const int m_copy = (a.tcopy && !(a.flags & kCommOnly)) ? min(m_pad, a.lead_rows) : m_pad;
+  const int n_batches = m_copy / RB;
   const int upr = (a.K / 8 + 63) / 64;       // 64-lane units of 16 bytes per row
   const uint32_t row_bytes = (uint32_t)a.K * 2;
   const int nw = a.n_comm * kWaves;
@@ -603,6 +612,201 @@ __device__ __forceinline__ void ring_consumer(const FusedArgs& a, const uint16_t
 }
 
 // ---------------------------------------------------------------------------
+// In-tile copy ("PCIe sync protocols" §3-§5 carried out inside a compute
+// item): a wave of a compute workgroup copies its share of the rows of a later
+// round's slabs (fg_plan.hpp), one 1 KB segment (64 lanes x 16 bytes) per K
+// loop stage, in the shadow of the stage's MFMAs: the segment loaded in stage
+// k is stored in stage k + 1 (device-coherent write-through stores). Once the
+// wave's last store has been acknowledged (the wait for the stage loads that
+// follows it), each of its rows adds 1 to its 128-row block's arrival counter
+// ("PCIe sync protocols" §5, one add per row as on the pages), at a boundary
+// between stage pairs; after the K loop each row adds 1 to its chunk's
+// election count and the add that completes a chunk publishes seq into the
+// chunk's slot (§3).
+// Lane l describes row l of the wave (at most 64 rows).
+// ---------------------------------------------------------------------------
+struct TileCopy {
+  const FusedArgs& a;
+  CopyPlan plan;
+  int x, rho0, n_rows;     // list, first non-lead row and row count of this wave
+  int upr;                 // segments per row (K * 2 / 1024)
+  int n_seg, seg, r, u;    // segments to load, the next one, its row and segment in the row
+  int pend0, pr0, pu0;     // the segment loaded in the last even stage waits for its store: row, segment
+  int pend1, pr1, pu1;     // the same for the last odd stage
+  int k_mid;               // stage in which the rows are counted
+  int counted;             // the counting adds are issued
+  long long t_cnt;         // issue time of the counting adds (the TRACE stamp of the blocks they complete)
+  uint32_t row_bytes;
+  __amdgpu_buffer_rsrc_t rG;
+  bool strict;
+  int info;                // per lane: (shard << 24 | stream index), -1 for a padding row
+  int grow;                // per lane: gathered row
+  uint32_t src_lo, src_hi; // per lane: address of the source row (0 for a padding row)
+  uint32_t voff;           // per lane: byte offset of the lane's 16 bytes in a segment
+  v4i data0, data1;        // segments loaded in even / odd stages
+
+  __device__ __forceinline__ TileCopy(const FusedArgs& a_, const CopyPlan& p, __amdgpu_buffer_rsrc_t rg)
+      : a(a_), plan(p), x(0), rho0(0), n_rows(0), upr(1), n_seg(0), seg(0), r(0), u(0), pend0(0), pr0(0), pu0(0),
+        pend1(0), pr1(0), pu1(0),
+        k_mid(-1), counted(1), t_cnt(0), row_bytes((uint32_t)a_.K * 2), rG(rg),
+        strict((a_.flags & kStrict) != 0), info(-1), grow(0), src_lo(0), src_hi(0), voff(0) {}
+
+  // Rows [c0, c1) of list x's non-lead rows for the item; this wave's share.
+  __device__ __forceinline__ void begin(int x_, int c0, int c1, int wave, int lane) {
+    x = x_;
+    const int n = c1 - c0;
+    const int w0 = c0 + n * wave / kWaves, w1 = c0 + n * (wave + 1) / kWaves;
+    rho0 = w0;
+    n_rows = min(w1 - w0, 64);
+    // a lane describes one row: a share above 64 rows would leave rows
+    // uncounted, and their gates closed (the schedule never gives one)
+    if (w1 - w0 > 64 && lane == 0) raise_error(a.err, kErrProtocol, 0x40000000 | rho0);
+    upr = a.K / 512;
+    n_seg = n_rows * upr;
+    seg = 0; r = 0; u = 0; pend0 = 0; pend1 = 0;
+    counted = n_rows > 0 ? 0 : 1;
+    // the last segment is loaded in phase B of stage n_seg - 1 and stored in
+    // phase B of stage n_seg + 1; the wait in phase A of stage n_seg + 2
+    // acknowledges the store
+    k_mid = n_rows > 0 ? n_seg + 2 : -1;
+    info = -1;
+    grow = 0;
+    src_lo = src_hi = 0;
+    // computed by an opaque instruction, so that the compiler keeps it in one
+    // register instead of recomputing it into registers the stages reuse
+    asm volatile("v_lshlrev_b32 %0, 4, %1" : "=v"(voff) : "v"(lane));
+    if (lane < n_rows) {
+      grow = plan_row(plan, x, rho0 + lane);
+      info = inv_read(a.inv, grow, a.route_ver);
+      if (info >= 0) {
+        // the source row's address, read here once so that the loop needs no
+        // scalar load (whose wait would also cover the stage's LDS reads)
+        const uint64_t p = (uint64_t)(a.shards[info >> 24] + (size_t)a.src_of[grow] * a.K);
+        src_lo = (uint32_t)p;
+        src_hi = (uint32_t)(p >> 32);
+      }
+    }
+  }
+
+  // The copy in the K loop (P = the stage's parity): early in phase B of
+  // stage k the wave stores the segment it loaded in stage k - 2 and loads
+  // the next one into the same registers; the load's latency hides behind
+  // the rest of phase B and phase A of stage k + 1, which ends with the wait
+  // for the wave's loads. Both instructions are issued in every stage, with a
+  // zero-sized descriptor when there is nothing to move (the buffer unit
+  // drops such a store and returns zeros for such a load). Between a load and
+  // its store lie two of the stage barriers, before which the compiler waits
+  // for every memory operation of the wave, so neither the store waits for
+  // its data nor the next load for the store; the two register sets stay
+  // allocated through the loop (finish() reads them), so no other value lands
+  // in registers a store still reads; the per-lane offset is a register set
+  // once per item. With any of these missing, the compiler put a wait for all
+  // loads in flight at the top of the stage.
+  template <int P>
+  __device__ __forceinline__ void store(int) {
+    const int spr = P ? pr1 : pr0, spu = P ? pu1 : pu0;
+    const int g = readlane(grow, spr);
+    const bool st = (P ? pend1 : pend0) && readlane(info, spr) >= 0;
+    const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(a.gathered + (size_t)g * a.K + spu * 512, st ? 1024u : 0u);
+    store16_coherent(rd, voff, P ? data1 : data0);
+    if (P) pend1 = 0; else pend0 = 0;
+  }
+
+  template <int P>
+  __device__ __forceinline__ void load(int) {
+    const bool ld = seg < n_seg;
+    const int rr = min(r, 63);
+    const int inf = readlane(info, rr);
+    const bool valid = ld && inf >= 0;
+    const uint64_t row = ((uint64_t)(uint32_t)readlane((int)src_hi, rr) << 32) | (uint32_t)readlane((int)src_lo, rr);
+    // an invalid load has a zero-sized descriptor, so its base is never used
+    const uint16_t* sp = (const uint16_t*)row + u * 512;
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(sp, valid ? 1024u : 0u);
+    // the registers stay reserved until this load (the store just issued reads them)
+    if (P) asm volatile("" : "+v"(data1)); else asm volatile("" : "+v"(data0));
+    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
+    if (P) { data1 = v; pend1 = ld; pr1 = r; pu1 = u; }
+    else { data0 = v; pend0 = ld; pr0 = r; pu0 = u; }
+    seg += ld;
+    const int nu = u + ld;
+    const bool wrap = nu == upr;
+    u = wrap ? 0 : nu;
+    r += wrap;
+  }
+
+  // In phase A of stage k, after the wait for the wave's loads (which
+  // acknowledged the wave's last store when k > that store's stage): the
+  // wave's rows are added to their 128-row blocks' arrival counters, one add
+  // per block (reading R5: wave-aggregated adds). Each add is issued by one lane with the
+  // counter's address in the buffer descriptor and returns nothing; the
+  // stage's barrier waits for it. A block that overshoots is reported by its
+  // gate's waiter, which checks for a count above 128.
+  __device__ __forceinline__ void mid(int k) {
+    if (k == k_mid) count();
+  }
+
+  __device__ __forceinline__ void count() {
+    const int lane = threadIdx.x & 63;
+    if (strict) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    t_cnt = (long long)now_ticks();
+    const int blk = (lane < n_rows && info >= 0) ? grow / kRB : -1;
+    uint64_t pending = ballot(blk >= 0);
+    while (pending) {
+      const int l = __ffsll((long long)pending) - 1;
+      const int b = readlane(blk, l);
+      const uint64_t m = ballot(blk == b) & pending;
+      pending &= ~m;
+      if (lane == 0)
+        __builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(__popcll(m), buffer_rsrc(a.counter_cur + (size_t)b * kCtr, 4),
+                                                       0, 0, 0);
+    }
+    counted = 1;
+  }
+
+  // After the K loop: finish the copy if the loop was too short for it, count
+  // if not yet done, then elect ("PCIe sync protocols" §3): every row adds 1
+  // to its 64-row chunk's election count, and the add that completes a chunk
+  // publishes seq into the chunk's slot; an add past the chunk's size is a
+  // protocol error.
+  __device__ __forceinline__ void finish() {
+    // keeps both register sets of the copy allocated through the K loop
+    asm volatile("" ::"v"(data0), "v"(data1));
+    if (n_rows == 0) return;
+    if (!counted) {
+      while (pend0 || pend1 || seg < n_seg) {
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        store<0>(0);
+        store<1>(0);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        load<0>(0);
+        load<1>(0);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      count();
+    }
+    const int lane = threadIdx.x & 63;
+    // TRACE: each block's stamp rises to the issue time of this wave's add;
+    // the last add to a block completes it, so its stamp is the block's publish
+    if ((a.flags & kTrace) && lane < n_rows && info >= 0)
+      atomicMax((unsigned long long*)a.rb_time + grow / kRB, (unsigned long long)t_cnt);
+    if (lane < n_rows && info >= 0) {
+      const int s = info >> 24, c = (info & 0xFFFFFF) / kChunk, ch = s * a.chunk_cap + c;
+      const int expect = min(kChunk, a.stream_len[s] - kChunk * c);
+      const int old = strict ? fetch_add_acq_rel(a.elect_cur + ch, 1) : fetch_add_relaxed(a.elect_cur + ch, 1);
+      if (old + 1 == expect) {
+        if (!((a.flags & kDropPublish) && ch == 0)) slot_publish(a.slot + ch, a.seq, strict);
+        if (a.flags & kVerify) {
+          atomicAdd(a.pub_count + ch, 1);
+          atomicAdd(a.stats + ST_PUBLISHES, 1ull);
+        }
+      } else if (old + 1 > expect) {
+        raise_error(a.err, kErrProtocol, 0x10000000 | ch);
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Compute role ("PCIe sync protocols" §5 gate).
 //
 // Work lists. With a grid that is a multiple of the 8 XCDs (workgroup i runs
@@ -644,6 +848,8 @@ struct TileLists {
   int per_list;  // workgroups per list
   int forced_r;  // split tiles per list when given (>= 0), else -1: leftover of each list
   bool split;    // the tail is split
+  bool lead_order;  // in-tile copy: the lead slabs first, then groups (fg_plan.hpp)
+  CopyPlan plan;
   __device__ int slabs_of(int x) const { return by_group ? gslab[x + 1] - gslab[x] : (n_slabs - x + nx - 1) / nx; }
   __device__ int slab_at(int x, int i) const { return by_group ? gslab[x] + i : x + nx * i; }
   __device__ int len(int x) const { return slabs_of(x) * n_tn; }
@@ -660,6 +866,7 @@ struct TileLists {
   // the same, given list x's slab count and (grouped lists) first slab, so that
   // a workgroup's own list needs no table load per item
   __device__ int tile_in(int x, int ns, int base, int j) const {
+    if (lead_order) return plan_tile(plan, x, j);
     const int g = j / (GS * n_tn);
     const int gs = min(GS, ns - g * GS);
     const int rr = j - g * GS * n_tn;
@@ -676,7 +883,8 @@ template <int BM, int BN>
 __device__ __forceinline__ bool run_item(const FusedArgs& a, char* const* lds, int* sh, int m0, int n0,
                                          int g, int q, int P, int nk2, bool strict, long long& gate,
                                          __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rO,
-                                         __amdgpu_buffer_rsrc_t rW, long long* tr, int* pf_tick, int& pf_j) {
+                                         __amdgpu_buffer_rsrc_t rW, long long* tr, int* pf_tick, int& pf_j,
+                                         TileCopy& cp) {
   using T = Tile<BM, BN>;
   const bool whole = q < 0;
   const int part = whole ? 0 : q % P;
@@ -694,7 +902,8 @@ __device__ __forceinline__ bool run_item(const FusedArgs& a, char* const* lds, i
   // k0, k1 count k-iterations of 64 (128 bytes of a row)
   tile_mainloop<BM, BN>(rA, (uint32_t)m0 * row_bytes + (uint32_t)k0 * 128u, rB,
                         (uint32_t)n0 * row_bytes + (uint32_t)k0 * 128u, row_bytes, k1 - k0, lds[0], lds[1], lds[2],
-                        lds[3], acc);
+                        lds[3], acc, cp);
+  cp.finish();
   if (whole) {
     // thread 0 (when pf_tick is given): the next ticket goes out before the
     // stores; the opaque zero keeps the atomic optimizer from rewriting the add
@@ -760,6 +969,18 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
     L.GN = L.nx == 1 ? L.n_tn : gn;
     L.GS = L.nx == 1 ? 1 : max(1, per_list / gn);
   }
+  // in-tile copy (fg_plan.hpp): the lead slabs first in every list; the
+  // items copy the other rows unless the gates are pre-opened
+  L.lead_order = a.tcopy && L.nx == kXcds && !L.by_group;
+  L.plan.n_slabs = L.n_slabs;
+  L.plan.half_last = (m_pad % 256) != 0;
+  L.plan.nx = kXcds;
+  L.plan.per_list = per_list;
+  L.plan.n_tn = L.n_tn;
+  L.plan.GS = L.GS;
+  L.plan.GN = L.GN;
+  L.plan.lead = plan_lead_slabs(per_list, L.n_tn);
+  const bool copy_in_items = L.lead_order && !(a.flags & kGemmOnly);
   const int n_tiles = L.n_slabs * L.n_tn;
   // Split-K tail. Default: every list keeps a whole number of rounds of whole
   // tiles (a multiple of its workgroups); its leftover tiles are split into
@@ -806,14 +1027,14 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
   for (;;) {
     if (threadIdx.x == 0) {
       const long long t_take = (long long)now_ticks();
-      int tile = -1, q = -1, entry = 0;
+      int tile = -1, q = -1, entry = 0, jitem = -1;
       // the error flag is read with the item's first loads and examined once
       // they are out (an item taken after an error is dropped)
       const int err_word = poll_relaxed(a.err.dev + opaque_zero());   // stays a per-lane value until used
       if (!own_done) {
         const int j = pf_valid ? pf_j : fetch_add_relaxed(my_tick, 1);
         pf_valid = false;
-        if (j < my_whole) tile = L.tile_in(x, my_ns, my_base, j);
+        if (j < my_whole) { tile = L.tile_in(x, my_ns, my_base, j); jitem = j; }
         else own_done = true;
       }
       if (tile < 0 && R > 0) {
@@ -883,12 +1104,14 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
       sh[3] = q;
       sh[4] = entry;
       sh[5] = grp;
+      sh[6] = jitem;
     }
     __syncthreads();
     const int tile = __builtin_amdgcn_readfirstlane(sh[0]);
     const int q = __builtin_amdgcn_readfirstlane(sh[3]);
     const int entry = __builtin_amdgcn_readfirstlane(sh[4]);
     const int g = __builtin_amdgcn_readfirstlane(sh[5]);
+    const int jitem = __builtin_amdgcn_readfirstlane(sh[6]);
     if (!sh[1]) break;
     // the tile reads the gathered rows with device-scope loads issued after the
     // gate poll returned 128; the formal acquire fence is the strict variant
@@ -899,10 +1122,16 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
                                                                             : nullptr;
     int* const pf_tick = (threadIdx.x == 0 && q < 0 && !own_done) ? my_tick : nullptr;
     const long long gate_before = gate;
+    TileCopy cp(a, L.plan, rA);
+    if (copy_in_items && q < 0 && jitem >= 0) {
+      int c0, c1;
+      plan_item_rows(L.plan, x, jitem, &c0, &c1);
+      cp.begin(x, c0, c1, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), threadIdx.x & 63);
+    }
     const bool ok = (entry & 1) ? run_item<128, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr,
-                                                    pf_tick, pf_j)
+                                                    pf_tick, pf_j, cp)
                                 : run_item<256, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr,
-                                                    pf_tick, pf_j);
+                                                    pf_tick, pf_j, cp);
     if (pf_tick) pf_valid = true;
     max_wait = max(max_wait, gate - gate_before);   // a split-K part's wait for its siblings
     if (!ok) break;
@@ -930,7 +1159,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(FusedArgs) {
   __shared__ __attribute__((aligned(16))) char lds3[kS23];
   char* const lds[4] = {lds0, lds1, lds2, lds3};
   __shared__ const uint16_t* sh_shard[FG_MAX_SHARDS];
-  __shared__ int sh[6];   // item broadcast: tile, ok, part ok, part, slab entry, group
+  __shared__ int sh[8];   // item broadcast: tile, ok, part ok, part, slab entry, group, list item
   long long* wt = a.wgtime + (size_t)blockIdx.x * kWgTimeFields;
   const long long t_start = (long long)now_ticks();
   const long long c_start = (long long)__builtin_amdgcn_s_memtime();
@@ -1020,6 +1249,7 @@ struct RouteArgs {
   int* stream_len;
   int* group_off_out;
   unsigned long long* inv;
+  int* src_of;               // [m_pad_cap] source row of each gathered row (read with the inverse map)
   int* seed;
   int* group_of_rb;
   int* rbcount;              // EXPLICIT: real rows per row block (zero between calls)
@@ -1111,6 +1341,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_contig_kernel(RouteArgs a
   for (int g = tid; g < M; g += nth) {
     const int s = g / R, i = g - s * R;
     a.inv[g] = inv_pack(a.ver, (s << 24) | i);
+    a.src_of[g] = i;
     a.src_row[s * a.rs_cap + i] = i;
     a.dst_row[s * a.rs_cap + i] = g;
   }
@@ -1149,6 +1380,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_explicit_kernel(RouteArgs
     }
     a.src_row[f] = src;
     a.dst_row[f] = dst;
+    a.src_of[dst] = src;
     const unsigned long long old = atomicExch(a.inv + dst, inv_pack(a.ver, (s << 24) | i));
     if ((uint32_t)(old >> 32) == a.ver) {
       raise_error(a.err, kErrProtocol, 0x30000000 | dst);
@@ -1328,6 +1560,7 @@ __device__ void topk_place(const RouteArgs& a, const uint8_t* sh_tk, const int* 
     a.src_row[s * a.rs_cap + i] = t;
     a.src_k[s * a.rs_cap + i] = kk;
     a.dst_row[s * a.rs_cap + i] = rank;
+    a.src_of[rank] = t;
     a.inv[rank] = inv_pack(a.ver, (s << 24) | i);
   }
 }

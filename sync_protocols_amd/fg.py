@@ -44,7 +44,8 @@ class FgConfig(C.Structure):
                 ("n_gemm_wg", C.c_int32), ("tile_n", C.c_int32), ("timeout_ns", C.c_int64),
                 ("stress_producers", C.c_int32), ("stress_consumers", C.c_int32),
                 ("stress_max_chunks", C.c_int32), ("split_parts", C.c_int32), ("split_tiles", C.c_int32),
-                ("tile_order", C.c_int32), ("copy_rows", C.c_int32), ("combine_wg", C.c_int32)]
+                ("tile_order", C.c_int32), ("copy_rows", C.c_int32), ("combine_wg", C.c_int32),
+                ("copy_mode", C.c_int32)]
 
 
 class FgRoute(C.Structure):
@@ -67,7 +68,8 @@ class FgStats(C.Structure):
                 ("split_parts", C.c_int32), ("combine_seq", C.c_int32), ("clock_mhz", C.c_double),
                 ("litmus_stale", C.c_int64), ("litmus_words", C.c_int64),
                 ("expected_publishes", C.c_int64), ("timeouts", C.c_int64), ("max_wait_ns", C.c_int64),
-                ("first_timeout_id", C.c_int32), ("reserved3", C.c_int32)]
+                ("first_timeout_id", C.c_int32), ("copy_in_tiles", C.c_int32), ("lead_rows", C.c_int32),
+                ("reserved4", C.c_int32)]
 
 
 class FgViews(C.Structure):
@@ -79,7 +81,8 @@ class FgViews(C.Structure):
         ("trace_cap", C.c_int32), ("wall_khz", C.c_int64), ("desc", C.c_void_p), ("slab", C.c_void_p),
         ("group_slab", C.c_void_p), ("combine_slot", C.c_void_p), ("combine_elect", C.c_void_p),
         ("combine_pub", C.c_void_p), ("src_k", C.c_void_p), ("tok_first", C.c_void_p),
-        ("ring_tail", C.c_void_p), ("ring_head", C.c_void_p), ("ring_cap", C.c_int32), ("reserved2", C.c_int32)]
+        ("ring_tail", C.c_void_p), ("ring_head", C.c_void_p), ("ring_cap", C.c_int32), ("reserved2", C.c_int32),
+        ("src_of", C.c_void_p)]
 
 
 class FgError(RuntimeError):
@@ -147,11 +150,15 @@ def _ptr(t: torch.Tensor) -> C.c_void_p:
     return C.c_void_p(t.data_ptr())
 
 
+COPY_WORKGROUPS, COPY_IN_TILES = 0, 1
+
+
 def make_config(n_shards, max_rows_per_shard, K, N, n_groups=1, n_comm_wg=0, n_gemm_wg=0, tile_n=0,
                 timeout_ns=0, stress=(0, 0, 0), split_parts=0, split_tiles=0, tile_order=0,
-                copy_rows=0, combine_wg=0) -> FgConfig:
+                copy_rows=0, combine_wg=0, copy_mode=COPY_WORKGROUPS) -> FgConfig:
     return FgConfig(n_shards, max_rows_per_shard, K, N, n_groups, n_comm_wg, n_gemm_wg, tile_n, timeout_ns,
-                    stress[0], stress[1], stress[2], split_parts, split_tiles, tile_order, copy_rows, combine_wg)
+                    stress[0], stress[1], stress[2], split_parts, split_tiles, tile_order, copy_rows, combine_wg,
+                    copy_mode)
 
 
 def ring_bytes(cfg: FgConfig, n_channels: int, ring_chunks: int) -> int:

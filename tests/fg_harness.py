@@ -87,12 +87,12 @@ def ep_case(seed, n_shards, tokens, K, N, n_experts=64, topk=8, n_local=8, exper
 
 
 def make_ctx(case: Case, *, n_comm=0, n_gemm=0, tile_n=0, timeout_ns=0, max_rows=None, split_parts=0,
-             split_tiles=0, tile_order=0, combine_wg=0, copy_rows=0) -> fg.Context:
+             split_tiles=0, tile_order=0, combine_wg=0, copy_rows=0, copy_mode=fg.COPY_WORKGROUPS) -> fg.Context:
     max_rows = max_rows or max(int(case.lay.stream_len.max()), case.rows_per_shard)
     cfg = fg.make_config(len(case.shards), max_rows, case.K, case.N, n_groups=case.n_groups,
                          n_comm_wg=n_comm, n_gemm_wg=n_gemm, tile_n=tile_n, timeout_ns=timeout_ns,
                          split_parts=split_parts, split_tiles=split_tiles, tile_order=tile_order,
-                         combine_wg=combine_wg, copy_rows=copy_rows)
+                         combine_wg=combine_wg, copy_rows=copy_rows, copy_mode=copy_mode)
     return fg.Context(cfg)
 
 
@@ -133,6 +133,7 @@ def control_plane(ctx: fg.Context, n_shards: int):
         group_slab=ctx.read_i32(v.group_slab, 65).numpy(),
         src_row=ctx.read_i32(v.src_row, S * ctx.cfg.max_rows_per_shard).numpy().reshape(S, -1),
         dst_row=ctx.read_i32(v.dst_row, S * ctx.cfg.max_rows_per_shard).numpy().reshape(S, -1),
+        src_of=ctx.read_i32(v.src_of, v.m_pad_cap).numpy(),
         chunk_cap=cc, rb_cap=rbc)
 
 
@@ -161,6 +162,9 @@ def check_route(case: Case, cp) -> None:
         n = int(lay.stream_len[s])
         assert np.array_equal(cp["src_row"][s, :n], lay.src_row[s]), f"src_row shard {s}"
         assert np.array_equal(cp["dst_row"][s, :n], lay.dst_row[s]), f"dst_row shard {s}"
+        # the per-row source table the in-tile copy reads
+        assert np.array_equal(cp["src_of"][np.asarray(lay.dst_row[s], dtype=np.int64)], lay.src_row[s]), \
+            f"source row of the gathered rows of shard {s}"
     assert np.array_equal(cp["group_off"][:lay.n_groups + 1], lay.group_off), "group offsets"
     want = expected_slabs(lay)
     assert int(cp["desc"][0]) == lay.m_pad and int(cp["desc"][1]) == len(want), "m_pad / slab count"
