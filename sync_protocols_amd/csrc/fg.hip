@@ -100,6 +100,7 @@ struct fg_ctx {
   int route_cached_mode = -1;
   int route_cached_rows = -1;
   int last_grid = 0;
+  int last_n_comm = 0;   // copy-role workgroups of the last fused kernel (all of them with the in-tile copy)
   int last_m_pad = 0;
   int last_tcopy = 0, last_lead_rows = 0;
   unsigned long long host_stats[ST_COUNT] = {};
@@ -628,6 +629,7 @@ static fg_status gather_gemm_launch(fg_ctx* ctx, const void* const* shards, cons
     ctx->last_lead_rows = a.tcopy ? a.lead_rows : 0;
   }
   ctx->last_grid = a.n_comm + a.n_gemm;
+  ctx->last_n_comm = a.n_comm;
   ctx->last_m_pad = m_pad;
   return ctx->tile_n == 256 ? launch_fused<256>(a, stream) : launch_fused<128>(a, stream);
 }
@@ -827,7 +829,7 @@ fg_status fg_stats(fg_ctx* ctx, fg_stats_t* out, int wait) {
       const long long* t = wg + (size_t)i * kWgTimeFields;
       t0 = std::min(t0, t[WT_START]);
       t1 = std::max(t1, t[WT_END]);
-      if (i < ctx->n_comm) c1 = std::max(c1, t[WT_COMM_END]);
+      if (i < ctx->last_n_comm) c1 = std::max(c1, t[WT_COMM_END]);
       cyc += (double)(t[WT_CLK1] - t[WT_CLK0]);
       wmax = std::max(wmax, t[WT_MAXWAIT]);
       wall += (double)(t[WT_END] - t[WT_START]);
