@@ -234,12 +234,15 @@ struct Mix {
 // mid(k) between phase A's wait for this wave's loads and its workgroup
 // barrier, where the compiler waits for every memory operation anyway, so
 // that what mid issues leaves nothing pending for the rest of the loop.
+// Items that copy nothing run the loop with NoHook: with the copy's
+// instructions issued empty in every stage the tile was 4-8 % slower.
 struct NoHook {
   template <int P>
   __device__ __forceinline__ void store(int) {}
   template <int P>
   __device__ __forceinline__ void load(int) {}
   __device__ __forceinline__ void mid(int) {}
+  __device__ __forceinline__ void finish() {}
 };
 
 // Phase A of stage k (in `cur`, its k-step 0 fragments in f0): the MFMAs of

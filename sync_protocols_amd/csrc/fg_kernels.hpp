@@ -637,6 +637,7 @@ struct TileCopy {
   int counted;             // the counting adds are issued
   long long t_cnt;         // issue time of the counting adds (the TRACE stamp of the blocks they complete)
   uint32_t row_bytes;
+  uint32_t g_lo, g_hi;     // the gathered buffer, held in registers (no argument load in the loop)
   __amdgpu_buffer_rsrc_t rG;
   bool strict;
   int info;                // per lane: (shard << 24 | stream index), -1 for a padding row
@@ -648,12 +649,15 @@ struct TileCopy {
   __device__ __forceinline__ TileCopy(const FusedArgs& a_, const CopyPlan& p, __amdgpu_buffer_rsrc_t rg)
       : a(a_), plan(p), x(0), rho0(0), n_rows(0), upr(1), n_seg(0), seg(0), r(0), u(0), pend0(0), pr0(0), pu0(0),
         pend1(0), pr1(0), pu1(0),
-        k_mid(-1), counted(1), t_cnt(0), row_bytes((uint32_t)a_.K * 2), rG(rg),
+        k_mid(-1), counted(1), t_cnt(0), row_bytes((uint32_t)a_.K * 2), g_lo((uint32_t)(uintptr_t)a_.gathered),
+        g_hi((uint32_t)((uintptr_t)a_.gathered >> 32)), rG(rg),
         strict((a_.flags & kStrict) != 0), info(-1), grow(0), src_lo(0), src_hi(0), voff(0) {}
 
   // Rows [c0, c1) of list x's non-lead rows for the item; this wave's share.
   __device__ __forceinline__ void begin(int x_, int c0, int c1, int wave, int lane) {
     x = x_;
+    // opaque, so that the compiler keeps them instead of reloading the argument inside the loop
+    asm volatile("" : "+s"(g_lo), "+s"(g_hi));
     const int n = c1 - c0;
     const int w0 = c0 + n * wave / kWaves, w1 = c0 + n * (wave + 1) / kWaves;
     rho0 = w0;
@@ -692,41 +696,42 @@ struct TileCopy {
   // stage k the wave stores the segment it loaded in stage k - 2 and loads
   // the next one into the same registers; the load's latency hides behind
   // the rest of phase B and phase A of stage k + 1, which ends with the wait
-  // for the wave's loads. Both instructions are issued in every stage, with a
-  // zero-sized descriptor when there is nothing to move (the buffer unit
-  // drops such a store and returns zeros for such a load). Between a load and
-  // its store lie two of the stage barriers, before which the compiler waits
-  // for every memory operation of the wave, so neither the store waits for
-  // its data nor the next load for the store; the two register sets stay
-  // allocated through the loop (finish() reads them), so no other value lands
-  // in registers a store still reads; the per-lane offset is a register set
-  // once per item. With any of these missing, the compiler put a wait for all
-  // loads in flight at the top of the stage.
+  // for the wave's loads. Each is a uniform branch, taken only while there
+  // is a segment to move (the branch costs a few scalar instructions; the
+  // descriptors and the instructions, issued empty in every stage, cost 4-8 %
+  // of the tile). Between a load and its store lie two of the stage barriers,
+  // before which the compiler waits for every memory operation of the wave,
+  // so neither the store waits for its data nor the next load for the store;
+  // the two register sets stay allocated through the loop (finish() reads
+  // them), so no other value lands in registers a store still reads; the
+  // per-lane offset is a register set once per item. With any of these
+  // missing, the compiler put a wait for all loads in flight at the top of
+  // the stage.
   template <int P>
   __device__ __forceinline__ void store(int) {
     const int spr = P ? pr1 : pr0, spu = P ? pu1 : pu0;
-    const int g = readlane(grow, spr);
-    const bool st = (P ? pend1 : pend0) && readlane(info, spr) >= 0;
-    const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(a.gathered + (size_t)g * a.K + spu * 512, st ? 1024u : 0u);
-    store16_coherent(rd, voff, P ? data1 : data0);
+    if ((P ? pend1 : pend0) && readlane(info, spr) >= 0) {
+      const int g = readlane(grow, spr);
+      const uint16_t* gbase = (const uint16_t*)(((uint64_t)g_hi << 32) | g_lo);
+      const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(gbase + (size_t)g * (row_bytes / 2) + spu * 512, 1024u);
+      store16_coherent(rd, voff, P ? data1 : data0);
+    }
     if (P) pend1 = 0; else pend0 = 0;
   }
 
   template <int P>
   __device__ __forceinline__ void load(int) {
     const bool ld = seg < n_seg;
-    const int rr = min(r, 63);
-    const int inf = readlane(info, rr);
-    const bool valid = ld && inf >= 0;
-    const uint64_t row = ((uint64_t)(uint32_t)readlane((int)src_hi, rr) << 32) | (uint32_t)readlane((int)src_lo, rr);
-    // an invalid load has a zero-sized descriptor, so its base is never used
-    const uint16_t* sp = (const uint16_t*)row + u * 512;
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(sp, valid ? 1024u : 0u);
-    // the registers stay reserved until this load (the store just issued reads them)
-    if (P) asm volatile("" : "+v"(data1)); else asm volatile("" : "+v"(data0));
-    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
-    if (P) { data1 = v; pend1 = ld; pr1 = r; pu1 = u; }
-    else { data0 = v; pend0 = ld; pr0 = r; pu0 = u; }
+    if (ld && readlane(info, r) >= 0) {
+      const uint64_t row = ((uint64_t)(uint32_t)readlane((int)src_hi, r) << 32) | (uint32_t)readlane((int)src_lo, r);
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc((const uint16_t*)row + u * 512, 1024u);
+      // the registers stay reserved until this load (the store just issued reads them)
+      if (P) asm volatile("" : "+v"(data1)); else asm volatile("" : "+v"(data0));
+      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
+      if (P) data1 = v; else data0 = v;
+    }
+    if (P) { pend1 = ld; pr1 = r; pu1 = u; }
+    else { pend0 = ld; pr0 = r; pu0 = u; }
     seg += ld;
     const int nu = u + ld;
     const bool wrap = nu == upr;
@@ -879,12 +884,12 @@ struct TileLists {
 
 // One work item on a BM-row slab: the tile (whole) or one k-range of it
 // (part q of P, split slot `slot`). Returns false if a wait failed.
-template <int BM, int BN>
+template <int BM, int BN, class Hook>
 __device__ __forceinline__ bool run_item(const FusedArgs& a, char* const* lds, int* sh, int m0, int n0,
                                          int g, int q, int P, int nk2, bool strict, long long& gate,
                                          __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rO,
                                          __amdgpu_buffer_rsrc_t rW, long long* tr, int* pf_tick, int& pf_j,
-                                         TileCopy& cp) {
+                                         Hook& cp) {
   using T = Tile<BM, BN>;
   const bool whole = q < 0;
   const int part = whole ? 0 : q % P;
@@ -1122,16 +1127,24 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
                                                                             : nullptr;
     int* const pf_tick = (threadIdx.x == 0 && q < 0 && !own_done) ? my_tick : nullptr;
     const long long gate_before = gate;
-    TileCopy cp(a, L.plan, rA);
-    if (copy_in_items && q < 0 && jitem >= 0) {
-      int c0, c1;
-      plan_item_rows(L.plan, x, jitem, &c0, &c1);
+    // an item with rows to copy runs the loop with the copy; every other item without it
+    int c0 = 0, c1 = 0;
+    if (copy_in_items && q < 0 && jitem >= 0) plan_item_rows(L.plan, x, jitem, &c0, &c1);
+    bool ok;
+    if (c1 > c0) {
+      TileCopy cp(a, L.plan, rA);
       cp.begin(x, c0, c1, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), threadIdx.x & 63);
+      ok = (entry & 1) ? run_item<128, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr, pf_tick,
+                                           pf_j, cp)
+                       : run_item<256, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr, pf_tick,
+                                           pf_j, cp);
+    } else {
+      NoHook nh;
+      ok = (entry & 1) ? run_item<128, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr, pf_tick,
+                                           pf_j, nh)
+                       : run_item<256, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr, pf_tick,
+                                           pf_j, nh);
     }
-    const bool ok = (entry & 1) ? run_item<128, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr,
-                                                    pf_tick, pf_j, cp)
-                                : run_item<256, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr,
-                                                    pf_tick, pf_j, cp);
     if (pf_tick) pf_valid = true;
     max_wait = max(max_wait, gate - gate_before);   // a split-K part's wait for its siblings
     if (!ok) break;
