@@ -638,7 +638,6 @@ struct TileCopy {
   long long t_cnt;         // issue time of the counting adds (the TRACE stamp of the blocks they complete)
   uint32_t row_bytes;
   uint32_t g_lo, g_hi;     // the gathered buffer, held in registers (no argument load in the loop)
-  __amdgpu_buffer_rsrc_t rG;
   bool strict;
   int info;                // per lane: (shard << 24 | stream index), -1 for a padding row
   int grow;                // per lane: gathered row
@@ -646,11 +645,11 @@ struct TileCopy {
   uint32_t voff;           // per lane: byte offset of the lane's 16 bytes in a segment
   v4i data0, data1;        // segments loaded in even / odd stages
 
-  __device__ __forceinline__ TileCopy(const FusedArgs& a_, const CopyPlan& p, __amdgpu_buffer_rsrc_t rg)
+  __device__ __forceinline__ TileCopy(const FusedArgs& a_, const CopyPlan& p)
       : a(a_), plan(p), x(0), rho0(0), n_rows(0), upr(1), n_seg(0), seg(0), r(0), u(0), pend0(0), pr0(0), pu0(0),
         pend1(0), pr1(0), pu1(0),
         k_mid(-1), counted(1), t_cnt(0), row_bytes((uint32_t)a_.K * 2), g_lo((uint32_t)(uintptr_t)a_.gathered),
-        g_hi((uint32_t)((uintptr_t)a_.gathered >> 32)), rG(rg),
+        g_hi((uint32_t)((uintptr_t)a_.gathered >> 32)),
         strict((a_.flags & kStrict) != 0), info(-1), grow(0), src_lo(0), src_hi(0), voff(0) {}
 
   // Rows [c0, c1) of list x's non-lead rows for the item; this wave's share.
@@ -1132,7 +1131,7 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
     if (copy_in_items && q < 0 && jitem >= 0) plan_item_rows(L.plan, x, jitem, &c0, &c1);
     bool ok;
     if (c1 > c0) {
-      TileCopy cp(a, L.plan, rA);
+      TileCopy cp(a, L.plan);
       cp.begin(x, c0, c1, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), threadIdx.x & 63);
       ok = (entry & 1) ? run_item<128, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr, pf_tick,
                                            pf_j, cp)
