@@ -121,7 +121,7 @@ def test_plan_random_shapes(driver):
     for _ in range(60):
         n_slabs = int(rng.integers(1, 300))
         half = int(rng.integers(0, 2))
-        per_list = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        per_list = int(rng.choice([1, 2, 4, 8, 9, 16, 17, 25, 32]))   # grid / 8 for grids of 8 to 256
         n_tn = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
         lists, items = run_plan(driver, n_slabs, half, per_list, n_tn)
         m = check_plan(lists, items, n_slabs, half, per_list, n_tn)

@@ -11,7 +11,9 @@ whichever workgroup copies its rows.
 
 Shapes: only lead rows; several groups of non-lead slabs; a 128-row last slab
 with padding rows; seeded permutation routes; a per-item share long enough
-that the copy is finished after the K loop."""
+that the copy is finished after the K loop; and 16 seeded random shapes with
+both tile widths, smaller grids, a grid that is not a multiple of the XCDs
+(which falls back to copy workgroups), strict fences and tracing."""
 import numpy as np
 import pytest
 import torch
@@ -149,4 +151,37 @@ def test_tile_copy_not_used_where_the_shape_does_not_allow_it():
     st = ctx.stats()
     assert st.error_code == 0 and st.copy_in_tiles == 0
     check_out(case, o)
+    ctx.close()
+
+
+def _draw_tile_case(seed):
+    rng = np.random.default_rng(seed)
+    kind = ["contiguous", "permutation", "explicit"][seed % 3]
+    K = int(rng.choice([1536, 2048, 2560, 3072, 4096]))
+    tile_n = int(rng.choice([128, 256]))
+    N = tile_n * int(rng.integers(1, 9))
+    S = int(rng.integers(1, 9))
+    R = int(rng.integers(1, 1500))
+    # grid: the default 256, 72 and 136 workgroups, or 201 (not a multiple of the 8 XCDs: copy workgroups instead)
+    n_comm, n_gemm = [(0, 0), (0, 0), (8, 64), (8, 128), (1, 200)][int(rng.integers(0, 5))]
+    flags = 0
+    if rng.random() < 0.3:
+        flags |= fg.CALL_STRICT
+    if rng.random() < 0.3:
+        flags |= fg.CALL_TRACE
+    return kind, K, tile_n, N, S, R, n_comm, n_gemm, flags
+
+
+@pytest.mark.parametrize("seed", range(700, 716))
+def test_tile_copy_random_shapes(seed):
+    kind, K, tile_n, N, S, R, n_comm, n_gemm, flags = _draw_tile_case(seed)
+    log(f"seed {seed}: in-tile copy, {S} x {R} rows ({kind}), K={K}, N={N}, tile_n={tile_n}, "
+        f"grid {n_comm}+{n_gemm}, flags={flags:#x}")
+    case = dense_case(seed, S, R, K, N, gather="permutation" if kind == "permutation" else "contiguous",
+                      use_explicit=kind == "explicit")
+    ctx = make_ctx(case, copy_mode=fg.COPY_IN_TILES, tile_n=tile_n, n_comm=n_comm, n_gemm=n_gemm)
+    st, _ = _calls(case, ctx, 2, flags=flags)
+    log(f"  copied in tiles: {st.copy_in_tiles}, lead rows {st.lead_rows}, whole tiles {st.tiles_whole}, "
+        f"split {st.tiles_split} x {st.split_parts}")
+    assert st.copy_in_tiles == (0 if n_gemm == 200 else 1), "the in-tile copy where the grid allows it"
     ctx.close()
