@@ -1,0 +1,68 @@
+"""Host checks of bench.py's bookkeeping (no GPU): the code hash that keys the
+recorded HBM byte counters ignores comments and white space but not code, and
+a counter record taken for other code is not reported."""
+import json
+import os
+import shutil
+
+import bench
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+
+def _tree(tmp_path):
+    """A copy of the HIP sources and the C header under tmp_path."""
+    shutil.copytree(os.path.join(ROOT, "sync_protocols_amd", "csrc"), tmp_path / "sync_protocols_amd" / "csrc")
+    os.makedirs(tmp_path / "include")
+    shutil.copy(os.path.join(ROOT, "include", "fg.h"), tmp_path / "include" / "fg.h")
+    os.makedirs(tmp_path / "profiles")
+    return tmp_path
+
+
+def _edit(path, old, new):
+    with open(path) as f:
+        text = f.read()
+    assert old in text
+    with open(path, "w") as f:
+        f.write(text.replace(old, new, 1))
+
+
+def test_hash_ignores_comments_not_code(tmp_path, monkeypatch):
+    root = _tree(tmp_path)
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    h0 = bench.kernel_source_hash()
+    assert h0 == bench.kernel_source_hash()
+    hdr = root / "include" / "fg.h"
+    _edit(hdr, "/* Per-call flags of fg_gather_gemm. */", "/* Per-call   flags, reworded. */\n\n")
+    assert bench.kernel_source_hash() == h0, "a comment or white-space edit changed the hash"
+    src = root / "sync_protocols_amd" / "csrc" / "fg_plan.hpp"
+    _edit(src, "return (per_list + n_tn - 1) / n_tn;", "return (per_list + n_tn) / n_tn;")
+    assert bench.kernel_source_hash() != h0, "a code edit left the hash unchanged"
+
+
+def test_traffic_record_only_for_the_same_code(tmp_path, monkeypatch):
+    root = _tree(tmp_path)
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(root / "profiles" / "traffic.json"))
+    assert bench.recorded_traffic("large") is None          # no record at all
+    rec = {"source_sha256": bench.kernel_source_hash(),
+           "workloads": {"large": {"hbm_bytes_per_launch": 123456789}}}
+    with open(root / "profiles" / "traffic.json", "w") as f:
+        json.dump(rec, f)
+    assert bench.recorded_traffic("large") == 123456789
+    assert bench.recorded_traffic("tp") is None             # no entry for this workload
+    rec["source_sha256"] = "0" * 64
+    with open(root / "profiles" / "traffic.json", "w") as f:
+        json.dump(rec, f)
+    assert bench.recorded_traffic("large") is None          # taken for other code
+
+
+def test_committed_traffic_record_matches_the_sources():
+    """The committed counter record is keyed to the committed kernel code, so
+    the bench line reports it (re-collected whenever the kernel changes)."""
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        rec = json.load(f)
+    assert rec["source_sha256"] == bench.kernel_source_hash()
+    for w in ("large", "tp"):
+        assert rec["workloads"][w]["hbm_bytes_per_launch"] > 0
