@@ -369,7 +369,7 @@ static size_t plane_layout(fg_ctx* ctx, char* base) {
                o_inv = take((size_t)ctx->m_pad_cap * 8), o_srcof = take((size_t)ctx->m_pad_cap * 4),
                o_grp = take((size_t)ctx->rb_cap * 4),
                o_src = take(nrs * 4), o_dst = take(nrs * 4), o_slen = take((size_t)S * 4),
-               o_goff = take((FG_MAX_GROUPS + 1) * 4), o_rbc = take((size_t)ctx->rb_cap * 4), o_desc = take(64), o_slab = take((size_t)ctx->rb_cap * 4), o_gslab = take((FG_MAX_GROUPS + 1) * 4),
+               o_goff = take((FG_MAX_GROUPS + 1) * 4), o_rbc = take((size_t)ctx->rb_cap * kRbSlots * 4), o_desc = take(64), o_slab = take((size_t)ctx->rb_cap * 4), o_gslab = take((FG_MAX_GROUPS + 1) * 4),
                o_wgc = take(wgc), o_wgb = take(wgc), o_tick = take(64), o_gtick = take(2 * kTickInts * 4),
                o_skc = take(2 * (size_t)ctx->split_slots * 4),
                o_trace = take((size_t)ctx->trace_cap * kTraceFields * 8), o_rbt = take((size_t)ctx->rb_cap * 8),

@@ -1264,7 +1264,7 @@ struct RouteArgs {
   int* src_of;               // [m_pad_cap] source row of each gathered row (read with the inverse map)
   int* seed;
   int* group_of_rb;
-  int* rbcount;              // EXPLICIT: real rows per row block (zero between calls)
+  int* rbcount;              // EXPLICIT: [rb_cap][kRbSlots] real rows per row block, in slots (zero between calls)
   int* counter_cur;          // [rb_cap][kCtr]
   int* elect_cur;
   int* desc;
@@ -1280,6 +1280,13 @@ struct RouteArgs {
 };
 
 constexpr int kRouteThreads = 256;
+// EXPLICIT: each row block's real-row count is spread over kRbSlots words
+// (workgroup w adds to slot w % kRbSlots), which the last workgroup sums. With
+// one word per block, a block's 128 adds arrive at the same address from 128
+// threads: measured 22.5 us per Large layout (a permutation of 32768 rows),
+// 13.0 us with 8 slots, 14.9 us with 32 (the sums and clears then cost more).
+constexpr int kRbSlots = 8;
+static_assert((kRbSlots & (kRbSlots - 1)) == 0, "slot of workgroup w = w & (kRbSlots - 1)");
 
 
 // True in every thread of the workgroup that finishes last.
@@ -1398,7 +1405,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_explicit_kernel(RouteArgs
       raise_error(a.err, kErrProtocol, 0x30000000 | dst);
       atomicOr(a.ticket + 1, 1);
     }
-    atomicAdd(a.rbcount + dst / kRB, 1);
+    atomicAdd(a.rbcount + (dst / kRB) * kRbSlots + (blockIdx.x & (kRbSlots - 1)), 1);
   }
   if (!last_workgroup(a.ticket, &sh_last)) return;
   if ((int)threadIdx.x <= a.n_groups) sh_goff[threadIdx.x] = a.group_off[threadIdx.x];
@@ -1406,10 +1413,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_explicit_kernel(RouteArgs
   __syncthreads();
   const int fail = __hip_atomic_load(a.ticket + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   route_finish(a, fail ? 0 : a.m_pad, sh_goff, a.n_groups, fail != 0, [&](int rb) {
-    return __hip_atomic_load(a.rbcount + rb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int n = 0;
+    for (int j = 0; j < kRbSlots; ++j)
+      n += __hip_atomic_load(a.rbcount + rb * kRbSlots + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return n;
   });
   __syncthreads();
-  for (int rb = threadIdx.x; rb < a.rb_cap; rb += blockDim.x) a.rbcount[rb] = 0;
+  for (int i = threadIdx.x; i < a.rb_cap * kRbSlots; i += blockDim.x) a.rbcount[i] = 0;
   if (threadIdx.x == 0) { a.ticket[0] = 0; a.ticket[1] = 0; }
 }
 
