@@ -200,3 +200,37 @@ def test_zero_length_shard_streams():
     from fg_harness import Case
     case = Case("dense", d.shards, d.w, lay, route, 1, d.sigma_x, d.sigma_w, R)
     _run_and_check(case, 3)
+
+
+@pytest.mark.parametrize("seed,lens,R,hole_frac", [
+    (4101, [3000, 2500, 2999, 1], 3000, 0.10),   # 12,000 stream slots: 47 layout workgroups
+    (4102, [4096, 0, 4096, 333], 4096, 0.30),    # a third of the gathered rows are padding
+])
+def test_explicit_route_scattered_padding(seed, lens, R, hole_frac):
+    """An explicit route whose padding rows are scattered over the whole
+    gathered buffer, laid out by many workgroups: every row block's real-row
+    count is assembled from the adds of several workgroups, and the seeds,
+    counters, gathered rows and output must match the oracle."""
+    log(f"explicit route, {sum(lens)} rows over {len(lens)} shards, {hole_frac:.0%} padding")
+    S, K, N = len(lens), 256, 256
+    d = W.dense_inputs(seed, S, R, K, N)
+    rng = np.random.default_rng(seed)
+    m = sum(lens)
+    m_pad = -(-int(m / (1 - hole_frac)) // 128) * 128
+    dst_all = rng.permutation(m_pad)[:m]
+    src = np.zeros((S, R), np.int32)
+    dst = np.zeros((S, R), np.int32)
+    src_l, dst_l, j = [], [], 0
+    for s in range(S):
+        srow = rng.permutation(R)[:lens[s]]
+        src[s, :lens[s]] = srow
+        dst[s, :lens[s]] = dst_all[j:j + lens[s]]
+        src_l.append(srow.astype(np.int64))
+        dst_l.append(dst_all[j:j + lens[s]].astype(np.int64))
+        j += lens[s]
+    lay = O.Layout(src_l, dst_l, m_pad, np.array([0, m_pad]))
+    assert int(np.count_nonzero(O.seeds(lay))) > lay.m_pad // 128 // 2, "padding in most row blocks"
+    route = fg.route_explicit(lens, torch.from_numpy(src).to(DEV), torch.from_numpy(dst).to(DEV), m_pad, R)
+    from fg_harness import Case
+    case = Case("dense", d.shards, d.w, lay, route, 1, d.sigma_x, d.sigma_w, R)
+    _run_and_check(case, 3)
