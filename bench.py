@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_CLOCK_MHZ = 2400.0       # the clock that peak is quoted at
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "fused gather-GEMM TFLOP/s + overlap efficiency; slot-signal latency (\u00b5s)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -662,6 +663,11 @@ def main():
                           "algorithmic_flop_per_launch": b.flop,
                           "algorithmic_gather_bytes_per_launch": b.gather_bytes,
                           "clock_mhz": round(st.clock_mhz, 0)}
+    if st.clock_mhz > 0:
+        # context, not the contract's frac: the same peak scaled to the shader
+        # clock the part held under this load (it is power-limited below 2.4 GHz)
+        peak_clk = PEAK_BF16_TFLOPS * st.clock_mhz / PEAK_CLOCK_MHZ
+        result["roofline"].update(peak_at_clock=round(peak_clk, 1), frac_at_clock=round(achieved / peak_clk, 4))
 
     if not args.no_extras and args.mode == "fused":
         n_rep = max(10, args.steps)
