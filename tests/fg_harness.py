@@ -76,6 +76,31 @@ def dense_case(seed, n_shards, rows, K, N, gather="contiguous", use_explicit=Fal
     return Case("dense", d.shards, d.w, lay, route, 1, d.sigma_x, d.sigma_w, rows)
 
 
+def holes_case(seed, lens, R, K, N, hole_frac) -> Case:
+    """An explicit route whose streams (lengths `lens`, at most R rows per
+    shard) land on a seeded random subset of the gathered rows: about
+    `hole_frac` of them stay padding, scattered over every row block."""
+    S = len(lens)
+    d = W.dense_inputs(seed, S, R, K, N)
+    rng = np.random.default_rng(seed)
+    m = sum(lens)
+    m_pad = max(128, -(-int(m / (1 - hole_frac)) // 128) * 128)
+    dst_all = rng.permutation(m_pad)[:m]
+    src = np.zeros((S, R), np.int32)
+    dst = np.zeros((S, R), np.int32)
+    src_l, dst_l, j = [], [], 0
+    for s in range(S):
+        srow = rng.permutation(R)[:lens[s]]
+        src[s, :lens[s]] = srow
+        dst[s, :lens[s]] = dst_all[j:j + lens[s]]
+        src_l.append(srow.astype(np.int64))
+        dst_l.append(dst_all[j:j + lens[s]].astype(np.int64))
+        j += lens[s]
+    lay = O.Layout(src_l, dst_l, m_pad, np.array([0, m_pad]))
+    route = fg.route_explicit(lens, torch.from_numpy(src).to(DEV), torch.from_numpy(dst).to(DEV), m_pad, R)
+    return Case("dense", d.shards, d.w, lay, route, 1, d.sigma_x, d.sigma_w, R)
+
+
 def ep_case(seed, n_shards, tokens, K, N, n_experts=64, topk=8, n_local=8, expert_base=0) -> Case:
     e = W.ep_inputs(seed, n_shards=n_shards, tokens=tokens, K=K, N=N, n_experts=n_experts, topk=topk,
                     n_local=n_local, expert_base=expert_base)

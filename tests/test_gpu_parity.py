@@ -10,7 +10,8 @@ import oracle as O
 from sync_protocols_amd import fg
 from sync_protocols_amd import workloads as W
 from fg_harness import (DEV, POISON, bits, buffers, check_control_plane, check_gathered, check_out,
-                        check_route, control_plane, dense_case, ep_case, log, make_ctx, poison_, run_iters)
+                        check_route, control_plane, dense_case, ep_case, holes_case, log, make_ctx, poison_,
+                        run_iters)
 
 pytestmark = pytest.mark.gpu
 
@@ -212,25 +213,6 @@ def test_explicit_route_scattered_padding(seed, lens, R, hole_frac):
     count is assembled from the adds of several workgroups, and the seeds,
     counters, gathered rows and output must match the oracle."""
     log(f"explicit route, {sum(lens)} rows over {len(lens)} shards, {hole_frac:.0%} padding")
-    S, K, N = len(lens), 256, 256
-    d = W.dense_inputs(seed, S, R, K, N)
-    rng = np.random.default_rng(seed)
-    m = sum(lens)
-    m_pad = -(-int(m / (1 - hole_frac)) // 128) * 128
-    dst_all = rng.permutation(m_pad)[:m]
-    src = np.zeros((S, R), np.int32)
-    dst = np.zeros((S, R), np.int32)
-    src_l, dst_l, j = [], [], 0
-    for s in range(S):
-        srow = rng.permutation(R)[:lens[s]]
-        src[s, :lens[s]] = srow
-        dst[s, :lens[s]] = dst_all[j:j + lens[s]]
-        src_l.append(srow.astype(np.int64))
-        dst_l.append(dst_all[j:j + lens[s]].astype(np.int64))
-        j += lens[s]
-    lay = O.Layout(src_l, dst_l, m_pad, np.array([0, m_pad]))
-    assert int(np.count_nonzero(O.seeds(lay))) > lay.m_pad // 128 // 2, "padding in most row blocks"
-    route = fg.route_explicit(lens, torch.from_numpy(src).to(DEV), torch.from_numpy(dst).to(DEV), m_pad, R)
-    from fg_harness import Case
-    case = Case("dense", d.shards, d.w, lay, route, 1, d.sigma_x, d.sigma_w, R)
+    case = holes_case(seed, lens, R, 256, 256, hole_frac)
+    assert int(np.count_nonzero(O.seeds(case.lay))) > case.lay.m_pad // 128 // 2, "padding in most row blocks"
     _run_and_check(case, 3)

@@ -11,7 +11,7 @@ import pytest
 
 from sync_protocols_amd import fg
 from fg_harness import (buffers, check_control_plane, check_gathered, check_out, check_route, control_plane,
-                        dense_case, ep_case, log, make_ctx, run_iters)
+                        dense_case, ep_case, holes_case, log, make_ctx, run_iters)
 
 import oracle as O
 
@@ -106,3 +106,57 @@ def test_random_configuration(seed):
 def test_random_configuration_wide(seed):
     *rest, split = _draw_wide(seed)
     _check(seed, *rest, split, _flags(seed, rest[0]))
+
+
+def _draw_long(seed):
+    """Long rows (K up to 8192, the full-size workloads' row widths) at row
+    counts the float64 oracle checks in about a second, over four route kinds;
+    'holes' is an explicit route with padding scattered over every row block."""
+    rng = np.random.default_rng(seed)
+    kind = ["contig", "perm", "holes", "ep"][seed % 4]
+    K = int(rng.choice([3072, 4096, 7168, 8192]))
+    tile_n = int(rng.choice([128, 256]))
+    N = tile_n * int(rng.integers(1, 3))
+    n_comm = int(rng.choice([0, 24, 64]))
+    n_gemm = int(rng.choice([0, 40])) if n_comm else 0
+    copy_rows = int(rng.choice([0, 1, 2, 4]))
+    flags = fg.CALL_STRICT if rng.random() < 0.3 else 0
+    if kind == "ep":
+        n_experts = int(rng.choice([8, 16, 64]))
+        shape = dict(n_shards=int(rng.integers(1, 9)), tokens=int(rng.integers(16, 300)), n_experts=n_experts,
+                     topk=int(rng.integers(1, 9)), n_local=int(min(n_experts, rng.choice([2, 4, 8]))))
+    elif kind == "holes":
+        S = int(rng.integers(1, 9))
+        R = int(rng.integers(64, 700))
+        lens = [int(x) for x in rng.integers(0, R + 1, size=S)]
+        lens[0] = max(lens[0], 1)   # at least one real row
+        shape = dict(lens=lens, R=R, hole_frac=float(rng.choice([0.05, 0.2, 0.4])))
+    else:
+        shape = dict(n_shards=int(rng.integers(1, 9)), rows=int(rng.integers(32, 700)))
+    return kind, K, N, tile_n, n_comm, n_gemm, copy_rows, shape, flags
+
+
+@pytest.mark.parametrize("seed", list(range(300, 312)))
+def test_random_configuration_long_rows(seed):
+    kind, K, N, tile_n, n_comm, n_gemm, copy_rows, shape, flags = _draw_long(seed)
+    log(f"seed {seed}: {kind} {shape} K={K} N={N} tile_n={tile_n} n_comm={n_comm} n_gemm={n_gemm} "
+        f"copy_rows={copy_rows} flags={flags:#x}")
+    if kind == "ep":
+        case = ep_case(seed, shape["n_shards"], shape["tokens"], K, N, n_experts=shape["n_experts"],
+                       topk=shape["topk"], n_local=shape["n_local"])
+    elif kind == "holes":
+        case = holes_case(seed, shape["lens"], shape["R"], K, N, shape["hole_frac"])
+    else:
+        case = dense_case(seed, shape["n_shards"], shape["rows"], K, N,
+                          gather="permutation" if kind == "perm" else "contiguous")
+    ctx = make_ctx(case, n_comm=n_comm, n_gemm=n_gemm, tile_n=tile_n, copy_rows=copy_rows)
+    gathered, out = buffers(ctx, case)
+    iters = 2
+    st = run_iters(ctx, case, gathered, out, iters, flags=fg.CALL_VERIFY | flags)
+    cp = control_plane(ctx, len(case.shards))
+    check_route(case, cp)
+    check_control_plane(case, cp, iters, iters)
+    check_gathered(case, gathered, poisoned=True)
+    check_out(case, out)
+    assert st.publishes == iters * O.signal_counts(case.lay)["publishes"]
+    ctx.close()
