@@ -112,3 +112,34 @@ def test_ring_arguments():
     torch.cuda.synchronize()
     assert ctx.stats().error_code == 0
     ctx.close()
+
+
+def _draw_ring(seed):
+    rng = np.random.default_rng(seed)
+    kind = ["contig", "perm", "ep"][seed % 3]
+    K = int(rng.choice([256, 512, 1024]))
+    N = 128 * int(rng.integers(1, 5))
+    S = int(rng.integers(1, 7))
+    n_channels = int(rng.integers(1, 4))
+    ring_chunks = int(rng.integers(1, 4))
+    self_shard = int(rng.integers(-1, S))
+    n_comm = 8 * int(np.ceil(2 * S * n_channels / 8)) + 8 * int(rng.integers(0, 3))   # every ring served
+    return kind, K, N, S, n_channels, ring_chunks, self_shard, n_comm, rng
+
+
+@pytest.mark.parametrize("seed", list(range(500, 508)))
+def test_ring_random_configuration(seed):
+    """Seeded random ring dispatches: shard, row and ring counts, slots per
+    ring, the self shard and the route kind drawn per seed; gathered rows,
+    counters, ring words and output against the oracle."""
+    kind, K, N, S, n_channels, ring_chunks, self_shard, n_comm, rng = _draw_ring(seed)
+    if kind == "ep":
+        case = ep_case(seed, S, int(rng.integers(8, 300)), K, N, n_experts=16, topk=int(rng.integers(1, 5)),
+                       n_local=4)
+    else:
+        case = dense_case(seed, S, int(rng.integers(1, 600)), K, N,
+                          gather="permutation" if kind == "perm" else "contiguous")
+    log(f"seed {seed}: ring {kind}, {S} shards, K={K} N={N}, {n_channels} rings x {ring_chunks} slots per shard, "
+        f"self shard {self_shard}, {n_comm} copy workgroups")
+    _run(case, 2, n_channels=n_channels, ring_chunks=ring_chunks, self_shard=self_shard,
+         ctx_kw=dict(n_comm=n_comm))

@@ -145,3 +145,26 @@ def test_two_stage_invalid_arguments():
     torch.cuda.synchronize()
     assert ctx.stats().error_code == 0
     ctx.close()
+
+
+@pytest.mark.parametrize("seed", list(range(520, 528)))
+def test_two_stage_random_configuration(seed):
+    """Seeded random two-stage dispatches: shard and row counts, K, N, the
+    self shard, the copy workgroup count and the route kind drawn per seed;
+    staged rows, gathered rows, the control plane and output against the
+    oracle."""
+    rng = np.random.default_rng(seed)
+    kind = ["contig", "perm", "ep"][seed % 3]
+    K = int(rng.choice([256, 512, 1024]))
+    N = 128 * int(rng.integers(1, 5))
+    S = int(rng.integers(1, 7))
+    self_shard = int(rng.integers(-1, S))
+    n_comm = int(rng.choice([0, 8, 24, 64]))
+    if kind == "ep":
+        case = ep_case(seed, S, int(rng.integers(8, 300)), K, N, n_experts=16, topk=int(rng.integers(1, 5)),
+                       n_local=4)
+    else:
+        case = dense_case(seed, S, int(rng.integers(1, 600)), K, N,
+                          gather="permutation" if kind == "perm" else "contiguous")
+    log(f"seed {seed}: two-stage {kind}, {S} shards, K={K} N={N}, self shard {self_shard}, n_comm {n_comm}")
+    _run(case, 2, self_shard=self_shard, ctx_kw=dict(n_comm=n_comm))
