@@ -216,3 +216,37 @@ def test_explicit_route_scattered_padding(seed, lens, R, hole_frac):
     case = holes_case(seed, lens, R, 256, 256, hole_frac)
     assert int(np.count_nonzero(O.seeds(case.lay))) > case.lay.m_pad // 128 // 2, "padding in most row blocks"
     _run_and_check(case, 3)
+
+
+def test_route_changes_on_one_context():
+    """One context, the route switched between calls: contiguous (A), a
+    permutation (B) and an explicit route with scattered padding and another
+    padded size (C), in the order A B C A C B B A. Every call must give the
+    oracle's route tables, gathered rows and output for the route it was
+    given: entries of an earlier route read as padding (versioned inverse
+    map), a cached contiguous layout is rebuilt after another route, and each
+    layout arms the parity its call uses; one publisher per chunk per call."""
+    seed, S, R, K, N = 4201, 4, 500, 512, 256
+    log(f"route changes on one context: {S} x {R} rows, K={K}, N={N}, routes A B C A C B B A")
+    cases = {"A": dense_case(seed, S, R, K, N),
+             "B": dense_case(seed, S, R, K, N, gather="permutation"),
+             "C": holes_case(seed, [R // 2, R // 3, R, 7], R, K, N, 0.3)}
+    assert cases["C"].lay.m_pad != cases["A"].lay.m_pad
+    ctx = make_ctx(cases["A"])
+    gathered, out = buffers(ctx, cases["A"])
+    expected = 0
+    for name in "ABCACBBA":
+        case = cases[name]
+        poison_(gathered)
+        poison_(out)
+        assert ctx.gather_gemm(case.shards, case.w, gathered, out, route=case.route, flags=fg.CALL_VERIFY) == fg.OK
+        torch.cuda.synchronize()
+        st = ctx.stats()
+        assert st.error_code == 0, (name, st.error_code, hex(st.error_id))
+        cp = control_plane(ctx, S)
+        check_route(case, cp)
+        check_gathered(case, gathered, poisoned=True)
+        check_out(case, out)
+        expected += O.signal_counts(case.lay)["publishes"]
+        assert st.publishes == expected == st.expected_publishes, name
+    ctx.close()
