@@ -15,8 +15,9 @@ import torch
 
 import oracle as O
 from sync_protocols_amd import fg
-from fg_harness import DEV, Case, buffers, check_control_plane, check_out, check_route, control_plane, ep_case, \
-    log, make_ctx
+from sync_protocols_amd import workloads as W
+from fg_harness import DEV, Case, buffers, check_control_plane, check_gathered, check_out, check_route, control_plane, \
+    ep_case, log, make_ctx, poison_
 
 pytestmark = pytest.mark.gpu
 
@@ -125,4 +126,42 @@ def test_topk_duplicate_local_expert_rejected(name, flags):
     st = ctx.stats()
     assert st.error_code == fg.EPROTOCOL, (st.error_code, hex(st.error_id))
     assert (st.error_id & 0x7F000000) == 0x48000000 and (st.error_id & 0xFFFFFF) == 1, hex(st.error_id)
+    ctx.close()
+
+
+def test_topk_route_changes_on_one_context():
+    """One context, a new top-k routing of the same tokens on every call (three
+    routings drawn from different seeds, in the order 1 2 3 1 3 2, the layout
+    path alternating): each call's route tables, combine tables, gathered rows
+    and output must be the oracle's for its own routing, with one publisher per
+    chunk per call."""
+    S, T, K, N, E, KK, L = 4, 300, 256, 256, 32, 4, 8
+    log(f"top-k route changes on one context: {S} x {T} tokens, top-{KK} of {E}, {L} local, routings 1 2 3 1 3 2")
+    base = ep_case(1190, S, T, K, N, n_experts=E, topk=KK, n_local=L)
+    cases = {1: base}
+    for i, seed in ((2, 1191), (3, 1192)):
+        tk = W.ep_inputs(seed, n_shards=S, tokens=T, K=K, N=N, n_experts=E, topk=KK, n_local=L).topk
+        lay = O.layout_topk(tk.numpy(), 0, L)
+        tk_dev = tk.to(DEV).contiguous()
+        cases[i] = Case("ep", base.shards_cpu, base.w_cpu, lay, fg.route_topk(tk_dev, T, 0), L, base.sigma_x,
+                        base.sigma_w, T, topk=tk_dev, expert_base=0)
+    max_rows = max(int(c.lay.stream_len.max()) for c in cases.values())
+    ctx = make_ctx(base, max_rows=max(max_rows, T))
+    g, o = buffers(ctx, base)
+    expected = 0
+    for t, i in enumerate((1, 2, 3, 1, 3, 2)):
+        case = cases[i]
+        name, flags = PATHS[t % len(PATHS)]
+        poison_(g)
+        poison_(o)
+        rc = ctx.gather_gemm(case.shards, case.w, g, o, route=case.route, flags=flags | fg.CALL_VERIFY)
+        assert rc == fg.OK, (i, name, fg.strerror(rc))
+        torch.cuda.synchronize()
+        st = ctx.stats()
+        assert st.error_code == 0, (i, name, st.error_code, hex(st.error_id))
+        _check_tables(ctx, case, case.topk.cpu().numpy())
+        check_gathered(case, g, poisoned=True)
+        check_out(case, o)
+        expected += O.signal_counts(case.lay)["publishes"]
+        assert st.publishes == expected == st.expected_publishes, (i, name)
     ctx.close()
