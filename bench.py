@@ -675,7 +675,7 @@ def main():
         result["overlap"] = ov
         result["publish_observe"] = observe_latency(ctx, b.step, fg, torch)
         log("bench: copy-workgroup sweep")
-        result["n_comm_sweep"] = n_comm_sweep(b, ov["T_comp_alone_us"], [16, 32, 64, 128, 192, 224], torch, fg)
+        result["n_comm_sweep"] = n_comm_sweep(b, ov["T_comp_alone_us"], [8, 16, 32, 64, 128, 192, 224], torch, fg)
         result["other_copy_mode"] = other_copy_mode(b, ov["T_comp_alone_us"], 1 - args.copy_mode, torch, fg)
     if not args.no_extras and args.mode == "fused" and not args.no_secondary:
         others = {}
