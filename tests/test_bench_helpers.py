@@ -66,3 +66,15 @@ def test_committed_traffic_record_matches_the_sources():
     assert rec["source_sha256"] == bench.kernel_source_hash()
     for w in ("large", "tp"):
         assert rec["workloads"][w]["hbm_bytes_per_launch"] > 0
+
+
+def test_more_than_one_gpu_is_refused():
+    """`bench.py --gpus N` with N > 1 (or a multi-rank launch) exits with a
+    message before it touches a GPU: the path runs on one GPU."""
+    import subprocess
+    import sys
+    for argv, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "8"})):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv], capture_output=True, text=True,
+                           env={**os.environ, **env}, timeout=120)
+        assert r.returncode == 2, (argv, env, r.returncode, r.stderr)
+        assert "one GPU" in r.stderr and r.stdout == ""
