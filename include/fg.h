@@ -269,8 +269,12 @@ fg_status fg_init(const fg_config* cfg, int hip_device, fg_ctx** out);
  *   gathered: device bf16 [m_pad_cap][K] (written; padding rows never written)
  *   out:      device bf16 [m_pad_cap][N]
  *   flags:    FG_CALL_* / FG_FAULT_*
- * Errors: FG_EINVAL (shapes, NULLs, stream), FG_ESTATE, FG_ETIMEOUT /
- * FG_EPROTOCOL from an earlier call, FG_EHIP. */
+ * Every device row buffer (shards, W, gathered, out, and the staging and ring
+ * buffers of the variants below) starts on a 16-byte boundary: rows move in
+ * 16-byte vectors.
+ * Errors: FG_EINVAL (shapes, NULLs, misaligned buffers, stream; the context is
+ * unchanged), FG_ESTATE, FG_ETIMEOUT / FG_EPROTOCOL from an earlier call,
+ * FG_EHIP. */
 fg_status fg_gather_gemm(fg_ctx* ctx, const void* const* shards, const fg_route* route,
                          const void* W, void* gathered, void* out, uint32_t flags,
                          hipStream_t stream);
@@ -371,8 +375,9 @@ fg_status fg_stress(fg_ctx* ctx, const int32_t* chunk_rows, const int32_t* delay
  *            waits), FG_CALL_VERIFY (publisher counts, polls), FG_CALL_STRICT,
  *            FG_FAULT_DROP_PUBLISH (publisher of chunk (0,0) skips its slot
  *            store: the waits on it time out -> FG_ETIMEOUT)
- * Errors: FG_EINVAL (route, NULLs, stream), FG_ESTATE, FG_ETIMEOUT /
- * FG_EPROTOCOL from an earlier call, FG_EHIP. */
+ * out, staging and y start on 16-byte boundaries, weights on a 4-byte one.
+ * Errors: FG_EINVAL (route, NULLs, misaligned buffers, stream), FG_ESTATE,
+ * FG_ETIMEOUT / FG_EPROTOCOL from an earlier call, FG_EHIP. */
 fg_status fg_combine(fg_ctx* ctx, const void* out, const float* weights, void* const* staging,
                      void* const* y, uint32_t flags, hipStream_t stream);
 

@@ -133,6 +133,11 @@ static int m_pad_capacity(const fg_config& c) {
   return (int)cap;
 }
 
+// Row data moves in 16-byte vectors (buffer loads and stores of four dwords,
+// global -> LDS loads of 16 bytes per lane), so every row buffer must start on
+// a 16-byte boundary; rows are K * 2 or N * 2 bytes apart, multiples of 256.
+static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 static bool config_ok(const fg_config* c) {
   if (!c) return false;
   if (c->n_shards < 1 || c->n_shards > FG_MAX_SHARDS) return false;
@@ -482,7 +487,10 @@ static fg_status gather_gemm_impl(fg_ctx* ctx, const void* const* shards, const 
   if (s != FG_OK) return s;
   const fg_config& c = ctx->cfg;
   if (!shards || !W || !gathered || !out) return FG_EINVAL;
-  for (int i = 0; i < c.n_shards; ++i) if (!shards[i]) return FG_EINVAL;
+  if (!al16(W) || !al16(gathered) || !al16(out) || !al16(rc.ring)) return FG_EINVAL;
+  for (int i = 0; i < c.n_shards; ++i) if (!shards[i] || !al16(shards[i])) return FG_EINVAL;
+  if (staging)
+    for (int i = 0; i < c.n_shards; ++i) if (!al16(staging[i])) return FG_EINVAL;
   if ((flags & FG_CALL_COMM_ONLY) && (flags & FG_CALL_GEMM_ONLY)) return FG_EINVAL;
   const int mode = route ? route->mode : FG_ROUTE_CONTIG;
   // watermark gating needs the contiguous layout and the one-stage copy (whose slots cover the rows)
@@ -736,7 +744,9 @@ fg_status fg_combine(fg_ctx* ctx, const void* out, const float* weights, void* c
   if (s != FG_OK) return s;
   const fg_config& c = ctx->cfg;
   if (!out || !weights || !staging || !y) return FG_EINVAL;
-  for (int i = 0; i < c.n_shards; ++i) if (!staging[i] || !y[i]) return FG_EINVAL;
+  if (!al16(out) || ((uintptr_t)weights & 3)) return FG_EINVAL;
+  for (int i = 0; i < c.n_shards; ++i)
+    if (!staging[i] || !y[i] || !al16(staging[i]) || !al16(y[i])) return FG_EINVAL;
   if ((flags & FG_CALL_COMM_ONLY) && (flags & FG_CALL_GEMM_ONLY)) return FG_EINVAL;
   if (ctx->route_cached_mode != FG_ROUTE_TOPK || ctx->topk_rows < 1) return FG_EINVAL;
   if (bind_stream(ctx, stream) != FG_OK) return FG_EINVAL;

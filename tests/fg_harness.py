@@ -25,6 +25,17 @@ def bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def misaligned_like(t: torch.Tensor, shift_bytes: int = 2) -> torch.Tensor:
+    """A copy of t whose first element sits shift_bytes past a 16-byte boundary."""
+    es = t.element_size()
+    assert shift_bytes % es == 0
+    flat = torch.empty(t.numel() + 16 // es, dtype=t.dtype, device=t.device)
+    view = flat[shift_bytes // es:shift_bytes // es + t.numel()].view(t.shape)
+    view.copy_(t)
+    assert view.data_ptr() % 16 == shift_bytes
+    return view
+
+
 def poison_(t: torch.Tensor) -> None:
     t.view(torch.int16).fill_(POISON)
 

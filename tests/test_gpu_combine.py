@@ -12,7 +12,7 @@ import torch
 import oracle as O
 from sync_protocols_amd import fg
 from sync_protocols_amd import workloads as W
-from fg_harness import DEV, Case, bits, buffers, ep_case, log, make_ctx, poison_
+from fg_harness import DEV, Case, bits, buffers, ep_case, log, make_ctx, misaligned_like, poison_
 
 pytestmark = pytest.mark.gpu
 
@@ -334,3 +334,24 @@ def test_combine_random_configuration(seed):
         r.combine(seed * 10 + t, flags=fg.CALL_VERIFY)
     r.check_plane(2, verify_iters=2)
     r.close()
+
+
+def test_combine_misaligned_buffers_rejected():
+    """The combine's expert outputs, staging and result rows start on 16-byte
+    boundaries and its gate weights on 4-byte ones; otherwise FG_EINVAL, and a
+    valid combine on the same context still matches the oracle."""
+    log("combine: misaligned buffers -> FG_EINVAL, then a valid call")
+    case = ep_case(2014, 4, 160, 128, 256, n_experts=16, topk=4, n_local=4)
+    r = CombineRun(case)
+    r.dispatch()
+    wd = torch.rand(r.S, r.T, r.KK, device=DEV)
+    ctx = r.ctx
+    assert ctx.combine(misaligned_like(r.out), wd, r.staging, r.y) == fg.EINVAL
+    assert ctx.combine(r.out, wd, [r.staging[0], misaligned_like(r.staging[1])] + r.staging[2:], r.y) == fg.EINVAL
+    assert ctx.combine(r.out, wd, r.staging, r.y[:3] + [misaligned_like(r.y[3], 8)]) == fg.EINVAL
+    flat = torch.empty(wd.numel() + 1, dtype=torch.uint8, device=DEV)
+    assert ctx.combine(r.out, flat[1:], r.staging, r.y) == fg.EINVAL     # weights 1 byte past a boundary
+    torch.cuda.synchronize()
+    assert ctx.stats().error_code == 0
+    r.combine(2015)
+    ctx.close()

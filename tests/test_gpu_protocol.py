@@ -8,7 +8,7 @@ import torch
 import oracle as O
 from sync_protocols_amd import fg
 from sync_protocols_amd import workloads as W
-from fg_harness import DEV, buffers, dense_case, log, make_ctx
+from fg_harness import DEV, buffers, check_out, dense_case, log, make_ctx, misaligned_like
 
 pytestmark = pytest.mark.gpu
 
@@ -210,4 +210,35 @@ def test_litmus_device_scope_loads_see_signalled_data():
     assert st2.error_code == 0
     assert st2.litmus_stale == st1.litmus_stale, "plain loads after the acquire fence returned stale words"
     assert ctx.litmus(0, 0) == fg.EINVAL and ctx.litmus(10, 3) == fg.EINVAL
+    ctx.close()
+
+
+def test_misaligned_buffers_rejected():
+    """Row buffers must start on 16-byte boundaries (rows move in 16-byte
+    vectors): a shard, the weights, the gathered or output buffer, a staging
+    buffer or a ring 2 bytes past one gives FG_EINVAL before anything is
+    launched, and the context then runs a valid call as before."""
+    log("misaligned row buffers -> FG_EINVAL; the context stays usable")
+    case = dense_case(45, 2, 128, 256, 256)
+    ctx = make_ctx(case)
+    g, o = buffers(ctx, case)
+    mis_shards = [case.shards[0], misaligned_like(case.shards[1])]
+    assert ctx.gather_gemm(mis_shards, case.w, g, o, route=case.route) == fg.EINVAL
+    assert ctx.gather_gemm(case.shards, misaligned_like(case.w), g, o, route=case.route) == fg.EINVAL
+    assert ctx.gather_gemm(case.shards, case.w, misaligned_like(g), o, route=case.route) == fg.EINVAL
+    assert ctx.gather_gemm(case.shards, case.w, g, misaligned_like(o, 8), route=case.route) == fg.EINVAL
+    staging = [torch.empty(128, case.K, dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    staging[1] = misaligned_like(staging[1], 4)
+    assert ctx.gather_gemm_staged(case.shards, case.w, staging, g, o, self_shard=0, route=case.route) == fg.EINVAL
+    assert ctx.views().ring_cap >= 2       # so the ring call below fails on the alignment alone
+    ring = torch.empty(fg.ring_bytes(ctx.cfg, 1, 2) + 16, dtype=torch.uint8, device=DEV)[2:]
+    assert ctx.gather_gemm_ring(case.shards, case.w, ring, g, o, n_channels=1, ring_chunks=2,
+                                route=case.route) == fg.EINVAL
+    torch.cuda.synchronize()
+    assert ctx.stats().error_code == 0
+    assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route, flags=fg.CALL_VERIFY) == fg.OK
+    torch.cuda.synchronize()
+    st = ctx.stats()
+    assert st.error_code == 0 and st.publishes == st.expected_publishes
+    check_out(case, o)
     ctx.close()
