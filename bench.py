@@ -140,6 +140,18 @@ def setup_workload(name, torch, fg, W):
                 max_rows=max_rows, K=K, N=N, S=S, info=info, inputs=inputs, iters=c["iters"], cfg=c)
 
 
+def _cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The oracle as it stands, on the host cores, over a bounded sample of the
     workload: whole steps (layout, gather of every row, float64 contraction of
@@ -210,6 +222,7 @@ def cpu_baseline(wl, budget_s=12.0):
     flop = 2.0 * done_rows * K * N
     what = "every real row" if rows is None else f"the first {rows} real rows"
     return dict(value=round(flop / dt / 1e12, 6), unit="TFLOP/s", cores=int(cores), kind="oracle",
+                host_threads=os.cpu_count() or 0, cpu_model=_cpu_model(),
                 sample=f"{steps} whole step(s) of the oracle (layout, gather of all rows, float64 contraction of "
                        f"{what} x K={K} x N={N}) in {dt:.1f} s; value = contraction FLOP / wall time")
 
