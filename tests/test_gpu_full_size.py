@@ -35,8 +35,8 @@ from fg_harness import (DEV, POISON, bits, buffers, check_control_plane, check_o
 pytestmark = pytest.mark.gpu
 
 
-def _full_size(case, iters, label):
-    ctx = make_ctx(case)
+def _full_size(case, iters, label, copy_mode=fg.COPY_WORKGROUPS):
+    ctx = make_ctx(case, copy_mode=copy_mode)
     gathered, out = buffers(ctx, case)
     lay = case.lay
     m_pad, S = lay.m_pad, lay.n_shards
@@ -94,7 +94,9 @@ def _full_size(case, iters, label):
     assert torch.equal(out[:m_pad].view(torch.int16), ref), f"{label}: strict fences changed the output bits"
     check_control_plane(case, control_plane(ctx, S), iters + 1, iters + 1)
     log(f"{label}: {iters} calls + 1 strict call bit-identical, control plane exact after each")
+    st = ctx.stats()
     ctx.close()
+    return st, ref
 
 
 def test_tp_full_size_every_call():
@@ -116,3 +118,29 @@ def test_large_full_size_every_call():
     log(f"Large: 8 x 4096 rows permuted, K=N=8192, {c['iters']} calls")
     case = dense_case(c["seed"], c["n_shards"], c["rows"], c["K"], c["N"], gather="permutation")
     _full_size(case, c["iters"], "large")
+
+
+@pytest.mark.parametrize("name", ["tp", "large"])
+def test_in_tile_copy_full_size_every_call(name):
+    """The in-tile copy mode (the compute tiles copy the rows of later rounds
+    inside their K loops) at the full TP and Large sizes over the configured
+    call counts, checked after every call as above; with no split tail the
+    output bits must also equal those of the copy-workgroup mode (the same
+    tiles sum in the same order)."""
+    c = W.CONFIGS[name]
+    gather = "permutation" if name == "large" else "contiguous"
+    log(f"{name}, in-tile copy: {c['n_shards']} x {c['rows']} rows ({gather}), K={c['K']}, N={c['N']}, "
+        f"{c['iters']} calls")
+    case = dense_case(c["seed"], c["n_shards"], c["rows"], c["K"], c["N"], gather=gather)
+    st, bits_tiles = _full_size(case, c["iters"], f"{name}/in-tile", copy_mode=fg.COPY_IN_TILES)
+    assert st.copy_in_tiles == 1 and st.lead_rows > 0, (st.copy_in_tiles, st.lead_rows)
+    ctx = make_ctx(case, copy_mode=fg.COPY_WORKGROUPS)
+    gathered, out = buffers(ctx, case)
+    assert ctx.gather_gemm(case.shards, case.w, gathered, out, route=case.route) == fg.OK
+    torch.cuda.synchronize()
+    st2 = ctx.stats()
+    assert st2.error_code == 0 and st2.copy_in_tiles == 0
+    if st.tiles_split == 0 and st2.tiles_split == 0:
+        assert torch.equal(out[:case.lay.m_pad].view(torch.int16), bits_tiles), \
+            f"{name}: in-tile copy and copy workgroups give different output bits"
+    ctx.close()
