@@ -225,6 +225,48 @@ def check_control_plane(case: Case, cp, t: int, verify_iters: int | None) -> Non
         assert np.array_equal(cp["pub_count"], exp_pub), "one publisher per chunk per iteration"
 
 
+class EveryCallCheck:
+    """Checks after every call of a full-size run, on the device: the gathered
+    real rows equal the oracle's gather bit for bit and the padding rows still
+    hold the poison; the output bits equal the first call's (the summation
+    order does not depend on which workgroup runs which item); every output
+    element is compared with the fp64 oracle product (computed once) on the
+    first call and on the call numbered `last`."""
+
+    def __init__(self, case: Case, last: int, label: str):
+        real = O.real_rows(case.lay)
+        self.case, self.last, self.label = case, last, label
+        self.real_idx = torch.from_numpy(np.nonzero(real)[0]).to(DEV)
+        self.pad_idx = torch.from_numpy(np.nonzero(~real)[0]).to(DEV)
+        self.G = torch.from_numpy(case.oracle_G.view(np.int16)).to(DEV)
+        self.C64 = None
+        self.ref = None
+        self.calls = 0
+
+    def __call__(self, gathered: torch.Tensor, out: torch.Tensor) -> None:
+        case, m_pad = self.case, self.case.lay.m_pad
+        self.calls += 1
+        t = self.calls
+        g = gathered[:m_pad].view(torch.int16)
+        assert torch.equal(g.index_select(0, self.real_idx), self.G.index_select(0, self.real_idx)), \
+            f"{self.label} call {t}: gathered rows differ from the oracle"
+        if self.pad_idx.numel():
+            assert bool((g.index_select(0, self.pad_idx) == POISON).all()), f"{self.label} call {t}: padding written"
+        o = out[:m_pad].view(torch.int16)
+        if t == 1 or t == self.last:
+            if self.C64 is None:
+                wb = bits(case.w_cpu)
+                self.C64 = O.gemm(case.oracle_G, wb if wb.ndim == 3 else wb[None], case.lay)
+            real = O.real_rows(case.lay)
+            r = O.gemm_check(bits(out[:m_pad]), self.C64, case.K, case.sigma_x, case.sigma_w,
+                             np.repeat(real[:, None], case.N, 1))
+            assert r["ok"], (self.label, t, r)
+        if self.ref is None:
+            self.ref = o.clone()
+        else:
+            assert torch.equal(o, self.ref), f"{self.label} call {t}: output bits differ from call 1"
+
+
 def check_gathered(case: Case, gathered: torch.Tensor, poisoned: bool) -> None:
     lay = case.lay
     G = bits(gathered[:lay.m_pad])

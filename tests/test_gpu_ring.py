@@ -8,8 +8,8 @@ import torch
 import oracle as O
 from sync_protocols_amd import fg
 from sync_protocols_amd import workloads as W
-from fg_harness import (DEV, bits, buffers, check_gathered, check_out, check_route, control_plane, dense_case,
-                        ep_case, log, make_ctx, poison_)
+from fg_harness import (DEV, EveryCallCheck, bits, buffers, check_gathered, check_out, check_route, control_plane,
+                        dense_case, ep_case, log, make_ctx, poison_)
 
 pytestmark = pytest.mark.gpu
 
@@ -24,7 +24,8 @@ def _ring_state(ctx, rings):
     return t[:, :rings, 0].copy(), h[:, :rings, 0].copy()
 
 
-def _run(case, iters, *, n_channels, ring_chunks, self_shard=-1, flags=0, ctx_kw=None, sample_rows=None):
+def _run(case, iters, *, n_channels, ring_chunks, self_shard=-1, flags=0, ctx_kw=None, sample_rows=None,
+         per_call=None):
     ctx = make_ctx(case, **(ctx_kw or {}))
     gathered, out = buffers(ctx, case)
     nbytes = fg.ring_bytes(ctx.cfg, n_channels, ring_chunks)
@@ -36,6 +37,10 @@ def _run(case, iters, *, n_channels, ring_chunks, self_shard=-1, flags=0, ctx_kw
         rc = ctx.gather_gemm_ring(case.shards, case.w, ring, gathered, out, n_channels=n_channels,
                                   ring_chunks=ring_chunks, self_shard=self_shard, route=case.route, flags=flags)
         assert rc == fg.OK, fg.strerror(rc)
+        if per_call is not None:
+            torch.cuda.synchronize()
+            assert ctx.stats().error_code == 0, t
+            per_call(gathered, out)
     torch.cuda.synchronize()
     st = ctx.stats()
     assert st.error_code == 0, (st.error_code, hex(st.error_id))
@@ -88,11 +93,12 @@ def test_ring_strict_fences():
 
 
 def test_ring_tp_full_size():
-    log("ring at the TP size: 4 x 2048 rows, K=N=4096, 8 rings per shard of 2 slots (1/4 of the streams), "
-        "self shard 0, 3 calls; every output element")
     c = W.CONFIGS["tp"]
+    log(f"ring at the TP size: 4 x 2048 rows, K=N=4096, 8 rings per shard of 2 slots (1/4 of the streams), "
+        f"self shard 0, {c['iters']} calls, each checked")
     case = dense_case(c["seed"], c["n_shards"], c["rows"], c["K"], c["N"])
-    _run(case, 3, n_channels=8, ring_chunks=2, self_shard=0)
+    _run(case, c["iters"], n_channels=8, ring_chunks=2, self_shard=0,
+         per_call=EveryCallCheck(case, c["iters"], "tp/ring"))
 
 
 def test_ring_arguments():

@@ -8,8 +8,8 @@ import torch
 import oracle as O
 from sync_protocols_amd import fg
 from sync_protocols_amd import workloads as W
-from fg_harness import (DEV, POISON, bits, buffers, check_gathered, check_out, check_route, control_plane,
-                        dense_case, ep_case, log, make_ctx, poison_)
+from fg_harness import (DEV, POISON, EveryCallCheck, bits, buffers, check_gathered, check_out, check_route,
+                        control_plane, dense_case, ep_case, log, make_ctx, poison_)
 
 pytestmark = pytest.mark.gpu
 
@@ -20,7 +20,7 @@ def _staging(ctx, case, self_shard):
             for s in range(len(case.shards))]
 
 
-def _run(case, iters, *, self_shard=-1, flags=0, ctx_kw=None, sample_rows=None):
+def _run(case, iters, *, self_shard=-1, flags=0, ctx_kw=None, sample_rows=None, per_call=None):
     ctx = make_ctx(case, **(ctx_kw or {}))
     gathered, out = buffers(ctx, case)
     staging = _staging(ctx, case, self_shard)
@@ -33,6 +33,10 @@ def _run(case, iters, *, self_shard=-1, flags=0, ctx_kw=None, sample_rows=None):
         rc = ctx.gather_gemm_staged(case.shards, case.w, staging, gathered, out, self_shard=self_shard,
                                     route=case.route, flags=flags | fg.CALL_VERIFY)
         assert rc == fg.OK, fg.strerror(rc)
+        if per_call is not None:
+            torch.cuda.synchronize()
+            assert ctx.stats().error_code == 0, t
+            per_call(gathered, out)
     torch.cuda.synchronize()
     st = ctx.stats()
     assert st.error_code == 0, (st.error_code, hex(st.error_id))
@@ -111,10 +115,10 @@ def test_two_stage_comm_only_then_gemm_only():
 
 
 def test_two_stage_tp_full_size():
-    log("two-stage at the TP size: 4 x 2048 rows, K=N=4096, self shard 0, 3 calls; every output element")
     c = W.CONFIGS["tp"]
+    log(f"two-stage at the TP size: 4 x 2048 rows, K=N=4096, self shard 0, {c['iters']} calls, each checked")
     case = dense_case(c["seed"], c["n_shards"], c["rows"], c["K"], c["N"])
-    _run(case, 3, self_shard=0)
+    _run(case, c["iters"], self_shard=0, per_call=EveryCallCheck(case, c["iters"], "tp/two-stage"))
 
 
 def test_two_stage_dropped_watermark_times_out():
