@@ -266,15 +266,20 @@ def test_combine_is_deterministic():
 
 
 def test_combine_full_ep_size():
-    log("combine at the EP workload size: 8 x 1024 tokens, top-8 of 64, 8 local, N=2048, every element")
+    """The configured EP call count, each call on new expert outputs and gate
+    weights: its staging rows bit-exact and every y element within the
+    tolerance (exact zero rows for tokens with no local pick); the combine
+    slots, election counts and publisher counts exact after the last."""
     c = W.CONFIGS["ep"]
+    log(f"combine at the EP workload size: 8 x 1024 tokens, top-8 of 64, 8 local, N=2048, {c['iters']} calls, "
+        f"every element of each")
     case = ep_case(c["seed"], c["n_shards"], c["tokens"], c["K"], c["N"], n_experts=c["n_experts"],
                    topk=c["topk"], n_local=c["n_local"], expert_base=c["expert_base"])
     r = CombineRun(case)
     r.dispatch()
-    for t in range(2):
+    for t in range(c["iters"]):
         r.combine(3700 + t, flags=fg.CALL_VERIFY)
-    r.check_plane(2, verify_iters=2)
+    r.check_plane(c["iters"], verify_iters=c["iters"])
     r.close()
 
 
