@@ -51,6 +51,14 @@ def test_noalloc_two_calls_second_smaller():
     _both(dense_case(502, 3, 100, 256, 256, gather="permutation"), "call 2 (3 x 100, K=256, N=256)")
 
 
+def test_noalloc_at_the_largest_documented_size():
+    """The size its scratch array is sized for: 8 shards x 4096 rows gathered by
+    a permutation, K = N = 8192; bit for bit as the context call, and every
+    output element against the oracle."""
+    log("no-alloc at 8 x 4096 rows permuted, K=N=8192")
+    _both(dense_case(504, 8, 4096, 8192, 8192, gather="permutation"), "8 x 4096, K=N=8192")
+
+
 def test_noalloc_rejects_what_it_cannot_hold():
     log("no-alloc: a control plane beyond the scratch size, bad flags and NULLs are refused before any launch")
     case = dense_case(503, 2, 128, 256, 256)
