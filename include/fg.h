@@ -34,6 +34,14 @@
  *   - A context is bound to the first stream it is used with; work on a
  *     different stream returns FG_EINVAL (the parity re-arming of the control
  *     plane relies on stream order between consecutive calls).
+ *   - The gather-GEMM and combine kernels are persistent grids sized to be
+ *     resident all at once, whose workgroups wait for one another ("PCIe sync
+ *     protocols" §6 audit). Two such kernels must not run at the same time on
+ *     one GPU: contexts used on different streams, or other long kernels
+ *     running concurrently, can keep part of a grid from starting. The waits
+ *     then end at the context's watchdog (timeout_ns) with FG_ETIMEOUT rather
+ *     than hanging. Contexts that share one stream run one after another and
+ *     are safe.
  */
 #ifndef FG_H
 #define FG_H

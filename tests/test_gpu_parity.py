@@ -250,3 +250,37 @@ def test_route_changes_on_one_context():
         expected += O.signal_counts(case.lay)["publishes"]
         assert st.publishes == expected == st.expected_publishes, name
     ctx.close()
+
+
+def test_two_contexts_share_one_stream():
+    """Two contexts of different shapes used alternately on one stream (A B A B
+    A B): each call matches the oracle for its own context and inputs, and each
+    context's control plane stays exact (its sequence runs on its own)."""
+    log("two contexts on one stream, alternating calls")
+    ca = dense_case(4301, 4, 300, 512, 256, gather="permutation")
+    cb = dense_case(4302, 2, 640, 256, 512)
+    xa, xb = make_ctx(ca), make_ctx(cb)
+    ga, oa = buffers(xa, ca)
+    gb, ob = buffers(xb, cb)
+    ta = tb = 0
+    for i in range(6):
+        case, ctx, g, o = (ca, xa, ga, oa) if i % 2 == 0 else (cb, xb, gb, ob)
+        poison_(g)
+        poison_(o)
+        assert ctx.gather_gemm(case.shards, case.w, g, o, route=case.route, flags=fg.CALL_VERIFY) == fg.OK
+        torch.cuda.synchronize()
+        st = ctx.stats()
+        assert st.error_code == 0, (i, st.error_code, hex(st.error_id))
+        if i % 2 == 0:
+            ta += 1
+            t = ta
+        else:
+            tb += 1
+            t = tb
+        cp = control_plane(ctx, len(case.shards))
+        check_route(case, cp)
+        check_control_plane(case, cp, t, t)
+        check_gathered(case, g, poisoned=True)
+        check_out(case, o)
+    xa.close()
+    xb.close()
