@@ -14,7 +14,8 @@ measurement method ("Know your platform" §5: T_comp alone with the same
 workgroups, T_comm alone, T_total), overlap efficiency and compute
 interference, the gather's HBM rate, a sweep of the copy-workgroup count
 ("Know your platform" §4), the publish-to-gate-observe latency from a traced
-call, the same fields for the TP share and the EP dispatch workloads,
+call, the same fields for the TP share and the EP dispatch workloads, the board
+power of each mode with the bound a power cap puts on overlap efficiency,
 slot-signal latency (ping-pong round trip, slot barrier), the protocol-stress
 signal rate, the two-stage, ring and combine entry points, the roofline of the
 fused kernel and the CPU oracle timed on a bounded sample on the host cores.
@@ -557,6 +558,92 @@ def other_copy_mode(b, t_comp_us, mode, torch, fg):
             "T_total_over_T_comp": round(t / t_comp_us, 4)}
 
 
+def _power_files():
+    """The board power sensor (microwatts) and the board's power cap, from the
+    GPU's hwmon node in sysfs; None where the node is missing or unreadable."""
+    import glob
+    for d in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*")):
+        inp, cap = os.path.join(d, "power1_input"), os.path.join(d, "power1_cap")
+        if not os.path.exists(inp):
+            inp = os.path.join(d, "power1_average")
+        try:
+            int(open(inp).read().strip())
+            c = int(open(cap).read().strip()) if os.path.exists(cap) else 0
+        except (OSError, ValueError):
+            continue
+        return inp, c
+    return None
+
+
+def power_fields(ctx, step, step_us, fg, torch, secs=1.5):
+    """Board power while GEMM-only, copy-only and fused steps run back to back
+    (about `secs` each; the power sensor, sampled every 5 ms from a host thread,
+    averages over a window, so the first third of each run is dropped), and the
+    bound that a fixed power cap puts on overlap efficiency.
+
+    Under full MFMA load the part runs at its power cap, so the copy's energy
+    comes out of the same budget as the contraction's: the fused step cannot
+    take less than T_comp + E_copy / P_cap, where E_copy is the energy the copy
+    adds. Counted from the idle board (its incremental energy, (P_copy -
+    P_idle) x T_comm) this bounds overlap efficiency by 1 - (P_copy - P_idle) /
+    P_cap; counted whole (P_copy x T_comm) by 1 - P_copy / P_cap. The first
+    reading ignores the static power that a busy part spends beyond idle, the
+    second counts all of it, so the bound lies between the two."""
+    import threading
+    pf = _power_files()
+    if pf is None:
+        return None
+    path, cap_uw = pf
+
+    def sample(stop, out):
+        while not stop.is_set():
+            try:
+                out.append(int(open(path).read().strip()))
+            except (OSError, ValueError):
+                pass
+            time.sleep(0.005)
+
+    torch.cuda.synchronize()
+    time.sleep(1.0)
+    idle = []
+    stop = threading.Event()
+    th = threading.Thread(target=sample, args=(stop, idle))
+    th.start()
+    time.sleep(0.3)
+    stop.set()
+    th.join()
+    res = {"sensor": path, "cap_W": round(cap_uw / 1e6, 1), "idle_W": round(statistics.median(idle) / 1e6, 1)}
+    for mode, flags in (("gemm_only", fg.CALL_GEMM_ONLY), ("comm_only", fg.CALL_COMM_ONLY), ("fused", 0)):
+        n = max(20, int(secs * 1e6 / step_us[mode]))
+        samples = []
+        stop = threading.Event()
+        th = threading.Thread(target=sample, args=(stop, samples))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        th.start()
+        e0.record()
+        for _ in range(n):
+            step(flags)
+        e1.record()
+        e1.synchronize()
+        stop.set()
+        th.join()
+        us = e0.elapsed_time(e1) * 1000.0 / n
+        w = statistics.mean(samples[len(samples) // 3:]) / 1e6 if len(samples) >= 6 else float("nan")
+        st = ctx.stats()
+        res[mode] = {"W": round(w, 1), "us_per_step": round(us, 2), "mJ_per_step": round(w * us / 1000.0, 2),
+                     "clock_mhz": round(st.clock_mhz, 0), "samples": len(samples)}
+    step()
+    torch.cuda.synchronize()
+    cap = res["cap_W"] or max(res["gemm_only"]["W"], res["fused"]["W"])
+    pc = res["comm_only"]["W"]
+    tc, tm, tt = res["gemm_only"]["us_per_step"], res["comm_only"]["us_per_step"], res["fused"]["us_per_step"]
+    res["overlap_efficiency_back_to_back"] = round((tc + tm - tt) / min(tc, tm), 4)
+    res["overlap_bound_incremental"] = round(1.0 - (pc - res["idle_W"]) / cap, 4)
+    res["overlap_bound_whole"] = round(1.0 - pc / cap, 4)
+    return res
+
+
 def secondary(name, steps, fg, W, torch):
     """Fused throughput (back-to-back steps after a warm-up), the three timings
     and overlap, and the publish-to-observe latency of another workload."""
@@ -568,6 +655,9 @@ def secondary(name, steps, fg, W, torch):
            "TFLOPs": round(b.flop / (t * 1e-6) / 1e12, 2),
            "frac_bf16_peak": round(b.flop / (t * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     res["overlap"] = overlap_fields(b.ctx, b.step, 10, b.flop, b.gather_bytes, fg, torch)
+    ov = res["overlap"]
+    res["power"] = power_fields(b.ctx, b.step, {"gemm_only": ov["T_comp_alone_us"], "comm_only": ov["T_comm_alone_us"],
+                                                "fused": ov["T_total_us"]}, fg, torch, secs=1.0)
     res["publish_observe"] = observe_latency(b.ctx, b.step, fg, torch)
     b.check()
     return b, res
@@ -686,6 +776,9 @@ def main():
         n_rep = max(10, args.steps)
         ov = overlap_fields(ctx, b.step, n_rep, b.flop, b.gather_bytes, fg, torch)
         result["overlap"] = ov
+        result["power"] = power_fields(ctx, b.step, {"gemm_only": ov["T_comp_alone_us"],
+                                                     "comm_only": ov["T_comm_alone_us"],
+                                                     "fused": ov["T_total_us"]}, fg, torch)
         result["publish_observe"] = observe_latency(ctx, b.step, fg, torch)
         log("bench: copy-workgroup sweep")
         result["n_comm_sweep"] = n_comm_sweep(b, ov["T_comp_alone_us"], [8, 16, 32, 64, 128, 192, 224], torch, fg)
