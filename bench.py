@@ -635,13 +635,20 @@ def power_fields(ctx, step, step_us, fg, torch, secs=1.5):
                      "clock_mhz": round(st.clock_mhz, 0), "samples": len(samples)}
     step()
     torch.cuda.synchronize()
+    res.update(power_bounds(res))
+    return res
+
+
+def power_bounds(res):
+    """Overlap efficiency of the back-to-back timings in `res` and the two
+    readings of its bound under the power cap (see power_fields)."""
     cap = res["cap_W"] or max(res["gemm_only"]["W"], res["fused"]["W"])
     pc = res["comm_only"]["W"]
     tc, tm, tt = res["gemm_only"]["us_per_step"], res["comm_only"]["us_per_step"], res["fused"]["us_per_step"]
-    res["overlap_efficiency_back_to_back"] = round((tc + tm - tt) / min(tc, tm), 4)
-    res["overlap_bound_incremental"] = round(1.0 - (pc - res["idle_W"]) / cap, 4)
-    res["overlap_bound_whole"] = round(1.0 - pc / cap, 4)
-    return res
+    return {"overlap_efficiency_back_to_back": round((tc + tm - tt) / min(tc, tm), 4),
+            "overlap_bound_incremental": round(1.0 - (pc - res["idle_W"]) / cap, 4),
+            "overlap_bound_whole": round(1.0 - pc / cap, 4),
+            "T_total_energy_floor_us": round(tc + pc * tm / cap, 2)}
 
 
 def secondary(name, steps, fg, W, torch):

@@ -1,6 +1,7 @@
 """Host checks of bench.py's bookkeeping (no GPU): the code hash that keys the
 recorded HBM byte counters ignores comments and white space but not code, and
-a counter record taken for other code is not reported."""
+a counter record taken for other code is not reported; the power-cap bound's
+arithmetic, and no power fields without a power sensor."""
 import json
 import os
 import shutil
@@ -78,3 +79,27 @@ def test_more_than_one_gpu_is_refused():
                            env={**os.environ, **env}, timeout=120)
         assert r.returncode == 2, (argv, env, r.returncode, r.stderr)
         assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_power_sensor_absent_gives_no_power_fields(monkeypatch):
+    """Without the board's hwmon node (as on a host with no GPU) the power
+    fields are left out rather than invented."""
+    monkeypatch.setattr("glob.glob", lambda pattern: [])
+    assert bench._power_files() is None
+
+
+def test_power_bound_arithmetic():
+    """The bound under a power cap: with the board at its cap, the fused step
+    takes at least T_comp + P_copy * T_comm / P_cap (the copy's whole energy),
+    so efficiency (T_comp + T_comm - T_total) / T_comm is at most 1 - P_copy /
+    P_cap; counted from the idle board, 1 - (P_copy - P_idle) / P_cap. A fused
+    step exactly at the energy floor reaches the whole-energy bound."""
+    res = {"cap_W": 1400.0, "idle_W": 300.0,
+           "gemm_only": {"W": 1400.0, "us_per_step": 3000.0},
+           "comm_only": {"W": 700.0, "us_per_step": 200.0},
+           "fused": {"W": 1400.0, "us_per_step": 3100.0}}
+    b = bench.power_bounds(res)
+    assert b["overlap_bound_whole"] == 0.5
+    assert abs(b["overlap_bound_incremental"] - (1 - 400 / 1400)) < 1e-4
+    assert b["T_total_energy_floor_us"] == 3100.0
+    assert b["overlap_efficiency_back_to_back"] == 0.5
