@@ -15,7 +15,8 @@ workgroups, T_comm alone, T_total), overlap efficiency and compute
 interference, the gather's HBM rate, a sweep of the copy-workgroup count
 ("Know your platform" §4), the publish-to-gate-observe latency from a traced
 call, the same fields for the TP share and the EP dispatch workloads, the board
-power of each mode with the bound a power cap puts on overlap efficiency,
+power of each mode with the bound a power cap puts on overlap efficiency, the
+vendor library's GEMM (torch.matmul) on the same operands for context,
 slot-signal latency (ping-pong round trip, slot barrier), the protocol-stress
 signal rate, the two-stage, ring and combine entry points, the roofline of the
 fused kernel and the CPU oracle timed on a bounded sample on the host cores.
@@ -639,6 +640,55 @@ def power_fields(ctx, step, step_us, fg, torch, secs=1.5):
     return res
 
 
+def library_gemm_fields(b, fg, torch, rounds=3, n=25, skip=8):
+    """The same contraction by the vendor library (torch.matmul, which PyTorch
+    hands to hipBLASLt) on the same operands: the gathered rows of the last
+    fused step and W as [K][N]. Context for the roofline fraction, timed beside
+    the fused kernel's GEMM-only and fused modes in alternating rounds (each
+    round: n back-to-back launches per variant, per-launch events, the first
+    `skip` dropped; medians over the rounds), plus the largest difference
+    between the two outputs."""
+    wl = b.wl
+    if wl["n_groups"] != 1:
+        return None
+    M = wl["m_real"]
+    A = b.gathered[:M]
+    Wt = wl["w"].reshape(wl["N"], wl["K"]).t().contiguous()   # [K][N], contiguous (no transposed view)
+    out = torch.empty(M, wl["N"], dtype=torch.bfloat16, device="cuda:0")
+    same = fg.CALL_SAME_ROUTE if wl["route"].mode != fg.ROUTE_CONTIG else 0
+
+    def timed(fn):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record()
+        for i in range(n):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(skip, n)]
+
+    variants = {"library": lambda: torch.matmul(A, Wt, out=out),
+                "gemm_only": lambda: b.step(fg.CALL_GEMM_ONLY | same),
+                "fused": lambda: b.step(same)}
+    ts = {k: [] for k in variants}
+    for _ in range(rounds):
+        for k, fn in variants.items():
+            ts[k] += timed(fn)
+    b.step(fg.CALL_GEMM_ONLY | same)
+    variants["library"]()
+    torch.cuda.synchronize()
+    diff = (b.out[:M].float() - out.float()).abs().max().item()
+    b.step()
+    torch.cuda.synchronize()
+    b.check()
+    med = {k: statistics.median(v) for k, v in ts.items()}
+    res = {k + "_us": round(v, 1) for k, v in med.items()}
+    res.update({k + "_TFLOPs": round(b.flop / (v * 1e-6) / 1e12, 1) for k, v in med.items()})
+    res["gemm_only_over_library"] = round(med["library"] / med["gemm_only"], 4)
+    res["fused_over_library"] = round(med["library"] / med["fused"], 4)
+    res["max_abs_diff_gemm_only_vs_library"] = diff
+    return res
+
+
 def power_bounds(res):
     """Overlap efficiency of the back-to-back timings in `res` and the two
     readings of its bound under the power cap (see power_fields)."""
@@ -666,6 +716,9 @@ def secondary(name, steps, fg, W, torch):
     res["power"] = power_fields(b.ctx, b.step, {"gemm_only": ov["T_comp_alone_us"], "comm_only": ov["T_comm_alone_us"],
                                                 "fused": ov["T_total_us"]}, fg, torch, secs=1.0)
     res["publish_observe"] = observe_latency(b.ctx, b.step, fg, torch)
+    lib = library_gemm_fields(b, fg, torch)
+    if lib is not None:
+        res["library_gemm"] = lib
     b.check()
     return b, res
 
@@ -685,8 +738,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="headline workload's fields only (no other workloads, latency, stress or other entry points)")
-    ap.add_argument("--mode", default="fused", choices=["fused", "gemm_only", "comm_only"],
-                    help="timed steps in this mode (profiling runs of the compute or copy role alone)")
+    ap.add_argument("--mode", default="fused", choices=["fused", "gemm_only", "comm_only", "library"],
+                    help="timed steps in this mode (profiling runs of the compute or copy role alone, or of the "
+                         "vendor library's GEMM on the same operands)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of a known size (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -704,6 +758,35 @@ def main():
     log(f"bench: workload {args.workload}, {args.warmup} warmup + {args.steps} timed steps ({args.mode})")
     b = Bench(args.workload, fg, W, torch, n_comm=args.n_comm, tile_n=args.tile_n, copy_mode=args.copy_mode)
     wl, ctx = b.wl, b.ctx
+    if args.mode == "library":
+        # profiling runs only: the same contraction by torch.matmul (hipBLASLt)
+        # on the gathered rows of one fused step and W as [K][N]
+        b.step()
+        M = wl["m_real"]
+        A = b.gathered[:M]
+        Wt = wl["w"].reshape(wl["N"], wl["K"]).t().contiguous()
+        out = torch.empty(M, wl["N"], dtype=torch.bfloat16, device="cuda:0")
+        for _ in range(args.warmup):
+            torch.matmul(A, Wt, out=out)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            torch.matmul(A, Wt, out=out)
+        e1.record()
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / args.steps
+        if args.copy_calibration:
+            src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda:0").fill_(1)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                torch.mul(src, 1.0, out=dst)
+            torch.cuda.synchronize()
+        b.close()
+        print(json.dumps({"mode": "library", "workload": args.workload, "steps": args.steps, "warmup": args.warmup,
+                          "us_per_step": round(us, 2), "TFLOPs": round(b.flop / (us * 1e-6) / 1e12, 1)}), flush=True)
+        return
     mode_flags = {"fused": 0, "gemm_only": fg.CALL_GEMM_ONLY, "comm_only": fg.CALL_COMM_ONLY}[args.mode]
     if mode_flags == fg.CALL_GEMM_ONLY:
         b.step()   # the gathered rows the compute role reads
@@ -787,6 +870,7 @@ def main():
                                                      "comm_only": ov["T_comm_alone_us"],
                                                      "fused": ov["T_total_us"]}, fg, torch)
         result["publish_observe"] = observe_latency(ctx, b.step, fg, torch)
+        result["library_gemm"] = library_gemm_fields(b, fg, torch)
         log("bench: copy-workgroup sweep")
         result["n_comm_sweep"] = n_comm_sweep(b, ov["T_comp_alone_us"], [8, 16, 32, 64, 128, 192, 224], torch, fg)
         result["other_copy_mode"] = other_copy_mode(b, ov["T_comp_alone_us"], 1 - args.copy_mode, torch, fg)

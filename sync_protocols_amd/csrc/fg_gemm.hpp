@@ -6,13 +6,19 @@
 //   W stored as [N][K] (K contiguous), fp32 accumulation, bf16 RNE output.
 //
 // Tile BM x BN, eight waves as 2 x 4 (two per SIMD), each wave (BM/2) x (BN/4) built from
-// v_mfma_f32_32x32x16_bf16 fragments. The weight tile is the MFMA "A" operand
-// and the gathered tile the "B" operand, so that each lane's four consecutive
-// accumulator values are four consecutive output columns of one row; the
-// epilogue (tile_store) regroups them through LDS into 16-byte pieces of whole
-// rows. Lane layout (measured on the part): A/B operand lane l holds row/col
-// l % 32 and k = 8 * (l / 32) + 0..7; result register v of lane l is
-// D[8 * (v / 4) + 4 * (l / 32) + v % 4][l % 32].
+// v_mfma_f32_16x16x32_bf16 fragments (the default), or from
+// v_mfma_f32_32x32x16_bf16 fragments in the build variants below. At the
+// part's power cap a stream of 16x16x32 MFMAs holds a higher clock than the
+// same FLOP in 32x32x16 ones (measured: 1.99 against 1.73 PFLOP/s of MFMA work
+// alone), since each instruction moves fewer accumulator bytes per product.
+// The weight tile is the MFMA "A" operand and the gathered tile the "B"
+// operand, so that each lane's four consecutive accumulator values are four
+// consecutive output columns of one row; the epilogue (tile_store) regroups
+// them through LDS into 16-byte pieces of whole rows. Lane layouts: 32x32x16,
+// operand lane l holds row/col l % 32 and k = 8 * (l / 32) + 0..7, result
+// register v of lane l is D[8 * (v / 4) + 4 * (l / 32) + v % 4][l % 32];
+// 16x16x32, operand lane l holds row/col l % 16 and k = 8 * (l / 16) + 0..7,
+// result register v of lane l is D[4 * (l / 16) + v][l % 16].
 //
 // LDS: two stages; per stage each operand tile is stored as rows of 64 k (one
 // 128-byte line = 8 slots of 16 bytes; full lines keep the L2 request rate at
@@ -20,6 +26,8 @@
 // Global -> LDS moves use buffer_load ... lds (16 bytes per lane, lane i writes
 // base + 16 i), so the swizzle is applied by choosing which chunk a lane fetches.
 #pragma once
+
+#include <type_traits>
 
 #include "fg_sync.hpp"
 
@@ -48,17 +56,24 @@ static_assert(kBK == 64 || kBK == 32, "stage depth");
 #ifndef FG_PINGPONG
 #define FG_PINGPONG 0
 #endif
+#ifndef FG_MFMA16
+#define FG_MFMA16 1
+#endif
 constexpr bool kPingPong = FG_PINGPONG != 0 && FG_WAVES == 8;   // the ping-pong stage schedule below
 constexpr int kWaves = FG_WAVES;    // waves per workgroup: 8 = two per SIMD, so one wave's memory
                                     // instructions issue while the other's MFMAs run; 4 = one per SIMD
                                     // with a 128 x 128 wave tile (fewer LDS reads per MFMA)
+// 16x16x32 MFMAs in the default schedule (64-k stages, eight waves, the
+// interleaved stage schedule); the other variants keep 32x32x16
+constexpr bool kMfma16 = FG_MFMA16 != 0 && FG_BK == 64 && FG_WAVES == 8 && !kPingPong;
 
 template <int BM, int BN>
 struct Tile {
   static constexpr int WGN = kWaves == 8 ? 4 : 2;     // waves along n
   static constexpr int WGM = kWaves / WGN;            // waves along m
   static constexpr int WM = BM / WGM, WN = BN / WGN;  // per-wave tile
-  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int FM = WM / 32, FN = WN / 32;   // 32 x 32 accumulator blocks per wave
+  static constexpr int VW = kMfma16 ? 2 * FM : FM;    // output rows per lane (row version words)
   static constexpr int A_BYTES = BM * kRowB;
   static constexpr int B_BYTES = BN * kRowB;
   static constexpr int STAGE = A_BYTES + B_BYTES;
@@ -107,15 +122,85 @@ __device__ __forceinline__ bf16x8 frag_read(const char* lds, int row, int c) {
   return *reinterpret_cast<const bf16x8*>(lds + row * kRowB + swz(c, row) * 16);
 }
 
+// Accumulators per wave, one 32 x 32 output block per (fm, fn): with 32x32x16
+// MFMAs one f32x16; with 16x16x32 the block's four 16 x 16 quarters, quarter
+// 2 i + j covering output columns 16 i .. 16 i + 15 and rows 16 j .. 16 j + 15
+// of the block.
 template <int BM, int BN>
-struct Acc {
+struct Acc32 {
   f32x16 v[Tile<BM, BN>::FM][Tile<BM, BN>::FN];
 };
+template <int BM, int BN>
+struct Acc16 {
+  f32x4 v[Tile<BM, BN>::FM][Tile<BM, BN>::FN][4];
+};
+template <int BM, int BN>
+using Acc = std::conditional_t<kMfma16, Acc16<BM, BN>, Acc32<BM, BN>>;
+
+// Accumulator group g (0..3) of block (fm, fn): four consecutive output
+// columns of one output row of the block, at row acc_row(g, lane) and first
+// column acc_col(g, lane) of the block.
+__device__ __forceinline__ int acc_row(int g, int lane) { return kMfma16 ? 16 * (g & 1) + (lane & 15) : (lane & 31); }
+__device__ __forceinline__ int acc_col(int g, int lane) {
+  return kMfma16 ? 16 * (g >> 1) + 4 * (lane >> 4) : 8 * g + 4 * (lane >> 5);
+}
+// The row version word (tile_row_versions) of group g of fragment row fm.
+__device__ __forceinline__ int acc_vw(int fm, int g) { return kMfma16 ? 2 * fm + (g & 1) : fm; }
 
 template <int BM, int BN>
-struct Frags {
+__device__ __forceinline__ f32x4 acc_group(const Acc32<BM, BN>& acc, int fm, int fn, int g) {
+  const f32x16& c = acc.v[fm][fn];
+  return f32x4{c[4 * g + 0], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
+}
+template <int BM, int BN>
+__device__ __forceinline__ f32x4 acc_group(const Acc16<BM, BN>& acc, int fm, int fn, int g) {
+  return acc.v[fm][fn][g];
+}
+template <int BM, int BN>
+__device__ __forceinline__ void acc_zero(Acc32<BM, BN>& acc) {
+#pragma unroll
+  for (int i = 0; i < Tile<BM, BN>::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < Tile<BM, BN>::FN; ++j) acc.v[i][j] = f32x16{};
+}
+template <int BM, int BN>
+__device__ __forceinline__ void acc_zero(Acc16<BM, BN>& acc) {
+#pragma unroll
+  for (int i = 0; i < Tile<BM, BN>::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < Tile<BM, BN>::FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc.v[i][j][q] = f32x4{};
+}
+
+// Fragments of one k-step. 32x32x16: the k-step is 16 k of the stage, with
+// the weight fragments b[fn] and the gathered-row fragments a[fm]. 16x16x32:
+// the k-step is half of the MFMAs of one 32-k half of the stage (k-step kk:
+// k half kk / 2, fragment rows fm of half kk % 2); w[2 fn + i] holds weight
+// rows 16 i .. 16 i + 15 of column block fn (read at even k-steps and kept for
+// the odd one), g[2 f + j] rows 16 j .. 16 j + 15 of the half's f-th fragment
+// row.
+template <int BM, int BN>
+struct Frags32 {
   bf16x8 b[Tile<BM, BN>::FN];
   bf16x8 a[Tile<BM, BN>::FM];
+};
+template <int BM, int BN>
+struct Frags16 {
+  bf16x8 w[2 * Tile<BM, BN>::FN];
+  bf16x8 g[Tile<BM, BN>::FM];
+};
+template <int BM, int BN>
+using Frags = std::conditional_t<kMfma16, Frags16<BM, BN>, Frags32<BM, BN>>;
+
+// MFMAs per k-step, and the fragment reads that k-step kk needs.
+template <int BM, int BN>
+struct KStep {
+  using T = Tile<BM, BN>;
+  static constexpr int NM = kMfma16 ? 2 * T::FM * T::FN : T::FM * T::FN;
+  __device__ static constexpr int nr(int kk) {
+    return kMfma16 ? (kk % 2 == 0 ? T::FM + 2 * T::FN : T::FM) : T::FM + T::FN;
+  }
 };
 
 template <int BM, int BN>
@@ -165,22 +250,68 @@ __device__ __forceinline__ void wait_vmcnt() {
 // issued in the shadow of one 32-cycle MFMA: the stage is a fixed sequence of
 // MFMA slots, each followed by at most one memory instruction, fenced so the
 // compiler keeps the order.
-template <int BM, int BN>
+// MFMA i of k-step KK.
+template <int BM, int BN, int KK = 0>
 __device__ __forceinline__ void mfma_one(const Frags<BM, BN>& f, Acc<BM, BN>& acc, int i) {
   using T = Tile<BM, BN>;
-  const int fm = i / T::FN, fn = i % T::FN;
-  acc.v[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc.v[fm][fn], 0, 0, 0);
+  if constexpr (kMfma16) {
+    // i -> (fn, column quarter qi, f, row quarter qj), qj fastest: the MFMAs of
+    // a k-step each update a different accumulator, and each weight fragment
+    // is used by consecutive MFMAs, so that at an odd k-step the weights die
+    // one by one and the next stage's weight fragments, read last, can take
+    // their registers
+    constexpr int H = T::FM / 2;
+    const int qj = i & 1, fl = (i >> 1) % H, qi = (i / (2 * H)) & 1, fn = i / (4 * H);
+    const int fm = (KK & 1) * H + fl;
+    acc.v[fm][fn][2 * qi + qj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.w[2 * fn + qi], f.g[2 * fl + qj],
+                                                                         acc.v[fm][fn][2 * qi + qj], 0, 0, 0);
+  } else {
+    const int fm = i / T::FN, fn = i % T::FN;
+    acc.v[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc.v[fm][fn], 0, 0, 0);
+  }
 }
 
-// Element e of a k-step's fragment set, in the order the MFMAs consume them:
-// b[0..FN), then a[0..FM).
+// Element e of k-step kk's fragment reads: 32x32x16, b[0..FN) then a[0..FM),
+// in the order the MFMAs consume them; 16x16x32, g[0..FM), then at even
+// k-steps w[0..2 FN) (w is carried over to the odd one), read last so that
+// they can reuse the registers of the weights that the MFMAs before them
+// release.
 template <int BM, int BN>
 __device__ __forceinline__ void frag_read_one(const char* ldsA, const char* ldsB, Frags<BM, BN>& f, int kk, int e,
                                               int wm, int wn, int lane) {
   using T = Tile<BM, BN>;
-  const int lr = lane & 31, kh = lane >> 5;
-  if (e < T::FN) f.b[e] = frag_read(ldsB, wn * T::WN + e * 32 + lr, kk * 2 + kh);
-  else f.a[e - T::FN] = frag_read(ldsA, wm * T::WM + (e - T::FN) * 32 + lr, kk * 2 + kh);
+  if constexpr (kMfma16) {
+    const int l16 = lane & 15, c = 4 * (kk >> 1) + (lane >> 4);   // 16-byte chunk of the stage row
+    if (e < T::FM) {
+      const int fm = (kk & 1) * (T::FM / 2) + (e >> 1);
+      f.g[e] = frag_read(ldsA, wm * T::WM + fm * 32 + 16 * (e & 1) + l16, c);
+    } else {
+      const int e2 = e - T::FM;
+      f.w[e2] = frag_read(ldsB, wn * T::WN + (e2 >> 1) * 32 + 16 * (e2 & 1) + l16, c);
+    }
+  } else {
+    const int lr = lane & 31, kh = lane >> 5;
+    if (e < T::FN) f.b[e] = frag_read(ldsB, wn * T::WN + e * 32 + lr, kk * 2 + kh);
+    else f.a[e - T::FN] = frag_read(ldsA, wm * T::WM + (e - T::FN) * 32 + lr, kk * 2 + kh);
+  }
+}
+
+// All of k-step kk's fragment reads.
+template <int BM, int BN>
+__device__ __forceinline__ void frags_read_kstep(const char* ldsA, const char* ldsB, Frags<BM, BN>& f, int kk, int wm,
+                                                 int wn, int lane) {
+#pragma unroll
+  for (int e = 0; e < KStep<BM, BN>::nr(kk); ++e) frag_read_one<BM, BN>(ldsA, ldsB, f, kk, e, wm, wn, lane);
+}
+
+// 16x16x32: the odd k-step of a k half uses the weight fragments read for the
+// even one.
+template <int BM, int BN>
+__device__ __forceinline__ void carry_weights(Frags<BM, BN>& dst, const Frags<BM, BN>& src) {
+  if constexpr (kMfma16) {
+#pragma unroll
+    for (int e = 0; e < 2 * Tile<BM, BN>::FN; ++e) dst.w[e] = src.w[e];
+  }
 }
 
 // Load q (0..LOADS) of this wave's share of a stage; the stage's k offset is
@@ -256,17 +387,19 @@ __device__ __forceinline__ void phase_a(const char* cur, Frags<BM, BN>& f0, Frag
                                         __amdgpu_buffer_rsrc_t rB, uint32_t b_off, uint32_t stride,
                                         uint32_t k1_bytes, char* nxt_w, int wave, Hook& hook, int kst) {
   using T = Tile<BM, BN>;
-  constexpr int NM = T::FM * T::FN;        // MFMAs per k-step
-  constexpr int NR = T::FM + T::FN;        // fragment reads per k-step
+  using KS = KStep<BM, BN>;
+  constexpr int NM = KS::NM;               // MFMAs per k-step
   constexpr int LB0 = T::LOADS_B / 2;      // weight loads in k-step 0's shadow, the rest in k-step 1's
-  using M0 = Mix<NR, has_next ? LB0 : 0>;
-  using M1 = Mix<NR, has_next ? T::LOADS_B - LB0 : 0>;
+  using M0 = Mix<KS::nr(1), has_next ? LB0 : 0>;
+  using M1 = Mix<KS::nr(2), has_next ? T::LOADS_B - LB0 : 0>;
+  constexpr int NR3 = KS::nr(3);
   const char* curB = cur + T::A_BYTES;
   Frags<BM, BN> f1, f2;
+  carry_weights<BM, BN>(f1, f0);
   // k-step 0 (reads k-step 1, weight loads of stage k+1)
 #pragma unroll
   for (int j = 0; j < NM; ++j) {
-    mfma_one<BM, BN>(f0, acc, j);
+    mfma_one<BM, BN, 0>(f0, acc, j);
 #pragma unroll
     for (int o = (j * M0::OPS) / NM; o < ((j + 1) * M0::OPS) / NM; ++o) {
       if (M0::load(o)) stage_load_one<BM, BN>(rA, a_off, rB, b_off, stride, k1_bytes, nxt_w, wave, lane,
@@ -278,7 +411,7 @@ __device__ __forceinline__ void phase_a(const char* cur, Frags<BM, BN>& f0, Frag
   // k-step 1 (reads k-step 2, the other weight loads of stage k+1)
 #pragma unroll
   for (int j = 0; j < NM; ++j) {
-    mfma_one<BM, BN>(f1, acc, j);
+    mfma_one<BM, BN, 1>(f1, acc, j);
 #pragma unroll
     for (int o = (j * M1::OPS) / NM; o < ((j + 1) * M1::OPS) / NM; ++o) {
       if (M1::load(o)) stage_load_one<BM, BN>(rA, a_off, rB, b_off, stride, k1_bytes, nxt_w, wave, lane,
@@ -288,11 +421,13 @@ __device__ __forceinline__ void phase_a(const char* cur, Frags<BM, BN>& f0, Frag
     FG_SCHED_FENCE();
   }
   // k-step 2 (reads k-step 3)
+  carry_weights<BM, BN>(f3, f2);
 #pragma unroll
   for (int j = 0; j < NM; ++j) {
-    mfma_one<BM, BN>(f2, acc, j);
+    mfma_one<BM, BN, 2>(f2, acc, j);
 #pragma unroll
-    for (int o = (j * NR) / NM; o < ((j + 1) * NR) / NM; ++o) frag_read_one<BM, BN>(cur, curB, f3, 3, o, wm, wn, lane);
+    for (int o = (j * NR3) / NM; o < ((j + 1) * NR3) / NM; ++o)
+      frag_read_one<BM, BN>(cur, curB, f3, 3, o, wm, wn, lane);
     FG_SCHED_FENCE();
   }
   if constexpr (has_next) {
@@ -312,12 +447,12 @@ __device__ __forceinline__ void phase_b(const char* nxt, Frags<BM, BN>& f3, Frag
                                         __amdgpu_buffer_rsrc_t rB, uint32_t b_off, uint32_t stride,
                                         uint32_t k2_bytes, char* cur_w, int wave, Hook& hook, int kst) {
   using T = Tile<BM, BN>;
-  constexpr int NM = T::FM * T::FN;
-  constexpr int NR = T::FM + T::FN;
-  using MB = Mix<NR, refill ? T::LOADS_A : 0>;
+  using KS = KStep<BM, BN>;
+  constexpr int NM = KS::NM;
+  using MB = Mix<KS::nr(0), refill ? T::LOADS_A : 0>;
 #pragma unroll
   for (int j = 0; j < NM; ++j) {
-    mfma_one<BM, BN>(f3, acc, j);
+    mfma_one<BM, BN, 3>(f3, acc, j);
     if (j == 0) {
       FG_SCHED_FENCE();
       hook.template store<PAR>(kst);
@@ -488,15 +623,35 @@ __device__ __forceinline__ void tile_mainloop_pp(__amdgpu_buffer_rsrc_t rA, uint
 // buffers in bytes (K * 2). l0..l3: the LDS stage buffers (distinct objects,
 // so the compiler can tell them apart when it places its own waits); the
 // 64-k variant uses l0 and l1.
+// The rows' version words (tile_row_versions, loaded before the K loop) as
+// one bit per word: bit v set = row word v is not the current route version
+// (a padding row). Computed once the words have arrived, so that the words
+// themselves do not hold registers through the K loop.
+template <int BM, int BN>
+__device__ __forceinline__ uint32_t pad_mask(const uint32_t (&ver_w)[Tile<BM, BN>::VW], uint32_t ver) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int v = 0; v < Tile<BM, BN>::VW; ++v) m |= (ver_w[v] != ver ? 1u : 0u) << v;
+  return m;
+}
+
+// ver_w / ver: a whole tile's row version words and the route version, folded
+// into `padmask` (pad_mask) once the first stage's loads, issued after the
+// words, have arrived; split-K parts pass has_rows = false.
 template <int BM, int BN, class Hook>
 __device__ __forceinline__ void tile_mainloop(__amdgpu_buffer_rsrc_t rA, uint32_t a_off,
                                               __amdgpu_buffer_rsrc_t rB, uint32_t b_off, uint32_t stride, int nk64,
-                                              char* l0, char* l1, char* l2, char* l3, Acc<BM, BN>& acc, Hook& hook) {
+                                              char* l0, char* l1, char* l2, char* l3, Acc<BM, BN>& acc, Hook& hook,
+                                              bool has_rows, const uint32_t (&ver_w)[Tile<BM, BN>::VW], uint32_t ver,
+                                              uint32_t& padmask) {
   using T = Tile<BM, BN>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / T::WGN, wn = wave % T::WGN;
   Frags<BM, BN> f0;
+  if constexpr (!(kBK == 64 && !kPingPong)) {
+    if (has_rows) padmask = pad_mask<BM, BN>(ver_w, ver);
+  }
   if constexpr (kBK == 64 && kPingPong) {
     tile_mainloop_pp<BM, BN>(rA, a_off, rB, b_off, stride, nk64, l0, l1, acc);
   } else if constexpr (kBK == 64) {
@@ -509,7 +664,8 @@ __device__ __forceinline__ void tile_mainloop(__amdgpu_buffer_rsrc_t rA, uint32_
     stage_load<BM, kPolA>(rA, a_off, stride, kRowB, lds1, wave, lane);
     wait_vmcnt<T::LOADS_A>();
     __syncthreads();
-    frags_read<BM, BN>(lds0, lds0 + T::A_BYTES, f0, 0, wm, wn, lane);
+    if (has_rows) padmask = pad_mask<BM, BN>(ver_w, ver);   // the words came before stage 0's loads
+    frags_read_kstep<BM, BN>(lds0, lds0 + T::A_BYTES, f0, 0, wm, wn, lane);
     // Rotated so that every iteration ends with phase A's workgroup barrier,
     // before which the compiler waits for all memory operations: nothing the
     // copy hook issues in phase B is still in flight where the loop's paths
@@ -576,48 +732,49 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // lane stores, loaded when the tile starts so that the store does not wait for
 // them: row m is padding when its word is not the current route version.
 template <int BM, int BN>
-__device__ __forceinline__ void tile_row_versions(const unsigned long long* inv, int m0, uint32_t (&ver_w)[Tile<BM, BN>::FM]) {
+__device__ __forceinline__ void tile_row_versions(const unsigned long long* inv, int m0,
+                                                  uint32_t (&ver_w)[Tile<BM, BN>::VW]) {
   using T = Tile<BM, BN>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / T::WGN;
   const uint32_t* words = reinterpret_cast<const uint32_t*>(inv);
 #pragma unroll
-  for (int fm = 0; fm < T::FM; ++fm) ver_w[fm] = words[2 * (m0 + wm * T::WM + fm * 32 + (lane & 31)) + 1];
+  for (int fm = 0; fm < T::FM; ++fm)
+#pragma unroll
+    for (int g = 0; g < (kMfma16 ? 2 : 1); ++g)
+      ver_w[acc_vw(fm, g)] = words[2 * (m0 + wm * T::WM + fm * 32 + acc_row(g, lane)) + 1];
 }
 
 // Direct store of the accumulators, 8 bytes per lane: rows as in tile_store,
 // for the variants whose stage buffers cannot hold a wave block per wave.
 template <int BM, int BN>
 __device__ __forceinline__ void tile_store_direct(__amdgpu_buffer_rsrc_t rO, int N, int m0, int n0,
-                                                  const Acc<BM, BN>& acc, const uint32_t (&ver_w)[Tile<BM, BN>::FM],
-                                                  uint32_t ver) {
+                                                  const Acc<BM, BN>& acc, uint32_t padmask) {
   using T = Tile<BM, BN>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / T::WGN, wn = wave % T::WGN;
-  const int lr = lane & 31, kh = lane >> 5;
 #pragma unroll
   for (int fm = 0; fm < T::FM; ++fm) {
-    const int m = m0 + wm * T::WM + fm * 32 + lr;
-    const bool pad = ver_w[fm] != ver;
-    const uint32_t row_off = (uint32_t)m * (uint32_t)N * 2;
 #pragma unroll
     for (int fn = 0; fn < T::FN; ++fn) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * T::WN + fn * 32 + 8 * g + 4 * kh;
-        const f32x16& c = acc.v[fm][fn];
+        const int m = m0 + wm * T::WM + fm * 32 + acc_row(g, lane);
+        const int n = n0 + wn * T::WN + fn * 32 + acc_col(g, lane);
+        const bool pad = (padmask >> acc_vw(fm, g)) & 1;
+        const f32x4 c = acc_group<BM, BN>(acc, fm, fn, g);
         v2i w;
-        w[0] = pad ? 0 : (int)pack_bf16x2(c[4 * g + 0], c[4 * g + 1]);
-        w[1] = pad ? 0 : (int)pack_bf16x2(c[4 * g + 2], c[4 * g + 3]);
-        __builtin_amdgcn_raw_buffer_store_b64(w, rO, row_off + (uint32_t)n * 2, 0, 0);
+        w[0] = pad ? 0 : (int)pack_bf16x2(c[0], c[1]);
+        w[1] = pad ? 0 : (int)pack_bf16x2(c[2], c[3]);
+        __builtin_amdgcn_raw_buffer_store_b64(w, rO, (uint32_t)m * (uint32_t)N * 2 + (uint32_t)n * 2, 0, 0);
       }
     }
   }
 }
 
 // Store the tile: padding rows (no current inverse-map entry) are written as zeros.
-// rO: output rows [*, N] (row stride N*2 bytes); m0, n0: tile origin; ver_w:
-// the rows' version words (tile_row_versions); l0, l1: the two LDS stage
+// rO: output rows [*, N] (row stride N*2 bytes); m0, n0: tile origin; padmask:
+// the rows' padding bits (pad_mask); l0, l1: the two LDS stage
 // buffers, free once the K loop's last barrier has passed (waves 0-3 use l0,
 // waves 4-7 l1).
 //
@@ -641,8 +798,7 @@ __device__ __forceinline__ void tile_store_direct(__amdgpu_buffer_rsrc_t rO, int
 // scheduler's workgroup barrier.
 template <int BM, int BN>
 __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int m0, int n0,
-                                           const Acc<BM, BN>& acc, const uint32_t (&ver_w)[Tile<BM, BN>::FM],
-                                           uint32_t ver, char* l0, char* l1) {
+                                           const Acc<BM, BN>& acc, uint32_t padmask, char* l0, char* l1) {
   using T = Tile<BM, BN>;
   constexpr int RB = T::WN * 2;          // bytes per row of the wave's block
   constexpr int CPR = RB / 16;           // 16-byte chunks per row
@@ -651,7 +807,7 @@ __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int
   constexpr int SUB = 32 * RB;           // bytes of one 32-row sub-block
   constexpr int NSUB = 4 * T::FM * SUB <= Tile<256, BN>::STAGE ? T::FM : 1;
   if constexpr (kWaves != 8 || 4 * SUB > Tile<256, BN>::STAGE) {
-    tile_store_direct<BM, BN>(rO, N, m0, n0, acc, ver_w, ver);   // the 4-wave variant
+    tile_store_direct<BM, BN>(rO, N, m0, n0, acc, padmask);   // the 4-wave variant
   } else {
     static_assert(RPI == 8 || RPI == 16, "read-back rows per access");
     // the lane's offsets are computed here, not hoisted out of the tile loop,
@@ -673,17 +829,41 @@ __device__ __forceinline__ void tile_store(__amdgpu_buffer_rsrc_t rO, int N, int
     const uint32_t out_lane = (uint32_t)(m0 + wm * T::WM + rr) * row_bytes + (uint32_t)(n0 + wn * T::WN + rc * 8) * 2;
 #pragma unroll
     for (int fm = 0; fm < T::FM; ++fm) {
-      char* const sub = wrow + (fm % NSUB) * SUB;
-      const bool pad = ver_w[fm] != ver;   // versioned inverse map: stale = padding
-#pragma unroll
-      for (int fn = 0; fn < T::FN; ++fn) {
+      if constexpr (kMfma16) {
+        // group g of lane l: row r = 16 (g & 1) + l % 16 of the sub-block,
+        // columns c0 .. c0 + 3 with c0 = 16 (g >> 1) + 4 (l / 16) in each
+        // column block: 16-byte chunk fn * 4 + c0 / 8, 8-byte half (c0 / 4) & 1
+        // (swapped in rows 16-31), the chunk's slot permuted as in swz. A
+        // half-wave writes 16 rows x 16 bytes: all 64 banks once.
+        char* const sub = blk + (fm % NSUB) * SUB;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x16& c = acc.v[fm][fn];
-          v2i w;
-          w[0] = pad ? 0 : (int)pack_bf16x2(c[4 * g + 0], c[4 * g + 1]);
-          w[1] = pad ? 0 : (int)pack_bf16x2(c[4 * g + 2], c[4 * g + 3]);
-          *reinterpret_cast<v2i*>(sub + (((fn * 4 + g) * 16) ^ sw)) = w;
+          const int r = acc_row(g, lane), c0 = acc_col(g, lane);
+          const bool pad = (padmask >> acc_vw(fm, g)) & 1;   // versioned inverse map: stale = padding
+          char* const row = sub + r * RB + ((((c0 >> 2) & 1) ^ (r >> 4)) * 8);
+          const int rsw = ((r / D) & (CPR - 1)) * 16;
+#pragma unroll
+          for (int fn = 0; fn < T::FN; ++fn) {
+            const f32x4 c = acc_group<BM, BN>(acc, fm, fn, g);
+            v2i w;
+            w[0] = pad ? 0 : (int)pack_bf16x2(c[0], c[1]);
+            w[1] = pad ? 0 : (int)pack_bf16x2(c[2], c[3]);
+            *reinterpret_cast<v2i*>(row + (((fn * 4 + (c0 >> 3)) * 16) ^ rsw)) = w;
+          }
+        }
+      } else {
+        char* const sub = wrow + (fm % NSUB) * SUB;
+        const bool pad = (padmask >> fm) & 1;   // versioned inverse map: stale = padding
+#pragma unroll
+        for (int fn = 0; fn < T::FN; ++fn) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 c = acc_group<BM, BN>(acc, fm, fn, g);
+            v2i w;
+            w[0] = pad ? 0 : (int)pack_bf16x2(c[0], c[1]);
+            w[1] = pad ? 0 : (int)pack_bf16x2(c[2], c[3]);
+            *reinterpret_cast<v2i*>(sub + (((fn * 4 + g) * 16) ^ sw)) = w;
+          }
         }
       }
       if constexpr (NSUB == T::FM) {
@@ -741,8 +921,7 @@ __device__ __forceinline__ void partial_store(__amdgpu_buffer_rsrc_t rW, uint32_
       for (int g = 0; g < 4; ++g) {
         // whole-vector bit casts only: a bit cast of a vector element lvalue
         // reads element 0 with this compiler
-        const f32x16& c = acc.v[fm][fn];
-        const f32x4 x = {c[4 * g + 0], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
+        const f32x4 x = acc_group<BM, BN>(acc, fm, fn, g);
         store16_coherent(rW, base + partial_off<BM, BN>(wave, f, g, lane), __builtin_bit_cast(v4i, x));
       }
     }
@@ -762,18 +941,17 @@ __device__ __forceinline__ void partial_sum_store(__amdgpu_buffer_rsrc_t rW, uin
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / T::WGN, wn = wave % T::WGN;
-  const int lr = lane & 31, kh = lane >> 5;
 #pragma unroll
   for (int fm = 0; fm < T::FM; ++fm) {
-    const int m = m0 + wm * T::WM + fm * 32 + lr;
-    const bool pad = (uint32_t)(inv[m] >> 32) != ver;
-    const uint32_t row_off = (uint32_t)m * (uint32_t)N * 2;
 #pragma unroll
     for (int fn = 0; fn < T::FN; ++fn) {
       const int f = fm * T::FN + fn;
       if (f % P != part) continue;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        const int m = m0 + wm * T::WM + fm * 32 + acc_row(g, lane);
+        const bool pad = (uint32_t)(inv[m] >> 32) != ver;
+        const uint32_t row_off = (uint32_t)m * (uint32_t)N * 2;
         // eight independent loads first (their latencies overlap); those of
         // parts q >= P point past the end of the buffer, where the buffer
         // unit returns zeros; then the sum in part order
@@ -787,7 +965,7 @@ __device__ __forceinline__ void partial_sum_store(__amdgpu_buffer_rsrc_t rW, uin
         f32x4 sum = v[0];
 #pragma unroll
         for (int q = 1; q < 8; ++q) sum += v[q];
-        const int n = n0 + wn * T::WN + fn * 32 + 8 * g + 4 * kh;
+        const int n = n0 + wn * T::WN + fn * 32 + acc_col(g, lane);
         v2i w;
         w[0] = pad ? 0 : (int)pack_bf16x2(sum[0], sum[1]);
         w[1] = pad ? 0 : (int)pack_bf16x2(sum[2], sum[3]);

@@ -631,26 +631,25 @@ struct TileCopy {
   int x, rho0, n_rows;     // list, first non-lead row and row count of this wave
   int upr;                 // segments per row (K * 2 / 1024)
   int n_seg, seg, r, u;    // segments to load, the next one, its row and segment in the row
-  int pend0, pr0, pu0;     // the segment loaded in the last even stage waits for its store: row, segment
-  int pend1, pr1, pu1;     // the same for the last odd stage
+  int pend0, pr0, pu0;     // the segment loaded in the last stage waits for its store: row, segment
   int k_mid;               // stage in which the rows are counted
   int counted;             // the counting adds are issued
   long long t_cnt;         // issue time of the counting adds (the TRACE stamp of the blocks they complete)
   uint32_t row_bytes;
   uint32_t g_lo, g_hi;     // the gathered buffer, held in registers (no argument load in the loop)
   bool strict;
-  int info;                // per lane: (shard << 24 | stream index), -1 for a padding row
-  int grow;                // per lane: gathered row
-  uint32_t src_lo, src_hi; // per lane: address of the source row (0 for a padding row)
+  // the wave's rows, entry i for row i: (shard << 24 | stream index, -1 for a
+  // padding row), gathered row, source row address (low, high); kept in LDS
+  // rather than in lane registers, which the K loop needs for its fragments
+  v4i* rows;
   uint32_t voff;           // per lane: byte offset of the lane's 16 bytes in a segment
-  v4i data0, data1;        // segments loaded in even / odd stages
+  v4i data0;               // the segment loaded in the last stage
 
-  __device__ __forceinline__ TileCopy(const FusedArgs& a_, const CopyPlan& p)
+  __device__ __forceinline__ TileCopy(const FusedArgs& a_, const CopyPlan& p, v4i* wave_rows)
       : a(a_), plan(p), x(0), rho0(0), n_rows(0), upr(1), n_seg(0), seg(0), r(0), u(0), pend0(0), pr0(0), pu0(0),
-        pend1(0), pr1(0), pu1(0),
         k_mid(-1), counted(1), t_cnt(0), row_bytes((uint32_t)a_.K * 2), g_lo((uint32_t)(uintptr_t)a_.gathered),
         g_hi((uint32_t)((uintptr_t)a_.gathered >> 32)),
-        strict((a_.flags & kStrict) != 0), info(-1), grow(0), src_lo(0), src_hi(0), voff(0) {}
+        strict((a_.flags & kStrict) != 0), rows(wave_rows), voff(0) {}
 
   // Rows [c0, c1) of list x's non-lead rows for the item; this wave's share.
   __device__ __forceinline__ void begin(int x_, int c0, int c1, int wave, int lane) {
@@ -666,15 +665,14 @@ struct TileCopy {
     if (w1 - w0 > 64 && lane == 0) raise_error(a.err, kErrProtocol, 0x40000000 | rho0);
     upr = a.K / 512;
     n_seg = n_rows * upr;
-    seg = 0; r = 0; u = 0; pend0 = 0; pend1 = 0;
+    seg = 0; r = 0; u = 0; pend0 = 0;
     counted = n_rows > 0 ? 0 : 1;
     // the last segment is loaded in phase B of stage n_seg - 1 and stored in
     // phase B of stage n_seg + 1; the wait in phase A of stage n_seg + 2
     // acknowledges the store
-    k_mid = n_rows > 0 ? n_seg + 2 : -1;
-    info = -1;
-    grow = 0;
-    src_lo = src_hi = 0;
+    k_mid = n_rows > 0 ? n_seg + 1 : -1;
+    int info = -1, grow = 0;
+    uint32_t src_lo = 0, src_hi = 0;
     // computed by an opaque instruction, so that the compiler keeps it in one
     // register instead of recomputing it into registers the stages reuse
     asm volatile("v_lshlrev_b32 %0, 4, %1" : "=v"(voff) : "v"(lane));
@@ -689,48 +687,54 @@ struct TileCopy {
         src_hi = (uint32_t)(p >> 32);
       }
     }
+    // only this wave reads its entries, and a wave's LDS operations complete in order
+    rows[lane] = v4i{info, grow, (int)src_lo, (int)src_hi};
   }
 
-  // The copy in the K loop (P = the stage's parity): early in phase B of
-  // stage k the wave stores the segment it loaded in stage k - 2 and loads
-  // the next one into the same registers; the load's latency hides behind
-  // the rest of phase B and phase A of stage k + 1, which ends with the wait
-  // for the wave's loads. Each is a uniform branch, taken only while there
-  // is a segment to move (the branch costs a few scalar instructions; the
-  // descriptors and the instructions, issued empty in every stage, cost 4-8 %
-  // of the tile). Between a load and its store lie two of the stage barriers,
-  // before which the compiler waits for every memory operation of the wave,
-  // so neither the store waits for its data nor the next load for the store;
-  // the two register sets stay allocated through the loop (finish() reads
-  // them), so no other value lands in registers a store still reads; the
-  // per-lane offset is a register set once per item. With any of these
-  // missing, the compiler put a wait for all loads in flight at the top of
-  // the stage.
+  // Entry i of the wave's rows, the same in every lane (i wave-uniform, < 64).
+  __device__ __forceinline__ v4i row_entry(int i) const { return rows[i]; }
+
+  // The copy in the K loop: early in phase B of stage k the wave stores the
+  // segment it loaded in stage k - 1 and loads the next one into the same
+  // registers; the load's latency hides behind the rest of phase B and phase
+  // A of stage k + 1, which ends with the wait for the wave's loads (P, the
+  // stage's parity, is not needed: one register set serves every stage).
+  // Each is a uniform branch, taken only while there is a segment to move
+  // (the branch costs a few scalar instructions; the descriptors and the
+  // instructions, issued empty in every stage, cost 4-8 % of the tile).
+  // Between a load and its store lies a stage barrier, before which the
+  // compiler waits for every memory operation of the wave, so the store does
+  // not wait for its data; the store reads its data registers when it issues,
+  // so the next load into them need not wait for it; the register set stays
+  // allocated through the loop (finish() reads it), so no other value lands
+  // in registers a store still reads; the per-lane offset is a register set
+  // once per item. With any of these missing, the compiler put a wait for all
+  // loads in flight at the top of the stage.
   template <int P>
   __device__ __forceinline__ void store(int) {
-    const int spr = P ? pr1 : pr0, spu = P ? pu1 : pu0;
-    if ((P ? pend1 : pend0) && readlane(info, spr) >= 0) {
-      const int g = readlane(grow, spr);
+    const v4i e = row_entry(pr0);
+    if (pend0 && __builtin_amdgcn_readfirstlane(e[0]) >= 0) {
+      const int g = __builtin_amdgcn_readfirstlane(e[1]);
       const uint16_t* gbase = (const uint16_t*)(((uint64_t)g_hi << 32) | g_lo);
-      const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(gbase + (size_t)g * (row_bytes / 2) + spu * 512, 1024u);
-      store16_coherent(rd, voff, P ? data1 : data0);
+      const __amdgpu_buffer_rsrc_t rd = buffer_rsrc(gbase + (size_t)g * (row_bytes / 2) + pu0 * 512, 1024u);
+      store16_coherent(rd, voff, data0);
     }
-    if (P) pend1 = 0; else pend0 = 0;
+    pend0 = 0;
   }
 
   template <int P>
   __device__ __forceinline__ void load(int) {
     const bool ld = seg < n_seg;
-    if (ld && readlane(info, r) >= 0) {
-      const uint64_t row = ((uint64_t)(uint32_t)readlane((int)src_hi, r) << 32) | (uint32_t)readlane((int)src_lo, r);
+    const v4i e = row_entry(min(r, 63));
+    if (ld && __builtin_amdgcn_readfirstlane(e[0]) >= 0) {
+      const uint64_t row = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(e[3]) << 32) |
+                           (uint32_t)__builtin_amdgcn_readfirstlane(e[2]);
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc((const uint16_t*)row + u * 512, 1024u);
       // the registers stay reserved until this load (the store just issued reads them)
-      if (P) asm volatile("" : "+v"(data1)); else asm volatile("" : "+v"(data0));
-      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
-      if (P) data1 = v; else data0 = v;
+      asm volatile("" : "+v"(data0));
+      data0 = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
     }
-    if (P) { pend1 = ld; pr1 = r; pu1 = u; }
-    else { pend0 = ld; pr0 = r; pu0 = u; }
+    pend0 = ld; pr0 = r; pu0 = u;
     seg += ld;
     const int nu = u + ld;
     const bool wrap = nu == upr;
@@ -753,7 +757,8 @@ struct TileCopy {
     const int lane = threadIdx.x & 63;
     if (strict) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     t_cnt = (long long)now_ticks();
-    const int blk = (lane < n_rows && info >= 0) ? grow / kRB : -1;
+    const v4i e = rows[lane];
+    const int blk = (lane < n_rows && e[0] >= 0) ? e[1] / kRB : -1;
     uint64_t pending = ballot(blk >= 0);
     while (pending) {
       const int l = __ffsll((long long)pending) - 1;
@@ -773,22 +778,22 @@ struct TileCopy {
   // publishes seq into the chunk's slot; an add past the chunk's size is a
   // protocol error.
   __device__ __forceinline__ void finish() {
-    // keeps both register sets of the copy allocated through the K loop
-    asm volatile("" ::"v"(data0), "v"(data1));
+    // keeps the copy's register set allocated through the K loop
+    asm volatile("" ::"v"(data0));
     if (n_rows == 0) return;
     if (!counted) {
-      while (pend0 || pend1 || seg < n_seg) {
+      while (pend0 || seg < n_seg) {
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         store<0>(0);
-        store<1>(0);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         load<0>(0);
-        load<1>(0);
       }
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       count();
     }
     const int lane = threadIdx.x & 63;
+    const v4i e = rows[lane];
+    const int info = e[0], grow = e[1];
     // TRACE: each block's stamp rises to the issue time of this wave's add;
     // the last add to a block completes it, so its stamp is the block's publish
     if ((a.flags & kTrace) && lane < n_rows && info >= 0)
@@ -897,23 +902,21 @@ __device__ __forceinline__ bool run_item(const FusedArgs& a, char* const* lds, i
   const int k0 = whole ? 0 : 2 * (nk2 * part / P);
   const int k1 = whole ? 2 * nk2 : 2 * (nk2 * (part + 1) / P);
   Acc<BM, BN> acc;
-#pragma unroll
-  for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) acc.v[i][j] = f32x16{};
-  uint32_t ver_w[T::FM];
+  acc_zero<BM, BN>(acc);
+  uint32_t ver_w[T::VW];
   if (whole) tile_row_versions<BM, BN>(a.inv, m0, ver_w);
+  uint32_t padmask = 0;
   // k0, k1 count k-iterations of 64 (128 bytes of a row)
   tile_mainloop<BM, BN>(rA, (uint32_t)m0 * row_bytes + (uint32_t)k0 * 128u, rB,
                         (uint32_t)n0 * row_bytes + (uint32_t)k0 * 128u, row_bytes, k1 - k0, lds[0], lds[1], lds[2],
-                        lds[3], acc, cp);
+                        lds[3], acc, cp, whole, ver_w, a.route_ver, padmask);
   cp.finish();
   if (whole) {
     // thread 0 (when pf_tick is given): the next ticket goes out before the
     // stores; the opaque zero keeps the atomic optimizer from rewriting the add
     // into a wave-wide one whose result it needs at once
     if (pf_tick) pf_j = fetch_add_relaxed(pf_tick + opaque_zero(), 1);
-    tile_store<BM, BN>(rO, a.N, m0, n0, acc, ver_w, a.route_ver, lds[0], lds[1]);
+    tile_store<BM, BN>(rO, a.N, m0, n0, acc, padmask, lds[0], lds[1]);
     return true;
   }
   // split-K part: blocks of one split tile are 256 x BN floats apart (the
@@ -956,6 +959,7 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
   // the group slab offsets (nine words) are read from LDS: the split tail
   // walks them once per list for every part it hands out
   __shared__ int sh_gslab[kXcds + 1];
+  __shared__ v4i sh_copy_rows[kWaves * 64];   // in-tile copy: each wave's row table (TileCopy)
   if (threadIdx.x <= kXcds) sh_gslab[threadIdx.x] = a.gslab[threadIdx.x];
   __syncthreads();
   L.gslab = sh_gslab;
@@ -1131,7 +1135,7 @@ __device__ __forceinline__ void gemm_role(const FusedArgs& a, char* const* lds, 
     if (copy_in_items && q < 0 && jitem >= 0) plan_item_rows(L.plan, x, jitem, &c0, &c1);
     bool ok;
     if (c1 > c0) {
-      TileCopy cp(a, L.plan);
+      TileCopy cp(a, L.plan, sh_copy_rows + 64 * __builtin_amdgcn_readfirstlane(threadIdx.x >> 6));
       cp.begin(x, c0, c1, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), threadIdx.x & 63);
       ok = (entry & 1) ? run_item<128, BN>(a, lds, sh, m0, n0, g, q, P, nk2, strict, gate, rA, rO, rW, tr, pf_tick,
                                            pf_j, cp)
