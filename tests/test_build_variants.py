@@ -1,5 +1,5 @@
 """The compile-time variants of the HIP sources (4-wave tile, ping-pong stage
-schedule, ring of four 32-k stages) still type-check for gfx950: a device-side
+schedule, ring of four 32-k stages, the 32x32x16 MFMA tile) still type-check for gfx950: a device-side
 syntax pass instantiates every kernel template, so a static assertion or a
 template error in a variant's path fails here (about a second each)."""
 import os
@@ -10,7 +10,7 @@ import pytest
 from sync_protocols_amd import build as B
 
 
-@pytest.mark.parametrize("define", ["-DFG_WAVES=4", "-DFG_PINGPONG=1", "-DFG_BK=32"])
+@pytest.mark.parametrize("define", ["-DFG_WAVES=4", "-DFG_PINGPONG=1", "-DFG_BK=32", "-DFG_MFMA16=0"])
 def test_variant_type_checks(define):
     if not os.path.exists(B.HIPCC):
         pytest.skip("hipcc is not available")
