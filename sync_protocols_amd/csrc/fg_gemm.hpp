@@ -45,7 +45,7 @@ constexpr int kBK = FG_BK;          // k per LDS stage: 64 (two stages of 128-by
                                     // four stages of 64-byte rows: same LDS, three stages of load lead)
 constexpr int kRowB = kBK * 2;      // bytes per tile row per stage
 constexpr int kRowsPerLoad = 1024 / kRowB;   // rows covered by one 64-lane 16-byte load
-constexpr int kKSteps = kBK / 16;   // MFMA k-steps per stage
+constexpr int kKSteps = kBK / 16;   // k-steps per stage (each a quarter of a 64-k stage's MFMAs, either shape)
 constexpr int kStages = kBK == 64 ? 2 : 4;
 constexpr int kChunks = kRowB / 16;          // 16-byte chunks per row and stage
 static_assert(kBK == 64 || kBK == 32, "stage depth");
