@@ -643,19 +643,35 @@ def power_fields(ctx, step, step_us, fg, torch, secs=1.5):
 def library_gemm_fields(b, fg, torch, rounds=3, n=25, skip=8):
     """The same contraction by the vendor library (torch.matmul, which PyTorch
     hands to hipBLASLt) on the same operands: the gathered rows of the last
-    fused step and W as [K][N]. Context for the roofline fraction, timed beside
+    fused step and W as [K][N] (grouped routes: one batched matmul over the
+    groups, padded to the largest). Context for the roofline fraction, timed beside
     the fused kernel's GEMM-only and fused modes in alternating rounds (each
     round: n back-to-back launches per variant, per-launch events, the first
     `skip` dropped; medians over the rounds), plus the largest difference
     between the two outputs."""
     wl = b.wl
-    if wl["n_groups"] != 1:
-        return None
-    M = wl["m_real"]
-    A = b.gathered[:M]
-    Wt = wl["w"].reshape(wl["N"], wl["K"]).t().contiguous()   # [K][N], contiguous (no transposed view)
-    out = torch.empty(M, wl["N"], dtype=torch.bfloat16, device="cuda:0")
     same = fg.CALL_SAME_ROUTE if wl["route"].mode != fg.ROUTE_CONTIG else 0
+    K, N, G = wl["K"], wl["N"], wl["n_groups"]
+    if G == 1:
+        M = wl["m_real"]
+        A = b.gathered[:M]
+        Wt = wl["w"].reshape(N, K).t().contiguous()   # [K][N], contiguous (no transposed view)
+        out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda:0")
+        lib_call = lambda: torch.matmul(A, Wt, out=out)  # noqa: E731
+        form = "one matmul"
+    else:
+        # grouped routes: one batched matmul over the groups, each padded to the
+        # largest group (padding rows of the gathered buffer are zero)
+        goff = b.ctx.read_i32(b.ctx.views().group_off, G + 1).tolist()
+        P = max(goff[g + 1] - goff[g] for g in range(G))
+        A = torch.zeros(G, P, K, dtype=torch.bfloat16, device="cuda:0")
+        for g in range(G):
+            A[g, :goff[g + 1] - goff[g]] = b.gathered[goff[g]:goff[g + 1]]
+        w3 = wl["w"].reshape(G, N, K)
+        Wt = torch.stack([w3[g].t().contiguous() for g in range(G)]).contiguous()   # [G][K][N]
+        outb = torch.empty(G, P, N, dtype=torch.bfloat16, device="cuda:0")
+        lib_call = lambda: torch.bmm(A, Wt, out=outb)  # noqa: E731
+        form = f"one batched matmul over {G} groups padded to {P} rows"
 
     def timed(fn):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
@@ -666,7 +682,7 @@ def library_gemm_fields(b, fg, torch, rounds=3, n=25, skip=8):
         torch.cuda.synchronize()
         return [ev[i].elapsed_time(ev[i + 1]) * 1000.0 for i in range(skip, n)]
 
-    variants = {"library": lambda: torch.matmul(A, Wt, out=out),
+    variants = {"library": lib_call,
                 "gemm_only": lambda: b.step(fg.CALL_GEMM_ONLY | same),
                 "fused": lambda: b.step(same)}
     ts = {k: [] for k in variants}
@@ -676,12 +692,17 @@ def library_gemm_fields(b, fg, torch, rounds=3, n=25, skip=8):
     b.step(fg.CALL_GEMM_ONLY | same)
     variants["library"]()
     torch.cuda.synchronize()
-    diff = (b.out[:M].float() - out.float()).abs().max().item()
+    if G == 1:
+        diff = (b.out[:M].float() - out.float()).abs().max().item()
+    else:
+        diff = max((b.out[goff[g]:goff[g + 1]].float() - outb[g, :goff[g + 1] - goff[g]].float()).abs().max().item()
+                   for g in range(G))
     b.step()
     torch.cuda.synchronize()
     b.check()
     med = {k: statistics.median(v) for k, v in ts.items()}
-    res = {k + "_us": round(v, 1) for k, v in med.items()}
+    res = {"library_form": form}
+    res.update({k + "_us": round(v, 1) for k, v in med.items()})
     res.update({k + "_TFLOPs": round(b.flop / (v * 1e-6) / 1e12, 1) for k, v in med.items()})
     res["gemm_only_over_library"] = round(med["library"] / med["gemm_only"], 4)
     res["fused_over_library"] = round(med["library"] / med["fused"], 4)
@@ -761,6 +782,9 @@ def main():
     if args.mode == "library":
         # profiling runs only: the same contraction by torch.matmul (hipBLASLt)
         # on the gathered rows of one fused step and W as [K][N]
+        if wl["n_groups"] != 1:
+            print("--mode library profiles the dense workloads (large, tp) only", file=sys.stderr)
+            sys.exit(2)
         b.step()
         M = wl["m_real"]
         A = b.gathered[:M]
